@@ -1,0 +1,235 @@
+"""fp64 CPU oracle of the Gated DeltaNet (GDN) token mixer.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the benchmark's CPU-baseline
+leg may import this module. The HIP library never calls it, and it shares no code with the
+library: it is the plain, slow definition the GPU results are checked against.
+
+Sources (the pages this follows; all quoted facts are restated, not copied):
+  [P2] "Qwen3.8-Flash-Next：架构、效率与技术谱系" (technical-report analysis notes)
+       §02 configuration table, GDN row: 48 value heads / 16 QK heads, head dim 128, short conv
+       kernel 4, Q/K/V go through the short causal conv.
+       §03 Gated DeltaNet, update equations: decay the state by alpha, read the error
+       e = v - S~^T k, write S = S~ + beta k e^T, read out y = S^T q; alpha and beta in (0, 1).
+       §03 "what Qwen changed": sigmoid output gate (instead of SiLU) and zero-centred RMSNorm.
+  [P3] "On the Design of Qwen3.8-Next Architecture … 精读" §四 4.1: product form of the same
+       recurrence, S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T, and q/k pass a
+       short conv + SiLU + L2 normalisation.
+  [P5] "Qwen3.8-Flash-Next" paper summary (hyper.ai, English), Method: learned projections then
+       short depthwise causal convolutions; L2-normalised queries and keys; head outputs are
+       normalised and then modulated by a sigmoid output gate.
+
+Readings where the pages are silent (every one is also listed in the design notes):
+  * conv + SiLU on q, k and v; L2 on q and k only.
+  * conv tap 3 multiplies the current token, taps 0..2 the three previous ones; no bias; the
+    history before a sequence start is ``conv_in`` (zeros when absent).
+  * L2: a / sqrt(sum(a^2) + l2_eps);  RMSNorm: y / sqrt(mean(y^2) + norm_eps) * (1 + w).
+  * value head h reads QK head floor(h * HK / HV) (contiguous groups).
+  * the state is stored [d_k][d_v] (row = key index); y carries an optional ``scale`` (1.0).
+
+Flags mirror the library's stage switches: CONV (conv + SiLU), L2QK, NORM, GATE.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+FLAG_CONV = 1
+FLAG_L2QK = 2
+FLAG_NORM = 4
+FLAG_GATE = 8
+FLAG_ALL = 15
+CONV_WIDTH = 4
+
+
+def silu(u):
+    """SiLU, u * sigmoid(u) ([P3] §四 4.1: SiLU after the short conv)."""
+    with np.errstate(over="ignore"):
+        return u / (1.0 + np.exp(-u))
+
+
+def sigmoid(z):
+    """Logistic function of the output gate ([P2] §03: the output gate is a sigmoid)."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def short_conv(x, w, hist):
+    """Causal depthwise conv of width 4 ([P2] §02 GDN row; [P5] Method).
+
+    x: [L, C] raw inputs of one sequence; w: [C, 4] taps; hist: [3, C] the three inputs before
+    the sequence start, oldest first. Returns u[t, c] = sum_j w[c, j] * x[t - 3 + j, c].
+    """
+    L = x.shape[0]
+    xx = np.concatenate([hist, x], axis=0)          # xx[t + 3] = x[t]
+    u = np.zeros((L, x.shape[1]), dtype=np.float64)
+    for j in range(CONV_WIDTH):
+        u += w[:, j][None, :] * xx[j:j + L]
+    return u
+
+
+def l2_normalize(a, eps):
+    """Row-wise L2 normalisation of queries and keys ([P5] Method; [P3] §四 4.1)."""
+    return a / np.sqrt(np.sum(a * a, axis=-1, keepdims=True) + eps)
+
+
+def gated_delta_rule(q, k, v, alpha, beta, S0, scale=1.0):
+    """Gated delta rule, error form ([P2] §03 update equations), one token at a time.
+
+    q, k: [L, d_k]; v: [L, d_v]; alpha, beta: [L]; S0: [d_k, d_v].
+    For each t:  S~ = alpha_t S;  e = v_t - S~^T k_t;  S = S~ + beta_t k_t e^T;  y_t = S^T q_t.
+    Returns (y [L, d_v], S_final [d_k, d_v]).
+    """
+    S = np.array(S0, dtype=np.float64, copy=True)
+    L, d_v = v.shape
+    y = np.empty((L, d_v), dtype=np.float64)
+    for t in range(L):
+        S_tilde = alpha[t] * S
+        e = v[t] - S_tilde.T @ k[t]
+        S = S_tilde + beta[t] * np.outer(k[t], e)
+        y[t] = scale * (S.T @ q[t])
+    return y, S
+
+
+def gated_delta_rule_product_form(q, k, v, alpha, beta, S0, scale=1.0):
+    """The same recurrence in product form ([P3] §四 4.1), kept only to pin the error form:
+    S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T;  y_t = S_t^T q_t."""
+    S = np.array(S0, dtype=np.float64, copy=True)
+    L, d_v = v.shape
+    eye = np.eye(k.shape[1])
+    y = np.empty((L, d_v), dtype=np.float64)
+    for t in range(L):
+        S = alpha[t] * (eye - beta[t] * np.outer(k[t], k[t])) @ S + beta[t] * np.outer(k[t], v[t])
+        y[t] = scale * (S.T @ q[t])
+    return y, S
+
+
+def zero_centred_rmsnorm(y, w, eps):
+    """RMSNorm over the d_v channels of one head with gain (1 + w) ([P2] §03: zero-centred
+    RMSNorm; [P5] Method: head outputs are normalised)."""
+    return y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps) * (1.0 + w)
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):          # a torch tensor: exact upcast of its values
+        a = a.detach().to("cpu").double().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def _head_channels(h, g, hk, hv, dk, dv):
+    """Channel index ranges (q | k | v order) of QK head g and value head h."""
+    q0 = g * dk
+    k0 = hk * dk + g * dk
+    v0 = 2 * hk * dk + h * dv
+    return slice(q0, q0 + dk), slice(k0, k0 + dk), slice(v0, v0 + dv)
+
+
+def gdn_chain(xq, xk, xv, wq, wk, wv, hq, hk_, hv_, alpha, beta, gate, norm_w, S0, *,
+              flags=FLAG_ALL, scale=1.0, l2_eps=1e-6, norm_eps=1e-6):
+    """The whole mixer for one (sequence, value head) chain.
+
+    xq, xk: [L, d_k] raw inputs of the chain's QK head; xv: [L, d_v] raw values;
+    wq/wk/wv: their conv taps [·, 4]; hq/hk_/hv_: their conv history [3, ·];
+    alpha, beta: [L]; gate: [L, d_v] logits; norm_w: [d_v]; S0: [d_k, d_v].
+    Steps: conv + SiLU, L2(q, k), gated delta rule, RMSNorm, sigmoid gate.
+    Returns (o [L, d_v], S_final [d_k, d_v]).
+    """
+    if flags & FLAG_CONV:
+        aq = silu(short_conv(xq, wq, hq))
+        ak = silu(short_conv(xk, wk, hk_))
+        av = silu(short_conv(xv, wv, hv_))
+    else:
+        aq, ak, av = xq, xk, xv
+    if flags & FLAG_L2QK:
+        aq = l2_normalize(aq, l2_eps)
+        ak = l2_normalize(ak, l2_eps)
+    y, S = gated_delta_rule(aq, ak, av, alpha, beta, S0, scale)
+    o = y
+    if flags & FLAG_NORM:
+        o = zero_centred_rmsnorm(o, norm_w, norm_eps)
+    if flags & FLAG_GATE:
+        o = o * sigmoid(gate)
+    return o, S
+
+
+def prefill_chain(inp, n, h, *, flags=FLAG_ALL, scale=1.0, l2_eps=1e-6, norm_eps=1e-6,
+                  state_in=None, conv_in=None):
+    """Run one (sequence n, value head h) chain of a packed prefill.
+
+    ``inp`` holds q [T,HK,dk], k [T,HK,dk], v [T,HV,dv], alpha/beta [T,HV], gate [T,HV,dv],
+    conv_w [C,4], norm_w [dv] or [HV,dv], cu_seqlens [N+1] and optional state_in
+    [N,HV,dk,dv] / conv_in [N,3,C] (arrays or tensors; values are upcast to fp64 exactly).
+    Returns (o [L, d_v], S_final [d_k, d_v]) for that chain.
+    """
+    cu = np.asarray(_f64(inp["cu_seqlens"]), dtype=np.int64)
+    s0, s1 = int(cu[n]), int(cu[n + 1])
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    hk, dk = q.shape[1], q.shape[2]
+    hv, dv = v.shape[1], v.shape[2]
+    g = (h * hk) // hv
+    cq, ck, cv = _head_channels(h, g, hk, hv, dk, dv)
+    conv_w = _f64(inp["conv_w"])
+    st = state_in if state_in is not None else inp.get("state_in")
+    ci = conv_in if conv_in is not None else inp.get("conv_in")
+    if ci is not None:
+        ci_n = _f64(ci[n])
+        hq, hk_, hv_ = ci_n[:, cq], ci_n[:, ck], ci_n[:, cv]
+    else:
+        hq, hk_, hv_ = (np.zeros((CONV_WIDTH - 1, dk)), np.zeros((CONV_WIDTH - 1, dk)),
+                        np.zeros((CONV_WIDTH - 1, dv)))
+    S0 = _f64(st[n, h]) if st is not None else np.zeros((dk, dv))
+    nw = _f64(inp["norm_w"])
+    nw = nw if nw.ndim == 1 else nw[h]
+    return gdn_chain(_f64(q[s0:s1, g]), _f64(k[s0:s1, g]), _f64(v[s0:s1, h]),
+                     conv_w[cq], conv_w[ck], conv_w[cv], hq, hk_, hv_,
+                     _f64(inp["alpha"][s0:s1, h]), _f64(inp["beta"][s0:s1, h]),
+                     _f64(inp["gate"][s0:s1, h]), nw, S0,
+                     flags=flags, scale=scale, l2_eps=l2_eps, norm_eps=norm_eps)
+
+
+def conv_tail(x_raw, hist):
+    """The last 3 raw inputs of a sequence per channel (history first when L < 3)."""
+    return np.concatenate([hist, x_raw], axis=0)[-(CONV_WIDTH - 1):]
+
+
+def gdn_prefill(inp, *, flags=FLAG_ALL, scale=1.0, l2_eps=1e-6, norm_eps=1e-6):
+    """Whole packed prefill: every (sequence, value head) chain, then the conv-cache tail.
+
+    Sequences split by ``cu_seqlens`` are independent. Returns (o [T,HV,dv],
+    state_out [N,HV,dk,dv], conv_out [N,3,C]) in fp64.
+    """
+    cu = np.asarray(_f64(inp["cu_seqlens"]), dtype=np.int64)
+    N = len(cu) - 1
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    C = 2 * hk * dk + hv * dv
+    o = np.zeros((T, hv, dv))
+    S_out = np.zeros((N, hv, dk, dv))
+    conv_out = np.zeros((N, CONV_WIDTH - 1, C))
+    ci = inp.get("conv_in")
+    for n in range(N):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        for h in range(hv):
+            o[s0:s1, h], S_out[n, h] = prefill_chain(inp, n, h, flags=flags, scale=scale,
+                                                     l2_eps=l2_eps, norm_eps=norm_eps)
+        x_raw = np.concatenate([_f64(q[s0:s1]).reshape(s1 - s0, -1),
+                                _f64(k[s0:s1]).reshape(s1 - s0, -1),
+                                _f64(v[s0:s1]).reshape(s1 - s0, -1)], axis=1)
+        hist = _f64(ci[n]) if ci is not None else np.zeros((CONV_WIDTH - 1, C))
+        conv_out[n] = conv_tail(x_raw, hist)
+    return o, S_out, conv_out
+
+
+def gdn_decode(step, state, conv_state, conv_w, norm_w, *, flags=FLAG_ALL, scale=1.0,
+               l2_eps=1e-6, norm_eps=1e-6):
+    """One decode step: the prefill with one token per sequence, state and conv cache carried.
+
+    ``step`` holds q [B,HK,dk], k [B,HK,dk], v [B,HV,dv], alpha/beta [B,HV], gate [B,HV,dv].
+    Returns (o [B,HV,dv], new state [B,HV,dk,dv], new conv cache [B,3,C]) in fp64.
+    """
+    B = step["q"].shape[0]
+    inp = dict(step)
+    inp.update(cu_seqlens=np.arange(B + 1), conv_w=conv_w, norm_w=norm_w,
+               state_in=state, conv_in=conv_state)
+    return gdn_prefill(inp, flags=flags, scale=scale, l2_eps=l2_eps, norm_eps=norm_eps)
