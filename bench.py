@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN token mixer on one MI355X.
+
+Headline: prefill tokens/s of one GDN layer at model shape (B=1, T=4096, 16 QK / 48 value heads,
+d=128, bf16 io, fp32 state). A step is one gdn_prefill call over that batch: conv + SiLU + L2,
+WY transform, state propagation, output + RMSNorm + gate, conv tail. The decode step (B=256, one
+token each, state streamed in place) is timed in the same run and reported beside it.
+
+Per-kernel times come from HIP events the library records on its stream around each stage, over
+the timed steps; the dominant kernel's algorithmic bytes (or flops) per launch divided by its mean
+duration gives the roofline fraction. The fp64 CPU oracle is timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+# Shape of the layer (16 QK heads, 48 value heads, d = 128, chunk 64).
+HK, HV, D, CH = 16, 48, 128, 64
+
+
+def stage_model(T: int, n_seqs: int):
+    """Algorithmic bytes and flops of each prefill stage for T tokens (bf16 io, model shape).
+
+    Bytes: each stage's inputs read once and outputs written once. Flops: dense-tile MFMA work
+    (2 per multiply-add) of the stage's contractions.
+    """
+    nc = -(-T // CH) + 0  # chunks (B=1 here: ceil(T / 64))
+    per_tok = {
+        # raw q/k/v in (20480 B) + normalised q/k/v out (20480 B)
+        "conv_silu_l2": dict(bytes=40960 * T + 10240 * 16, flops=0.0, bound="hbm"),
+        # k^, v^, alpha, beta in; U, Wk (bf16 64x128 per chunk and value head), G, K^T out
+        "wy_or_sequential": dict(bytes=(4096 + 12288 + 384) * T + nc * (HV * (2 * 64 * 128 * 2 + 64 * 4) + HK * 128 * 64 * 2),
+                                 flops=nc * HV * 3 * 2 * 64 * 64 * 128, bound="hbm"),
+        # Wk, U, K^T, G in; chunk-start states (bf16 128x128) and W (bf16 128x64) out; final states
+        "state": dict(bytes=nc * (HV * (2 * 64 * 128 * 2 + 64 * 4) + HK * 128 * 64 * 2)
+                      + nc * HV * (128 * 128 * 2 + 128 * 64 * 2) + n_seqs * HV * 128 * 128 * 4,
+                      flops=nc * HV * 2 * 2 * 64 * 128 * 128, bound="hbm"),
+        # q^, k^, G, chunk states, W, gate in; o out
+        "output_norm_gate": dict(bytes=(8192 + 12288 + 12288) * T + nc * HV * (128 * 128 * 2 + 128 * 64 * 2 + 64 * 4),
+                                 flops=nc * HV * (2 * 64 * 64 * 128 + 2 * 64 * 128 * 128 + 2 * 64 * 64 * 128),
+                                 bound="hbm"),
+        "conv_tail": dict(bytes=n_seqs * 3 * 10240 * 2 * 2, flops=0.0, bound="hbm"),
+        "chunk_table": dict(bytes=nc * 16, flops=0.0, bound="hbm"),
+    }
+    return per_tok
+
+
+def path_bytes(T: int, n_seqs: int, state_in: bool) -> float:
+    """Compulsory bytes of the whole prefill: raw q/k/v, gate, o, alpha/beta and the states."""
+    return 45440.0 * T + n_seqs * HV * 128 * 128 * 4 * (2 if state_in else 1)
+
+
+def path_flops(T: int) -> float:
+    """Dense-tile MFMA flops of the chunked algorithm (8.65 MFLOP per token at this shape)."""
+    nc = -(-T // CH)
+    per_chunk_head = (3 * 2 * 64 * 64 * 128          # Gram, U, Wk
+                      + 2 * 2 * 64 * 128 * 128       # Wk S, K^T W
+                      + 2 * 64 * 64 * 128            # Q K^T
+                      + 2 * 64 * 128 * 128           # Q S
+                      + 2 * 64 * 64 * 128)           # P W
+    return float(nc * HV * per_chunk_head)
+
+
+def decode_bytes(B: int) -> float:
+    """Per decode step: state read + write, conv cache read + write, q/k/v, gate, o, alpha/beta."""
+    return float(B * (HV * 128 * 128 * 4 * 2 + 3 * 10240 * 2 * 2 + 10240 * 2 + HV * 128 * 2 * 2 + HV * 8))
+
+
+def cpu_baseline(max_tokens: int):
+    """The fp64 oracle on the host: one layer at model shape (all 48 value heads), one thread."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle as O
+    from workloads import config_layer
+    inp = config_layer("cpu", T=max_tokens)
+    d = vars(inp)
+    with threadpool_limits(1):
+        O.prefill_chain(d, 0, 0)          # first-call warm-up (library dispatch setup)
+        t0 = time.perf_counter()
+        for h in range(HV):
+            O.prefill_chain(d, 0, h)
+        dt = time.perf_counter() - t0
+    return dict(value=max_tokens / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"fp64 numpy oracle, one layer at model shape, B=1, T={max_tokens}, all 48 value "
+                       f"heads (conv + SiLU + L2 + per-token recurrence + RMSNorm + gate), one thread, "
+                       f"{dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=4096, help="prefill length (one sequence)")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--decode-batch", type=int, default=256)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the GDN mixer path here has no multi-GPU code "
+              "(sequences and heads would shard without communication). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_token_amd import gdn
+    from workloads import config_layer, decode_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gdn.load_library()
+    stream = torch.cuda.current_stream()
+
+    # ---------------- prefill: one layer, B=1, T tokens -----------------------------------------
+    T = args.tokens
+    inp = config_layer(dev, T=T)
+    cfg = gdn.cfg_for(HK, HV, D, D, torch.bfloat16)
+    out = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
+    state_out = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
+    conv_out = torch.empty((1, 3, inp.n_channels), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_workspace(cfg, 1, T), dtype=torch.uint8, device=dev)
+    cu_host = inp.cu_seqlens.cpu()
+
+    def step():
+        gdn.gdn_prefill(cfg, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.gate,
+                        inp.conv_w, inp.norm_w, state_in=None, state_out=state_out, conv_out=conv_out,
+                        out=out, workspace=ws, cu_seqlens_host=cu_host)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # stage events: N_STAGES + 1 per timed step, created by recording once
+    import ctypes
+    nev = gdn.N_STAGES + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in evs]
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        gdn.gdn_set_stage_events(handles[i])
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    gdn.gdn_set_stage_events(None)
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j, name in enumerate(gdn.STAGE_NAMES)}
+
+    model = stage_model(T, 1)
+    dom = max(stage_ms, key=stage_ms.get)
+    dm = model[dom]
+    dom_s = stage_ms[dom] * 1e-3
+    if dm["bound"] == "hbm":
+        achieved = dm["bytes"] / dom_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None)
+    else:
+        achieved = dm["flops"] / dom_s / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+    roof["kernel"] = dom
+    roof["ms_per_launch"] = round(stage_ms[dom], 5)
+    roof["algorithmic_bytes"] = dm["bytes"]
+    roof["algorithmic_flops"] = dm["flops"]
+
+    pb, pf = path_bytes(T, 1, False), path_flops(T)
+    t_hbm, t_mfma = pb / (HBM_PEAK_GBPS * 1e9), pf / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    s = ms_step * 1e-3
+    path = dict(bytes=pb, flops=pf, hbm_bound_us=round(t_hbm * 1e6, 2), mfma_bound_us=round(t_mfma * 1e6, 2),
+                frac_of_roofline=round(max(t_hbm, t_mfma) / s, 4), frac_of_mfma_bound=round(t_mfma / s, 4),
+                achieved_GBps=round(pb / s / 1e9, 1), achieved_TFLOPs=round(pf / s / 1e12, 2))
+
+    result = {
+        "metric": "GDN prefill tokens/s/GPU (48 v-heads, d=128) + decode step us at B=256; % roofline",
+        "value": round(T / s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"GDN layer prefill, B=1, T={T}, 16 QK / 48 value heads, d=128, chunk 64, "
+                               f"bf16 io, fp32 state, conv4+SiLU+L2+RMSNorm+sigmoid gate",
+                   "batch": 1, "seq_len": T},
+        "roofline": roof,
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "path_roofline": path,
+        "wall_s": round(t_wall, 4),
+    }
+
+    # ---------------- decode: B sequences, one token each ----------------------------------------
+    if not args.no_decode:
+        B, S = args.decode_batch, args.decode_steps
+        di = decode_inputs(B, S, n_qk_heads=HK, n_v_heads=HV, d_k=D, d_v=D, io_dtype=torch.bfloat16,
+                           device=dev)
+        # starting states: the final state and conv tail of a 1024-token prefill of each sequence
+        pre = config_layer(dev, T=1024 * B, seed=1)
+        pre.cu_seqlens = (torch.arange(B + 1, dtype=torch.int32) * 1024).to(dev)
+        st = torch.empty((B, HV, D, D), dtype=torch.float32, device=dev)
+        cst = torch.empty((B, 3, inp.n_channels), dtype=torch.bfloat16, device=dev)
+        gdn.gdn_prefill(cfg, pre.cu_seqlens, pre.q, pre.k, pre.v, pre.alpha, pre.beta, pre.gate, pre.conv_w,
+                        pre.norm_w, state_out=st, conv_out=cst)
+        del pre
+        dout = torch.empty((B, HV, D), dtype=torch.bfloat16, device=dev)
+
+        def dstep(i):
+            gdn.gdn_decode_step(cfg, di.q[i], di.k[i], di.v[i], di.alpha[i], di.beta[i], di.gate[i],
+                                di.conv_w, di.norm_w, cst, st, out=dout)
+
+        for i in range(min(args.warmup, S)):
+            dstep(i)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for i in range(S):
+            dstep(i)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        us = d0.elapsed_time(d1) * 1e3 / S
+        db = decode_bytes(B)
+        gbps = db / (us * 1e-6) / 1e9
+        result["decode"] = {
+            "workload": f"decode step, B={B} sequences x 1 token, 16 QK / 48 value heads, d=128, bf16 io, "
+                        f"fp32 state in place, {S} consecutive steps",
+            "us_per_step": round(us, 2),
+            "roofline": dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                             frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=None, kernel="decode",
+                             algorithmic_bytes=db),
+        }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/* gdn.h — C ABI of the Gated DeltaNet (GDN) token mixer for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the mixer of one GDN layer; sources are web pages on Qwen3.8-Flash-Next):
+ *   1. short causal depthwise conv of width 4 on the raw q, k and v channels, then SiLU
+ *      ("Qwen3.8-Flash-Next：架构、效率与技术谱系" §02 configuration table, GDN row; paper
+ *      reading "On the Design of Qwen3.8-Next Architecture … 精读" §四 4.1);
+ *   2. L2 normalisation of q and k per head (paper summary "Qwen3.8-Flash-Next", Method);
+ *   3. the gated delta rule per value head h, QK head g = floor(h * HK / HV), state S [d_k][d_v]
+ *      (analysis notes §03 update equations):
+ *          S~ = alpha_t S;  e = v_t - S~^T k_t;  S = S~ + beta_t k_t e^T;  y_t = scale * S^T q_t
+ *   4. zero-centred RMSNorm over the d_v channels of each head, multiplier (1 + w)
+ *      (analysis notes §03, changes made to GDN), then
+ *   5. a sigmoid output gate, elementwise (paper summary, Method: normalised, then gated).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library allocates no memory,
+ *     keeps no device state between calls and never synchronises: work is enqueued on the
+ *     caller's stream (`hip_stream`, a hipStream_t; NULL = the default stream) and the call
+ *     returns after the enqueue. Device faults surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host first. On failure the call returns a status, enqueues
+ *     nothing, leaves every output untouched and records a message for gdn_last_error().
+ *     A failing kernel launch returns GDN_E_HIP.
+ *   - Tensor pointers must be 16-byte aligned, except alpha, beta and cu_seqlens (4-byte). Row
+ *     strides are in elements and must keep every row 16-byte aligned (a multiple of 8 for bf16,
+ *     of 4 for fp32).
+ *   - "io" tensors (q, k, v, gate, out, conv state) have the dtype cfg->io_dtype; alpha, beta,
+ *     conv weights, norm gains and recurrent states are always fp32.
+ *   - Channel order of the conv (weights and conv state): all q channels [HK][d_k], then all k
+ *     channels [HK][d_k], then all v channels [HV][d_v]; C_tot = 2*HK*d_k + HV*d_v.
+ *   - Conv tap j (0..3) multiplies the input 3-j tokens before the current one (tap 3 = current).
+ *     The conv state holds the 3 most recent raw inputs per channel, oldest first.
+ *   - Functions are reentrant; concurrent calls need distinct workspaces. Prefill results are
+ *     bitwise reproducible for a fixed configuration and device (no atomics).
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_E_NULL = 1,        /* a required pointer is NULL                                   */
+  GDN_E_SHAPE = 2,       /* head counts, dims, lengths or cu_seqlens are inconsistent    */
+  GDN_E_DTYPE = 3,       /* unknown io dtype                                             */
+  GDN_E_ALIGN = 4,       /* pointer or stride breaks the 16-byte rule                    */
+  GDN_E_WORKSPACE = 5,   /* workspace NULL or smaller than gdn_prefill_workspace()      */
+  GDN_E_UNSUPPORTED = 6, /* valid but not implemented (e.g. conv width != 4, d > 128)    */
+  GDN_E_HIP = 7,         /* a HIP runtime call or kernel launch failed                   */
+  GDN_E_VALUE = 8        /* a scalar parameter is out of range (eps < 0, flags)          */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* Stage switches (cfg->flags). GDN_CONV covers the conv and its SiLU. With NORM and GATE off the
+ * output is the raw readout y. GDN_ALL is the layer as the pages describe it. */
+enum { GDN_CONV = 1u, GDN_L2QK = 2u, GDN_NORM = 4u, GDN_GATE = 8u, GDN_ALL = 15u };
+
+typedef struct gdn_cfg {
+  int32_t n_qk_heads;       /* HK: 16 at the model shape                                      */
+  int32_t n_v_heads;        /* HV: 48 at the model shape; HV % HK == 0                        */
+  int32_t d_k;              /* key/query head dim: 128 at the model shape; 16, 32, 64 or 128 */
+  int32_t d_v;              /* value head dim: 128 at the model shape; 16, 32, 64 or 128     */
+  int32_t conv_width;       /* must be 4                                                      */
+  int32_t io_dtype;         /* gdn_dtype                                                      */
+  uint32_t flags;           /* GDN_* stage switches                                           */
+  float scale;              /* readout scale on y (1.0)                                       */
+  float l2_eps;             /* q/k L2: a / sqrt(sum a^2 + l2_eps) (1e-6)                      */
+  float norm_eps;           /* RMSNorm: y / sqrt(mean y^2 + norm_eps) (1e-6)                  */
+  int32_t norm_head_stride; /* 0: one gain vector w[d_v] for all heads; d_v: w[HV][d_v]      */
+} gdn_cfg;
+
+/* Fills *cfg with the model-shape defaults: HK=16, HV=48, d_k=d_v=128, width 4, bf16,
+ * GDN_ALL, scale 1, eps 1e-6, shared gain. */
+void gdn_cfg_default(gdn_cfg* cfg);
+
+/* Bytes of device workspace gdn_prefill needs for this configuration, for any packing of
+ * `total_tokens` tokens into `n_seqs` sequences. Pure host computation. */
+gdn_status gdn_prefill_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                                 size_t* bytes);
+
+/* Packed (variable-length) prefill of `n_seqs` independent sequences, `total_tokens` tokens in
+ * all. Sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]).
+ *
+ *   cu_seqlens        device int32 [n_seqs+1], cu[0] = 0, cu[n_seqs] = total_tokens,
+ *                     non-decreasing. Out-of-range device values are clamped, never read
+ *                     out of bounds, but give meaningless results.
+ *   cu_seqlens_host   optional host copy of the same array; when given it is validated
+ *                     (GDN_E_SHAPE on violation). May be NULL.
+ *   q, k              io [T][HK][d_k], token row stride ld_q / ld_k elements (>= HK*d_k).
+ *   v                 io [T][HV][d_v], token row stride ld_v (>= HV*d_v).
+ *   alpha, beta       fp32 [T][HV]: per-token decay in (0, 1] and write strength in [0, 1].
+ *   gate              io [T][HV][d_v] sigmoid-gate logits; required iff GDN_GATE.
+ *   conv_w            fp32 [C_tot][4]; required iff GDN_CONV.
+ *   norm_w            fp32 [d_v] (norm_head_stride 0) or [HV][d_v]; required iff GDN_NORM.
+ *   state_in          fp32 [n_seqs][HV][d_k][d_v] initial states; NULL = zeros.
+ *   state_out         fp32 [n_seqs][HV][d_k][d_v] final states; NULL = not written.
+ *                     May alias state_in.
+ *   conv_in           io [n_seqs][3][C_tot] raw inputs before each sequence; NULL = zeros.
+ *   conv_out          io [n_seqs][3][C_tot] the last 3 raw inputs of each sequence (from conv_in
+ *                     when a sequence is shorter than 3); NULL = not written. May alias conv_in.
+ *   out               io [T][HV][d_v] mixer output (raw y when NORM and GATE are off).
+ *   workspace         device scratch of at least gdn_prefill_workspace() bytes, 256-byte
+ *                     aligned; its contents on entry do not matter.
+ * The bf16 path at d_k = d_v = 128 runs the chunked (64-token) WY form on bf16 MFMA with an
+ * fp32 state; every other configuration (and every fp32-io call) runs a token-sequential fp32
+ * recurrence, which keeps fp32 accuracy. */
+gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                       const void* q, const void* k, const void* v,
+                       int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                       const float* alpha, const float* beta, const void* gate,
+                       const float* conv_w, const float* norm_w,
+                       const float* state_in, float* state_out,
+                       const void* conv_in, void* conv_out,
+                       void* out, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* One decode step for `batch` independent sequences, one new token each: the prefill above with
+ * every sequence of length 1, its state and conv cache updated in place.
+ *   q, k        io [B][HK][d_k], row stride ld_q / ld_k;  v io [B][HV][d_v], row stride ld_v.
+ *   alpha, beta fp32 [B][HV];  gate io [B][HV][d_v] (iff GDN_GATE).
+ *   conv_w, norm_w as for gdn_prefill.
+ *   conv_state  io [B][3][C_tot]: read as the history, then shifted to end with this token.
+ *               Required iff GDN_CONV.
+ *   state       fp32 [B][HV][d_k][d_v], updated in place.
+ *   out         io [B][HV][d_v].
+ * Any supported head dims and io dtype; HV / HK <= 64. */
+gdn_status gdn_decode_step(const gdn_cfg* cfg, int32_t batch,
+                           const void* q, const void* k, const void* v,
+                           int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                           const float* alpha, const float* beta, const void* gate,
+                           const float* conv_w, const float* norm_w,
+                           void* conv_state, float* state, void* out, void* hip_stream);
+
+/* Stage timing for profilers (host-side, per calling thread). After this call, every gdn_prefill
+ * on this thread records events[i] on its stream before stage i and events[GDN_N_STAGES] after the
+ * last stage, for the stages
+ *   0 chunk table, 1 conv + SiLU + L2, 2 WY transform (or the token-sequential recurrence),
+ *   3 state propagation, 4 output + RMSNorm + gate, 5 conv-cache tail;
+ * stages a path does not run get back-to-back events. `events` holds GDN_N_STAGES + 1 hipEvent_t
+ * handles created by the caller and must stay valid while set; NULL switches recording off.
+ * Returns GDN_E_SHAPE if n_events != GDN_N_STAGES + 1. */
+#define GDN_N_STAGES 6
+gdn_status gdn_set_stage_events(void* const* events, int32_t n_events);
+
+/* Static description of a status code. */
+const char* gdn_status_string(gdn_status status);
+
+/* Message of the last failing call on this thread ("" if none). Valid until the next call. */
+const char* gdn_last_error(void);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,296 @@
+// C ABI of the GDN mixer: host-side validation, workspace layout and kernel dispatch.
+// Every check runs before any HIP call, so a rejected call enqueues nothing and touches no output.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+static thread_local char g_last_error[512] = "";
+static thread_local void* const* g_stage_events = nullptr;
+
+// Records the stage event `i` on `s` when stage timing is on.
+static hipError_t mark(int i, hipStream_t s) {
+  if (!g_stage_events) return hipSuccess;
+  return hipEventRecord(static_cast<hipEvent_t>(g_stage_events[i]), s);
+}
+
+static gdn_status fail(gdn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Validates the configuration and fills the fields of Problem that depend on it alone.
+static gdn_status check_cfg(const gdn_cfg* cfg, Problem& p) {
+  if (!cfg) return fail(GDN_E_NULL, "cfg is NULL");
+  if (cfg->io_dtype != GDN_BF16 && cfg->io_dtype != GDN_F32)
+    return fail(GDN_E_DTYPE, "io_dtype %d is neither GDN_BF16 nor GDN_F32", cfg->io_dtype);
+  if (cfg->n_qk_heads <= 0 || cfg->n_v_heads <= 0)
+    return fail(GDN_E_SHAPE, "head counts must be positive (HK=%d, HV=%d)", cfg->n_qk_heads, cfg->n_v_heads);
+  if (cfg->n_v_heads % cfg->n_qk_heads != 0)
+    return fail(GDN_E_SHAPE, "HV=%d is not a multiple of HK=%d", cfg->n_v_heads, cfg->n_qk_heads);
+  if (cfg->d_k <= 0 || cfg->d_v <= 0)
+    return fail(GDN_E_SHAPE, "head dims must be positive (d_k=%d, d_v=%d)", cfg->d_k, cfg->d_v);
+  if (!supported_dim(cfg->d_k) || !supported_dim(cfg->d_v))
+    return fail(GDN_E_UNSUPPORTED, "head dims must be 16, 32, 64 or 128 (d_k=%d, d_v=%d)", cfg->d_k, cfg->d_v);
+  if (cfg->conv_width != 4) return fail(GDN_E_UNSUPPORTED, "conv_width %d: only 4 is implemented", cfg->conv_width);
+  if (cfg->flags & ~uint32_t(GDN_ALL)) return fail(GDN_E_VALUE, "unknown flag bits 0x%x", cfg->flags);
+  if (!(cfg->l2_eps >= 0.f) || !(cfg->norm_eps >= 0.f))
+    return fail(GDN_E_VALUE, "eps values must be >= 0 (l2_eps=%g, norm_eps=%g)", cfg->l2_eps, cfg->norm_eps);
+  if (cfg->norm_head_stride != 0 && cfg->norm_head_stride != cfg->d_v)
+    return fail(GDN_E_SHAPE, "norm_head_stride must be 0 or d_v (%d)", cfg->norm_head_stride);
+  p.hk = cfg->n_qk_heads;
+  p.hv = cfg->n_v_heads;
+  p.dk = cfg->d_k;
+  p.dv = cfg->d_v;
+  p.C = 2 * int64_t(p.hk) * p.dk + int64_t(p.hv) * p.dv;
+  p.flags = cfg->flags;
+  p.scale = cfg->scale;
+  p.l2_eps = cfg->l2_eps;
+  p.norm_eps = cfg->norm_eps;
+  p.norm_stride = cfg->norm_head_stride;
+  p.bf16 = cfg->io_dtype == GDN_BF16;
+  return GDN_OK;
+}
+
+Workspace plan_workspace(const Problem& p, void* base) {
+  Workspace ws;
+  char* b = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = b ? static_cast<void*>(b + off) : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  const bool chunked = use_chunked(p);
+  const size_t wt = chunked ? 2 : 4;  // bytes of the normalised q/k/v work arrays
+  ws.seq_chunk_off = static_cast<int32_t*>(take(sizeof(int32_t) * size_t(p.n_seqs + 1)));
+  ws.chunk_tab = static_cast<int4*>(take(sizeof(int4) * size_t(chunked ? p.nc_max : 0)));
+  ws.qhat = take(wt * size_t(p.T) * p.hk * p.dk);
+  ws.khat = take(wt * size_t(p.T) * p.hk * p.dk);
+  ws.vhat = take(wt * size_t(p.T) * p.hv * p.dv);
+  if (chunked) {
+    const size_t nc = size_t(p.nc_max);
+    ws.G = static_cast<float*>(take(sizeof(float) * nc * p.hv * 64));
+    ws.Wk = static_cast<uint16_t*>(take(2 * nc * p.hv * 64 * 128));
+    ws.U = static_cast<uint16_t*>(take(2 * nc * p.hv * 64 * 128));
+    ws.KT = static_cast<uint16_t*>(take(2 * nc * p.hk * 128 * 64));
+    ws.ST = static_cast<uint16_t*>(take(2 * nc * p.hv * 128 * 128));
+    ws.WT = static_cast<uint16_t*>(take(2 * nc * p.hv * 128 * 64));
+  }
+  ws.bytes = off;
+  return ws;
+}
+
+static hipError_t run(hipError_t e, const char* what) {
+  if (e != hipSuccess) fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return e;
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+void gdn_cfg_default(gdn_cfg* cfg) {
+  if (!cfg) return;
+  cfg->n_qk_heads = 16;
+  cfg->n_v_heads = 48;
+  cfg->d_k = 128;
+  cfg->d_v = 128;
+  cfg->conv_width = 4;
+  cfg->io_dtype = GDN_BF16;
+  cfg->flags = GDN_ALL;
+  cfg->scale = 1.0f;
+  cfg->l2_eps = 1e-6f;
+  cfg->norm_eps = 1e-6f;
+  cfg->norm_head_stride = 0;
+}
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status gdn_set_stage_events(void* const* events, int32_t n_events) {
+  g_last_error[0] = 0;
+  if (events && n_events != GDN_N_STAGES + 1)
+    return fail(GDN_E_SHAPE, "need %d events, got %d", GDN_N_STAGES + 1, n_events);
+  g_stage_events = events;
+  return GDN_OK;
+}
+
+const char* gdn_last_error(void) { return g_last_error; }
+
+const char* gdn_status_string(gdn_status st) {
+  switch (st) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_E_NULL: return "GDN_E_NULL: a required pointer is NULL";
+    case GDN_E_SHAPE: return "GDN_E_SHAPE: inconsistent shapes or sequence lengths";
+    case GDN_E_DTYPE: return "GDN_E_DTYPE: unknown io dtype";
+    case GDN_E_ALIGN: return "GDN_E_ALIGN: pointer or stride not 16-byte aligned";
+    case GDN_E_WORKSPACE: return "GDN_E_WORKSPACE: workspace missing or too small";
+    case GDN_E_UNSUPPORTED: return "GDN_E_UNSUPPORTED: configuration not implemented";
+    case GDN_E_HIP: return "GDN_E_HIP: HIP runtime error";
+    case GDN_E_VALUE: return "GDN_E_VALUE: scalar parameter out of range";
+  }
+  return "unknown gdn_status";
+}
+
+gdn_status gdn_prefill_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, size_t* bytes) {
+  g_last_error[0] = 0;
+  if (!bytes) return fail(GDN_E_NULL, "bytes is NULL");
+  Problem p{};
+  gdn_status st = check_cfg(cfg, p);
+  if (st != GDN_OK) return st;
+  if (n_seqs < 0 || total_tokens < 0) return fail(GDN_E_SHAPE, "negative n_seqs or total_tokens");
+  if (n_seqs == 0 && total_tokens > 0) return fail(GDN_E_SHAPE, "tokens without sequences");
+  if (total_tokens > (int64_t(1) << 31) - 1) return fail(GDN_E_UNSUPPORTED, "total_tokens >= 2^31");
+  p.n_seqs = n_seqs;
+  p.T = total_tokens;
+  p.nc_max = total_tokens / kChunk + n_seqs;
+  *bytes = plan_workspace(p, nullptr).bytes;
+  return GDN_OK;
+}
+
+gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                       const void* q, const void* k, const void* v,
+                       int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                       const float* alpha, const float* beta, const void* gate,
+                       const float* conv_w, const float* norm_w,
+                       const float* state_in, float* state_out,
+                       const void* conv_in, void* conv_out,
+                       void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_cfg(cfg, p);
+  if (st != GDN_OK) return st;
+  if (n_seqs < 0 || total_tokens < 0) return fail(GDN_E_SHAPE, "negative n_seqs (%d) or total_tokens (%lld)", n_seqs, (long long)total_tokens);
+  if (n_seqs == 0 && total_tokens > 0) return fail(GDN_E_SHAPE, "tokens without sequences");
+  if (total_tokens > (int64_t(1) << 31) - 1) return fail(GDN_E_UNSUPPORTED, "total_tokens >= 2^31");
+  p.n_seqs = n_seqs;
+  p.T = total_tokens;
+  p.nc_max = total_tokens / kChunk + n_seqs;
+  const uint32_t f = p.flags;
+  // required pointers
+  if (n_seqs > 0 && !cu_seqlens) return fail(GDN_E_NULL, "cu_seqlens is NULL");
+  if (total_tokens > 0) {
+    if (!q || !k || !v) return fail(GDN_E_NULL, "q, k and v are required");
+    if (!alpha || !beta) return fail(GDN_E_NULL, "alpha and beta are required");
+    if (!out) return fail(GDN_E_NULL, "out is required");
+    if ((f & GDN_GATE) && !gate) return fail(GDN_E_NULL, "gate is required with GDN_GATE");
+    if ((f & GDN_NORM) && !norm_w) return fail(GDN_E_NULL, "norm_w is required with GDN_NORM");
+  }
+  if ((f & GDN_CONV) && !conv_w && (total_tokens > 0)) return fail(GDN_E_NULL, "conv_w is required with GDN_CONV");
+  // strides and alignment
+  const int64_t elem = p.bf16 ? 2 : 4;
+  const int64_t qrow = int64_t(p.hk) * p.dk, vrow = int64_t(p.hv) * p.dv;
+  if (ld_q < qrow || ld_k < qrow || ld_v < vrow)
+    return fail(GDN_E_SHAPE, "row strides too small (ld_q=%lld, ld_k=%lld >= %lld; ld_v=%lld >= %lld)",
+                (long long)ld_q, (long long)ld_k, (long long)qrow, (long long)ld_v, (long long)vrow);
+  if ((ld_q * elem) % 16 || (ld_k * elem) % 16 || (ld_v * elem) % 16)
+    return fail(GDN_E_ALIGN, "row strides must be multiples of 16 bytes");
+  const void* ptrs[] = {q, k, v, gate, conv_w, norm_w, state_in, state_out, conv_in, conv_out, out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (!aligned4(alpha) || !aligned4(beta) || !aligned4(cu_seqlens))
+    return fail(GDN_E_ALIGN, "alpha, beta and cu_seqlens must be 4-byte aligned");
+  if (conv_in && conv_out && conv_in != conv_out) {
+    // partial overlap is not allowed; exact aliasing is
+    const char* a0 = static_cast<const char*>(conv_in);
+    const char* b0 = static_cast<const char*>(conv_out);
+    const size_t nb = size_t(n_seqs) * 3 * size_t(p.C) * size_t(elem);
+    if (a0 < b0 + nb && b0 < a0 + nb) return fail(GDN_E_VALUE, "conv_in and conv_out overlap without being equal");
+  }
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0) return fail(GDN_E_SHAPE, "cu_seqlens[0] = %d, expected 0", cu_seqlens_host[0]);
+    for (int i = 0; i < n_seqs; ++i)
+      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return fail(GDN_E_SHAPE, "cu_seqlens decreases at %d", i);
+    if (int64_t(cu_seqlens_host[n_seqs]) != total_tokens)
+      return fail(GDN_E_SHAPE, "cu_seqlens[%d] = %d, expected total_tokens = %lld", n_seqs, cu_seqlens_host[n_seqs], (long long)total_tokens);
+  }
+  const Workspace need = plan_workspace(p, nullptr);
+  if (!workspace && need.bytes > 0) return fail(GDN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need.bytes);
+  if (workspace_bytes < need.bytes) return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need.bytes);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
+  if (n_seqs == 0) return GDN_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const Workspace ws = plan_workspace(p, workspace);
+  const bool chunked = use_chunked(p);
+  const bool any = total_tokens > 0;
+#define GDN_STEP(i, expr, what) \
+  if (run(mark(i, s), "event record") != hipSuccess || (run((expr), what) != hipSuccess)) return GDN_E_HIP;
+  GDN_STEP(0, hipSuccess, "")  // the chunk table is built inside the conv launch
+  GDN_STEP(1, launch_conv(p, cu_seqlens, q, k, v, ld_q, ld_k, ld_v, conv_w, conv_in, ws, chunked, s), "conv")
+  if (chunked) {
+    GDN_STEP(2, any ? launch_wy(p, ws, alpha, beta, s) : hipSuccess, "wy")
+    GDN_STEP(3, launch_state(p, ws, state_in, state_out, s), "state")
+    GDN_STEP(4, any ? launch_output(p, ws, gate, norm_w, out, s) : hipSuccess, "output")
+  } else {
+    GDN_STEP(2, launch_sequential(p, cu_seqlens, ws, alpha, beta, gate, norm_w, state_in, state_out, out, s),
+             "sequential")
+    GDN_STEP(3, hipSuccess, "")
+    GDN_STEP(4, hipSuccess, "")
+  }
+  GDN_STEP(5, conv_out ? launch_conv_tail(p, cu_seqlens, q, k, v, ld_q, ld_k, ld_v, conv_in, conv_out, s) : hipSuccess,
+           "conv tail")
+  if (run(mark(GDN_N_STAGES, s), "event record") != hipSuccess) return GDN_E_HIP;
+#undef GDN_STEP
+  return GDN_OK;
+}
+
+gdn_status gdn_decode_step(const gdn_cfg* cfg, int32_t batch,
+                           const void* q, const void* k, const void* v,
+                           int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                           const float* alpha, const float* beta, const void* gate,
+                           const float* conv_w, const float* norm_w,
+                           void* conv_state, float* state, void* out, void* hip_stream) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_cfg(cfg, p);
+  if (st != GDN_OK) return st;
+  if (batch < 0) return fail(GDN_E_SHAPE, "negative batch %d", batch);
+  p.n_seqs = batch;
+  p.T = batch;
+  p.nc_max = 0;
+  const uint32_t f = p.flags;
+  if (batch > 0) {
+    if (!q || !k || !v) return fail(GDN_E_NULL, "q, k and v are required");
+    if (!alpha || !beta) return fail(GDN_E_NULL, "alpha and beta are required");
+    if (!state) return fail(GDN_E_NULL, "state is required");
+    if (!out) return fail(GDN_E_NULL, "out is required");
+    if ((f & GDN_GATE) && !gate) return fail(GDN_E_NULL, "gate is required with GDN_GATE");
+    if ((f & GDN_NORM) && !norm_w) return fail(GDN_E_NULL, "norm_w is required with GDN_NORM");
+    if ((f & GDN_CONV) && (!conv_w || !conv_state)) return fail(GDN_E_NULL, "conv_w and conv_state are required with GDN_CONV");
+  }
+  const int64_t elem = p.bf16 ? 2 : 4;
+  const int64_t qrow = int64_t(p.hk) * p.dk, vrow = int64_t(p.hv) * p.dv;
+  if (ld_q < qrow || ld_k < qrow || ld_v < vrow) return fail(GDN_E_SHAPE, "row strides too small");
+  if ((ld_q * elem) % 16 || (ld_k * elem) % 16 || (ld_v * elem) % 16)
+    return fail(GDN_E_ALIGN, "row strides must be multiples of 16 bytes");
+  const void* ptrs[] = {q, k, v, gate, conv_w, norm_w, conv_state, state, out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (!aligned4(alpha) || !aligned4(beta)) return fail(GDN_E_ALIGN, "alpha and beta must be 4-byte aligned");
+  if (p.hv / p.hk > 64) return fail(GDN_E_UNSUPPORTED, "HV/HK = %d > 64", p.hv / p.hk);
+  if (batch == 0) return GDN_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (run(launch_decode(p, batch, q, k, v, ld_q, ld_k, ld_v, alpha, beta, gate, conv_w, norm_w, conv_state,
+                        state, out, s), "decode") != hipSuccess)
+    return GDN_E_HIP;
+  return GDN_OK;
+}
+
+}  // extern "C"

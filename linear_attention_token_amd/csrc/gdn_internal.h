@@ -1,0 +1,74 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+constexpr int kChunk = 64;  // tokens per chunk of the WY form
+
+// Problem description after validation; every launcher reads it.
+struct Problem {
+  int hk, hv, dk, dv;
+  int n_seqs;
+  int64_t T;
+  int64_t C;          // conv channels: 2*hk*dk + hv*dv
+  int64_t nc_max;     // bound on the number of 64-token chunks: T/64 + n_seqs
+  uint32_t flags;
+  float scale, l2_eps, norm_eps;
+  int norm_stride;    // 0 or dv
+  bool bf16;          // io dtype
+};
+
+// Device workspace regions. Offsets are computed by plan_workspace() and are 256-byte aligned.
+struct Workspace {
+  // both paths
+  int32_t* seq_chunk_off = nullptr;  // [n_seqs + 1] first chunk of each sequence
+  int4* chunk_tab = nullptr;         // [nc_max] (start token, length, sequence, 0)
+  void* qhat = nullptr;              // [T][hk][dk]  work type
+  void* khat = nullptr;              // [T][hk][dk]
+  void* vhat = nullptr;              // [T][hv][dv]
+  // chunked bf16 path only
+  float* G = nullptr;                // fp32 [nc][hv][64]    in-chunk cumulative log decay
+  uint16_t* Wk = nullptr;            // bf16 [nc][hv][64][128]  T diag(beta*gamma) K
+  uint16_t* U = nullptr;             // bf16 [nc][hv][64][128]  T diag(beta) V
+  uint16_t* KT = nullptr;            // bf16 [nc][hk][128][64]  K^T of each chunk
+  uint16_t* ST = nullptr;            // bf16 [nc][hv][128][128] chunk-start state, transposed
+  uint16_t* WT = nullptr;            // bf16 [nc][hv][128][64]  chunk write W, transposed
+  size_t bytes = 0;
+};
+
+// True when the chunked MFMA path serves this problem.
+inline bool use_chunked(const Problem& p) { return p.bf16 && p.dk == 128 && p.dv == 128; }
+
+// Carves `base` (may be null to only size it) into the regions the chosen path needs.
+Workspace plan_workspace(const Problem& p, void* base);
+
+// ---- launchers (each returns hipGetLastError() after its launches) ----
+hipError_t launch_conv(const Problem& p, const int32_t* cu, const void* q, const void* k, const void* v,
+                       int64_t ld_q, int64_t ld_k, int64_t ld_v, const float* conv_w,
+                       const void* conv_in, const Workspace& ws, bool work_bf16, hipStream_t s);
+// (the conv launch also builds the chunk table when the chunked path runs)
+hipError_t launch_conv_tail(const Problem& p, const int32_t* cu, const void* q, const void* k,
+                            const void* v, int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                            const void* conv_in, void* conv_out, hipStream_t s);
+hipError_t launch_sequential(const Problem& p, const int32_t* cu, const Workspace& ws,
+                             const float* alpha, const float* beta, const void* gate,
+                             const float* norm_w, const float* state_in, float* state_out, void* out,
+                             hipStream_t s);
+hipError_t launch_wy(const Problem& p, const Workspace& ws, const float* alpha, const float* beta,
+                     hipStream_t s);
+hipError_t launch_state(const Problem& p, const Workspace& ws, const float* state_in, float* state_out,
+                        hipStream_t s);
+hipError_t launch_output(const Problem& p, const Workspace& ws, const void* gate, const float* norm_w,
+                         void* out, hipStream_t s);
+hipError_t launch_decode(const Problem& p, int batch, const void* q, const void* k, const void* v,
+                         int64_t ld_q, int64_t ld_k, int64_t ld_v, const float* alpha, const float* beta,
+                         const void* gate, const float* conv_w, const float* norm_w, void* conv_state,
+                         float* state, void* out, hipStream_t s);
+
+}  // namespace gdn

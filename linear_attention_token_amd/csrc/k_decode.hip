@@ -1,0 +1,192 @@
+// Decode step: one new token for each of B sequences, conv cache and fp32 state updated in place.
+//
+// The mixer with a sequence length of one (analysis notes "Qwen3.8-Flash-Next：架构、效率与技术谱系"
+// §02 GDN row and §03 update equations; paper reading §四 4.1; paper summary, Method):
+//   conv with the cached 3 inputs + SiLU, L2(q, k), then per value head, in one pass over S:
+//   a = S^T k, b = S^T q, e = v - alpha a, y = alpha b + beta (q.k) e, S <- alpha S + beta k e^T,
+//   then RMSNorm and the sigmoid gate.
+//
+// One block per (sequence, QK group). The block owns every conv channel of its group (q and k of
+// the QK head, v of its HV/HK value heads), so the in-place cache update has a single writer and
+// the value heads that share q/k read them from LDS. Each value head is handled by a team of 256
+// threads that streams the 128x128 fp32 state from HBM once with 16-byte loads, all of a thread's
+// loads in flight at once, and writes it back once. The kernel is bound by HBM bandwidth.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+constexpr int kTeam = 256;
+constexpr int kDecMaxRows = 16;
+
+struct DecodeArgs {
+  int B, hk, hv, dk, dv, R, teams;
+  int64_t C;
+  const void *q, *k, *v;
+  int64_t ld_q, ld_k, ld_v;
+  const float *alpha, *beta;
+  const void* gate;
+  const float *conv_w, *norm_w;
+  int norm_stride;
+  void* conv_state;
+  float* state;
+  void* out;
+  uint32_t flags;
+  float scale, l2_eps, norm_eps;
+};
+
+template <typename IO>
+__global__ void __launch_bounds__(768) k_decode(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  const int nch = 2 * a.dk + a.R * a.dv;
+  float* act = smem;                  // [nch]: q | k | v of the group's heads, after conv + SiLU
+  float* red = smem + ((nch + 3) & ~3);  // per team: red_a[256*4], red_b[256*4]
+  __shared__ float scal[4];           // 1/|q|, 1/|k|, q.k (normalised)
+
+  // ---- conv + SiLU for the group's channels; single-writer cache shift ----
+  const int64_t qk_ch = int64_t(a.hk) * a.dk;
+  for (int c = tid; c < nch; c += nthreads) {
+    int64_t gc;          // global channel index
+    const IO* src;
+    if (c < a.dk) { gc = int64_t(g) * a.dk + c; src = static_cast<const IO*>(a.q) + int64_t(b) * a.ld_q + (gc); }
+    else if (c < 2 * a.dk) { gc = qk_ch + int64_t(g) * a.dk + (c - a.dk); src = static_cast<const IO*>(a.k) + int64_t(b) * a.ld_k + (gc - qk_ch); }
+    else { gc = 2 * qk_ch + int64_t(g) * a.R * a.dv + (c - 2 * a.dk); src = static_cast<const IO*>(a.v) + int64_t(b) * a.ld_v + (gc - 2 * qk_ch); }
+    const float x = io<IO>::ld(src);
+    float u = x;
+    if (a.flags & GDN_CONV) {
+      IO* cs = static_cast<IO*>(a.conv_state) + int64_t(b) * 3 * a.C + gc;
+      const float h0 = io<IO>::ld(cs), h1 = io<IO>::ld(cs + a.C), h2 = io<IO>::ld(cs + 2 * a.C);
+      const float4 w = reinterpret_cast<const float4*>(a.conv_w)[gc];
+      u = w.x * h0 + w.y * h1 + w.z * h2 + w.w * x;
+      u = siluf_(u);
+      io<IO>::st(cs, h1);
+      io<IO>::st(cs + a.C, h2);
+      io<IO>::st(cs + 2 * a.C, x);
+    }
+    act[c] = u;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float sq = 0.f, sk = 0.f;
+    for (int i = tid; i < a.dk; i += 64) { sq += act[i] * act[i]; sk += act[a.dk + i] * act[a.dk + i]; }
+    sq = group_sum<64>(sq);
+    sk = group_sum<64>(sk);
+    const bool l2 = (a.flags & GDN_L2QK) != 0;
+    const float rq = l2 ? 1.0f / sqrtf(sq + a.l2_eps) : 1.0f;
+    const float rk = l2 ? 1.0f / sqrtf(sk + a.l2_eps) : 1.0f;
+    float d = 0.f;
+    for (int i = tid; i < a.dk; i += 64) d += act[i] * act[a.dk + i];
+    d = group_sum<64>(d);
+    if (tid == 0) { scal[0] = rq; scal[1] = rk; scal[2] = d * rq * rk; }
+  }
+  __syncthreads();
+  const float rq = scal[0], rk = scal[1], qk = scal[2];
+
+  // ---- state update, one team per value head ----
+  const int team = tid / kTeam, lt = tid % kTeam;
+  const int ncg = a.dv / 4, nrg = kTeam / ncg;
+  const int cg = lt % ncg, rg = lt / ncg, col = 4 * cg;
+  float* red_a = red + team * (2 * kTeam * 4);
+  float* red_b = red_a + kTeam * 4;
+  const int iters = (a.R + a.teams - 1) / a.teams;
+  for (int it = 0; it < iters; ++it) {
+    const int r = team + it * a.teams;
+    const bool live = r < a.R;
+    const int h = g * a.R + (live ? r : 0);
+    float* Sp = a.state + (size_t(b) * a.hv + h) * size_t(a.dk) * a.dv;
+    float S[kDecMaxRows][4];
+#pragma unroll
+    for (int j = 0; j < kDecMaxRows; ++j) {
+      const int i = rg + j * nrg;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (live && i < a.dk) v = *reinterpret_cast<const float4*>(Sp + size_t(i) * a.dv + col);
+      S[j][0] = v.x; S[j][1] = v.y; S[j][2] = v.z; S[j][3] = v.w;
+    }
+    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kDecMaxRows; ++j) {
+      const int i = rg + j * nrg;
+      if (i < a.dk) {
+        const float qi = act[i] * rq, ki = act[a.dk + i] * rk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { pa[e] += S[j][e] * ki; pb[e] += S[j][e] * qi; }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { red_a[rg * a.dv + col + e] = pa[e]; red_b[rg * a.dv + col + e] = pb[e]; }
+    __syncthreads();
+    float av[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
+    const int nr = min(nrg, a.dk);
+    for (int rr = 0; rr < nr; ++rr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { av[e] += red_a[rr * a.dv + col + e]; bv[e] += red_b[rr * a.dv + col + e]; }
+    }
+    const float al = live ? a.alpha[size_t(b) * a.hv + h] : 0.f;
+    const float be = live ? a.beta[size_t(b) * a.hv + h] : 0.f;
+    float ev[4], y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float vv = act[2 * a.dk + (live ? r : 0) * a.dv + col + e];
+      ev[e] = vv - al * av[e];
+      y[e] = a.scale * (al * bv[e] + be * qk * ev[e]);
+    }
+    if (live) {
+#pragma unroll
+      for (int j = 0; j < kDecMaxRows; ++j) {
+        const int i = rg + j * nrg;
+        if (i < a.dk) {
+          const float bk = be * act[a.dk + i] * rk;
+          float4 o;
+          o.x = al * S[j][0] + bk * ev[0];
+          o.y = al * S[j][1] + bk * ev[1];
+          o.z = al * S[j][2] + bk * ev[2];
+          o.w = al * S[j][3] + bk * ev[3];
+          *reinterpret_cast<float4*>(Sp + size_t(i) * a.dv + col) = o;
+        }
+      }
+    }
+    float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+    for (int o = ncg >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (live && rg == 0) {
+      const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(ss / float(a.dv) + a.norm_eps) : 1.0f;
+      const IO* gp = static_cast<const IO*>(a.gate) + (size_t(b) * a.hv + h) * a.dv + col;
+      IO* op = static_cast<IO*>(a.out) + (size_t(b) * a.hv + h) * a.dv + col;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float o = y[e];
+        if (a.flags & GDN_NORM) o = o * rs * (1.0f + a.norm_w[size_t(h) * a.norm_stride + col + e]);
+        if (a.flags & GDN_GATE) o *= sigmoidf_(io<IO>::ld(gp + e));
+        io<IO>::st(op + e, o);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+size_t decode_smem_bytes(const Problem& p, int teams) {
+  const int R = p.hv / p.hk;
+  const int nch = 2 * p.dk + R * p.dv;
+  return size_t((nch + 3) & ~3) * 4 + size_t(teams) * 2 * kTeam * 4 * 4;
+}
+
+hipError_t launch_decode(const Problem& p, int batch, const void* q, const void* k, const void* v,
+                         int64_t ld_q, int64_t ld_k, int64_t ld_v, const float* alpha, const float* beta,
+                         const void* gate, const float* conv_w, const float* norm_w, void* conv_state,
+                         float* state, void* out, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  const int R = p.hv / p.hk;
+  const int teams = R < 3 ? R : 3;
+  DecodeArgs a{batch, p.hk, p.hv, p.dk, p.dv, R, teams, p.C, q, k, v, ld_q, ld_k, ld_v, alpha, beta,
+               gate, conv_w, norm_w, p.norm_stride, conv_state, state, out, p.flags, p.scale,
+               p.l2_eps, p.norm_eps};
+  const size_t smem = decode_smem_bytes(p, teams);
+  dim3 grid(unsigned(batch), unsigned(p.hk));
+  if (p.bf16) hipLaunchKernelGGL(k_decode<bf16>, grid, dim3(kTeam * teams), smem, s, a);
+  else hipLaunchKernelGGL(k_decode<float>, grid, dim3(kTeam * teams), smem, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,252 @@
+// Chunk WY/UT transform of the gated delta rule, one block per (64-token chunk, value head).
+//
+// Unrolling the update equations of the analysis notes "Qwen3.8-Flash-Next：架构、效率与技术谱系"
+// (§03) over a chunk that starts from state S, with G_t = sum_{s<=t} ln alpha_s and
+// gamma_t = exp(G_t), the effective writes w_t = beta_t e_t satisfy
+//     (I + A) W = diag(beta) V - diag(beta gamma) K S,   A[t,i] = beta_t exp(G_t - G_i) k_t.k_i (i < t)
+// so with T = (I + A)^-1:  W = U - Wk S,  U = T diag(beta) V,  Wk = T diag(beta gamma) K.
+// U and Wk depend only on the chunk, so every chunk is transformed in parallel here; the state
+// pass then needs only two products per chunk.
+//
+// Steps: k^ k^T on bf16 MFMA (fp32 accumulate) -> A in fp32 -> T by blocked forward substitution
+// in fp32 (16x16 diagonal blocks inverted per column, off-diagonal blocks merged with fp32 MFMA)
+// -> T diag(beta), T diag(beta gamma) rounded to bf16 -> U, Wk on bf16 MFMA.
+// Rows past the end of a partial chunk carry beta = 0 and ln alpha = 0, so their U and Wk rows are
+// zero and G stays at the last real token.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+struct WyArgs {
+  const int4* tab;
+  int hk, hv, R;
+  const uint16_t *khat, *vhat;    // bf16 [T][hk][128], [T][hv][128]
+  const float *alpha, *beta;      // [T][hv]
+  float* G;                       // [nc][hv][64]
+  uint16_t *Wk, *U;               // [nc][hv][64][128]
+  uint16_t* KT;                   // [nc][hk][128][64]
+};
+
+constexpr int kKsLd = 144;   // bf16 row stride of the 64x128 k^ tile (and of T' / T'' later)
+constexpr int kKTLd = 72;    // bf16 row stride of the transposed 128x64 tiles
+constexpr int kFLd = 72;     // fp32 row stride of the 64x64 A and T matrices
+
+// T_ij = -D_i * sum_{k=j}^{i-1} A_ik T_kj for block row i > j (16x16 blocks), by one wave.
+__device__ __forceinline__ void wy_offdiag(const float* Am, float* Tm, float* X, int i, int j, int lane) {
+  const int li = lane & 15, lq = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kb = j; kb < i; ++kb) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float av = Am[(16 * i + li) * kFLd + 16 * kb + 4 * kk + lq];
+      const float bv = Tm[(16 * kb + 4 * kk + lq) * kFLd + 16 * j + li];
+      acc = mfma16x16x4f32(av, bv, acc);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) X[(4 * lq + r) * 16 + li] = acc[r];
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const float av = Tm[(16 * i + li) * kFLd + 16 * i + 4 * kk + lq];
+    const float bv = X[(4 * kk + lq) * 16 + li];
+    acc2 = mfma16x16x4f32(av, bv, acc2);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Tm[(16 * i + 4 * lq + r) * kFLd + 16 * j + li] = -acc2[r];
+}
+
+__global__ void __launch_bounds__(256) k_wy(WyArgs a) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int4 ct = a.tab[c];
+  const int len = ct.y;
+  if (len <= 0) return;
+  const int64_t start = ct.x;
+  const int g = h / a.R;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lq = lane >> 4;
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kKsLd];    // k^ rows; later T', T''
+  __shared__ __attribute__((aligned(16))) uint16_t KTs[128 * kKTLd];  // k^ transposed
+  __shared__ __attribute__((aligned(16))) float Am[64 * kFLd];        // A; later V^ transposed
+  __shared__ __attribute__((aligned(16))) float Tm[64 * kFLd];        // T; later staging
+  __shared__ float Xs[4][256];
+  __shared__ float Gs[64], Bs[64];
+
+  // ---- load k^ (row-major and transposed), alpha/beta -> G ----
+  const int64_t krow = int64_t(a.hk) * 128;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + it * 256;  // 64 rows x 16 segments
+    const int t = idx >> 4, sg = idx & 15;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < len) v = *reinterpret_cast<const uint4*>(a.khat + (start + t) * krow + g * 128 + sg * 8);
+    *reinterpret_cast<uint4*>(&Ks[t * kKsLd + sg * 8]) = v;
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      KTs[(sg * 8 + 2 * e) * kKTLd + t] = uint16_t(wv[e] & 0xffffu);
+      KTs[(sg * 8 + 2 * e + 1) * kKTLd + t] = uint16_t(wv[e] >> 16);
+    }
+  }
+  if (w == 0) {
+    float la = 0.f, be = 0.f;
+    if (lane < len) {
+      la = logf(a.alpha[(start + lane) * a.hv + h]);
+      be = a.beta[(start + lane) * a.hv + h];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(la, o, 64);
+      if (lane >= o) la += y;
+    }
+    Gs[lane] = la;
+    Bs[lane] = be;
+    a.G[(int64_t(c) * a.hv + h) * 64 + lane] = la;
+  }
+  __syncthreads();
+
+  // K^T of the chunk for the state pass, written once per QK head
+  if (h % a.R == 0) {
+    uint16_t* dst = a.KT + (int64_t(c) * a.hk + g) * 128 * 64;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = tid + it * 256;  // 128 rows x 8 segments
+      const int r = idx >> 3, sg = idx & 7;
+      *reinterpret_cast<uint4*>(dst + r * 64 + sg * 8) = *reinterpret_cast<const uint4*>(&KTs[r * kKTLd + sg * 8]);
+    }
+  }
+
+  // ---- Gram k^ k^T (lower block triangle) on MFMA -> A[t,i] = beta_t exp(G_t - G_i) k_t.k_i, i < t
+  for (int nt = 0; nt < 4; ++nt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (nt <= w) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const short8 av = ld_short8(&Ks[(16 * w + li) * kKsLd + 32 * s + 8 * lq]);
+        const short8 bv = ld_short8(&Ks[(16 * nt + li) * kKsLd + 32 * s + 8 * lq]);
+        acc = mfma16x16x32(av, bv, acc);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * w + 4 * lq + r, i = 16 * nt + li;
+      Am[t * kFLd + i] = (i < t) ? Bs[t] * __expf(Gs[t] - Gs[i]) * acc[r] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- diagonal 16x16 blocks: D_w = (I + A_ww)^-1 by forward substitution, lane = column ----
+  {
+    const int b0 = 16 * w;
+    if (lane < 16) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < r; ++s) v -= Am[(b0 + r) * kFLd + b0 + s] * x[s];
+        x[r] = v;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * kFLd + b0 + lane] = x[r];
+    }
+    // zero the blocks above the diagonal in this block row
+    for (int idx = lane; idx < 16 * 64; idx += 64) {
+      const int r = idx >> 6, col = idx & 63;
+      if (col >= b0 + 16) Tm[(b0 + r) * kFLd + col] = 0.f;
+    }
+  }
+  __syncthreads();
+  // ---- off-diagonal blocks, level by level ----
+  if (w < 3) wy_offdiag(Am, Tm, Xs[w], w + 1, w, lane);         // T10, T21, T32
+  __syncthreads();
+  if (w < 2) wy_offdiag(Am, Tm, Xs[w], w + 2, w, lane);         // T20, T31
+  __syncthreads();
+  if (w == 0) wy_offdiag(Am, Tm, Xs[w], 3, 0, lane);            // T30
+  __syncthreads();
+
+  // ---- T' = T diag(beta), T'' = T diag(beta gamma) in bf16 (reuse Ks); V^ transposed into Am ----
+  uint16_t* T1 = Ks;                 // [64][72]
+  uint16_t* T2 = Ks + 64 * kKTLd;    // [64][72]
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int t = idx >> 6, i = idx & 63;
+    const float tv = Tm[t * kFLd + i];
+    const float b = Bs[i];
+    T1[t * kKTLd + i] = f2bf(tv * b);
+    T2[t * kKTLd + i] = f2bf(tv * b * __expf(Gs[i]));
+  }
+  uint16_t* VTs = reinterpret_cast<uint16_t*>(Am);  // [128][72]
+  const int64_t vrow = int64_t(a.hv) * 128;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + it * 256;
+    const int t = idx >> 4, sg = idx & 15;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < len) v = *reinterpret_cast<const uint4*>(a.vhat + (start + t) * vrow + h * 128 + sg * 8);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      VTs[(sg * 8 + 2 * e) * kKTLd + t] = uint16_t(wv[e] & 0xffffu);
+      VTs[(sg * 8 + 2 * e + 1) * kKTLd + t] = uint16_t(wv[e] >> 16);
+    }
+  }
+  __syncthreads();
+
+  // ---- U = T' V^, Wk = T'' K^  (rows 16w.., all 128 columns) ----
+  f32x4 accU[8], accW[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    accU[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accW[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const short8 a1 = ld_short8(&T1[(16 * w + li) * kKTLd + 32 * s + 8 * lq]);
+    const short8 a2 = ld_short8(&T2[(16 * w + li) * kKTLd + 32 * s + 8 * lq]);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const short8 bv = ld_short8(&VTs[(16 * nt + li) * kKTLd + 32 * s + 8 * lq]);
+      const short8 bk = ld_short8(&KTs[(16 * nt + li) * kKTLd + 32 * s + 8 * lq]);
+      accU[nt] = mfma16x16x32(a1, bv, accU[nt]);
+      accW[nt] = mfma16x16x32(a2, bk, accW[nt]);
+    }
+  }
+  __syncthreads();  // every wave is done reading T', T'', V^T: reuse Tm / Am as output staging
+  uint16_t* Us = reinterpret_cast<uint16_t*>(Tm);  // [64][136]
+  uint16_t* Ws = reinterpret_cast<uint16_t*>(Am);  // [64][136]
+  constexpr int kOLd = 136;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * w + 4 * lq + r, col = 16 * nt + li;
+      Us[t * kOLd + col] = f2bf(accU[nt][r]);
+      Ws[t * kOLd + col] = f2bf(accW[nt][r]);
+    }
+  }
+  __syncthreads();
+  uint16_t* Ug = a.U + (int64_t(c) * a.hv + h) * 64 * 128;
+  uint16_t* Wg = a.Wk + (int64_t(c) * a.hv + h) * 64 * 128;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + it * 256;
+    const int t = idx >> 4, sg = idx & 15;
+    *reinterpret_cast<uint4*>(Ug + t * 128 + sg * 8) = *reinterpret_cast<const uint4*>(&Us[t * kOLd + sg * 8]);
+    *reinterpret_cast<uint4*>(Wg + t * 128 + sg * 8) = *reinterpret_cast<const uint4*>(&Ws[t * kOLd + sg * 8]);
+  }
+}
+
+hipError_t launch_wy(const Problem& p, const Workspace& ws, const float* alpha, const float* beta,
+                     hipStream_t s) {
+  if (p.nc_max == 0) return hipSuccess;
+  WyArgs a{ws.chunk_tab, p.hk, p.hv, p.hv / p.hk, static_cast<const uint16_t*>(ws.khat),
+           static_cast<const uint16_t*>(ws.vhat), alpha, beta, ws.G, ws.Wk, ws.U, ws.KT};
+  hipLaunchKernelGGL(k_wy, dim3(unsigned(p.nc_max), unsigned(p.hv)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,238 @@
+"""Thin ctypes binding of libgdn.so (include/gdn.h), same entry-point names.
+
+Argument marshalling only: tensors become device pointers and strides, the current torch stream
+becomes the hipStream_t, outputs and the prefill workspace are allocated with torch. Every step of
+the mixer runs in the library's HIP kernels. There is no fallback: without the built library or a
+GPU these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+GDN_BF16, GDN_F32 = 0, 1
+GDN_CONV, GDN_L2QK, GDN_NORM, GDN_GATE, GDN_ALL = 1, 2, 4, 8, 15
+STATUS = {0: "GDN_OK", 1: "GDN_E_NULL", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE", 4: "GDN_E_ALIGN",
+          5: "GDN_E_WORKSPACE", 6: "GDN_E_UNSUPPORTED", 7: "GDN_E_HIP", 8: "GDN_E_VALUE"}
+EXPORTS = ("gdn_cfg_default", "gdn_prefill_workspace", "gdn_prefill", "gdn_decode_step",
+           "gdn_set_stage_events", "gdn_status_string", "gdn_last_error", "gdn_abi_version")
+N_STAGES = 6
+STAGE_NAMES = ("chunk_table", "conv_silu_l2", "wy_or_sequential", "state", "output_norm_gate", "conv_tail")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class gdn_cfg(ctypes.Structure):
+    _fields_ = [("n_qk_heads", ctypes.c_int32), ("n_v_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("conv_width", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32), ("scale", ctypes.c_float),
+                ("l2_eps", ctypes.c_float), ("norm_eps", ctypes.c_float),
+                ("norm_head_stride", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libgdn.so once and declares the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.gdn_cfg_default.argtypes = [ctypes.POINTER(gdn_cfg)]
+    lib.gdn_cfg_default.restype = None
+    lib.gdn_prefill_workspace.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, _I64,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_prefill_workspace.restype = ctypes.c_int
+    lib.gdn_prefill.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, _I64, _P, _P, _P, _P, _P,
+                                _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                ctypes.c_size_t, _P]
+    lib.gdn_prefill.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, _P, _P, _P, _I64, _I64,
+                                    _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+    lib.gdn_set_stage_events.restype = ctypes.c_int
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GdnError(status, load_library().gdn_last_error().decode())
+
+
+def gdn_cfg_default(**overrides) -> gdn_cfg:
+    """The library's default configuration (model shape, bf16, all stages), then ``overrides``."""
+    cfg = gdn_cfg()
+    load_library().gdn_cfg_default(ctypes.byref(cfg))
+    for k, v in overrides.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+def gdn_abi_version() -> int:
+    return load_library().gdn_abi_version()
+
+
+def gdn_set_stage_events(events) -> None:
+    """Records raw hipEvent_t handles around each prefill stage (None switches it off).
+
+    ``events`` is a ctypes array of N_STAGES + 1 handles that the caller keeps alive."""
+    lib = load_library()
+    if events is None:
+        _check(lib.gdn_set_stage_events(None, 0))
+    else:
+        _check(lib.gdn_set_stage_events(events, len(events)))
+
+
+def gdn_prefill_workspace(cfg: gdn_cfg, n_seqs: int, total_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().gdn_prefill_workspace(ctypes.byref(cfg), n_seqs, total_tokens, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("gdn tensors must be on the GPU")
+    return t.data_ptr()
+
+
+def _row_stride(t: torch.Tensor, inner: int) -> int:
+    """Token row stride of a [rows, heads, dim] view whose (heads, dim) block is contiguous."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError("q/k/v need contiguous (heads, dim) blocks per token")
+    return t.stride(0) if t.shape[0] > 0 else inner
+
+
+def _expect(t, shape, dtype, name, optional=False):
+    """Host-side check that a buffer has exactly the shape, dtype and layout the kernels index."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_common(cfg, T, io, alpha, beta, gate, conv_w, norm_w, out):
+    hv, dv = cfg.n_v_heads, cfg.d_v
+    C = 2 * cfg.n_qk_heads * cfg.d_k + hv * dv
+    _expect(alpha, (T, hv), torch.float32, "alpha")
+    _expect(beta, (T, hv), torch.float32, "beta")
+    _expect(gate, (T, hv, dv), io, "gate", optional=not (cfg.flags & GDN_GATE))
+    _expect(conv_w, (C, 4), torch.float32, "conv_w", optional=not (cfg.flags & GDN_CONV))
+    if cfg.flags & GDN_NORM:
+        shape = (dv,) if cfg.norm_head_stride == 0 else (hv, dv)
+        _expect(norm_w, shape, torch.float32, "norm_w")
+    _expect(out, (T, hv, dv), io, "out")
+    return C
+
+
+def _check_qkv(cfg, q, k, v, io):
+    T = int(q.shape[0])
+    for t, name, heads, d in ((q, "q", cfg.n_qk_heads, cfg.d_k), (k, "k", cfg.n_qk_heads, cfg.d_k),
+                              (v, "v", cfg.n_v_heads, cfg.d_v)):
+        if t.dim() != 3 or tuple(t.shape) != (T, heads, d) or t.dtype != io:
+            raise ValueError(f"{name}: expected ({T}, {heads}, {d}) {io}, got {tuple(t.shape)} {t.dtype}")
+    return T
+
+
+def _io_dtype(cfg):
+    return torch.bfloat16 if cfg.io_dtype == GDN_BF16 else torch.float32
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def gdn_prefill(cfg: gdn_cfg, cu_seqlens: torch.Tensor, q, k, v, alpha, beta, gate, conv_w, norm_w,
+                state_in=None, state_out=None, conv_in=None, conv_out=None, out=None, workspace=None,
+                cu_seqlens_host: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Packed prefill; returns ``out`` [T, HV, d_v] (allocated when not given).
+
+    Writes ``state_out`` / ``conv_out`` when given. ``workspace`` (uint8, >= gdn_prefill_workspace
+    bytes) is allocated when not given.
+    """
+    lib = load_library()
+    io = _io_dtype(cfg)
+    n_seqs = int(cu_seqlens.numel()) - 1
+    T = _check_qkv(cfg, q, k, v, io)
+    if out is None:
+        out = torch.empty((T, cfg.n_v_heads, cfg.d_v), dtype=io, device=q.device)
+    C = _check_common(cfg, T, io, alpha, beta, gate, conv_w, norm_w, out)
+    _expect(cu_seqlens, (n_seqs + 1,), torch.int32, "cu_seqlens")
+    sshape = (n_seqs, cfg.n_v_heads, cfg.d_k, cfg.d_v)
+    _expect(state_in, sshape, torch.float32, "state_in", optional=True)
+    _expect(state_out, sshape, torch.float32, "state_out", optional=True)
+    _expect(conv_in, (n_seqs, 3, C), io, "conv_in", optional=True)
+    _expect(conv_out, (n_seqs, 3, C), io, "conv_out", optional=True)
+    need = gdn_prefill_workspace(cfg, n_seqs, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace needs {need} uint8 elements")
+    host = None
+    if cu_seqlens_host is not None:
+        host = cu_seqlens_host.to(torch.int32).contiguous()
+    st = lib.gdn_prefill(ctypes.byref(cfg), n_seqs, T, _ptr(cu_seqlens),
+                         host.data_ptr() if host is not None else None,
+                         _ptr(q), _ptr(k), _ptr(v), _row_stride(q, cfg.n_qk_heads * cfg.d_k),
+                         _row_stride(k, cfg.n_qk_heads * cfg.d_k), _row_stride(v, cfg.n_v_heads * cfg.d_v),
+                         _ptr(alpha), _ptr(beta), _ptr(gate), _ptr(conv_w), _ptr(norm_w),
+                         _ptr(state_in), _ptr(state_out), _ptr(conv_in), _ptr(conv_out), _ptr(out),
+                         _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return out
+
+
+def gdn_decode_step(cfg: gdn_cfg, q, k, v, alpha, beta, gate, conv_w, norm_w, conv_state, state,
+                    out=None, stream=None) -> torch.Tensor:
+    """One decode step for B sequences; updates ``state`` and ``conv_state`` in place."""
+    lib = load_library()
+    io = _io_dtype(cfg)
+    B = _check_qkv(cfg, q, k, v, io)
+    if out is None:
+        out = torch.empty((B, cfg.n_v_heads, cfg.d_v), dtype=io, device=q.device)
+    C = _check_common(cfg, B, io, alpha, beta, gate, conv_w, norm_w, out)
+    _expect(state, (B, cfg.n_v_heads, cfg.d_k, cfg.d_v), torch.float32, "state")
+    _expect(conv_state, (B, 3, C), io, "conv_state", optional=not (cfg.flags & GDN_CONV))
+    st = lib.gdn_decode_step(ctypes.byref(cfg), B, _ptr(q), _ptr(k), _ptr(v),
+                             _row_stride(q, cfg.n_qk_heads * cfg.d_k), _row_stride(k, cfg.n_qk_heads * cfg.d_k),
+                             _row_stride(v, cfg.n_v_heads * cfg.d_v), _ptr(alpha), _ptr(beta), _ptr(gate),
+                             _ptr(conv_w), _ptr(norm_w), _ptr(conv_state), _ptr(state), _ptr(out),
+                             _stream(stream))
+    _check(st)
+    return out
+
+
+def cfg_for(n_qk_heads: int, n_v_heads: int, d_k: int, d_v: int, dtype: torch.dtype,
+            flags: int = GDN_ALL, **kw) -> gdn_cfg:
+    """Configuration for a shape and io dtype."""
+    io = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return gdn_cfg_default(n_qk_heads=n_qk_heads, n_v_heads=n_v_heads, d_k=d_k, d_v=d_v, io_dtype=io,
+                           flags=flags, **kw)

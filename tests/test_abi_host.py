@@ -1,0 +1,140 @@
+"""Host-only tests of the C ABI: the library loads without a GPU, exports every function the header
+declares, sizes workspaces, and rejects bad arguments before any HIP call (so these run on CPU).
+Every gdn_prefill / gdn_decode_step call here is invalid on purpose and must return early."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+gdn = pytest.importorskip("linear_attention_token_amd.gdn")
+
+if not os.path.exists(gdn.LIB_PATH):
+    pytest.skip("libgdn.so not built (run __graft_entry__.build())", allow_module_level=True)
+
+lib = gdn.load_library()
+A = 0x100000           # a fake, 16-byte aligned "device" address; never dereferenced
+T_, N_ = 128, 1
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_function():
+    funcs = header_functions()
+    assert set(funcs) == set(gdn.EXPORTS)
+    for f in funcs:
+        assert hasattr(lib, f), f"libgdn.so does not export {f}"
+
+
+def test_abi_version_and_defaults():
+    assert lib.gdn_abi_version() == 1
+    c = gdn.gdn_cfg_default()
+    assert (c.n_qk_heads, c.n_v_heads, c.d_k, c.d_v, c.conv_width) == (16, 48, 128, 128, 4)
+    assert c.io_dtype == gdn.GDN_BF16 and c.flags == gdn.GDN_ALL and c.norm_head_stride == 0
+    assert abs(c.scale - 1.0) < 1e-9 and abs(c.l2_eps - 1e-6) < 1e-12 and abs(c.norm_eps - 1e-6) < 1e-12
+    for s in range(9):
+        assert lib.gdn_status_string(s).decode().startswith(gdn.STATUS[s])
+
+
+def test_workspace_sizes():
+    c = gdn.gdn_cfg_default()
+    small = gdn.gdn_prefill_workspace(c, 1, 4096)
+    big = gdn.gdn_prefill_workspace(c, 1, 8192)
+    assert 0 < small < big
+    # chunk bound floor(T/64) + N: the chunked path holds at least U, Wk, chunk states and W
+    nc = 4096 // 64 + 1
+    assert small >= nc * 48 * (2 * 64 * 128 * 2 + 128 * 128 * 2 + 128 * 64 * 2)
+    # more sequences for the same tokens can only need more chunks
+    assert gdn.gdn_prefill_workspace(c, 32, 4096) >= small
+    f = gdn.gdn_cfg_default(io_dtype=gdn.GDN_F32, n_qk_heads=1, n_v_heads=1, d_k=16, d_v=16)
+    assert gdn.gdn_prefill_workspace(f, 1, 64) >= 3 * 64 * 16 * 4
+    assert gdn.gdn_prefill_workspace(c, 0, 0) >= 0
+
+
+def _prefill(cfg, n_seqs=N_, T=T_, cu=A, cu_host=None, q=A, k=A, v=A, ld_q=2048, ld_k=2048, ld_v=6144,
+             alpha=A, beta=A, gate=A, conv_w=A, norm_w=A, state_in=None, state_out=None, conv_in=None,
+             conv_out=None, out=A, ws=A, ws_bytes=1 << 40):
+    ch = None
+    if cu_host is not None:
+        ch = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    return lib.gdn_prefill(ctypes.byref(cfg), n_seqs, T, cu, ch, q, k, v, ld_q, ld_k, ld_v, alpha, beta,
+                           gate, conv_w, norm_w, state_in, state_out, conv_in, conv_out, out, ws, ws_bytes,
+                           None)
+
+
+def _err(st, code):
+    assert st == code, (gdn.STATUS.get(st), lib.gdn_last_error().decode())
+    assert len(lib.gdn_last_error()) > 0
+
+
+def test_prefill_rejects_bad_config():
+    _err(lib.gdn_prefill(None, 1, 128, A, None, A, A, A, 2048, 2048, 6144, A, A, A, A, A, None, None,
+                         None, None, A, A, 1 << 40, None), 1)
+    _err(_prefill(gdn.gdn_cfg_default(n_v_heads=47)), 2)              # HV % HK != 0
+    _err(_prefill(gdn.gdn_cfg_default(d_k=48)), 6)                    # unsupported dim
+    _err(_prefill(gdn.gdn_cfg_default(d_v=256)), 6)
+    _err(_prefill(gdn.gdn_cfg_default(conv_width=3)), 6)
+    _err(_prefill(gdn.gdn_cfg_default(io_dtype=7)), 3)
+    _err(_prefill(gdn.gdn_cfg_default(flags=16)), 8)
+    _err(_prefill(gdn.gdn_cfg_default(l2_eps=-1.0)), 8)
+    _err(_prefill(gdn.gdn_cfg_default(norm_eps=float("nan"))), 8)
+    _err(_prefill(gdn.gdn_cfg_default(norm_head_stride=7)), 2)
+    _err(_prefill(gdn.gdn_cfg_default(n_qk_heads=0)), 2)
+
+
+def test_prefill_rejects_bad_arguments():
+    c = gdn.gdn_cfg_default()
+    _err(_prefill(c, n_seqs=-1), 2)
+    _err(_prefill(c, n_seqs=0, T=5), 2)
+    _err(_prefill(c, cu=None), 1)
+    _err(_prefill(c, q=None), 1)
+    _err(_prefill(c, alpha=None), 1)
+    _err(_prefill(c, out=None), 1)
+    _err(_prefill(c, gate=None), 1)                                   # GDN_GATE needs gate
+    _err(_prefill(c, norm_w=None), 1)                                 # GDN_NORM needs norm_w
+    _err(_prefill(c, conv_w=None), 1)                                 # GDN_CONV needs conv_w
+    _err(_prefill(c, ld_q=1024), 2)                                   # stride below a token row
+    _err(_prefill(c, ld_v=6148), 4)                                   # stride not 16-byte
+    _err(_prefill(c, q=A + 2), 4)                                     # misaligned pointer
+    _err(_prefill(c, state_out=A + 4), 4)
+    _err(_prefill(c, ws=None, ws_bytes=0), 5)
+    need = gdn.gdn_prefill_workspace(c, N_, T_)
+    _err(_prefill(c, ws_bytes=need - 1), 5)
+    _err(_prefill(c, ws=A + 16), 4)                                   # workspace 256-byte aligned
+    _err(_prefill(c, cu_host=[1, T_]), 2)                             # cu[0] != 0
+    _err(_prefill(c, n_seqs=2, cu_host=[0, 100, 90]), 2)              # decreasing
+    _err(_prefill(c, cu_host=[0, T_ - 1]), 2)                         # cu[N] != T
+    _err(_prefill(c, conv_in=A, conv_out=A + 256), 8)                 # partial overlap
+
+
+def test_flags_relax_required_pointers():
+    """With GATE/NORM/CONV off those tensors may be NULL; the call then fails only on what is
+    still wrong (here: a workspace that is too small), proving the NULLs were accepted."""
+    c = gdn.gdn_cfg_default(flags=gdn.GDN_L2QK)
+    _err(_prefill(c, gate=None, norm_w=None, conv_w=None, ws_bytes=16), 5)
+
+
+def _decode(cfg, B=4, q=A, k=A, v=A, alpha=A, beta=A, gate=A, conv_w=A, norm_w=A, conv_state=A,
+            state=A, out=A, ld=(2048, 2048, 6144)):
+    return lib.gdn_decode_step(ctypes.byref(cfg), B, q, k, v, ld[0], ld[1], ld[2], alpha, beta, gate,
+                               conv_w, norm_w, conv_state, state, out, None)
+
+
+def test_decode_rejects_bad_arguments():
+    c = gdn.gdn_cfg_default()
+    _err(_decode(c, B=-1), 2)
+    _err(_decode(c, state=None), 1)
+    _err(_decode(c, conv_state=None), 1)
+    _err(_decode(c, gate=None), 1)
+    _err(_decode(c, out=None), 1)
+    _err(_decode(c, state=A + 8), 4)
+    _err(_decode(c, ld=(2048, 2000, 6144)), 2)
+    _err(_decode(gdn.gdn_cfg_default(d_k=100)), 6)
+    _err(_decode(gdn.gdn_cfg_default(n_v_heads=40)), 2)

@@ -1,0 +1,269 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle, element by element.
+
+Bars: relative L2 <= 1e-4 for fp32 io and <= 1e-2 for bf16 io, on outputs and final states; the
+conv tail is a copy and must match exactly. Small cases run the whole oracle; model-shape cases at
+full size compare sampled (sequence, value head) chains, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import (prefill_inputs, decode_inputs, config_tiny, config_layer, config_long,
+                       config_varlen, loguniform_lengths)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from linear_attention_token_amd import gdn  # noqa: E402  (raises if libgdn.so is missing)
+from gdn_testutil import TOL, rel_l2, run_prefill, oracle_prefill, oracle_chain, seq_bounds  # noqa: E402
+
+gdn.load_library()
+DEV = "cuda"
+
+
+def _check_full(inp, flags=gdn.GDN_ALL, tol=None):
+    tol = tol if tol is not None else TOL[inp.io_dtype]
+    out, st, cv = run_prefill(inp, flags)
+    o_ref, s_ref, c_ref = oracle_prefill(inp.to("cpu"), flags=flags)
+    e_o, e_s = rel_l2(out, o_ref), rel_l2(st, s_ref)
+    print(f"rel_l2 out={e_o:.3e} state={e_s:.3e}", flush=True)
+    assert e_o <= tol and e_s <= tol, (e_o, e_s)
+    np.testing.assert_array_equal(cv.double().cpu().numpy(), c_ref)
+    return out, st, cv
+
+
+# ------------------------------------------------------------------ fp32 io (sequential path) ---
+
+@pytest.mark.parametrize("flags", [gdn.GDN_CONV | gdn.GDN_L2QK, gdn.GDN_ALL])
+def test_tiny_fp32(flags):
+    """T=64, one QK head and one value head, d=16, fp32; raw readout and the full layer."""
+    _check_full(config_tiny(DEV), flags)
+
+
+def test_fp32_multihead_varlen_with_history():
+    inp = prefill_inputs([37, 64, 1, 130, 2], n_qk_heads=2, n_v_heads=6, d_k=32, d_v=32,
+                         io_dtype=torch.float32, seed=3, device=DEV, s0_std=0.1, conv_in_std=1.0)
+    _check_full(inp)
+
+
+def test_fp32_model_dims_short():
+    inp = prefill_inputs([70, 9], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128,
+                         io_dtype=torch.float32, seed=4, device=DEV, s0_std=0.02)
+    _check_full(inp)
+
+
+# ------------------------------------------------------------------ bf16 io (chunked path) -------
+
+def test_bf16_chunked_ragged():
+    """Several chunks, a ragged tail, sequences shorter than the conv window and one chunk long."""
+    inp = prefill_inputs([200, 64, 3, 130, 1], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128,
+                         io_dtype=torch.bfloat16, seed=5, device=DEV, s0_std=0.01, conv_in_std=1.0)
+    _check_full(inp)
+
+
+@pytest.mark.parametrize("flags", [gdn.GDN_CONV | gdn.GDN_L2QK, gdn.GDN_L2QK | gdn.GDN_NORM | gdn.GDN_GATE])
+def test_bf16_chunked_stage_flags(flags):
+    inp = prefill_inputs([150], n_qk_heads=1, n_v_heads=3, d_k=128, d_v=128,
+                         io_dtype=torch.bfloat16, seed=6, device=DEV, s0_std=0.01)
+    _check_full(inp, flags)
+
+
+def test_bf16_other_dims_sequential():
+    """bf16 io at d=64 runs the fp32 sequential kernel."""
+    inp = prefill_inputs([100, 33], n_qk_heads=2, n_v_heads=4, d_k=64, d_v=64,
+                         io_dtype=torch.bfloat16, seed=7, device=DEV, s0_std=0.01)
+    _check_full(inp)
+
+
+def test_layer_model_shape_full():
+    """One layer at model shape (T=4096, 16/48 heads, d=128, bf16), whole output and all states."""
+    _check_full(config_layer(DEV))
+
+
+def _sampled(inp, chains, flags=gdn.GDN_ALL):
+    out, st, cv = run_prefill(inp, flags)
+    tol = TOL[inp.io_dtype]
+    for n, h in chains:
+        s0, s1 = seq_bounds(inp, n)
+        o_ref, s_ref = oracle_chain(inp, n, h, flags)
+        e_o, e_s = rel_l2(out[s0:s1, h], o_ref), rel_l2(st[n, h], s_ref)
+        print(f"seq {n} head {h} len {s1 - s0}: rel_l2 out={e_o:.3e} state={e_s:.3e}", flush=True)
+        assert e_o <= tol and e_s <= tol, (n, h, e_o, e_s)
+    return out, st, cv
+
+
+def test_varlen_model_shape_sampled():
+    """32 packed sequences, lengths log-uniform in [512, 32768], S0 ~ N(0, 0.01): sampled chains."""
+    inp = config_varlen(DEV)
+    lens = np.diff(inp.cu_seqlens.cpu().numpy())
+    order = np.argsort(lens)
+    chains = [(int(order[0]), 0), (int(order[len(order) // 2]), 25), (int(order[-1]), 47)]
+    _, st, _ = _sampled(inp, chains)
+    assert torch.isfinite(st).all()
+
+
+def test_long_prefill_sampled():
+    """T = 262144 (native context), B=1, model shape: two value heads against the oracle."""
+    inp = config_long(DEV)
+    _sampled(inp, [(0, 0), (0, 46)])
+
+
+# ------------------------------------------------------------------ invariants -------------------
+
+def test_packed_equals_separate_bitwise():
+    lengths = [130, 64, 5, 77]
+    inp = prefill_inputs(lengths, n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128,
+                         io_dtype=torch.bfloat16, seed=8, device=DEV, s0_std=0.01, conv_in_std=1.0)
+    out, st, cv = run_prefill(inp)
+    cu = inp.cu_seqlens.cpu().numpy()
+    for n, L in enumerate(lengths):
+        s0, s1 = cu[n], cu[n + 1]
+        one = prefill_inputs([L], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128, io_dtype=torch.bfloat16,
+                             seed=8, device=DEV)
+        for key in ("q", "k", "v", "alpha", "beta", "gate"):
+            setattr(one, key, getattr(inp, key)[s0:s1].contiguous())
+        one.conv_w, one.norm_w = inp.conv_w, inp.norm_w
+        one.state_in = inp.state_in[n:n + 1].contiguous()
+        one.conv_in = inp.conv_in[n:n + 1].contiguous()
+        o1, s1_, c1 = run_prefill(one)
+        assert torch.equal(o1, out[s0:s1]) and torch.equal(s1_[0], st[n]) and torch.equal(c1[0], cv[n])
+
+
+def test_repeat_runs_bitwise():
+    inp = prefill_inputs([300, 45], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128,
+                         io_dtype=torch.bfloat16, seed=9, device=DEV, s0_std=0.01)
+    a = run_prefill(inp)
+    b = run_prefill(inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_alpha_one_beta_zero_keeps_state():
+    inp = prefill_inputs([150, 20], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128,
+                         io_dtype=torch.bfloat16, seed=10, device=DEV, alpha_recipe="one",
+                         beta_recipe="zero", s0_std=0.05)
+    out, st, _ = run_prefill(inp)
+    assert torch.equal(st, inp.state_in)
+    o_ref, _, _ = oracle_prefill(inp.to("cpu"))
+    assert rel_l2(out, o_ref) <= 1e-2
+
+
+@pytest.mark.parametrize("T1", [1, 64, 100])
+def test_continuation(T1):
+    """prefill(T1 + T2) == prefill(T1) -> (state, conv tail) -> prefill(T2), within tolerance."""
+    T = 230
+    inp = prefill_inputs([T], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128, io_dtype=torch.bfloat16,
+                         seed=11, device=DEV, s0_std=0.01, conv_in_std=1.0)
+    out, st, cv = run_prefill(inp)
+
+    def part(a, b, s_in, c_in):
+        p = prefill_inputs([b - a], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128, io_dtype=torch.bfloat16,
+                           seed=11, device=DEV)
+        for key in ("q", "k", "v", "alpha", "beta", "gate"):
+            setattr(p, key, getattr(inp, key)[a:b].contiguous())
+        p.conv_w, p.norm_w, p.state_in, p.conv_in = inp.conv_w, inp.norm_w, s_in, c_in
+        return run_prefill(p)
+
+    oa, sa, ca = part(0, T1, inp.state_in, inp.conv_in)
+    ob, sb, cb = part(T1, T, sa, ca)
+    assert torch.equal(cb, cv)
+    assert rel_l2(torch.cat([oa, ob]), out) <= 1e-2 and rel_l2(sb, st) <= 1e-2
+
+
+def test_state_in_place_alias():
+    inp = prefill_inputs([100, 70], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128, io_dtype=torch.bfloat16,
+                         seed=12, device=DEV, s0_std=0.01, conv_in_std=1.0)
+    out, st, cv = run_prefill(inp)
+    cfg = gdn.cfg_for(2, 6, 128, 128, torch.bfloat16)
+    s_io = inp.state_in.clone()
+    c_io = inp.conv_in.clone()
+    out2 = gdn.gdn_prefill(cfg, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.gate, inp.conv_w,
+                           inp.norm_w, state_in=s_io, state_out=s_io, conv_in=c_io, conv_out=c_io)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(s_io, st) and torch.equal(c_io, cv)
+
+
+# ------------------------------------------------------------------ decode -----------------------
+
+def _decode_steps(di, steps, flags=gdn.GDN_ALL):
+    cfg = gdn.cfg_for(di.n_qk_heads, di.n_v_heads, di.d_k, di.d_v, di.io_dtype, flags=flags)
+    state = di.state.clone()
+    conv = di.conv_state.clone()
+    outs = []
+    for s in range(steps):
+        outs.append(gdn.gdn_decode_step(cfg, di.q[s], di.k[s], di.v[s], di.alpha[s], di.beta[s], di.gate[s],
+                                        di.conv_w, di.norm_w, conv, state))
+    torch.cuda.synchronize()
+    return torch.stack(outs), state, conv
+
+
+def _oracle_decode_seq(di, b, steps, flags=O.FLAG_ALL, heads=None):
+    """Decode of sequence b over `steps` steps == prefill of those tokens from the cached state."""
+    inp = dict(q=di.q[:steps, b], k=di.k[:steps, b], v=di.v[:steps, b], alpha=di.alpha[:steps, b],
+               beta=di.beta[:steps, b], gate=di.gate[:steps, b], conv_w=di.conv_w, norm_w=di.norm_w,
+               cu_seqlens=np.array([0, steps]), state_in=di.state[b:b + 1], conv_in=di.conv_state[b:b + 1])
+    res = {}
+    for h in (heads if heads is not None else range(di.n_v_heads)):
+        res[h] = O.prefill_chain(inp, 0, h, flags=flags)
+    return res
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_decode_small(io):
+    di = decode_inputs(4, 5, n_qk_heads=1, n_v_heads=1, d_k=16, d_v=16, io_dtype=io, device=DEV,
+                       alpha_recipe="softplus", state_std=0.1)
+    outs, st, cv = _decode_steps(di, 5)
+    tol = TOL[io]
+    for b in range(4):
+        ref = _oracle_decode_seq(di, b, 5)
+        o_ref, s_ref = ref[0]
+        assert rel_l2(outs[:, b, 0], o_ref) <= tol and rel_l2(st[b, 0], s_ref) <= tol
+    # conv cache: the last 3 raw inputs
+    x_last = torch.cat([di.q[2:5].reshape(3, 4, -1), di.k[2:5].reshape(3, 4, -1), di.v[2:5].reshape(3, 4, -1)], -1)
+    assert torch.equal(cv, x_last.transpose(0, 1))
+
+
+def test_decode_model_shape():
+    """B=256 at model shape: all sequences for 8 steps, and 4 sequences x 48 heads over 1000 steps."""
+    di = decode_inputs(256, 1000, n_qk_heads=16, n_v_heads=48, d_k=128, d_v=128, io_dtype=torch.bfloat16,
+                       device=DEV)
+    outs8, st8, _ = _decode_steps(di, 8)
+    errs = []
+    for b in range(0, 256, 17):
+        ref = _oracle_decode_seq(di, b, 8)
+        for h, (o_ref, s_ref) in ref.items():
+            errs.append((rel_l2(outs8[:, b, h], o_ref), rel_l2(st8[b, h], s_ref)))
+    worst = np.max(np.array(errs), axis=0)
+    print(f"8 steps: worst rel_l2 out={worst[0]:.3e} state={worst[1]:.3e}", flush=True)
+    assert worst[0] <= 1e-2 and worst[1] <= 1e-2
+    outs, st, _ = _decode_steps(di, 1000)
+    for b in (0, 85, 170, 255):
+        ref = _oracle_decode_seq(di, b, 1000)
+        o_ref = np.stack([ref[h][0] for h in range(48)], axis=1)
+        s_ref = np.stack([ref[h][1] for h in range(48)], axis=0)
+        e_o, e_s = rel_l2(outs[:, b], o_ref), rel_l2(st[b], s_ref)
+        print(f"1000 steps seq {b}: rel_l2 out={e_o:.3e} state={e_s:.3e}", flush=True)
+        assert e_o <= 1e-2 and e_s <= 1e-2
+
+
+def test_decode_equals_prefill_last_token():
+    """prefill(T) and prefill(T-1) + decode_step agree on the last output and the final state."""
+    T = 97
+    inp = prefill_inputs([T], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128, io_dtype=torch.bfloat16,
+                         seed=13, device=DEV, s0_std=0.01)
+    out, st, cv = run_prefill(inp)
+    head = prefill_inputs([T - 1], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128, io_dtype=torch.bfloat16,
+                          seed=13, device=DEV)
+    for key in ("q", "k", "v", "alpha", "beta", "gate"):
+        setattr(head, key, getattr(inp, key)[:T - 1].contiguous())
+    head.conv_w, head.norm_w, head.state_in = inp.conv_w, inp.norm_w, inp.state_in
+    _, sh, ch = run_prefill(head)
+    cfg = gdn.cfg_for(2, 6, 128, 128, torch.bfloat16)
+    od = gdn.gdn_decode_step(cfg, inp.q[T - 1:], inp.k[T - 1:], inp.v[T - 1:], inp.alpha[T - 1:], inp.beta[T - 1:],
+                             inp.gate[T - 1:], inp.conv_w, inp.norm_w, ch, sh)
+    torch.cuda.synchronize()
+    assert rel_l2(od[0], out[T - 1]) <= 1e-2 and rel_l2(sh, st) <= 1e-2
+    assert torch.equal(ch, cv)
