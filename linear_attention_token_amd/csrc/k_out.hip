@@ -39,8 +39,12 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
   const int li = lane & 15, lq = lane >> 4;
   constexpr int kLd = 136;
   constexpr int kPLd = 72;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kLd];
+  constexpr int kYLd = 132;  // fp32 row stride of the staged Y tile (64 x 132 x 4 B fits Qs + Ks)
+  // one buffer for the Q and K tiles, reused afterwards for the fp32 Y tile
+  __shared__ __attribute__((aligned(16))) uint16_t QKs[2 * 64 * kLd];
+  static_assert(64 * kYLd * 4 <= 2 * 64 * kLd * 2, "Y tile must fit the Q/K buffer");
+  uint16_t* Qs = QKs;
+  uint16_t* Ks = QKs + 64 * kLd;
   __shared__ __attribute__((aligned(16))) uint16_t Ps[64 * kPLd];
   __shared__ float Gs[64];
   __shared__ float red[4][64];
@@ -55,6 +59,17 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
     for (int s = 0; s < 4; ++s) bs[nt][s] = ld_short8(st + (32 * w + 16 * nt + li) * 128 + 32 * s + 8 * lq);
 #pragma unroll
     for (int s = 0; s < 2; ++s) bw[nt][s] = ld_short8(wt + (32 * w + 16 * nt + li) * 64 + 32 * s + 8 * lq);
+  }
+  // gate tile of this chunk and head, 16 bytes per thread and piece: piece p = tid + 256 * it covers
+  // row p / 16, columns 8 * (p % 16) .. +8 (fully coalesced 256-byte rows)
+  const int64_t orow = int64_t(a.hv) * 128;
+  uint4 gv[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int pidx = tid + it * 256, t = pidx >> 4, sg = pidx & 15;
+    gv[it] = make_uint4(0, 0, 0, 0);
+    if ((a.flags & GDN_GATE) && t < len)
+      gv[it] = *reinterpret_cast<const uint4*>(a.gate + (start + t) * orow + h * 128 + sg * 8);
   }
   const int64_t krow = int64_t(a.hk) * 128;
 #pragma unroll
@@ -119,7 +134,9 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
     }
   }
 
-  // scale, RMSNorm over the 128 columns of each row, gain, sigmoid gate
+  // scale and RMSNorm row sums; Y (fp32) staged in LDS over the Q/K tiles for a coalesced epilogue
+  __syncthreads();  // every wave is done reading Qs / Ks / Ps
+  float* Ys = reinterpret_cast<float*>(QKs);  // [64][kYLd] fp32 over the Q/K buffer
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -127,35 +144,32 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
       float ss = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        acc[mt][nt][r] *= a.scale;
-        ss += acc[mt][nt][r] * acc[mt][nt][r];
+        const float y = acc[mt][nt][r] * a.scale;
+        ss += y * y;
+        Ys[(16 * mt + 4 * lq + r) * kYLd + 32 * w + 16 * nt + li] = y;
       }
       ss = group_sum<16>(ss);
       if (li == 0) red[w][16 * mt + 4 * lq + r] = ss;
     }
   }
   __syncthreads();
-  const int64_t orow = int64_t(a.hv) * 128;
-  float gain[2];
+  // epilogue: piece p = tid + 256 * it -> row p / 16, columns 8 * (p % 16) .. +8
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-    gain[nt] = (a.flags & GDN_NORM) ? 1.0f + a.norm_w[int64_t(h) * a.norm_stride + 32 * w + 16 * nt + li] : 1.0f;
+  for (int it = 0; it < 4; ++it) {
+    const int pidx = tid + it * 256, t = pidx >> 4, sg = pidx & 15;
+    if (t >= len) continue;
+    const float tot = red[0][t] + red[1][t] + red[2][t] + red[3][t];
+    const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(tot * (1.0f / 128.0f) + a.norm_eps) : 1.0f;
+    float gl[8], o[8];
+    vec16<bf16>::cvt(gv[it], gl);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * mt + 4 * lq + r;
-      if (t >= len) continue;
-      const float tot = red[0][t] + red[1][t] + red[2][t] + red[3][t];
-      const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(tot * (1.0f / 128.0f) + a.norm_eps) : 1.0f;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int64_t off = (start + t) * orow + h * 128 + 32 * w + 16 * nt + li;
-        float o = acc[mt][nt][r] * rs * gain[nt];
-        if (a.flags & GDN_GATE) o *= sigmoidf_(bf2f(a.gate[off]));
-        a.out[off] = f2bf(o);
-      }
+    for (int e = 0; e < 8; ++e) {
+      float v = Ys[t * kYLd + sg * 8 + e] * rs;
+      if (a.flags & GDN_NORM) v *= 1.0f + a.norm_w[int64_t(h) * a.norm_stride + sg * 8 + e];
+      if (a.flags & GDN_GATE) v *= sigmoidf_(gl[e]);
+      o[e] = v;
     }
+    vec16<bf16>::st(reinterpret_cast<bf16*>(a.out + (start + t) * orow + h * 128 + sg * 8), o);
   }
 }
 

@@ -7,16 +7,17 @@
 // (§03) applied to 64 tokens at once (U, Wk, G from the WY kernel). The chunk-start state and W are
 // stored (bf16) for the output kernel, which then runs chunk-parallel.
 //
-// The d_v columns of S are independent in these products, so a chain is split into 4 slices of
-// 32 columns: one block of 4 waves per (sequence, value head, slice). Wave w owns state rows
-// 32w..32w+31 (two 16-row MFMA tiles) and W rows 16w..16w+15; S and W cross waves through LDS in
-// bf16 as the B operand of the bf16 MFMAs, accumulation stays fp32.
+// The d_v columns of S are independent in these products, so a chain is split into 2 slices of
+// 64 columns: one block of 4 waves per (sequence, value head, slice). Wave w owns state rows
+// 32w..32w+31 (two 16-row MFMA tiles) and W rows 16w..16w+15 of the slice; S and W cross waves through LDS in
+// bf16 as the B operand of the bf16 MFMAs, accumulation stays fp32. Each wave streams its own
+// operands (A operands of Wk and K^T, its U tiles, G) through a private LDS ring (see below).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-constexpr int kSlice = 32;
+constexpr int kSlice = 32;  // state columns per block
 constexpr int kSlices = 128 / kSlice;
 
 struct StateArgs {
@@ -29,133 +30,202 @@ struct StateArgs {
   float* state_out;
 };
 
-struct ChunkOperands {
-  short8 wk[4];        // A operand of Wk S: Wk rows 16w + li, k = 32s + 8lq .. +8
-  short8 kt[2][2];     // A operand of K^T W~: K^T rows 32w + 16m + li, tokens 32s + 8lq .. +8
-  uint16_t u[2][4];    // U rows 16w + 4lq + r, columns 16nt + li of this slice (raw bf16)
-  float gr[4];         // G of rows 16w + 4lq + r
-  float gc;            // G of the last row (decay over the whole chunk)
-};
+// ---- explicit memory operations -------------------------------------------------------------
+// The chunk operands stream through a per-wave ring in LDS, filled by direct global->LDS loads
+// (no VGPR destinations) issued kDepth-1 steps ahead. Loads and the two per-step stores are
+// issued here and waited for with explicit vmcnt counts, so the wait for chunk c covers exactly
+// its own loads and the newer loads stay in flight.
 
-__device__ __forceinline__ void load_chunk(const StateArgs& a, int64_t c, int h, int g, int sl, int w,
-                                           int li, int lq, ChunkOperands& o) {
-  const uint16_t* wk = a.Wk + (c * a.hv + h) * 64 * 128;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+// 16 (dma16) or 4 (dma4) bytes per lane from gptr to LDS address m0 + size * lane.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0v) : "memory");
+}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// The trailing s_nop covers the gfx9 hazard of a VALU overwriting the data VGPRs of a store wider
+// than 8 bytes right after it (the compiler's hazard recognizer does not see inside inline asm).
+__device__ __forceinline__ void st16(void* gptr, const void* lds_src) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds_src);
+  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(gptr), "v"(v) : "memory");
+}
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m0v) : "memory");
+}
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int kDepth = 3;                       // ring slots: loads run kDepth - 1 steps ahead
+constexpr int kNT = kSlice / 16;                // 16-column tiles per block
+constexpr int kLoadsPerChunk = 4 + 4 + kNT / 2 + 1;  // per wave per chunk: Wk, K^T, U, G
+constexpr int kStoresPerStep = kNT + kNT / 2;   // st16 per wave per step: chunk state, W
+constexpr int kWaveSlot = 4096 + 4096 + kNT * 512 + 256;  // bytes per wave per ring slot
+constexpr int kStLd = 136;                      // bf16 row stride of S^T [cols][128 k]
+constexpr int kWtLd = 72;                       // bf16 row stride of W~^T and W^T [cols][64 tokens]
+constexpr size_t kStateSmem = size_t(kDepth) * 4 * kWaveSlot + kSlice * kStLd * 2 + 2 * kSlice * kWtLd * 2;
+
+// Wave slot layout (bytes): [0, 4096) Wk A operands [s][lane][16]; [4096, 8192) K^T A operands
+// [m*2+s][lane][16]; then U [tile][lane][4 bf16] (512 B per 16-column tile); then G[64] fp32.
+__device__ __forceinline__ void issue_chunk(const StateArgs& a, int64_t c, int h, int g, int sl, int w,
+                                            int lane, uint32_t wslot) {
+  const int li = lane & 15, lq = lane >> 4;
+  const uint16_t* wk = a.Wk + (c * a.hv + h) * 64 * 128 + (16 * w + li) * 128 + 8 * lq;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) o.wk[s] = ld_short8(wk + (16 * w + li) * 128 + 32 * s + 8 * lq);
-  const uint16_t* kt = a.KT + (c * a.hk + g) * 128 * 64;
+  for (int s = 0; s < 4; ++s) dma16(wk + 32 * s, wslot + s * 1024);
+  const uint16_t* kt = a.KT + (c * a.hk + g) * 128 * 64 + (32 * w + li) * 64 + 8 * lq;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) o.kt[m][s] = ld_short8(kt + (32 * w + 16 * m + li) * 64 + 32 * s + 8 * lq);
-  const uint16_t* u = a.U + (c * a.hv + h) * 64 * 128;
+    for (int s = 0; s < 2; ++s) dma16(kt + 16 * m * 64 + 32 * s, wslot + 4096 + (m * 2 + s) * 1024);
+  const uint16_t* u = a.U + (c * a.hv + h) * 64 * 128 + (w * 8 + kNT * sl) * 256 + lane * 8;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o.u[nt][r] = u[(16 * w + 4 * lq + r) * 128 + kSlice * sl + 16 * nt + li];
-  const float* G = a.G + (c * a.hv + h) * 64;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) o.gr[r] = G[16 * w + 4 * lq + r];
-  o.gc = G[63];
+  for (int i = 0; i < kNT / 2; ++i) dma16(u + i * 512, wslot + 8192 + i * 1024);
+  dma4(a.G + (c * a.hv + h) * 64 + lane, wslot + 8192 + kNT * 512);
 }
 
 __global__ void __launch_bounds__(256) k_state(StateArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int n = blockIdx.x, h = blockIdx.y, sl = blockIdx.z;
   const int g = h / a.R;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
-  constexpr int kStLd = 136;  // bf16 row stride of S^T [32 cols][128 k]
-  constexpr int kWtLd = 72;   // bf16 row stride of W~^T [32 cols][64 tokens]
-  __shared__ __attribute__((aligned(16))) uint16_t STs[kSlice * kStLd];
-  __shared__ __attribute__((aligned(16))) uint16_t WTs[kSlice * kWtLd];
+  uint16_t* STs = reinterpret_cast<uint16_t*>(smem + size_t(kDepth) * 4 * kWaveSlot);
+  uint16_t* WTs = STs + kSlice * kStLd;   // W~^T: B operand of K^T W~
+  uint16_t* WUs = WTs + kSlice * kWtLd;    // W^T unscaled: staged for the coalesced store
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-  // state rows 32w + 16m + 4lq + r, columns 32sl + 16nt + li
-  f32x4 S[2][2];
+  // state rows 32w + 16m + 4lq + r, columns kSlice*sl + 16nt + li
+  f32x4 S[2][kNT];
   const size_t sbase = (size_t(n) * a.hv + h) * 128 * 128;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         S[m][nt][r] = a.state_in ? a.state_in[sbase + size_t(32 * w + 16 * m + 4 * lq + r) * 128 + kSlice * sl + 16 * nt + li] : 0.f;
 
   const int64_t c0 = a.seq_off[n], c1 = a.seq_off[n + 1];
+  if (c0 < c1) {
+    const int64_t clast = c1 - 1;
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i)
+      issue_chunk(a, min(c0 + i, clast), h, g, sl, w, lane, ring + uint32_t((i * 4 + w) * kWaveSlot));
 
-  // One chunk step from the operands in `cur` (loaded one step ahead, so their latency hides
-  // behind the previous step).
-  auto chunk_step = [&](const ChunkOperands& cur, int64_t c) {
-    // S (bf16) -> LDS as S^T, and to the chunk-state output
-    uint16_t* stg = a.ST + (size_t(c) * a.hv + h) * 128 * 128;
+    for (int64_t c = c0; c < c1; ++c) {
+      const int64_t j = c - c0;
+      const int slot = int(j % kDepth);
+      // wait for this chunk's loads: newer in flight are kDepth-2 chunks of loads and the stores of
+      // min(j, kDepth-1) steps
+      constexpr int kBase = (kDepth - 2) * kLoadsPerChunk;
+      if (j >= kDepth - 1) wait_vm<kBase + (kDepth - 1) * kStoresPerStep>();
+      else if (j == 1) wait_vm<kBase + kStoresPerStep>();
+      else wait_vm<kBase>();
+      // refill the slot freed by the previous step (its LDS reads finished before its MFMAs ran)
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      issue_chunk(a, min(c + kDepth - 1, clast), h, g, sl, w, lane,
+                  ring + uint32_t((int((j + kDepth - 1) % kDepth) * 4 + w) * kWaveSlot));
+
+      const unsigned char* ws = smem + size_t(slot * 4 + w) * kWaveSlot;
+      short8 wk[4], kt[2][2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int s = 0; s < 4; ++s) wk[s] = *reinterpret_cast<const short8*>(ws + s * 1024 + lane * 16);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int col = 16 * nt + li, k0 = 32 * w + 16 * m + 4 * lq;
-        const uint32_t lo = pack_bf16x2(S[m][nt][0], S[m][nt][1]);
-        const uint32_t hi = pack_bf16x2(S[m][nt][2], S[m][nt][3]);
-        *reinterpret_cast<uint2*>(&STs[col * kStLd + k0]) = make_uint2(lo, hi);
-        *reinterpret_cast<uint2*>(stg + size_t(kSlice * sl + col) * 128 + k0) = make_uint2(lo, hi);
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) kt[m][s] = *reinterpret_cast<const short8*>(ws + 4096 + (m * 2 + s) * 1024 + lane * 16);
+      uint2 uu[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) uu[nt] = *reinterpret_cast<const uint2*>(ws + 8192 + (nt * 64 + lane) * 8);
+      const float* Gl = reinterpret_cast<const float*>(ws + 8192 + kNT * 512);
+      const float4 gr = *reinterpret_cast<const float4*>(Gl + 16 * w + 4 * lq);
+      const float gc = Gl[63];
+
+      // S (bf16) -> LDS as S^T
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const int col = 16 * nt + li, k0 = 32 * w + 16 * m + 4 * lq;
+          *reinterpret_cast<uint2*>(&STs[col * kStLd + k0]) =
+              make_uint2(pack_bf16x2(S[m][nt][0], S[m][nt][1]), pack_bf16x2(S[m][nt][2], S[m][nt][3]));
+        }
+      __syncthreads();
+      // chunk-start state to the output kernel: full 256-byte rows, 16 bytes per lane
+      {
+        uint16_t* stg = a.ST + (size_t(c) * a.hv + h) * 128 * 128 + size_t(kSlice * sl) * 128;
+#pragma unroll
+        for (int i = 0; i < kNT; ++i) {
+          const int row = (kSlice / 4) * w + 4 * i + (lane >> 4), seg = lane & 15;
+          st16(stg + row * 128 + seg * 8, &STs[row * kStLd + seg * 8]);
+        }
       }
-    __syncthreads();
 
-    // W = U - Wk S   (rows 16w + 4lq + r, columns 16nt + li)
-    f32x4 Wt[2];
+      // W = U - Wk S   (rows 16w + 4lq + r, columns 16nt + li)
+      f32x4 Wt[kNT];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < kNT; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = mfma16x16x32(cur.wk[s], ld_short8(&STs[(16 * nt + li) * kStLd + 32 * s + 8 * lq]), acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Wt[nt][r] = bf2f(cur.u[nt][r]) - acc[r];
-    }
-    // W^T to the output kernel; W~ = diag(exp(G_C - G_i)) W to LDS as the B operand of K^T W~
-    uint16_t* wtg = a.WT + (size_t(c) * a.hv + h) * 128 * 64;
-    float dec[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dec[r] = __expf(cur.gc - cur.gr[r]);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int col = 16 * nt + li, t0 = 16 * w + 4 * lq;
-      const uint32_t lo = pack_bf16x2(Wt[nt][0], Wt[nt][1]);
-      const uint32_t hi = pack_bf16x2(Wt[nt][2], Wt[nt][3]);
-      *reinterpret_cast<uint2*>(wtg + size_t(kSlice * sl + col) * 64 + t0) = make_uint2(lo, hi);
-      const uint32_t lo2 = pack_bf16x2(Wt[nt][0] * dec[0], Wt[nt][1] * dec[1]);
-      const uint32_t hi2 = pack_bf16x2(Wt[nt][2] * dec[2], Wt[nt][3] * dec[3]);
-      *reinterpret_cast<uint2*>(&WTs[col * kWtLd + t0]) = make_uint2(lo2, hi2);
-    }
-    __syncthreads();
-
-    // S <- exp(G_C) S + K^T W~
-    const float gC = __expf(cur.gc);
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4 acc = S[m][nt] * gC;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          acc = mfma16x16x32(cur.kt[m][s], ld_short8(&WTs[(16 * nt + li) * kWtLd + 32 * s + 8 * lq]), acc);
-        S[m][nt] = acc;
+        for (int s = 0; s < 4; ++s)
+          acc = mfma16x16x32(wk[s], ld_short8(&STs[(16 * nt + li) * kStLd + 32 * s + 8 * lq]), acc);
+        const uint2 u = uu[nt];
+        Wt[nt][0] = __uint_as_float(u.x << 16) - acc[0];
+        Wt[nt][1] = __uint_as_float(u.x & 0xffff0000u) - acc[1];
+        Wt[nt][2] = __uint_as_float(u.y << 16) - acc[2];
+        Wt[nt][3] = __uint_as_float(u.y & 0xffff0000u) - acc[3];
       }
-  };
+      // W^T staged for the output kernel; W~ = diag(exp(G_C - G_i)) W to LDS as the B operand of K^T W~
+      const float dec[4] = {__expf(gc - gr.x), __expf(gc - gr.y), __expf(gc - gr.z), __expf(gc - gr.w)};
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const int col = 16 * nt + li, t0 = 16 * w + 4 * lq;
+        *reinterpret_cast<uint2*>(&WUs[col * kWtLd + t0]) =
+            make_uint2(pack_bf16x2(Wt[nt][0], Wt[nt][1]), pack_bf16x2(Wt[nt][2], Wt[nt][3]));
+        *reinterpret_cast<uint2*>(&WTs[col * kWtLd + t0]) =
+            make_uint2(pack_bf16x2(Wt[nt][0] * dec[0], Wt[nt][1] * dec[1]),
+                       pack_bf16x2(Wt[nt][2] * dec[2], Wt[nt][3] * dec[3]));
+      }
+      __syncthreads();
+      // W^T to the output kernel: full 128-byte rows, 16 bytes per lane
+      {
+        uint16_t* wtg = a.WT + (size_t(c) * a.hv + h) * 128 * 64 + size_t(kSlice * sl) * 64;
+#pragma unroll
+        for (int i = 0; i < kNT / 2; ++i) {
+          const int row = (kSlice / 4) * w + 8 * i + (lane >> 3), seg = lane & 7;
+          st16(wtg + row * 64 + seg * 8, &WUs[row * kWtLd + seg * 8]);
+        }
+      }
 
-  // ping-pong operand buffers: step c uses one while the loads for step c + 1 fill the other
-  ChunkOperands bufA, bufB;
-  if (c0 < c1) load_chunk(a, c0, h, g, sl, w, li, lq, bufA);
-  for (int64_t c = c0; c < c1; c += 2) {
-    if (c + 1 < c1) load_chunk(a, c + 1, h, g, sl, w, li, lq, bufB);
-    chunk_step(bufA, c);
-    if (c + 1 >= c1) break;
-    if (c + 2 < c1) load_chunk(a, c + 2, h, g, sl, w, li, lq, bufA);
-    chunk_step(bufB, c + 1);
+      // S <- exp(G_C) S + K^T W~
+      const float gC = __expf(gc);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          f32x4 acc = S[m][nt] * gC;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            acc = mfma16x16x32(kt[m][s], ld_short8(&WTs[(16 * nt + li) * kWtLd + 32 * s + 8 * lq]), acc);
+          S[m][nt] = acc;
+        }
+    }
+    // no load may still be writing this block's LDS when it exits
+    wait_vm<0>();
   }
 
   if (a.state_out) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           a.state_out[sbase + size_t(32 * w + 16 * m + 4 * lq + r) * 128 + kSlice * sl + 16 * nt + li] = S[m][nt][r];
@@ -167,7 +237,15 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const float* stat
   if (p.n_seqs == 0) return hipSuccess;
   StateArgs a{ws.seq_chunk_off, p.hk, p.hv, p.hv / p.hk, ws.G, ws.Wk, ws.U, ws.KT, ws.ST, ws.WT,
               state_in, state_out};
-  hipLaunchKernelGGL(k_state, dim3(unsigned(p.n_seqs), unsigned(p.hv), unsigned(kSlices)), dim3(256), 0, s, a);
+  static bool attr_set = false;  // same value on every device; idempotent, so a race is harmless
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_state),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kStateSmem));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_state, dim3(unsigned(p.n_seqs), unsigned(p.hv), unsigned(kSlices)), dim3(256),
+                     kStateSmem, s, a);
   return hipGetLastError();
 }
 

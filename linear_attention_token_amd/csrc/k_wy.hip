@@ -24,7 +24,8 @@ struct WyArgs {
   const uint16_t *khat, *vhat;    // bf16 [T][hk][128], [T][hv][128]
   const float *alpha, *beta;      // [T][hv]
   float* G;                       // [nc][hv][64]
-  uint16_t *Wk, *U;               // [nc][hv][64][128]
+  uint16_t *Wk;                   // [nc][hv][64][128]
+  uint16_t *U;                    // [nc][hv][4 waves][8 tiles][64 lanes][4 rows]
   uint16_t* KT;                   // [nc][hk][128][64]
 };
 
@@ -76,12 +77,21 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
   __shared__ float Xs[4][256];
   __shared__ float Gs[64], Bs[64];
 
-  // ---- load k^ (row-major and transposed), alpha/beta -> G ----
+  // ---- load k^ (row-major and transposed) and prefetch v^; alpha/beta -> G ----
+  // piece (t = idx % 64, sg = idx / 64) of idx = tid + 256 * it: wave w handles column segments
+  // w + 4 * it of all 64 rows, so its transposed 2-byte LDS writes cover 128 contiguous bytes.
   const int64_t krow = int64_t(a.hk) * 128;
+  const int64_t vrow = int64_t(a.hv) * 128;
+  uint4 vv[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int idx = tid + it * 256;  // 64 rows x 16 segments
-    const int t = idx >> 4, sg = idx & 15;
+    const int t = lane, sg = w + 4 * it;
+    vv[it] = make_uint4(0, 0, 0, 0);
+    if (t < len) vv[it] = *reinterpret_cast<const uint4*>(a.vhat + (start + t) * vrow + h * 128 + sg * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int t = lane, sg = w + 4 * it;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (t < len) v = *reinterpret_cast<const uint4*>(a.khat + (start + t) * krow + g * 128 + sg * 8);
     *reinterpret_cast<uint4*>(&Ks[t * kKsLd + sg * 8]) = v;
@@ -180,14 +190,10 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
     T2[t * kKTLd + i] = f2bf(tv * b * __expf(Gs[i]));
   }
   uint16_t* VTs = reinterpret_cast<uint16_t*>(Am);  // [128][72]
-  const int64_t vrow = int64_t(a.hv) * 128;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int idx = tid + it * 256;
-    const int t = idx >> 4, sg = idx & 15;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < len) v = *reinterpret_cast<const uint4*>(a.vhat + (start + t) * vrow + h * 128 + sg * 8);
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    const int t = lane, sg = w + 4 * it;
+    const uint32_t wv[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       VTs[(sg * 8 + 2 * e) * kKTLd + t] = uint16_t(wv[e] & 0xffffu);
@@ -215,27 +221,30 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
       accW[nt] = mfma16x16x32(a2, bk, accW[nt]);
     }
   }
-  __syncthreads();  // every wave is done reading T', T'', V^T: reuse Tm / Am as output staging
-  uint16_t* Us = reinterpret_cast<uint16_t*>(Tm);  // [64][136]
-  uint16_t* Ws = reinterpret_cast<uint16_t*>(Am);  // [64][136]
+  // U goes out in this accumulator layout, [wave][16-col tile][lane][4 rows], which is exactly how
+  // the state kernel consumes it (8 contiguous bytes per lane).
+  uint16_t* Ug = a.U + (int64_t(c) * a.hv + h) * 64 * 128;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+    *reinterpret_cast<uint2*>(Ug + ((w * 8 + nt) * 64 + lane) * 4) =
+        make_uint2(pack_bf16x2(accU[nt][0], accU[nt][1]), pack_bf16x2(accU[nt][2], accU[nt][3]));
+  // Tm is no longer read after T' and T'' were formed: reuse it as output staging for Wk
+  uint16_t* Ws = reinterpret_cast<uint16_t*>(Tm);  // [64][136]
   constexpr int kOLd = 136;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * w + 4 * lq + r, col = 16 * nt + li;
-      Us[t * kOLd + col] = f2bf(accU[nt][r]);
       Ws[t * kOLd + col] = f2bf(accW[nt][r]);
     }
   }
   __syncthreads();
-  uint16_t* Ug = a.U + (int64_t(c) * a.hv + h) * 64 * 128;
   uint16_t* Wg = a.Wk + (int64_t(c) * a.hv + h) * 64 * 128;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int idx = tid + it * 256;
     const int t = idx >> 4, sg = idx & 15;
-    *reinterpret_cast<uint4*>(Ug + t * 128 + sg * 8) = *reinterpret_cast<const uint4*>(&Us[t * kOLd + sg * 8]);
     *reinterpret_cast<uint4*>(Wg + t * 128 + sg * 8) = *reinterpret_cast<const uint4*>(&Ws[t * kOLd + sg * 8]);
   }
 }
