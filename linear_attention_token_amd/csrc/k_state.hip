@@ -31,10 +31,10 @@ struct StateArgs {
 };
 
 // ---- explicit memory operations -------------------------------------------------------------
-// The chunk operands stream through a per-wave ring in LDS, filled by direct global->LDS loads
-// (no VGPR destinations) issued kDepth-1 steps ahead. Loads and the two per-step stores are
-// issued here and waited for with explicit vmcnt counts, so the wait for chunk c covers exactly
-// its own loads and the newer loads stay in flight.
+// The chunk operands stream through a ring in LDS (one region per compute wave), filled by direct
+// global->LDS loads (no VGPR destinations) that a fifth, producer wave issues kDepth-1 steps ahead
+// and waits for with explicit vmcnt counts; the four compute waves never stall on load issue.
+// The compute waves write the chunk state and W with coalesced stores from LDS.
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
@@ -90,135 +90,150 @@ __device__ __forceinline__ void issue_chunk(const StateArgs& a, int64_t c, int h
   dma4(a.G + (c * a.hv + h) * 64 + lane, wslot + 8192 + kNT * 512);
 }
 
-__global__ void __launch_bounds__(256) k_state(StateArgs a) {
+__global__ void __launch_bounds__(320) k_state(StateArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int n = blockIdx.x, h = blockIdx.y, sl = blockIdx.z;
   const int g = h / a.R;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;  // waves 0-3 compute, wave 4 loads
   const int li = lane & 15, lq = lane >> 4;
+  const bool producer = (w == 4);
   uint16_t* STs = reinterpret_cast<uint16_t*>(smem + size_t(kDepth) * 4 * kWaveSlot);
   uint16_t* WTs = STs + kSlice * kStLd;   // W~^T: B operand of K^T W~
   uint16_t* WUs = WTs + kSlice * kWtLd;    // W^T unscaled: staged for the coalesced store
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const int64_t c0 = a.seq_off[n], c1 = a.seq_off[n + 1];
+  const int64_t clast = c1 > c0 ? c1 - 1 : c0;
 
   // state rows 32w + 16m + 4lq + r, columns kSlice*sl + 16nt + li
   f32x4 S[2][kNT];
   const size_t sbase = (size_t(n) * a.hv + h) * 128 * 128;
+  if (!producer) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[m][nt][r] = a.state_in ? a.state_in[sbase + size_t(32 * w + 16 * m + 4 * lq + r) * 128 + kSlice * sl + 16 * nt + li] : 0.f;
-
-  const int64_t c0 = a.seq_off[n], c1 = a.seq_off[n + 1];
-  if (c0 < c1) {
-    const int64_t clast = c1 - 1;
-#pragma unroll
-    for (int i = 0; i < kDepth - 1; ++i)
-      issue_chunk(a, min(c0 + i, clast), h, g, sl, w, lane, ring + uint32_t((i * 4 + w) * kWaveSlot));
-
-    for (int64_t c = c0; c < c1; ++c) {
-      const int64_t j = c - c0;
-      const int slot = int(j % kDepth);
-      // wait for this chunk's loads: newer in flight are kDepth-2 chunks of loads and the stores of
-      // min(j, kDepth-1) steps
-      constexpr int kBase = (kDepth - 2) * kLoadsPerChunk;
-      if (j >= kDepth - 1) wait_vm<kBase + (kDepth - 1) * kStoresPerStep>();
-      else if (j == 1) wait_vm<kBase + kStoresPerStep>();
-      else wait_vm<kBase>();
-      // refill the slot freed by the previous step (its LDS reads finished before its MFMAs ran)
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      issue_chunk(a, min(c + kDepth - 1, clast), h, g, sl, w, lane,
-                  ring + uint32_t((int((j + kDepth - 1) % kDepth) * 4 + w) * kWaveSlot));
-
-      const unsigned char* ws = smem + size_t(slot * 4 + w) * kWaveSlot;
-      short8 wk[4], kt[2][2];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wk[s] = *reinterpret_cast<const short8*>(ws + s * 1024 + lane * 16);
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) kt[m][s] = *reinterpret_cast<const short8*>(ws + 4096 + (m * 2 + s) * 1024 + lane * 16);
-      uint2 uu[kNT];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) uu[nt] = *reinterpret_cast<const uint2*>(ws + 8192 + (nt * 64 + lane) * 8);
-      const float* Gl = reinterpret_cast<const float*>(ws + 8192 + kNT * 512);
-      const float4 gr = *reinterpret_cast<const float4*>(Gl + 16 * w + 4 * lq);
-      const float gc = Gl[63];
-
-      // S (bf16) -> LDS as S^T
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int col = 16 * nt + li, k0 = 32 * w + 16 * m + 4 * lq;
-          *reinterpret_cast<uint2*>(&STs[col * kStLd + k0]) =
-              make_uint2(pack_bf16x2(S[m][nt][0], S[m][nt][1]), pack_bf16x2(S[m][nt][2], S[m][nt][3]));
-        }
-      __syncthreads();
-      // chunk-start state to the output kernel: full 256-byte rows, 16 bytes per lane
-      {
-        uint16_t* stg = a.ST + (size_t(c) * a.hv + h) * 128 * 128 + size_t(kSlice * sl) * 128;
-#pragma unroll
-        for (int i = 0; i < kNT; ++i) {
-          const int row = (kSlice / 4) * w + 4 * i + (lane >> 4), seg = lane & 15;
-          st16(stg + row * 128 + seg * 8, &STs[row * kStLd + seg * 8]);
-        }
-      }
-
-      // W = U - Wk S   (rows 16w + 4lq + r, columns 16nt + li)
-      f32x4 Wt[kNT];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma16x16x32(wk[s], ld_short8(&STs[(16 * nt + li) * kStLd + 32 * s + 8 * lq]), acc);
-        const uint2 u = uu[nt];
-        Wt[nt][0] = __uint_as_float(u.x << 16) - acc[0];
-        Wt[nt][1] = __uint_as_float(u.x & 0xffff0000u) - acc[1];
-        Wt[nt][2] = __uint_as_float(u.y << 16) - acc[2];
-        Wt[nt][3] = __uint_as_float(u.y & 0xffff0000u) - acc[3];
-      }
-      // W^T staged for the output kernel; W~ = diag(exp(G_C - G_i)) W to LDS as the B operand of K^T W~
-      const float dec[4] = {__expf(gc - gr.x), __expf(gc - gr.y), __expf(gc - gr.z), __expf(gc - gr.w)};
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int col = 16 * nt + li, t0 = 16 * w + 4 * lq;
-        *reinterpret_cast<uint2*>(&WUs[col * kWtLd + t0]) =
-            make_uint2(pack_bf16x2(Wt[nt][0], Wt[nt][1]), pack_bf16x2(Wt[nt][2], Wt[nt][3]));
-        *reinterpret_cast<uint2*>(&WTs[col * kWtLd + t0]) =
-            make_uint2(pack_bf16x2(Wt[nt][0] * dec[0], Wt[nt][1] * dec[1]),
-                       pack_bf16x2(Wt[nt][2] * dec[2], Wt[nt][3] * dec[3]));
-      }
-      __syncthreads();
-      // W^T to the output kernel: full 128-byte rows, 16 bytes per lane
-      {
-        uint16_t* wtg = a.WT + (size_t(c) * a.hv + h) * 128 * 64 + size_t(kSlice * sl) * 64;
-#pragma unroll
-        for (int i = 0; i < kNT / 2; ++i) {
-          const int row = (kSlice / 4) * w + 8 * i + (lane >> 3), seg = lane & 7;
-          st16(wtg + row * 64 + seg * 8, &WUs[row * kWtLd + seg * 8]);
-        }
-      }
-
-      // S <- exp(G_C) S + K^T W~
-      const float gC = __expf(gc);
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          f32x4 acc = S[m][nt] * gC;
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            acc = mfma16x16x32(kt[m][s], ld_short8(&WTs[(16 * nt + li) * kWtLd + 32 * s + 8 * lq]), acc);
-          S[m][nt] = acc;
-        }
-    }
-    // no load may still be writing this block's LDS when it exits
+        for (int r = 0; r < 4; ++r)
+          S[m][nt][r] = a.state_in ? a.state_in[sbase + size_t(32 * w + 16 * m + 4 * lq + r) * 128 + kSlice * sl + 16 * nt + li] : 0.f;
+    // settle these loads here, so no wait inside the loop has to cover them (the loop's own
+    // stores would then be waited for too)
     wait_vm<0>();
+  }
+  // the producer issues the operand loads of compute waves [cw0, cw1) for one chunk into one slot
+  auto produce = [&](int64_t c, int slot, int cw0, int cw1) {
+    for (int cw = cw0; cw < cw1; ++cw)
+      issue_chunk(a, min(c, clast), h, g, sl, cw, lane, ring + uint32_t((slot * 4 + cw) * kWaveSlot));
+  };
+  if (c0 < c1 && producer) {
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i) produce(c0 + i, i, 0, 4);
+    wait_vm<(kDepth - 2) * 4 * kLoadsPerChunk>();  // chunk c0 has landed
+  }
+
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t j = c - c0;
+    const int slot = int(j % kDepth);
+    __syncthreads();  // B0: chunk c is in its ring slot
+    if (producer) {
+      // refill the slot read during step c - 1 (its reads finished before that step's B1), spread
+      // over the step so no barrier waits for the producer
+      const int fill = int((j + kDepth - 1) % kDepth);
+      produce(c + kDepth - 1, fill, 0, 1);
+      __syncthreads();  // B1
+      produce(c + kDepth - 1, fill, 1, 3);
+      __syncthreads();  // B2
+      produce(c + kDepth - 1, fill, 3, 4);
+      wait_vm<(kDepth - 2) * 4 * kLoadsPerChunk>();  // chunk c + 1 has landed
+      continue;
+    }
+
+    const unsigned char* ws = smem + size_t(slot * 4 + w) * kWaveSlot;
+    short8 wk[4], kt[2][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) wk[s] = *reinterpret_cast<const short8*>(ws + s * 1024 + lane * 16);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) kt[m][s] = *reinterpret_cast<const short8*>(ws + 4096 + (m * 2 + s) * 1024 + lane * 16);
+    uint2 uu[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) uu[nt] = *reinterpret_cast<const uint2*>(ws + 8192 + (nt * 64 + lane) * 8);
+    const float* Gl = reinterpret_cast<const float*>(ws + 8192 + kNT * 512);
+    const float4 gr = *reinterpret_cast<const float4*>(Gl + 16 * w + 4 * lq);
+    const float gc = Gl[63];
+
+    // S (bf16) -> LDS as S^T
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const int col = 16 * nt + li, k0 = 32 * w + 16 * m + 4 * lq;
+        *reinterpret_cast<uint2*>(&STs[col * kStLd + k0]) =
+            make_uint2(pack_bf16x2(S[m][nt][0], S[m][nt][1]), pack_bf16x2(S[m][nt][2], S[m][nt][3]));
+      }
+    __syncthreads();  // B1
+    // chunk-start state to the output kernel: full 256-byte rows, 16 bytes per lane
+    {
+      uint16_t* stg = a.ST + (size_t(c) * a.hv + h) * 128 * 128 + size_t(kSlice * sl) * 128;
+#pragma unroll
+      for (int i = 0; i < kNT; ++i) {
+        const int row = (kSlice / 4) * w + 4 * i + (lane >> 4), seg = lane & 15;
+        st16(stg + row * 128 + seg * 8, &STs[row * kStLd + seg * 8]);
+      }
+    }
+
+    // W = U - Wk S   (rows 16w + 4lq + r, columns 16nt + li)
+    f32x4 Wt[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = mfma16x16x32(wk[s], ld_short8(&STs[(16 * nt + li) * kStLd + 32 * s + 8 * lq]), acc);
+      const uint2 u = uu[nt];
+      Wt[nt][0] = __uint_as_float(u.x << 16) - acc[0];
+      Wt[nt][1] = __uint_as_float(u.x & 0xffff0000u) - acc[1];
+      Wt[nt][2] = __uint_as_float(u.y << 16) - acc[2];
+      Wt[nt][3] = __uint_as_float(u.y & 0xffff0000u) - acc[3];
+    }
+    // W^T staged for the output kernel; W~ = diag(exp(G_C - G_i)) W to LDS as the B operand of K^T W~
+    const float dec[4] = {__expf(gc - gr.x), __expf(gc - gr.y), __expf(gc - gr.z), __expf(gc - gr.w)};
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int col = 16 * nt + li, t0 = 16 * w + 4 * lq;
+      *reinterpret_cast<uint2*>(&WUs[col * kWtLd + t0]) =
+          make_uint2(pack_bf16x2(Wt[nt][0], Wt[nt][1]), pack_bf16x2(Wt[nt][2], Wt[nt][3]));
+      *reinterpret_cast<uint2*>(&WTs[col * kWtLd + t0]) =
+          make_uint2(pack_bf16x2(Wt[nt][0] * dec[0], Wt[nt][1] * dec[1]),
+                     pack_bf16x2(Wt[nt][2] * dec[2], Wt[nt][3] * dec[3]));
+    }
+    __syncthreads();  // B2
+    // W^T to the output kernel: full 128-byte rows, 16 bytes per lane
+    {
+      uint16_t* wtg = a.WT + (size_t(c) * a.hv + h) * 128 * 64 + size_t(kSlice * sl) * 64;
+#pragma unroll
+      for (int i = 0; i < kNT / 2; ++i) {
+        const int row = (kSlice / 4) * w + 8 * i + (lane >> 3), seg = lane & 7;
+        st16(wtg + row * 64 + seg * 8, &WUs[row * kWtLd + seg * 8]);
+      }
+    }
+
+    // S <- exp(G_C) S + K^T W~
+    const float gC = __expf(gc);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        f32x4 acc = S[m][nt] * gC;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          acc = mfma16x16x32(kt[m][s], ld_short8(&WTs[(16 * nt + li) * kWtLd + 32 * s + 8 * lq]), acc);
+        S[m][nt] = acc;
+      }
+  }
+  if (producer) {
+    wait_vm<0>();  // no load may still be writing this block's LDS when it exits
+    return;
   }
 
   if (a.state_out) {
@@ -244,7 +259,7 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const float* stat
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_state, dim3(unsigned(p.n_seqs), unsigned(p.hv), unsigned(kSlices)), dim3(256),
+  hipLaunchKernelGGL(k_state, dim3(unsigned(p.n_seqs), unsigned(p.hv), unsigned(kSlices)), dim3(320),
                      kStateSmem, s, a);
   return hipGetLastError();
 }
