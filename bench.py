@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="run one part only (for profilers); 'copy' times a plain 1 GiB device copy, the "
+                         "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -128,99 +131,119 @@ def main():
     gdn.load_library()
     stream = torch.cuda.current_stream()
 
-    # ---------------- prefill: one layer, B=1, T tokens -----------------------------------------
-    T = args.tokens
-    inp = config_layer(dev, T=T)
+    if args.only == "copy":
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms_per_copy": round(ms, 4),
+                          "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
+
     cfg = gdn.cfg_for(HK, HV, D, D, torch.bfloat16)
-    out = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
-    state_out = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
-    conv_out = torch.empty((1, 3, inp.n_channels), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(gdn.gdn_prefill_workspace(cfg, 1, T), dtype=torch.uint8, device=dev)
-    cu_host = inp.cu_seqlens.cpu()
+    result = {}
+    if args.only in ("all", "prefill"):
+        # ---------------- prefill: one layer, B=1, T tokens -----------------------------------------
+        T = args.tokens
+        inp = config_layer(dev, T=T)
+        out = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
+        state_out = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
+        conv_out = torch.empty((1, 3, inp.n_channels), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(gdn.gdn_prefill_workspace(cfg, 1, T), dtype=torch.uint8, device=dev)
+        cu_host = inp.cu_seqlens.cpu()
 
-    def step():
-        gdn.gdn_prefill(cfg, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.gate,
-                        inp.conv_w, inp.norm_w, state_in=None, state_out=state_out, conv_out=conv_out,
-                        out=out, workspace=ws, cu_seqlens_host=cu_host)
+        def step():
+            gdn.gdn_prefill(cfg, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.gate,
+                            inp.conv_w, inp.norm_w, state_in=None, state_out=state_out, conv_out=conv_out,
+                            out=out, workspace=ws, cu_seqlens_host=cu_host)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
 
-    # stage events: N_STAGES + 1 per timed step, created by recording once
-    import ctypes
-    nev = gdn.N_STAGES + 1
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    for row in evs:
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in evs]
+        # stage events: N_STAGES + 1 per timed step, created by recording once
+        import ctypes
+        nev = gdn.N_STAGES + 1
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        for row in evs:
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in evs]
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        gdn.gdn_set_stage_events(handles[i])
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    gdn.gdn_set_stage_events(None)
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
-    stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-                for j, name in enumerate(gdn.STAGE_NAMES)}
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            gdn.gdn_set_stage_events(handles[i])
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        gdn.gdn_set_stage_events(None)
+        ms_total = start.elapsed_time(end)
+        ms_step = ms_total / args.steps
+        stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+                    for j, name in enumerate(gdn.STAGE_NAMES)}
 
-    model = stage_model(T, 1)
-    dom = max(stage_ms, key=stage_ms.get)
-    dm = model[dom]
-    dom_s = stage_ms[dom] * 1e-3
-    if dm["bound"] == "hbm":
-        achieved = dm["bytes"] / dom_s / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None)
-    else:
-        achieved = dm["flops"] / dom_s / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
-    roof["kernel"] = dom
-    roof["ms_per_launch"] = round(stage_ms[dom], 5)
-    roof["algorithmic_bytes"] = dm["bytes"]
-    roof["algorithmic_flops"] = dm["flops"]
+        model = stage_model(T, 1)
+        dom = max(stage_ms, key=stage_ms.get)
+        dm = model[dom]
+        dom_s = stage_ms[dom] * 1e-3
+        if dm["bound"] == "hbm":
+            achieved = dm["bytes"] / dom_s / 1e9
+            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None)
+        else:
+            achieved = dm["flops"] / dom_s / 1e12
+            roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+        roof["kernel"] = dom
+        roof["ms_per_launch"] = round(stage_ms[dom], 5)
+        roof["algorithmic_bytes"] = dm["bytes"]
+        roof["algorithmic_flops"] = dm["flops"]
 
-    pb, pf = path_bytes(T, 1, False), path_flops(T)
-    t_hbm, t_mfma = pb / (HBM_PEAK_GBPS * 1e9), pf / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    s = ms_step * 1e-3
-    path = dict(bytes=pb, flops=pf, hbm_bound_us=round(t_hbm * 1e6, 2), mfma_bound_us=round(t_mfma * 1e6, 2),
-                frac_of_roofline=round(max(t_hbm, t_mfma) / s, 4), frac_of_mfma_bound=round(t_mfma / s, 4),
-                achieved_GBps=round(pb / s / 1e9, 1), achieved_TFLOPs=round(pf / s / 1e12, 2))
+        pb, pf = path_bytes(T, 1, False), path_flops(T)
+        t_hbm, t_mfma = pb / (HBM_PEAK_GBPS * 1e9), pf / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        s = ms_step * 1e-3
+        path = dict(bytes=pb, flops=pf, hbm_bound_us=round(t_hbm * 1e6, 2), mfma_bound_us=round(t_mfma * 1e6, 2),
+                    frac_of_roofline=round(max(t_hbm, t_mfma) / s, 4), frac_of_mfma_bound=round(t_mfma / s, 4),
+                    achieved_GBps=round(pb / s / 1e9, 1), achieved_TFLOPs=round(pf / s / 1e12, 2))
 
-    result = {
-        "metric": "GDN prefill tokens/s/GPU (48 v-heads, d=128) + decode step us at B=256; % roofline",
-        "value": round(T / s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"GDN layer prefill, B=1, T={T}, 16 QK / 48 value heads, d=128, chunk 64, "
-                               f"bf16 io, fp32 state, conv4+SiLU+L2+RMSNorm+sigmoid gate",
-                   "batch": 1, "seq_len": T},
-        "roofline": roof,
-        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
-        "path_roofline": path,
-        "wall_s": round(t_wall, 4),
-    }
+        result.update({
+            "metric": "GDN prefill tokens/s/GPU (48 v-heads, d=128) + decode step us at B=256; % roofline",
+            "value": round(T / s, 1),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"GDN layer prefill, B=1, T={T}, 16 QK / 48 value heads, d=128, chunk 64, "
+                                   f"bf16 io, fp32 state, conv4+SiLU+L2+RMSNorm+sigmoid gate",
+                       "batch": 1, "seq_len": T},
+            "roofline": roof,
+            "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+            "path_roofline": path,
+            "wall_s": round(t_wall, 4),
+        })
 
-    # ---------------- decode: B sequences, one token each ----------------------------------------
-    if not args.no_decode:
+    if args.only in ("all", "decode") and not args.no_decode:
+        # ---------------- decode: B sequences, one token each ------------------------------------
         B, S = args.decode_batch, args.decode_steps
         di = decode_inputs(B, S, n_qk_heads=HK, n_v_heads=HV, d_k=D, d_v=D, io_dtype=torch.bfloat16,
                            device=dev)
@@ -228,7 +251,7 @@ def main():
         pre = config_layer(dev, T=1024 * B, seed=1)
         pre.cu_seqlens = (torch.arange(B + 1, dtype=torch.int32) * 1024).to(dev)
         st = torch.empty((B, HV, D, D), dtype=torch.float32, device=dev)
-        cst = torch.empty((B, 3, inp.n_channels), dtype=torch.bfloat16, device=dev)
+        cst = torch.empty((B, 3, 2 * HK * D + HV * D), dtype=torch.bfloat16, device=dev)
         gdn.gdn_prefill(cfg, pre.cu_seqlens, pre.q, pre.k, pre.v, pre.alpha, pre.beta, pre.gate, pre.conv_w,
                         pre.norm_w, state_out=st, conv_out=cst)
         del pre
@@ -259,7 +282,7 @@ def main():
                              algorithmic_bytes=db),
         }
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.only == "all":
         result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
 
     print(json.dumps(result), flush=True)

@@ -71,6 +71,19 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
     if ((a.flags & GDN_GATE) && t < len)
       gv[it] = *reinterpret_cast<const uint4*>(a.gate + (start + t) * orow + h * 128 + sg * 8);
   }
+  // zero-centred gain (1 + w) of this thread's 8 epilogue columns (the same for all its pieces)
+  float gain[8];
+  {
+    const int sg = tid & 15;
+    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
+    if (a.flags & GDN_NORM) {
+      const float4* wp = reinterpret_cast<const float4*>(a.norm_w + int64_t(h) * a.norm_stride + sg * 8);
+      g0 = wp[0];
+      g1 = wp[1];
+    }
+    gain[0] = 1.f + g0.x; gain[1] = 1.f + g0.y; gain[2] = 1.f + g0.z; gain[3] = 1.f + g0.w;
+    gain[4] = 1.f + g1.x; gain[5] = 1.f + g1.y; gain[6] = 1.f + g1.z; gain[7] = 1.f + g1.w;
+  }
   const int64_t krow = int64_t(a.hk) * 128;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -165,7 +178,7 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = Ys[t * kYLd + sg * 8 + e] * rs;
-      if (a.flags & GDN_NORM) v *= 1.0f + a.norm_w[int64_t(h) * a.norm_stride + sg * 8 + e];
+      if (a.flags & GDN_NORM) v *= gain[e];
       if (a.flags & GDN_GATE) v *= sigmoidf_(gl[e]);
       o[e] = v;
     }
