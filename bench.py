@@ -13,6 +13,7 @@ duration gives the roofline fraction. The fp64 CPU oracle is timed on the host a
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,7 +36,7 @@ def stage_model(T: int, n_seqs: int):
     Bytes: each stage's inputs read once and outputs written once. Flops: dense-tile MFMA work
     (2 per multiply-add) of the stage's contractions.
     """
-    nc = -(-T // CH) + 0  # chunks (B=1 here: ceil(T / 64))
+    nc = -(-T // CH)  # chunks (B=1 here: ceil(T / 64))
     per_tok = {
         # raw q/k/v in (20480 B) + normalised q/k/v out (20480 B)
         "conv_silu_l2": dict(bytes=40960 * T + 10240 * 16, flops=0.0, bound="hbm"),
@@ -75,6 +76,37 @@ def path_flops(T: int) -> float:
 def decode_bytes(B: int) -> float:
     """Per decode step: state read + write, conv cache read + write, q/k/v, gate, o, alpha/beta."""
     return float(B * (HV * 128 * 128 * 4 * 2 + 3 * 10240 * 2 * 2 + 10240 * 2 + HV * 128 * 2 * 2 + HV * 8))
+
+
+KERNEL_DIR = os.path.join(ROOT, "linear_attention_token_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash(src: str) -> str:
+    """sha256 over a kernel's source file and the two headers every kernel includes."""
+    h = hashlib.sha256()
+    for f in (src, "gdn_device.h", "gdn_internal.h"):
+        with open(os.path.join(KERNEL_DIR, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+STAGE_SOURCE = {"conv_silu_l2": "k_conv.hip", "wy_or_sequential": "k_wy.hip", "state": "k_state.hip",
+                "output_norm_gate": "k_out.hip", "conv_tail": "k_conv.hip", "decode": "k_decode.hip"}
+
+
+def measured_traffic(stage: str, grid_tag: str):
+    """HBM bytes per launch of a stage from the committed counter summary (FETCH_SIZE and WRITE_SIZE
+    scaled by a plain copy's readings), or None when absent, taken at another launch shape, or taken
+    on a different kernel source than the one built now."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            k = json.load(fh)["kernels"][stage]
+    except (OSError, KeyError, ValueError):
+        return None
+    if k.get("workload") != grid_tag or k.get("source_sha256") != kernel_source_hash(STAGE_SOURCE[stage]):
+        return None
+    return round(float(k["traffic_bytes"]))
 
 
 def cpu_baseline(max_tokens: int):
@@ -203,11 +235,12 @@ def main():
         if dm["bound"] == "hbm":
             achieved = dm["bytes"] / dom_s / 1e9
             roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=None)
+                        frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=measured_traffic(dom, f"prefill T={T}"))
         else:
             achieved = dm["flops"] / dom_s / 1e12
             roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+                        frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                        traffic=measured_traffic(dom, f"prefill T={T}"))
         roof["kernel"] = dom
         roof["ms_per_launch"] = round(stage_ms[dom], 5)
         roof["algorithmic_bytes"] = dm["bytes"]
@@ -278,7 +311,8 @@ def main():
                         f"fp32 state in place, {S} consecutive steps",
             "us_per_step": round(us, 2),
             "roofline": dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                             frac=round(gbps / HBM_PEAK_GBPS, 4), traffic=None, kernel="decode",
+                             frac=round(gbps / HBM_PEAK_GBPS, 4),
+                             traffic=measured_traffic("decode", f"decode B={B}"), kernel="decode",
                              algorithmic_bytes=db),
         }
 

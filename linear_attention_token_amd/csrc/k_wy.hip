@@ -82,6 +82,12 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
   // w + 4 * it of all 64 rows, so its transposed 2-byte LDS writes cover 128 contiguous bytes.
   const int64_t krow = int64_t(a.hk) * 128;
   const int64_t vrow = int64_t(a.hv) * 128;
+  // decay and write strength of this chunk (wave 0 scans them), issued with the other loads
+  float la_raw = 1.f, be_raw = 0.f;
+  if (w == 0 && lane < len) {
+    la_raw = a.alpha[(start + lane) * a.hv + h];
+    be_raw = a.beta[(start + lane) * a.hv + h];
+  }
   uint4 vv[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -103,11 +109,8 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
     }
   }
   if (w == 0) {
-    float la = 0.f, be = 0.f;
-    if (lane < len) {
-      la = logf(a.alpha[(start + lane) * a.hv + h]);
-      be = a.beta[(start + lane) * a.hv + h];
-    }
+    float la = lane < len ? logf(la_raw) : 0.f;
+    const float be = be_raw;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(la, o, 64);
