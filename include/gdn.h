@@ -110,7 +110,10 @@ gdn_status gdn_prefill_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t tot
  *                     aligned; its contents on entry do not matter.
  * The bf16 path at d_k = d_v = 128 runs the chunked (64-token) WY form on bf16 MFMA with an
  * fp32 state; every other configuration (and every fp32-io call) runs a token-sequential fp32
- * recurrence, which keeps fp32 accuracy. */
+ * recurrence, which keeps fp32 accuracy.
+ * total_tokens must stay below 2^31 and small enough that every kernel grid fits in 2^32
+ * work-items (about 22M tokens at 48 value heads); beyond that both calls return
+ * GDN_E_UNSUPPORTED and the batch must be split. */
 gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
                        const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                        const void* q, const void* k, const void* v,

@@ -147,6 +147,17 @@ const char* gdn_status_string(gdn_status st) {
   return "unknown gdn_status";
 }
 
+// Every launch's grid, counted in work-items, must fit in 32 bits.
+static bool launches_fit(const Problem& p) {
+  const int64_t lim = (int64_t(1) << 32) - 1;
+  const int vec = p.bf16 ? 8 : 4;
+  const int64_t strips = (p.T + kConvStrip - 1) / kConvStrip;
+  const int64_t cblk = ((p.C + vec - 1) / vec + 255) / 256;
+  const int64_t conv = (int64_t(kXcds) * ((strips + kXcds - 1) / kXcds) * cblk + 1) * 256;
+  const int64_t chunks = xcd_blocks(p.nc_max * p.hk, p.hv / p.hk) * 256;
+  return conv <= lim && chunks <= lim;
+}
+
 gdn_status gdn_prefill_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, size_t* bytes) {
   g_last_error[0] = 0;
   if (!bytes) return fail(GDN_E_NULL, "bytes is NULL");
@@ -159,6 +170,7 @@ gdn_status gdn_prefill_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t tot
   p.n_seqs = n_seqs;
   p.T = total_tokens;
   p.nc_max = total_tokens / kChunk + n_seqs;
+  if (!launches_fit(p)) return fail(GDN_E_UNSUPPORTED, "too many tokens for one call; split the batch");
   *bytes = plan_workspace(p, nullptr).bytes;
   return GDN_OK;
 }
@@ -182,6 +194,7 @@ gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
   p.n_seqs = n_seqs;
   p.T = total_tokens;
   p.nc_max = total_tokens / kChunk + n_seqs;
+  if (!launches_fit(p)) return fail(GDN_E_UNSUPPORTED, "too many tokens for one call; split the batch");
   const uint32_t f = p.flags;
   // required pointers
   if (n_seqs > 0 && !cu_seqlens) return fail(GDN_E_NULL, "cu_seqlens is NULL");

@@ -115,6 +115,54 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ---- direct global -> LDS loads with explicit waits ----------------------------------------------
+// The compiler's own wait insertion treats these loads conservatively (a full vmcnt(0) at barriers),
+// so they are issued from inline asm and waited for with explicit vmcnt counts.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+// 16 (dma16) or 4 (dma4) bytes per lane from gptr to LDS address lds + size * lane; `lds` must be
+// the same in all lanes.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0v) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m0v) : "memory");
+}
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Row order pi used between the WY kernel and the chunk scan: inside every block of 32 rows,
+// position 4q + r (q, r < 4) holds row 8q + r and position 16 + 4q + r holds row 8q + 4 + r. With
+// it, accumulator tiles 2s and 2s + 1 of an MFMA lane (rows 4q + r) are together the 8 consecutive
+// rows 32s + 8q .. +7 that an operand lane covers, so accumulators feed the next product directly.
+__device__ __forceinline__ int pi32(int x) {
+  const int b = x & ~31, y = x & 31;
+  return b + ((y & 15) >> 2) * 8 + (y >> 4) * 4 + (y & 3);
+}
+
+// Two fp32 accumulator tiles (4 + 4 rows) -> one bf16 MFMA operand (8 k values).
+__device__ __forceinline__ short8 pack8(const f32x4& a, const f32x4& b) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                    pack_bf16x2(b[2], b[3])};
+  return __builtin_bit_cast(short8, v);
+}
+
+// Unit and position inside the unit of block b under the XCD-aware numbering (see xcd_blocks):
+// block b = 8 * (per_unit * j + sub) + x serves unit 8 * j + x.
+__device__ __forceinline__ void xcd_item(int b, int per_unit, int& unit, int& sub) {
+  const int x = b & 7, k = b >> 3, j = k / per_unit;
+  unit = 8 * j + x;
+  sub = k - j * per_unit;
+}
+
 // Logistic function and SiLU on the hardware exp2 / reciprocal.
 __device__ __forceinline__ float sigmoidf_(float z) { return frcp(1.0f + __expf(-z)); }
 __device__ __forceinline__ float siluf_(float u) { return u * frcp(1.0f + __expf(-u)); }

@@ -9,7 +9,18 @@
 
 namespace gdn {
 
-constexpr int kChunk = 64;  // tokens per chunk of the WY form
+constexpr int kChunk = 64;      // tokens per chunk of the WY form
+constexpr int kConvStrip = 16;  // tokens per thread of the conv kernel
+
+// XCD-aware block numbering. The blocks of a launch are dealt round-robin over the chip's 8 XCDs
+// (block b runs on XCD b % 8), each with its own L2. Work that reads the same tiles (the value heads
+// of one QK head) forms a unit of `per_unit` blocks; numbering the blocks as xcd_item() decodes them
+// puts all blocks of a unit on one XCD, back to back, so the first one's misses fill that XCD's L2
+// for the others. Grids are 1-D with xcd_blocks() blocks; items past the last unit exit at once.
+constexpr int kXcds = 8;
+inline int64_t xcd_blocks(int64_t units, int per_unit) {
+  return int64_t(kXcds) * per_unit * ((units + kXcds - 1) / kXcds);
+}
 
 // Problem description after validation; every launcher reads it.
 struct Problem {

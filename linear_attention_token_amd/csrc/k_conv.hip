@@ -88,23 +88,31 @@ struct ConvArgs {
   void *qhat, *khat, *vhat;
   uint32_t flags;
   float l2_eps;
-  // chunk table (chunked path only): built by the extra last column of blocks
+  // block numbering: strips of kConvStrip tokens x blocks of 256 channel groups
+  int64_t n_strips, strips_per_xcd;
+  int n_cblk;
+  // chunk table (chunked path only): built by the extra last block
   int64_t nc_max;
   int32_t* seq_off;
   int4* tab;
 };
 
-constexpr int kConvStrip = 16;  // tokens per thread
-
 // IO: input/history type; WT: type of the normalised outputs.
 template <typename IO, typename WT>
 __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
-  if (blockIdx.x == gridDim.x - 1) {  // the extra block column builds the chunk table
-    if (blockIdx.y == 0 && a.tab != nullptr) build_chunk_table(a.cu, a.n_seqs, a.T, a.nc_max, a.seq_off, a.tab);
+  if (blockIdx.x == gridDim.x - 1) {  // the extra last block builds the chunk table
+    if (a.tab != nullptr) build_chunk_table(a.cu, a.n_seqs, a.T, a.nc_max, a.seq_off, a.tab);
     return;
   }
+  // Block b runs on XCD b % 8 (blocks are dealt round-robin over the XCDs). Each XCD walks its own
+  // run of consecutive strips, all channel blocks of a strip before the next strip, so the 3 halo
+  // rows a strip reads were fetched into the same XCD's L2 by the strip just before it.
+  const int xcd = int(blockIdx.x & 7), kx = int(blockIdx.x >> 3);
+  const int64_t strip = int64_t(xcd) * a.strips_per_xcd + kx / a.n_cblk;
+  const int cblk = kx % a.n_cblk;
+  if (strip >= a.n_strips) return;
   constexpr int VEC = vec16<IO>::N;
-  const int64_t cg = int64_t(blockIdx.y) * blockDim.x + threadIdx.x;
+  const int64_t cg = int64_t(cblk) * blockDim.x + threadIdx.x;
   const int64_t c0 = cg * VEC;
   const bool active = c0 < a.C;
   const int64_t qk_ch = int64_t(a.hk) * a.dk;
@@ -129,7 +137,7 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
   const int width = a.dk / VEC;  // lanes per q/k head
 
   // raw rows t0-3 .. t0+15 of this thread's channels, all loads in flight together
-  const int64_t t0 = int64_t(blockIdx.x) * kConvStrip;
+  const int64_t t0 = strip * kConvStrip;
   uint4 xr[kConvStrip + 3];
 #pragma unroll
   for (int j = 0; j < kConvStrip + 3; ++j) {
@@ -216,14 +224,18 @@ hipError_t launch_conv(const Problem& p, const int32_t* cu, const void* q, const
                        int64_t ld_q, int64_t ld_k, int64_t ld_v, const float* conv_w,
                        const void* conv_in, const Workspace& ws, bool work_bf16, hipStream_t s) {
   const bool table = work_bf16 && ws.chunk_tab != nullptr;
-  ConvArgs a{cu, p.n_seqs, p.T, p.C, p.hk, p.hv, p.dk, p.dv, q, k, v, ld_q, ld_k, ld_v,
-             conv_w, conv_in, ws.qhat, ws.khat, ws.vhat, p.flags, p.l2_eps,
-             p.nc_max, table ? ws.seq_chunk_off : nullptr, table ? ws.chunk_tab : nullptr};
   if (p.T == 0 && !table) return hipSuccess;
   const int vec = p.bf16 ? 8 : 4;
   const int64_t groups = (p.C + vec - 1) / vec;
-  // token strips along x (plus one block column for the chunk table), channel blocks along y
-  dim3 grid(unsigned((p.T + kConvStrip - 1) / kConvStrip + 1), unsigned((groups + 255) / 256));
+  const int n_cblk = int((groups + 255) / 256);
+  const int64_t n_strips = (p.T + kConvStrip - 1) / kConvStrip;
+  const int64_t per_xcd = (n_strips + kXcds - 1) / kXcds;
+  ConvArgs a{cu, p.n_seqs, p.T, p.C, p.hk, p.hv, p.dk, p.dv, q, k, v, ld_q, ld_k, ld_v,
+             conv_w, conv_in, ws.qhat, ws.khat, ws.vhat, p.flags, p.l2_eps,
+             n_strips, per_xcd, n_cblk,
+             p.nc_max, table ? ws.seq_chunk_off : nullptr, table ? ws.chunk_tab : nullptr};
+  // kXcds x per_xcd x n_cblk strip blocks, then one block for the chunk table
+  const dim3 grid(unsigned(int64_t(kXcds) * per_xcd * n_cblk + 1));
   if (p.bf16) {
     if (work_bf16) hipLaunchKernelGGL((k_conv<bf16, bf16>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_conv<bf16, float>), grid, dim3(256), 0, s, a);

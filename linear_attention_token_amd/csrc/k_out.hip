@@ -16,6 +16,7 @@ namespace gdn {
 
 struct OutArgs {
   const int4* tab;
+  int n_units;                   // chunks x QK heads
   int hk, hv, R;
   const uint16_t *qhat, *khat;   // bf16 [T][hk][128]
   const float* G;                // [nc][hv][64]
@@ -29,12 +30,15 @@ struct OutArgs {
 };
 
 __global__ void __launch_bounds__(256) k_out(OutArgs a) {
-  const int c = blockIdx.x, h = blockIdx.y;
+  // the R value heads of a QK head read the same q^ / k^ tiles: keep them on one XCD
+  int u, hr;
+  xcd_item(int(blockIdx.x), a.R, u, hr);
+  if (u >= a.n_units) return;
+  const int c = u / a.hk, g = u - c * a.hk, h = g * a.R + hr;
   const int4 ct = a.tab[c];
   const int len = ct.y;
   if (len <= 0) return;
   const int64_t start = ct.x;
-  const int g = h / a.R;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
   constexpr int kLd = 136;
@@ -189,11 +193,13 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
 hipError_t launch_output(const Problem& p, const Workspace& ws, const void* gate, const float* norm_w,
                          void* out, hipStream_t s) {
   if (p.nc_max == 0) return hipSuccess;
-  OutArgs a{ws.chunk_tab, p.hk, p.hv, p.hv / p.hk, static_cast<const uint16_t*>(ws.qhat),
+  const int R = p.hv / p.hk;
+  const int64_t units = p.nc_max * p.hk;
+  OutArgs a{ws.chunk_tab, int(units), p.hk, p.hv, R, static_cast<const uint16_t*>(ws.qhat),
             static_cast<const uint16_t*>(ws.khat), ws.G, ws.ST, ws.WT,
             static_cast<const uint16_t*>(gate), norm_w, p.norm_stride, static_cast<uint16_t*>(out),
             p.flags, p.scale, p.norm_eps};
-  hipLaunchKernelGGL(k_out, dim3(unsigned(p.nc_max), unsigned(p.hv)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_out, dim3(unsigned(xcd_blocks(units, R))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,11 +7,12 @@
 // (§03) applied to 64 tokens at once (U, Wk, G from the WY kernel). The chunk-start state and W are
 // stored (bf16) for the output kernel, which then runs chunk-parallel.
 //
-// The d_v columns of S are independent in these products, so a chain is split into 2 slices of
-// 64 columns: one block of 4 waves per (sequence, value head, slice). Wave w owns state rows
-// 32w..32w+31 (two 16-row MFMA tiles) and W rows 16w..16w+15 of the slice; S and W cross waves through LDS in
-// bf16 as the B operand of the bf16 MFMAs, accumulation stays fp32. Each wave streams its own
-// operands (A operands of Wk and K^T, its U tiles, G) through a private LDS ring (see below).
+// The d_v columns of S are independent in these products, so a chain is split into 4 slices of
+// 32 columns: one block of 4 compute waves per (sequence, value head, slice). Wave w owns state
+// rows 32w..32w+31 (two 16-row MFMA tiles) and W rows 16w..16w+15 of the slice; S and W cross
+// waves through LDS in bf16 as the B operand of the bf16 MFMAs, accumulation stays fp32. Each wave
+// streams its own operands (A operands of Wk and K^T, its U tiles, G) through a private LDS ring
+// (see below).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -22,6 +23,7 @@ constexpr int kSlices = 128 / kSlice;
 
 struct StateArgs {
   const int32_t* seq_off;
+  int n_units;  // sequences x QK heads
   int hk, hv, R;
   const float* G;
   const uint16_t *Wk, *U, *KT;
@@ -36,30 +38,12 @@ struct StateArgs {
 // and waits for with explicit vmcnt counts; the four compute waves never stall on load issue.
 // The compute waves write the chunk state and W with coalesced stores from LDS.
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
-}
-// 16 (dma16) or 4 (dma4) bytes per lane from gptr to LDS address m0 + size * lane.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0v) : "memory");
-}
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // The trailing s_nop covers the gfx9 hazard of a VALU overwriting the data VGPRs of a store wider
 // than 8 bytes right after it (the compiler's hazard recognizer does not see inside inline asm).
 __device__ __forceinline__ void st16(void* gptr, const void* lds_src) {
   const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds_src);
   asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(gptr), "v"(v) : "memory");
-}
-// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m0v) : "memory");
-}
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 constexpr int kDepth = 3;                       // ring slots: loads run kDepth - 1 steps ahead
@@ -92,8 +76,12 @@ __device__ __forceinline__ void issue_chunk(const StateArgs& a, int64_t c, int h
 
 __global__ void __launch_bounds__(320) k_state(StateArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int n = blockIdx.x, h = blockIdx.y, sl = blockIdx.z;
-  const int g = h / a.R;
+  // the R value heads of a QK head (all their slices) read the same K^T tiles: keep them on one XCD
+  int u, sub;
+  xcd_item(int(blockIdx.x), a.R * kSlices, u, sub);
+  if (u >= a.n_units) return;
+  const int n = u / a.hk, g = u - n * a.hk;
+  const int h = g * a.R + sub / kSlices, sl = sub % kSlices;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;  // waves 0-3 compute, wave 4 loads
   const int li = lane & 15, lq = lane >> 4;
   const bool producer = (w == 4);
@@ -250,7 +238,9 @@ __global__ void __launch_bounds__(320) k_state(StateArgs a) {
 hipError_t launch_state(const Problem& p, const Workspace& ws, const float* state_in, float* state_out,
                         hipStream_t s) {
   if (p.n_seqs == 0) return hipSuccess;
-  StateArgs a{ws.seq_chunk_off, p.hk, p.hv, p.hv / p.hk, ws.G, ws.Wk, ws.U, ws.KT, ws.ST, ws.WT,
+  const int R = p.hv / p.hk;
+  const int64_t units = int64_t(p.n_seqs) * p.hk;
+  StateArgs a{ws.seq_chunk_off, int(units), p.hk, p.hv, R, ws.G, ws.Wk, ws.U, ws.KT, ws.ST, ws.WT,
               state_in, state_out};
   static bool attr_set = false;  // same value on every device; idempotent, so a race is harmless
   if (!attr_set) {
@@ -259,7 +249,7 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const float* stat
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_state, dim3(unsigned(p.n_seqs), unsigned(p.hv), unsigned(kSlices)), dim3(320),
+  hipLaunchKernelGGL(k_state, dim3(unsigned(xcd_blocks(units, R * kSlices))), dim3(320),
                      kStateSmem, s, a);
   return hipGetLastError();
 }

@@ -20,6 +20,7 @@ namespace gdn {
 
 struct WyArgs {
   const int4* tab;
+  int n_units;                    // chunks x QK heads
   int hk, hv, R;
   const uint16_t *khat, *vhat;    // bf16 [T][hk][128], [T][hv][128]
   const float *alpha, *beta;      // [T][hv]
@@ -61,12 +62,15 @@ __device__ __forceinline__ void wy_offdiag(const float* Am, float* Tm, float* X,
 }
 
 __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
-  const int c = blockIdx.x, h = blockIdx.y;
+  // the R value heads of a QK head read the same k^ tile: keep them on one XCD
+  int u, hr;
+  xcd_item(int(blockIdx.x), a.R, u, hr);
+  if (u >= a.n_units) return;
+  const int c = u / a.hk, g = u - c * a.hk, h = g * a.R + hr;
   const int4 ct = a.tab[c];
   const int len = ct.y;
   if (len <= 0) return;
   const int64_t start = ct.x;
-  const int g = h / a.R;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;
 
@@ -123,7 +127,7 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
   __syncthreads();
 
   // K^T of the chunk for the state pass, written once per QK head
-  if (h % a.R == 0) {
+  if (hr == 0) {
     uint16_t* dst = a.KT + (int64_t(c) * a.hk + g) * 128 * 64;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -150,6 +154,7 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
       Am[t * kFLd + i] = (i < t) ? Bs[t] * __expf(Gs[t] - Gs[i]) * acc[r] : 0.f;
     }
   }
+
   __syncthreads();
 
   // ---- diagonal 16x16 blocks: D_w = (I + A_ww)^-1 by forward substitution, lane = column ----
@@ -225,7 +230,7 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
     }
   }
   // U goes out in this accumulator layout, [wave][16-col tile][lane][4 rows], which is exactly how
-  // the state kernel consumes it (8 contiguous bytes per lane).
+  // the state pass consumes it (8 contiguous bytes per lane).
   uint16_t* Ug = a.U + (int64_t(c) * a.hv + h) * 64 * 128;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
@@ -255,9 +260,11 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
 hipError_t launch_wy(const Problem& p, const Workspace& ws, const float* alpha, const float* beta,
                      hipStream_t s) {
   if (p.nc_max == 0) return hipSuccess;
-  WyArgs a{ws.chunk_tab, p.hk, p.hv, p.hv / p.hk, static_cast<const uint16_t*>(ws.khat),
+  const int R = p.hv / p.hk;
+  const int64_t units = p.nc_max * p.hk;
+  WyArgs a{ws.chunk_tab, int(units), p.hk, p.hv, R, static_cast<const uint16_t*>(ws.khat),
            static_cast<const uint16_t*>(ws.vhat), alpha, beta, ws.G, ws.Wk, ws.U, ws.KT};
-  hipLaunchKernelGGL(k_wy, dim3(unsigned(p.nc_max), unsigned(p.hv)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_wy, dim3(unsigned(xcd_blocks(units, R))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

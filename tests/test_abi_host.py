@@ -58,6 +58,15 @@ def test_workspace_sizes():
     assert gdn.gdn_prefill_workspace(c, 0, 0) >= 0
 
 
+def test_oversized_calls_are_refused():
+    # grids of the chunked kernels would pass 2^32 work-items: refused up front, before any launch
+    c = gdn.gdn_cfg_default()
+    nbytes = ctypes.c_size_t(0)
+    _err(lib.gdn_prefill_workspace(ctypes.byref(c), 1, 1 << 30, ctypes.byref(nbytes)), 6)
+    _err(_prefill(c, n_seqs=1, T=1 << 30), 6)
+    assert gdn.gdn_prefill_workspace(c, 1, 1 << 24) > 0  # 16M tokens still fit
+
+
 def _prefill(cfg, n_seqs=N_, T=T_, cu=A, cu_host=None, q=A, k=A, v=A, ld_q=2048, ld_k=2048, ld_v=6144,
              alpha=A, beta=A, gate=A, conv_w=A, norm_w=A, state_in=None, state_out=None, conv_in=None,
              conv_out=None, out=A, ws=A, ws_bytes=1 << 40):
