@@ -1,4 +1,5 @@
-// Chunk WY/UT transform of the gated delta rule, one block per (64-token chunk, value head).
+// Chunk WY/UT transform of the gated delta rule, one block per (64-token chunk, QK head, batch of
+// value heads): the value heads of a QK head share its k^ tile, loaded and transposed once.
 //
 // Unrolling the update equations of the analysis notes "Qwen3.8-Flash-Next：架构、效率与技术谱系"
 // (§03) over a chunk that starts from state S, with G_t = sum_{s<=t} ln alpha_s and
@@ -13,6 +14,9 @@
 // -> T diag(beta), T diag(beta gamma) rounded to bf16 -> U, Wk on bf16 MFMA.
 // Rows past the end of a partial chunk carry beta = 0 and ln alpha = 0, so their U and Wk rows are
 // zero and G stays at the last real token.
+//
+// A block holds TEAMS teams of 4 waves, one per value head of its batch; all teams run the same
+// steps in lockstep (block-wide barriers), each on its own LDS region.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -61,32 +65,41 @@ __device__ __forceinline__ void wy_offdiag(const float* Am, float* Tm, float* X,
   for (int r = 0; r < 4; ++r) Tm[(16 * i + 4 * lq + r) * kFLd + 16 * j + li] = -acc2[r];
 }
 
-__global__ void __launch_bounds__(256) k_wy(WyArgs a) {
-  // the R value heads of a QK head read the same k^ tile: keep them on one XCD
-  int u, hr;
-  xcd_item(int(blockIdx.x), a.R, u, hr);
+template <int TEAMS>
+__global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a) {
+  // block -> (chunk, QK head) unit and batch of TEAMS value heads; the batches of one unit run on
+  // one XCD, back to back
+  int u, hb;
+  xcd_item(int(blockIdx.x), a.R / TEAMS, u, hb);
   if (u >= a.n_units) return;
-  const int c = u / a.hk, g = u - c * a.hk, h = g * a.R + hr;
+  const int c = u / a.hk, g = u - c * a.hk;
   const int4 ct = a.tab[c];
   const int len = ct.y;
   if (len <= 0) return;
   const int64_t start = ct.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, team = tid >> 8, w = (tid >> 6) & 3;
+  const int ttid = tid & 255;  // thread index inside the team
   const int li = lane & 15, lq = lane >> 4;
+  const int hr = hb * TEAMS + team, h = g * a.R + hr;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kKsLd];    // k^ rows; later T', T''
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kKsLd];    // k^ rows
   __shared__ __attribute__((aligned(16))) uint16_t KTs[128 * kKTLd];  // k^ transposed
-  __shared__ __attribute__((aligned(16))) float Am[64 * kFLd];        // A; later V^ transposed
-  __shared__ __attribute__((aligned(16))) float Tm[64 * kFLd];        // T; later staging
-  __shared__ float Xs[4][256];
-  __shared__ float Gs[64], Bs[64];
+  __shared__ __attribute__((aligned(16))) float Am_[TEAMS][64 * kFLd];  // A; later T', T''; Wk staging
+  __shared__ __attribute__((aligned(16))) float Tm_[TEAMS][64 * kFLd];  // T; later V^ transposed
+  __shared__ float Xs_[TEAMS][4][256];
+  __shared__ float Gs_[TEAMS][64], Bs_[TEAMS][64];
+  float* Am = Am_[team];
+  float* Tm = Tm_[team];
+  float (*Xs)[256] = Xs_[team];
+  float* Gs = Gs_[team];
+  float* Bs = Bs_[team];
 
-  // ---- load k^ (row-major and transposed) and prefetch v^; alpha/beta -> G ----
-  // piece (t = idx % 64, sg = idx / 64) of idx = tid + 256 * it: wave w handles column segments
-  // w + 4 * it of all 64 rows, so its transposed 2-byte LDS writes cover 128 contiguous bytes.
+  // ---- load k^ (row-major and transposed; all teams) and prefetch v^; alpha/beta -> G ----
+  // piece (t = idx % 64, sg = idx / 64) of idx = tid + 256 TEAMS it: a wave handles one column
+  // segment of all 64 rows, so its transposed 2-byte LDS writes cover 128 contiguous bytes.
   const int64_t krow = int64_t(a.hk) * 128;
   const int64_t vrow = int64_t(a.hv) * 128;
-  // decay and write strength of this chunk (wave 0 scans them), issued with the other loads
+  // decay and write strength of this chunk (wave 0 of the team scans them), issued with the loads
   float la_raw = 1.f, be_raw = 0.f;
   if (w == 0 && lane < len) {
     la_raw = a.alpha[(start + lane) * a.hv + h];
@@ -100,8 +113,10 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
     if (t < len) vv[it] = *reinterpret_cast<const uint4*>(a.vhat + (start + t) * vrow + h * 128 + sg * 8);
   }
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int t = lane, sg = w + 4 * it;
+  for (int it = 0; it < (1024 + 256 * TEAMS - 1) / (256 * TEAMS); ++it) {
+    const int idx = tid + 256 * TEAMS * it;
+    if (idx >= 1024) break;
+    const int t = idx & 63, sg = idx >> 6;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (t < len) v = *reinterpret_cast<const uint4*>(a.khat + (start + t) * krow + g * 128 + sg * 8);
     *reinterpret_cast<uint4*>(&Ks[t * kKsLd + sg * 8]) = v;
@@ -131,7 +146,7 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
     uint16_t* dst = a.KT + (int64_t(c) * a.hk + g) * 128 * 64;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int idx = tid + it * 256;  // 128 rows x 8 segments
+      const int idx = ttid + it * 256;  // 128 rows x 8 segments
       const int r = idx >> 3, sg = idx & 7;
       *reinterpret_cast<uint4*>(dst + r * 64 + sg * 8) = *reinterpret_cast<const uint4*>(&KTs[r * kKTLd + sg * 8]);
     }
@@ -187,17 +202,18 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
   if (w == 0) wy_offdiag(Am, Tm, Xs[w], 3, 0, lane);            // T30
   __syncthreads();
 
-  // ---- T' = T diag(beta), T'' = T diag(beta gamma) in bf16 (reuse Ks); V^ transposed into Am ----
-  uint16_t* T1 = Ks;                 // [64][72]
-  uint16_t* T2 = Ks + 64 * kKTLd;    // [64][72]
-  for (int idx = tid; idx < 64 * 64; idx += 256) {
+  // ---- T' = T diag(beta), T'' = T diag(beta gamma) in bf16 over A; then V^ transposed over T ----
+  uint16_t* T1 = reinterpret_cast<uint16_t*>(Am);  // [64][72]
+  uint16_t* T2 = T1 + 64 * kKTLd;                  // [64][72]
+  for (int idx = ttid; idx < 64 * 64; idx += 256) {
     const int t = idx >> 6, i = idx & 63;
     const float tv = Tm[t * kFLd + i];
     const float b = Bs[i];
     T1[t * kKTLd + i] = f2bf(tv * b);
     T2[t * kKTLd + i] = f2bf(tv * b * __expf(Gs[i]));
   }
-  uint16_t* VTs = reinterpret_cast<uint16_t*>(Am);  // [128][72]
+  __syncthreads();  // T is read completely
+  uint16_t* VTs = reinterpret_cast<uint16_t*>(Tm);  // [128][72]
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int t = lane, sg = w + 4 * it;
@@ -236,8 +252,9 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
   for (int nt = 0; nt < 8; ++nt)
     *reinterpret_cast<uint2*>(Ug + ((w * 8 + nt) * 64 + lane) * 4) =
         make_uint2(pack_bf16x2(accU[nt][0], accU[nt][1]), pack_bf16x2(accU[nt][2], accU[nt][3]));
-  // Tm is no longer read after T' and T'' were formed: reuse it as output staging for Wk
-  uint16_t* Ws = reinterpret_cast<uint16_t*>(Tm);  // [64][136]
+  // T', T'' are dead once every wave of the team is done with them: stage Wk over them
+  __syncthreads();
+  uint16_t* Ws = reinterpret_cast<uint16_t*>(Am);  // [64][136]
   constexpr int kOLd = 136;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
@@ -251,7 +268,7 @@ __global__ void __launch_bounds__(256) k_wy(WyArgs a) {
   uint16_t* Wg = a.Wk + (int64_t(c) * a.hv + h) * 64 * 128;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int idx = tid + it * 256;
+    const int idx = ttid + it * 256;
     const int t = idx >> 4, sg = idx & 15;
     *reinterpret_cast<uint4*>(Wg + t * 128 + sg * 8) = *reinterpret_cast<const uint4*>(&Ws[t * kOLd + sg * 8]);
   }
@@ -264,7 +281,10 @@ hipError_t launch_wy(const Problem& p, const Workspace& ws, const float* alpha, 
   const int64_t units = p.nc_max * p.hk;
   WyArgs a{ws.chunk_tab, int(units), p.hk, p.hv, R, static_cast<const uint16_t*>(ws.khat),
            static_cast<const uint16_t*>(ws.vhat), alpha, beta, ws.G, ws.Wk, ws.U, ws.KT};
-  hipLaunchKernelGGL(k_wy, dim3(unsigned(xcd_blocks(units, R))), dim3(256), 0, s, a);
+  // value heads per block: three teams fill the LDS of a CU
+  if (R % 3 == 0) hipLaunchKernelGGL(k_wy<3>, dim3(unsigned(xcd_blocks(units, R / 3))), dim3(768), 0, s, a);
+  else if (R % 2 == 0) hipLaunchKernelGGL(k_wy<2>, dim3(unsigned(xcd_blocks(units, R / 2))), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL(k_wy<1>, dim3(unsigned(xcd_blocks(units, R))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -64,6 +64,14 @@ def test_bf16_chunked_ragged():
     _check_full(inp)
 
 
+@pytest.mark.parametrize("hk,hv", [(2, 2), (2, 4), (1, 4), (1, 5), (1, 6)])
+def test_bf16_chunked_head_ratios(hk, hv):
+    """Value heads per QK head from 1 to 6: the WY kernel batches 1, 2 or 3 of them per block."""
+    inp = prefill_inputs([150, 64, 3], n_qk_heads=hk, n_v_heads=hv, d_k=128, d_v=128,
+                         io_dtype=torch.bfloat16, seed=11 + hv, device=DEV, s0_std=0.01, conv_in_std=1.0)
+    _check_full(inp)
+
+
 @pytest.mark.parametrize("flags", [gdn.GDN_CONV | gdn.GDN_L2QK, gdn.GDN_L2QK | gdn.GDN_NORM | gdn.GDN_GATE])
 def test_bf16_chunked_stage_flags(flags):
     inp = prefill_inputs([150], n_qk_heads=1, n_v_heads=3, d_k=128, d_v=128,
