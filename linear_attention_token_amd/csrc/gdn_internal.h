@@ -46,7 +46,7 @@ struct Workspace {
   // chunked bf16 path only
   float* G = nullptr;                // fp32 [nc][hv][64]    in-chunk cumulative log decay
   uint16_t* Wk = nullptr;            // bf16 [nc][hv][64][128]  T diag(beta*gamma) K
-  uint16_t* U = nullptr;             // bf16 [nc][hv][4 waves][8 tiles][64 lanes][4]  T diag(beta) V
+  uint16_t* U = nullptr;             // bf16 [nc][hv][4][4 tile pairs][64 lanes][2][4]  T diag(beta) V
   uint16_t* KT = nullptr;            // bf16 [nc][hk][128][64]  K^T of each chunk
   uint16_t* ST = nullptr;            // bf16 [nc][hv][128][128] chunk-start state, transposed
   uint16_t* WT = nullptr;            // bf16 [nc][hv][128][64]  chunk write W, transposed

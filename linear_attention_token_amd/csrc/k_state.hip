@@ -56,7 +56,8 @@ constexpr int kWtLd = 72;                       // bf16 row stride of W~^T and W
 constexpr size_t kStateSmem = size_t(kDepth) * 4 * kWaveSlot + kSlice * kStLd * 2 + 2 * kSlice * kWtLd * 2;
 
 // Wave slot layout (bytes): [0, 4096) Wk A operands [s][lane][16]; [4096, 8192) K^T A operands
-// [m*2+s][lane][16]; then U [tile][lane][4 bf16] (512 B per 16-column tile); then G[64] fp32.
+// [m*2+s][lane][16]; then U [tile pair][lane][2 tiles][4 bf16] (1 KB per pair of 16-column
+// tiles); then G[64] fp32.
 __device__ __forceinline__ void issue_chunk(const StateArgs& a, int64_t c, int h, int g, int sl, int w,
                                             int lane, uint32_t wslot) {
   const int li = lane & 15, lq = lane >> 4;
@@ -145,7 +146,8 @@ __global__ void __launch_bounds__(320) k_state(StateArgs a) {
       for (int s = 0; s < 2; ++s) kt[m][s] = *reinterpret_cast<const short8*>(ws + 4096 + (m * 2 + s) * 1024 + lane * 16);
     uint2 uu[kNT];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) uu[nt] = *reinterpret_cast<const uint2*>(ws + 8192 + (nt * 64 + lane) * 8);
+    for (int nt = 0; nt < kNT; ++nt)
+      uu[nt] = *reinterpret_cast<const uint2*>(ws + 8192 + ((nt >> 1) * 64 + lane) * 16 + (nt & 1) * 8);
     const float* Gl = reinterpret_cast<const float*>(ws + 8192 + kNT * 512);
     const float4 gr = *reinterpret_cast<const float4*>(Gl + 16 * w + 4 * lq);
     const float gc = Gl[63];

@@ -17,20 +17,21 @@
 //
 // A block holds TEAMS teams of 4 waves, one per value head of its batch; all teams run the same
 // steps in lockstep (block-wide barriers), each on its own LDS region.
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
 struct WyArgs {
-  const int4* tab;
   int n_units;                    // chunks x QK heads
   int hk, hv, R;
   const uint16_t *khat, *vhat;    // bf16 [T][hk][128], [T][hv][128]
   const float *alpha, *beta;      // [T][hv]
   float* G;                       // [nc][hv][64]
   uint16_t *Wk;                   // [nc][hv][64][128]
-  uint16_t *U;                    // [nc][hv][4 waves][8 tiles][64 lanes][4 rows]
+  uint16_t *U;                    // [nc][hv][4 waves][4 tile pairs][64 lanes][2 tiles][4 rows]
   uint16_t* KT;                   // [nc][hk][128][64]
 };
 
@@ -65,60 +66,109 @@ __device__ __forceinline__ void wy_offdiag(const float* Am, float* Tm, float* X,
   for (int r = 0; r < 4; ++r) Tm[(16 * i + 4 * lq + r) * kFLd + 16 * j + li] = -acc2[r];
 }
 
+// Block b works through the items b, b + gridDim.x, ... (one item = chunk, QK head and batch of
+// TEAMS value heads) with one block per CU; the raw inputs of its next item are loaded into
+// registers while the current one is transformed, so loads overlap compute.
 template <int TEAMS>
-__global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a) {
-  // block -> (chunk, QK head) unit and batch of TEAMS value heads; the batches of one unit run on
-  // one XCD, back to back
-  int u, hb;
-  xcd_item(int(blockIdx.x), a.R / TEAMS, u, hb);
-  if (u >= a.n_units) return;
-  const int c = u / a.hk, g = u - c * a.hk;
-  const int4 ct = a.tab[c];
-  const int len = ct.y;
-  if (len <= 0) return;
-  const int64_t start = ct.x;
+__global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __restrict__ tab) {
+  constexpr int kKIt = (1024 + 256 * TEAMS - 1) / (256 * TEAMS);  // k^ pieces per thread
   const int tid = threadIdx.x, lane = tid & 63, team = tid >> 8, w = (tid >> 6) & 3;
   const int ttid = tid & 255;  // thread index inside the team
   const int li = lane & 15, lq = lane >> 4;
-  const int hr = hb * TEAMS + team, h = g * a.R + hr;
+  const int nb = a.R / TEAMS;  // batches of value heads per QK head
+  const int n_items = a.n_units * nb;
+  const int64_t krow = int64_t(a.hk) * 128;
+  const int64_t vrow = int64_t(a.hv) * 128;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kKsLd];    // k^ rows
-  __shared__ __attribute__((aligned(16))) uint16_t KTs[128 * kKTLd];  // k^ transposed
+  __shared__ __attribute__((aligned(16))) uint16_t Ks_[64 * kKsLd];    // k^ rows
+  __shared__ __attribute__((aligned(16))) uint16_t KTs_[128 * kKTLd];  // k^ transposed
   __shared__ __attribute__((aligned(16))) float Am_[TEAMS][64 * kFLd];  // A; later T', T''; Wk staging
   __shared__ __attribute__((aligned(16))) float Tm_[TEAMS][64 * kFLd];  // T; later V^ transposed
   __shared__ float Xs_[TEAMS][4][256];
-  __shared__ float Gs_[TEAMS][64], Bs_[TEAMS][64];
-  float* Am = Am_[team];
-  float* Tm = Tm_[team];
-  float (*Xs)[256] = Xs_[team];
-  float* Gs = Gs_[team];
-  float* Bs = Bs_[team];
+  __shared__ __attribute__((aligned(16))) float Gs_[TEAMS][64], Bs_[TEAMS][64], Cs_[TEAMS][64];
 
-  // ---- load k^ (row-major and transposed; all teams) and prefetch v^; alpha/beta -> G ----
-  // piece (t = idx % 64, sg = idx / 64) of idx = tid + 256 TEAMS it: a wave handles one column
-  // segment of all 64 rows, so its transposed 2-byte LDS writes cover 128 contiguous bytes.
-  const int64_t krow = int64_t(a.hk) * 128;
-  const int64_t vrow = int64_t(a.hv) * 128;
-  // decay and write strength of this chunk (wave 0 of the team scans them), issued with the loads
+  // item -> chunk c, QK head g, this thread's value head h; chunk start and length
+  struct Item { int c, g, hr, h, len; int64_t start; };
+  auto decode = [&](int item) {
+    Item it;
+    const int u = item / nb, hb = item - u * nb;
+    it.c = u / a.hk;
+    it.g = u - it.c * a.hk;
+    it.hr = hb * TEAMS + team;
+    it.h = it.g * a.R + it.hr;
+    const int4 ct = tab[it.c];  // wave-uniform address: a scalar load
+    it.start = ct.x;
+    it.len = ct.y;
+    return it;
+  };
+  // raw inputs of an item: k^ pieces (t = idx % 64, segment idx / 64 of idx = tid + 256 TEAMS j; a
+  // wave covers one column segment of all 64 rows, so its transposed LDS writes are contiguous),
+  // v^ pieces (t = lane, segment w + 4j of this team's head), alpha and beta (wave 0 of a team)
+  uint4 kv[kKIt], vv[4];
   float la_raw = 1.f, be_raw = 0.f;
-  if (w == 0 && lane < len) {
-    la_raw = a.alpha[(start + lane) * a.hv + h];
-    be_raw = a.beta[(start + lane) * a.hv + h];
-  }
-  uint4 vv[4];
+  auto fetch_k = [&](int item) {
+    if (item >= n_items) return;
+    const Item it = decode(item);
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int t = lane, sg = w + 4 * it;
-    vv[it] = make_uint4(0, 0, 0, 0);
-    if (t < len) vv[it] = *reinterpret_cast<const uint4*>(a.vhat + (start + t) * vrow + h * 128 + sg * 8);
-  }
+    for (int j = 0; j < kKIt; ++j) {
+      const int idx = tid + 256 * TEAMS * j, t = idx & 63, sg = idx >> 6;
+      kv[j] = make_uint4(0, 0, 0, 0);
+      if (idx < 1024 && t < it.len)
+        kv[j] = *reinterpret_cast<const uint4*>(a.khat + (it.start + t) * krow + it.g * 128 + sg * 8);
+    }
+  };
+  auto fetch_v = [&](int item) {
+    if (item >= n_items) return;
+    const Item it = decode(item);
 #pragma unroll
-  for (int it = 0; it < (1024 + 256 * TEAMS - 1) / (256 * TEAMS); ++it) {
-    const int idx = tid + 256 * TEAMS * it;
+    for (int j = 0; j < 4; ++j) {
+      vv[j] = make_uint4(0, 0, 0, 0);
+      if (lane < it.len)
+        vv[j] = *reinterpret_cast<const uint4*>(a.vhat + (it.start + lane) * vrow + it.h * 128 + (w + 4 * j) * 8);
+    }
+    la_raw = 1.f;
+    be_raw = 0.f;
+    if (w == 0 && lane < it.len) {
+      la_raw = a.alpha[(it.start + lane) * a.hv + it.h];
+      be_raw = a.beta[(it.start + lane) * a.hv + it.h];
+    }
+  };
+
+  int item = blockIdx.x;
+  fetch_k(item);
+  fetch_v(item);
+  for (; item < n_items; item += gridDim.x) {
+    const Item it = decode(item);
+    const int c = it.c, g = it.g, hr = it.hr, h = it.h, len = it.len;
+    const int64_t start = it.start;
+    // Thread indices and LDS views are rebuilt from an opaque zero in each item, so that the
+    // compiler recomputes their many per-lane derivatives instead of keeping them all live across
+    // the item loop (more registers than the three-team block has).
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    const int tid = int(threadIdx.x) + z, lane = tid & 63, w = (tid >> 6) & 3, ttid = tid & 255;
+    const int li = lane & 15, lq = lane >> 4;
+    uint16_t* const Ks = Ks_ + z;
+    uint16_t* const KTs = KTs_ + z;
+    float* const Am = Am_[team] + z;
+    float* const Tm = Tm_[team] + z;
+    float (*const Xs)[256] = reinterpret_cast<float (*)[256]>(&Xs_[team][0][0] + z);
+    float* const Gs = Gs_[team] + z;
+    float* const Bs = Bs_[team] + z;
+    float* const Cs = Cs_[team] + z;  // beta exp(G)
+    if (len <= 0) {  // past the last chunk (uniform over the block)
+      fetch_k(item + gridDim.x);
+      fetch_v(item + gridDim.x);
+      continue;
+    }
+
+  // ---- k^ into LDS (row-major and transposed; all teams); alpha/beta -> G ----
+#pragma unroll
+  for (int j = 0; j < kKIt; ++j) {
+    const int idx = tid + 256 * TEAMS * j;
     if (idx >= 1024) break;
     const int t = idx & 63, sg = idx >> 6;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < len) v = *reinterpret_cast<const uint4*>(a.khat + (start + t) * krow + g * 128 + sg * 8);
+    const uint4 v = kv[j];
     *reinterpret_cast<uint4*>(&Ks[t * kKsLd + sg * 8]) = v;
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -137,9 +187,11 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a) {
     }
     Gs[lane] = la;
     Bs[lane] = be;
+    Cs[lane] = be * __expf(la);
     a.G[(int64_t(c) * a.hv + h) * 64 + lane] = la;
   }
   __syncthreads();
+  fetch_k(item + gridDim.x);  // the next item's k^ flies while this one is transformed
 
   // K^T of the chunk for the state pass, written once per QK head
   if (hr == 0) {
@@ -205,12 +257,16 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a) {
   // ---- T' = T diag(beta), T'' = T diag(beta gamma) in bf16 over A; then V^ transposed over T ----
   uint16_t* T1 = reinterpret_cast<uint16_t*>(Am);  // [64][72]
   uint16_t* T2 = T1 + 64 * kKTLd;                  // [64][72]
-  for (int idx = ttid; idx < 64 * 64; idx += 256) {
-    const int t = idx >> 6, i = idx & 63;
-    const float tv = Tm[t * kFLd + i];
-    const float b = Bs[i];
-    T1[t * kKTLd + i] = f2bf(tv * b);
-    T2[t * kKTLd + i] = f2bf(tv * b * __expf(Gs[i]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // 4 consecutive columns per thread and pass
+    const int idx = ttid + 256 * j, t = idx >> 4, i0 = (idx & 15) * 4;
+    const float4 tv = *reinterpret_cast<const float4*>(&Tm[t * kFLd + i0]);
+    const float4 b = *reinterpret_cast<const float4*>(&Bs[i0]);
+    const float4 cg = *reinterpret_cast<const float4*>(&Cs[i0]);
+    *reinterpret_cast<uint2*>(&T1[t * kKTLd + i0]) =
+        make_uint2(pack_bf16x2(tv.x * b.x, tv.y * b.y), pack_bf16x2(tv.z * b.z, tv.w * b.w));
+    *reinterpret_cast<uint2*>(&T2[t * kKTLd + i0]) =
+        make_uint2(pack_bf16x2(tv.x * cg.x, tv.y * cg.y), pack_bf16x2(tv.z * cg.z, tv.w * cg.w));
   }
   __syncthreads();  // T is read completely
   uint16_t* VTs = reinterpret_cast<uint16_t*>(Tm);  // [128][72]
@@ -226,52 +282,56 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a) {
   }
   __syncthreads();
 
-  // ---- U = T' V^, Wk = T'' K^  (rows 16w.., all 128 columns) ----
-  f32x4 accU[8], accW[8];
+  // ---- U = T' V^, then Wk = T'' K^  (rows 16w.., all 128 columns), one accumulator set at a time
+  f32x4 acc[8];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    accU[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accW[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const short8 a1 = ld_short8(&T1[(16 * w + li) * kKTLd + 32 * s + 8 * lq]);
-    const short8 a2 = ld_short8(&T2[(16 * w + li) * kKTLd + 32 * s + 8 * lq]);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const short8 bv = ld_short8(&VTs[(16 * nt + li) * kKTLd + 32 * s + 8 * lq]);
-      const short8 bk = ld_short8(&KTs[(16 * nt + li) * kKTLd + 32 * s + 8 * lq]);
-      accU[nt] = mfma16x16x32(a1, bv, accU[nt]);
-      accW[nt] = mfma16x16x32(a2, bk, accW[nt]);
-    }
+    for (int nt = 0; nt < 8; ++nt)
+      acc[nt] = mfma16x16x32(a1, ld_short8(&VTs[(16 * nt + li) * kKTLd + 32 * s + 8 * lq]), acc[nt]);
   }
-  // U goes out in this accumulator layout, [wave][16-col tile][lane][4 rows], which is exactly how
-  // the state pass consumes it (8 contiguous bytes per lane).
+  fetch_v(item + gridDim.x);  // V^ of this item is in LDS; the next item's flies meanwhile
+  // U goes out in this accumulator layout, tiles paired: [wave][tile pair][lane][2 tiles][4 rows],
+  // which is how the state pass consumes it (16 contiguous bytes per lane)
   uint16_t* Ug = a.U + (int64_t(c) * a.hv + h) * 64 * 128;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-    *reinterpret_cast<uint2*>(Ug + ((w * 8 + nt) * 64 + lane) * 4) =
-        make_uint2(pack_bf16x2(accU[nt][0], accU[nt][1]), pack_bf16x2(accU[nt][2], accU[nt][3]));
-  // T', T'' are dead once every wave of the team is done with them: stage Wk over them
-  __syncthreads();
-  uint16_t* Ws = reinterpret_cast<uint16_t*>(Am);  // [64][136]
-  constexpr int kOLd = 136;
+  for (int p = 0; p < 4; ++p)
+    *reinterpret_cast<uint4*>(Ug + ((w * 4 + p) * 64 + lane) * 8) =
+        make_uint4(pack_bf16x2(acc[2 * p][0], acc[2 * p][1]), pack_bf16x2(acc[2 * p][2], acc[2 * p][3]),
+                   pack_bf16x2(acc[2 * p + 1][0], acc[2 * p + 1][1]),
+                   pack_bf16x2(acc[2 * p + 1][2], acc[2 * p + 1][3]));
+  // Wk^T = K^T T''^T with the rows of K^T (channels) in the order pi: accumulator tiles 2s, 2s + 1
+  // of lane (token 16w + li, lq) hold Wk[token][32s + 8lq .. +7], stored as one 16-byte piece
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * w + 4 * lq + r, col = 16 * nt + li;
-      Ws[t * kOLd + col] = f2bf(accW[nt][r]);
-    }
+  for (int s = 0; s < 2; ++s) {
+    const short8 b2 = ld_short8(&T2[(16 * w + li) * kKTLd + 32 * s + 8 * lq]);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+      acc[nt] = mfma16x16x32(ld_short8(&KTs[pi32(16 * nt + li) * kKTLd + 32 * s + 8 * lq]), b2, acc[nt]);
   }
-  __syncthreads();
-  uint16_t* Wg = a.Wk + (int64_t(c) * a.hv + h) * 64 * 128;
+  uint16_t* Wg = a.Wk + (int64_t(c) * a.hv + h) * 64 * 128 + (16 * w + li) * 128 + 8 * lq;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = ttid + it * 256;
-    const int t = idx >> 4, sg = idx & 15;
-    *reinterpret_cast<uint4*>(Wg + t * 128 + sg * 8) = *reinterpret_cast<const uint4*>(&Ws[t * kOLd + sg * 8]);
+  for (int s = 0; s < 4; ++s) *reinterpret_cast<short8*>(Wg + 32 * s) = pack8(acc[2 * s], acc[2 * s + 1]);
+  __syncthreads();  // every read of this item's LDS is done before the next item overwrites it
+  }  // items
+}
+
+static int cu_count() {
+  // one entry per device; hipDeviceGetAttribute is cheap, so a race only repeats the query
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
   }
+  return counts[dev];
 }
 
 hipError_t launch_wy(const Problem& p, const Workspace& ws, const float* alpha, const float* beta,
@@ -279,12 +339,16 @@ hipError_t launch_wy(const Problem& p, const Workspace& ws, const float* alpha, 
   if (p.nc_max == 0) return hipSuccess;
   const int R = p.hv / p.hk;
   const int64_t units = p.nc_max * p.hk;
-  WyArgs a{ws.chunk_tab, int(units), p.hk, p.hv, R, static_cast<const uint16_t*>(ws.khat),
+  WyArgs a{int(units), p.hk, p.hv, R, static_cast<const uint16_t*>(ws.khat),
            static_cast<const uint16_t*>(ws.vhat), alpha, beta, ws.G, ws.Wk, ws.U, ws.KT};
-  // value heads per block: three teams fill the LDS of a CU
-  if (R % 3 == 0) hipLaunchKernelGGL(k_wy<3>, dim3(unsigned(xcd_blocks(units, R / 3))), dim3(768), 0, s, a);
-  else if (R % 2 == 0) hipLaunchKernelGGL(k_wy<2>, dim3(unsigned(xcd_blocks(units, R / 2))), dim3(512), 0, s, a);
-  else hipLaunchKernelGGL(k_wy<1>, dim3(unsigned(xcd_blocks(units, R))), dim3(256), 0, s, a);
+  // value heads per block: three teams fill the LDS of a CU, so one block per CU (two with one
+  // team), each working through its share of the items
+  const int teams = R % 3 == 0 ? 3 : (R % 2 == 0 ? 2 : 1);
+  const int64_t items = units * (R / teams);
+  const unsigned grid = unsigned(std::min<int64_t>(items, int64_t(cu_count()) * (teams == 1 ? 2 : 1)));
+  if (teams == 3) hipLaunchKernelGGL(k_wy<3>, dim3(grid), dim3(768), 0, s, a, ws.chunk_tab);
+  else if (teams == 2) hipLaunchKernelGGL(k_wy<2>, dim3(grid), dim3(512), 0, s, a, ws.chunk_tab);
+  else hipLaunchKernelGGL(k_wy<1>, dim3(grid), dim3(256), 0, s, a, ws.chunk_tab);
   return hipGetLastError();
 }
 

@@ -94,15 +94,25 @@ def gdn_abi_version() -> int:
     return load_library().gdn_abi_version()
 
 
+_stage_events = None  # the array the library points at, kept alive while it is set
+
+
 def gdn_set_stage_events(events) -> None:
     """Records raw hipEvent_t handles around each prefill stage (None switches it off).
 
-    ``events`` is a ctypes array of N_STAGES + 1 handles that the caller keeps alive."""
+    ``events`` is a ctypes array of N_STAGES + 1 handles (or a sequence of integer handles, copied
+    into one); the array stays referenced here until the next call, since the library keeps its
+    address. The events themselves must outlive the prefills that record them."""
+    global _stage_events
     lib = load_library()
     if events is None:
         _check(lib.gdn_set_stage_events(None, 0))
-    else:
-        _check(lib.gdn_set_stage_events(events, len(events)))
+        _stage_events = None
+        return
+    if not isinstance(events, ctypes.Array):
+        events = (ctypes.c_void_p * len(events))(*events)
+    _check(lib.gdn_set_stage_events(events, len(events)))
+    _stage_events = events
 
 
 def gdn_prefill_workspace(cfg: gdn_cfg, n_seqs: int, total_tokens: int) -> int:
