@@ -6,8 +6,10 @@ d=128, bf16 io, fp32 state). A step is one gdn_prefill call over that batch: con
 WY transform, state propagation, output + RMSNorm + gate, conv tail. The decode step (B=256, one
 token each, state streamed in place) is timed in the same run and reported beside it.
 
-Per-kernel times come from HIP events the library records on its stream around each stage, over
-the timed steps; the dominant kernel's algorithmic bytes (or flops) per launch divided by its mean
+The headline times K eager steps between two events on the library's stream. Per-kernel times
+come from HIP events the library records on the same stream around each stage, in a second pass of
+the same K steps right after (recording them inside the headline loop would add host work between
+launches); the dominant kernel's algorithmic bytes (or flops) per launch divided by its mean
 duration gives the roofline fraction. The fp64 CPU oracle is timed on the host as a baseline.
 """
 from __future__ import annotations
@@ -139,6 +141,8 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the reference timing of one captured HIP graph replayed per step")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="run one part only (for profilers); 'copy' times a plain 1 GiB device copy, the "
@@ -202,7 +206,35 @@ def main():
             step()
         torch.cuda.synchronize()
 
-        # stage events: N_STAGES + 1 per timed step, created by recording once
+        # headline: K eager steps bracketed by events, no stage events inside
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        ms_step = start.elapsed_time(end) / args.steps
+
+        # the same steps replayed from one captured HIP graph, for reference
+        ms_step_graph = None
+        if not args.no_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            graph.replay()
+            torch.cuda.synchronize()
+            start.record(stream)
+            for _ in range(args.steps):
+                graph.replay()
+            end.record(stream)
+            torch.cuda.synchronize()
+            ms_step_graph = start.elapsed_time(end) / args.steps
+
+        # per-stage times: a separate eager pass with the library's stage events (N_STAGES + 1 per
+        # step, created by recording once)
         import ctypes
         nev = gdn.N_STAGES + 1
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
@@ -211,20 +243,11 @@ def main():
                 e.record(stream)
         torch.cuda.synchronize()
         handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in evs]
-
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter()
-        start.record(stream)
         for i in range(args.steps):
             gdn.gdn_set_stage_events(handles[i])
             step()
-        end.record(stream)
         torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall
         gdn.gdn_set_stage_events(None)
-        ms_total = start.elapsed_time(end)
-        ms_step = ms_total / args.steps
         stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
                     for j, name in enumerate(gdn.STAGE_NAMES)}
 
@@ -261,6 +284,7 @@ def main():
             "steps": args.steps,
             "warmup": args.warmup,
             "ms_per_step": round(ms_step, 5),
+            "ms_per_step_graph_replay": round(ms_step_graph, 5) if ms_step_graph is not None else None,
             "higher_is_better": True,
             "scaling": "weak",
             "vs_baseline": None,

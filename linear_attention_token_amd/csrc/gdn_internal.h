@@ -10,7 +10,7 @@
 namespace gdn {
 
 constexpr int kChunk = 64;      // tokens per chunk of the WY form
-constexpr int kConvStrip = 16;  // tokens per thread of the conv kernel
+constexpr int kConvStrip = 8;   // tokens per thread of the conv kernel
 
 // XCD-aware block numbering. The blocks of a launch are dealt round-robin over the chip's 8 XCDs
 // (block b runs on XCD b % 8), each with its own L2. Work that reads the same tiles (the value heads

@@ -18,7 +18,7 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 from linear_attention_token_amd import gdn  # noqa: E402  (raises if libgdn.so is missing)
-from gdn_testutil import TOL, rel_l2, run_prefill, oracle_prefill, oracle_chain, seq_bounds  # noqa: E402
+from gdn_testutil import TOL, rel_l2, cfg_of, run_prefill, oracle_prefill, oracle_chain, seq_bounds  # noqa: E402
 
 gdn.load_library()
 DEV = "cuda"
@@ -147,6 +147,40 @@ def test_repeat_runs_bitwise():
     b = run_prefill(inp)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_graph_replay_matches_eager():
+    """A prefill captured in a HIP graph and replayed several times, with other GPU work and
+    synchronisations between the replays, reproduces the eager result bit for bit each time (the
+    library records no memset or host-side work that a graph would freeze)."""
+    inp = prefill_inputs([200, 64, 3], n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128,
+                         io_dtype=torch.bfloat16, seed=21, device=DEV, s0_std=0.01, conv_in_std=1.0)
+    cfg = cfg_of(inp)
+    N, T = inp.n_seqs, int(inp.q.shape[0])
+    out = torch.empty((T, inp.n_v_heads, inp.d_v), dtype=inp.io_dtype, device=DEV)
+    st = torch.empty((N, inp.n_v_heads, inp.d_k, inp.d_v), dtype=torch.float32, device=DEV)
+    cv = torch.empty((N, 3, inp.n_channels), dtype=inp.io_dtype, device=DEV)
+    ws = torch.empty(gdn.gdn_prefill_workspace(cfg, N, T), dtype=torch.uint8, device=DEV)
+    host = inp.cu_seqlens.cpu()
+
+    def step():
+        gdn.gdn_prefill(cfg, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.gate, inp.conv_w,
+                        inp.norm_w, state_in=inp.state_in, state_out=st, conv_in=inp.conv_in, conv_out=cv,
+                        out=out, workspace=ws, cu_seqlens_host=host)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (out.clone(), st.clone(), cv.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        for t in (out, st, cv, ws):
+            t.zero_()                    # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(st, ref[1]) and torch.equal(cv, ref[2])
 
 
 def test_alpha_one_beta_zero_keeps_state():
