@@ -33,10 +33,13 @@ struct StateArgs {
 };
 
 // ---- explicit memory operations -------------------------------------------------------------
-// The chunk operands stream through a ring in LDS (one region per compute wave), filled by direct
-// global->LDS loads (no VGPR destinations) that a fifth, producer wave issues kDepth-1 steps ahead
-// and waits for with explicit vmcnt counts; the four compute waves never stall on load issue.
-// The compute waves write the chunk state and W with coalesced stores from LDS.
+// The chunk operands stream through a ring in LDS, filled by direct global->LDS loads (no VGPR
+// destinations) that a fifth, producer wave issues kDepth-1 steps ahead and waits for with explicit
+// vmcnt counts; the four compute waves never stall on load issue. Every load moves 1 KB of
+// consecutive global bytes (whole rows): such loads stream about twice as fast per CU as loads
+// gathering 64-byte pieces of 16 rows. The 16-byte pieces of a row are placed in LDS in an XOR
+// order, so that the compute waves' MFMA operand reads (16 rows, the same columns) hit distinct
+// banks. The compute waves write the chunk state and W with coalesced stores from LDS.
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // The trailing s_nop covers the gfx9 hazard of a VALU overwriting the data VGPRs of a store wider
@@ -48,31 +51,32 @@ __device__ __forceinline__ void st16(void* gptr, const void* lds_src) {
 
 constexpr int kDepth = 3;                       // ring slots: loads run kDepth - 1 steps ahead
 constexpr int kNT = kSlice / 16;                // 16-column tiles per block
-constexpr int kLoadsPerChunk = 4 + 4 + kNT / 2 + 1;  // per wave per chunk: Wk, K^T, U, G
-constexpr int kStoresPerStep = kNT + kNT / 2;   // st16 per wave per step: chunk state, W
-constexpr int kWaveSlot = 4096 + 4096 + kNT * 512 + 256;  // bytes per wave per ring slot
+static_assert(kNT == 2, "one U tile pair per compute wave");
+// Slot layout (bytes): Wk [64 rows][256 B], K^T [128 rows][128 B], U [4 waves][1 KB tile pair],
+// G [64] fp32. Row r of Wk keeps its 16-byte piece q at slot q ^ (r % 16); row r of K^T keeps
+// piece q at slot q ^ ((r / 2) % 8).
+constexpr int kOffWk = 0, kOffKT = 16384, kOffU = 32768, kOffG = 36864;
+constexpr int kSlot = kOffG + 256;
+constexpr int kLoadsPerChunk = 16 + 16 + 4 + 1;  // Wk (4 rows each), K^T (8 rows each), U, G
 constexpr int kStLd = 136;                      // bf16 row stride of S^T [cols][128 k]
 constexpr int kWtLd = 72;                       // bf16 row stride of W~^T and W^T [cols][64 tokens]
-constexpr size_t kStateSmem = size_t(kDepth) * 4 * kWaveSlot + kSlice * kStLd * 2 + 2 * kSlice * kWtLd * 2;
+constexpr size_t kStateSmem = size_t(kDepth) * kSlot + kSlice * kStLd * 2 + 2 * kSlice * kWtLd * 2;
 
-// Wave slot layout (bytes): [0, 4096) Wk A operands [s][lane][16]; [4096, 8192) K^T A operands
-// [m*2+s][lane][16]; then U [tile pair][lane][2 tiles][4 bf16] (1 KB per pair of 16-column
-// tiles); then G[64] fp32.
-__device__ __forceinline__ void issue_chunk(const StateArgs& a, int64_t c, int h, int g, int sl, int w,
-                                            int lane, uint32_t wslot) {
-  const int li = lane & 15, lq = lane >> 4;
-  const uint16_t* wk = a.Wk + (c * a.hv + h) * 64 * 128 + (16 * w + li) * 128 + 8 * lq;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) dma16(wk + 32 * s, wslot + s * 1024);
-  const uint16_t* kt = a.KT + (c * a.hk + g) * 128 * 64 + (32 * w + li) * 64 + 8 * lq;
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) dma16(kt + 16 * m * 64 + 32 * s, wslot + 4096 + (m * 2 + s) * 1024);
-  const uint16_t* u = a.U + (c * a.hv + h) * 64 * 128 + (w * 8 + kNT * sl) * 256 + lane * 8;
-#pragma unroll
-  for (int i = 0; i < kNT / 2; ++i) dma16(u + i * 512, wslot + 8192 + i * 1024);
-  dma4(a.G + (c * a.hv + h) * 64 + lane, wslot + 8192 + kNT * 512);
+// Load i of chunk c into the ring slot at LDS address `slot`.
+__device__ __forceinline__ void issue_load(const StateArgs& a, int64_t c, int h, int g, int sl, int lane,
+                                           uint32_t slot, int i) {
+  if (i < 16) {  // Wk rows 4i .. 4i+3
+    const int r = 4 * i + (lane >> 4), piece = (lane & 15) ^ (r & 15);
+    dma16(a.Wk + (c * a.hv + h) * 8192 + r * 128 + piece * 8, slot + kOffWk + i * 1024);
+  } else if (i < 32) {  // K^T rows 8k .. 8k+7
+    const int k = i - 16, r = 8 * k + (lane >> 3), piece = (lane & 7) ^ ((r >> 1) & 7);
+    dma16(a.KT + (c * a.hk + g) * 8192 + r * 64 + piece * 8, slot + kOffKT + k * 1024);
+  } else if (i < 36) {  // U tile pair sl of accumulator row tile (wave) i - 32
+    const int w = i - 32;
+    dma16(a.U + (c * a.hv + h) * 8192 + (w * 4 + sl) * 512 + lane * 8, slot + kOffU + w * 1024);
+  } else {
+    dma4(a.G + (c * a.hv + h) * 64 + lane, slot + kOffG);
+  }
 }
 
 __global__ void __launch_bounds__(320) k_state(StateArgs a) {
@@ -86,7 +90,7 @@ __global__ void __launch_bounds__(320) k_state(StateArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;  // waves 0-3 compute, wave 4 loads
   const int li = lane & 15, lq = lane >> 4;
   const bool producer = (w == 4);
-  uint16_t* STs = reinterpret_cast<uint16_t*>(smem + size_t(kDepth) * 4 * kWaveSlot);
+  uint16_t* STs = reinterpret_cast<uint16_t*>(smem + size_t(kDepth) * kSlot);
   uint16_t* WTs = STs + kSlice * kStLd;   // W~^T: B operand of K^T W~
   uint16_t* WUs = WTs + kSlice * kWtLd;    // W^T unscaled: staged for the coalesced store
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
@@ -108,15 +112,17 @@ __global__ void __launch_bounds__(320) k_state(StateArgs a) {
     // stores would then be waited for too)
     wait_vm<0>();
   }
-  // the producer issues the operand loads of compute waves [cw0, cw1) for one chunk into one slot
-  auto produce = [&](int64_t c, int slot, int cw0, int cw1) {
-    for (int cw = cw0; cw < cw1; ++cw)
-      issue_chunk(a, min(c, clast), h, g, sl, cw, lane, ring + uint32_t((slot * 4 + cw) * kWaveSlot));
+  // the producer issues loads [i0, i1) of one chunk into one slot
+  auto produce = [&](int64_t c, int slot, int i0, int i1) {
+    const int64_t cc = min(c, clast);
+    const uint32_t sa = ring + uint32_t(slot * kSlot);
+#pragma unroll
+    for (int i = i0; i < i1; ++i) issue_load(a, cc, h, g, sl, lane, sa, i);
   };
   if (c0 < c1 && producer) {
 #pragma unroll
-    for (int i = 0; i < kDepth - 1; ++i) produce(c0 + i, i, 0, 4);
-    wait_vm<(kDepth - 2) * 4 * kLoadsPerChunk>();  // chunk c0 has landed
+    for (int i = 0; i < kDepth - 1; ++i) produce(c0 + i, i, 0, kLoadsPerChunk);
+    wait_vm<(kDepth - 2) * kLoadsPerChunk>();  // chunk c0 has landed
   }
 
   for (int64_t c = c0; c < c1; ++c) {
@@ -127,28 +133,33 @@ __global__ void __launch_bounds__(320) k_state(StateArgs a) {
       // refill the slot read during step c - 1 (its reads finished before that step's B1), spread
       // over the step so no barrier waits for the producer
       const int fill = int((j + kDepth - 1) % kDepth);
-      produce(c + kDepth - 1, fill, 0, 1);
+      produce(c + kDepth - 1, fill, 0, 13);
       __syncthreads();  // B1
-      produce(c + kDepth - 1, fill, 1, 3);
+      produce(c + kDepth - 1, fill, 13, 26);
       __syncthreads();  // B2
-      produce(c + kDepth - 1, fill, 3, 4);
-      wait_vm<(kDepth - 2) * 4 * kLoadsPerChunk>();  // chunk c + 1 has landed
+      produce(c + kDepth - 1, fill, 26, kLoadsPerChunk);
+      wait_vm<(kDepth - 2) * kLoadsPerChunk>();  // chunk c + 1 has landed
       continue;
     }
 
-    const unsigned char* ws = smem + size_t(slot * 4 + w) * kWaveSlot;
+    const unsigned char* sb = smem + size_t(slot) * kSlot;
+    // A operands: Wk rows 16w + li and K^T rows 32w + 16m + li, columns 32s + 8lq .. +7 (piece
+    // 4s + lq), each at its XOR slot
     short8 wk[4], kt[2][2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wk[s] = *reinterpret_cast<const short8*>(ws + s * 1024 + lane * 16);
+    for (int s = 0; s < 4; ++s)
+      wk[s] = *reinterpret_cast<const short8*>(sb + kOffWk + (16 * w + li) * 256 + (((4 * s + lq) ^ li) << 4));
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) kt[m][s] = *reinterpret_cast<const short8*>(ws + 4096 + (m * 2 + s) * 1024 + lane * 16);
+      for (int s = 0; s < 2; ++s)
+        kt[m][s] = *reinterpret_cast<const short8*>(sb + kOffKT + (32 * w + 16 * m + li) * 128 +
+                                                    (((4 * s + lq) ^ (li >> 1)) << 4));
     uint2 uu[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
-      uu[nt] = *reinterpret_cast<const uint2*>(ws + 8192 + ((nt >> 1) * 64 + lane) * 16 + (nt & 1) * 8);
-    const float* Gl = reinterpret_cast<const float*>(ws + 8192 + kNT * 512);
+      uu[nt] = *reinterpret_cast<const uint2*>(sb + kOffU + w * 1024 + lane * 16 + nt * 8);
+    const float* Gl = reinterpret_cast<const float*>(sb + kOffG);
     const float4 gr = *reinterpret_cast<const float4*>(Gl + 16 * w + 4 * lq);
     const float gc = Gl[63];
 
