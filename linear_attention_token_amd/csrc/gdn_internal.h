@@ -48,8 +48,8 @@ struct Workspace {
   uint16_t* Wk = nullptr;            // bf16 [nc][hv][64][128]  T diag(beta*gamma) K
   uint16_t* U = nullptr;             // bf16 [nc][hv][4][4 tile pairs][64 lanes][2][4]  T diag(beta) V
   uint16_t* KT = nullptr;            // bf16 [nc][hk][128][64]  K^T of each chunk
-  uint16_t* ST = nullptr;            // bf16 [nc][hv][128][128] chunk-start state, transposed
-  uint16_t* WT = nullptr;            // bf16 [nc][hv][128][64]  chunk write W, transposed
+  uint16_t* ST = nullptr;            // bf16 [nc][hv][4][2][4][64 lanes][8] chunk-start state pieces
+  uint16_t* WT = nullptr;            // bf16 [nc][hv][4][2][2][64 lanes][8] chunk write W pieces
   size_t bytes = 0;
 };
 

@@ -20,7 +20,7 @@ struct OutArgs {
   int hk, hv, R;
   const uint16_t *qhat, *khat;   // bf16 [T][hk][128]
   const float* G;                // [nc][hv][64]
-  const uint16_t *ST, *WT;       // [nc][hv][128][128], [nc][hv][128][64]
+  const uint16_t *ST, *WT;       // [nc][hv] operand pieces of 1 KB (see the state pass)
   const uint16_t* gate;          // bf16 [T][hv][128]
   const float* norm_w;
   int norm_stride;
@@ -53,16 +53,17 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
   __shared__ float Gs[64];
   __shared__ float red[4][64];
 
-  // B operands of this wave's columns (chunk state and W), issued first so they overlap the rest
+  // B operands of this wave's columns (chunk state and W), issued first so they overlap the rest;
+  // the state pass stores them as these operand pieces, 1 KB of consecutive bytes per load
   const uint16_t* st = a.ST + (int64_t(c) * a.hv + h) * 128 * 128;
   const uint16_t* wt = a.WT + (int64_t(c) * a.hv + h) * 128 * 64;
   short8 bs[2][4], bw[2][2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bs[nt][s] = ld_short8(st + (32 * w + 16 * nt + li) * 128 + 32 * s + 8 * lq);
+    for (int s = 0; s < 4; ++s) bs[nt][s] = ld_short8(st + (((w * 2 + nt) * 4 + s) * 64 + lane) * 8);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) bw[nt][s] = ld_short8(wt + (32 * w + 16 * nt + li) * 64 + 32 * s + 8 * lq);
+    for (int s = 0; s < 2; ++s) bw[nt][s] = ld_short8(wt + (((w * 2 + nt) * 2 + s) * 64 + lane) * 8);
   }
   // gate tile of this chunk and head, 16 bytes per thread and piece: piece p = tid + 256 * it covers
   // row p / 16, columns 8 * (p % 16) .. +8 (fully coalesced 256-byte rows)

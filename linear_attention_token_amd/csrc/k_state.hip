@@ -173,14 +173,13 @@ __global__ void __launch_bounds__(320) k_state(StateArgs a) {
             make_uint2(pack_bf16x2(S[m][nt][0], S[m][nt][1]), pack_bf16x2(S[m][nt][2], S[m][nt][3]));
       }
     __syncthreads();  // B1
-    // chunk-start state to the output kernel: full 256-byte rows, 16 bytes per lane
+    // chunk-start state to the output kernel, in its MFMA operand pieces: piece (sl, nt, w) holds
+    // columns 32sl + 16nt + (lane % 16), rows 32w + 8 (lane / 16) .. +7 -- 1 KB per store
     {
-      uint16_t* stg = a.ST + (size_t(c) * a.hv + h) * 128 * 128 + size_t(kSlice * sl) * 128;
+      uint16_t* stf = a.ST + (size_t(c) * a.hv + h) * 128 * 128;
 #pragma unroll
-      for (int i = 0; i < kNT; ++i) {
-        const int row = (kSlice / 4) * w + 4 * i + (lane >> 4), seg = lane & 15;
-        st16(stg + row * 128 + seg * 8, &STs[row * kStLd + seg * 8]);
-      }
+      for (int nt = 0; nt < kNT; ++nt)
+        st16(stf + (((sl * kNT + nt) * 4 + w) * 64 + lane) * 8, &STs[(16 * nt + li) * kStLd + 32 * w + 8 * lq]);
     }
 
     // W = U - Wk S   (rows 16w + 4lq + r, columns 16nt + li)
@@ -209,14 +208,12 @@ __global__ void __launch_bounds__(320) k_state(StateArgs a) {
                      pack_bf16x2(Wt[nt][2] * dec[2], Wt[nt][3] * dec[3]));
     }
     __syncthreads();  // B2
-    // W^T to the output kernel: full 128-byte rows, 16 bytes per lane
+    // W^T to the output kernel, in its MFMA operand pieces: wave w stores piece (sl, nt, s) with
+    // nt = w / 2, s = w % 2: columns 32sl + 16nt + (lane % 16), tokens 32s + 8 (lane / 16) .. +7
     {
-      uint16_t* wtg = a.WT + (size_t(c) * a.hv + h) * 128 * 64 + size_t(kSlice * sl) * 64;
-#pragma unroll
-      for (int i = 0; i < kNT / 2; ++i) {
-        const int row = (kSlice / 4) * w + 8 * i + (lane >> 3), seg = lane & 7;
-        st16(wtg + row * 64 + seg * 8, &WUs[row * kWtLd + seg * 8]);
-      }
+      const int nt = w >> 1, s = w & 1;
+      uint16_t* wtf = a.WT + (size_t(c) * a.hv + h) * 128 * 64;
+      st16(wtf + (((sl * kNT + nt) * 2 + s) * 64 + lane) * 8, &WUs[(16 * nt + li) * kWtLd + 32 * s + 8 * lq]);
     }
 
     // S <- exp(G_C) S + K^T W~
