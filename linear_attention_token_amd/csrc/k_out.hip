@@ -7,8 +7,11 @@
 // gate (analysis notes §03 changes made to GDN; paper summary "Qwen3.8-Flash-Next", Method: head
 // outputs are normalised, then gated).
 //
-// Wave w computes columns 32w..32w+31 of Y for all 64 rows (its own slice of the chunk state and
-// of W); RMSNorm row sums are combined across the four waves in LDS. bf16 MFMA, fp32 accumulate.
+// Wave w computes channels 32w..32w+31 of Y for all 64 tokens (its own slice of the chunk state and
+// of W), as Y^T = S^T Q^T + W^T P^T: the chunk-state and W pieces are then A operands as loaded, and
+// each lane ends with 4 consecutive channels of a token, so RMSNorm, gain and gate run on registers
+// and the lane stores 8 bytes. Per-token sums of squares are combined across the four waves in LDS.
+// bf16 MFMA, fp32 accumulate.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -43,10 +46,7 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
   const int li = lane & 15, lq = lane >> 4;
   constexpr int kLd = 136;
   constexpr int kPLd = 72;
-  constexpr int kYLd = 132;  // fp32 row stride of the staged Y tile (64 x 132 x 4 B fits Qs + Ks)
-  // one buffer for the Q and K tiles, reused afterwards for the fp32 Y tile
-  __shared__ __attribute__((aligned(16))) uint16_t QKs[2 * 64 * kLd];
-  static_assert(64 * kYLd * 4 <= 2 * 64 * kLd * 2, "Y tile must fit the Q/K buffer");
+  __shared__ __attribute__((aligned(16))) uint16_t QKs[2 * 64 * kLd];  // Q and K tiles
   uint16_t* Qs = QKs;
   uint16_t* Ks = QKs + 64 * kLd;
   __shared__ __attribute__((aligned(16))) uint16_t Ps[64 * kPLd];
@@ -65,29 +65,27 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) bw[nt][s] = ld_short8(wt + (((w * 2 + nt) * 2 + s) * 64 + lane) * 8);
   }
-  // gate tile of this chunk and head, 16 bytes per thread and piece: piece p = tid + 256 * it covers
-  // row p / 16, columns 8 * (p % 16) .. +8 (fully coalesced 256-byte rows)
+  // gate logits of this lane's outputs: token 16tt + li, channels 32w + 16nt + 4lq .. +3 (rows past
+  // the chunk end read the last row; those outputs are not stored)
   const int64_t orow = int64_t(a.hv) * 128;
-  uint4 gv[4];
+  uint2 gv[4][2];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int pidx = tid + it * 256, t = pidx >> 4, sg = pidx & 15;
-    gv[it] = make_uint4(0, 0, 0, 0);
-    if ((a.flags & GDN_GATE) && t < len)
-      gv[it] = *reinterpret_cast<const uint4*>(a.gate + (start + t) * orow + h * 128 + sg * 8);
-  }
-  // zero-centred gain (1 + w) of this thread's 8 epilogue columns (the same for all its pieces)
-  float gain[8];
-  {
-    const int sg = tid & 15;
-    float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0;
-    if (a.flags & GDN_NORM) {
-      const float4* wp = reinterpret_cast<const float4*>(a.norm_w + int64_t(h) * a.norm_stride + sg * 8);
-      g0 = wp[0];
-      g1 = wp[1];
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      gv[tt][nt] = make_uint2(0u, 0u);
+      if (a.flags & GDN_GATE)
+        gv[tt][nt] = *reinterpret_cast<const uint2*>(a.gate + (start + min(16 * tt + li, len - 1)) * orow + h * 128 +
+                                                     32 * w + 16 * nt + 4 * lq);
     }
-    gain[0] = 1.f + g0.x; gain[1] = 1.f + g0.y; gain[2] = 1.f + g0.z; gain[3] = 1.f + g0.w;
-    gain[4] = 1.f + g1.x; gain[5] = 1.f + g1.y; gain[6] = 1.f + g1.z; gain[7] = 1.f + g1.w;
+  // zero-centred gain (1 + w) of this lane's 8 channels
+  float gain[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.flags & GDN_NORM)
+      g4 = *reinterpret_cast<const float4*>(a.norm_w + int64_t(h) * a.norm_stride + 32 * w + 16 * nt + 4 * lq);
+    gain[nt][0] = 1.f + g4.x; gain[nt][1] = 1.f + g4.y; gain[nt][2] = 1.f + g4.z; gain[nt][3] = 1.f + g4.w;
   }
   const int64_t krow = int64_t(a.hk) * 128;
 #pragma unroll
@@ -122,72 +120,70 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
   }
   __syncthreads();
 
-  // Y: wave w owns columns 32w..32w+31 (two 16-column tiles) for all 64 rows, so it reads only its
-  // own columns of the chunk state and of W; the RMSNorm row sums are combined across waves in LDS.
+  // Y^T: acc[tt][nt][r] is channel 32w + 16nt + 4lq + r of token 16tt + li
   f32x4 acc[4][2];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const short8 qa = ld_short8(&Qs[(16 * mt + li) * kLd + 32 * s + 8 * lq]);
+      const short8 qb = ld_short8(&Qs[(16 * tt + li) * kLd + 32 * s + 8 * lq]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32(qa, bs[nt][s], acc[mt][nt]);
+      for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = mfma16x16x32(bs[nt][s], qb, acc[tt][nt]);
     }
-    float gam[4];
+    const float gam = __expf(Gs[16 * tt + li]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) gam[r] = __expf(Gs[16 * mt + 4 * lq + r]);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mt][nt][r] *= gam[r];
+    for (int nt = 0; nt < 2; ++nt) acc[tt][nt] *= gam;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const short8 pa = ld_short8(&Ps[(16 * mt + li) * kPLd + 32 * s + 8 * lq]);
+      if (32 * s > 16 * tt + 15) continue;  // P is zero above the diagonal
+      const short8 pb = ld_short8(&Ps[(16 * tt + li) * kPLd + 32 * s + 8 * lq]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32(pa, bw[nt][s], acc[mt][nt]);
+      for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = mfma16x16x32(bw[nt][s], pb, acc[tt][nt]);
     }
   }
 
-  // scale and RMSNorm row sums; Y (fp32) staged in LDS over the Q/K tiles for a coalesced epilogue
-  __syncthreads();  // every wave is done reading Qs / Ks / Ps
-  float* Ys = reinterpret_cast<float*>(QKs);  // [64][kYLd] fp32 over the Q/K buffer
+  // scale, and each token's sum of squares over this wave's 32 channels
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int tt = 0; tt < 4; ++tt) {
+    float ss = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float ss = 0.f;
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float y = acc[mt][nt][r] * a.scale;
-        ss += y * y;
-        Ys[(16 * mt + 4 * lq + r) * kYLd + 32 * w + 16 * nt + li] = y;
+      for (int r = 0; r < 4; ++r) {
+        acc[tt][nt][r] *= a.scale;
+        ss += acc[tt][nt][r] * acc[tt][nt][r];
       }
-      ss = group_sum<16>(ss);
-      if (li == 0) red[w][16 * mt + 4 * lq + r] = ss;
-    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (lq == 0) red[w][16 * tt + li] = ss;
   }
   __syncthreads();
-  // epilogue: piece p = tid + 256 * it -> row p / 16, columns 8 * (p % 16) .. +8
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int pidx = tid + it * 256, t = pidx >> 4, sg = pidx & 15;
-    if (t >= len) continue;
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = 16 * tt + li;
     const float tot = red[0][t] + red[1][t] + red[2][t] + red[3][t];
     const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(tot * (1.0f / 128.0f) + a.norm_eps) : 1.0f;
-    float gl[8], o[8];
-    vec16<bf16>::cvt(gv[it], gl);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = Ys[t * kYLd + sg * 8 + e] * rs;
-      if (a.flags & GDN_NORM) v *= gain[e];
-      if (a.flags & GDN_GATE) v *= sigmoidf_(gl[e]);
-      o[e] = v;
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint2 gg = gv[tt][nt];
+      const float gl[4] = {__uint_as_float(gg.x << 16), __uint_as_float(gg.x & 0xffff0000u),
+                           __uint_as_float(gg.y << 16), __uint_as_float(gg.y & 0xffff0000u)};
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[tt][nt][r] * rs;
+        if (a.flags & GDN_NORM) v *= gain[nt][r];
+        if (a.flags & GDN_GATE) v *= sigmoidf_(gl[r]);
+        o[r] = v;
+      }
+      if (t < len)
+        *reinterpret_cast<uint2*>(a.out + (start + t) * orow + h * 128 + 32 * w + 16 * nt + 4 * lq) =
+            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     }
-    vec16<bf16>::st(reinterpret_cast<bf16*>(a.out + (start + t) * orow + h * 128 + sg * 8), o);
   }
 }
 
