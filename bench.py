@@ -134,8 +134,8 @@ def cpu_baseline(max_tokens: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--tokens", type=int, default=4096, help="prefill length (one sequence)")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--decode-batch", type=int, default=256)

@@ -32,7 +32,7 @@ struct OutArgs {
   float scale, norm_eps;
 };
 
-__global__ void __launch_bounds__(256) k_out(OutArgs a) {
+__global__ void __launch_bounds__(256, 4) k_out(OutArgs a) {
   // the R value heads of a QK head read the same q^ / k^ tiles: keep them on one XCD
   int u, hr;
   xcd_item(int(blockIdx.x), a.R, u, hr);
@@ -49,7 +49,7 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t QKs[2 * 64 * kLd];  // Q and K tiles
   uint16_t* Qs = QKs;
   uint16_t* Ks = QKs + 64 * kLd;
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[64 * kPLd];
+  uint16_t* Ps = Ks;  // P [64][kPLd] over the K tile once every wave is done with K
   __shared__ float Gs[64];
   __shared__ float red[4][64];
 
@@ -103,21 +103,26 @@ __global__ void __launch_bounds__(256) k_out(OutArgs a) {
   if (tid < 64) Gs[tid] = a.G[(int64_t(c) * a.hv + h) * 64 + tid];
   __syncthreads();
 
-  // P = L o E o (Q K^T) in bf16
+  // P = L o E o (Q K^T) in bf16, written over K once all waves are done reading it
+  f32x4 pacc[4];
+#pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    pacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (nt <= w) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        acc = mfma16x16x32(ld_short8(&Qs[(16 * w + li) * kLd + 32 * s + 8 * lq]),
-                           ld_short8(&Ks[(16 * nt + li) * kLd + 32 * s + 8 * lq]), acc);
+        pacc[nt] = mfma16x16x32(ld_short8(&Qs[(16 * w + li) * kLd + 32 * s + 8 * lq]),
+                                ld_short8(&Ks[(16 * nt + li) * kLd + 32 * s + 8 * lq]), pacc[nt]);
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * w + 4 * lq + r, i = 16 * nt + li;
-      Ps[t * kPLd + i] = f2bf(i <= t ? acc[r] * __expf(Gs[t] - Gs[i]) : 0.f);
+      Ps[t * kPLd + i] = f2bf(i <= t ? pacc[nt][r] * __expf(Gs[t] - Gs[i]) : 0.f);
     }
-  }
   __syncthreads();
 
   // Y^T: acc[tt][nt][r] is channel 32w + 16nt + 4lq + r of token 16tt + li
