@@ -145,7 +145,8 @@ gdn_status gdn_decode_step(const gdn_cfg* cfg, int32_t batch,
  * on this thread records events[i] on its stream before stage i and events[GDN_N_STAGES] after the
  * last stage, for the stages
  *   0 chunk table, 1 conv + SiLU + L2, 2 WY transform (or the token-sequential recurrence),
- *   3 state propagation, 4 output + RMSNorm + gate, 5 conv-cache tail;
+ *   3 state propagation, 4 output + RMSNorm + gate, 5 conv-cache tail (on the chunked path the
+ *   output stage writes the conv tail too);
  * stages a path does not run get back-to-back events. `events` holds GDN_N_STAGES + 1 hipEvent_t
  * handles created by the caller and must stay valid while set; NULL switches recording off.
  * Returns GDN_E_SHAPE if n_events != GDN_N_STAGES + 1. */

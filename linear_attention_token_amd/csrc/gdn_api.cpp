@@ -154,7 +154,7 @@ static bool launches_fit(const Problem& p) {
   const int64_t strips = (p.T + kConvStrip - 1) / kConvStrip;
   const int64_t cblk = ((p.C + vec - 1) / vec + 255) / 256;
   const int64_t conv = (int64_t(kXcds) * ((strips + kXcds - 1) / kXcds) * cblk + 1) * 256;
-  const int64_t chunks = xcd_blocks(p.nc_max * p.hk, p.hv / p.hk) * 256;
+  const int64_t chunks = (xcd_blocks(p.nc_max * p.hk, p.hv / p.hk) + int64_t(p.n_seqs) * cblk) * 256;
   return conv <= lim && chunks <= lim;
 }
 
@@ -248,17 +248,21 @@ gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
   GDN_STEP(0, hipSuccess, "")  // the chunk table is built inside the conv launch
   GDN_STEP(1, launch_conv(p, cu_seqlens, q, k, v, ld_q, ld_k, ld_v, conv_w, conv_in, ws, chunked, s), "conv")
   if (chunked) {
+    // the output kernel's extra blocks write the conv tail (conv_in is no longer read by then)
+    const ConvTailArgs tail = conv_tail_args(p, cu_seqlens, q, k, v, ld_q, ld_k, ld_v, conv_in, conv_out);
     GDN_STEP(2, any ? launch_wy(p, ws, alpha, beta, s) : hipSuccess, "wy")
     GDN_STEP(3, launch_state(p, ws, state_in, state_out, s), "state")
-    GDN_STEP(4, any ? launch_output(p, ws, gate, norm_w, out, s) : hipSuccess, "output")
+    GDN_STEP(4, any ? launch_output(p, ws, gate, norm_w, out, tail, s) : hipSuccess, "output")
+    GDN_STEP(5, (conv_out && !any) ? launch_conv_tail(p, cu_seqlens, q, k, v, ld_q, ld_k, ld_v, conv_in, conv_out, s)
+                                   : hipSuccess, "conv tail")
   } else {
     GDN_STEP(2, launch_sequential(p, cu_seqlens, ws, alpha, beta, gate, norm_w, state_in, state_out, out, s),
              "sequential")
     GDN_STEP(3, hipSuccess, "")
     GDN_STEP(4, hipSuccess, "")
+    GDN_STEP(5, conv_out ? launch_conv_tail(p, cu_seqlens, q, k, v, ld_q, ld_k, ld_v, conv_in, conv_out, s)
+                         : hipSuccess, "conv tail")
   }
-  GDN_STEP(5, conv_out ? launch_conv_tail(p, cu_seqlens, q, k, v, ld_q, ld_k, ld_v, conv_in, conv_out, s) : hipSuccess,
-           "conv tail")
   if (run(mark(GDN_N_STAGES, s), "event record") != hipSuccess) return GDN_E_HIP;
 #undef GDN_STEP
   return GDN_OK;

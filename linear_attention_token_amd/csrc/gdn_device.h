@@ -163,6 +163,36 @@ __device__ __forceinline__ void xcd_item(int b, int per_unit, int& unit, int& su
   sub = k - j * per_unit;
 }
 
+// One thread of the conv-cache tail (ConvTailArgs in gdn_internal.h): sequence n, channel group g.
+template <typename IO, typename A>
+__device__ __forceinline__ void conv_tail_piece(const A& a, int n, int64_t g) {
+  constexpr int VEC = vec16<IO>::N;
+  const int64_t c0 = g * VEC;
+  if (n >= a.n_seqs || c0 >= a.C) return;
+  const int64_t s0 = min<int64_t>(max<int64_t>(a.cu[n], 0), a.T);
+  const int64_t s1 = min<int64_t>(max<int64_t>(a.cu[n + 1], s0), a.T);
+  const IO* src;
+  int64_t ld;
+  if (c0 < a.qk_ch) { src = static_cast<const IO*>(a.q) + c0; ld = a.ld_q; }
+  else if (c0 < 2 * a.qk_ch) { src = static_cast<const IO*>(a.k) + (c0 - a.qk_ch); ld = a.ld_k; }
+  else { src = static_cast<const IO*>(a.v) + (c0 - 2 * a.qk_ch); ld = a.ld_v; }
+  const IO* cin = static_cast<const IO*>(a.conv_in);
+  IO* cout = static_cast<IO*>(a.conv_out);
+  float r[3][VEC];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int64_t pos = s1 - 3 + j;
+    if (pos >= s0) vec16<IO>::ld(src + pos * ld, r[j]);
+    else if (cin != nullptr) vec16<IO>::ld(cin + (int64_t(n) * 3 + (3 + (pos - s0))) * a.C + c0, r[j]);
+    else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) r[j][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) vec16<IO>::st(cout + (int64_t(n) * 3 + j) * a.C + c0, r[j]);
+}
+
 // Logistic function and SiLU on the hardware exp2 / reciprocal.
 __device__ __forceinline__ float sigmoidf_(float z) { return frcp(1.0f + __expf(-z)); }
 __device__ __forceinline__ float siluf_(float u) { return u * frcp(1.0f + __expf(-u)); }

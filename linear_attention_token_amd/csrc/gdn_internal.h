@@ -59,6 +59,29 @@ inline bool use_chunked(const Problem& p) { return p.bf16 && p.dk == 128 && p.dv
 // Carves `base` (may be null to only size it) into the regions the chosen path needs.
 Workspace plan_workspace(const Problem& p, void* base);
 
+// Conv-cache tail: conv_out[n][r] = the raw q/k/v input at position end - 3 + r of sequence n, or
+// the matching conv_in row when the sequence is shorter than 3 (zeros without conv_in). Work item
+// (n, channel group of 16 bytes); every thread reads its three rows before writing any, so
+// conv_out may alias conv_in. Run by the standalone tail kernel or by extra output-kernel blocks.
+struct ConvTailArgs {
+  const int32_t* cu;
+  int n_seqs;
+  int64_t T, C, qk_ch;
+  const void *q, *k, *v;
+  int64_t ld_q, ld_k, ld_v;
+  const void* conv_in;
+  void* conv_out;
+  int cblk;  // blocks of 256 channel groups per sequence
+};
+inline ConvTailArgs conv_tail_args(const Problem& p, const int32_t* cu, const void* q, const void* k,
+                                   const void* v, int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                                   const void* conv_in, void* conv_out) {
+  const int vec = p.bf16 ? 8 : 4;
+  const int64_t groups = (p.C + vec - 1) / vec;
+  return ConvTailArgs{cu, p.n_seqs, p.T, p.C, int64_t(p.hk) * p.dk, q, k, v, ld_q, ld_k, ld_v,
+                      conv_in, conv_out, int((groups + 255) / 256)};
+}
+
 // ---- launchers (each returns hipGetLastError() after its launches) ----
 hipError_t launch_conv(const Problem& p, const int32_t* cu, const void* q, const void* k, const void* v,
                        int64_t ld_q, int64_t ld_k, int64_t ld_v, const float* conv_w,
@@ -75,8 +98,9 @@ hipError_t launch_wy(const Problem& p, const Workspace& ws, const float* alpha, 
                      hipStream_t s);
 hipError_t launch_state(const Problem& p, const Workspace& ws, const float* state_in, float* state_out,
                         hipStream_t s);
+// also writes the conv tail when tail.conv_out is set
 hipError_t launch_output(const Problem& p, const Workspace& ws, const void* gate, const float* norm_w,
-                         void* out, hipStream_t s);
+                         void* out, const ConvTailArgs& tail, hipStream_t s);
 hipError_t launch_decode(const Problem& p, int batch, const void* q, const void* k, const void* v,
                          int64_t ld_q, int64_t ld_k, int64_t ld_v, const float* alpha, const float* beta,
                          const void* gate, const float* conv_w, const float* norm_w, void* conv_state,

@@ -246,56 +246,20 @@ hipError_t launch_conv(const Problem& p, const int32_t* cu, const void* q, const
 }
 
 // ------------------------------------------------------------------------------------------------
-// conv_out[n][r] = raw input at position end - 3 + r of sequence n, or the matching conv_in row when
-// the sequence is shorter than 3 (zeros without conv_in). All three rows are read before any is
-// written, so conv_out may alias conv_in.
+// Standalone conv-cache tail (the chunked path folds the same work into the output kernel).
 template <typename IO>
-__global__ void __launch_bounds__(256) k_conv_tail(const int32_t* __restrict__ cu, int n_seqs, int64_t T,
-                                                   int64_t C, int64_t qk_ch, const IO* q, const IO* k,
-                                                   const IO* v, int64_t ld_q, int64_t ld_k, int64_t ld_v,
-                                                   const IO* conv_in, IO* conv_out) {
-  constexpr int VEC = vec16<IO>::N;
-  const int n = blockIdx.x;
-  const int64_t c0 = (int64_t(blockIdx.y) * blockDim.x + threadIdx.x) * VEC;
-  if (c0 >= C) return;
-  const int64_t s0 = min<int64_t>(max<int64_t>(cu[n], 0), T);
-  const int64_t s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), T);
-  const IO* src;
-  int64_t ld;
-  if (c0 < qk_ch) { src = q + c0; ld = ld_q; }
-  else if (c0 < 2 * qk_ch) { src = k + (c0 - qk_ch); ld = ld_k; }
-  else { src = v + (c0 - 2 * qk_ch); ld = ld_v; }
-  float r[3][VEC];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int64_t pos = s1 - 3 + j;
-    if (pos >= s0) vec16<IO>::ld(src + pos * ld, r[j]);
-    else if (conv_in != nullptr) vec16<IO>::ld(conv_in + (int64_t(n) * 3 + (3 + (pos - s0))) * C + c0, r[j]);
-    else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) r[j][e] = 0.f;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 3; ++j) vec16<IO>::st(conv_out + (int64_t(n) * 3 + j) * C + c0, r[j]);
+__global__ void __launch_bounds__(256) k_conv_tail(ConvTailArgs a) {
+  conv_tail_piece<IO>(a, blockIdx.x, int64_t(blockIdx.y) * blockDim.x + threadIdx.x);
 }
 
 hipError_t launch_conv_tail(const Problem& p, const int32_t* cu, const void* q, const void* k,
                             const void* v, int64_t ld_q, int64_t ld_k, int64_t ld_v,
                             const void* conv_in, void* conv_out, hipStream_t s) {
   if (p.n_seqs == 0) return hipSuccess;
-  const int vec = p.bf16 ? 8 : 4;
-  const int64_t groups = (p.C + vec - 1) / vec;
-  dim3 grid(unsigned(p.n_seqs), unsigned((groups + 255) / 256));
-  const int64_t qk = int64_t(p.hk) * p.dk;
-  if (p.bf16)
-    hipLaunchKernelGGL(k_conv_tail<bf16>, grid, dim3(256), 0, s, cu, p.n_seqs, p.T, p.C, qk,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, ld_q, ld_k, ld_v,
-                       (const bf16*)conv_in, (bf16*)conv_out);
-  else
-    hipLaunchKernelGGL(k_conv_tail<float>, grid, dim3(256), 0, s, cu, p.n_seqs, p.T, p.C, qk,
-                       (const float*)q, (const float*)k, (const float*)v, ld_q, ld_k, ld_v,
-                       (const float*)conv_in, (float*)conv_out);
+  const ConvTailArgs a = conv_tail_args(p, cu, q, k, v, ld_q, ld_k, ld_v, conv_in, conv_out);
+  const dim3 grid(unsigned(p.n_seqs), unsigned(a.cblk));
+  if (p.bf16) hipLaunchKernelGGL(k_conv_tail<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_conv_tail<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ namespace gdn {
 struct OutArgs {
   const int4* tab;
   int n_units;                   // chunks x QK heads
+  int n_main;                    // blocks of the output proper; the rest write the conv tail
   int hk, hv, R;
   const uint16_t *qhat, *khat;   // bf16 [T][hk][128]
   const float* G;                // [nc][hv][64]
@@ -32,7 +33,12 @@ struct OutArgs {
   float scale, norm_eps;
 };
 
-__global__ void __launch_bounds__(256, 4) k_out(OutArgs a) {
+__global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
+  if (int(blockIdx.x) >= a.n_main) {  // conv-cache tail (no barrier below is reached)
+    const int b = int(blockIdx.x) - a.n_main, n = b / tail.cblk;
+    conv_tail_piece<bf16>(tail, n, int64_t(b - n * tail.cblk) * 256 + threadIdx.x);
+    return;
+  }
   // the R value heads of a QK head read the same q^ / k^ tiles: keep them on one XCD
   int u, hr;
   xcd_item(int(blockIdx.x), a.R, u, hr);
@@ -193,15 +199,17 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a) {
 }
 
 hipError_t launch_output(const Problem& p, const Workspace& ws, const void* gate, const float* norm_w,
-                         void* out, hipStream_t s) {
+                         void* out, const ConvTailArgs& tail, hipStream_t s) {
   if (p.nc_max == 0) return hipSuccess;
   const int R = p.hv / p.hk;
   const int64_t units = p.nc_max * p.hk;
-  OutArgs a{ws.chunk_tab, int(units), p.hk, p.hv, R, static_cast<const uint16_t*>(ws.qhat),
+  const int64_t n_main = xcd_blocks(units, R);
+  const int64_t n_tail = tail.conv_out != nullptr ? int64_t(tail.n_seqs) * tail.cblk : 0;
+  OutArgs a{ws.chunk_tab, int(units), int(n_main), p.hk, p.hv, R, static_cast<const uint16_t*>(ws.qhat),
             static_cast<const uint16_t*>(ws.khat), ws.G, ws.ST, ws.WT,
             static_cast<const uint16_t*>(gate), norm_w, p.norm_stride, static_cast<uint16_t*>(out),
             p.flags, p.scale, p.norm_eps};
-  hipLaunchKernelGGL(k_out, dim3(unsigned(xcd_blocks(units, R))), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_out, dim3(unsigned(n_main + n_tail)), dim3(256), 0, s, a, tail);
   return hipGetLastError();
 }
 
