@@ -107,6 +107,18 @@ __device__ __forceinline__ short8 ld_short8(const void* p) {
   return *reinterpret_cast<const short8*>(p);
 }
 
+// 16x16x16 bf16 MFMA, fp32 accumulate. A: row i, 4 consecutive k starting at 4q; B: column i, the
+// same 4 k; accumulator as above -- so an accumulator tile, rounded, is directly a B operand.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16x16x16(const short4v& a, const short4v& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ short4v ld_short4(const void* p) {
+  return *reinterpret_cast<const short4v*>(p);
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
@@ -153,6 +165,16 @@ __device__ __forceinline__ short8 pack8(const f32x4& a, const f32x4& b) {
   const u32x4v v = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
                     pack_bf16x2(b[2], b[3])};
   return __builtin_bit_cast(short8, v);
+}
+
+// One fp32 accumulator tile -> bf16 operand; two bf16 tiles -> one 16-byte piece.
+__device__ __forceinline__ short4v pack4(const f32x4& a) {
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  const u32x2v v = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+  return __builtin_bit_cast(short4v, v);
+}
+__device__ __forceinline__ short8 join8(const short4v& a, const short4v& b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Unit and position inside the unit of block b under the XCD-aware numbering (see xcd_blocks):

@@ -9,9 +9,12 @@
 // U and Wk depend only on the chunk, so every chunk is transformed in parallel here; the state
 // pass then needs only two products per chunk.
 //
-// Steps: k^ k^T on bf16 MFMA (fp32 accumulate) -> A in fp32 -> T by blocked forward substitution
-// in fp32 (16x16 diagonal blocks inverted per column, off-diagonal blocks merged with fp32 MFMA)
-// -> T diag(beta), T diag(beta gamma) rounded to bf16 -> U, Wk on bf16 MFMA.
+// Steps: k^ k^T on bf16 MFMA (fp32 accumulate) -> A; the 16x16 diagonal blocks of I + A inverted
+// in fp32 by forward substitution (D_i); then [U | Wk] solves (I + A) X = [diag(beta) V | diag(beta
+// gamma) K] by block forward substitution over the four 16-token blocks,
+//     X_i = D_i (B_i - sum_{k<i} A_ik X_k),
+// on bf16 MFMA (fp32 accumulate), each wave owning four of the sixteen 16-column tiles of X, so
+// the blocks X_k it needs stay in its registers.
 // Rows past the end of a partial chunk carry beta = 0 and ln alpha = 0, so their U and Wk rows are
 // zero and G stays at the last real token.
 //
@@ -35,36 +38,8 @@ struct WyArgs {
   uint16_t* KT;                   // [nc][hk][128][64]
 };
 
-constexpr int kKsLd = 144;   // bf16 row stride of the 64x128 k^ tile (and of T' / T'' later)
-constexpr int kKTLd = 72;    // bf16 row stride of the transposed 128x64 tiles
-constexpr int kFLd = 72;     // fp32 row stride of the 64x64 A and T matrices
-
-// T_ij = -D_i * sum_{k=j}^{i-1} A_ik T_kj for block row i > j (16x16 blocks), by one wave.
-__device__ __forceinline__ void wy_offdiag(const float* Am, float* Tm, float* X, int i, int j, int lane) {
-  const int li = lane & 15, lq = lane >> 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = j; kb < i; ++kb) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float av = Am[(16 * i + li) * kFLd + 16 * kb + 4 * kk + lq];
-      const float bv = Tm[(16 * kb + 4 * kk + lq) * kFLd + 16 * j + li];
-      acc = mfma16x16x4f32(av, bv, acc);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) X[(4 * lq + r) * 16 + li] = acc[r];
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
-  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const float av = Tm[(16 * i + li) * kFLd + 16 * i + 4 * kk + lq];
-    const float bv = X[(4 * kk + lq) * 16 + li];
-    acc2 = mfma16x16x4f32(av, bv, acc2);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) Tm[(16 * i + 4 * lq + r) * kFLd + 16 * j + li] = -acc2[r];
-}
+constexpr int kKsLd = 144;   // bf16 row stride of the 64x128 k^ tile
+constexpr int kKTLd = 72;    // bf16 row stride of the transposed 128x64 tiles and of -A
 
 // Block b works through the items b, b + gridDim.x, ... (one item = chunk, QK head and batch of
 // TEAMS value heads) with one block per CU; the raw inputs of its next item are loaded into
@@ -82,9 +57,11 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks_[64 * kKsLd];    // k^ rows
   __shared__ __attribute__((aligned(16))) uint16_t KTs_[128 * kKTLd];  // k^ transposed
-  __shared__ __attribute__((aligned(16))) float Am_[TEAMS][64 * kFLd];  // A; later T', T''; Wk staging
-  __shared__ __attribute__((aligned(16))) float Tm_[TEAMS][64 * kFLd];  // T; later V^ transposed
-  __shared__ float Xs_[TEAMS][4][256];
+  // per team: -A in bf16 with D_i on the diagonal blocks; A's diagonal blocks in fp32; V^
+  // transposed (later the Wk staging)
+  __shared__ __attribute__((aligned(16))) uint16_t Ab_[TEAMS][64 * kKTLd];
+  __shared__ __attribute__((aligned(16))) float Df_[TEAMS][4][16][16];
+  __shared__ __attribute__((aligned(16))) uint16_t VTs_[TEAMS][128 * kKTLd];
   __shared__ __attribute__((aligned(16))) float Gs_[TEAMS][64], Bs_[TEAMS][64], Cs_[TEAMS][64];
 
   // item -> chunk c, QK head g, this thread's value head h; chunk start and length
@@ -150,9 +127,9 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     const int li = lane & 15, lq = lane >> 4;
     uint16_t* const Ks = Ks_ + z;
     uint16_t* const KTs = KTs_ + z;
-    float* const Am = Am_[team] + z;
-    float* const Tm = Tm_[team] + z;
-    float (*const Xs)[256] = reinterpret_cast<float (*)[256]>(&Xs_[team][0][0] + z);
+    uint16_t* const Ab = Ab_[team] + z;
+    float (*const Df)[16][16] = reinterpret_cast<float (*)[16][16]>(&Df_[team][0][0][0] + z);
+    uint16_t* const VTs = VTs_[team] + z;
     float* const Gs = Gs_[team] + z;
     float* const Bs = Bs_[team] + z;
     float* const Cs = Cs_[team] + z;  // beta exp(G)
@@ -177,6 +154,17 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
       KTs[(sg * 8 + 2 * e + 1) * kKTLd + t] = uint16_t(wv[e] >> 16);
     }
   }
+  // V^ transposed, from this item's prefetched pieces
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int t = lane, sg = w + 4 * it;
+    const uint32_t wv[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      VTs[(sg * 8 + 2 * e) * kKTLd + t] = uint16_t(wv[e] & 0xffffu);
+      VTs[(sg * 8 + 2 * e + 1) * kKTLd + t] = uint16_t(wv[e] >> 16);
+    }
+  }
   if (w == 0) {
     float la = lane < len ? logf(la_raw) : 0.f;
     const float be = be_raw;
@@ -191,7 +179,8 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     a.G[(int64_t(c) * a.hv + h) * 64 + lane] = la;
   }
   __syncthreads();
-  fetch_k(item + gridDim.x);  // the next item's k^ flies while this one is transformed
+  fetch_k(item + gridDim.x);  // the next item's inputs fly while this one is transformed
+  fetch_v(item + gridDim.x);
 
   // K^T of the chunk for the state pass, written once per QK head
   if (hr == 0) {
@@ -204,119 +193,106 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     }
   }
 
-  // ---- Gram k^ k^T (lower block triangle) on MFMA -> A[t,i] = beta_t exp(G_t - G_i) k_t.k_i, i < t
+  // ---- Gram k^ k^T (lower block triangle) on MFMA; A[t,i] = beta_t exp(G_t - G_i) k_t.k_i, i < t:
+  // -A in bf16 for the off-diagonal blocks, A in fp32 for the diagonal ones
   for (int nt = 0; nt < 4; ++nt) {
+    if (nt > w) break;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (nt <= w) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const short8 av = ld_short8(&Ks[(16 * w + li) * kKsLd + 32 * s + 8 * lq]);
-        const short8 bv = ld_short8(&Ks[(16 * nt + li) * kKsLd + 32 * s + 8 * lq]);
-        acc = mfma16x16x32(av, bv, acc);
-      }
+    for (int s = 0; s < 4; ++s) {
+      const short8 av = ld_short8(&Ks[(16 * w + li) * kKsLd + 32 * s + 8 * lq]);
+      const short8 bv = ld_short8(&Ks[(16 * nt + li) * kKsLd + 32 * s + 8 * lq]);
+      acc = mfma16x16x32(av, bv, acc);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * w + 4 * lq + r, i = 16 * nt + li;
-      Am[t * kFLd + i] = (i < t) ? Bs[t] * __expf(Gs[t] - Gs[i]) * acc[r] : 0.f;
-    }
-  }
-
-  __syncthreads();
-
-  // ---- diagonal 16x16 blocks: D_w = (I + A_ww)^-1 by forward substitution, lane = column ----
-  {
-    const int b0 = 16 * w;
-    if (lane < 16) {
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < r; ++s) v -= Am[(b0 + r) * kFLd + b0 + s] * x[s];
-        x[r] = v;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * kFLd + b0 + lane] = x[r];
-    }
-    // zero the blocks above the diagonal in this block row
-    for (int idx = lane; idx < 16 * 64; idx += 64) {
-      const int r = idx >> 6, col = idx & 63;
-      if (col >= b0 + 16) Tm[(b0 + r) * kFLd + col] = 0.f;
+      const float av = (i < t) ? Bs[t] * __expf(Gs[t] - Gs[i]) * acc[r] : 0.f;
+      if (nt < w) Ab[t * kKTLd + i] = f2bf(-av);
+      else Df[w][4 * lq + r][li] = av;
     }
   }
   __syncthreads();
-  // ---- off-diagonal blocks, level by level ----
-  if (w < 3) wy_offdiag(Am, Tm, Xs[w], w + 1, w, lane);         // T10, T21, T32
-  __syncthreads();
-  if (w < 2) wy_offdiag(Am, Tm, Xs[w], w + 2, w, lane);         // T20, T31
-  __syncthreads();
-  if (w == 0) wy_offdiag(Am, Tm, Xs[w], 3, 0, lane);            // T30
+
+  // ---- D_w = (I + A_ww)^-1 by forward substitution, lane = column; into Ab's diagonal block ----
+  if (lane < 16) {
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) v -= Df[w][r][s] * x[s];
+      x[r] = v;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ab[(16 * w + r) * kKTLd + 16 * w + lane] = f2bf(x[r]);
+  }
   __syncthreads();
 
-  // ---- T' = T diag(beta), T'' = T diag(beta gamma) in bf16 over A; then V^ transposed over T ----
-  uint16_t* T1 = reinterpret_cast<uint16_t*>(Am);  // [64][72]
-  uint16_t* T2 = T1 + 64 * kKTLd;                  // [64][72]
+  // ---- X = [U | Wk] by block forward substitution. Wave w owns column tiles 4w .. 4w+3 of the 16:
+  // tiles 0-7 of U (source V^, row scale beta), tiles 8-15 of Wk (source K^, row scale beta gamma).
+  // A tile (rows 16i.., 16 columns) is kept as the bf16 MFMA operand xb[i][j]: lane (c, q) holds
+  // rows 16i + 4q .. +3 of column c, which is both the accumulator layout and the B-operand layout
+  // of the 16x16x16 MFMA.
+  const bool wk_tiles = w >= 2;
+  const uint16_t* src = wk_tiles ? KTs : VTs;  // transposed sources [column][token]
+  const float* rs = wk_tiles ? Cs : Bs;
+  const int col0 = 16 * (4 * w - (wk_tiles ? 8 : 0));  // first source column of this wave
+  short4v xb[4][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {  // 4 consecutive columns per thread and pass
-    const int idx = ttid + 256 * j, t = idx >> 4, i0 = (idx & 15) * 4;
-    const float4 tv = *reinterpret_cast<const float4*>(&Tm[t * kFLd + i0]);
-    const float4 b = *reinterpret_cast<const float4*>(&Bs[i0]);
-    const float4 cg = *reinterpret_cast<const float4*>(&Cs[i0]);
-    *reinterpret_cast<uint2*>(&T1[t * kKTLd + i0]) =
-        make_uint2(pack_bf16x2(tv.x * b.x, tv.y * b.y), pack_bf16x2(tv.z * b.z, tv.w * b.w));
-    *reinterpret_cast<uint2*>(&T2[t * kKTLd + i0]) =
-        make_uint2(pack_bf16x2(tv.x * cg.x, tv.y * cg.y), pack_bf16x2(tv.z * cg.z, tv.w * cg.w));
+  for (int i = 0; i < 4; ++i) {
+    const float4 sc = *reinterpret_cast<const float4*>(&rs[16 * i + 4 * lq]);
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 sv = *reinterpret_cast<const uint2*>(&src[(col0 + 16 * j + li) * kKTLd + 16 * i + 4 * lq]);
+      acc[j] = f32x4{__uint_as_float(sv.x << 16) * sc.x, __uint_as_float(sv.x & 0xffff0000u) * sc.y,
+                     __uint_as_float(sv.y << 16) * sc.z, __uint_as_float(sv.y & 0xffff0000u) * sc.w};
+    }
+#pragma unroll
+    for (int k = 0; k < i; ++k) {  // acc -= A_ik X_k  (Ab holds -A)
+      const short4v af = ld_short4(&Ab[(16 * i + li) * kKTLd + 16 * k + 4 * lq]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x16(af, xb[k][j], acc[j]);
+    }
+    const short4v df = ld_short4(&Ab[(16 * i + li) * kKTLd + 16 * i + 4 * lq]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = mfma16x16x16(df, pack4(acc[j]), f32x4{0.f, 0.f, 0.f, 0.f});
+      xb[i][j] = pack4(x);
+    }
   }
-  __syncthreads();  // T is read completely
-  uint16_t* VTs = reinterpret_cast<uint16_t*>(Tm);  // [128][72]
+
+  // U goes out in its accumulator layout with tiles paired, [row block][tile pair][lane][2][4],
+  // which is how the state pass consumes it (16 contiguous bytes per lane)
+  if (!wk_tiles) {
+    uint16_t* Ug = a.U + (int64_t(c) * a.hv + h) * 64 * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp)
+        *reinterpret_cast<short8*>(Ug + ((i * 4 + 2 * w + jp) * 64 + lane) * 8) = join8(xb[i][2 * jp], xb[i][2 * jp + 1]);
+  }
+  __syncthreads();  // V^ transposed is dead: stage Wk over it
+  uint16_t* Ws = VTs;  // [64][136]
+  constexpr int kOLd = 136;
+  if (wk_tiles) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Ws[(16 * i + 4 * lq + r) * kOLd + col0 + 16 * j + li] = uint16_t(xb[i][j][r]);
+  }
+  __syncthreads();
+  uint16_t* Wg = a.Wk + (int64_t(c) * a.hv + h) * 64 * 128;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int t = lane, sg = w + 4 * it;
-    const uint32_t wv[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      VTs[(sg * 8 + 2 * e) * kKTLd + t] = uint16_t(wv[e] & 0xffffu);
-      VTs[(sg * 8 + 2 * e + 1) * kKTLd + t] = uint16_t(wv[e] >> 16);
-    }
+    const int idx = ttid + it * 256;
+    const int t = idx >> 4, sg = idx & 15;
+    *reinterpret_cast<uint4*>(Wg + t * 128 + sg * 8) = *reinterpret_cast<const uint4*>(&Ws[t * kOLd + sg * 8]);
   }
-  __syncthreads();
-
-  // ---- U = T' V^, then Wk = T'' K^  (rows 16w.., all 128 columns), one accumulator set at a time
-  f32x4 acc[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const short8 a1 = ld_short8(&T1[(16 * w + li) * kKTLd + 32 * s + 8 * lq]);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      acc[nt] = mfma16x16x32(a1, ld_short8(&VTs[(16 * nt + li) * kKTLd + 32 * s + 8 * lq]), acc[nt]);
-  }
-  fetch_v(item + gridDim.x);  // V^ of this item is in LDS; the next item's flies meanwhile
-  // U goes out in this accumulator layout, tiles paired: [wave][tile pair][lane][2 tiles][4 rows],
-  // which is how the state pass consumes it (16 contiguous bytes per lane)
-  uint16_t* Ug = a.U + (int64_t(c) * a.hv + h) * 64 * 128;
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-    *reinterpret_cast<uint4*>(Ug + ((w * 4 + p) * 64 + lane) * 8) =
-        make_uint4(pack_bf16x2(acc[2 * p][0], acc[2 * p][1]), pack_bf16x2(acc[2 * p][2], acc[2 * p][3]),
-                   pack_bf16x2(acc[2 * p + 1][0], acc[2 * p + 1][1]),
-                   pack_bf16x2(acc[2 * p + 1][2], acc[2 * p + 1][3]));
-  // Wk^T = K^T T''^T with the rows of K^T (channels) in the order pi: accumulator tiles 2s, 2s + 1
-  // of lane (token 16w + li, lq) hold Wk[token][32s + 8lq .. +7], stored as one 16-byte piece
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const short8 b2 = ld_short8(&T2[(16 * w + li) * kKTLd + 32 * s + 8 * lq]);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      acc[nt] = mfma16x16x32(ld_short8(&KTs[pi32(16 * nt + li) * kKTLd + 32 * s + 8 * lq]), b2, acc[nt]);
-  }
-  uint16_t* Wg = a.Wk + (int64_t(c) * a.hv + h) * 64 * 128 + (16 * w + li) * 128 + 8 * lq;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) *reinterpret_cast<short8*>(Wg + 32 * s) = pack8(acc[2 * s], acc[2 * s + 1]);
   __syncthreads();  // every read of this item's LDS is done before the next item overwrites it
   }  // items
 }
