@@ -167,6 +167,17 @@ __device__ __forceinline__ short8 pack8(const f32x4& a, const f32x4& b) {
   return __builtin_bit_cast(short8, v);
 }
 
+// Buffer loads: a wave-uniform base and size in SGPRs, a 32-bit byte offset per lane and a
+// constant (SGPR) offset per access, so a run of loads at fixed distances needs one address
+// register. Out-of-range accesses read zero.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ float4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // One fp32 accumulator tile -> bf16 operand; two bf16 tiles -> one 16-byte piece.
 __device__ __forceinline__ short4v pack4(const f32x4& a) {
   typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));

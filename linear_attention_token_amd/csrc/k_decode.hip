@@ -166,6 +166,146 @@ __global__ void __launch_bounds__(768) k_decode(DecodeArgs a) {
   }
 }
 
+// Head size 128 (the model's): one block of 256 threads per (sequence, QK group), which walks the
+// group's value heads one after another. Thread (cg, rg) = (t % 32, t / 32) holds columns 4cg .. +3
+// of rows rg + 8j (j < 16) of a head's state, so one load instruction of a wave reads two adjacent
+// 512-byte rows. The first head's state is requested before the conv runs; several blocks share a
+// CU (at most 128 registers per thread), so one block's loads overlap another's reductions and
+// stores, and no CU waits on a block-wide phase.
+constexpr int kD = 128;
+
+template <typename IO>
+__global__ void __launch_bounds__(256, 4) k_decode_d128(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int cg = t & 31, rg = t >> 5, col = 4 * cg;
+  const int R = a.R;
+  float* act = smem;                // [(2 + R) * 128]: q | k | v of the group's heads, after conv + SiLU
+  float* red = smem + (2 + R) * kD;  // [2 buffers][4 waves][a, b][128]
+  __shared__ float nrm[8];
+
+  const size_t head = size_t(kD) * kD;
+  float* const S0 = a.state + (size_t(b) * a.hv + size_t(g) * R) * head;
+  const int soff = (rg * kD + col) * 4;  // row j of this thread: soff + 4096 j bytes into the head
+  float4 S[16];
+  {
+    const auto rs = buf_rsrc(S0, int(head * 4));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) S[j] = buf_ld16(rs, soff, 4096 * j);
+  }
+
+  // ---- conv + SiLU of the group's channels (single writer of their cache) ----
+  const int64_t qk_ch = int64_t(a.hk) * kD;
+  auto conv1 = [&](int64_t gc, const IO* src) -> float {
+    const float x = io<IO>::ld(src);
+    if (!(a.flags & GDN_CONV)) return x;
+    IO* cs = static_cast<IO*>(a.conv_state) + int64_t(b) * 3 * a.C + gc;
+    const float h0 = io<IO>::ld(cs), h1 = io<IO>::ld(cs + a.C), h2 = io<IO>::ld(cs + 2 * a.C);
+    const float4 cw = reinterpret_cast<const float4*>(a.conv_w)[gc];
+    io<IO>::st(cs, h1);
+    io<IO>::st(cs + a.C, h2);
+    io<IO>::st(cs + 2 * a.C, x);
+    return siluf_(cw.x * h0 + cw.y * h1 + cw.z * h2 + cw.w * x);
+  };
+  float u;
+  if (t < kD) u = conv1(int64_t(g) * kD + t, static_cast<const IO*>(a.q) + int64_t(b) * a.ld_q + g * kD + t);
+  else u = conv1(qk_ch + int64_t(g) * kD + (t - kD), static_cast<const IO*>(a.k) + int64_t(b) * a.ld_k + g * kD + (t - kD));
+  act[t] = u;
+  for (int c = t; c < R * kD; c += 256)
+    act[2 * kD + c] = conv1(2 * qk_ch + int64_t(g) * R * kD + c,
+                            static_cast<const IO*>(a.v) + int64_t(b) * a.ld_v + int64_t(g) * R * kD + c);
+  // |q|^2 (waves 0, 1) and |k|^2 (waves 2, 3), then q.k
+  {
+    const float ss = group_sum<64>(u * u);
+    if (lane == 0) nrm[w] = ss;
+  }
+  __syncthreads();
+  if (t < kD) {
+    const float d = group_sum<64>(u * act[kD + t]);
+    if (lane == 0) nrm[4 + w] = d;
+  }
+  __syncthreads();
+  const bool l2 = (a.flags & GDN_L2QK) != 0;
+  const float rq = l2 ? 1.0f / sqrtf(nrm[0] + nrm[1] + a.l2_eps) : 1.0f;
+  const float rk = l2 ? 1.0f / sqrtf(nrm[2] + nrm[3] + a.l2_eps) : 1.0f;
+  const float qk = (nrm[4] + nrm[5]) * rq * rk;
+
+  for (int r = 0; r < R; ++r) {
+    const int h = g * R + r;
+    const auto rs = buf_rsrc(S0 + size_t(r) * head, int(head * 4));
+    const float al = a.alpha[size_t(b) * a.hv + h], be = a.beta[size_t(b) * a.hv + h];
+    float gt[4] = {0.f, 0.f, 0.f, 0.f};
+    if ((a.flags & GDN_GATE) && rg == 0) {
+      const IO* gp = static_cast<const IO*>(a.gate) + (size_t(b) * a.hv + h) * kD + col;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gt[e] = io<IO>::ld(gp + e);
+    }
+    if (r > 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) S[j] = buf_ld16(rs, soff, 4096 * j);
+    }
+    // a = S^T k^, b = S^T q^ over this thread's rows, then over the 8 row groups
+    float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float qi = act[rg + 8 * j], ki = act[kD + rg + 8 * j];
+      pa.x += S[j].x * ki; pa.y += S[j].y * ki; pa.z += S[j].z * ki; pa.w += S[j].w * ki;
+      pb.x += S[j].x * qi; pb.y += S[j].y * qi; pb.z += S[j].z * qi; pb.w += S[j].w * qi;
+    }
+    pa.x += __shfl_xor(pa.x, 32, 64); pa.y += __shfl_xor(pa.y, 32, 64);
+    pa.z += __shfl_xor(pa.z, 32, 64); pa.w += __shfl_xor(pa.w, 32, 64);
+    pb.x += __shfl_xor(pb.x, 32, 64); pb.y += __shfl_xor(pb.y, 32, 64);
+    pb.z += __shfl_xor(pb.z, 32, 64); pb.w += __shfl_xor(pb.w, 32, 64);
+    float* const rb = red + (r & 1) * (8 * kD);  // two buffers: one barrier per head suffices
+    if (lane < 32) {
+      *reinterpret_cast<float4*>(&rb[(2 * w) * kD + col]) = pa;
+      *reinterpret_cast<float4*>(&rb[(2 * w + 1) * kD + col]) = pb;
+    }
+    __syncthreads();
+    float av[4] = {0.f, 0.f, 0.f, 0.f}, bv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float4 x = *reinterpret_cast<const float4*>(&rb[(2 * ww) * kD + col]);
+      const float4 y = *reinterpret_cast<const float4*>(&rb[(2 * ww + 1) * kD + col]);
+      av[0] += x.x; av[1] += x.y; av[2] += x.z; av[3] += x.w;
+      bv[0] += y.x; bv[1] += y.y; bv[2] += y.z; bv[3] += y.w;
+    }
+    float ev[4], y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ev[e] = act[(2 + r) * kD + col + e] - al * (av[e] * rk);
+      y[e] = a.scale * (al * (bv[e] * rq) + be * qk * ev[e]);
+    }
+    // S <- alpha S + beta k^ e^T. Written with global stores: buffer stores whose data registers
+    // the compiler refills right after issue were seen to lose single dwords on gfx950.
+    float* const Sp = S0 + size_t(r) * head;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float bk = be * rk * act[kD + rg + 8 * j];
+      float4 o;
+      o.x = al * S[j].x + bk * ev[0];
+      o.y = al * S[j].y + bk * ev[1];
+      o.z = al * S[j].z + bk * ev[2];
+      o.w = al * S[j].w + bk * ev[3];
+      *reinterpret_cast<float4*>(Sp + (rg + 8 * j) * kD + col) = o;
+    }
+    // RMSNorm over the head's 128 outputs (the 32 lanes of a row group hold them all), gain, gate
+    const float ss = group_sum<32>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
+    if (rg == 0) {
+      const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(ss / float(kD) + a.norm_eps) : 1.0f;
+      IO* op = static_cast<IO*>(a.out) + (size_t(b) * a.hv + h) * kD + col;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float o = y[e];
+        if (a.flags & GDN_NORM) o = o * rs * (1.0f + a.norm_w[size_t(h) * a.norm_stride + col + e]);
+        if (a.flags & GDN_GATE) o *= sigmoidf_(gt[e]);
+        io<IO>::st(op + e, o);
+      }
+    }
+  }
+}
+
 size_t decode_smem_bytes(const Problem& p, int teams) {
   const int R = p.hv / p.hk;
   const int nch = 2 * p.dk + R * p.dv;
@@ -182,8 +322,14 @@ hipError_t launch_decode(const Problem& p, int batch, const void* q, const void*
   DecodeArgs a{batch, p.hk, p.hv, p.dk, p.dv, R, teams, p.C, q, k, v, ld_q, ld_k, ld_v, alpha, beta,
                gate, conv_w, norm_w, p.norm_stride, conv_state, state, out, p.flags, p.scale,
                p.l2_eps, p.norm_eps};
-  const size_t smem = decode_smem_bytes(p, teams);
   dim3 grid(unsigned(batch), unsigned(p.hk));
+  if (p.dk == kD && p.dv == kD) {
+    const size_t smem = size_t(2 + R) * kD * 4 + 8 * kD * 4 * 2;
+    if (p.bf16) hipLaunchKernelGGL(k_decode_d128<bf16>, grid, dim3(256), smem, s, a);
+    else hipLaunchKernelGGL(k_decode_d128<float>, grid, dim3(256), smem, s, a);
+    return hipGetLastError();
+  }
+  const size_t smem = decode_smem_bytes(p, teams);
   if (p.bf16) hipLaunchKernelGGL(k_decode<bf16>, grid, dim3(kTeam * teams), smem, s, a);
   else hipLaunchKernelGGL(k_decode<float>, grid, dim3(kTeam * teams), smem, s, a);
   return hipGetLastError();

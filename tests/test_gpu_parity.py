@@ -268,6 +268,43 @@ def test_decode_small(io):
     assert torch.equal(cv, x_last.transpose(0, 1))
 
 
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("hk,hv", [(1, 1), (2, 4), (1, 5)])
+@pytest.mark.parametrize("flags", [gdn.GDN_ALL, gdn.GDN_CONV | gdn.GDN_L2QK, gdn.GDN_L2QK])
+def test_decode_d128_head_ratios(io, hk, hv, flags):
+    """Head size 128 (the dedicated decode kernel): value heads per QK head 1, 2 and 5 (the v
+    channels of a group span more than one pass of the block), every flag subset the kernel
+    branches on, fp32 and bf16 io; the conv cache ends as the last three raw inputs."""
+    B, steps = 3, 4
+    di = decode_inputs(B, steps, n_qk_heads=hk, n_v_heads=hv, d_k=128, d_v=128, io_dtype=io, device=DEV,
+                       seed=29 + hv, state_std=0.05)
+    outs, st, cv = _decode_steps(di, steps, flags=flags)
+    tol = TOL[io]
+    for b in range(B):
+        ref = _oracle_decode_seq(di, b, steps, flags=flags)
+        for h, (o_ref, s_ref) in ref.items():
+            e_o, e_s = rel_l2(outs[:, b, h], o_ref), rel_l2(st[b, h], s_ref)
+            assert e_o <= tol and e_s <= tol, (b, h, e_o, e_s)
+    if flags & gdn.GDN_CONV:
+        x_last = torch.cat([di.q[steps - 3:steps].reshape(3, B, -1), di.k[steps - 3:steps].reshape(3, B, -1),
+                            di.v[steps - 3:steps].reshape(3, B, -1)], -1)
+        assert torch.equal(cv, x_last.transpose(0, 1))
+
+
+def test_decode_model_shape_fp32_every_head():
+    """One fp32 step at B=256, model shape: every value head of a sample of sequences to 1e-4, so a
+    single wrong element of the 128x128 state of any head fails."""
+    di = decode_inputs(256, 1, n_qk_heads=16, n_v_heads=48, d_k=128, d_v=128, io_dtype=torch.float32,
+                       device=DEV, seed=5)
+    outs, st, _ = _decode_steps(di, 1)
+    for b in range(0, 256, 5):
+        ref = _oracle_decode_seq(di, b, 1)
+        for h, (o_ref, s_ref) in ref.items():
+            e_o, e_s = rel_l2(outs[:, b, h], o_ref), rel_l2(st[b, h], s_ref)
+            assert e_o <= 1e-4 and e_s <= 1e-4, (b, h, e_o, e_s)
+            assert np.max(np.abs(st[b, h].double().cpu().numpy() - s_ref)) <= 1e-5 * np.max(np.abs(s_ref))
+
+
 def test_decode_model_shape():
     """B=256 at model shape: all sequences for 8 steps, and 4 sequences x 48 heads over 1000 steps."""
     di = decode_inputs(256, 1000, n_qk_heads=16, n_v_heads=48, d_k=128, d_v=128, io_dtype=torch.bfloat16,
