@@ -302,6 +302,8 @@ gdn_status gdn_decode_step(const gdn_cfg* cfg, int32_t batch,
     if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
   if (!aligned4(alpha) || !aligned4(beta)) return fail(GDN_E_ALIGN, "alpha and beta must be 4-byte aligned");
   if (p.hv / p.hk > 64) return fail(GDN_E_UNSUPPORTED, "HV/HK = %d > 64", p.hv / p.hk);
+  if (int64_t(batch) * p.hk * 768 > int64_t(UINT32_MAX))
+    return fail(GDN_E_UNSUPPORTED, "batch x QK heads = %lld is too large for one launch", (long long)batch * p.hk);
   if (batch == 0) return GDN_OK;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   if (run(launch_decode(p, batch, q, k, v, ld_q, ld_k, ld_v, alpha, beta, gate, conv_w, norm_w, conv_state,

@@ -169,52 +169,94 @@ __global__ void __launch_bounds__(768) k_decode(DecodeArgs a) {
 // Head size 128 (the model's): one block of 256 threads per (sequence, QK group), which walks the
 // group's value heads one after another. Thread (cg, rg) = (t % 32, t / 32) holds columns 4cg .. +3
 // of rows rg + 8j (j < 16) of a head's state, so one load instruction of a wave reads two adjacent
-// 512-byte rows. The first head's state is requested before the conv runs; several blocks share a
-// CU (at most 128 registers per thread), so one block's loads overlap another's reductions and
-// stores, and no CU waits on a block-wide phase.
+// 512-byte rows. The first head's state is requested before the conv runs and each next head's
+// before the current one is reduced, so a block always has a state in flight; two blocks share a
+// CU. State is streamed with non-temporal loads and stores (each byte is touched once per step).
 constexpr int kD = 128;
 
 template <typename IO>
-__global__ void __launch_bounds__(256, 4) k_decode_d128(DecodeArgs a) {
+__global__ void __launch_bounds__(256, 2) k_decode_d128(DecodeArgs a) {
   extern __shared__ float smem[];
-  const int b = blockIdx.x, g = blockIdx.y;
+  // block = b * hk + g: consecutive blocks stream consecutive 192 KB pieces of the state
+  const int b = int(blockIdx.x / unsigned(a.hk)), g = int(blockIdx.x - unsigned(b) * unsigned(a.hk));
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int cg = t & 31, rg = t >> 5, col = 4 * cg;
   const int R = a.R;
-  float* act = smem;                // [(2 + R) * 128]: q | k | v of the group's heads, after conv + SiLU
-  float* red = smem + (2 + R) * kD;  // [2 buffers][4 waves][a, b][128]
+  float* act = smem;                    // [(2 + R) * 128]: q | k | v of the group's heads, after conv + SiLU
+  float* red = smem + (2 + 2 * R) * kD;  // [2 buffers][4 waves][a, b][128]
   __shared__ float nrm[8];
 
   const size_t head = size_t(kD) * kD;
   float* const S0 = a.state + (size_t(b) * a.hv + size_t(g) * R) * head;
   const int soff = (rg * kD + col) * 4;  // row j of this thread: soff + 4096 j bytes into the head
-  float4 S[16];
+  float4 S[16], N[16];  // this head's state and the next head's, in flight meanwhile
   {
     const auto rs = buf_rsrc(S0, int(head * 4));
 #pragma unroll
-    for (int j = 0; j < 16; ++j) S[j] = buf_ld16(rs, soff, 4096 * j);
+    for (int j = 0; j < 16; ++j) S[j] = buf_ld16_nt(rs, soff, 4096 * j);
   }
 
-  // ---- conv + SiLU of the group's channels (single writer of their cache) ----
+  // ---- conv + SiLU of the group's channels (single writer of their cache) and the group's gate
+  // logits. A pass covers 768 channels (all of them for up to 4 value heads per group) and issues
+  // every load before the first use, so the pass costs one memory round trip ----
+  const int nch = (2 + R) * kD, nv = R * kD;
+  float* const gsh = act + nch;  // [R * 128] gate logits
   const int64_t qk_ch = int64_t(a.hk) * kD;
-  auto conv1 = [&](int64_t gc, const IO* src) -> float {
-    const float x = io<IO>::ld(src);
-    if (!(a.flags & GDN_CONV)) return x;
-    IO* cs = static_cast<IO*>(a.conv_state) + int64_t(b) * 3 * a.C + gc;
-    const float h0 = io<IO>::ld(cs), h1 = io<IO>::ld(cs + a.C), h2 = io<IO>::ld(cs + 2 * a.C);
-    const float4 cw = reinterpret_cast<const float4*>(a.conv_w)[gc];
-    io<IO>::st(cs, h1);
-    io<IO>::st(cs + a.C, h2);
-    io<IO>::st(cs + 2 * a.C, x);
-    return siluf_(cw.x * h0 + cw.y * h1 + cw.z * h2 + cw.w * x);
-  };
-  float u;
-  if (t < kD) u = conv1(int64_t(g) * kD + t, static_cast<const IO*>(a.q) + int64_t(b) * a.ld_q + g * kD + t);
-  else u = conv1(qk_ch + int64_t(g) * kD + (t - kD), static_cast<const IO*>(a.k) + int64_t(b) * a.ld_k + g * kD + (t - kD));
-  act[t] = u;
-  for (int c = t; c < R * kD; c += 256)
-    act[2 * kD + c] = conv1(2 * qk_ch + int64_t(g) * R * kD + c,
-                            static_cast<const IO*>(a.v) + int64_t(b) * a.ld_v + int64_t(g) * R * kD + c);
+  const bool conv = (a.flags & GDN_CONV) != 0, gate = (a.flags & GDN_GATE) != 0;
+  const IO* const gsrc = static_cast<const IO*>(a.gate) + (size_t(b) * a.hv + size_t(g) * R) * kD;  // [R * 128]
+  // Loads are issued unconditionally from clamped (always valid) addresses and converted only after
+  // the whole pass is in flight; lanes past the end discard their values.
+  float gv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) gv[u] = io<IO>::ld(gsrc + min(t + 256 * u, nv - 1));
+  float u_qk = 0.f;  // this thread's q (t < 128) or k channel after conv + SiLU
+  for (int c0 = 0; c0 < nch; c0 += 768) {
+    float x[3], h[3][3];
+    float4 cw[3];
+    int64_t gcs[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int c = min(c0 + t + 256 * u, nch - 1);
+      const bool isq = c < kD, isk = !isq && c < 2 * kD;
+      const int cc = isq ? c : isk ? c - kD : c - 2 * kD;
+      gcs[u] = (isq ? int64_t(0) : isk ? qk_ch : 2 * qk_ch) + int64_t(g) * (isq || isk ? kD : nv) + cc;
+      const IO* src = isq ? static_cast<const IO*>(a.q) + int64_t(b) * a.ld_q + g * kD
+                    : isk ? static_cast<const IO*>(a.k) + int64_t(b) * a.ld_k + g * kD
+                          : static_cast<const IO*>(a.v) + int64_t(b) * a.ld_v + int64_t(g) * nv;
+      x[u] = io<IO>::ld(src + cc);
+      // without the conv the cache and weights may be absent: read valid stand-ins instead
+      const IO* cs = conv ? static_cast<const IO*>(a.conv_state) + int64_t(b) * 3 * a.C + gcs[u] : src + cc;
+      const int64_t cstep = conv ? a.C : 0;
+      h[u][0] = io<IO>::ld(cs);
+      h[u][1] = io<IO>::ld(cs + cstep);
+      h[u][2] = io<IO>::ld(cs + 2 * cstep);
+      cw[u] = conv ? reinterpret_cast<const float4*>(a.conv_w)[gcs[u]] : *reinterpret_cast<const float4*>(S0);
+    }
+    asm volatile("" ::: "memory");  // keeps the loads above from being sunk into the branches below
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int c = c0 + t + 256 * u;
+      if (c < nch) {
+        float val = x[u];
+        if (conv) {
+          IO* cs = static_cast<IO*>(a.conv_state) + int64_t(b) * 3 * a.C + gcs[u];
+          io<IO>::st(cs, h[u][1]);
+          io<IO>::st(cs + a.C, h[u][2]);
+          io<IO>::st(cs + 2 * a.C, x[u]);
+          val = siluf_(cw[u].x * h[u][0] + cw[u].y * h[u][1] + cw[u].z * h[u][2] + cw[u].w * x[u]);
+        }
+        act[c] = val;
+        if (c0 == 0 && u == 0) u_qk = val;
+      }
+    }
+  }
+  if (gate) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (t + 256 * u < nv) gsh[t + 256 * u] = gv[u];
+    for (int c = t + 512; c < nv; c += 256) gsh[c] = io<IO>::ld(gsrc + c);
+  }
+  const float u = u_qk;
   // |q|^2 (waves 0, 1) and |k|^2 (waves 2, 3), then q.k
   {
     const float ss = group_sum<64>(u * u);
@@ -233,17 +275,11 @@ __global__ void __launch_bounds__(256, 4) k_decode_d128(DecodeArgs a) {
 
   for (int r = 0; r < R; ++r) {
     const int h = g * R + r;
-    const auto rs = buf_rsrc(S0 + size_t(r) * head, int(head * 4));
     const float al = a.alpha[size_t(b) * a.hv + h], be = a.beta[size_t(b) * a.hv + h];
-    float gt[4] = {0.f, 0.f, 0.f, 0.f};
-    if ((a.flags & GDN_GATE) && rg == 0) {
-      const IO* gp = static_cast<const IO*>(a.gate) + (size_t(b) * a.hv + h) * kD + col;
+    if (r + 1 < R) {
+      const auto rn = buf_rsrc(S0 + size_t(r + 1) * head, int(head * 4));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gt[e] = io<IO>::ld(gp + e);
-    }
-    if (r > 0) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) S[j] = buf_ld16(rs, soff, 4096 * j);
+      for (int j = 0; j < 16; ++j) N[j] = buf_ld16_nt(rn, soff, 4096 * j);
     }
     // a = S^T k^, b = S^T q^ over this thread's rows, then over the 8 row groups
     float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa;
@@ -288,8 +324,10 @@ __global__ void __launch_bounds__(256, 4) k_decode_d128(DecodeArgs a) {
       o.y = al * S[j].y + bk * ev[1];
       o.z = al * S[j].z + bk * ev[2];
       o.w = al * S[j].w + bk * ev[3];
-      *reinterpret_cast<float4*>(Sp + (rg + 8 * j) * kD + col) = o;
+      __builtin_nontemporal_store(__builtin_bit_cast(f32x4, o), reinterpret_cast<f32x4*>(Sp + (rg + 8 * j) * kD + col));
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) S[j] = N[j];
     // RMSNorm over the head's 128 outputs (the 32 lanes of a row group hold them all), gain, gate
     const float ss = group_sum<32>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
     if (rg == 0) {
@@ -299,7 +337,7 @@ __global__ void __launch_bounds__(256, 4) k_decode_d128(DecodeArgs a) {
       for (int e = 0; e < 4; ++e) {
         float o = y[e];
         if (a.flags & GDN_NORM) o = o * rs * (1.0f + a.norm_w[size_t(h) * a.norm_stride + col + e]);
-        if (a.flags & GDN_GATE) o *= sigmoidf_(gt[e]);
+        if (gate) o *= sigmoidf_(gsh[r * kD + col + e]);
         io<IO>::st(op + e, o);
       }
     }
@@ -324,9 +362,10 @@ hipError_t launch_decode(const Problem& p, int batch, const void* q, const void*
                p.l2_eps, p.norm_eps};
   dim3 grid(unsigned(batch), unsigned(p.hk));
   if (p.dk == kD && p.dv == kD) {
-    const size_t smem = size_t(2 + R) * kD * 4 + 8 * kD * 4 * 2;
-    if (p.bf16) hipLaunchKernelGGL(k_decode_d128<bf16>, grid, dim3(256), smem, s, a);
-    else hipLaunchKernelGGL(k_decode_d128<float>, grid, dim3(256), smem, s, a);
+    const size_t smem = size_t(2 + 2 * R) * kD * 4 + 8 * kD * 4 * 2;
+    const dim3 grid1(unsigned(batch) * unsigned(p.hk));
+    if (p.bf16) hipLaunchKernelGGL(k_decode_d128<bf16>, grid1, dim3(256), smem, s, a);
+    else hipLaunchKernelGGL(k_decode_d128<float>, grid1, dim3(256), smem, s, a);
     return hipGetLastError();
   }
   const size_t smem = decode_smem_bytes(p, teams);

@@ -269,12 +269,14 @@ def test_decode_small(io):
 
 
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("hk,hv", [(1, 1), (2, 4), (1, 5)])
-@pytest.mark.parametrize("flags", [gdn.GDN_ALL, gdn.GDN_CONV | gdn.GDN_L2QK, gdn.GDN_L2QK])
+@pytest.mark.parametrize("hk,hv,flags", [(1, 1, gdn.GDN_ALL), (2, 4, gdn.GDN_ALL), (1, 5, gdn.GDN_ALL),
+                                         (1, 1, gdn.GDN_CONV | gdn.GDN_L2QK), (2, 4, gdn.GDN_CONV | gdn.GDN_L2QK),
+                                         (1, 5, gdn.GDN_L2QK), (2, 4, gdn.GDN_L2QK), (1, 64, gdn.GDN_ALL)])
 def test_decode_d128_head_ratios(io, hk, hv, flags):
-    """Head size 128 (the dedicated decode kernel): value heads per QK head 1, 2 and 5 (the v
-    channels of a group span more than one pass of the block), every flag subset the kernel
-    branches on, fp32 and bf16 io; the conv cache ends as the last three raw inputs."""
+    """Head size 128 (the dedicated decode kernel): value heads per QK head 1, 2, 5 (the v channels
+    of a group span more than one load pass of the block) and 64 (the largest ratio, the most
+    LDS), the flag subsets the kernel branches on, fp32 and bf16 io; the conv cache ends as the
+    last three raw inputs."""
     B, steps = 3, 4
     di = decode_inputs(B, steps, n_qk_heads=hk, n_v_heads=hv, d_k=128, d_v=128, io_dtype=io, device=DEV,
                        seed=29 + hv, state_std=0.05)
