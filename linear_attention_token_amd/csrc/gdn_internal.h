@@ -46,10 +46,10 @@ struct Workspace {
   // chunked bf16 path only
   float* G = nullptr;                // fp32 [nc][hv][64]    in-chunk cumulative log decay
   uint16_t* Wk = nullptr;            // bf16 [nc][hv][64][128]  T diag(beta*gamma) K
-  uint16_t* U = nullptr;             // bf16 [nc][hv][4][4 tile pairs][64 lanes][2][4]  T diag(beta) V
+  uint16_t* U = nullptr;             // bf16 [nc][hv][8 col tiles][2 token slabs][64 lanes][8]  T diag(beta) V
   uint16_t* KT = nullptr;            // bf16 [nc][hk][128][64]  K^T of each chunk
-  uint16_t* ST = nullptr;            // bf16 [nc][hv][4][2][4][64 lanes][8] chunk-start state pieces
-  uint16_t* WT = nullptr;            // bf16 [nc][hv][4][2][2][64 lanes][8] chunk write W pieces
+  uint16_t* ST = nullptr;            // bf16 [nc][hv][8 col tiles][4 row slabs][64 lanes][8] chunk-start state pieces
+  uint16_t* WT = nullptr;            // bf16 [nc][hv][8 col tiles][2 token slabs][64 lanes][8] chunk write W pieces
   size_t bytes = 0;
 };
 

@@ -7,19 +7,29 @@
 // (§03) applied to 64 tokens at once (U, Wk, G from the WY kernel). The chunk-start state and W are
 // stored (bf16) for the output kernel, which then runs chunk-parallel.
 //
-// The d_v columns of S are independent in these products, so a chain is split into 4 slices of
-// 32 columns: one block of 4 compute waves per (sequence, value head, slice). Wave w owns state
-// rows 32w..32w+31 (two 16-row MFMA tiles) and W rows 16w..16w+15 of the slice; S and W cross
-// waves through LDS in bf16 as the B operand of the bf16 MFMAs, accumulation stays fp32. Each wave
-// streams its own operands (A operands of Wk and K^T, its U tiles, G) through a private LDS ring
-// (see below).
+// The d_v columns of S are independent in these products. One block serves a (sequence, value head,
+// 32-column slice); each of its two compute waves owns one 16-column tile of S for all 128 rows,
+// so both products of a chunk run on the wave's own registers:
+//   * S is held in the row order pi (pi32 in gdn_device.h): the wave's accumulator tiles 2s and
+//     2s + 1 are then, rounded to bf16, the B operand of rows 32s .. 32s + 31 -- W = U - Wk S needs
+//     no exchange of S between waves;
+//   * W is computed with its token rows in the order pi as well, so rounded W~ is directly the B
+//     operand of K^T W~;
+//   * the chunk-start state and W go to the output kernel as those same 16-byte operand pieces,
+//     straight from registers.
+// The only per-chunk synchronisation is the hand-over of the chunk's operands (A operands Wk and
+// K^T, the wave's U, G), which two producer waves stream through an LDS ring; the compute waves
+// read the next chunk's operands from the ring into registers while the current chunk's MFMAs
+// run, and the barrier between chunks does not wait for those reads.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-constexpr int kSlice = 32;  // state columns per block
-constexpr int kSlices = 128 / kSlice;
+constexpr int kSlices = 4;  // column slices per value head: one block each
+constexpr int kTilesPerBlock = 128 / 16 / kSlices;  // 16-column tiles per block
+constexpr int kComputeWaves = 2;
+constexpr int kTilesPerWave = kTilesPerBlock / kComputeWaves;  // each A-operand read feeds this many MFMAs
 
 struct StateArgs {
   const int32_t* seq_off;
@@ -32,202 +42,243 @@ struct StateArgs {
   float* state_out;
 };
 
-// ---- explicit memory operations -------------------------------------------------------------
+// ---- operand ring ------------------------------------------------------------------------------
 // The chunk operands stream through a ring in LDS, filled by direct global->LDS loads (no VGPR
-// destinations) that a fifth, producer wave issues kDepth-1 steps ahead and waits for with explicit
-// vmcnt counts; the four compute waves never stall on load issue. Every load moves 1 KB of
-// consecutive global bytes (whole rows): such loads stream about twice as fast per CU as loads
-// gathering 64-byte pieces of 16 rows. The 16-byte pieces of a row are placed in LDS in an XOR
-// order, so that the compute waves' MFMA operand reads (16 rows, the same columns) hit distinct
-// banks. The compute waves write the chunk state and W with coalesced stores from LDS.
+// destinations) that two producer waves issue kDepth-1 chunks ahead and wait for with explicit
+// vmcnt counts (two chunks of loads exceed what one wave may have outstanding); the compute waves
+// never stall on load issue. Every load moves 1 KB of consecutive
+// global bytes (whole rows): such loads stream about twice as fast per CU as loads gathering
+// 64-byte pieces of 16 rows. The 16-byte pieces of a row sit in LDS in an XOR order chosen so that
+// the MFMA operand reads (rows pi(16t + i), i < 16, one piece) hit distinct banks.
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-// The trailing s_nop covers the gfx9 hazard of a VALU overwriting the data VGPRs of a store wider
-// than 8 bytes right after it (the compiler's hazard recognizer does not see inside inline asm).
-__device__ __forceinline__ void st16(void* gptr, const void* lds_src) {
-  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds_src);
-  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(gptr), "v"(v) : "memory");
+// 16-byte global store of a register piece.
+__device__ __forceinline__ void stg16(uint16_t* gptr, const short8& v) {
+  *reinterpret_cast<short8*>(gptr) = v;
 }
 
-constexpr int kDepth = 3;                       // ring slots: loads run kDepth - 1 steps ahead
-constexpr int kNT = kSlice / 16;                // 16-column tiles per block
-static_assert(kNT == 2, "one U tile pair per compute wave");
-// Slot layout (bytes): Wk [64 rows][256 B], K^T [128 rows][128 B], U [4 waves][1 KB tile pair],
-// G [64] fp32. Row r of Wk keeps its 16-byte piece q at slot q ^ (r % 16); row r of K^T keeps
-// piece q at slot q ^ ((r / 2) % 8).
-constexpr int kOffWk = 0, kOffKT = 16384, kOffU = 32768, kOffG = 36864;
+constexpr int kDepth = 4;  // ring slots
+// Slot layout (bytes): Wk [64 rows][256 B], K^T [128 rows][128 B], U [compute waves][2 slabs]
+// [1 KB], G [64] fp32.
+constexpr int kULoads = 2 * kTilesPerBlock;
+constexpr int kOffWk = 0, kOffKT = 16384, kOffU = 32768, kOffG = kOffU + 1024 * kULoads;
 constexpr int kSlot = kOffG + 256;
-constexpr int kLoadsPerChunk = 16 + 16 + 4 + 1;  // Wk (4 rows each), K^T (8 rows each), U, G
-constexpr int kStLd = 136;                      // bf16 row stride of S^T [cols][128 k]
-constexpr int kWtLd = 72;                       // bf16 row stride of W~^T and W^T [cols][64 tokens]
-constexpr size_t kStateSmem = size_t(kDepth) * kSlot + kSlice * kStLd * 2 + 2 * kSlice * kWtLd * 2;
+constexpr int kLoadsPerChunk = 16 + 16 + kULoads + 1;  // Wk (4 rows each), K^T (8 rows each), U, G
+constexpr size_t kStateSmem = size_t(kDepth) * kSlot;
+// XOR keys: Wk row r (16 pieces) uses bits 0, 1, 3, 4 of r; K^T row r (8 pieces, two rows per 64
+// banks) uses bits 1, 3, 4. Over the rows pi(16t + i), i < 16, both are one-to-one (per parity
+// of r for K^T).
+__device__ __forceinline__ int wk_key(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
+__device__ __forceinline__ int kt_key(int r) { return ((r >> 1) & 1) | (((r >> 3) & 3) << 1); }
 
 // Load i of chunk c into the ring slot at LDS address `slot`.
 __device__ __forceinline__ void issue_load(const StateArgs& a, int64_t c, int h, int g, int sl, int lane,
                                            uint32_t slot, int i) {
   if (i < 16) {  // Wk rows 4i .. 4i+3
-    const int r = 4 * i + (lane >> 4), piece = (lane & 15) ^ (r & 15);
+    const int r = 4 * i + (lane >> 4), piece = (lane & 15) ^ wk_key(r);
     dma16(a.Wk + (c * a.hv + h) * 8192 + r * 128 + piece * 8, slot + kOffWk + i * 1024);
   } else if (i < 32) {  // K^T rows 8k .. 8k+7
-    const int k = i - 16, r = 8 * k + (lane >> 3), piece = (lane & 7) ^ ((r >> 1) & 7);
+    const int k = i - 16, r = 8 * k + (lane >> 3), piece = (lane & 7) ^ kt_key(r);
     dma16(a.KT + (c * a.hk + g) * 8192 + r * 64 + piece * 8, slot + kOffKT + k * 1024);
-  } else if (i < 36) {  // U tile pair sl of accumulator row tile (wave) i - 32
-    const int w = i - 32;
-    dma16(a.U + (c * a.hv + h) * 8192 + (w * 4 + sl) * 512 + lane * 8, slot + kOffU + w * 1024);
+  } else if (i < 32 + kULoads) {  // U: column tile kTilesPerBlock sl + (i - 32) / 2, token slab (i - 32) % 2
+    const int k = i - 32;
+    dma16(a.U + (c * a.hv + h) * 8192 + ((kTilesPerBlock * sl) * 2 + k) * 512 + lane * 8, slot + kOffU + k * 1024);
   } else {
     dma4(a.G + (c * a.hv + h) * 64 + lane, slot + kOffG);
   }
 }
 
-__global__ void __launch_bounds__(320) k_state(StateArgs a) {
+constexpr int kProducers = 2;  // waves issuing the ring loads; each has its own vmcnt budget
+constexpr int kLoadsP0 = (kLoadsPerChunk + 1) / 2;  // loads [0, kLoadsP0) by producer 0, the rest by 1
+
+__global__ void __launch_bounds__(64 * (kComputeWaves + kProducers)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_state(StateArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // the R value heads of a QK head (all their slices) read the same K^T tiles: keep them on one XCD
+  // the R value heads of a QK head (both halves) read the same K^T tiles: keep them on one XCD
   int u, sub;
   xcd_item(int(blockIdx.x), a.R * kSlices, u, sub);
   if (u >= a.n_units) return;
   const int n = u / a.hk, g = u - n * a.hk;
   const int h = g * a.R + sub / kSlices, sl = sub % kSlices;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;  // waves 0-3 compute, wave 4 loads
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;  // compute waves first, then loaders
   const int li = lane & 15, lq = lane >> 4;
-  const bool producer = (w == 4);
-  uint16_t* STs = reinterpret_cast<uint16_t*>(smem + size_t(kDepth) * kSlot);
-  uint16_t* WTs = STs + kSlice * kStLd;   // W~^T: B operand of K^T W~
-  uint16_t* WUs = WTs + kSlice * kWtLd;    // W^T unscaled: staged for the coalesced store
+  const bool producer = (w >= kComputeWaves);
+  const int pw = w - kComputeWaves;
+  const int jc0 = kTilesPerBlock * sl + kTilesPerWave * w;  // this wave's first column tile
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const int64_t c0 = a.seq_off[n], c1 = a.seq_off[n + 1];
   const int64_t clast = c1 > c0 ? c1 - 1 : c0;
 
-  // state rows 32w + 16m + 4lq + r, columns kSlice*sl + 16nt + li
-  f32x4 S[2][kNT];
+  // S[v][m][r]: state row pi(16m + 4lq + r), column 16(jc0 + v) + li
+  f32x4 S[kTilesPerWave][8];
   const size_t sbase = (size_t(n) * a.hv + h) * 128 * 128;
   if (!producer) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int v = 0; v < kTilesPerWave; ++v)
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          S[m][nt][r] = a.state_in ? a.state_in[sbase + size_t(32 * w + 16 * m + 4 * lq + r) * 128 + kSlice * sl + 16 * nt + li] : 0.f;
+          S[v][m][r] = a.state_in ? a.state_in[sbase + size_t(pi32(16 * m + 4 * lq + r)) * 128 + 16 * (jc0 + v) + li] : 0.f;
     // settle these loads here, so no wait inside the loop has to cover them (the loop's own
     // stores would then be waited for too)
     wait_vm<0>();
   }
-  // the producer issues loads [i0, i1) of one chunk into one slot
-  auto produce = [&](int64_t c, int slot, int i0, int i1) {
+  // a producer issues its share of the loads of one chunk into one slot
+  auto produce = [&](int64_t c, int slot) {
     const int64_t cc = min(c, clast);
     const uint32_t sa = ring + uint32_t(slot * kSlot);
+    if (pw == 0) {
 #pragma unroll
-    for (int i = i0; i < i1; ++i) issue_load(a, cc, h, g, sl, lane, sa, i);
+      for (int i = 0; i < kLoadsP0; ++i) issue_load(a, cc, h, g, sl, lane, sa, i);
+    } else {
+#pragma unroll
+      for (int i = kLoadsP0; i < kLoadsPerChunk; ++i) issue_load(a, cc, h, g, sl, lane, sa, i);
+    }
   };
-  if (c0 < c1 && producer) {
+  auto settle = [&]() {  // all but the last chunk issued have landed
+    if (pw == 0) wait_vm<kLoadsP0>();
+    else wait_vm<kLoadsPerChunk - kLoadsP0>();
+  };
+  // Block barrier without the memory fence of __syncthreads: LDS reads issued before it (the next
+  // chunk's operands) stay in flight across it. The memory clobber keeps the compiler from moving
+  // memory accesses across it; ring data is published by the producers' vmcnt waits before it.
+  auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
+
+  // A-operand rows (ring rows) of this lane: token pi(16t + li), state row pi(16m + li)
+  int tok[4], srow[8];
 #pragma unroll
-    for (int i = 0; i < kDepth - 1; ++i) produce(c0 + i, i, 0, kLoadsPerChunk);
-    wait_vm<(kDepth - 2) * kLoadsPerChunk>();  // chunk c0 has landed
+  for (int t = 0; t < 4; ++t) tok[t] = pi32(16 * t + li);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) srow[m] = pi32(16 * m + li);
+
+  // Operands of one chunk, read from its ring slot into registers: Wk rows tok[t] and K^T rows
+  // srow[m], columns 32s + 8lq .. +7 (piece 4s + lq) at their XOR slots; this wave's U pieces; G.
+  struct Ops {
+    short8 wk[4][4], kt[8][2];
+    uint4 up[kTilesPerWave][2];
+    float4 gt[4];
+    float gc;
+  };
+  auto read_ops = [&](int slot, Ops& o) {
+    const unsigned char* sb = smem + size_t(slot) * kSlot;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = tok[t];
+        o.wk[t][s] = *reinterpret_cast<const short8*>(sb + kOffWk + r * 256 + (((4 * s + lq) ^ wk_key(r)) << 4));
+      }
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int r = srow[m];
+        o.kt[m][s] = *reinterpret_cast<const short8*>(sb + kOffKT + r * 128 + (((4 * s + lq) ^ kt_key(r)) << 4));
+      }
+#pragma unroll
+    for (int v = 0; v < kTilesPerWave; ++v)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        o.up[v][s] = *reinterpret_cast<const uint4*>(sb + kOffU + ((kTilesPerWave * w + v) * 2 + s) * 1024 + lane * 16);
+    const float* Gl = reinterpret_cast<const float*>(sb + kOffG);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o.gt[k] = *reinterpret_cast<const float4*>(Gl + 32 * (k >> 1) + 8 * lq + 4 * (k & 1));
+    o.gc = Gl[63];
+  };
+
+  // Ring schedule (kDepth = 4 slots): the producers keep two chunks in flight and, before barrier
+  // j, have chunk j + 2 landed; after barrier j - 1 the compute waves read chunk j + 1's operands
+  // while they compute chunk j. The slot refilled after barrier j - 1 (chunk j + 3) held chunk j - 1,
+  // whose operands were consumed before barrier j - 1.
+  Ops op;
+  if (c0 < c1) {
+    if (producer) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) produce(c0 + i, i);
+      settle();  // chunks c0 and c0 + 1 have landed
+    }
+    barrier();
+    if (!producer) read_ops(0, op);
   }
 
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t j = c - c0;
-    const int slot = int(j % kDepth);
-    __syncthreads();  // B0: chunk c is in its ring slot
     if (producer) {
-      // refill the slot read during step c - 1 (its reads finished before that step's B1), spread
-      // over the step so no barrier waits for the producer
-      const int fill = int((j + kDepth - 1) % kDepth);
-      produce(c + kDepth - 1, fill, 0, 13);
-      __syncthreads();  // B1
-      produce(c + kDepth - 1, fill, 13, 26);
-      __syncthreads();  // B2
-      produce(c + kDepth - 1, fill, 26, kLoadsPerChunk);
-      wait_vm<(kDepth - 2) * kLoadsPerChunk>();  // chunk c + 1 has landed
+      produce(c + 3, int((j + 3) % kDepth));
+      settle();  // chunk c + 2 has landed
+      barrier();
       continue;
     }
 
-    const unsigned char* sb = smem + size_t(slot) * kSlot;
-    // A operands: Wk rows 16w + li and K^T rows 32w + 16m + li, columns 32s + 8lq .. +7 (piece
-    // 4s + lq), each at its XOR slot
-    short8 wk[4], kt[2][2];
+    // chunk-start state in bf16: B operand of rows 32s .. +31 (rows 32s + 8lq .. +7 in this lane),
+    // and the output kernel's piece (column tile jc0 + v, row slab s)
+    short8 sbf[kTilesPerWave][4];
+    uint16_t* stf = a.ST + (size_t(c) * a.hv + h) * 128 * 128;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      wk[s] = *reinterpret_cast<const short8*>(sb + kOffWk + (16 * w + li) * 256 + (((4 * s + lq) ^ li) << 4));
+    for (int v = 0; v < kTilesPerWave; ++v)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        kt[m][s] = *reinterpret_cast<const short8*>(sb + kOffKT + (32 * w + 16 * m + li) * 128 +
-                                                    (((4 * s + lq) ^ (li >> 1)) << 4));
-    uint2 uu[kNT];
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-      uu[nt] = *reinterpret_cast<const uint2*>(sb + kOffU + w * 1024 + lane * 16 + nt * 8);
-    const float* Gl = reinterpret_cast<const float*>(sb + kOffG);
-    const float4 gr = *reinterpret_cast<const float4*>(Gl + 16 * w + 4 * lq);
-    const float gc = Gl[63];
-
-    // S (bf16) -> LDS as S^T
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int col = 16 * nt + li, k0 = 32 * w + 16 * m + 4 * lq;
-        *reinterpret_cast<uint2*>(&STs[col * kStLd + k0]) =
-            make_uint2(pack_bf16x2(S[m][nt][0], S[m][nt][1]), pack_bf16x2(S[m][nt][2], S[m][nt][3]));
+      for (int s = 0; s < 4; ++s) {
+        sbf[v][s] = pack8(S[v][2 * s], S[v][2 * s + 1]);
+        stg16(stf + (((jc0 + v) * 4 + s) * 64 + lane) * 8, sbf[v][s]);
       }
-    __syncthreads();  // B1
-    // chunk-start state to the output kernel, in its MFMA operand pieces: piece (sl, nt, w) holds
-    // columns 32sl + 16nt + (lane % 16), rows 32w + 8 (lane / 16) .. +7 -- 1 KB per store
-    {
-      uint16_t* stf = a.ST + (size_t(c) * a.hv + h) * 128 * 128;
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-        st16(stf + (((sl * kNT + nt) * 4 + w) * 64 + lane) * 8, &STs[(16 * nt + li) * kStLd + 32 * w + 8 * lq]);
-    }
 
-    // W = U - Wk S   (rows 16w + 4lq + r, columns 16nt + li)
-    f32x4 Wt[kNT];
+    // W = U - Wk S, token rows in the order pi: W[t][r] is token pi(16t + 4lq + r) = 32(t/2) +
+    // 8lq + 4(t%2) + r, whose U value is element 4(t%2) + r of this lane's U piece of slab t/2
+    f32x4 W[kTilesPerWave][4];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc[kTilesPerWave];
+#pragma unroll
+      for (int v = 0; v < kTilesPerWave; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        acc = mfma16x16x32(wk[s], ld_short8(&STs[(16 * nt + li) * kStLd + 32 * s + 8 * lq]), acc);
-      const uint2 u = uu[nt];
-      Wt[nt][0] = __uint_as_float(u.x << 16) - acc[0];
-      Wt[nt][1] = __uint_as_float(u.x & 0xffff0000u) - acc[1];
-      Wt[nt][2] = __uint_as_float(u.y << 16) - acc[2];
-      Wt[nt][3] = __uint_as_float(u.y & 0xffff0000u) - acc[3];
-    }
-    // W^T staged for the output kernel; W~ = diag(exp(G_C - G_i)) W to LDS as the B operand of K^T W~
-    const float dec[4] = {__expf(gc - gr.x), __expf(gc - gr.y), __expf(gc - gr.z), __expf(gc - gr.w)};
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      const int col = 16 * nt + li, t0 = 16 * w + 4 * lq;
-      *reinterpret_cast<uint2*>(&WUs[col * kWtLd + t0]) =
-          make_uint2(pack_bf16x2(Wt[nt][0], Wt[nt][1]), pack_bf16x2(Wt[nt][2], Wt[nt][3]));
-      *reinterpret_cast<uint2*>(&WTs[col * kWtLd + t0]) =
-          make_uint2(pack_bf16x2(Wt[nt][0] * dec[0], Wt[nt][1] * dec[1]),
-                     pack_bf16x2(Wt[nt][2] * dec[2], Wt[nt][3] * dec[3]));
+        for (int v = 0; v < kTilesPerWave; ++v) acc[v] = mfma16x16x32(op.wk[t][s], sbf[v][s], acc[v]);
+#pragma unroll
+      for (int v = 0; v < kTilesPerWave; ++v) W[v][t] = acc[v];
     }
-    __syncthreads();  // B2
-    // W^T to the output kernel, in its MFMA operand pieces: wave w stores piece (sl, nt, s) with
-    // nt = w / 2, s = w % 2: columns 32sl + 16nt + (lane % 16), tokens 32s + 8 (lane / 16) .. +7
-    {
-      const int nt = w >> 1, s = w & 1;
-      uint16_t* wtf = a.WT + (size_t(c) * a.hv + h) * 128 * 64;
-      st16(wtf + (((sl * kNT + nt) * 2 + s) * 64 + lane) * 8, &WUs[(16 * nt + li) * kWtLd + 32 * s + 8 * lq]);
+    short8 wbf[kTilesPerWave][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float gt[8] = {op.gt[2 * s].x, op.gt[2 * s].y, op.gt[2 * s].z, op.gt[2 * s].w,
+                           op.gt[2 * s + 1].x, op.gt[2 * s + 1].y, op.gt[2 * s + 1].z, op.gt[2 * s + 1].w};
+      float dec[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dec[e] = __expf(op.gc - gt[e]);
+#pragma unroll
+      for (int v = 0; v < kTilesPerWave; ++v) {
+        const uint32_t uw[4] = {op.up[v][s].x, op.up[v][s].y, op.up[v][s].z, op.up[v][s].w};
+        f32x4 wt[2], wd[2];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float uv = __uint_as_float(e & 1 ? uw[e >> 1] & 0xffff0000u : uw[e >> 1] << 16);
+          const float wv = uv - W[v][2 * s + (e >> 2)][e & 3];
+          wt[e >> 2][e & 3] = wv;
+          wd[e >> 2][e & 3] = wv * dec[e];
+        }
+        wbf[v][s] = pack8(wd[0], wd[1]);   // W~ = diag(exp(G_C - G_i)) W: B operand of K^T W~
+        // W, tokens 32s + 8lq .. +7: the output kernel's piece
+        stg16(a.WT + (size_t(c) * a.hv + h) * 128 * 64 + (((jc0 + v) * 2 + s) * 64 + lane) * 8, pack8(wt[0], wt[1]));
+      }
     }
 
     // S <- exp(G_C) S + K^T W~
-    const float gC = __expf(gc);
+    const float gC = __expf(op.gc);
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 8; ++m) {
+      f32x4 acc[kTilesPerWave];
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        f32x4 acc = S[m][nt] * gC;
+      for (int v = 0; v < kTilesPerWave; ++v) acc[v] = S[v][m] * gC;
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          acc = mfma16x16x32(kt[m][s], ld_short8(&WTs[(16 * nt + li) * kWtLd + 32 * s + 8 * lq]), acc);
-        S[m][nt] = acc;
-      }
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int v = 0; v < kTilesPerWave; ++v) acc[v] = mfma16x16x32(op.kt[m][s], wbf[v][s], acc[v]);
+#pragma unroll
+      for (int v = 0; v < kTilesPerWave; ++v) S[v][m] = acc[v];
+    }
+    if (c + 1 < c1) read_ops(int((j + 1) % kDepth), op);  // the next chunk's, over this one's MFMAs
+    barrier();
   }
   if (producer) {
     wait_vm<0>();  // no load may still be writing this block's LDS when it exits
@@ -236,12 +287,12 @@ __global__ void __launch_bounds__(320) k_state(StateArgs a) {
 
   if (a.state_out) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int v = 0; v < kTilesPerWave; ++v)
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          a.state_out[sbase + size_t(32 * w + 16 * m + 4 * lq + r) * 128 + kSlice * sl + 16 * nt + li] = S[m][nt][r];
+          a.state_out[sbase + size_t(pi32(16 * m + 4 * lq + r)) * 128 + 16 * (jc0 + v) + li] = S[v][m][r];
   }
 }
 
@@ -259,7 +310,7 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const float* stat
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_state, dim3(unsigned(xcd_blocks(units, R * kSlices))), dim3(320),
+  hipLaunchKernelGGL(k_state, dim3(unsigned(xcd_blocks(units, R * kSlices))), dim3(64 * (kComputeWaves + kProducers)),
                      kStateSmem, s, a);
   return hipGetLastError();
 }

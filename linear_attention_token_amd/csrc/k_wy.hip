@@ -34,7 +34,7 @@ struct WyArgs {
   const float *alpha, *beta;      // [T][hv]
   float* G;                       // [nc][hv][64]
   uint16_t *Wk;                   // [nc][hv][64][128]
-  uint16_t *U;                    // [nc][hv][4 waves][4 tile pairs][64 lanes][2 tiles][4 rows]
+  uint16_t *U;                    // [nc][hv][8 column tiles][2 token slabs][64 lanes][8 tokens]
   uint16_t* KT;                   // [nc][hk][128][64]
 };
 
@@ -263,15 +263,18 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     }
   }
 
-  // U goes out in its accumulator layout with tiles paired, [row block][tile pair][lane][2][4],
-  // which is how the state pass consumes it (16 contiguous bytes per lane)
+  // U goes out as the state pass's 16-byte pieces: piece (column tile j, token slab s), lane
+  // (i, q) holds tokens 32s + 8q .. +7 of column 16j + i. This lane's rows 16ib + 4lq .. +3 are
+  // the half 4 (lq % 2) .. +3 of the piece of lane (li, 2 (ib % 2) + lq / 2) in slab ib / 2.
   if (!wk_tiles) {
     uint16_t* Ug = a.U + (int64_t(c) * a.hv + h) * 64 * 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp)
-        *reinterpret_cast<short8*>(Ug + ((i * 4 + 2 * w + jp) * 64 + lane) * 8) = join8(xb[i][2 * jp], xb[i][2 * jp + 1]);
+      for (int j = 0; j < 4; ++j) {
+        const int sl = i >> 1, q = 2 * (i & 1) + (lq >> 1);
+        *reinterpret_cast<short4v*>(Ug + (((4 * w + j) * 2 + sl) * 64 + q * 16 + li) * 8 + 4 * (lq & 1)) = xb[i][j];
+      }
   }
   __syncthreads();  // V^ transposed is dead: stage Wk over it
   uint16_t* Ws = VTs;  // [64][136]
