@@ -213,9 +213,9 @@ def gdn_prefill(inp, *, flags=FLAG_ALL, scale=1.0, l2_eps=1e-6, norm_eps=1e-6):
         for h in range(hv):
             o[s0:s1, h], S_out[n, h] = prefill_chain(inp, n, h, flags=flags, scale=scale,
                                                      l2_eps=l2_eps, norm_eps=norm_eps)
-        x_raw = np.concatenate([_f64(q[s0:s1]).reshape(s1 - s0, -1),
-                                _f64(k[s0:s1]).reshape(s1 - s0, -1),
-                                _f64(v[s0:s1]).reshape(s1 - s0, -1)], axis=1)
+        x_raw = np.concatenate([_f64(q[s0:s1]).reshape(s1 - s0, hk * dk),
+                                _f64(k[s0:s1]).reshape(s1 - s0, hk * dk),
+                                _f64(v[s0:s1]).reshape(s1 - s0, hv * dv)], axis=1)
         hist = _f64(ci[n]) if ci is not None else np.zeros((CONV_WIDTH - 1, C))
         conv_out[n] = conv_tail(x_raw, hist)
     return o, S_out, conv_out

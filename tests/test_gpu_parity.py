@@ -64,6 +64,34 @@ def test_bf16_chunked_ragged():
     _check_full(inp)
 
 
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_fused_qkv_views_and_empty_sequences(io):
+    """q, k, v as column slices of one [T, C] projection output (token row stride C, the usual
+    caller layout), in a packed batch with zero-length sequences: identical (bitwise) to contiguous
+    copies, within tolerance of the oracle, and empty sequences pass state and conv cache through."""
+    lens = [0, 70, 0, 5, 0, 64]
+    inp = prefill_inputs(lens, n_qk_heads=2, n_v_heads=6, d_k=128, d_v=128, io_dtype=io, seed=21, device=DEV,
+                         s0_std=0.01, conv_in_std=1.0)
+    T, hk, hv = inp.q.shape[0], 2, 6
+    ref_out, ref_st, ref_cv = run_prefill(inp)
+    fused = torch.cat([inp.q.reshape(T, -1), inp.k.reshape(T, -1), inp.v.reshape(T, -1)], dim=1)
+    qc = hk * 128
+    inp.q = fused[:, :qc].view(T, hk, 128)
+    inp.k = fused[:, qc:2 * qc].view(T, hk, 128)
+    inp.v = fused[:, 2 * qc:].view(T, hv, 128)
+    assert not inp.q.is_contiguous() and inp.q.stride(0) == fused.shape[1]
+    out, st, cv = run_prefill(inp)
+    assert torch.equal(out, ref_out) and torch.equal(st, ref_st) and torch.equal(cv, ref_cv)
+    o_ref, s_ref, c_ref = oracle_prefill(inp.to("cpu"))
+    tol = TOL[io]
+    assert rel_l2(out, o_ref) <= tol and rel_l2(st, s_ref) <= tol
+    np.testing.assert_array_equal(cv.double().cpu().numpy(), c_ref)
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert torch.equal(st[n], inp.state_in[n])
+            assert torch.equal(cv[n], inp.conv_in[n])
+
+
 @pytest.mark.parametrize("hk,hv", [(2, 2), (2, 4), (1, 4), (1, 5), (1, 6)])
 def test_bf16_chunked_head_ratios(hk, hv):
     """Value heads per QK head from 1 to 6: the WY kernel batches 1, 2 or 3 of them per block."""

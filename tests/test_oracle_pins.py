@@ -307,6 +307,25 @@ def test_packed_equals_separate():
         assert np.array_equal(o1, o[s0:s1]) and np.array_equal(S1[0], S[n]) and np.array_equal(c1[0], c[n])
 
 
+def test_empty_sequences_pass_through():
+    """A zero-length sequence in a packed batch produces no output rows, keeps its initial state
+    and conv cache exactly, and leaves its neighbours as they are without it."""
+    lengths = [0, 7, 0, 3, 0]
+    inp = _small(lengths, s0_std=0.1, conv_in_std=1.0)
+    o, S, c = O.gdn_prefill(inp)
+    assert o.shape[0] == sum(lengths)
+    for n in (0, 2, 4):
+        assert np.array_equal(S[n], inp["state_in"][n].double().numpy())
+        assert np.array_equal(c[n], inp["conv_in"][n].double().numpy())
+    keep = [1, 3]
+    dense = {k: v for k, v in inp.items()}
+    dense["state_in"] = inp["state_in"][keep]
+    dense["conv_in"] = inp["conv_in"][keep]
+    dense["cu_seqlens"] = np.array([0, 7, 10])
+    o2, S2, c2 = O.gdn_prefill(dense)
+    assert np.array_equal(o2, o) and np.array_equal(S2, S[keep]) and np.array_equal(c2, c[keep])
+
+
 @pytest.mark.parametrize("T1", [1, 2, 5, 17])
 def test_continuation_and_decode(T1):
     """prefill(T1 + T2) == prefill(T1) -> (state, conv tail) -> prefill(T2), bitwise; and the
