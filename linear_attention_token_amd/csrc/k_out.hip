@@ -9,9 +9,10 @@
 //
 // Wave w computes channels 32w..32w+31 of Y for all 64 tokens (its own slice of the chunk state and
 // of W), as Y^T = S^T Q^T + W^T P^T: the chunk-state and W pieces are then A operands as loaded, and
-// each lane ends with 4 consecutive channels of a token, so RMSNorm, gain and gate run on registers
-// and the lane stores 8 bytes. Per-token sums of squares are combined across the four waves in LDS.
-// bf16 MFMA, fp32 accumulate.
+// each lane ends with 4 consecutive channels of a token, so RMSNorm, gain and gate run on registers.
+// Per-token sums of squares are combined across the four waves in LDS. The gate tile is loaded and
+// the output tile stored as whole 256-byte token rows (16 bytes per lane), passing through LDS in
+// between. bf16 MFMA, fp32 accumulate.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -71,19 +72,18 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) bw[nt][s] = ld_short8(wt + (((w * 2 + nt) * 2 + s) * 64 + lane) * 8);
   }
-  // gate logits of this lane's outputs: token 16tt + li, channels 32w + 16nt + 4lq .. +3 (rows past
-  // the chunk end read the last row; those outputs are not stored)
+  // gate logits as whole token rows: piece idx = tid + 256 it is token idx / 16, channels
+  // 8 (idx % 16) .. +7 (rows past the chunk end read the last row; their outputs are not stored)
   const int64_t orow = int64_t(a.hv) * 128;
-  uint2 gv[4][2];
+  uint4 gq[4];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      gv[tt][nt] = make_uint2(0u, 0u);
-      if (a.flags & GDN_GATE)
-        gv[tt][nt] = *reinterpret_cast<const uint2*>(a.gate + (start + min(16 * tt + li, len - 1)) * orow + h * 128 +
-                                                     32 * w + 16 * nt + 4 * lq);
-    }
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + it * 256;
+    gq[it] = make_uint4(0u, 0u, 0u, 0u);
+    if (a.flags & GDN_GATE)
+      gq[it] = *reinterpret_cast<const uint4*>(a.gate + (start + min(idx >> 4, len - 1)) * orow + h * 128 +
+                                               (idx & 15) * 8);
+  }
   // zero-centred gain (1 + w) of this lane's 8 channels
   float gain[2][4];
 #pragma unroll
@@ -172,6 +172,15 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
     ss += __shfl_xor(ss, 32, 64);
     if (lq == 0) red[w][16 * tt + li] = ss;
   }
+  __syncthreads();  // every wave is past its last read of Q and P
+  // the gate tile [64][kLd] over Q; each lane then replaces the 8 bytes of logits it reads with the
+  // 8 bytes of output it computes from them, so the output tile needs no further barrier to form
+  uint16_t* Os = Qs;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + it * 256;
+    *reinterpret_cast<uint4*>(&Os[(idx >> 4) * kLd + (idx & 15) * 8]) = gq[it];
+  }
   __syncthreads();
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
@@ -180,7 +189,8 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
     const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(tot * (1.0f / 128.0f) + a.norm_eps) : 1.0f;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const uint2 gg = gv[tt][nt];
+      uint2* slot = reinterpret_cast<uint2*>(&Os[t * kLd + 32 * w + 16 * nt + 4 * lq]);
+      const uint2 gg = *slot;
       const float gl[4] = {__uint_as_float(gg.x << 16), __uint_as_float(gg.x & 0xffff0000u),
                            __uint_as_float(gg.y << 16), __uint_as_float(gg.y & 0xffff0000u)};
       float o[4];
@@ -191,10 +201,16 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
         if (a.flags & GDN_GATE) v *= sigmoidf_(gl[r]);
         o[r] = v;
       }
-      if (t < len)
-        *reinterpret_cast<uint2*>(a.out + (start + t) * orow + h * 128 + 32 * w + 16 * nt + 4 * lq) =
-            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      *slot = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = tid + it * 256, t = idx >> 4;
+    if (t < len)
+      *reinterpret_cast<uint4*>(a.out + (start + t) * orow + h * 128 + (idx & 15) * 8) =
+          *reinterpret_cast<const uint4*>(&Os[t * kLd + (idx & 15) * 8]);
   }
 }
 
