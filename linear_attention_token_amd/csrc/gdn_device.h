@@ -159,6 +159,14 @@ __device__ __forceinline__ int pi32(int x) {
   return b + ((y & 15) >> 2) * 8 + (y >> 4) * 4 + (y & 3);
 }
 
+// LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i passes the address of
+// row i / 4, columns 4 (i % 4) .. +3 of a 4 x 16 block of 16-bit elements, and receives column i of
+// the block's four rows (element r = row r).
+__device__ __forceinline__ short4v ld_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) short4v lds_short4v;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p));
+}
+
 // Two fp32 accumulator tiles (4 + 4 rows) -> one bf16 MFMA operand (8 k values).
 __device__ __forceinline__ short8 pack8(const f32x4& a, const f32x4& b) {
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));

@@ -19,7 +19,9 @@
 // zero and G stays at the last real token.
 //
 // A block holds TEAMS teams of 4 waves, one per value head of its batch; all teams run the same
-// steps in lockstep (block-wide barriers), each on its own LDS region.
+// steps in lockstep (block-wide barriers), each on its own LDS region. k^ and v^ are loaded as
+// whole token rows and kept row-major in LDS; the substitution reads them as transposed MFMA
+// operands with LDS transpose reads.
 #include <algorithm>
 
 #include "gdn_device.h"
@@ -38,8 +40,8 @@ struct WyArgs {
   uint16_t* KT;                   // [nc][hk][128][64]
 };
 
-constexpr int kKsLd = 144;   // bf16 row stride of the 64x128 k^ tile
-constexpr int kKTLd = 72;    // bf16 row stride of the transposed 128x64 tiles and of -A
+constexpr int kKsLd = 144;   // bf16 row stride of the 64x128 k^ and v^ tiles
+constexpr int kKTLd = 72;    // bf16 row stride of the transposed 128x64 k^ tile and of -A
 
 // Block b works through the items b, b + gridDim.x, ... (one item = chunk, QK head and batch of
 // TEAMS value heads) with one block per CU; the raw inputs of its next item are loaded into
@@ -57,11 +59,11 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks_[64 * kKsLd];    // k^ rows
   __shared__ __attribute__((aligned(16))) uint16_t KTs_[128 * kKTLd];  // k^ transposed
-  // per team: -A in bf16 with D_i on the diagonal blocks; A's diagonal blocks in fp32; V^
-  // transposed (later the Wk staging)
+  // per team: -A in bf16 with D_i on the diagonal blocks; A's diagonal blocks in fp32; v^ rows
+  // (later the Wk staging)
   __shared__ __attribute__((aligned(16))) uint16_t Ab_[TEAMS][64 * kKTLd];
   __shared__ __attribute__((aligned(16))) float Df_[TEAMS][4][16][16];
-  __shared__ __attribute__((aligned(16))) uint16_t VTs_[TEAMS][128 * kKTLd];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs_[TEAMS][64 * kKsLd];
   __shared__ __attribute__((aligned(16))) float Gs_[TEAMS][64], Bs_[TEAMS][64], Cs_[TEAMS][64];
 
   // item -> chunk c, QK head g, this thread's value head h; chunk start and length
@@ -78,9 +80,9 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     it.len = ct.y;
     return it;
   };
-  // raw inputs of an item: k^ pieces (t = idx % 64, segment idx / 64 of idx = tid + 256 TEAMS j; a
-  // wave covers one column segment of all 64 rows, so its transposed LDS writes are contiguous),
-  // v^ pieces (t = lane, segment w + 4j of this team's head), alpha and beta (wave 0 of a team)
+  // raw inputs of an item, as 16-byte pieces of whole token rows (a wave load covers four 256-byte
+  // rows): k^ pieces idx = tid + 256 TEAMS j, v^ pieces idx = ttid + 256 j of this team's head, each
+  // token idx / 16, segment idx % 16; alpha and beta (wave 0 of a team)
   uint4 kv[kKIt], vv[4];
   float la_raw = 1.f, be_raw = 0.f;
   auto fetch_k = [&](int item) {
@@ -88,7 +90,7 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     const Item it = decode(item);
 #pragma unroll
     for (int j = 0; j < kKIt; ++j) {
-      const int idx = tid + 256 * TEAMS * j, t = idx & 63, sg = idx >> 6;
+      const int idx = tid + 256 * TEAMS * j, t = idx >> 4, sg = idx & 15;
       kv[j] = make_uint4(0, 0, 0, 0);
       if (idx < 1024 && t < it.len)
         kv[j] = *reinterpret_cast<const uint4*>(a.khat + (it.start + t) * krow + it.g * 128 + sg * 8);
@@ -99,9 +101,10 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     const Item it = decode(item);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const int idx = ttid + 256 * j, t = idx >> 4, sg = idx & 15;
       vv[j] = make_uint4(0, 0, 0, 0);
-      if (lane < it.len)
-        vv[j] = *reinterpret_cast<const uint4*>(a.vhat + (it.start + lane) * vrow + it.h * 128 + (w + 4 * j) * 8);
+      if (t < it.len)
+        vv[j] = *reinterpret_cast<const uint4*>(a.vhat + (it.start + t) * vrow + it.h * 128 + sg * 8);
     }
     la_raw = 1.f;
     be_raw = 0.f;
@@ -129,7 +132,7 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     uint16_t* const KTs = KTs_ + z;
     uint16_t* const Ab = Ab_[team] + z;
     float (*const Df)[16][16] = reinterpret_cast<float (*)[16][16]>(&Df_[team][0][0][0] + z);
-    uint16_t* const VTs = VTs_[team] + z;
+    uint16_t* const Vs = Vs_[team] + z;
     float* const Gs = Gs_[team] + z;
     float* const Bs = Bs_[team] + z;
     float* const Cs = Cs_[team] + z;  // beta exp(G)
@@ -139,31 +142,17 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
       continue;
     }
 
-  // ---- k^ into LDS (row-major and transposed; all teams); alpha/beta -> G ----
+  // ---- k^ and v^ rows into LDS; alpha/beta -> G ----
 #pragma unroll
   for (int j = 0; j < kKIt; ++j) {
     const int idx = tid + 256 * TEAMS * j;
     if (idx >= 1024) break;
-    const int t = idx & 63, sg = idx >> 6;
-    const uint4 v = kv[j];
-    *reinterpret_cast<uint4*>(&Ks[t * kKsLd + sg * 8]) = v;
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      KTs[(sg * 8 + 2 * e) * kKTLd + t] = uint16_t(wv[e] & 0xffffu);
-      KTs[(sg * 8 + 2 * e + 1) * kKTLd + t] = uint16_t(wv[e] >> 16);
-    }
+    *reinterpret_cast<uint4*>(&Ks[(idx >> 4) * kKsLd + (idx & 15) * 8]) = kv[j];
   }
-  // V^ transposed, from this item's prefetched pieces
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int t = lane, sg = w + 4 * it;
-    const uint32_t wv[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      VTs[(sg * 8 + 2 * e) * kKTLd + t] = uint16_t(wv[e] & 0xffffu);
-      VTs[(sg * 8 + 2 * e + 1) * kKTLd + t] = uint16_t(wv[e] >> 16);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int idx = ttid + 256 * j;
+    *reinterpret_cast<uint4*>(&Vs[(idx >> 4) * kKsLd + (idx & 15) * 8]) = vv[j];
   }
   if (w == 0) {
     float la = lane < len ? logf(la_raw) : 0.f;
@@ -182,15 +171,12 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
   fetch_k(item + gridDim.x);  // the next item's inputs fly while this one is transformed
   fetch_v(item + gridDim.x);
 
-  // K^T of the chunk for the state pass, written once per QK head
-  if (hr == 0) {
-    uint16_t* dst = a.KT + (int64_t(c) * a.hk + g) * 128 * 64;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = ttid + it * 256;  // 128 rows x 8 segments
-      const int r = idx >> 3, sg = idx & 7;
-      *reinterpret_cast<uint4*>(dst + r * 64 + sg * 8) = *reinterpret_cast<const uint4*>(&KTs[r * kKTLd + sg * 8]);
-    }
+  // K^T of the chunk for the state pass, formed by transpose reads of the k^ rows: read q of the
+  // 32 (16 channels x 16 tokens) covers channels 16 (q % 8) .., tokens 16 (q / 8) + 4 lq .. +3
+  for (int q = tid >> 6; q < 32; q += 4 * TEAMS) {
+    const int cb = q & 7, tb = q >> 3;
+    const short4v v = ld_tr16(&Ks[(16 * tb + 4 * lq + (li >> 2)) * kKsLd + 16 * cb + 4 * (li & 3)]);
+    *reinterpret_cast<short4v*>(&KTs[(16 * cb + li) * kKTLd + 16 * tb + 4 * lq]) = v;
   }
 
   // ---- Gram k^ k^T (lower block triangle) on MFMA; A[t,i] = beta_t exp(G_t - G_i) k_t.k_i, i < t:
@@ -214,6 +200,17 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
   }
   __syncthreads();
 
+  // K^T of the chunk for the state pass, written once per QK head
+  if (hr == 0) {
+    uint16_t* dst = a.KT + (int64_t(c) * a.hk + g) * 128 * 64;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = ttid + it * 256;  // 128 rows x 8 segments
+      const int r = idx >> 3, sg = idx & 7;
+      *reinterpret_cast<uint4*>(dst + r * 64 + sg * 8) = *reinterpret_cast<const uint4*>(&KTs[r * kKTLd + sg * 8]);
+    }
+  }
+
   // ---- D_w = (I + A_ww)^-1 by forward substitution, lane = column; into Ab's diagonal block ----
   if (lane < 16) {
     float x[16];
@@ -235,7 +232,7 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
   // rows 16i + 4q .. +3 of column c, which is both the accumulator layout and the B-operand layout
   // of the 16x16x16 MFMA.
   const bool wk_tiles = w >= 2;
-  const uint16_t* src = wk_tiles ? KTs : VTs;  // transposed sources [column][token]
+  const uint16_t* src = wk_tiles ? Ks : Vs;  // sources [token][column]
   const float* rs = wk_tiles ? Cs : Bs;
   const int col0 = 16 * (4 * w - (wk_tiles ? 8 : 0));  // first source column of this wave
   short4v xb[4][4];
@@ -244,10 +241,9 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
     const float4 sc = *reinterpret_cast<const float4*>(&rs[16 * i + 4 * lq]);
     f32x4 acc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint2 sv = *reinterpret_cast<const uint2*>(&src[(col0 + 16 * j + li) * kKTLd + 16 * i + 4 * lq]);
-      acc[j] = f32x4{__uint_as_float(sv.x << 16) * sc.x, __uint_as_float(sv.x & 0xffff0000u) * sc.y,
-                     __uint_as_float(sv.y << 16) * sc.z, __uint_as_float(sv.y & 0xffff0000u) * sc.w};
+    for (int j = 0; j < 4; ++j) {  // column col0 + 16j + li, tokens 16i + 4lq .. +3
+      const short4v sv = ld_tr16(&src[(16 * i + 4 * lq + (li >> 2)) * kKsLd + col0 + 16 * j + 4 * (li & 3)]);
+      acc[j] = f32x4{bf2f(sv[0]) * sc.x, bf2f(sv[1]) * sc.y, bf2f(sv[2]) * sc.z, bf2f(sv[3]) * sc.w};
     }
 #pragma unroll
     for (int k = 0; k < i; ++k) {  // acc -= A_ik X_k  (Ab holds -A)
@@ -276,8 +272,8 @@ __global__ void __launch_bounds__(256 * TEAMS) k_wy(WyArgs a, const int4* __rest
         *reinterpret_cast<short4v*>(Ug + (((4 * w + j) * 2 + sl) * 64 + q * 16 + li) * 8 + 4 * (lq & 1)) = xb[i][j];
       }
   }
-  __syncthreads();  // V^ transposed is dead: stage Wk over it
-  uint16_t* Ws = VTs;  // [64][136]
+  __syncthreads();  // the v^ rows are dead: stage Wk over them
+  uint16_t* Ws = Vs;  // [64][136]
   constexpr int kOLd = 136;
   if (wk_tiles) {
 #pragma unroll
