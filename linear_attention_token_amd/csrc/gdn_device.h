@@ -85,6 +85,18 @@ template <> struct vec16<bf16> {
   }
 };
 
+// Non-temporal 16-byte accesses, for streams touched once per step (read-once inputs, results
+// read back only by a later kernel): they do not displace data that is reused soon from the
+// caches.
+typedef uint32_t u32x4nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldnt16(const void* p) {
+  const u32x4nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x4nt*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void stnt16(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4nt*>(p));
+}
+
 // MFMA operand / accumulator vectors.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short8 __attribute__((ext_vector_type(8)));

@@ -61,16 +61,20 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
   __shared__ float red[4][64];
 
   // B operands of this wave's columns (chunk state and W), issued first so they overlap the rest;
-  // the state pass stores them as these operand pieces, 1 KB of consecutive bytes per load
+  // the state pass stores them as these operand pieces, 1 KB of consecutive bytes per load. They,
+  // the gate and the output are touched once, so they go non-temporal, leaving the caches to q^ and
+  // k^, which the value heads of a QK head share.
   const uint16_t* st = a.ST + (int64_t(c) * a.hv + h) * 128 * 128;
   const uint16_t* wt = a.WT + (int64_t(c) * a.hv + h) * 128 * 64;
   short8 bs[2][4], bw[2][2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bs[nt][s] = ld_short8(st + (((w * 2 + nt) * 4 + s) * 64 + lane) * 8);
+    for (int s = 0; s < 4; ++s)
+      bs[nt][s] = __builtin_nontemporal_load(reinterpret_cast<const short8*>(st + (((w * 2 + nt) * 4 + s) * 64 + lane) * 8));
 #pragma unroll
-    for (int s = 0; s < 2; ++s) bw[nt][s] = ld_short8(wt + (((w * 2 + nt) * 2 + s) * 64 + lane) * 8);
+    for (int s = 0; s < 2; ++s)
+      bw[nt][s] = __builtin_nontemporal_load(reinterpret_cast<const short8*>(wt + (((w * 2 + nt) * 2 + s) * 64 + lane) * 8));
   }
   // gate logits as whole token rows: piece idx = tid + 256 it is token idx / 16, channels
   // 8 (idx % 16) .. +7 (rows past the chunk end read the last row; their outputs are not stored)
@@ -81,8 +85,7 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
     const int idx = tid + it * 256;
     gq[it] = make_uint4(0u, 0u, 0u, 0u);
     if (a.flags & GDN_GATE)
-      gq[it] = *reinterpret_cast<const uint4*>(a.gate + (start + min(idx >> 4, len - 1)) * orow + h * 128 +
-                                               (idx & 15) * 8);
+      gq[it] = ldnt16(a.gate + (start + min(idx >> 4, len - 1)) * orow + h * 128 + (idx & 15) * 8);
   }
   // zero-centred gain (1 + w) of this lane's 8 channels
   float gain[2][4];
@@ -209,8 +212,7 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
   for (int it = 0; it < 4; ++it) {
     const int idx = tid + it * 256, t = idx >> 4;
     if (t < len)
-      *reinterpret_cast<uint4*>(a.out + (start + t) * orow + h * 128 + (idx & 15) * 8) =
-          *reinterpret_cast<const uint4*>(&Os[t * kLd + (idx & 15) * 8]);
+      stnt16(a.out + (start + t) * orow + h * 128 + (idx & 15) * 8, *reinterpret_cast<const uint4*>(&Os[t * kLd + (idx & 15) * 8]));
   }
 }
 

@@ -52,9 +52,10 @@ struct StateArgs {
 // the MFMA operand reads (rows pi(16t + i), i < 16, one piece) hit distinct banks.
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-// 16-byte global store of a register piece.
+// 16-byte global store of a register piece; non-temporal, since the pieces are read back only by
+// the output kernel, while the ring's operands are reused from the caches by neighbouring blocks.
 __device__ __forceinline__ void stg16(uint16_t* gptr, const short8& v) {
-  *reinterpret_cast<short8*>(gptr) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<short8*>(gptr));
 }
 
 constexpr int kDepth = 4;  // ring slots
@@ -160,8 +161,14 @@ k_state(StateArgs a) {
     float4 gt[4];
     float gc;
   };
+  // LDS returns reads in issue order, so they are issued in the order the chunk step consumes
+  // them (G, Wk, U, K^T): each wait then covers only what the next instruction needs.
   auto read_ops = [&](int slot, Ops& o) {
     const unsigned char* sb = smem + size_t(slot) * kSlot;
+    const float* Gl = reinterpret_cast<const float*>(sb + kOffG);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o.gt[k] = *reinterpret_cast<const float4*>(Gl + 32 * (k >> 1) + 8 * lq + 4 * (k & 1));
+    o.gc = Gl[63];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -170,21 +177,17 @@ k_state(StateArgs a) {
         o.wk[t][s] = *reinterpret_cast<const short8*>(sb + kOffWk + r * 256 + (((4 * s + lq) ^ wk_key(r)) << 4));
       }
 #pragma unroll
+    for (int v = 0; v < kTilesPerWave; ++v)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        o.up[v][s] = *reinterpret_cast<const uint4*>(sb + kOffU + ((kTilesPerWave * w + v) * 2 + s) * 1024 + lane * 16);
+#pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int r = srow[m];
         o.kt[m][s] = *reinterpret_cast<const short8*>(sb + kOffKT + r * 128 + (((4 * s + lq) ^ kt_key(r)) << 4));
       }
-#pragma unroll
-    for (int v = 0; v < kTilesPerWave; ++v)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        o.up[v][s] = *reinterpret_cast<const uint4*>(sb + kOffU + ((kTilesPerWave * w + v) * 2 + s) * 1024 + lane * 16);
-    const float* Gl = reinterpret_cast<const float*>(sb + kOffG);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o.gt[k] = *reinterpret_cast<const float4*>(Gl + 32 * (k >> 1) + 8 * lq + 4 * (k & 1));
-    o.gc = Gl[63];
   };
 
   // Ring schedule (kDepth = 4 slots): the producers keep two chunks in flight and, before barrier
@@ -277,7 +280,9 @@ k_state(StateArgs a) {
 #pragma unroll
       for (int v = 0; v < kTilesPerWave; ++v) S[v][m] = acc[v];
     }
-    if (c + 1 < c1) read_ops(int((j + 1) % kDepth), op);  // the next chunk's, over this one's MFMAs
+    // the next chunk's operands, over this one's MFMAs (unconditional, so that they share the
+    // MFMAs' basic block; after the last chunk the slot's contents are read and not used)
+    read_ops(int((j + 1) % kDepth), op);
     barrier();
   }
   if (producer) {
