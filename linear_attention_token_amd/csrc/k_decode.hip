@@ -170,12 +170,16 @@ __global__ void __launch_bounds__(768) k_decode(DecodeArgs a) {
 // group's value heads one after another. Thread (cg, rg) = (t % 32, t / 32) holds columns 4cg .. +3
 // of rows rg + 8j (j < 16) of a head's state, so one load instruction of a wave reads two adjacent
 // 512-byte rows. The first head's state is requested before the conv runs and each next head's
-// before the current one is reduced, so a block always has a state in flight; two blocks share a
-// CU. State is streamed with non-temporal loads and stores (each byte is touched once per step).
+// before the current one is reduced, so a block always has a state in flight; three blocks share
+// a CU (167 VGPRs, no spills: the staging below keeps the per-head registers to the two states). State is streamed with non-temporal loads and stores (each byte is touched once per step).
+// Everything else a head needs (alpha, beta, gain, gate logits) is staged in LDS up front, and every
+// wave issues the same memory instructions in every head (the last head's prefetch goes through an
+// empty buffer range, which reads zeros without touching memory), so the compiler's waits for the
+// prefetched state are exact counts that let the previous head's stores stay in flight.
 constexpr int kD = 128;
 
 template <typename IO>
-__global__ void __launch_bounds__(256, 2) k_decode_d128(DecodeArgs a) {
+__global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
   extern __shared__ float smem[];
   // block = b * hk + g: consecutive blocks stream consecutive 192 KB pieces of the state
   const int b = int(blockIdx.x / unsigned(a.hk)), g = int(blockIdx.x - unsigned(b) * unsigned(a.hk));
@@ -184,6 +188,8 @@ __global__ void __launch_bounds__(256, 2) k_decode_d128(DecodeArgs a) {
   const int R = a.R;
   float* act = smem;                    // [(2 + R) * 128]: q | k | v of the group's heads, after conv + SiLU
   float* red = smem + (2 + 2 * R) * kD;  // [2 buffers][4 waves][a, b][128]
+  float* nwsh = red + 8 * kD * 2;        // [R * 128] zero-centred gains (1 + w)
+  float* absh = nwsh + R * kD;           // [2 R] alpha, beta of the group's heads
   __shared__ float nrm[8];
 
   const size_t head = size_t(kD) * kD;
@@ -256,6 +262,9 @@ __global__ void __launch_bounds__(256, 2) k_decode_d128(DecodeArgs a) {
       if (t + 256 * u < nv) gsh[t + 256 * u] = gv[u];
     for (int c = t + 512; c < nv; c += 256) gsh[c] = io<IO>::ld(gsrc + c);
   }
+  for (int c = t; c < nv; c += 256)
+    nwsh[c] = 1.0f + ((a.flags & GDN_NORM) ? a.norm_w[size_t(g * R + c / kD) * a.norm_stride + c % kD] : 0.f);
+  for (int c = t; c < 2 * R; c += 256) absh[c] = (c < R ? a.alpha : a.beta)[size_t(b) * a.hv + g * R + (c < R ? c : c - R)];
   const float u = u_qk;
   // |q|^2 (waves 0, 1) and |k|^2 (waves 2, 3), then q.k
   {
@@ -275,9 +284,9 @@ __global__ void __launch_bounds__(256, 2) k_decode_d128(DecodeArgs a) {
 
   for (int r = 0; r < R; ++r) {
     const int h = g * R + r;
-    const float al = a.alpha[size_t(b) * a.hv + h], be = a.beta[size_t(b) * a.hv + h];
-    if (r + 1 < R) {
-      const auto rn = buf_rsrc(S0 + size_t(r + 1) * head, int(head * 4));
+    const float al = absh[r], be = absh[R + r];
+    {  // the next head's state; after the last head an empty range (zeros, no memory access)
+      const auto rn = buf_rsrc(S0 + size_t(r + 1 < R ? r + 1 : r) * head, r + 1 < R ? int(head * 4) : 0);
 #pragma unroll
       for (int j = 0; j < 16; ++j) N[j] = buf_ld16_nt(rn, soff, 4096 * j);
     }
@@ -328,19 +337,14 @@ __global__ void __launch_bounds__(256, 2) k_decode_d128(DecodeArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) S[j] = N[j];
-    // RMSNorm over the head's 128 outputs (the 32 lanes of a row group hold them all), gain, gate
+    // RMSNorm over the head's 128 outputs (every row group holds them all), gain, gate; wave w
+    // stores channel col + w of each column group (its two row groups write the same values)
     const float ss = group_sum<32>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
-    if (rg == 0) {
-      const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(ss / float(kD) + a.norm_eps) : 1.0f;
-      IO* op = static_cast<IO*>(a.out) + (size_t(b) * a.hv + h) * kD + col;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float o = y[e];
-        if (a.flags & GDN_NORM) o = o * rs * (1.0f + a.norm_w[size_t(h) * a.norm_stride + col + e]);
-        if (gate) o *= sigmoidf_(gsh[r * kD + col + e]);
-        io<IO>::st(op + e, o);
-      }
-    }
+    const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(ss / float(kD) + a.norm_eps) : 1.0f;
+    const float yw = w == 0 ? y[0] : w == 1 ? y[1] : w == 2 ? y[2] : y[3];
+    float o = yw * rs * nwsh[r * kD + col + w];
+    if (gate) o *= sigmoidf_(gsh[r * kD + col + w]);
+    io<IO>::st(static_cast<IO*>(a.out) + (size_t(b) * a.hv + h) * kD + col + w, o);
   }
 }
 
@@ -362,7 +366,7 @@ hipError_t launch_decode(const Problem& p, int batch, const void* q, const void*
                p.l2_eps, p.norm_eps};
   dim3 grid(unsigned(batch), unsigned(p.hk));
   if (p.dk == kD && p.dv == kD) {
-    const size_t smem = size_t(2 + 2 * R) * kD * 4 + 8 * kD * 4 * 2;
+    const size_t smem = size_t(2 + 2 * R) * kD * 4 + 8 * kD * 4 * 2 + size_t(R) * kD * 4 + size_t(2 * R) * 4;
     const dim3 grid1(unsigned(batch) * unsigned(p.hk));
     if (p.bf16) hipLaunchKernelGGL(k_decode_d128<bf16>, grid1, dim3(256), smem, s, a);
     else hipLaunchKernelGGL(k_decode_d128<float>, grid1, dim3(256), smem, s, a);
