@@ -16,7 +16,10 @@ Sources (the pages this follows; all quoted facts are restated, not copied):
        short conv + SiLU + L2 normalisation.
   [P5] "Qwen3.8-Flash-Next" paper summary (hyper.ai, English), Method: learned projections then
        short depthwise causal convolutions; L2-normalised queries and keys; head outputs are
-       normalised and then modulated by a sigmoid output gate.
+       normalised and then modulated by a sigmoid output gate. Results: four-step speculative
+       decoding with multi-token prediction (MTP), mean accepted length about 4.
+  [P2] §01 (MTP row: one layer trained for multi-step prediction) and the §04 results table
+       (four-step MTP accepted length): drafts of several tokens are checked in one pass.
 
 Readings where the pages are silent (every one is also listed in the design notes):
   * conv + SiLU on q, k and v; L2 on q and k only.
@@ -233,3 +236,44 @@ def gdn_decode(step, state, conv_state, conv_w, norm_w, *, flags=FLAG_ALL, scale
     inp.update(cu_seqlens=np.arange(B + 1), conv_w=conv_w, norm_w=norm_w,
                state_in=state, conv_in=conv_state)
     return gdn_prefill(inp, flags=flags, scale=scale, l2_eps=l2_eps, norm_eps=norm_eps)
+
+
+def _rows(x, rows):
+    """Rows ``rows`` of a [T, ...] array or tensor, as fp64."""
+    return _f64(x)[np.asarray(rows, dtype=np.int64)]
+
+
+def gdn_verify(steps, state, conv_state, conv_w, norm_w, *, n_tok, flags=FLAG_ALL, scale=1.0,
+               l2_eps=1e-6, norm_eps=1e-6):
+    """Speculative verify: each of the B sequences brings K = ``n_tok`` draft tokens (rows
+    b*K .. b*K+K-1 of ``steps``), which run through the mixer from the sequence's cached state and
+    conv cache. Checking a multi-token draft in one pass is how the four-step MTP decoding of the
+    pages ([P5] results, [P2] §01 / §04) uses the layer. The cache itself is not advanced here.
+
+    ``steps`` holds q [B*K,HK,dk], k [B*K,HK,dk], v [B*K,HV,dv], alpha/beta [B*K,HV],
+    gate [B*K,HV,dv]. Returns o [B*K,HV,dv] in fp64: by definition the prefill of each draft
+    (a sequence of length K) from that cache.
+    """
+    B = int(np.asarray(_f64(state)).shape[0])
+    inp = dict(steps)
+    inp.update(cu_seqlens=np.arange(B + 1) * n_tok, conv_w=conv_w, norm_w=norm_w,
+               state_in=state, conv_in=conv_state)
+    o, _, _ = gdn_prefill(inp, flags=flags, scale=scale, l2_eps=l2_eps, norm_eps=norm_eps)
+    return o
+
+
+def gdn_commit(steps, n_accept, state, conv_state, conv_w, norm_w, *, n_tok, flags=FLAG_ALL,
+               scale=1.0, l2_eps=1e-6, norm_eps=1e-6):
+    """Speculative commit: the state and conv cache of sequence b after its first ``n_accept[b]``
+    draft tokens (0 <= n <= K), i.e. the cache a prefill of only the accepted tokens leaves.
+    Returns (state [B,HV,dk,dv], conv cache [B,3,C]) in fp64.
+    """
+    B = int(np.asarray(_f64(state)).shape[0])
+    n = [int(x) for x in np.asarray(n_accept).reshape(-1)]
+    assert len(n) == B and all(0 <= x <= n_tok for x in n)
+    rows = [b * n_tok + t for b in range(B) for t in range(n[b])]
+    inp = {key: _rows(steps[key], rows) for key in ("q", "k", "v", "alpha", "beta", "gate")}
+    inp.update(cu_seqlens=np.concatenate([[0], np.cumsum(n)]), conv_w=conv_w, norm_w=norm_w,
+               state_in=state, conv_in=conv_state)
+    _, S, c = gdn_prefill(inp, flags=flags, scale=scale, l2_eps=l2_eps, norm_eps=norm_eps)
+    return S, c

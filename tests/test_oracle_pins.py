@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle as O
-from workloads import prefill_inputs
+from workloads import prefill_inputs, decode_inputs
 
 
 def _rand_chain(rng, L, dk, dv, unit_k=True):
@@ -363,3 +363,59 @@ def test_short_sequences_take_history_from_conv_in():
     np.testing.assert_array_equal(c[0][:2], ci[0][1:])
     np.testing.assert_array_equal(c[0][2], x0)
     np.testing.assert_array_equal(c[1][0], ci[1][2])
+
+
+# ------------------------------------------------------------- speculative verify / commit -----
+
+def _drafts(B, K, hk=2, hv=4, d=8, seed=5):
+    """K draft tokens for B sequences: the step-major draw of decode_inputs, re-laid out with the
+    drafts of sequence b in rows b*K .. b*K+K-1, plus the same steps kept step-major."""
+    di = decode_inputs(B, K, n_qk_heads=hk, n_v_heads=hv, d_k=d, d_v=d, io_dtype=torch.float32,
+                       seed=seed, state_std=0.1)
+    steps = {key: getattr(di, key) for key in ("q", "k", "v", "alpha", "beta", "gate")}
+    packed = {key: x.transpose(0, 1).reshape(B * K, *x.shape[2:]) for key, x in steps.items()}
+    return di, steps, packed
+
+
+def _decode_run(di, steps, n_steps):
+    """The oracle's one-token decode step applied n_steps times per sequence, cache carried."""
+    S, c = di.state, di.conv_state
+    outs = []
+    for t in range(n_steps):
+        step = {key: x[t] for key, x in steps.items()}
+        o, S, c = O.gdn_decode(step, S, c, di.conv_w, di.norm_w)
+        outs.append(o)
+    return outs, S, c
+
+
+def test_verify_equals_token_by_token_decode():
+    """Verifying K drafts in one pass gives, token for token, the outputs of K decode steps, and
+    leaves the cache it reads untouched."""
+    B, K = 3, 4
+    di, steps, packed = _drafts(B, K)
+    S0, c0 = di.state.clone(), di.conv_state.clone()
+    o = O.gdn_verify(packed, di.state, di.conv_state, di.conv_w, di.norm_w, n_tok=K)
+    outs, _, _ = _decode_run(di, steps, K)
+    for t in range(K):
+        assert np.array_equal(o.reshape(B, K, *o.shape[1:])[:, t], outs[t])
+    assert torch.equal(di.state, S0) and torch.equal(di.conv_state, c0)
+
+
+@pytest.mark.parametrize("n_accept", [[0, 0, 0], [4, 4, 4], [0, 4, 2], [1, 3, 0]])
+def test_commit_equals_accepted_decode_steps(n_accept):
+    """Committing n of the K drafts leaves exactly the cache of n decode steps (n = 0: the cache
+    unchanged), per sequence."""
+    B, K = 3, 4
+    di, steps, packed = _drafts(B, K)
+    S, c = O.gdn_commit(packed, np.array(n_accept), di.state, di.conv_state, di.conv_w, di.norm_w, n_tok=K)
+    for b, n in enumerate(n_accept):
+        one = {key: x[:, b:b + 1] for key, x in steps.items()}
+        sub = type("D", (), {})()
+        sub.state, sub.conv_state = di.state[b:b + 1], di.conv_state[b:b + 1]
+        sub.conv_w, sub.norm_w = di.conv_w, di.norm_w
+        _, Sn, cn = _decode_run(sub, one, n)
+        as64 = lambda x: x.double().numpy() if torch.is_tensor(x) else np.asarray(x, dtype=np.float64)
+        assert np.array_equal(S[b], as64(Sn)[0]) and np.array_equal(c[b], as64(cn)[0])
+    for b, n in enumerate(n_accept):
+        if n == 0:
+            assert np.array_equal(S[b], di.state[b].double().numpy())
