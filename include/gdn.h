@@ -141,6 +141,53 @@ gdn_status gdn_decode_step(const gdn_cfg* cfg, int32_t batch,
                            const float* conv_w, const float* norm_w,
                            void* conv_state, float* state, void* out, void* hip_stream);
 
+/* Speculative (multi-token) decoding, as used with the multi-token-prediction (MTP) drafts of the
+ * pages' four-step speculative decoding (paper summary "Qwen3.8-Flash-Next", results; analysis
+ * notes "Qwen3.8-Flash-Next：架构、效率与技术谱系" §01 MTP row, §04 results table): each sequence
+ * brings a draft of K tokens, the layer runs all of them in one call (gdn_verify), and once the
+ * caller knows how many were accepted, gdn_commit advances the cache by that prefix.
+ *
+ * gdn_verify is the prefill of each draft (a sequence of K tokens) from the sequence's cached state
+ * and conv cache, which it only reads. It also fills `log` with what gdn_commit needs: per draft
+ * token, the normalised key of each QK head, the error e = v - alpha S^T k of each value head
+ * (fp32), alpha, beta and the raw conv inputs -- about (HK + HV) KB per token instead of a 64 KB
+ * state checkpoint per value head. gdn_commit then applies the first n_accept[b] of those rank-1
+ * updates, S <- alpha S + beta k e^T, with the same fp32 operations verify used, so the committed
+ * state equals verify's state after that many tokens (and, to fp32 rounding, that many decode
+ * steps). Supported for d_k = d_v = 128, HV/HK <= 4, 1 <= n_tok <= 8, either io dtype; other
+ * shapes return GDN_E_UNSUPPORTED.
+ *
+ * gdn_verify_log_bytes: bytes of the log for (cfg, batch, n_tok). Pure host computation.
+ *
+ * gdn_verify arguments (B = batch, K = n_tok; the drafts of sequence b are token rows b*K .. b*K+K-1):
+ *   q, k        io [B*K][HK][d_k], row stride ld_q / ld_k;  v io [B*K][HV][d_v], row stride ld_v.
+ *   alpha, beta fp32 [B*K][HV];  gate io [B*K][HV][d_v] (iff GDN_GATE).
+ *   conv_w, norm_w as for gdn_prefill.
+ *   conv_state  io [B][3][C_tot], read only (iff GDN_CONV).
+ *   state       fp32 [B][HV][d_k][d_v], read only.
+ *   out         io [B*K][HV][d_v]: the layer output of every draft token.
+ *   log         device buffer of at least gdn_verify_log_bytes() bytes, 256-byte aligned, owned by
+ *               the caller; overwritten. It must stay unchanged until the matching gdn_commit.
+ *
+ * gdn_commit arguments (same cfg, batch and n_tok as the verify that filled `log`):
+ *   n_accept    device int32 [B]: accepted drafts per sequence; values outside [0, K] are clamped.
+ *               Sequences with 0 are left untouched.
+ *   conv_state  io [B][3][C_tot], advanced in place to end with the last accepted token (iff
+ *               GDN_CONV).
+ *   state       fp32 [B][HV][d_k][d_v], advanced in place.
+ * A commit with every n_accept = K leaves the cache a K-token decode would; calling gdn_commit
+ * twice on one log applies the prefix twice. */
+gdn_status gdn_verify_log_bytes(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, size_t* bytes);
+gdn_status gdn_verify(const gdn_cfg* cfg, int32_t batch, int32_t n_tok,
+                      const void* q, const void* k, const void* v,
+                      int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                      const float* alpha, const float* beta, const void* gate,
+                      const float* conv_w, const float* norm_w,
+                      const void* conv_state, const float* state, void* out,
+                      void* log, size_t log_bytes, void* hip_stream);
+gdn_status gdn_commit(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, const int32_t* n_accept,
+                      const void* log, size_t log_bytes, void* conv_state, float* state, void* hip_stream);
+
 /* Stage timing for profilers (host-side, per calling thread). After this call, every gdn_prefill
  * on this thread records events[i] on its stream before stage i and events[GDN_N_STAGES] after the
  * last stage, for the stages

@@ -312,4 +312,101 @@ gdn_status gdn_decode_step(const gdn_cfg* cfg, int32_t batch,
   return GDN_OK;
 }
 
+// Shape checks shared by the speculative-decoding entry points; fills p for B sequences of K drafts.
+static gdn_status check_mtp(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, Problem& p) {
+  gdn_status st = check_cfg(cfg, p);
+  if (st != GDN_OK) return st;
+  if (batch < 0) return fail(GDN_E_SHAPE, "negative batch %d", batch);
+  if (n_tok < 1) return fail(GDN_E_SHAPE, "n_tok = %d: a draft has at least one token", n_tok);
+  if (n_tok > kMaxDrafts) return fail(GDN_E_UNSUPPORTED, "n_tok = %d > %d draft tokens", n_tok, kMaxDrafts);
+  if (p.dk != 128 || p.dv != 128)
+    return fail(GDN_E_UNSUPPORTED, "speculative decoding is implemented for d_k = d_v = 128 (got %d, %d)", p.dk, p.dv);
+  if (p.hv / p.hk > kMaxMtpRatio)
+    return fail(GDN_E_UNSUPPORTED, "speculative decoding needs HV/HK <= %d (got %d)", kMaxMtpRatio, p.hv / p.hk);
+  if (int64_t(batch) * p.hk * 256 > int64_t(UINT32_MAX))
+    return fail(GDN_E_UNSUPPORTED, "batch x QK heads = %lld is too large for one launch", (long long)batch * p.hk);
+  p.n_seqs = batch;
+  p.T = int64_t(batch) * n_tok;
+  p.nc_max = 0;
+  return GDN_OK;
+}
+
+gdn_status gdn_verify_log_bytes(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, size_t* bytes) {
+  g_last_error[0] = 0;
+  if (!bytes) return fail(GDN_E_NULL, "bytes is NULL");
+  Problem p{};
+  const gdn_status st = check_mtp(cfg, batch, n_tok, p);
+  if (st != GDN_OK) return st;
+  *bytes = plan_mtp_log(p, batch, n_tok, nullptr).bytes;
+  return GDN_OK;
+}
+
+gdn_status gdn_verify(const gdn_cfg* cfg, int32_t batch, int32_t n_tok,
+                      const void* q, const void* k, const void* v,
+                      int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                      const float* alpha, const float* beta, const void* gate,
+                      const float* conv_w, const float* norm_w,
+                      const void* conv_state, const float* state, void* out,
+                      void* log, size_t log_bytes, void* hip_stream) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_mtp(cfg, batch, n_tok, p);
+  if (st != GDN_OK) return st;
+  const uint32_t f = p.flags;
+  if (batch > 0) {
+    if (!q || !k || !v) return fail(GDN_E_NULL, "q, k and v are required");
+    if (!alpha || !beta) return fail(GDN_E_NULL, "alpha and beta are required");
+    if (!state) return fail(GDN_E_NULL, "state is required");
+    if (!out) return fail(GDN_E_NULL, "out is required");
+    if (!log) return fail(GDN_E_NULL, "log is required");
+    if ((f & GDN_GATE) && !gate) return fail(GDN_E_NULL, "gate is required with GDN_GATE");
+    if ((f & GDN_NORM) && !norm_w) return fail(GDN_E_NULL, "norm_w is required with GDN_NORM");
+    if ((f & GDN_CONV) && (!conv_w || !conv_state)) return fail(GDN_E_NULL, "conv_w and conv_state are required with GDN_CONV");
+  }
+  const int64_t elem = p.bf16 ? 2 : 4;
+  const int64_t qrow = int64_t(p.hk) * p.dk, vrow = int64_t(p.hv) * p.dv;
+  if (ld_q < qrow || ld_k < qrow || ld_v < vrow) return fail(GDN_E_SHAPE, "row strides too small");
+  if ((ld_q * elem) % 16 || (ld_k * elem) % 16 || (ld_v * elem) % 16)
+    return fail(GDN_E_ALIGN, "row strides must be multiples of 16 bytes");
+  const void* ptrs[] = {q, k, v, gate, conv_w, norm_w, conv_state, state, out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (!aligned4(alpha) || !aligned4(beta)) return fail(GDN_E_ALIGN, "alpha and beta must be 4-byte aligned");
+  if (log && (reinterpret_cast<uintptr_t>(log) & 255u)) return fail(GDN_E_ALIGN, "log must be 256-byte aligned");
+  const MtpLog need = plan_mtp_log(p, batch, n_tok, nullptr);
+  if (batch > 0 && log_bytes < need.bytes) return fail(GDN_E_WORKSPACE, "log has %zu bytes, %zu needed", log_bytes, need.bytes);
+  if (batch == 0) return GDN_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (run(launch_verify(p, batch, n_tok, q, k, v, ld_q, ld_k, ld_v, alpha, beta, gate, conv_w, norm_w, conv_state,
+                        state, out, plan_mtp_log(p, batch, n_tok, log), s), "verify") != hipSuccess)
+    return GDN_E_HIP;
+  return GDN_OK;
+}
+
+gdn_status gdn_commit(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, const int32_t* n_accept,
+                      const void* log, size_t log_bytes, void* conv_state, float* state, void* hip_stream) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_mtp(cfg, batch, n_tok, p);
+  if (st != GDN_OK) return st;
+  if (batch > 0) {
+    if (!n_accept) return fail(GDN_E_NULL, "n_accept is required");
+    if (!log) return fail(GDN_E_NULL, "log is required");
+    if (!state) return fail(GDN_E_NULL, "state is required");
+    if ((p.flags & GDN_CONV) && !conv_state) return fail(GDN_E_NULL, "conv_state is required with GDN_CONV");
+  }
+  if ((state && !aligned16(state)) || (conv_state && !aligned16(conv_state)))
+    return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (!aligned4(n_accept)) return fail(GDN_E_ALIGN, "n_accept must be 4-byte aligned");
+  if (log && (reinterpret_cast<uintptr_t>(log) & 255u)) return fail(GDN_E_ALIGN, "log must be 256-byte aligned");
+  const MtpLog need = plan_mtp_log(p, batch, n_tok, nullptr);
+  if (batch > 0 && log_bytes < need.bytes) return fail(GDN_E_WORKSPACE, "log has %zu bytes, %zu needed", log_bytes, need.bytes);
+  if (batch == 0) return GDN_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  MtpLog L = plan_mtp_log(p, batch, n_tok, const_cast<void*>(log));
+  if (run(launch_commit(p, batch, n_tok, n_accept, L, conv_state, state, s), "commit") != hipSuccess)
+    return GDN_E_HIP;
+  return GDN_OK;
+}
+
 }  // extern "C"

@@ -106,4 +106,24 @@ hipError_t launch_decode(const Problem& p, int batch, const void* q, const void*
                          const void* gate, const float* conv_w, const float* norm_w, void* conv_state,
                          float* state, void* out, hipStream_t s);
 
+// Log of a speculative verify (multi-token decode), read back by the commit: per sequence b and
+// draft token t, the normalised key of each QK head, the error e of each value head, alpha and
+// beta, and (with the conv) the raw inputs. Regions are 256-byte aligned, in this order.
+constexpr int kMaxDrafts = 8;   // draft tokens per verify
+constexpr int kMaxMtpRatio = 4; // value heads per QK head on the verify path
+struct MtpLog {
+  float* kh = nullptr;   // fp32 [B][K][HK][d_k]
+  float* e = nullptr;    // fp32 [B][K][HV][d_v]
+  float* ab = nullptr;   // fp32 [B][K][HV][2]
+  void* raw = nullptr;   // io   [B][K][C]
+  size_t bytes = 0;
+};
+MtpLog plan_mtp_log(const Problem& p, int batch, int n_tok, void* base);
+hipError_t launch_verify(const Problem& p, int batch, int n_tok, const void* q, const void* k, const void* v,
+                         int64_t ld_q, int64_t ld_k, int64_t ld_v, const float* alpha, const float* beta,
+                         const void* gate, const float* conv_w, const float* norm_w, const void* conv_state,
+                         const float* state, void* out, const MtpLog& log, hipStream_t s);
+hipError_t launch_commit(const Problem& p, int batch, int n_tok, const int32_t* n_accept, const MtpLog& log,
+                         void* conv_state, float* state, hipStream_t s);
+
 }  // namespace gdn

@@ -20,6 +20,7 @@ GDN_CONV, GDN_L2QK, GDN_NORM, GDN_GATE, GDN_ALL = 1, 2, 4, 8, 15
 STATUS = {0: "GDN_OK", 1: "GDN_E_NULL", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE", 4: "GDN_E_ALIGN",
           5: "GDN_E_WORKSPACE", 6: "GDN_E_UNSUPPORTED", 7: "GDN_E_HIP", 8: "GDN_E_VALUE"}
 EXPORTS = ("gdn_cfg_default", "gdn_prefill_workspace", "gdn_prefill", "gdn_decode_step",
+           "gdn_verify_log_bytes", "gdn_verify", "gdn_commit",
            "gdn_set_stage_events", "gdn_status_string", "gdn_last_error", "gdn_abi_version")
 N_STAGES = 6
 STAGE_NAMES = ("chunk_table", "conv_silu_l2", "wy_or_sequential", "state", "output_norm_gate", "conv_tail")
@@ -64,6 +65,15 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode_step.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, _P, _P, _P, _I64, _I64,
                                     _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_verify_log_bytes.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_verify_log_bytes.restype = ctypes.c_int
+    lib.gdn_verify.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _I64, _I64,
+                               _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_verify.restype = ctypes.c_int
+    lib.gdn_commit.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t,
+                               _P, _P, _P]
+    lib.gdn_commit.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -238,6 +248,59 @@ def gdn_decode_step(cfg: gdn_cfg, q, k, v, alpha, beta, gate, conv_w, norm_w, co
                              _stream(stream))
     _check(st)
     return out
+
+
+def gdn_verify_log_bytes(cfg: gdn_cfg, batch: int, n_tok: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().gdn_verify_log_bytes(ctypes.byref(cfg), batch, n_tok, ctypes.byref(n)))
+    return int(n.value)
+
+
+def gdn_verify(cfg: gdn_cfg, n_tok: int, q, k, v, alpha, beta, gate, conv_w, norm_w, conv_state, state,
+               out=None, log=None, stream=None):
+    """Speculative verify of ``n_tok`` draft tokens per sequence (rows b*K .. b*K+K-1 of q, k, v,
+    alpha, beta, gate). Reads ``state`` and ``conv_state`` without changing them; returns
+    (out [B*K, HV, d_v], log), allocating either when not given."""
+    lib = load_library()
+    io = _io_dtype(cfg)
+    T = _check_qkv(cfg, q, k, v, io)
+    if n_tok < 1 or T % n_tok:
+        raise ValueError(f"{T} token rows are not a whole number of {n_tok}-token drafts")
+    B = T // n_tok
+    if out is None:
+        out = torch.empty((T, cfg.n_v_heads, cfg.d_v), dtype=io, device=q.device)
+    C = _check_common(cfg, T, io, alpha, beta, gate, conv_w, norm_w, out)
+    _expect(state, (B, cfg.n_v_heads, cfg.d_k, cfg.d_v), torch.float32, "state")
+    _expect(conv_state, (B, 3, C), io, "conv_state", optional=not (cfg.flags & GDN_CONV))
+    need = gdn_verify_log_bytes(cfg, B, n_tok)
+    if log is None:
+        log = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if log.dtype != torch.uint8 or log.numel() < need:
+        raise ValueError(f"log needs {need} uint8 elements")
+    st = lib.gdn_verify(ctypes.byref(cfg), B, n_tok, _ptr(q), _ptr(k), _ptr(v),
+                        _row_stride(q, cfg.n_qk_heads * cfg.d_k), _row_stride(k, cfg.n_qk_heads * cfg.d_k),
+                        _row_stride(v, cfg.n_v_heads * cfg.d_v), _ptr(alpha), _ptr(beta), _ptr(gate),
+                        _ptr(conv_w), _ptr(norm_w), _ptr(conv_state), _ptr(state), _ptr(out),
+                        _ptr(log), log.numel(), _stream(stream))
+    _check(st)
+    return out, log
+
+
+def gdn_commit(cfg: gdn_cfg, n_tok: int, n_accept, log, conv_state, state, stream=None) -> None:
+    """Advances ``state`` and ``conv_state`` in place by the first ``n_accept[b]`` drafts of the
+    verify that filled ``log`` (``n_accept``: int32 [B] on the GPU)."""
+    lib = load_library()
+    io = _io_dtype(cfg)
+    B = int(n_accept.numel())
+    C = 2 * cfg.n_qk_heads * cfg.d_k + cfg.n_v_heads * cfg.d_v
+    _expect(n_accept, (B,), torch.int32, "n_accept")
+    _expect(state, (B, cfg.n_v_heads, cfg.d_k, cfg.d_v), torch.float32, "state")
+    _expect(conv_state, (B, 3, C), io, "conv_state", optional=not (cfg.flags & GDN_CONV))
+    if log.dtype != torch.uint8:
+        raise ValueError("log must be the uint8 buffer gdn_verify filled")
+    st = lib.gdn_commit(ctypes.byref(cfg), B, n_tok, _ptr(n_accept), _ptr(log), log.numel(), _ptr(conv_state),
+                        _ptr(state), _stream(stream))
+    _check(st)
 
 
 def cfg_for(n_qk_heads: int, n_v_heads: int, d_k: int, d_v: int, dtype: torch.dtype,

@@ -147,3 +147,53 @@ def test_decode_rejects_bad_arguments():
     _err(_decode(c, ld=(2048, 2000, 6144)), 2)
     _err(_decode(gdn.gdn_cfg_default(d_k=100)), 6)
     _err(_decode(gdn.gdn_cfg_default(n_v_heads=40)), 2)
+
+
+def test_verify_log_sizes():
+    c = gdn.gdn_cfg_default()
+    n = gdn.gdn_verify_log_bytes(c, 256, 4)
+    # per token: k^ of 16 QK heads and e of 48 value heads in fp32, alpha/beta, raw inputs (bf16)
+    rows = 256 * 4
+    assert n >= rows * (16 * 128 * 4 + 48 * 128 * 4 + 48 * 8 + 10240 * 2)
+    assert n < rows * (16 * 128 * 4 + 48 * 128 * 4 + 48 * 8 + 10240 * 2) + 4 * 256
+    assert gdn.gdn_verify_log_bytes(c, 256, 5) > n
+    assert gdn.gdn_verify_log_bytes(c, 0, 4) == 0
+
+
+def _verify(cfg, B=4, K=4, q=A, k=A, v=A, alpha=A, beta=A, gate=A, conv_w=A, norm_w=A, conv_state=A,
+            state=A, out=A, log=A, log_bytes=1 << 40, ld=(2048, 2048, 6144)):
+    return lib.gdn_verify(ctypes.byref(cfg), B, K, q, k, v, ld[0], ld[1], ld[2], alpha, beta, gate, conv_w,
+                          norm_w, conv_state, state, out, log, log_bytes, None)
+
+
+def _commit(cfg, B=4, K=4, n_accept=A, log=A, log_bytes=1 << 40, conv_state=A, state=A):
+    return lib.gdn_commit(ctypes.byref(cfg), B, K, n_accept, log, log_bytes, conv_state, state, None)
+
+
+def test_verify_and_commit_reject_bad_arguments():
+    c = gdn.gdn_cfg_default()
+    nbytes = ctypes.c_size_t(0)
+    _err(lib.gdn_verify_log_bytes(ctypes.byref(c), 4, 0, ctypes.byref(nbytes)), 2)
+    _err(lib.gdn_verify_log_bytes(ctypes.byref(c), 4, 9, ctypes.byref(nbytes)), 6)
+    _err(lib.gdn_verify_log_bytes(ctypes.byref(c), 4, 4, None), 1)
+    for call in (_verify, _commit):
+        _err(call(c, B=-1), 2)
+        _err(call(c, K=0), 2)
+        _err(call(c, K=9), 6)
+        _err(call(gdn.gdn_cfg_default(d_k=64, d_v=64)), 6)        # only d = 128
+        _err(call(gdn.gdn_cfg_default(n_qk_heads=8, n_v_heads=48)), 6)  # HV/HK = 6 > 4
+        _err(call(c, log=None), 1)
+        _err(call(c, log=A + 128), 4)                              # log 256-byte aligned
+        _err(call(c, log_bytes=1024), 5)
+        _err(call(c, state=None), 1)
+        _err(call(c, state=A + 8), 4)
+        _err(call(c, conv_state=None), 1)
+    _err(_verify(c, out=None), 1)
+    _err(_verify(c, gate=None), 1)
+    _err(_verify(c, ld=(2048, 2000, 6144)), 2)
+    _err(_commit(c, n_accept=None), 1)
+    _err(_commit(c, n_accept=A + 2), 4)
+    # with the conv off the conv cache may be absent; an empty batch does nothing
+    off = gdn.gdn_cfg_default(flags=gdn.GDN_L2QK | gdn.GDN_NORM | gdn.GDN_GATE)
+    assert _verify(off, B=0, conv_state=None) == 0
+    assert _commit(off, B=0, conv_state=None) == 0

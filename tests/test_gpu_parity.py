@@ -376,3 +376,90 @@ def test_decode_equals_prefill_last_token():
     torch.cuda.synchronize()
     assert rel_l2(od[0], out[T - 1]) <= 1e-2 and rel_l2(sh, st) <= 1e-2
     assert torch.equal(ch, cv)
+
+
+# ------------------------------------------------------------- speculative verify / commit -------
+
+def _drafts(B, K, io, hk=2, hv=6, seed=31):
+    """K draft tokens for B sequences (decode_inputs' step-major draw), with the drafts of
+    sequence b as rows b*K .. b*K+K-1."""
+    di = decode_inputs(B, K, n_qk_heads=hk, n_v_heads=hv, d_k=128, d_v=128, io_dtype=io, seed=seed,
+                       device=DEV, state_std=0.02)
+    packed = {key: getattr(di, key).transpose(0, 1).reshape(B * K, *getattr(di, key).shape[2:]).contiguous()
+              for key in ("q", "k", "v", "alpha", "beta", "gate")}
+    return di, packed
+
+
+def _verify(cfg, K, di, p, state=None, conv=None):
+    return gdn.gdn_verify(cfg, K, p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["gate"], di.conv_w,
+                          di.norm_w, di.conv_state if conv is None else conv, di.state if state is None else state)
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("K", [1, 4, 5, 8])
+def test_verify_commit(io, K):
+    """Verify = the prefill of each K-token draft from the cache (which it leaves unchanged);
+    commit(n) = the cache after the first n drafts, per sequence (n = 0 leaves it untouched)."""
+    B = 5
+    di, p = _drafts(B, K, io)
+    cfg = gdn.cfg_for(2, 6, 128, 128, io)
+    S0, c0 = di.state.clone(), di.conv_state.clone()
+    print(f"verify io={io} K={K}", flush=True)
+    out, log = _verify(cfg, K, di, p)
+    torch.cuda.synchronize()
+    assert torch.equal(di.state, S0) and torch.equal(di.conv_state, c0)
+    cpu = {key: x.cpu() for key, x in p.items()}
+    o_ref = O.gdn_verify(cpu, S0.cpu(), c0.cpu(), di.conv_w.cpu(), di.norm_w.cpu(), n_tok=K)
+    e_o = rel_l2(out, o_ref)
+    n_acc = [0, K, K // 2, 1, K - 1]
+    print(f"commit n={n_acc}", flush=True)
+    gdn.gdn_commit(cfg, K, torch.tensor(n_acc, dtype=torch.int32, device=DEV), log, di.conv_state, di.state)
+    torch.cuda.synchronize()
+    S_ref, c_ref = O.gdn_commit(cpu, np.array(n_acc), S0.cpu(), c0.cpu(), di.conv_w.cpu(), di.norm_w.cpu(), n_tok=K)
+    e_s = rel_l2(di.state, S_ref)
+    print(f"rel_l2 out={e_o:.3e} state={e_s:.3e}", flush=True)
+    assert e_o <= TOL[io] and e_s <= TOL[io], (e_o, e_s)
+    np.testing.assert_array_equal(di.conv_state.double().cpu().numpy(), c_ref)
+    for b, n in enumerate(n_acc):
+        if n == 0:
+            assert torch.equal(di.state[b], S0[b]) and torch.equal(di.conv_state[b], c0[b])
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_commit_replays_verify_exactly(io):
+    """After committing 2 of 5 drafts, verifying the other 3 from the committed cache reproduces the
+    first verify's outputs for them bit for bit: commit applies exactly the updates verify made."""
+    B, K, n = 4, 5, 2
+    di, p = _drafts(B, K, io, seed=33)
+    cfg = gdn.cfg_for(2, 6, 128, 128, io)
+    out, log = _verify(cfg, K, di, p)
+    gdn.gdn_commit(cfg, K, torch.full((B,), n, dtype=torch.int32, device=DEV), log, di.conv_state, di.state)
+    rest = {key: x.reshape(B, K, *x.shape[1:])[:, n:].reshape(B * (K - n), *x.shape[1:]).contiguous()
+            for key, x in p.items()}
+    out2, _ = _verify(cfg, K - n, di, rest)
+    torch.cuda.synchronize()
+    tail = out.reshape(B, K, *out.shape[1:])[:, n:].reshape(B * (K - n), *out.shape[1:])
+    assert torch.equal(out2, tail)
+
+
+def test_verify_commit_model_shape():
+    """B = 256 sequences, 4-token drafts, 16 QK / 48 value heads, bf16: every 16th sequence against the
+    oracle (outputs and committed states), accepted lengths 0..4."""
+    B, K = 256, 4
+    di, p = _drafts(B, K, torch.bfloat16, hk=16, hv=48, seed=35)
+    cfg = gdn.cfg_for(16, 48, 128, 128, torch.bfloat16)
+    S0, c0 = di.state.clone(), di.conv_state.clone()
+    out, log = _verify(cfg, K, di, p)
+    n_acc = torch.arange(B, dtype=torch.int32, device=DEV) % (K + 1)
+    gdn.gdn_commit(cfg, K, n_acc, log, di.conv_state, di.state)
+    torch.cuda.synchronize()
+    pick = list(range(0, B, 16))
+    rows = [b * K + t for b in pick for t in range(K)]
+    cpu = {key: x[rows].cpu() for key, x in p.items()}
+    o_ref = O.gdn_verify(cpu, S0[pick].cpu(), c0[pick].cpu(), di.conv_w.cpu(), di.norm_w.cpu(), n_tok=K)
+    S_ref, c_ref = O.gdn_commit(cpu, n_acc[pick].cpu().numpy(), S0[pick].cpu(), c0[pick].cpu(), di.conv_w.cpu(),
+                                di.norm_w.cpu(), n_tok=K)
+    e_o, e_s = rel_l2(out[rows], o_ref), rel_l2(di.state[pick], S_ref)
+    print(f"rel_l2 out={e_o:.3e} state={e_s:.3e}", flush=True)
+    assert e_o <= TOL[torch.bfloat16] and e_s <= TOL[torch.bfloat16]
+    np.testing.assert_array_equal(di.conv_state[pick].double().cpu().numpy(), c_ref)
