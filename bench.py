@@ -4,7 +4,9 @@
 Headline: prefill tokens/s of one GDN layer at model shape (B=1, T=4096, 16 QK / 48 value heads,
 d=128, bf16 io, fp32 state). A step is one gdn_prefill call over that batch: conv + SiLU + L2,
 WY transform, state propagation, output + RMSNorm + gate, conv tail. The decode step (B=256, one
-token each, state streamed in place) is timed in the same run and reported beside it.
+token each, state streamed in place) and the speculative step (B=256, a 5-token draft each:
+gdn_verify of all of it, then gdn_commit of the accepted tokens) are timed in the same run and
+reported beside it.
 
 The headline times K eager steps between two events on the library's stream. Per-kernel times
 come from HIP events the library records on the same stream around each stage, in a second pass of
@@ -80,6 +82,22 @@ def decode_bytes(B: int) -> float:
     return float(B * (HV * 128 * 128 * 4 * 2 + 3 * 10240 * 2 * 2 + 10240 * 2 + HV * 128 * 2 * 2 + HV * 8))
 
 
+def verify_bytes(B: int, K: int) -> float:
+    """Per speculative verify of K tokens: state read, conv cache read, raw q/k/v, gate, o and
+    alpha/beta of the K tokens, and the log (k^ per QK head, e per value head in fp32, alpha/beta,
+    raw inputs)."""
+    C = 2 * HK * 128 + HV * 128
+    per_tok = C * 2 + HV * 128 * 2 * 2 + HV * 8 + (HK + HV) * 128 * 4 + HV * 8 + C * 2
+    return float(B * (HV * 128 * 128 * 4 + 3 * C * 2 + K * per_tok))
+
+
+def commit_bytes(B: int, K: int) -> float:
+    """Per commit of all K tokens: state read + write, the log's k^, e and alpha/beta of the K
+    tokens, the 3 newest raw rows and the conv cache written."""
+    C = 2 * HK * 128 + HV * 128
+    return float(B * (HV * 128 * 128 * 4 * 2 + K * ((HK + HV) * 128 * 4 + HV * 8) + 3 * C * 2 * 2))
+
+
 KERNEL_DIR = os.path.join(ROOT, "linear_attention_token_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -94,7 +112,8 @@ def kernel_source_hash(src: str) -> str:
 
 
 STAGE_SOURCE = {"conv_silu_l2": "k_conv.hip", "wy_or_sequential": "k_wy.hip", "state": "k_state.hip",
-                "output_norm_gate": "k_out.hip", "conv_tail": "k_conv.hip", "decode": "k_decode.hip"}
+                "output_norm_gate": "k_out.hip", "conv_tail": "k_conv.hip", "decode": "k_decode.hip",
+                "verify": "k_mtp.hip", "commit": "k_mtp.hip"}
 
 
 def measured_traffic(stage: str, grid_tag: str):
@@ -140,11 +159,14 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--decode-batch", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--spec-tokens", type=int, default=5,
+                    help="tokens per speculative verify: the last sampled token + 4 MTP drafts")
+    ap.add_argument("--spec-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the reference timing of one captured HIP graph replayed per step")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "speculative", "copy"], default="all",
                     help="run one part only (for profilers); 'copy' times a plain 1 GiB device copy, the "
                          "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
@@ -338,6 +360,58 @@ def main():
                              frac=round(gbps / HBM_PEAK_GBPS, 4),
                              traffic=measured_traffic("decode", f"decode B={B}"), kernel="decode",
                              algorithmic_bytes=db),
+        }
+
+    if args.only in ("all", "speculative") and not args.no_decode:
+        # ------------- speculative decoding: B sequences, K-token drafts, verify + commit -----------
+        B, K, S = args.decode_batch, args.spec_tokens, args.spec_steps
+        sp = decode_inputs(B, K, n_qk_heads=HK, n_v_heads=HV, d_k=D, d_v=D, io_dtype=torch.bfloat16,
+                           device=dev, seed=3)
+        pk = {key: getattr(sp, key).transpose(0, 1).reshape(B * K, *getattr(sp, key).shape[2:]).contiguous()
+              for key in ("q", "k", "v", "alpha", "beta", "gate")}
+        sst, scs = sp.state, sp.conv_state
+        sout = torch.empty((B * K, HV, D), dtype=torch.bfloat16, device=dev)
+        slog = torch.empty(gdn.gdn_verify_log_bytes(cfg, B, K), dtype=torch.uint8, device=dev)
+        nacc = torch.full((B,), K, dtype=torch.int32, device=dev)
+
+        def verify():
+            gdn.gdn_verify(cfg, K, pk["q"], pk["k"], pk["v"], pk["alpha"], pk["beta"], pk["gate"], sp.conv_w,
+                           sp.norm_w, scs, sst, out=sout, log=slog)
+
+        def commit():
+            gdn.gdn_commit(cfg, K, nacc, slog, scs, sst)
+
+        def timed(fn):
+            for _ in range(min(args.warmup, S)):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(S):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / S
+
+        us_v = timed(verify)
+        us_c = timed(commit)
+        us_s = timed(lambda: (verify(), commit()))
+        vb, cb = verify_bytes(B, K), commit_bytes(B, K)
+        acc = 4.06  # mean accepted length of four-step MTP speculation on the pages
+
+        def roof(nbytes, us, kernel):
+            gb = nbytes / (us * 1e-6) / 1e9
+            return dict(bound="hbm", achieved=round(gb, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                        frac=round(gb / HBM_PEAK_GBPS, 4), traffic=measured_traffic(kernel, f"{kernel} B={B} K={K}"),
+                        kernel=kernel, algorithmic_bytes=nbytes)
+
+        result["speculative"] = {
+            "workload": f"speculative decode step, B={B} sequences x {K}-token drafts (last sampled token + "
+                        f"{K - 1} MTP drafts), 16 QK / 48 value heads, d=128, bf16 io, fp32 state; verify of all "
+                        f"tokens, then commit of all of them",
+            "us_verify": round(us_v, 2), "us_commit": round(us_c, 2), "us_per_step": round(us_s, 2),
+            "mean_accepted_tokens": acc, "us_per_accepted_token": round(us_s / acc, 2),
+            "roofline_verify": roof(vb, us_v, "verify"), "roofline_commit": roof(cb, us_c, "commit"),
         }
 
     if not args.no_cpu_baseline and args.only == "all":

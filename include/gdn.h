@@ -152,10 +152,9 @@ gdn_status gdn_decode_step(const gdn_cfg* cfg, int32_t batch,
  * token, the normalised key of each QK head, the error e = v - alpha S^T k of each value head
  * (fp32), alpha, beta and the raw conv inputs -- about (HK + HV) KB per token instead of a 64 KB
  * state checkpoint per value head. gdn_commit then applies the first n_accept[b] of those rank-1
- * updates, S <- alpha S + beta k e^T, with the same fp32 operations verify used, so the committed
- * state equals verify's state after that many tokens (and, to fp32 rounding, that many decode
- * steps). Supported for d_k = d_v = 128, HV/HK <= 4, 1 <= n_tok <= 8, either io dtype; other
- * shapes return GDN_E_UNSUPPORTED.
+ * updates, S <- alpha S + beta k e^T, in order: the cache that many decode steps would leave, up
+ * to fp32 rounding. Supported for d_k = d_v = 128, HV/HK <= 4, 1 <= n_tok <= 8, either io dtype;
+ * other shapes return GDN_E_UNSUPPORTED.
  *
  * gdn_verify_log_bytes: bytes of the log for (cfg, batch, n_tok). Pure host computation.
  *

@@ -12,9 +12,8 @@
 // Instead of a state checkpoint per draft token (64 KB per value head and token), verify logs the
 // rank-1 factors of each token's update S <- alpha S + (beta k) e^T -- the normalised key of each
 // QK head and the error e of each value head in fp32 (1 KB per token and head), alpha, beta, and
-// the raw conv inputs -- and commit replays the first n of them onto the stored state with the
-// same fp32 operations verify used in registers, so the committed state is exactly verify's state
-// after n tokens. Verify reads each state once and writes none; commit reads and writes it once.
+// the raw conv inputs -- and commit applies the first n of them, in order, to the stored state.
+// Verify reads each state once and writes none; commit reads and writes it once.
 //
 // Both kernels run one 256-thread block per (sequence, QK group) with the register layout of the
 // decode step: thread (cg, rg) = (t % 32, t / 32) holds columns 4cg .. +3 of rows rg + 8j (j < 16)
@@ -49,9 +48,7 @@ struct MtpArgs {
   float scale, l2_eps, norm_eps;
 };
 
-// One rank-1 step on a 16-byte piece of state row i: S <- alpha S + (beta k_i) e^T. Verify applies
-// it in registers and commit replays it from the log; the explicit fused multiply-adds make both
-// round alike.
+// One rank-1 step on a 16-byte piece of state row i: S <- alpha S + (beta k_i) e^T.
 __device__ __forceinline__ float4 rank1(const float4& s, float al, float bk, const float4& e) {
   return make_float4(fmaf(bk, e.x, al * s.x), fmaf(bk, e.y, al * s.y), fmaf(bk, e.z, al * s.z),
                      fmaf(bk, e.w, al * s.w));
@@ -66,27 +63,58 @@ __device__ __forceinline__ int64_t group_channel(int c, int g, int R, int hk) {
   return 2 * qk_ch + int64_t(g) * R * kD + (c - 2 * kD);
 }
 
-size_t verify_smem_floats(int K, int R) {
-  const int nch = (2 + R) * kD, nv = R * kD;
-  return size_t(K) * nch + size_t(K) * nv + nv + ((2 * R * K + 3) & ~3) + ((K + 3) & ~3) + 2 * 8 * kD;
+// LDS layout of the verify kernel (offsets in floats, every region 16-byte aligned).
+struct VerifyLds {
+  int act, cst, gsh, nwsh, absh, Gh, cA, cB, dkk, dqk, red, ssr, total;
+};
+__host__ __device__ inline VerifyLds verify_lds(int K, int R) {
+  auto pad = [](int n) { return (n + 3) & ~3; };
+  VerifyLds L;
+  L.act = 0;                                   // [K][(2 + R) 128]
+  L.cst = L.act + K * (2 + R) * kD;            // [3][(2 + R) 128] conv cache rows
+  L.gsh = L.cst + 3 * (2 + R) * kD;            // [K][R 128]
+  L.nwsh = L.gsh + K * R * kD;                 // [R 128]
+  L.absh = L.nwsh + R * kD;                    // [K][2R]
+  L.Gh = L.absh + pad(2 * R * K);              // [R][K]
+  L.cA = L.Gh + pad(R * K);                    // [R][K][K]
+  L.cB = L.cA + pad(R * K * K);                // [R][K][K]
+  L.dkk = L.cB + pad(R * K * K);               // [K][K]
+  L.dqk = L.dkk + pad(K * K);                  // [K][K]
+  L.red = L.dqk + pad(K * K);                  // [K][2][4][128]
+  L.ssr = L.red + K * 2 * 4 * kD;              // [4][K]
+  L.total = L.ssr + pad(4 * K);
+  return L;
 }
+size_t verify_smem_floats(int K, int R) { return size_t(verify_lds(K, R).total); }
 size_t commit_smem_floats(int K, int R) { return size_t(K) * kD + size_t(K) * R * kD + ((2 * R * K + 3) & ~3); }
 
-// Two blocks per CU: at three, the token loop's registers push part of the next head's prefetch
-// into scratch, whose spill stores wait for those loads at once.
+// Verify needs no state after a draft token, only the outputs and the errors e, and over a draft of
+// K tokens both follow from the cached state S0 in closed form (the update equations unrolled, as
+// in the chunked prefill): with G_t the cumulative log decay of the draft, gamma_t = exp(G_t),
+//   e_t = v_t - gamma_t S0^T k_t - sum_{i<t} exp(G_t - G_i) (k_t.k_i) beta_i e_i
+//   y_t = gamma_t S0^T q_t + sum_{i<=t} exp(G_t - G_i) (q_t.k_i) beta_i e_i.
+// So a head needs one pass over S0 for the 2K products S0^T k_t, S0^T q_t (one barrier), then a
+// K-step recurrence that is independent per column, instead of K dependent steps.
 template <typename IO>
-__global__ void __launch_bounds__(256, 2) k_verify_d128(MtpArgs a) {
+__global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int b = int(blockIdx.x / unsigned(a.hk)), g = int(blockIdx.x - unsigned(b) * unsigned(a.hk));
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int cg = t & 31, rg = t >> 5, col = 4 * cg;
   const int R = a.R, K = a.K, nch = (2 + R) * kD, nv = R * kD;
-  float* const act = smem;                           // [K][nch]: q^ | k^ | v^ of each draft token
-  float* const gsh = act + K * nch;                  // [K][nv] gate logits
-  float* const nwsh = gsh + K * nv;                  // [nv] gains (1 + w)
-  float* const absh = nwsh + nv;                     // [K][2R] alpha | beta
-  float* const qks = absh + ((2 * R * K + 3) & ~3);  // [K] q^.k^
-  float* const red = qks + ((K + 3) & ~3);           // [2 buffers][4 waves][a, b][128]
+  const VerifyLds L = verify_lds(K, R);
+  float* const act = smem + L.act;    // [K][nch]: q^ | k^ | v^ of each draft token
+  float* const cst = smem + L.cst;    // [3][nch] conv cache rows
+  float* const gsh = smem + L.gsh;    // [K][nv] gate logits
+  float* const nwsh = smem + L.nwsh;  // [nv] gains (1 + w)
+  float* const absh = smem + L.absh;  // [K][2R] alpha | beta
+  float* const Gh = smem + L.Gh;      // [R][K] cumulative log decay over the draft
+  float* const cA = smem + L.cA;      // [R][K][K] exp(G_t - G_i) (k_t.k_i) beta_i, i < t
+  float* const cB = smem + L.cB;      // [R][K][K] exp(G_t - G_i) (q_t.k_i) beta_i, i <= t
+  float* const dkk = smem + L.dkk;    // [K][K] k_t.k_i
+  float* const dqk = smem + L.dqk;    // [K][K] q_t.k_i
+  float* const red = smem + L.red;    // [K][a, b][4 waves][128] partial products
+  float* const ssr = smem + L.ssr;    // [4 waves][K] partial sums of squares
 
   const size_t head = size_t(kD) * kD;
   const float* const S0 = a.state_in + (size_t(b) * a.hv + size_t(g) * R) * head;
@@ -98,51 +126,26 @@ __global__ void __launch_bounds__(256, 2) k_verify_d128(MtpArgs a) {
     for (int j = 0; j < 16; ++j) S[j] = buf_ld16_nt(rs, soff, 4096 * j);
   }
 
-  // ---- conv + SiLU of the group's channels for every draft token (3 passes of 256 channels cover
-  // the 640-768 channels of a group); the raw inputs go to the log for the commit ----
+  // ---- inputs of the group, all requested together as 16-byte pieces: the drafts' raw q | k | v
+  // rows (into act, and copied to the log for the commit), the conv cache rows, the gate logits;
+  // conv weights, gains, alpha and beta alongside ----
   const bool conv = (a.flags & GDN_CONV) != 0, gate = (a.flags & GDN_GATE) != 0;
   const int64_t row0 = int64_t(b) * K;  // token row of draft 0
-#pragma unroll 1
-  for (int u = 0; u < 3; ++u) {  // (not unrolled: the first state is in flight meanwhile)
-    const int c = min(t + 256 * u, nch - 1);  // threads past the end redo the last channel, unstored
-    const int64_t gc = group_channel(c, g, R, a.hk);
-    const IO* src;
-    int64_t ld;
-    if (c < kD) {
-      src = static_cast<const IO*>(a.q) + int64_t(g) * kD + c; ld = a.ld_q;
-    } else if (c < 2 * kD) {
-      src = static_cast<const IO*>(a.k) + int64_t(g) * kD + (c - kD); ld = a.ld_k;
-    } else {
-      src = static_cast<const IO*>(a.v) + int64_t(g) * nv + (c - 2 * kD); ld = a.ld_v;
-    }
-    float x[3 + kMaxDrafts];  // the three cached inputs, then the drafts
+  constexpr int VEC = vec16<IO>::N;     // io elements per piece
+  const int prow = nch / VEC, pv = nv / VEC;
+  const int n_raw = K * prow, n_cache = conv ? 3 * prow : 0, n_all = n_raw + n_cache + (gate ? K * pv : 0);
+  float4 cw[3];
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      x[j] = conv ? io<IO>::ld(static_cast<const IO*>(a.conv_in) + (int64_t(b) * 3 + j) * a.C + gc) : 0.f;
-#pragma unroll
-    for (int tt = 0; tt < kMaxDrafts; ++tt) x[3 + tt] = tt < K ? io<IO>::ld(src + (row0 + tt) * ld) : 0.f;
-    const float4 cw = conv ? reinterpret_cast<const float4*>(a.conv_w)[gc] : make_float4(0.f, 0.f, 0.f, 1.f);
-    if (t + 256 * u < nch) {
-#pragma unroll
-      for (int tt = 0; tt < kMaxDrafts; ++tt) {
-        if (tt >= K) break;
-        float val = x[3 + tt];
-        if (conv) {
-          val = siluf_(cw.x * x[tt] + cw.y * x[tt + 1] + cw.z * x[tt + 2] + cw.w * x[tt + 3]);
-          io<IO>::st(static_cast<IO*>(a.log.raw) + (row0 + tt) * a.C + gc, x[3 + tt]);
-        }
-        act[tt * nch + c] = val;
-      }
-    }
+  for (int u = 0; u < 3; ++u) {
+    const int c = min(t + 256 * u, nch - 1);
+    cw[u] = conv ? reinterpret_cast<const float4*>(a.conv_w)[group_channel(c, g, R, a.hk)] : make_float4(0.f, 0.f, 0.f, 1.f);
   }
-  // gate logits, gains, alpha and beta of the group's heads (alpha and beta also to the log)
-  if (gate)
-    for (int i = t; i < K * nv; i += 256) {
-      const int tt = i / nv, j = i - tt * nv;
-      gsh[i] = io<IO>::ld(static_cast<const IO*>(a.gate) + ((row0 + tt) * a.hv + int64_t(g) * R) * kD + j);
-    }
-  for (int i = t; i < nv; i += 256)
-    nwsh[i] = 1.0f + ((a.flags & GDN_NORM) ? a.norm_w[size_t(g * R + i / kD) * a.norm_stride + i % kD] : 0.f);
+  for (int i = t; i < nv / 4; i += 256) {
+    float4 nw = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.flags & GDN_NORM)
+      nw = *reinterpret_cast<const float4*>(a.norm_w + size_t(g * R + (4 * i) / kD) * a.norm_stride + (4 * i) % kD);
+    *reinterpret_cast<float4*>(nwsh + 4 * i) = make_float4(1.f + nw.x, 1.f + nw.y, 1.f + nw.z, 1.f + nw.w);
+  }
   for (int i = t; i < 2 * R * K; i += 256) {
     const int tt = i / (2 * R), j = i - tt * 2 * R, r = j < R ? j : j - R;
     const int64_t ix = (row0 + tt) * a.hv + int64_t(g) * R + r;
@@ -150,16 +153,78 @@ __global__ void __launch_bounds__(256, 2) k_verify_d128(MtpArgs a) {
     absh[i] = val;
     a.log.ab[ix * 2 + (j < R ? 0 : 1)] = val;
   }
+  for (int base = 0; base < n_all; base += 4 * 256) {
+    uint4 pc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // issue up to four pieces per thread before using any
+      const int i = base + u * 256 + t;
+      pc[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < n_raw) {
+        const int tt = i / prow, c0 = (i - tt * prow) * VEC;
+        const IO* src = c0 < kD ? static_cast<const IO*>(a.q) + (row0 + tt) * a.ld_q + int64_t(g) * kD + c0
+                      : c0 < 2 * kD ? static_cast<const IO*>(a.k) + (row0 + tt) * a.ld_k + int64_t(g) * kD + (c0 - kD)
+                                    : static_cast<const IO*>(a.v) + (row0 + tt) * a.ld_v + int64_t(g) * nv + (c0 - 2 * kD);
+        pc[u] = *reinterpret_cast<const uint4*>(src);
+      } else if (i < n_raw + n_cache) {
+        const int j = (i - n_raw) / prow, c0 = (i - n_raw - j * prow) * VEC;
+        pc[u] = *reinterpret_cast<const uint4*>(static_cast<const IO*>(a.conv_in) + (int64_t(b) * 3 + j) * a.C +
+                                                group_channel(c0, g, R, a.hk));
+      } else if (i < n_all) {
+        const int i2 = i - n_raw - n_cache, tt = i2 / pv, c0 = (i2 - tt * pv) * VEC;
+        pc[u] = *reinterpret_cast<const uint4*>(static_cast<const IO*>(a.gate) + ((row0 + tt) * a.hv + int64_t(g) * R) * kD + c0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * 256 + t;
+      if (i >= n_all) break;
+      float f[VEC];
+      vec16<IO>::cvt(pc[u], f);
+      float* dst;
+      if (i < n_raw) {
+        const int tt = i / prow, c0 = (i - tt * prow) * VEC;
+        dst = act + tt * nch + c0;
+        if (conv) *reinterpret_cast<uint4*>(static_cast<IO*>(a.log.raw) + (row0 + tt) * a.C + group_channel(c0, g, R, a.hk)) = pc[u];
+      } else if (i < n_raw + n_cache) {
+        const int j = (i - n_raw) / prow, c0 = (i - n_raw - j * prow) * VEC;
+        dst = cst + j * nch + c0;
+      } else {
+        const int i2 = i - n_raw - n_cache, tt = i2 / pv, c0 = (i2 - tt * pv) * VEC;
+        dst = gsh + tt * nv + c0;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+    }
+  }
+  __syncthreads();
+  // conv + SiLU in place, one channel column per thread (tap 3 on the current token)
+  if (conv) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int c = t + 256 * u;
+      if (c < nch) {
+        float x[3 + kMaxDrafts];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) x[j] = cst[j * nch + c];
+#pragma unroll
+        for (int tt = 0; tt < kMaxDrafts; ++tt) x[3 + tt] = tt < K ? act[tt * nch + c] : 0.f;
+#pragma unroll
+        for (int tt = 0; tt < kMaxDrafts; ++tt)
+          if (tt < K)
+            act[tt * nch + c] = siluf_(cw[u].x * x[tt] + cw[u].y * x[tt + 1] + cw[u].z * x[tt + 2] + cw[u].w * x[tt + 3]);
+      }
+    }
+  }
   __syncthreads();
 
-  // ---- L2 of q and k per draft token (wave w takes tokens w, w + 4), q^.k^, k^ to the log ----
+  // ---- L2 of q and k per draft token (wave w takes tokens w, w + 4), k^ to the log; cumulative
+  // log decays of each head ----
   const bool l2 = (a.flags & GDN_L2QK) != 0;
   for (int tt = w; tt < K; tt += 4) {
     float* const aq = act + tt * nch;
     float* const ak = aq + kD;
     const float q0 = aq[2 * lane], q1 = aq[2 * lane + 1], k0 = ak[2 * lane], k1 = ak[2 * lane + 1];
     const float sq = group_sum<64>(q0 * q0 + q1 * q1), sk = group_sum<64>(k0 * k0 + k1 * k1);
-    const float d = group_sum<64>(q0 * k0 + q1 * k1);
     const float rq = l2 ? 1.0f / sqrtf(sq + a.l2_eps) : 1.0f, rk = l2 ? 1.0f / sqrtf(sk + a.l2_eps) : 1.0f;
     const float kh0 = k0 * rk, kh1 = k1 * rk;
     aq[2 * lane] = q0 * rq;
@@ -167,12 +232,36 @@ __global__ void __launch_bounds__(256, 2) k_verify_d128(MtpArgs a) {
     ak[2 * lane] = kh0;
     ak[2 * lane + 1] = kh1;
     *reinterpret_cast<float2*>(a.log.kh + ((row0 + tt) * a.hk + g) * kD + 2 * lane) = make_float2(kh0, kh1);
-    if (lane == 0) qks[tt] = d * rq * rk;
+  }
+  if (t < R) {
+    float gsum = 0.f;
+    for (int tt = 0; tt < K; ++tt) {
+      gsum += logf(absh[tt * 2 * R + t]);
+      Gh[t * K + tt] = gsum;
+    }
+  }
+  __syncthreads();
+  // ---- k_t.k_i (i < t) and q_t.k_i (i <= t) of the draft, one wave per pair ----
+  for (int pidx = w; pidx < 2 * K * K; pidx += 4) {
+    const int isq = pidx >= K * K, pr = isq ? pidx - K * K : pidx, tt = pr / K, i = pr - tt * K;
+    if (i > tt || (!isq && i == tt)) continue;  // wave-uniform
+    const float* const x = act + tt * nch + (isq ? 0 : kD);
+    const float* const y = act + i * nch + kD;
+    const float d = group_sum<64>(x[2 * lane] * y[2 * lane] + x[2 * lane + 1] * y[2 * lane + 1]);
+    if (lane == 0) (isq ? dqk : dkk)[tt * K + i] = d;
+  }
+  __syncthreads();
+  for (int i3 = t; i3 < R * K * K; i3 += 256) {
+    const int r = i3 / (K * K), pr = i3 - r * K * K, tt = pr / K, i = pr - tt * K;
+    const float dec = i <= tt ? __expf(Gh[r * K + tt] - Gh[r * K + i]) * absh[i * 2 * R + R + r] : 0.f;
+    cA[i3] = i < tt ? dec * dkk[tt * K + i] : 0.f;
+    cB[i3] = i <= tt ? dec * dqk[tt * K + i] : 0.f;
   }
   __syncthreads();
 
-  // ---- value heads in turn, each through the K drafts with its state in registers ----
-  int ph = 0;  // reduction buffer parity: one barrier per token step
+  // ---- value heads in turn ----
+  const int c = t & (kD - 1);  // column of the per-column phase
+  const bool store_e = t < kD;  // threads 0..127 log e, threads 128..255 store the outputs
   for (int r = 0; r < R; ++r) {
     const int h = g * R + r;
     {  // the next head's state; after the last head an empty range (zeros, no memory access)
@@ -180,11 +269,10 @@ __global__ void __launch_bounds__(256, 2) k_verify_d128(MtpArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) N[j] = buf_ld16_nt(rn, soff, 4096 * j);
     }
+    // S0^T k_t and S0^T q_t of every draft token over this thread's rows, then over row-group pairs
     for (int tt = 0; tt < K; ++tt) {
       const float* const aq = act + tt * nch;
       const float* const ak = aq + kD;
-      const float al = absh[tt * 2 * R + r], be = absh[tt * 2 * R + R + r];
-      // a = S^T k^, b = S^T q^ over this thread's rows, then over the 8 row groups
       float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -196,41 +284,58 @@ __global__ void __launch_bounds__(256, 2) k_verify_d128(MtpArgs a) {
       pa.z += __shfl_xor(pa.z, 32, 64); pa.w += __shfl_xor(pa.w, 32, 64);
       pb.x += __shfl_xor(pb.x, 32, 64); pb.y += __shfl_xor(pb.y, 32, 64);
       pb.z += __shfl_xor(pb.z, 32, 64); pb.w += __shfl_xor(pb.w, 32, 64);
-      float* const rb = red + (ph & 1) * (8 * kD);
-      ++ph;
       if (lane < 32) {
-        *reinterpret_cast<float4*>(&rb[(2 * w) * kD + col]) = pa;
-        *reinterpret_cast<float4*>(&rb[(2 * w + 1) * kD + col]) = pb;
+        *reinterpret_cast<float4*>(&red[((tt * 2) * 4 + w) * kD + col]) = pa;
+        *reinterpret_cast<float4*>(&red[((tt * 2 + 1) * 4 + w) * kD + col]) = pb;
       }
-      __syncthreads();
-      float4 av = make_float4(0.f, 0.f, 0.f, 0.f), bv = av;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float4 x = *reinterpret_cast<const float4*>(&rb[(2 * ww) * kD + col]);
-        const float4 y = *reinterpret_cast<const float4*>(&rb[(2 * ww + 1) * kD + col]);
-        av.x += x.x; av.y += x.y; av.z += x.z; av.w += x.w;
-        bv.x += y.x; bv.y += y.y; bv.z += y.z; bv.w += y.w;
-      }
-      // e = v^ - alpha a (S~ = alpha S);  y = S_t^T q^ = alpha b + beta (q^.k^) e
-      const float4 vv = *reinterpret_cast<const float4*>(aq + (2 + r) * kD + col);
-      const float4 ev = make_float4(vv.x - al * av.x, vv.y - al * av.y, vv.z - al * av.z, vv.w - al * av.w);
-      const float bq = be * qks[tt];
-      const float y[4] = {a.scale * (al * bv.x + bq * ev.x), a.scale * (al * bv.y + bq * ev.y),
-                          a.scale * (al * bv.z + bq * ev.z), a.scale * (al * bv.w + bq * ev.w)};
-      // e to the log: wave w stores columns 32w .. 32w + 31 (lanes 8w .. 8w + 7 of its row group)
-      if ((lane >> 3) == w)
-        *reinterpret_cast<float4*>(a.log.e + ((row0 + tt) * a.hv + h) * kD + col) = ev;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) S[j] = rank1(S[j], al, be * ak[rg + 8 * j], ev);
-      // RMSNorm over the head's 128 outputs (every row group holds them all), gain, gate; wave w
-      // stores channel col + w of each column group (its two row groups write the same values)
-      const float ss = group_sum<32>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
-      const float rsn = (a.flags & GDN_NORM) ? 1.0f / sqrtf(ss / float(kD) + a.norm_eps) : 1.0f;
-      const float yw = w == 0 ? y[0] : w == 1 ? y[1] : w == 2 ? y[2] : y[3];
-      float o = yw * rsn * nwsh[r * kD + col + w];
-      if (gate) o *= sigmoidf_(gsh[tt * nv + r * kD + col + w]);
-      io<IO>::st(static_cast<IO*>(a.out) + ((row0 + tt) * a.hv + h) * kD + col + w, o);
     }
+    __syncthreads();
+    // per column c (every thread; the two halves of the block compute the same values): e_t, y_t
+    float e[kMaxDrafts], y[kMaxDrafts];
+    const float* const cAr = cA + r * K * K;
+    const float* const cBr = cB + r * K * K;
+#pragma unroll
+    for (int tt = 0; tt < kMaxDrafts; ++tt) {
+      e[tt] = 0.f;
+      y[tt] = 0.f;
+      if (tt < K) {
+        const float* const rt = red + (tt * 2) * 4 * kD + c;
+        const float a0 = (rt[0] + rt[kD]) + (rt[2 * kD] + rt[3 * kD]);
+        const float b0 = (rt[4 * kD] + rt[5 * kD]) + (rt[6 * kD] + rt[7 * kD]);
+        const float gam = __expf(Gh[r * K + tt]);
+        float ev = act[tt * nch + (2 + r) * kD + c] - gam * a0;
+        float yv = gam * b0;
+#pragma unroll
+        for (int i = 0; i < kMaxDrafts; ++i)
+          if (i < tt) {
+            ev -= cAr[tt * K + i] * e[i];
+            yv += cBr[tt * K + i] * e[i];
+          }
+        e[tt] = ev;
+        y[tt] = a.scale * (yv + cBr[tt * K + tt] * ev);
+      }
+    }
+    // RMSNorm sums per token over the 128 columns (waves 0-1 and 2-3 each cover all of them)
+#pragma unroll
+    for (int tt = 0; tt < kMaxDrafts; ++tt)
+      if (tt < K) {
+        const float ss = group_sum<64>(y[tt] * y[tt]);
+        if (lane == 0) ssr[w * K + tt] = ss;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < kMaxDrafts; ++tt)
+      if (tt < K) {
+        if (store_e) {
+          a.log.e[((row0 + tt) * a.hv + h) * kD + c] = e[tt];
+        } else {
+          const float ss = ssr[2 * K + tt] + ssr[3 * K + tt];
+          const float rsn = (a.flags & GDN_NORM) ? 1.0f / sqrtf(ss / float(kD) + a.norm_eps) : 1.0f;
+          float o = y[tt] * rsn * nwsh[r * kD + c];
+          if (gate) o *= sigmoidf_(gsh[tt * nv + r * kD + c]);
+          io<IO>::st(static_cast<IO*>(a.out) + ((row0 + tt) * a.hv + h) * kD + c, o);
+        }
+      }
 #pragma unroll
     for (int j = 0; j < 16; ++j) S[j] = N[j];
   }
