@@ -20,6 +20,12 @@ Sources (the pages this follows; all quoted facts are restated, not copied):
        decoding with multi-token prediction (MTP), mean accepted length about 4.
   [P2] §01 (MTP row: one layer trained for multi-step prediction) and the §04 results table
        (four-step MTP accepted length): drafts of several tokens are checked in one pass.
+  [P1] paper reading "Qwen3.8-Flash-Next" (方法): the normalised residual stream goes through
+       learned projections, then the short conv; a data-dependent decay gate sets how long the
+       state lives and a write gate scales the delta update.
+  [P2] §07 optimizer table: the GDN input is one fused matrix in Megatron made of independent
+       operators (q, k, v, ...), the GDN input and output projections are 2-D weights, and the GDN
+       alpha / beta parameters are vectors.
 
 Readings where the pages are silent (every one is also listed in the design notes):
   * conv + SiLU on q, k and v; L2 on q and k only.
@@ -28,6 +34,10 @@ Readings where the pages are silent (every one is also listed in the design note
   * L2: a / sqrt(sum(a^2) + l2_eps);  RMSNorm: y / sqrt(mean(y^2) + norm_eps) * (1 + w).
   * value head h reads QK head floor(h * HK / HV) (contiguous groups).
   * the state is stored [d_k][d_v] (row = key index); y carries an optional ``scale`` (1.0).
+  * projections (the pages give no formula for the gates): q | k | v = x W_qkv, gate logits
+    z = x W_z, gate pre-activations [a | b] = x W_ab, then beta = sigmoid(b) and
+    alpha = exp(-exp(A_h) * softplus(a + delta_h)) with per-head vectors A, delta; the output
+    projection is y = o W_out.
 
 Flags mirror the library's stage switches: CONV (conv + SiLU), L2QK, NORM, GATE.
 """
@@ -277,3 +287,36 @@ def gdn_commit(steps, n_accept, state, conv_state, conv_w, norm_w, *, n_tok, fla
                state_in=state, conv_in=conv_state)
     _, S, c = gdn_prefill(inp, flags=flags, scale=scale, l2_eps=l2_eps, norm_eps=norm_eps)
     return S, c
+
+
+def softplus(x):
+    """log(1 + e^x), evaluated without overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def gate_alpha_beta(a, b, a_log, dt_bias):
+    """Data-dependent decay and write gates of every (token, value head) ([P1] 方法; the formula
+    is a reading, the pages give none): alpha = exp(-exp(A_h) softplus(a + delta_h)) in (0, 1],
+    beta = sigmoid(b) in (0, 1). a, b: [T, HV]; a_log (A), dt_bias (delta): [HV]."""
+    a, b = _f64(a), _f64(b)
+    alpha = np.exp(-np.exp(_f64(a_log))[None, :] * softplus(a + _f64(dt_bias)[None, :]))
+    return alpha, sigmoid(b)
+
+
+def in_projection(x, w_qkv, w_z, w_ab, a_log, dt_bias):
+    """The layer's input side ([P1] 方法, [P2] §07): the normalised residual stream x [T, hidden]
+    through the fused input matrix. Returns (qkv [T, C] in the conv's channel order q | k | v,
+    gate logits z [T, HV*dv], alpha [T, HV], beta [T, HV]) in fp64."""
+    x = _f64(x)
+    qkv = x @ _f64(w_qkv)
+    z = x @ _f64(w_z)
+    ab = x @ _f64(w_ab)
+    hv = ab.shape[1] // 2
+    alpha, beta = gate_alpha_beta(ab[:, :hv], ab[:, hv:], a_log, dt_bias)
+    return qkv, z, alpha, beta
+
+
+def out_projection(o, w_out):
+    """The mixer output o [T, HV*dv] back to the residual width: o W_out, fp64."""
+    return _f64(o) @ _f64(w_out)

@@ -419,3 +419,49 @@ def test_commit_equals_accepted_decode_steps(n_accept):
     for b, n in enumerate(n_accept):
         if n == 0:
             assert np.array_equal(S[b], di.state[b].double().numpy())
+
+
+# ------------------------------------------------------------------ projections and gates -------
+
+def test_in_projection_matches_brute_force():
+    """q | k | v, z and the gate pre-activations are plain products x W: checked against explicit
+    loops on a tiny layer, and the gates against their formula written per element."""
+    from workloads import projection_inputs
+    p = projection_inputs(3, hidden=5, n_qk_heads=1, n_v_heads=2, d_k=2, d_v=2, io_dtype=torch.float32, seed=2)
+    qkv, z, alpha, beta = O.in_projection(p.x, p.w_qkv, p.w_z, p.w_ab, p.a_log, p.dt_bias)
+    x = p.x.double().tolist()
+
+    def mm(w):
+        w = w.double().tolist()
+        return [[sum(x[t][i] * w[i][j] for i in range(len(w))) for j in range(len(w[0]))] for t in range(len(x))]
+    np.testing.assert_allclose(qkv, mm(p.w_qkv), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(z, mm(p.w_z), rtol=1e-13, atol=1e-14)
+    ab = mm(p.w_ab)
+    import math
+    for t in range(3):
+        for h in range(2):
+            u = ab[t][h] + float(p.dt_bias[h])
+            sp = math.log(1.0 + math.exp(u))
+            assert abs(alpha[t, h] - math.exp(-math.exp(float(p.a_log[h])) * sp)) < 1e-14
+            assert abs(beta[t, h] - 1.0 / (1.0 + math.exp(-ab[t][2 + h]))) < 1e-14
+
+
+def test_gate_limits():
+    """alpha -> 1 when the decay rate exp(A) -> 0 or the pre-activation -> -inf; alpha is
+    decreasing in a; beta = 1/2 at b = 0; softplus(0) = ln 2 and softplus(x) ~ x for large x."""
+    a = np.array([[-50.0, 0.0, 3.0, 40.0]])
+    b = np.array([[0.0, -40.0, 2.0, 40.0]])
+    al, be = O.gate_alpha_beta(a, b, np.full(4, -60.0), np.zeros(4))
+    np.testing.assert_allclose(al, 1.0, rtol=0, atol=1e-20)
+    al, be = O.gate_alpha_beta(a, b, np.zeros(4), np.zeros(4))
+    assert al[0, 0] >= 1 - 1e-15 and np.all(np.diff(al[0]) < 0)
+    assert abs(al[0, 1] - 0.5) < 1e-15  # exp(-ln 2)
+    assert abs(np.log(al[0, 3]) + 40.0) < 1e-12
+    assert be[0, 0] == 0.5 and be[0, 1] < 1e-17 and abs(be[0, 3] - 1.0) < 1e-17
+    assert abs(O.softplus(0.0) - np.log(2.0)) < 1e-16 and O.softplus(800.0) == 800.0
+
+
+def test_out_projection_is_a_product():
+    o = np.arange(6.0).reshape(2, 3)
+    w = np.array([[1.0, 0.0], [0.0, 2.0], [1.0, -1.0]])
+    np.testing.assert_array_equal(O.out_projection(o, w), [[2.0, 0.0], [8.0, 3.0]])

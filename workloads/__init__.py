@@ -9,6 +9,8 @@ from .gen import (  # noqa: F401
     DecodeInputs,
     prefill_inputs,
     decode_inputs,
+    ProjectionInputs,
+    projection_inputs,
     loguniform_lengths,
     config_tiny,
     config_layer,

@@ -195,6 +195,39 @@ def decode_inputs(batch: int, n_steps: int, *, n_qk_heads: int, n_v_heads: int, 
                         norm_w, state, conv_state)
 
 
+@dataclass
+class ProjectionInputs:
+    """The layer's projections around the mixer: x [T, hidden] (normalised residual stream, io
+    dtype), w_qkv [hidden, C] (q | k | v columns in conv channel order), w_z [hidden, HV*dv] (gate
+    logits), w_ab [hidden, 2*HV] (decay / write gate pre-activations), a_log, dt_bias [HV] fp32
+    (the per-head gate vectors), w_out [HV*dv, hidden]."""
+    x: torch.Tensor
+    w_qkv: torch.Tensor
+    w_z: torch.Tensor
+    w_ab: torch.Tensor
+    a_log: torch.Tensor
+    dt_bias: torch.Tensor
+    w_out: torch.Tensor
+
+
+def projection_inputs(T: int, *, hidden: int, n_qk_heads: int, n_v_heads: int, d_k: int, d_v: int,
+                      io_dtype: torch.dtype = torch.bfloat16, seed: int = 0, device="cpu") -> ProjectionInputs:
+    """x ~ N(0, 1); weights ~ N(0, 1/fan_in) so projected values are ~N(0, 1); exp(A) ~ U(0.5, 2)
+    and delta ~ U(-5, -2), which put alpha mostly in [0.9, 0.999] like the layer workloads."""
+    C = 2 * n_qk_heads * d_k + n_v_heads * d_v
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    s_in, s_out = hidden ** -0.5, (n_v_heads * d_v) ** -0.5
+    x = _normal(g, (T, hidden), 1.0, device).to(io_dtype)
+    w_qkv = _normal(g, (hidden, C), s_in, device).to(io_dtype)
+    w_z = _normal(g, (hidden, n_v_heads * d_v), s_in, device).to(io_dtype)
+    w_ab = _normal(g, (hidden, 2 * n_v_heads), s_in, device).to(io_dtype)
+    a_log = torch.log(torch.rand((n_v_heads,), generator=g, device=device) * 1.5 + 0.5)
+    dt_bias = torch.rand((n_v_heads,), generator=g, device=device) * 3.0 - 5.0
+    w_out = _normal(g, (n_v_heads * d_v, hidden), s_out, device).to(io_dtype)
+    return ProjectionInputs(x, w_qkv, w_z, w_ab, a_log, dt_bias, w_out)
+
+
 # --- the five workloads (tiny correctness case, one layer, long prefill, varlen, decode) -----
 
 MODEL_HEADS = dict(n_qk_heads=16, n_v_heads=48, d_k=128, d_v=128)
