@@ -13,8 +13,9 @@
  *   5. a sigmoid output gate, elementwise (paper summary, Method: normalised, then gated).
  *
  * Conventions shared by every entry point:
- *   - Tensor pointers are DEVICE pointers owned by the caller. The library allocates no memory,
- *     keeps no device state between calls and never synchronises: work is enqueued on the
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library allocates no memory
+ *     (the projections' GEMM library keeps one handle per device), keeps no other state between
+ *     calls and never synchronises: work is enqueued on the
  *     caller's stream (`hip_stream`, a hipStream_t; NULL = the default stream) and the call
  *     returns after the enqueue. Device faults surface at the caller's next synchronisation.
  *   - Arguments are validated on the host first. On failure the call returns a status, enqueues
@@ -186,6 +187,37 @@ gdn_status gdn_verify(const gdn_cfg* cfg, int32_t batch, int32_t n_tok,
                       void* log, size_t log_bytes, void* hip_stream);
 gdn_status gdn_commit(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, const int32_t* n_accept,
                       const void* log, size_t log_bytes, void* conv_state, float* state, void* hip_stream);
+
+/* Projections around the mixer (bf16 io). The normalised residual stream goes through learned
+ * projections before the short conv, with a data-dependent decay gate and a write gate (paper
+ * reading "Qwen3.8-Flash-Next", 方法); the GDN input is one fused matrix of independent operators and
+ * the gates have per-head vector parameters (analysis notes "Qwen3.8-Flash-Next：架构、效率与技术谱系"
+ * §07 optimizer table). The pages give no gate formula; the one implemented is
+ *     alpha = exp(-exp(a_log[h]) * softplus(a + dt_bias[h])),  beta = sigmoid(b),  [a | b] = x W_ab^T.
+ * Weights use the linear-layer layout [out features][in features], row-major, bf16.
+ *
+ * gdn_proj_workspace: bytes of device workspace both calls need (the GEMM library's scratch).
+ *
+ * gdn_in_proj (T tokens, hidden width H, H % 32 == 0, HV <= 64):
+ *   x        bf16 [T][H], row stride ld_x (>= H, a multiple of 8): the normalised residual stream.
+ *   w_qkv    bf16 [C_tot][H]: output channels in the conv's order (q heads, k heads, v heads).
+ *   w_z      bf16 [HV*d_v][H]: gate logits.   w_ab  bf16 [2*HV][H]: a (rows 0..HV-1), then b.
+ *   a_log, dt_bias  fp32 [HV].
+ *   qkv      bf16 [T][C_tot] out: pass q, k, v to gdn_prefill as views of it (row stride C_tot).
+ *   z        bf16 [T][HV][d_v] out: the gate logits gdn_prefill takes.
+ *   alpha, beta  fp32 [T][HV] out (gate pre-activations accumulated in fp32).
+ * gdn_out_proj: y bf16 [T][H] = o W_out^T with o bf16 [T][HV*d_v] (the mixer output) and
+ *   w_out bf16 [H][HV*d_v].
+ * The plain products run in hipBLASLt (bf16 in, fp32 accumulate, bf16 out); the first call on a
+ * device creates a hipBLASLt handle that lives until the process ends, and each GEMM shape's
+ * algorithm is chosen once. Returns GDN_E_UNSUPPORTED for fp32 io. */
+gdn_status gdn_proj_workspace(size_t* bytes);
+gdn_status gdn_in_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const void* x, int64_t ld_x,
+                       const void* w_qkv, const void* w_z, const void* w_ab, const float* a_log,
+                       const float* dt_bias, void* qkv, void* z, float* alpha, float* beta,
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
+gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const void* o, const void* w_out,
+                        void* y, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Stage timing for profilers (host-side, per calling thread). After this call, every gdn_prefill
  * on this thread records events[i] on its stream before stage i and events[GDN_N_STAGES] after the

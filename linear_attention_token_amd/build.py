@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.cpp", "k_conv.hip", "k_seq.hip", "k_decode.hip", "k_mtp.hip", "k_wy.hip", "k_state.hip",
+SOURCES = ["gdn_api.cpp", "k_conv.hip", "k_seq.hip", "k_decode.hip", "k_mtp.hip", "k_proj.hip", "k_wy.hip", "k_state.hip",
            "k_out.hip"]
 
 ARCH = "gfx950"
@@ -46,7 +46,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-lhipblaslt", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

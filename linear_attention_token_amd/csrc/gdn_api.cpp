@@ -409,4 +409,76 @@ gdn_status gdn_commit(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, const in
   return GDN_OK;
 }
 
+gdn_status gdn_proj_workspace(size_t* bytes) {
+  g_last_error[0] = 0;
+  if (!bytes) return fail(GDN_E_NULL, "bytes is NULL");
+  *bytes = kProjWorkspace;
+  return GDN_OK;
+}
+
+static gdn_status check_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, Problem& p) {
+  gdn_status st = check_cfg(cfg, p);
+  if (st != GDN_OK) return st;
+  if (!p.bf16) return fail(GDN_E_UNSUPPORTED, "the projections are implemented for bf16 io");
+  if (hidden <= 0 || hidden % 32) return fail(GDN_E_SHAPE, "hidden = %d must be a positive multiple of 32", hidden);
+  if (T < 0 || T > int64_t(INT32_MAX) * 8) return fail(GDN_E_SHAPE, "T = %lld out of range", (long long)T);
+  if (p.hv > 64) return fail(GDN_E_UNSUPPORTED, "HV = %d > 64 for the gate kernel", p.hv);
+  return GDN_OK;
+}
+
+gdn_status gdn_in_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const void* x, int64_t ld_x,
+                       const void* w_qkv, const void* w_z, const void* w_ab, const float* a_log, const float* dt_bias,
+                       void* qkv, void* z, float* alpha, float* beta, void* workspace, size_t workspace_bytes,
+                       void* hip_stream) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_proj(cfg, hidden, T, p);
+  if (st != GDN_OK) return st;
+  if (T > 0) {
+    if (!x || !w_qkv || !w_z || !w_ab || !a_log || !dt_bias) return fail(GDN_E_NULL, "x, the weights and the gate vectors are required");
+    if (!qkv || !z || !alpha || !beta) return fail(GDN_E_NULL, "qkv, z, alpha and beta are required");
+    if (!workspace) return fail(GDN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", kProjWorkspace);
+  }
+  if (ld_x < hidden || ld_x % 8) return fail(GDN_E_SHAPE, "ld_x = %lld must be >= hidden and a multiple of 8", (long long)ld_x);
+  const void* ptrs[] = {x, w_qkv, w_z, w_ab, qkv, z};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (!aligned4(a_log) || !aligned4(dt_bias) || !aligned4(alpha) || !aligned4(beta))
+    return fail(GDN_E_ALIGN, "a_log, dt_bias, alpha and beta must be 4-byte aligned");
+  if (T > 0 && workspace_bytes < kProjWorkspace) return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, kProjWorkspace);
+  if (T == 0) return GDN_OK;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const char* why = "";
+  const int64_t vz = int64_t(p.hv) * p.dv;
+  if (gemm_bf16_tn(p.C, T, hidden, w_qkv, hidden, x, ld_x, qkv, p.C, workspace, workspace_bytes, s, &why) != hipSuccess ||
+      gemm_bf16_tn(vz, T, hidden, w_z, hidden, x, ld_x, z, vz, workspace, workspace_bytes, s, &why) != hipSuccess)
+    return fail(GDN_E_HIP, "input projection: %s", why);
+  if (run(launch_gates(x, ld_x, T, hidden, w_ab, p.hv, a_log, dt_bias, alpha, beta, s), "gates") != hipSuccess)
+    return GDN_E_HIP;
+  return GDN_OK;
+}
+
+gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const void* o, const void* w_out, void* y,
+                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_proj(cfg, hidden, T, p);
+  if (st != GDN_OK) return st;
+  if (T > 0) {
+    if (!o || !w_out || !y) return fail(GDN_E_NULL, "o, w_out and y are required");
+    if (!workspace) return fail(GDN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", kProjWorkspace);
+  }
+  const void* ptrs[] = {o, w_out, y};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (T > 0 && workspace_bytes < kProjWorkspace) return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, kProjWorkspace);
+  if (T == 0) return GDN_OK;
+  const char* why = "";
+  const int64_t vz = int64_t(p.hv) * p.dv;
+  if (gemm_bf16_tn(hidden, T, vz, w_out, vz, o, vz, y, hidden, workspace, workspace_bytes,
+                   static_cast<hipStream_t>(hip_stream), &why) != hipSuccess)
+    return fail(GDN_E_HIP, "output projection: %s", why);
+  return GDN_OK;
+}
+
 }  // extern "C"

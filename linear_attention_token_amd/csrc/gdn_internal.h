@@ -126,4 +126,12 @@ hipError_t launch_verify(const Problem& p, int batch, int n_tok, const void* q, 
 hipError_t launch_commit(const Problem& p, int batch, int n_tok, const int32_t* n_accept, const MtpLog& log,
                          void* conv_state, float* state, hipStream_t s);
 
+// Projections around the mixer (bf16): hipBLASLt GEMM D (M x N, column-major, ld ldd) = A^T B with
+// A (K x M, ld lda), B (K x N, ld ldb); and the fused gate kernel (alpha, beta from x W_ab^T).
+constexpr size_t kProjWorkspace = size_t(32) << 20;  // hipBLASLt workspace the projections need
+hipError_t gemm_bf16_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        void* D, int64_t ldd, void* ws, size_t ws_bytes, hipStream_t s, const char** why);
+hipError_t launch_gates(const void* x, int64_t ld_x, int64_t T, int H, const void* w_ab, int hv, const float* a_log,
+                        const float* dt_bias, float* alpha, float* beta, hipStream_t s);
+
 }  // namespace gdn

@@ -21,6 +21,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_E_NULL", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE", 4: "
           5: "GDN_E_WORKSPACE", 6: "GDN_E_UNSUPPORTED", 7: "GDN_E_HIP", 8: "GDN_E_VALUE"}
 EXPORTS = ("gdn_cfg_default", "gdn_prefill_workspace", "gdn_prefill", "gdn_decode_step",
            "gdn_verify_log_bytes", "gdn_verify", "gdn_commit",
+           "gdn_proj_workspace", "gdn_in_proj", "gdn_out_proj",
            "gdn_set_stage_events", "gdn_status_string", "gdn_last_error", "gdn_abi_version")
 N_STAGES = 6
 STAGE_NAMES = ("chunk_table", "conv_silu_l2", "wy_or_sequential", "state", "output_norm_gate", "conv_tail")
@@ -74,6 +75,13 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_commit.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t,
                                _P, _P, _P]
     lib.gdn_commit.restype = ctypes.c_int
+    lib.gdn_proj_workspace.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_proj_workspace.restype = ctypes.c_int
+    lib.gdn_in_proj.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_in_proj.restype = ctypes.c_int
+    lib.gdn_out_proj.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gdn_out_proj.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -301,6 +309,80 @@ def gdn_commit(cfg: gdn_cfg, n_tok: int, n_accept, log, conv_state, state, strea
     st = lib.gdn_commit(ctypes.byref(cfg), B, n_tok, _ptr(n_accept), _ptr(log), log.numel(), _ptr(conv_state),
                         _ptr(state), _stream(stream))
     _check(st)
+
+
+def gdn_proj_workspace() -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().gdn_proj_workspace(ctypes.byref(n)))
+    return int(n.value)
+
+
+def _proj_ws(workspace, device):
+    need = gdn_proj_workspace()
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace needs {need} uint8 elements")
+    return workspace
+
+
+def gdn_in_proj(cfg: gdn_cfg, x, w_qkv, w_z, w_ab, a_log, dt_bias, qkv=None, z=None, alpha=None, beta=None,
+                workspace=None, stream=None):
+    """Input projection of x [T, hidden] (bf16; rows may be strided): returns (qkv [T, C_tot],
+    z [T, HV, d_v], alpha [T, HV], beta [T, HV]), allocating outputs that are not given."""
+    lib = load_library()
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a bf16 [T, hidden] matrix with contiguous rows")
+    T, H = int(x.shape[0]), int(x.shape[1])
+    hv, dv = cfg.n_v_heads, cfg.d_v
+    C = 2 * cfg.n_qk_heads * cfg.d_k + hv * dv
+    _expect(w_qkv, (C, H), torch.bfloat16, "w_qkv")
+    _expect(w_z, (hv * dv, H), torch.bfloat16, "w_z")
+    _expect(w_ab, (2 * hv, H), torch.bfloat16, "w_ab")
+    _expect(a_log, (hv,), torch.float32, "a_log")
+    _expect(dt_bias, (hv,), torch.float32, "dt_bias")
+    dev = x.device
+    qkv = torch.empty((T, C), dtype=torch.bfloat16, device=dev) if qkv is None else qkv
+    z = torch.empty((T, hv, dv), dtype=torch.bfloat16, device=dev) if z is None else z
+    alpha = torch.empty((T, hv), dtype=torch.float32, device=dev) if alpha is None else alpha
+    beta = torch.empty((T, hv), dtype=torch.float32, device=dev) if beta is None else beta
+    _expect(qkv, (T, C), torch.bfloat16, "qkv")
+    _expect(z, (T, hv, dv), torch.bfloat16, "z")
+    _expect(alpha, (T, hv), torch.float32, "alpha")
+    _expect(beta, (T, hv), torch.float32, "beta")
+    workspace = _proj_ws(workspace, dev)
+    st = lib.gdn_in_proj(ctypes.byref(cfg), H, T, _ptr(x), x.stride(0) if T > 0 else H, _ptr(w_qkv), _ptr(w_z),
+                         _ptr(w_ab), _ptr(a_log), _ptr(dt_bias), _ptr(qkv), _ptr(z), _ptr(alpha), _ptr(beta),
+                         _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return qkv, z, alpha, beta
+
+
+def qkv_views(cfg: gdn_cfg, qkv):
+    """q, k, v as [T, heads, dim] views of a [T, C_tot] input-projection output."""
+    T = qkv.shape[0]
+    qc = cfg.n_qk_heads * cfg.d_k
+    return (qkv[:, :qc].view(T, cfg.n_qk_heads, cfg.d_k), qkv[:, qc:2 * qc].view(T, cfg.n_qk_heads, cfg.d_k),
+            qkv[:, 2 * qc:].view(T, cfg.n_v_heads, cfg.d_v))
+
+
+def gdn_out_proj(cfg: gdn_cfg, o, w_out, y=None, workspace=None, stream=None) -> torch.Tensor:
+    """Output projection of the mixer output o [T, HV, d_v] (or [T, HV*d_v]); returns y [T, hidden]."""
+    lib = load_library()
+    T = int(o.shape[0])
+    vz = cfg.n_v_heads * cfg.d_v
+    o2 = o.reshape(T, vz)
+    _expect(o2, (T, vz), torch.bfloat16, "o")
+    if w_out.dim() != 2 or w_out.shape[1] != vz:
+        raise ValueError(f"w_out: expected (hidden, {vz})")
+    H = int(w_out.shape[0])
+    _expect(w_out, (H, vz), torch.bfloat16, "w_out")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=o.device) if y is None else y
+    _expect(y, (T, H), torch.bfloat16, "y")
+    workspace = _proj_ws(workspace, o.device)
+    _check(lib.gdn_out_proj(ctypes.byref(cfg), H, T, _ptr(o2), _ptr(w_out), _ptr(y), _ptr(workspace),
+                            workspace.numel(), _stream(stream)))
+    return y
 
 
 def cfg_for(n_qk_heads: int, n_v_heads: int, d_k: int, d_v: int, dtype: torch.dtype,

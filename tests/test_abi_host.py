@@ -197,3 +197,34 @@ def test_verify_and_commit_reject_bad_arguments():
     off = gdn.gdn_cfg_default(flags=gdn.GDN_L2QK | gdn.GDN_NORM | gdn.GDN_GATE)
     assert _verify(off, B=0, conv_state=None) == 0
     assert _commit(off, B=0, conv_state=None) == 0
+
+
+def test_projections_reject_bad_arguments():
+    c = gdn.gdn_cfg_default()
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_proj_workspace(ctypes.byref(n)) == 0 and n.value >= 1 << 20
+    _err(lib.gdn_proj_workspace(None), 1)
+
+    def inp(cfg=c, H=2560, T=64, x=A, ld=2560, wq=A, wz=A, wab=A, al=A, dt=A, qkv=A, z=A, alpha=A, beta=A,
+            ws=A, wsb=1 << 30):
+        return lib.gdn_in_proj(ctypes.byref(cfg), H, T, x, ld, wq, wz, wab, al, dt, qkv, z, alpha, beta, ws, wsb, None)
+
+    def outp(cfg=c, H=2560, T=64, o=A, w=A, y=A, ws=A, wsb=1 << 30):
+        return lib.gdn_out_proj(ctypes.byref(cfg), H, T, o, w, y, ws, wsb, None)
+
+    for call in (inp, outp):
+        _err(call(cfg=gdn.gdn_cfg_default(io_dtype=gdn.GDN_F32)), 6)
+        _err(call(H=100), 2)                     # hidden % 32
+        _err(call(T=-1), 2)
+        _err(call(ws=None), 5)
+        _err(call(wsb=1024), 5)
+        _err(call(cfg=gdn.gdn_cfg_default(n_qk_heads=16, n_v_heads=80)), 6)  # HV > 64
+    _err(inp(x=None), 1)
+    _err(inp(beta=None), 1)
+    _err(inp(ld=2000), 2)
+    _err(inp(ld=2564), 2)                        # rows must stay 16-byte aligned
+    _err(inp(qkv=A + 8), 4)
+    _err(inp(alpha=A + 2), 4)
+    _err(outp(o=None), 1)
+    _err(outp(y=A + 8), 4)
+    assert inp(T=0, x=None, qkv=None) == 0 and outp(T=0, o=None) == 0

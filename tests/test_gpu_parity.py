@@ -466,3 +466,68 @@ def test_verify_commit_model_shape():
     print(f"rel_l2 out={e_o:.3e} state={e_s:.3e}", flush=True)
     assert e_o <= TOL[torch.bfloat16] and e_s <= TOL[torch.bfloat16]
     np.testing.assert_array_equal(di.conv_state[pick].double().cpu().numpy(), c_ref)
+
+
+# ------------------------------------------------------------------ projections around the mixer ---
+
+def _proj(T, hidden, hk, hv, seed=41):
+    from workloads import projection_inputs
+    return projection_inputs(T, hidden=hidden, n_qk_heads=hk, n_v_heads=hv, d_k=128, d_v=128, seed=seed, device=DEV)
+
+
+@pytest.mark.parametrize("T,hidden,hk,hv", [(200, 256, 2, 6), (512, 2560, 16, 48), (1, 64, 1, 3)])
+def test_in_proj(T, hidden, hk, hv):
+    """q | k | v and gate logits (bf16 GEMM outputs) and alpha, beta (fp32 gate pre-activations and
+    formula) against the oracle's products of the same bf16 values."""
+    p = _proj(T, hidden, hk, hv)
+    cfg = gdn.cfg_for(hk, hv, 128, 128, torch.bfloat16)
+    qkv, z, al, be = gdn.gdn_in_proj(cfg, p.x, p.w_qkv, p.w_z, p.w_ab, p.a_log, p.dt_bias)
+    torch.cuda.synchronize()
+    r_qkv, r_z, r_al, r_be = O.in_projection(p.x.cpu(), p.w_qkv.cpu().T, p.w_z.cpu().T, p.w_ab.cpu().T,
+                                             p.a_log.cpu(), p.dt_bias.cpu())
+    errs = (rel_l2(qkv, r_qkv), rel_l2(z.reshape(T, -1), r_z), rel_l2(al, r_al), rel_l2(be, r_be))
+    print("rel_l2 qkv %.3e z %.3e alpha %.3e beta %.3e" % errs, flush=True)
+    assert errs[0] <= TOL[torch.bfloat16] and errs[1] <= TOL[torch.bfloat16]
+    assert errs[2] <= 1e-4 and errs[3] <= 1e-4
+
+
+def test_out_proj():
+    T, hidden = 300, 512
+    p = _proj(T, hidden, 2, 6, seed=43)
+    cfg = gdn.cfg_for(2, 6, 128, 128, torch.bfloat16)
+    o = torch.randn((T, 6, 128), generator=torch.Generator(device=DEV).manual_seed(3), device=DEV).to(torch.bfloat16)
+    y = gdn.gdn_out_proj(cfg, o, p.w_out)
+    torch.cuda.synchronize()
+    err = rel_l2(y, O.out_projection(o.cpu().reshape(T, -1), p.w_out.cpu().T))
+    print(f"rel_l2 y {err:.3e}", flush=True)
+    assert err <= TOL[torch.bfloat16]
+
+
+def test_layer_end_to_end():
+    """x -> input projection -> mixer (prefill, two packed sequences) -> output projection, against the
+    oracle: its projections, with the projected activations rounded to bf16 as the GPU path stores
+    them, its mixer, and its output projection."""
+    T, hidden, hk, hv = 160, 256, 2, 6
+    p = _proj(T, hidden, hk, hv, seed=45)
+    cfg = gdn.cfg_for(hk, hv, 128, 128, torch.bfloat16)
+    g = torch.Generator(device=DEV).manual_seed(7)
+    conv_w = (torch.randn((2 * hk * 128 + hv * 128, 4), generator=g, device=DEV) * 0.5)
+    norm_w = torch.randn((128,), generator=g, device=DEV) * 0.02
+    cu = torch.tensor([0, 100, T], dtype=torch.int32, device=DEV)
+    qkv, z, al, be = gdn.gdn_in_proj(cfg, p.x, p.w_qkv, p.w_z, p.w_ab, p.a_log, p.dt_bias)
+    q, k, v = gdn.qkv_views(cfg, qkv)
+    o = gdn.gdn_prefill(cfg, cu, q, k, v, al, be, z, conv_w, norm_w, cu_seqlens_host=cu.cpu())
+    y = gdn.gdn_out_proj(cfg, o, p.w_out)
+    torch.cuda.synchronize()
+    r_qkv, r_z, r_al, r_be = O.in_projection(p.x.cpu(), p.w_qkv.cpu().T, p.w_z.cpu().T, p.w_ab.cpu().T,
+                                             p.a_log.cpu(), p.dt_bias.cpu())
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    qc = hk * 128
+    inp = dict(q=bf(r_qkv[:, :qc]).reshape(T, hk, 128), k=bf(r_qkv[:, qc:2 * qc]).reshape(T, hk, 128),
+               v=bf(r_qkv[:, 2 * qc:]).reshape(T, hv, 128), alpha=r_al, beta=r_be, gate=bf(r_z).reshape(T, hv, 128),
+               conv_w=conv_w.cpu(), norm_w=norm_w.cpu(), cu_seqlens=cu.cpu().numpy())
+    r_o, _, _ = O.gdn_prefill(inp)
+    r_y = O.out_projection(r_o.reshape(T, -1), p.w_out.cpu().T)
+    err = rel_l2(y, r_y)
+    print(f"rel_l2 layer {err:.3e}", flush=True)
+    assert err <= TOL[torch.bfloat16]

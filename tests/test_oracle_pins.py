@@ -428,11 +428,11 @@ def test_in_projection_matches_brute_force():
     loops on a tiny layer, and the gates against their formula written per element."""
     from workloads import projection_inputs
     p = projection_inputs(3, hidden=5, n_qk_heads=1, n_v_heads=2, d_k=2, d_v=2, io_dtype=torch.float32, seed=2)
-    qkv, z, alpha, beta = O.in_projection(p.x, p.w_qkv, p.w_z, p.w_ab, p.a_log, p.dt_bias)
+    qkv, z, alpha, beta = O.in_projection(p.x, p.w_qkv.T, p.w_z.T, p.w_ab.T, p.a_log, p.dt_bias)
     x = p.x.double().tolist()
 
-    def mm(w):
-        w = w.double().tolist()
+    def mm(w):  # x W^T for a weight in the [out][in] layout, by explicit loops
+        w = w.double().T.tolist()
         return [[sum(x[t][i] * w[i][j] for i in range(len(w))) for j in range(len(w[0]))] for t in range(len(x))]
     np.testing.assert_allclose(qkv, mm(p.w_qkv), rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(z, mm(p.w_z), rtol=1e-13, atol=1e-14)

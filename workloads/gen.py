@@ -197,10 +197,10 @@ def decode_inputs(batch: int, n_steps: int, *, n_qk_heads: int, n_v_heads: int, 
 
 @dataclass
 class ProjectionInputs:
-    """The layer's projections around the mixer: x [T, hidden] (normalised residual stream, io
-    dtype), w_qkv [hidden, C] (q | k | v columns in conv channel order), w_z [hidden, HV*dv] (gate
-    logits), w_ab [hidden, 2*HV] (decay / write gate pre-activations), a_log, dt_bias [HV] fp32
-    (the per-head gate vectors), w_out [HV*dv, hidden]."""
+    """The layer's projections around the mixer, weights in the linear-layer layout [out][in]:
+    x [T, hidden] (normalised residual stream, io dtype), w_qkv [C, hidden] (q | k | v rows in conv
+    channel order), w_z [HV*dv, hidden] (gate logits), w_ab [2*HV, hidden] (decay / write gate
+    pre-activations), a_log, dt_bias [HV] fp32 (the per-head gate vectors), w_out [hidden, HV*dv]."""
     x: torch.Tensor
     w_qkv: torch.Tensor
     w_z: torch.Tensor
@@ -219,12 +219,12 @@ def projection_inputs(T: int, *, hidden: int, n_qk_heads: int, n_v_heads: int, d
     g.manual_seed(seed)
     s_in, s_out = hidden ** -0.5, (n_v_heads * d_v) ** -0.5
     x = _normal(g, (T, hidden), 1.0, device).to(io_dtype)
-    w_qkv = _normal(g, (hidden, C), s_in, device).to(io_dtype)
-    w_z = _normal(g, (hidden, n_v_heads * d_v), s_in, device).to(io_dtype)
-    w_ab = _normal(g, (hidden, 2 * n_v_heads), s_in, device).to(io_dtype)
+    w_qkv = _normal(g, (C, hidden), s_in, device).to(io_dtype)
+    w_z = _normal(g, (n_v_heads * d_v, hidden), s_in, device).to(io_dtype)
+    w_ab = _normal(g, (2 * n_v_heads, hidden), s_in, device).to(io_dtype)
     a_log = torch.log(torch.rand((n_v_heads,), generator=g, device=device) * 1.5 + 0.5)
     dt_bias = torch.rand((n_v_heads,), generator=g, device=device) * 3.0 - 5.0
-    w_out = _normal(g, (n_v_heads * d_v, hidden), s_out, device).to(io_dtype)
+    w_out = _normal(g, (hidden, n_v_heads * d_v), s_out, device).to(io_dtype)
     return ProjectionInputs(x, w_qkv, w_z, w_ab, a_log, dt_bias, w_out)
 
 
