@@ -166,7 +166,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the reference timing of one captured HIP graph replayed per step")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "speculative", "copy"], default="all",
+    ap.add_argument("--hidden", type=int, default=2560, help="residual width of the layer leg")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "speculative", "layer", "copy"], default="all",
                     help="run one part only (for profilers); 'copy' times a plain 1 GiB device copy, the "
                          "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
@@ -360,6 +361,68 @@ def main():
                              frac=round(gbps / HBM_PEAK_GBPS, 4),
                              traffic=measured_traffic("decode", f"decode B={B}"), kernel="decode",
                              algorithmic_bytes=db),
+        }
+
+    if args.only in ("all", "layer"):
+        # ------------- the whole layer: input projection + gates, mixer, output projection ------------
+        from workloads import projection_inputs
+        T, Hd = 4096, args.hidden
+        pj = projection_inputs(T, hidden=Hd, n_qk_heads=HK, n_v_heads=HV, d_k=D, d_v=D, device=dev, seed=5)
+        lay = config_layer(dev, T=T)
+        C = 2 * HK * D + HV * D
+        qkv = torch.empty((T, C), dtype=torch.bfloat16, device=dev)
+        zg = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
+        al = torch.empty((T, HV), dtype=torch.float32, device=dev)
+        be = torch.empty((T, HV), dtype=torch.float32, device=dev)
+        lo = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
+        ly = torch.empty((T, Hd), dtype=torch.bfloat16, device=dev)
+        pws = torch.empty(gdn.gdn_proj_workspace(), dtype=torch.uint8, device=dev)
+        lws = torch.empty(gdn.gdn_prefill_workspace(cfg, 1, T), dtype=torch.uint8, device=dev)
+        lst = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
+        lq, lk, lv = gdn.qkv_views(cfg, qkv)
+        cuh = lay.cu_seqlens.cpu()
+
+        def in_proj():
+            gdn.gdn_in_proj(cfg, pj.x, pj.w_qkv, pj.w_z, pj.w_ab, pj.a_log, pj.dt_bias, qkv=qkv, z=zg, alpha=al,
+                            beta=be, workspace=pws)
+
+        def mixer():
+            gdn.gdn_prefill(cfg, lay.cu_seqlens, lq, lk, lv, al, be, zg, lay.conv_w, lay.norm_w, state_out=lst,
+                            out=lo, workspace=lws, cu_seqlens_host=cuh)
+
+        def out_proj():
+            gdn.gdn_out_proj(cfg, lo, pj.w_out, y=ly, workspace=pws)
+
+        def timed_n(fn, n):
+            for _ in range(min(args.warmup, n)):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n  # ms
+
+        n = args.steps
+        ms_in, ms_mix, ms_out = timed_n(in_proj, n), timed_n(mixer, n), timed_n(out_proj, n)
+        ms_layer = timed_n(lambda: (in_proj(), mixer(), out_proj()), n)
+        f_in = 2.0 * T * Hd * (C + HV * D + 2 * HV)
+        f_out = 2.0 * T * HV * D * Hd
+
+        def mroof(fl, ms):
+            tf = fl / (ms * 1e-3) / 1e12
+            return dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), algorithmic_flops=fl)
+
+        result["layer"] = {
+            "workload": f"one GDN layer, B=1, T={T}, hidden {Hd}: input projection (q|k|v, gate logits, "
+                        f"alpha/beta) + mixer (16 QK / 48 value heads, d=128) + output projection, bf16, "
+                        f"synthetic weights",
+            "ms_per_step": round(ms_layer, 5), "tokens_per_s": round(T / (ms_layer * 1e-3), 1),
+            "ms_in_proj": round(ms_in, 5), "ms_mixer": round(ms_mix, 5), "ms_out_proj": round(ms_out, 5),
+            "roofline_in_proj": mroof(f_in, ms_in), "roofline_out_proj": mroof(f_out, ms_out),
         }
 
     if args.only in ("all", "speculative") and not args.no_decode:

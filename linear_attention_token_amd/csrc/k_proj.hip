@@ -135,19 +135,25 @@ hipError_t gemm_bf16_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
     if (!have) {
       hipblasLtMatmulPreference_t pref = nullptr;
       uint64_t cap = ws_bytes;
-      hipblasLtMatmulHeuristicResult_t res[1];
+      constexpr int kCand = 8;
+      hipblasLtMatmulHeuristicResult_t res[kCand];
       int n = 0;
       st = hipblasLtMatmulPreferenceCreate(&pref);
       if (st == HIPBLAS_STATUS_SUCCESS)
         st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap));
       if (st == HIPBLAS_STATUS_SUCCESS)
-        st = hipblasLtMatmulAlgoGetHeuristic(h, op, la, lb, ld, ld, pref, 1, res, &n);
+        st = hipblasLtMatmulAlgoGetHeuristic(h, op, la, lb, ld, ld, pref, kCand, res, &n);
       if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-      if (st == HIPBLAS_STATUS_SUCCESS && n < 1) st = HIPBLAS_STATUS_NOT_SUPPORTED;
+      // a returned entry is usable only if its own state is success (its other fields are
+      // undefined otherwise) and its workspace fits the caller's
+      int pick = -1;
+      for (int i = 0; st == HIPBLAS_STATUS_SUCCESS && i < n && i < kCand && pick < 0; ++i)
+        if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes) pick = i;
+      if (st == HIPBLAS_STATUS_SUCCESS && pick < 0) st = HIPBLAS_STATUS_NOT_SUPPORTED;
       if (st == HIPBLAS_STATUS_SUCCESS) {
-        algo = res[0].algo;
+        algo = res[pick].algo;
         have = true;
-        if (g_ncache < 64) g_cache[g_ncache++] = GemmEntry{key, algo, res[0].workspaceSize};
+        if (g_ncache < 64) g_cache[g_ncache++] = GemmEntry{key, algo, res[pick].workspaceSize};
       }
     }
   }
