@@ -25,47 +25,60 @@
 
 namespace gdn {
 
-constexpr int kGateTok = 16;     // tokens per block of the gate kernel
-constexpr int kGateTiles = 8;    // 16-column tiles: 2 HV <= 128
+constexpr int kGateTok = 16;   // tokens per block of the gate kernel
+constexpr int kGateWaves = 8;  // waves per block, each a slice of the k-steps
+constexpr int kGateBatch = 5;  // k-steps whose operands a wave loads before multiplying any
 
-// [a | b] = x W_ab^T for 16 tokens, on 16x16x32 bf16 MFMA; wave w takes k-steps w, w + 4, ... and
-// the four partial tiles are summed in LDS; then the gates.
-__global__ void __launch_bounds__(256) k_gates(const uint16_t* __restrict__ x, int64_t ld_x, int64_t T, int H,
-                                               const uint16_t* __restrict__ w_ab, int hv,
-                                               const float* __restrict__ a_log, const float* __restrict__ dt_bias,
-                                               float* __restrict__ alpha, float* __restrict__ beta) {
-  __shared__ float part[4][kGateTiles][16][16];
+// [a | b] = x W_ab^T for 16 tokens on 16x16x32 bf16 MFMA, NT column tiles of 16 (2 HV <= 16 NT).
+// Wave w takes k-steps w, w + 8, ...; it loads kGateBatch steps of operands (its x piece and the NT
+// weight pieces of each) before multiplying, so a block's whole reduction costs about two memory
+// round trips; the eight partial tiles are summed in LDS, then the gates.
+template <int NT>
+__global__ void __launch_bounds__(64 * kGateWaves) k_gates(const uint16_t* __restrict__ x, int64_t ld_x, int64_t T,
+                                                          int H, const uint16_t* __restrict__ w_ab, int hv,
+                                                          const float* __restrict__ a_log,
+                                                          const float* __restrict__ dt_bias,
+                                                          float* __restrict__ alpha, float* __restrict__ beta) {
+  __shared__ float part[kGateWaves][NT][16][16];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, li = lane & 15, lq = lane >> 4;
   const int64_t t0 = int64_t(blockIdx.x) * kGateTok;
-  const int ncol = 2 * hv, ntile = (ncol + 15) / 16;
+  const int ncol = 2 * hv, nks = H / 32;
   const int64_t row = min(t0 + li, T - 1);  // rows past the end read the last row, not stored
-  f32x4 acc[kGateTiles];
-#pragma unroll
-  for (int j = 0; j < kGateTiles; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t* xr = x + row * ld_x + 8 * lq;
-  for (int s = w; s < H / 32; s += 4) {
-    const short8 av = ld_short8(xr + 32 * s);
+  const uint16_t* wr[NT];
 #pragma unroll
-    for (int j = 0; j < kGateTiles; ++j) {
-      if (j >= ntile) break;
-      const int col = min(16 * j + li, ncol - 1);
-      const short8 bv = ld_short8(w_ab + int64_t(col) * H + 32 * s + 8 * lq);
-      acc[j] = mfma16x16x32(av, bv, acc[j]);
+  for (int j = 0; j < NT; ++j) wr[j] = w_ab + int64_t(min(16 * j + li, ncol - 1)) * H + 8 * lq;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = w; s0 < nks; s0 += kGateWaves * kGateBatch) {
+    short8 av[kGateBatch], bv[kGateBatch][NT];
+#pragma unroll
+    for (int u = 0; u < kGateBatch; ++u) {
+      const int s = min(s0 + kGateWaves * u, nks - 1);  // clamped steps are loaded and not used
+      av[u] = ld_short8(xr + 32 * s);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) bv[u][j] = ld_short8(wr[j] + 32 * s);
     }
+#pragma unroll
+    for (int u = 0; u < kGateBatch; ++u)
+      if (s0 + kGateWaves * u < nks) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] = mfma16x16x32(av[u], bv[u][j], acc[j]);
+      }
   }
   // acc[j][r]: token 4lq + r, column 16j + li
 #pragma unroll
-  for (int j = 0; j < kGateTiles; ++j) {
-    if (j >= ntile) break;
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[w][j][4 * lq + r][li] = acc[j][r];
-  }
   __syncthreads();
-  for (int i = t; i < kGateTok * ncol; i += 256) {
+  for (int i = t; i < kGateTok * ncol; i += 64 * kGateWaves) {
     const int tok = i / ncol, col = i - tok * ncol;
     if (t0 + tok >= T) continue;
-    const float v = (part[0][col >> 4][tok][col & 15] + part[1][col >> 4][tok][col & 15]) +
-                    (part[2][col >> 4][tok][col & 15] + part[3][col >> 4][tok][col & 15]);
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kGateWaves; ++ww) v += part[ww][col >> 4][tok][col & 15];
     if (col < hv) {
       const float u = v + dt_bias[col];
       const float sp = fmaxf(u, 0.f) + log1pf(__expf(-fabsf(u)));  // softplus without overflow
@@ -174,9 +187,16 @@ hipError_t gemm_bf16_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
 hipError_t launch_gates(const void* x, int64_t ld_x, int64_t T, int H, const void* w_ab, int hv, const float* a_log,
                         const float* dt_bias, float* alpha, float* beta, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 grid(unsigned((T + kGateTok - 1) / kGateTok));
-  hipLaunchKernelGGL(k_gates, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), ld_x, T, H,
-                     static_cast<const uint16_t*>(w_ab), hv, a_log, dt_bias, alpha, beta);
+  const dim3 grid(unsigned((T + kGateTok - 1) / kGateTok)), block(64 * kGateWaves);
+  const auto* xp = static_cast<const uint16_t*>(x);
+  const auto* wp = static_cast<const uint16_t*>(w_ab);
+  switch ((2 * hv + 15) / 16) {  // column tiles; hv <= 64 is checked by the caller
+#define GDN_GATES(NT) \
+  case NT: hipLaunchKernelGGL(k_gates<NT>, grid, block, 0, s, xp, ld_x, T, H, wp, hv, a_log, dt_bias, alpha, beta); break;
+    GDN_GATES(1) GDN_GATES(2) GDN_GATES(3) GDN_GATES(4) GDN_GATES(5) GDN_GATES(6) GDN_GATES(7) GDN_GATES(8)
+#undef GDN_GATES
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
