@@ -4,4 +4,5 @@ from .gdn_oracle import (  # noqa: F401
     silu, sigmoid, short_conv, l2_normalize, gated_delta_rule, gated_delta_rule_product_form,
     zero_centred_rmsnorm, gdn_chain, prefill_chain, conv_tail, gdn_prefill, gdn_decode,
     gdn_verify, gdn_commit, softplus, gate_alpha_beta, in_projection, out_projection,
+    QSA_BLOCK, QSA_TOPK, partial_rope, qsa_compress, qsa_scores, qsa_select,
 )

@@ -20,6 +20,10 @@ Sources (the pages this follows; all quoted facts are restated, not copied):
        decoding with multi-token prediction (MTP), mean accepted length about 4.
   [P2] §01 (MTP row: one layer trained for multi-step prediction) and the §04 results table
        (four-step MTP accepted length): drafts of several tokens are checked in one pass.
+  [P2] §04 (QSA indexer data flow): 4 query heads and 1 key head; keys average-pooled over 4-token
+       micro-blocks, RMS-normalised, then given partial RoPE at the block's start position; block
+       score = sum over heads of ReLU(q . k_b), only for blocks already complete; the top 512 blocks
+       (2048 tokens) are kept and the incomplete tail block is always added.
   [P1] paper reading "Qwen3.8-Flash-Next" (方法): the normalised residual stream goes through
        learned projections, then the short conv; a data-dependent decay gate sets how long the
        state lives and a write gate scales the delta update.
@@ -34,6 +38,9 @@ Readings where the pages are silent (every one is also listed in the design note
   * L2: a / sqrt(sum(a^2) + l2_eps);  RMSNorm: y / sqrt(mean(y^2) + norm_eps) * (1 + w).
   * value head h reads QK head floor(h * HK / HV) (contiguous groups).
   * the state is stored [d_k][d_v] (row = key index); y carries an optional ``scale`` (1.0).
+  * QSA indexer (what the pages leave open): RMSNorm of the pooled key is m / sqrt(mean(m^2) +
+    1e-6) * w; partial RoPE rotates dims d and d + 32 (d < 32) of the first 64 by position * 1e4^(-d/32),
+    queries at their token index, compressed keys at 4b; ties in the top-k go to the lower block.
   * projections (the pages give no formula for the gates): q | k | v = x W_qkv, gate logits
     z = x W_z, gate pre-activations [a | b] = x W_ab, then beta = sigmoid(b) and
     alpha = exp(-exp(A_h) * softplus(a + delta_h)) with per-head vectors A, delta; the output
@@ -320,3 +327,58 @@ def in_projection(x, w_qkv, w_z, w_ab, a_log, dt_bias):
 def out_projection(o, w_out):
     """The mixer output o [T, HV*dv] back to the residual width: o W_out, fp64."""
     return _f64(o) @ _f64(w_out)
+
+
+# ------------------------------------------------------------------------ QSA compressed indexer ----
+
+QSA_BLOCK = 4        # keys per micro-block ([P2] §04: r = 4)
+QSA_TOPK = 512       # blocks kept per query (K = 2048 tokens)
+QSA_ROPE_DIMS = 64   # rotated dims of the 128 (a reading: "partial RoPE")
+QSA_ROPE_BASE = 1e4
+
+
+def partial_rope(x, pos):
+    """Rotate dims (d, d + 32), d < 32, of x [..., 128] by angle pos * base^(-d/32) (fp64)."""
+    x = np.array(_f64(x), dtype=np.float64, copy=True)
+    half = QSA_ROPE_DIMS // 2
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * QSA_ROPE_BASE ** (-np.arange(half) / half)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half].copy(), x[..., half:2 * half].copy()
+    x[..., :half] = a * c - b * s
+    x[..., half:2 * half] = a * s + b * c
+    return x
+
+
+def qsa_compress(k, w, eps=1e-6):
+    """Compressed keys of the complete micro-blocks of one sequence ([P2] §04): the mean of each 4
+    keys, RMS-normalised with gain w, then partial RoPE at the block's first position 4b.
+    k [T, 128] -> [floor(T/4), 128] fp64."""
+    k = _f64(k)
+    nb = k.shape[0] // QSA_BLOCK
+    m = k[:nb * QSA_BLOCK].reshape(nb, QSA_BLOCK, -1).mean(axis=1)
+    m = m / np.sqrt(np.mean(m * m, axis=1, keepdims=True) + eps) * _f64(w)[None, :]
+    return partial_rope(m, QSA_BLOCK * np.arange(nb))
+
+
+def qsa_scores(q, kbar, pos):
+    """I[i, b] = sum over the 4 heads of ReLU(rope(q_ih, pos_i) . kbar_b) for the blocks complete at
+    query i (4b + 3 <= pos_i); -inf elsewhere. q [M, 4, 128], kbar [N, 128], pos [M]."""
+    qr = partial_rope(q, np.asarray(pos)[:, None] * np.ones((1, _f64(q).shape[1])))
+    sc = np.maximum(np.einsum("mhd,nd->mhn", qr, _f64(kbar)), 0.0).sum(axis=1)
+    valid = (QSA_BLOCK * np.arange(sc.shape[1])[None, :] + QSA_BLOCK - 1) <= np.asarray(pos)[:, None]
+    return np.where(valid, sc, -np.inf)
+
+
+def qsa_select(scores, pos, topk=QSA_TOPK):
+    """Per query: the top-k complete blocks by score (ties to the lower block), listed in block
+    order, and the first token of the incomplete tail block (pos + 1 when the block is complete).
+    Returns (list of index arrays, tail_start [M])."""
+    out = []
+    for row in scores:
+        cand = np.nonzero(np.isfinite(row))[0]
+        if len(cand) > topk:
+            order = sorted(cand, key=lambda b: (-row[b], b))[:topk]
+            cand = np.sort(np.array(order))
+        out.append(cand.astype(np.int64))
+    pos = np.asarray(pos)
+    return out, QSA_BLOCK * ((pos + 1) // QSA_BLOCK)
