@@ -2,6 +2,8 @@
 // Every check runs before any HIP call, so a rejected call enqueues nothing and touches no output.
 #include <stdarg.h>
 #include <stdio.h>
+#include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include "gdn_internal.h"
@@ -97,6 +99,34 @@ Workspace plan_workspace(const Problem& p, void* base) {
 static hipError_t run(hipError_t e, const char* what) {
   if (e != hipSuccess) fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return e;
+}
+
+// QSA indexer configuration and cache capacity -> QsaShape.
+static gdn_status check_qsa(const qsa_cfg* cfg, int64_t cap, QsaShape& sh) {
+  if (!cfg) return fail(GDN_E_NULL, "cfg is NULL");
+  if (cfg->io_dtype != GDN_BF16 && cfg->io_dtype != GDN_F32)
+    return fail(GDN_E_DTYPE, "io_dtype %d is neither GDN_BF16 nor GDN_F32", cfg->io_dtype);
+  if (cfg->n_heads != 4 || cfg->d != 128 || cfg->block != 4)
+    return fail(GDN_E_UNSUPPORTED, "only 4 heads of dim 128 and blocks of 4 are implemented (%d, %d, %d)",
+                cfg->n_heads, cfg->d, cfg->block);
+  if (cfg->topk < 1 || cfg->topk > 4096) return fail(GDN_E_UNSUPPORTED, "topk %d is outside 1..4096", cfg->topk);
+  if (cfg->rope_dims < 0 || cfg->rope_dims > 128 || cfg->rope_dims % 16)
+    return fail(GDN_E_UNSUPPORTED, "rope_dims %d must be a multiple of 16 in 0..128", cfg->rope_dims);
+  if (!(cfg->rope_base > 0.f) || !(cfg->rope_base < 3.4e38f))
+    return fail(GDN_E_VALUE, "rope_base %g must be positive and finite", cfg->rope_base);
+  if (!(cfg->norm_eps >= 0.f)) return fail(GDN_E_VALUE, "norm_eps %g must be >= 0", cfg->norm_eps);
+  if (cap < 0) return fail(GDN_E_SHAPE, "negative cap_blocks %lld", (long long)cap);
+  const int64_t cap_max = int64_t(kSelSeg) * (kSelSeg / cfg->topk);
+  if (cap > cap_max)
+    return fail(GDN_E_UNSUPPORTED, "cap_blocks %lld exceeds %lld, the most a query can select from at topk %d",
+                (long long)cap, (long long)cap_max, cfg->topk);
+  sh.topk = cfg->topk;
+  sh.half = cfg->rope_dims / 2;
+  sh.log2_base = log2(double(cfg->rope_base));
+  sh.eps = cfg->norm_eps;
+  sh.bf16 = cfg->io_dtype == GDN_BF16;
+  sh.cap = cap;
+  return GDN_OK;
 }
 
 }  // namespace gdn
@@ -478,6 +508,154 @@ gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const voi
   if (gemm_bf16_tn(hidden, T, vz, w_out, vz, o, vz, y, hidden, workspace, workspace_bytes,
                    static_cast<hipStream_t>(hip_stream), &why) != hipSuccess)
     return fail(GDN_E_HIP, "output projection: %s", why);
+  return GDN_OK;
+}
+
+void qsa_cfg_default(qsa_cfg* cfg) {
+  if (!cfg) return;
+  cfg->n_heads = 4;
+  cfg->d = 128;
+  cfg->block = 4;
+  cfg->topk = 512;
+  cfg->rope_dims = 64;
+  cfg->io_dtype = GDN_BF16;
+  cfg->rope_base = 10000.f;
+  cfg->norm_eps = 1e-6f;
+}
+
+gdn_status qsa_compress(const qsa_cfg* cfg, int32_t n_seqs, int64_t total_tokens, const int32_t* cu_seqlens,
+                        const int32_t* cu_seqlens_host, const void* k, int64_t ld_k, const float* norm_w, void* kbar,
+                        int64_t cap_blocks, void* pending, void* hip_stream) {
+  g_last_error[0] = 0;
+  QsaShape sh{};
+  gdn_status st = check_qsa(cfg, cap_blocks, sh);
+  if (st != GDN_OK) return st;
+  if (n_seqs < 0 || total_tokens < 0) return fail(GDN_E_SHAPE, "negative n_seqs or total_tokens");
+  if (n_seqs > 65535) return fail(GDN_E_UNSUPPORTED, "n_seqs %d > 65535", n_seqs);
+  if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_E_UNSUPPORTED, "total_tokens must stay below 2^31");
+  if (n_seqs == 0 && total_tokens != 0) return fail(GDN_E_SHAPE, "tokens without sequences");
+  if (n_seqs == 0) return GDN_OK;
+  if (!cu_seqlens) return fail(GDN_E_NULL, "cu_seqlens is required");
+  if (total_tokens > 0 && (!k || !norm_w || (!kbar && cap_blocks > 0)))
+    return fail(GDN_E_NULL, "k, norm_w and kbar are required");
+  const int64_t elem = sh.bf16 ? 2 : 4;
+  if (ld_k < 128) return fail(GDN_E_SHAPE, "ld_k %lld < 128", (long long)ld_k);
+  if ((ld_k * elem) % 16) return fail(GDN_E_ALIGN, "ld_k must be a multiple of 16 bytes");
+  const void* ptrs[] = {k, norm_w, kbar, pending};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (!aligned4(cu_seqlens)) return fail(GDN_E_ALIGN, "cu_seqlens must be 4-byte aligned");
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[n_seqs] != total_tokens)
+      return fail(GDN_E_SHAPE, "cu_seqlens must start at 0 and end at total_tokens");
+    for (int i = 0; i < n_seqs; ++i) {
+      const int64_t len = int64_t(cu_seqlens_host[i + 1]) - cu_seqlens_host[i];
+      if (len < 0) return fail(GDN_E_SHAPE, "cu_seqlens decreases at %d", i);
+      if (len / 4 > cap_blocks)
+        return fail(GDN_E_SHAPE, "sequence %d has %lld blocks, cap_blocks is %lld", i, (long long)(len / 4),
+                    (long long)cap_blocks);
+    }
+  }
+  if (total_tokens == 0) return GDN_OK;
+  if (run(launch_qsa_compress(sh, n_seqs, total_tokens, cu_seqlens, k, ld_k, norm_w, kbar, pending,
+                              static_cast<hipStream_t>(hip_stream)), "qsa compress") != hipSuccess)
+    return GDN_E_HIP;
+  return GDN_OK;
+}
+
+gdn_status qsa_workspace(const qsa_cfg* cfg, int64_t rows, int64_t cap_blocks, size_t* bytes) {
+  g_last_error[0] = 0;
+  QsaShape sh{};
+  gdn_status st = check_qsa(cfg, cap_blocks, sh);
+  if (st != GDN_OK) return st;
+  if (!bytes) return fail(GDN_E_NULL, "bytes is NULL");
+  if (rows < 0) return fail(GDN_E_SHAPE, "negative rows");
+  plan_qsa_ws(sh, rows, nullptr, bytes);
+  return GDN_OK;
+}
+
+// Checks shared by qsa_select and qsa_decode.
+static gdn_status check_qsa_rows(const QsaShape& sh, int64_t rows, const void* q, int64_t ld_q, const void* kbar,
+                                 const int32_t* sel, const int32_t* n_sel, const int32_t* tail) {
+  if (rows > 0 && (!q || !sel || !n_sel || !tail || (!kbar && sh.cap > 0)))
+    return fail(GDN_E_NULL, "q, kbar, sel, n_sel and tail are required");
+  const int64_t elem = sh.bf16 ? 2 : 4;
+  if (ld_q < 512) return fail(GDN_E_SHAPE, "ld_q %lld < 4 * 128", (long long)ld_q);
+  if ((ld_q * elem) % 16) return fail(GDN_E_ALIGN, "ld_q must be a multiple of 16 bytes");
+  if ((q && !aligned16(q)) || (kbar && !aligned16(kbar)))
+    return fail(GDN_E_ALIGN, "q and kbar must be 16-byte aligned");
+  if (!aligned4(sel) || !aligned4(n_sel) || !aligned4(tail))
+    return fail(GDN_E_ALIGN, "sel, n_sel and tail must be 4-byte aligned");
+  return GDN_OK;
+}
+
+gdn_status qsa_select(const qsa_cfg* cfg, int32_t n_seqs, int64_t total_tokens, const int32_t* cu_seqlens,
+                      const void* q, int64_t ld_q, const void* kbar, int64_t cap_blocks, int32_t* sel,
+                      int32_t* n_sel, int32_t* tail, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_last_error[0] = 0;
+  QsaShape sh{};
+  gdn_status st = check_qsa(cfg, cap_blocks, sh);
+  if (st != GDN_OK) return st;
+  if (n_seqs < 0 || total_tokens < 0) return fail(GDN_E_SHAPE, "negative n_seqs or total_tokens");
+  if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_E_UNSUPPORTED, "total_tokens must stay below 2^31");
+  if (n_seqs == 0 && total_tokens != 0) return fail(GDN_E_SHAPE, "tokens without sequences");
+  if (total_tokens > 0 && !cu_seqlens) return fail(GDN_E_NULL, "cu_seqlens is required");
+  if (cu_seqlens && !aligned4(cu_seqlens)) return fail(GDN_E_ALIGN, "cu_seqlens must be 4-byte aligned");
+  st = check_qsa_rows(sh, total_tokens, q, ld_q, kbar, sel, n_sel, tail);
+  if (st != GDN_OK) return st;
+  if (total_tokens == 0) return GDN_OK;
+  size_t one = 0;
+  plan_qsa_ws(sh, 1, nullptr, &one);
+  if (!workspace || workspace_bytes < one)
+    return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, at least %zu needed", workspace ? workspace_bytes : 0, one);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
+  int64_t lo = 1, hi = total_tokens;  // most rows whose workspace fits
+  while (lo < hi) {
+    const int64_t mid = hi - (hi - lo) / 2;
+    size_t b = 0;
+    plan_qsa_ws(sh, mid, nullptr, &b);
+    if (b <= workspace_bytes) lo = mid; else hi = mid - 1;
+  }
+  size_t used = 0;
+  const QsaWs ws = plan_qsa_ws(sh, lo, workspace, &used);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  for (int64_t r0 = 0; r0 < total_tokens; r0 += lo)
+    if (run(launch_qsa_rows(sh, ws, r0, std::min(lo, total_tokens - r0), cu_seqlens, n_seqs, nullptr, q, ld_q, kbar,
+                            sel, n_sel, tail, s), "qsa select") != hipSuccess)
+      return GDN_E_HIP;
+  return GDN_OK;
+}
+
+gdn_status qsa_decode(const qsa_cfg* cfg, int32_t batch, const int32_t* n_tok, const void* q, int64_t ld_q,
+                      const void* k, int64_t ld_k, const float* norm_w, void* pending, void* kbar,
+                      int64_t cap_blocks, int32_t* sel, int32_t* n_sel, int32_t* tail, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  g_last_error[0] = 0;
+  QsaShape sh{};
+  gdn_status st = check_qsa(cfg, cap_blocks, sh);
+  if (st != GDN_OK) return st;
+  if (batch < 0) return fail(GDN_E_SHAPE, "negative batch %d", batch);
+  st = check_qsa_rows(sh, batch, q, ld_q, kbar, sel, n_sel, tail);
+  if (st != GDN_OK) return st;
+  if (batch > 0 && (!n_tok || !k || !norm_w || !pending)) return fail(GDN_E_NULL, "n_tok, k, norm_w and pending are required");
+  const int64_t elem = sh.bf16 ? 2 : 4;
+  if (ld_k < 128) return fail(GDN_E_SHAPE, "ld_k %lld < 128", (long long)ld_k);
+  if ((ld_k * elem) % 16) return fail(GDN_E_ALIGN, "ld_k must be a multiple of 16 bytes");
+  if ((k && !aligned16(k)) || (norm_w && !aligned16(norm_w)) || (pending && !aligned16(pending)))
+    return fail(GDN_E_ALIGN, "k, norm_w and pending must be 16-byte aligned");
+  if (!aligned4(n_tok)) return fail(GDN_E_ALIGN, "n_tok must be 4-byte aligned");
+  if (batch == 0) return GDN_OK;
+  size_t need = 0;
+  plan_qsa_ws(sh, batch, nullptr, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
+  const QsaWs ws = plan_qsa_ws(sh, batch, workspace, &need);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (run(launch_qsa_append(sh, batch, n_tok, k, ld_k, norm_w, pending, kbar, s), "qsa append") != hipSuccess ||
+      run(launch_qsa_rows(sh, ws, 0, batch, nullptr, batch, n_tok, q, ld_q, kbar, sel, n_sel, tail, s),
+          "qsa decode select") != hipSuccess)
+    return GDN_E_HIP;
   return GDN_OK;
 }
 

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "gdn.h"
+#include "qsa.h"
 
 namespace gdn {
 
@@ -133,5 +134,36 @@ hipError_t gemm_bf16_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
                         void* D, int64_t ldd, void* ws, size_t ws_bytes, hipStream_t s, const char** why);
 hipError_t launch_gates(const void* x, int64_t ld_x, int64_t T, int H, const void* w_ab, int hv, const float* a_log,
                         const float* dt_bias, float* alpha, float* beta, hipStream_t s);
+
+// ---- QSA compressed indexer ----
+constexpr int kSelSeg = 16384;  // scores per select workgroup (1024 threads x 16)
+
+struct QsaShape {
+  int topk;
+  int half;          // rope_dims / 2
+  double log2_base;  // log2(rope_base)
+  float eps;         // RMSNorm eps
+  bool bf16;         // io dtype
+  int64_t cap;       // compressed-key cache capacity per sequence, in blocks
+};
+
+struct QsaWs {
+  float* qr;          // [rows][4][128] rotated queries
+  int2* info;         // [rows] (sequence, position)
+  float* scores;      // [rows][ld_s]
+  int64_t ld_s;
+  uint32_t* cand_key; // [rows][segmax][topk] segment candidates (rows longer than one segment)
+  int32_t* cand_idx;
+  int segmax;
+};
+
+QsaWs plan_qsa_ws(const QsaShape& sh, int64_t rows, void* base, size_t* bytes);
+hipError_t launch_qsa_compress(const QsaShape& sh, int n_seqs, int64_t T, const int32_t* cu, const void* k,
+                               int64_t ld_k, const float* norm_w, void* kbar, void* pending, hipStream_t s);
+hipError_t launch_qsa_append(const QsaShape& sh, int B, const int32_t* n_tok, const void* k, int64_t ld_k,
+                             const float* norm_w, void* pending, void* kbar, hipStream_t s);
+hipError_t launch_qsa_rows(const QsaShape& sh, const QsaWs& ws, int64_t row0, int64_t rows, const int32_t* cu,
+                           int n_seqs, const int32_t* n_tok, const void* q, int64_t ld_q, const void* kbar,
+                           int32_t* sel, int32_t* n_sel, int32_t* tail, hipStream_t s);
 
 }  // namespace gdn

@@ -1,0 +1,563 @@
+// Compressed block indexer of Qwen Sparse Attention (analysis notes "Qwen3.8-Flash-Next：架构、效率与
+// 技术谱系" §04 indexer data flow; paper reading "On the Design of Qwen3.8-Next Architecture … 精读"
+// §四 4.2): keys pooled over 4-token micro-blocks, RMS-normalised and rotated to the block's first
+// position; each query's 4 heads score every complete block by a sum of ReLU'd dot products; the
+// top-k blocks are kept.
+//
+// Kernels:
+//   k_qsa_compress  one 16-lane group per block: pool, RMSNorm, partial RoPE, store (HBM-bound);
+//   k_qsa_append    decode: a token's key joins its sequence's pending block, or completes it;
+//   k_qsa_qprep     one row per query: find its sequence and position, rotate its 4 heads (fp32);
+//   k_qsa_score     a row's compressed keys streamed by 16-lane groups, 16 B per lane (HBM-bound
+//                   in decode, where the cache is read once per step);
+//   k_qsa_select    one 1024-thread block per 16384 scores: exact top-k by a 3-digit radix select
+//                   on the score bits held in registers, then an ordered compaction;
+//   k_qsa_merge     rows longer than one segment: the same select over the segments' candidates
+//                   (every global top-k block is in its own segment's top-k).
+//
+// Lane layout shared by the vector kernels: lane m of a 16-lane group holds dims 8m .. 8m+7.
+// Rotation pairs dim d with d + rope_dims/2 (d < rope_dims/2) at angle pos * base^(-2d/rope_dims);
+// the angle is formed and reduced mod 2 pi in fp64, so positions near 2^20 keep fp32 accuracy.
+#include <math.h>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+constexpr int kQsaD = 128;       // head dim of indexer queries and keys
+constexpr int kQsaHeads = 4;     // query heads
+constexpr int kScoreChunk = 1024;  // blocks per workgroup of the score kernel
+constexpr int kScoreUnroll = 8;    // blocks per 16-lane group in flight
+constexpr int kSelThreads = 1024;
+constexpr int kSelPer = 16;        // scores per thread
+
+// ---- rotation -------------------------------------------------------------------------------
+struct RopeLane {
+  double theta[8];  // angle per position of each of the lane's dims (0 for unrotated lanes)
+  int partner;      // lane (within the group) holding the other member of each pair
+  int kind;         // 0 not rotated, 1 first member (x c - y s), 2 second member (y s + x c)
+};
+
+__device__ __forceinline__ RopeLane rope_lane(int m, const QsaShape& sh) {
+  RopeLane r;
+  const int h8 = sh.half / 8;
+  int first = 0;
+  if (m < h8) {
+    r.kind = 1; r.partner = m + h8; first = 8 * m;
+  } else if (m < 2 * h8) {
+    r.kind = 2; r.partner = m - h8; first = 8 * (m - h8);
+  } else {
+    r.kind = 0; r.partner = m;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    r.theta[i] = r.kind ? exp2(-double(first + i) / double(sh.half) * sh.log2_base) : 0.0;
+  return r;
+}
+
+__device__ __forceinline__ void rope8(float (&y)[8], const RopeLane& rl, double pos, int lane) {
+  const int src = (lane & 0x30) | rl.partner;
+  float yp[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) yp[i] = __shfl(y[i], src, kWave);
+  if (rl.kind == 0) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double a = pos * rl.theta[i];
+    const double n = rint(a * (0.5 / M_PI));
+    float s, c;
+    sincosf(float(fma(-n, 2.0 * M_PI, a)), &s, &c);
+    y[i] = rl.kind == 1 ? y[i] * c - yp[i] * s : yp[i] * s + y[i] * c;
+  }
+}
+
+template <typename IO>
+__device__ __forceinline__ void ld8(const IO* p, float (&o)[8]) {
+  constexpr int N = vec16<IO>::N;
+#pragma unroll
+  for (int i = 0; i < 8; i += N) vec16<IO>::ld(p + i, o + i);
+}
+
+template <typename IO>
+__device__ __forceinline__ void st8(IO* p, const float (&o)[8]) {
+  constexpr int N = vec16<IO>::N;
+#pragma unroll
+  for (int i = 0; i < 8; i += N) vec16<IO>::st(p + i, o + i);
+}
+
+// Pooled block sum (4 keys added) -> RMSNorm with gain -> rotation to pos0 -> store. The 16 lanes of
+// a group call it together.
+template <typename IO>
+__device__ __forceinline__ void finish_block(float (&y)[8], const float (&w)[8], const RopeLane& rl, int64_t pos0,
+                                             float eps, int lane, IO* out) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    y[i] *= 0.25f;
+    ss += y[i] * y[i];
+  }
+  ss = group_sum<16>(ss);
+  const float r = 1.0f / sqrtf(ss * (1.0f / kQsaD) + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] *= r * w[i];
+  rope8(y, rl, double(pos0), lane);
+  st8(out, y);
+}
+
+// ---- compression of a prefill: grid (block groups of 64, sequences), 16 groups per workgroup ----
+template <typename IO>
+__global__ void __launch_bounds__(256) k_qsa_compress(QsaShape sh, const IO* __restrict__ k, int64_t ld_k,
+                                                      const int32_t* __restrict__ cu, int64_t T,
+                                                      const float* __restrict__ norm_w, IO* __restrict__ kbar,
+                                                      IO* __restrict__ pending) {
+  const int t = threadIdx.x, lane = t & 63, g = t >> 4, m = t & 15;
+  const int n = blockIdx.y;
+  const int64_t s0 = min(max(int64_t(cu[n]), int64_t(0)), T);
+  const int64_t s1 = min(max(int64_t(cu[n + 1]), s0), T);
+  const int64_t len = s1 - s0, nb = min(len / 4, sh.cap);
+  float w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = norm_w[8 * m + i];
+  const RopeLane rl = rope_lane(m, sh);
+  for (int i = 0; i < 4; ++i) {
+    const int64_t b = int64_t(blockIdx.x) * 64 + g + 16 * i;
+    if (b >= nb) break;
+    float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float x[8];
+      ld8(k + (s0 + 4 * b + j) * ld_k + 8 * m, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] += x[e];
+    }
+    finish_block(y, w, rl, 4 * b, sh.eps, lane, kbar + (int64_t(n) * sh.cap + b) * kQsaD + 8 * m);
+  }
+  if (pending && blockIdx.x == 0 && g < int(len & 3)) {
+    float x[8];
+    ld8(k + (s0 + (len & ~int64_t(3)) + g) * ld_k + 8 * m, x);
+    st8(pending + (int64_t(n) * 3 + g) * kQsaD + 8 * m, x);
+  }
+}
+
+// ---- decode: the new key of sequence b joins slot (n-1) % 4 of its block; slot 3 completes it ----
+template <typename IO>
+__global__ void __launch_bounds__(64) k_qsa_append(QsaShape sh, int B, const int32_t* __restrict__ n_tok,
+                                                   const IO* __restrict__ k, int64_t ld_k,
+                                                   const float* __restrict__ norm_w, IO* __restrict__ pending,
+                                                   IO* __restrict__ kbar) {
+  const int t = threadIdx.x, lane = t, m = t & 15;
+  const int b = blockIdx.x * 4 + (t >> 4);
+  if (b >= B) return;
+  const int n = n_tok[b];
+  if (n < 1) return;
+  const int j = (n - 1) & 3;
+  float x[8];
+  ld8(k + int64_t(b) * ld_k + 8 * m, x);
+  if (j < 3) {
+    st8(pending + (int64_t(b) * 3 + j) * kQsaD + 8 * m, x);
+    return;
+  }
+  const int64_t blk = n / 4 - 1;
+  if (blk >= sh.cap) return;
+  float w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = norm_w[8 * m + i];
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj) {  // token order, as in the prefill compression
+    float p[8];
+    ld8(pending + (int64_t(b) * 3 + jj) * kQsaD + 8 * m, p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] += p[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] += x[e];
+  const RopeLane rl = rope_lane(m, sh);
+  finish_block(y, w, rl, 4 * blk, sh.eps, lane, kbar + (int64_t(b) * sh.cap + blk) * kQsaD + 8 * m);
+}
+
+// ---- per-row preparation: (sequence, position) and the rotated fp32 queries -------------------
+// Prefill rows are tokens row0 + r of the packed batch (cu given); decode rows are sequences with
+// position n_tok[r] - 1.
+template <typename IO>
+__global__ void __launch_bounds__(64) k_qsa_qprep(QsaShape sh, const IO* __restrict__ q, int64_t ld_q,
+                                                  int64_t row0, const int32_t* __restrict__ cu, int n_seqs,
+                                                  const int32_t* __restrict__ n_tok, float* __restrict__ qr,
+                                                  int2* __restrict__ info) {
+  const int t = threadIdx.x, h = t >> 4, m = t & 15;
+  const int64_t r = blockIdx.x, row = row0 + r;
+  int seq, pos;
+  if (cu) {
+    int lo = 0, hi = n_seqs;  // largest n with cu[n] <= row
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (int64_t(cu[mid]) <= row) lo = mid; else hi = mid;
+    }
+    seq = lo;
+    pos = int(row - min(int64_t(cu[lo]), row));
+  } else {
+    seq = int(r);
+    pos = n_tok[r] - 1;
+  }
+  float y[8];
+  ld8(q + row * ld_q + h * kQsaD + 8 * m, y);
+  const RopeLane rl = rope_lane(m, sh);
+  rope8(y, rl, double(max(pos, 0)), t);
+  float* o = qr + r * (kQsaHeads * kQsaD) + h * kQsaD + 8 * m;
+  *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(y[4], y[5], y[6], y[7]);
+  if (t == 0) info[r] = make_int2(seq, pos);
+}
+
+__device__ __forceinline__ int64_t row_blocks(int pos, int64_t cap) {
+  return pos < 0 ? 0 : min(int64_t(pos + 1) / 4, cap);
+}
+
+// Sum over the 4 heads of ReLU(dot) for one compressed key: p[h] are a lane's partial dots over its
+// 8 dims. The heads are spread over the lanes while being reduced (lane bits 3, 2 pick the head), so
+// the whole reduction takes 7 shuffles instead of 16.
+__device__ __forceinline__ float head_relu_sum(const float (&p)[4], int m) {
+  const bool b3 = m & 8, b2 = m & 4;
+  const float r0 = __shfl_xor(b3 ? p[0] : p[2], 8, kWave);
+  const float r1 = __shfl_xor(b3 ? p[1] : p[3], 8, kWave);
+  const float k0 = (b3 ? p[2] : p[0]) + r0, k1 = (b3 ? p[3] : p[1]) + r1;  // heads 2 b3, 2 b3 + 1
+  const float r = __shfl_xor(b2 ? k0 : k1, 4, kWave);
+  float v = (b2 ? k1 : k0) + r;  // head 2 b3 + b2, summed over 4 lanes
+  v += __shfl_xor(v, 2, kWave);
+  v += __shfl_xor(v, 1, kWave);
+  v = fmaxf(v, 0.f);
+  v += __shfl_xor(v, 4, kWave);
+  v += __shfl_xor(v, 8, kWave);
+  return v;
+}
+
+// ---- scores: grid (rows, block chunks of 1024); 16 groups of 16 lanes, one compressed key each --
+template <typename IO>
+__global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __restrict__ qr,
+                                                   const int2* __restrict__ info, const IO* __restrict__ kbar,
+                                                   float* __restrict__ scores, int64_t ld_s) {
+  constexpr int N = vec16<IO>::N, V = 8 / N;
+  const int t = threadIdx.x, g = t >> 4, m = t & 15;
+  const int64_t r = blockIdx.x;
+  const int2 in = info[r];
+  const int64_t nb = row_blocks(in.y, sh.cap);
+  const int64_t b0 = int64_t(blockIdx.y) * kScoreChunk;
+  if (b0 >= nb) return;
+  const int64_t end = min(b0 + kScoreChunk, nb);
+  float qv[kQsaHeads][8];
+#pragma unroll
+  for (int h = 0; h < kQsaHeads; ++h) {
+    const float* p = qr + r * (kQsaHeads * kQsaD) + h * kQsaD + 8 * m;
+    const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
+    qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
+    qv[h][4] = c.x; qv[h][5] = c.y; qv[h][6] = c.z; qv[h][7] = c.w;
+  }
+  const IO* base = kbar + int64_t(in.x) * sh.cap * kQsaD + 8 * m;
+  float* out = scores + r * ld_s;
+  for (int64_t s = b0 + g; s < end; s += 16 * kScoreUnroll) {
+    uint4 raw[kScoreUnroll][V];
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int64_t b = min(s + 16 * u, end - 1);  // clamped blocks are loaded, not stored
+#pragma unroll
+      for (int v = 0; v < V; ++v) raw[u][v] = *reinterpret_cast<const uint4*>(base + b * kQsaD + v * N);
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      float x[8];
+#pragma unroll
+      for (int v = 0; v < V; ++v) vec16<IO>::cvt(raw[u][v], x + v * N);
+      float p[kQsaHeads];
+#pragma unroll
+      for (int h = 0; h < kQsaHeads; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaf(qv[h][i], x[i], a);
+        p[h] = a;
+      }
+      const float sc = head_relu_sum(p, m);
+      if (m == 0 && s + 16 * u < end) out[s + 16 * u] = sc;
+    }
+  }
+}
+
+// ---- exact top-k of up to 16384 keys held 16 per thread by 1024 threads ------------------------
+// Keys are score bits with the sign cleared: scores are >= 0, so the unsigned order of the bits is
+// the order of the scores. The k-th largest key is found digit by digit (bits 30..20, 19..9, 8..0),
+// each digit from a 2048-bin LDS histogram of the keys that match the digits found so far; then the
+// keys above it and the first `need_eq` keys equal to it, in index order, are selected.
+struct SelLds {
+  uint32_t hist[2048];
+  uint32_t table[kSelPer * 16];  // per (slot, wave): selected-above count << 16 | equal count
+  uint32_t wtot[16];
+  uint32_t digit, above;
+};
+
+// Inclusive scan of one value per thread over the 1024 threads; *total gets the sum.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, SelLds& L, uint32_t* total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) L.wtot[w] = v;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const uint32_t x = L.wtot[u];
+    off += u < w ? x : 0u;
+    tot += x;
+  }
+  *total = tot;
+  __syncthreads();
+  return v + off;
+}
+
+// Threshold key T and how many keys equal to T to take, for `need` <= number of valid keys.
+__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], uint32_t valid, uint32_t need,
+                                                SelLds& L, uint32_t* T_out, uint32_t* need_eq) {
+  const int t = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  const int shifts[3] = {20, 9, 0}, bits[3] = {11, 11, 9};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass], nbins = 1 << bits[pass];
+    L.hist[t] = 0;
+    L.hist[t + kSelThreads] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j)
+      if (((valid >> j) & 1u) && (key[j] & pmask) == prefix)
+        atomicAdd(&L.hist[(key[j] >> shift) & uint32_t(nbins - 1)], 1u);
+    __syncthreads();
+    // thread t: bins nbins-1-2t and nbins-2-2t, so the scan runs from the top bin down
+    const bool mine = 2 * t < nbins;
+    const uint32_t hh = mine ? L.hist[nbins - 1 - 2 * t] : 0u, hl = mine ? L.hist[nbins - 2 - 2 * t] : 0u;
+    uint32_t tot;
+    const uint32_t incl = block_scan(hh + hl, L, &tot);
+    const uint32_t excl = incl - hh - hl;
+    if (mine && excl < need && need <= incl) {
+      if (excl + hh >= need) {
+        L.digit = uint32_t(nbins - 1 - 2 * t);
+        L.above = excl;
+      } else {
+        L.digit = uint32_t(nbins - 2 - 2 * t);
+        L.above = excl + hh;
+      }
+    }
+    __syncthreads();
+    need -= L.above;
+    prefix |= L.digit << shift;
+    pmask |= uint32_t(nbins - 1) << shift;
+    __syncthreads();
+  }
+  *T_out = prefix;
+  *need_eq = need;
+}
+
+// Selects (all valid keys when n_valid <= k, else the top k) and calls emit(j, out_pos) for each
+// selected key j of this thread, out_pos counting in index order (index = j * 1024 + thread).
+// Returns the number selected.
+template <typename F>
+__device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], uint32_t valid, uint32_t n_valid,
+                                                uint32_t k, SelLds& L, F&& emit) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const bool all = n_valid <= k;
+  uint32_t T = 0, need_eq = 0;
+  if (!all) radix_threshold(key, valid, k, L, &T, &need_eq);
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  uint32_t pg[kSelPer], pe[kSelPer];
+#pragma unroll
+  for (int j = 0; j < kSelPer; ++j) {
+    const bool v = (valid >> j) & 1u;
+    const bool gt = v && (all || key[j] > T), eq = v && !all && key[j] == T;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    pg[j] = __popcll(bg & below);
+    pe[j] = __popcll(be & below);
+    if (lane == 0) L.table[j * 16 + w] = (uint32_t(__popcll(bg)) << 16) | uint32_t(__popcll(be));
+  }
+  __syncthreads();
+  const uint32_t tv = t < kSelPer * 16 ? L.table[t] : 0u;
+  uint32_t tot;
+  const uint32_t incl = block_scan(tv, L, &tot);
+  if (t < kSelPer * 16) L.table[t] = incl - tv;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSelPer; ++j) {
+    const bool v = (valid >> j) & 1u;
+    const bool gt = v && (all || key[j] > T), eq = v && !all && key[j] == T;
+    const uint32_t base = L.table[j * 16 + w];
+    const uint32_t gb = (base >> 16) + pg[j], eb = (base & 0xffffu) + pe[j];
+    if (gt || (eq && eb < need_eq)) emit(j, gb + min(eb, need_eq));
+  }
+  return (tot >> 16) + min(tot & 0xffffu, need_eq);
+}
+
+__device__ __forceinline__ void finish_row(int32_t* sel_row, uint32_t count, uint32_t k, int pos, int32_t* n_sel,
+                                           int32_t* tail) {
+  for (uint32_t p = count + threadIdx.x; p < k; p += kSelThreads) sel_row[p] = -1;
+  if (threadIdx.x == 0) {
+    *n_sel = int32_t(count);
+    *tail = pos < 0 ? 0 : 4 * ((pos + 1) / 4);
+  }
+}
+
+// Segment pass: grid (rows, segments). A row with one segment is finished here; longer rows leave
+// their segment's top-k (key, block) candidates for k_qsa_merge.
+__global__ void __launch_bounds__(kSelThreads) k_qsa_select(QsaShape sh, const int2* __restrict__ info,
+                                                            const float* __restrict__ scores, int64_t ld_s,
+                                                            uint32_t* __restrict__ cand_key,
+                                                            int32_t* __restrict__ cand_idx, int segmax,
+                                                            int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+                                                            int32_t* __restrict__ tail) {
+  __shared__ SelLds L;
+  const int t = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int sg = blockIdx.y;
+  const int pos = info[r].y;
+  const int64_t nb = row_blocks(pos, sh.cap);
+  const int nseg = int((nb + kSelSeg - 1) / kSelSeg);
+  if (sg >= max(nseg, 1)) return;
+  const int64_t seg0 = int64_t(sg) * kSelSeg;
+  const uint32_t n = uint32_t(min(int64_t(kSelSeg), nb - seg0 > 0 ? nb - seg0 : int64_t(0)));
+  const float* row = scores + r * ld_s + seg0;
+  uint32_t key[kSelPer], valid = 0;
+#pragma unroll
+  for (int j = 0; j < kSelPer; ++j) {
+    const uint32_t i = uint32_t(j * kSelThreads + t);
+    const bool v = i < n;
+    key[j] = v ? (__float_as_uint(row[i]) & 0x7fffffffu) : 0u;
+    valid |= uint32_t(v) << j;
+  }
+  const uint32_t k = uint32_t(sh.topk);
+  if (nseg <= 1) {
+    int32_t* srow = sel + r * sh.topk;
+    const uint32_t cnt = select_topk(key, valid, n, k, L, [&](int j, uint32_t p) { srow[p] = j * kSelThreads + t; });
+    finish_row(srow, cnt, k, pos, n_sel + r, tail + r);
+  } else {
+    const int64_t c0 = (r * segmax + sg) * int64_t(sh.topk);
+    select_topk(key, valid, n, k, L, [&](int j, uint32_t p) {
+      cand_key[c0 + p] = key[j];
+      cand_idx[c0 + p] = int32_t(seg0 + j * kSelThreads + t);
+    });
+  }
+}
+
+// Merge pass for rows of several segments: candidates of segment s sit at s * k .. s * k + c_s - 1,
+// in block order, so list position order is block order.
+__global__ void __launch_bounds__(kSelThreads) k_qsa_merge(QsaShape sh, const int2* __restrict__ info,
+                                                           const uint32_t* __restrict__ cand_key,
+                                                           const int32_t* __restrict__ cand_idx, int segmax,
+                                                           int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+                                                           int32_t* __restrict__ tail) {
+  __shared__ SelLds L;
+  const int t = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int pos = info[r].y;
+  const int64_t nb = row_blocks(pos, sh.cap);
+  const int nseg = int((nb + kSelSeg - 1) / kSelSeg);
+  if (nseg <= 1) return;
+  const uint32_t k = uint32_t(sh.topk);
+  const int64_t c0 = r * segmax * int64_t(sh.topk);
+  uint32_t key[kSelPer], valid = 0, nv = 0;
+  int32_t idx[kSelPer];
+#pragma unroll
+  for (int j = 0; j < kSelPer; ++j) {
+    const uint32_t p = uint32_t(j * kSelThreads + t), s = p / k, i = p - s * k;
+    const int64_t cs = s < uint32_t(nseg) ? min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)) : 0;
+    const bool v = int64_t(i) < cs;
+    key[j] = v ? cand_key[c0 + p] : 0u;
+    idx[j] = v ? cand_idx[c0 + p] : 0;
+    valid |= uint32_t(v) << j;
+  }
+  for (int s = 0; s < nseg; ++s) nv += uint32_t(min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)));
+  int32_t* srow = sel + r * sh.topk;
+  const uint32_t cnt = select_topk(key, valid, nv, k, L, [&](int j, uint32_t p) { srow[p] = idx[j]; });
+  finish_row(srow, cnt, k, pos, n_sel + r, tail + r);
+}
+
+// ---- launchers ----------------------------------------------------------------------------------
+QsaWs plan_qsa_ws(const QsaShape& sh, int64_t rows, void* base, size_t* bytes) {
+  QsaWs ws{};
+  char* b = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) -> void* {
+    void* r = b ? static_cast<void*>(b + off) : nullptr;
+    off += (n + 255) & ~size_t(255);
+    return r;
+  };
+  ws.segmax = int(std::max<int64_t>(1, (sh.cap + kSelSeg - 1) / kSelSeg));
+  ws.ld_s = (sh.cap + 63) & ~int64_t(63);
+  ws.qr = static_cast<float*>(take(sizeof(float) * size_t(rows) * kQsaHeads * kQsaD));
+  ws.info = static_cast<int2*>(take(sizeof(int2) * size_t(rows)));
+  ws.scores = static_cast<float*>(take(sizeof(float) * size_t(rows) * size_t(ws.ld_s)));
+  const size_t nc = ws.segmax > 1 ? size_t(rows) * ws.segmax * size_t(sh.topk) : 0;
+  ws.cand_key = static_cast<uint32_t*>(take(sizeof(uint32_t) * nc));
+  ws.cand_idx = static_cast<int32_t*>(take(sizeof(int32_t) * nc));
+  *bytes = off;
+  return ws;
+}
+
+hipError_t launch_qsa_compress(const QsaShape& sh, int n_seqs, int64_t T, const int32_t* cu, const void* k,
+                               int64_t ld_k, const float* norm_w, void* kbar, void* pending, hipStream_t s) {
+  const int64_t nbmax = std::min<int64_t>(T / 4, sh.cap);
+  const dim3 grid(unsigned(std::max<int64_t>(1, (nbmax + 63) / 64)), unsigned(n_seqs));
+  if (sh.bf16)
+    hipLaunchKernelGGL(k_qsa_compress<bf16>, grid, dim3(256), 0, s, sh, static_cast<const bf16*>(k), ld_k, cu, T,
+                       norm_w, static_cast<bf16*>(kbar), static_cast<bf16*>(pending));
+  else
+    hipLaunchKernelGGL(k_qsa_compress<float>, grid, dim3(256), 0, s, sh, static_cast<const float*>(k), ld_k, cu, T,
+                       norm_w, static_cast<float*>(kbar), static_cast<float*>(pending));
+  return hipGetLastError();
+}
+
+hipError_t launch_qsa_append(const QsaShape& sh, int B, const int32_t* n_tok, const void* k, int64_t ld_k,
+                             const float* norm_w, void* pending, void* kbar, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((B + 3) / 4));
+  if (sh.bf16)
+    hipLaunchKernelGGL(k_qsa_append<bf16>, grid, dim3(64), 0, s, sh, B, n_tok, static_cast<const bf16*>(k), ld_k,
+                       norm_w, static_cast<bf16*>(pending), static_cast<bf16*>(kbar));
+  else
+    hipLaunchKernelGGL(k_qsa_append<float>, grid, dim3(64), 0, s, sh, B, n_tok, static_cast<const float*>(k), ld_k,
+                       norm_w, static_cast<float*>(pending), static_cast<float*>(kbar));
+  return hipGetLastError();
+}
+
+hipError_t launch_qsa_rows(const QsaShape& sh, const QsaWs& ws, int64_t row0, int64_t rows, const int32_t* cu,
+                           int n_seqs, const int32_t* n_tok, const void* q, int64_t ld_q, const void* kbar,
+                           int32_t* sel, int32_t* n_sel, int32_t* tail, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const dim3 rgrid(static_cast<unsigned>(rows));
+  if (sh.bf16)
+    hipLaunchKernelGGL(k_qsa_qprep<bf16>, rgrid, dim3(64), 0, s, sh, static_cast<const bf16*>(q), ld_q, row0, cu,
+                       n_seqs, n_tok, ws.qr, ws.info);
+  else
+    hipLaunchKernelGGL(k_qsa_qprep<float>, rgrid, dim3(64), 0, s, sh, static_cast<const float*>(q), ld_q, row0, cu,
+                       n_seqs, n_tok, ws.qr, ws.info);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 sgrid(unsigned(rows), unsigned(std::max<int64_t>(1, (sh.cap + kScoreChunk - 1) / kScoreChunk)));
+  if (sh.cap > 0) {
+    if (sh.bf16)
+      hipLaunchKernelGGL(k_qsa_score<bf16>, sgrid, dim3(256), 0, s, sh, ws.qr, ws.info,
+                         static_cast<const bf16*>(kbar), ws.scores, ws.ld_s);
+    else
+      hipLaunchKernelGGL(k_qsa_score<float>, sgrid, dim3(256), 0, s, sh, ws.qr, ws.info,
+                         static_cast<const float*>(kbar), ws.scores, ws.ld_s);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int32_t* sel_r = sel + row0 * sh.topk;
+  hipLaunchKernelGGL(k_qsa_select, dim3(unsigned(rows), unsigned(ws.segmax)), dim3(kSelThreads), 0, s, sh, ws.info,
+                     ws.scores, ws.ld_s, ws.cand_key, ws.cand_idx, ws.segmax, sel_r, n_sel + row0, tail + row0);
+  e = hipGetLastError();
+  if (e != hipSuccess || ws.segmax <= 1) return e;
+  hipLaunchKernelGGL(k_qsa_merge, rgrid, dim3(kSelThreads), 0, s, sh, ws.info, ws.cand_key, ws.cand_idx, ws.segmax,
+                     sel_r, n_sel + row0, tail + row0);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -2,15 +2,17 @@
 declares, sizes workspaces, and rejects bad arguments before any HIP call (so these run on CPU).
 Every gdn_prefill / gdn_decode_step call here is invalid on purpose and must return early."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gdn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gdn.h", "qsa.h")]
 
 gdn = pytest.importorskip("linear_attention_token_amd.gdn")
+qsa = pytest.importorskip("linear_attention_token_amd.qsa")
 
 if not os.path.exists(gdn.LIB_PATH):
     pytest.skip("libgdn.so not built (run __graft_entry__.build())", allow_module_level=True)
@@ -21,14 +23,16 @@ T_, N_ = 128, 1
 
 
 def header_functions():
-    txt = open(HEADER).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", txt)))
+    funcs = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        txt = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        funcs |= set(re.findall(r"\b((?:gdn|qsa)_[a-z_0-9]+)\s*\(", txt))
+    return sorted(funcs)
 
 
 def test_exports_every_declared_function():
     funcs = header_functions()
-    assert set(funcs) == set(gdn.EXPORTS)
+    assert set(funcs) == set(gdn.EXPORTS) | set(qsa.EXPORTS)
     for f in funcs:
         assert hasattr(lib, f), f"libgdn.so does not export {f}"
 
@@ -228,3 +232,67 @@ def test_projections_reject_bad_arguments():
     _err(outp(o=None), 1)
     _err(outp(y=A + 8), 4)
     assert inp(T=0, x=None, qkv=None) == 0 and outp(T=0, o=None) == 0
+
+
+def test_qsa_defaults_and_workspace():
+    c = qsa.qsa_cfg_default()
+    assert (c.n_heads, c.d, c.block, c.topk, c.rope_dims, c.io_dtype) == (4, 128, 4, 512, 64, gdn.GDN_BF16)
+    assert abs(c.rope_base - 1e4) < 1e-3 and abs(c.norm_eps - 1e-6) < 1e-12
+    one = qsa.qsa_workspace(c, 1, 1 << 18)
+    many = qsa.qsa_workspace(c, 8, 1 << 18)
+    assert one >= (1 << 18) * 4 + 2048 and many >= 8 * (1 << 18) * 4
+    # 256K blocks = 16 select segments: each row also keeps 16 x 512 (key, block) candidates
+    assert many >= 8 * ((1 << 18) * 4 + 16 * 512 * 8)
+    assert qsa.qsa_workspace(c, 0, 0) >= 0
+
+
+def test_qsa_reject_bad_arguments():
+    c = qsa.qsa_cfg_default()
+    cu = (ctypes.c_int32 * 3)(0, 40, 100)
+    n = ctypes.c_size_t(0)
+    L = qsa._lib()
+    _err(L.qsa_workspace(ctypes.byref(qsa.qsa_cfg_default(n_heads=8)), 1, 16, ctypes.byref(n)), 6)
+    _err(L.qsa_workspace(ctypes.byref(qsa.qsa_cfg_default(topk=0)), 1, 16, ctypes.byref(n)), 6)
+    _err(L.qsa_workspace(ctypes.byref(qsa.qsa_cfg_default(rope_dims=40)), 1, 16, ctypes.byref(n)), 6)
+    _err(L.qsa_workspace(ctypes.byref(qsa.qsa_cfg_default(io_dtype=5)), 1, 16, ctypes.byref(n)), 3)
+    _err(L.qsa_workspace(ctypes.byref(qsa.qsa_cfg_default(norm_eps=-1.0)), 1, 16, ctypes.byref(n)), 8)
+    _err(L.qsa_workspace(ctypes.byref(c), 1, 16384 * 32 + 1, ctypes.byref(n)), 6)   # beyond 2M tokens at top-512
+    assert L.qsa_workspace(ctypes.byref(c), 1, 16384 * 32, ctypes.byref(n)) == 0
+
+    def comp(cfg=c, N=2, T=100, cud=A, cuh=cu, k=A, ld=128, w=A, kb=A, cap=64, pend=A):
+        return L.qsa_compress(ctypes.byref(cfg), N, T, cud, ctypes.cast(cuh, ctypes.c_void_p) if cuh else None,
+                              k, ld, w, kb, cap, pend, None)
+
+    _err(comp(cap=10), 2)            # sequence 1 has 15 blocks
+    _err(comp(cuh=(ctypes.c_int32 * 3)(0, 50, 40)), 2)
+    _err(comp(k=None), 1)
+    _err(comp(cud=None), 1)
+    _err(comp(ld=100), 2)
+    _err(comp(ld=132), 4)
+    _err(comp(kb=A + 8), 4)
+    _err(comp(N=70000), 6)
+    assert comp(N=0, T=0) == 0 and comp(T=0, cuh=(ctypes.c_int32 * 3)(0, 0, 0)) == 0
+
+    def sel(cfg=c, N=2, T=100, cud=A, q=A, ld=512, kb=A, cap=64, s=A, ns=A, tl=A, ws=A, wsb=1 << 30):
+        return L.qsa_select(ctypes.byref(cfg), N, T, cud, q, ld, kb, cap, s, ns, tl, ws, wsb, None)
+
+    _err(sel(q=None), 1)
+    _err(sel(cud=None), 1)
+    _err(sel(ld=256), 2)
+    _err(sel(ws=None), 5)
+    _err(sel(wsb=100), 5)
+    _err(sel(ws=A + 16), 4)
+    _err(sel(ns=A + 2), 4)
+    assert sel(T=0, q=None) == 0
+
+    def dec(cfg=c, B=2, nt=A, q=A, ldq=512, k=A, ldk=128, w=A, pend=A, kb=A, cap=64, s=A, ns=A, tl=A, ws=A,
+            wsb=1 << 30):
+        return L.qsa_decode(ctypes.byref(cfg), B, nt, q, ldq, k, ldk, w, pend, kb, cap, s, ns, tl, ws, wsb, None)
+
+    _err(dec(nt=None), 1)
+    _err(dec(pend=None), 1)
+    _err(dec(B=-1), 2)
+    _err(dec(ldk=64), 2)
+    _err(dec(wsb=64), 5)
+    _err(dec(cap=-1), 2)
+    assert dec(B=0, q=None, k=None) == 0

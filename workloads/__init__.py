@@ -11,6 +11,8 @@ from .gen import (  # noqa: F401
     decode_inputs,
     ProjectionInputs,
     projection_inputs,
+    IndexerInputs,
+    indexer_inputs,
     loguniform_lengths,
     config_tiny,
     config_layer,

@@ -228,6 +228,31 @@ def projection_inputs(T: int, *, hidden: int, n_qk_heads: int, n_v_heads: int, d
     return ProjectionInputs(x, w_qkv, w_z, w_ab, a_log, dt_bias, w_out)
 
 
+@dataclass
+class IndexerInputs:
+    """Inputs of the QSA compressed indexer (analysis notes §02 configuration table, QSA indexer row:
+    4 query heads and one shared key head of dim 128): q [T, 4, 128] and k [T, 128] in the io dtype,
+    the RMSNorm gain norm_w [128] fp32, and the packing cu_seqlens int32 [N+1]."""
+    cu_seqlens: torch.Tensor
+    q: torch.Tensor
+    k: torch.Tensor
+    norm_w: torch.Tensor
+
+
+def indexer_inputs(lengths: Sequence[int], *, io_dtype: torch.dtype = torch.bfloat16, seed: int = 0,
+                   device="cpu") -> IndexerInputs:
+    """q, k ~ N(0, 1) per element (the scale of a projection of the normalised residual stream);
+    norm_w ~ U(0.5, 1.5). Drawn in the order q, k, norm_w."""
+    T = int(sum(lengths))
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32, device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    q = _normal(g, (T, 4, 128), 1.0, device).to(io_dtype)
+    k = _normal(g, (T, 128), 1.0, device).to(io_dtype)
+    norm_w = torch.rand((128,), generator=g, device=device) + 0.5
+    return IndexerInputs(cu, q, k, norm_w)
+
+
 # --- the five workloads (tiny correctness case, one layer, long prefill, varlen, decode) -----
 
 MODEL_HEADS = dict(n_qk_heads=16, n_v_heads=48, d_k=128, d_v=128)
