@@ -355,7 +355,7 @@ def qsa_compress(k, w, eps=1e-6):
     k [T, 128] -> [floor(T/4), 128] fp64."""
     k = _f64(k)
     nb = k.shape[0] // QSA_BLOCK
-    m = k[:nb * QSA_BLOCK].reshape(nb, QSA_BLOCK, -1).mean(axis=1)
+    m = k[:nb * QSA_BLOCK].reshape(nb, QSA_BLOCK, k.shape[1]).mean(axis=1)
     m = m / np.sqrt(np.mean(m * m, axis=1, keepdims=True) + eps) * _f64(w)[None, :]
     return partial_rope(m, QSA_BLOCK * np.arange(nb))
 

@@ -57,6 +57,7 @@ def test_compress_brute_force():
     w = rng.uniform(0.5, 1.5, 128)
     kb = O.qsa_compress(k, w)
     assert kb.shape == (10, 128)
+    assert O.qsa_compress(k[:0], w).shape == (0, 128) and O.qsa_compress(k[:3], w).shape == (0, 128)
     for b in range(10):
         m = [sum(k[4 * b + j, d] for j in range(4)) / 4 for d in range(128)]
         r = math.sqrt(sum(x * x for x in m) / 128 + 1e-6)
