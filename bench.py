@@ -150,6 +150,90 @@ def cpu_baseline(max_tokens: int):
                        f"{dt:.1f} s")
 
 
+def indexer_leg(args, dev, stream):
+    """QSA compressed indexer: a decode step of B sequences at a long context (append the token's key,
+    score every complete block, keep the top 512) and a prefill of one sequence (compress, then
+    select for every token). Decode streams the compressed-key cache once per step, so it is priced
+    against HBM; the prefill's block scores are fp32 vector FMAs over a cache that stays in L2, so they
+    are priced against the fp32 vector peak."""
+    import torch
+    from linear_attention_token_amd import qsa
+    from workloads import indexer_inputs
+
+    cfg = qsa.cfg_for(torch.bfloat16)
+    B, N, S = args.qsa_batch, args.qsa_context, args.qsa_steps
+    cap = N // 4
+
+    def timed(fn, n):
+        for _ in range(min(args.warmup, n, 5)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    # decode: caches of N - 1 tokens per sequence, then the N-th token (it completes block N/4 - 1)
+    kbar = torch.empty((B, cap, 128), dtype=torch.bfloat16, device=dev)
+    pend = torch.empty((B, 3, 128), dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        x = indexer_inputs([N - 1], io_dtype=torch.bfloat16, seed=100 + b, device=dev, queries=False)
+        qsa.qsa_compress(cfg, x.cu_seqlens, x.k, x.norm_w, kbar[b:b + 1], pend[b:b + 1])
+        del x
+    xs = indexer_inputs([B], io_dtype=torch.bfloat16, seed=99, device=dev)
+    n_tok = torch.full((B,), N, dtype=torch.int32, device=dev)
+    ws = torch.empty(qsa.qsa_workspace(cfg, B, cap), dtype=torch.uint8, device=dev)
+    sel = torch.empty((B, cfg.topk), dtype=torch.int32, device=dev)
+    nsel = torch.empty((B,), dtype=torch.int32, device=dev)
+    tail = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def dec():
+        qsa.qsa_decode(cfg, n_tok, xs.q, xs.k, xs.norm_w, pend, kbar, sel, nsel, tail, workspace=ws)
+
+    us_dec = timed(dec, S)
+    nb = N // 4
+    dec_bytes = B * (nb * 128 * 2 + 4 * 128 * 2 + 4 * 128 * 2 + cfg.topk * 4)
+    gb = dec_bytes / (us_dec * 1e-6) / 1e9
+    del kbar, ws
+    torch.cuda.empty_cache()
+
+    # prefill: one sequence of T tokens
+    T = args.qsa_prefill
+    xp = indexer_inputs([T], io_dtype=torch.bfloat16, seed=7, device=dev)
+    capp = T // 4
+    kb = torch.empty((1, capp, 128), dtype=torch.bfloat16, device=dev)
+    wsp = torch.empty(qsa.qsa_workspace(cfg, T, capp), dtype=torch.uint8, device=dev)
+    ps, pn, pt = (torch.empty((T, cfg.topk), dtype=torch.int32, device=dev),
+                  torch.empty((T,), dtype=torch.int32, device=dev), torch.empty((T,), dtype=torch.int32, device=dev))
+
+    def pre():
+        qsa.qsa_compress(cfg, xp.cu_seqlens, xp.k, xp.norm_w, kb)
+        qsa.qsa_select(cfg, xp.cu_seqlens, xp.q, kb, ps, pn, pt, workspace=wsp)
+
+    us_pre = timed(pre, max(3, S // 10))
+    pairs = sum((i + 1) // 4 for i in range(T))  # (token, complete block) scores
+    flops = pairs * 4 * 128 * 2
+    tf = flops / (us_pre * 1e-6) / 1e12
+    del wsp
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"QSA indexer (4 query heads, 1 key head, d=128, blocks of 4, top-512, bf16 io): decode step of "
+                    f"B={B} sequences at {N} tokens (append + score {nb} blocks + select), prefill of one "
+                    f"{T}-token sequence (compress + select for every token)",
+        "us_decode_step": round(us_dec, 2),
+        "roofline_decode": dict(bound="hbm", achieved=round(gb, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                                frac=round(gb / HBM_PEAK_GBPS, 4), algorithmic_bytes=dec_bytes,
+                                note="whole qsa_decode call: compressed-key cache read once"),
+        "ms_prefill": round(us_pre / 1e3, 3), "prefill_tokens_per_s": round(T / (us_pre * 1e-6), 1),
+        "roofline_prefill": dict(bound="alu", achieved=round(tf, 2), peak=157.3, unit="TFLOP/s",
+                                 frac=round(tf / 157.3, 4), algorithmic_flops=flops,
+                                 note="whole compress + select: fp32 FMAs of the block scores"),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,7 +251,12 @@ def main():
                     help="skip the reference timing of one captured HIP graph replayed per step")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--hidden", type=int, default=2560, help="residual width of the layer leg")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "speculative", "layer", "copy"], default="all",
+    ap.add_argument("--qsa-context", type=int, default=1 << 20, help="tokens per sequence of the indexer decode")
+    ap.add_argument("--qsa-batch", type=int, default=8, help="sequences of the indexer decode")
+    ap.add_argument("--qsa-prefill", type=int, default=32768, help="tokens of the indexer prefill (one sequence)")
+    ap.add_argument("--qsa-steps", type=int, default=50)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "speculative", "layer", "indexer", "copy"],
+                    default="all",
                     help="run one part only (for profilers); 'copy' times a plain 1 GiB device copy, the "
                          "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
@@ -476,6 +565,9 @@ def main():
             "mean_accepted_tokens": acc, "us_per_accepted_token": round(us_s / acc, 2),
             "roofline_verify": roof(vb, us_v, "verify"), "roofline_commit": roof(cb, us_c, "commit"),
         }
+
+    if args.only in ("all", "indexer"):
+        result["indexer"] = indexer_leg(args, dev, stream)
 
     if not args.no_cpu_baseline and args.only == "all":
         result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)

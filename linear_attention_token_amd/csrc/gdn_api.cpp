@@ -122,7 +122,7 @@ static gdn_status check_qsa(const qsa_cfg* cfg, int64_t cap, QsaShape& sh) {
                 (long long)cap, (long long)cap_max, cfg->topk);
   sh.topk = cfg->topk;
   sh.half = cfg->rope_dims / 2;
-  sh.log2_base = log2(double(cfg->rope_base));
+  for (int i = 0; i < 64; ++i) sh.theta[i] = i < sh.half ? pow(double(cfg->rope_base), -double(i) / sh.half) : 0.0;
   sh.eps = cfg->norm_eps;
   sh.bf16 = cfg->io_dtype == GDN_BF16;
   sh.cap = cap;
@@ -620,8 +620,8 @@ gdn_status qsa_select(const qsa_cfg* cfg, int32_t n_seqs, int64_t total_tokens, 
   const QsaWs ws = plan_qsa_ws(sh, lo, workspace, &used);
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   for (int64_t r0 = 0; r0 < total_tokens; r0 += lo)
-    if (run(launch_qsa_rows(sh, ws, r0, std::min(lo, total_tokens - r0), cu_seqlens, n_seqs, nullptr, q, ld_q, kbar,
-                            sel, n_sel, tail, s), "qsa select") != hipSuccess)
+    if (run(launch_qsa_rows(sh, ws, r0, std::min(lo, total_tokens - r0), cu_seqlens, n_seqs, nullptr, QsaAppend{},
+                            q, ld_q, kbar, sel, n_sel, tail, s), "qsa select") != hipSuccess)
       return GDN_E_HIP;
   return GDN_OK;
 }
@@ -652,9 +652,9 @@ gdn_status qsa_decode(const qsa_cfg* cfg, int32_t batch, const int32_t* n_tok, c
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
   const QsaWs ws = plan_qsa_ws(sh, batch, workspace, &need);
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (run(launch_qsa_append(sh, batch, n_tok, k, ld_k, norm_w, pending, kbar, s), "qsa append") != hipSuccess ||
-      run(launch_qsa_rows(sh, ws, 0, batch, nullptr, batch, n_tok, q, ld_q, kbar, sel, n_sel, tail, s),
-          "qsa decode select") != hipSuccess)
+  const QsaAppend ap{k, ld_k, norm_w, pending, kbar};
+  if (run(launch_qsa_rows(sh, ws, 0, batch, nullptr, batch, n_tok, ap, q, ld_q, kbar, sel, n_sel, tail, s),
+          "qsa decode") != hipSuccess)
     return GDN_E_HIP;
   return GDN_OK;
 }

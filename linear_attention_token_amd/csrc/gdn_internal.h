@@ -141,7 +141,7 @@ constexpr int kSelSeg = 16384;  // scores per select workgroup (1024 threads x 1
 struct QsaShape {
   int topk;
   int half;          // rope_dims / 2
-  double log2_base;  // log2(rope_base)
+  double theta[64];  // rotation angle per position of pair i: rope_base^(-i / half)
   float eps;         // RMSNorm eps
   bool bf16;         // io dtype
   int64_t cap;       // compressed-key cache capacity per sequence, in blocks
@@ -157,13 +157,20 @@ struct QsaWs {
   int segmax;
 };
 
+// Decode append: each row's new key k [rows][ld_k], the RMSNorm gain, and the caches it updates.
+struct QsaAppend {
+  const void* k;
+  int64_t ld_k;
+  const float* norm_w;
+  void* pending;
+  void* kbar;
+};
+
 QsaWs plan_qsa_ws(const QsaShape& sh, int64_t rows, void* base, size_t* bytes);
 hipError_t launch_qsa_compress(const QsaShape& sh, int n_seqs, int64_t T, const int32_t* cu, const void* k,
                                int64_t ld_k, const float* norm_w, void* kbar, void* pending, hipStream_t s);
-hipError_t launch_qsa_append(const QsaShape& sh, int B, const int32_t* n_tok, const void* k, int64_t ld_k,
-                             const float* norm_w, void* pending, void* kbar, hipStream_t s);
 hipError_t launch_qsa_rows(const QsaShape& sh, const QsaWs& ws, int64_t row0, int64_t rows, const int32_t* cu,
-                           int n_seqs, const int32_t* n_tok, const void* q, int64_t ld_q, const void* kbar,
-                           int32_t* sel, int32_t* n_sel, int32_t* tail, hipStream_t s);
+                           int n_seqs, const int32_t* n_tok, const QsaAppend& ap, const void* q, int64_t ld_q,
+                           const void* kbar, int32_t* sel, int32_t* n_sel, int32_t* tail, hipStream_t s);
 
 }  // namespace gdn

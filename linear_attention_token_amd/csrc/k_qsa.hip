@@ -6,8 +6,8 @@
 //
 // Kernels:
 //   k_qsa_compress  one 16-lane group per block: pool, RMSNorm, partial RoPE, store (HBM-bound);
-//   k_qsa_append    decode: a token's key joins its sequence's pending block, or completes it;
-//   k_qsa_qprep     one row per query: find its sequence and position, rotate its 4 heads (fp32);
+//   k_qsa_qprep     one row per query: find its sequence and position, rotate its 4 heads (fp32); in
+//                   decode, also the new key joins its sequence's pending block, or completes it;
 //   k_qsa_score     a row's compressed keys streamed by 16-lane groups, 16 B per lane (HBM-bound
 //                   in decode, where the cache is read once per step);
 //   k_qsa_select    one 1024-thread block per 16384 scores: exact top-k by a 3-digit radix select
@@ -52,7 +52,7 @@ __device__ __forceinline__ RopeLane rope_lane(int m, const QsaShape& sh) {
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    r.theta[i] = r.kind ? exp2(-double(first + i) / double(sh.half) * sh.log2_base) : 0.0;
+    r.theta[i] = r.kind ? sh.theta[first + i] : 0.0;
   return r;
 }
 
@@ -140,20 +140,17 @@ __global__ void __launch_bounds__(256) k_qsa_compress(QsaShape sh, const IO* __r
   }
 }
 
-// ---- decode: the new key of sequence b joins slot (n-1) % 4 of its block; slot 3 completes it ----
+// ---- decode: the new key of sequence b joins slot (n-1) % 4 of its block; slot 3 completes it.
+// Run by one 16-lane group.
 template <typename IO>
-__global__ void __launch_bounds__(64) k_qsa_append(QsaShape sh, int B, const int32_t* __restrict__ n_tok,
-                                                   const IO* __restrict__ k, int64_t ld_k,
-                                                   const float* __restrict__ norm_w, IO* __restrict__ pending,
-                                                   IO* __restrict__ kbar) {
-  const int t = threadIdx.x, lane = t, m = t & 15;
-  const int b = blockIdx.x * 4 + (t >> 4);
-  if (b >= B) return;
-  const int n = n_tok[b];
+__device__ __forceinline__ void append_key(const QsaShape& sh, int b, int n, const QsaAppend& ap, int lane) {
+  const int m = lane & 15;
   if (n < 1) return;
   const int j = (n - 1) & 3;
+  const IO* k = static_cast<const IO*>(ap.k);
+  IO* pending = static_cast<IO*>(ap.pending);
   float x[8];
-  ld8(k + int64_t(b) * ld_k + 8 * m, x);
+  ld8(k + int64_t(b) * ap.ld_k + 8 * m, x);
   if (j < 3) {
     st8(pending + (int64_t(b) * 3 + j) * kQsaD + 8 * m, x);
     return;
@@ -162,7 +159,7 @@ __global__ void __launch_bounds__(64) k_qsa_append(QsaShape sh, int B, const int
   if (blk >= sh.cap) return;
   float w[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = norm_w[8 * m + i];
+  for (int i = 0; i < 8; ++i) w[i] = ap.norm_w[8 * m + i];
   float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < 3; ++jj) {  // token order, as in the prefill compression
@@ -174,18 +171,21 @@ __global__ void __launch_bounds__(64) k_qsa_append(QsaShape sh, int B, const int
 #pragma unroll
   for (int e = 0; e < 8; ++e) y[e] += x[e];
   const RopeLane rl = rope_lane(m, sh);
-  finish_block(y, w, rl, 4 * blk, sh.eps, lane, kbar + (int64_t(b) * sh.cap + blk) * kQsaD + 8 * m);
+  finish_block(y, w, rl, 4 * blk, sh.eps, lane, static_cast<IO*>(ap.kbar) + (int64_t(b) * sh.cap + blk) * kQsaD + 8 * m);
 }
 
 // ---- per-row preparation: (sequence, position) and the rotated fp32 queries -------------------
 // Prefill rows are tokens row0 + r of the packed batch (cu given); decode rows are sequences with
 // position n_tok[r] - 1.
+// Decode rows (cu == nullptr) also append their sequence's new key (group 0), before any score
+// kernel reads the cache.
 template <typename IO>
 __global__ void __launch_bounds__(64) k_qsa_qprep(QsaShape sh, const IO* __restrict__ q, int64_t ld_q,
                                                   int64_t row0, const int32_t* __restrict__ cu, int n_seqs,
-                                                  const int32_t* __restrict__ n_tok, float* __restrict__ qr,
-                                                  int2* __restrict__ info) {
+                                                  const int32_t* __restrict__ n_tok, QsaAppend ap,
+                                                  float* __restrict__ qr, int2* __restrict__ info) {
   const int t = threadIdx.x, h = t >> 4, m = t & 15;
+  if (!cu && ap.k && h == 0) append_key<IO>(sh, int(blockIdx.x), n_tok[blockIdx.x], ap, t);
   const int64_t r = blockIdx.x, row = row0 + r;
   int seq, pos;
   if (cu) {
@@ -253,6 +253,7 @@ __global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __r
     qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
     qv[h][4] = c.x; qv[h][5] = c.y; qv[h][6] = c.z; qv[h][7] = c.w;
   }
+  // the cache is streamed once per call: non-temporal loads keep it from evicting the scores
   const IO* base = kbar + int64_t(in.x) * sh.cap * kQsaD + 8 * m;
   float* out = scores + r * ld_s;
   for (int64_t s = b0 + g; s < end; s += 16 * kScoreUnroll) {
@@ -261,7 +262,7 @@ __global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __r
     for (int u = 0; u < kScoreUnroll; ++u) {
       const int64_t b = min(s + 16 * u, end - 1);  // clamped blocks are loaded, not stored
 #pragma unroll
-      for (int v = 0; v < V; ++v) raw[u][v] = *reinterpret_cast<const uint4*>(base + b * kQsaD + v * N);
+      for (int v = 0; v < V; ++v) raw[u][v] = ldnt16(base + b * kQsaD + v * N);
     }
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
@@ -287,74 +288,145 @@ __global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __r
 // the order of the scores. The k-th largest key is found digit by digit (bits 30..20, 19..9, 8..0),
 // each digit from a 2048-bin LDS histogram of the keys that match the digits found so far; then the
 // keys above it and the first `need_eq` keys equal to it, in index order, are selected.
+constexpr int kHistPad = 2048 + 2048 / 32;  // bin b at b + b / 32: the digit wave reads runs 33 words apart
+constexpr int kGather = 256;                 // bucket sizes resolved by ranking instead of more digits
+
+__device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
+
 struct SelLds {
-  uint32_t hist[2048];
+  uint32_t hist[3][kHistPad];    // one histogram per digit, all cleared up front
   uint32_t table[kSelPer * 16];  // per (slot, wave): selected-above count << 16 | equal count
-  uint32_t wtot[16];
-  uint32_t digit, above;
+  uint32_t gkey[kGather];        // keys of the threshold bucket, when it is small
+  uint32_t wmin[16], wmax[16], wpos[16];
+  uint32_t digit, above, total, ngather;
 };
 
-// Inclusive scan of one value per thread over the 1024 threads; *total gets the sum.
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, SelLds& L, uint32_t* total) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+// Wave 0 finds the bin holding the need-th largest key: lane l holds its run of nbins/64 bins (from
+// the top bin down) in registers, a wave scan gives the count above each run, and the lane whose
+// run crosses `need` walks its registers.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint32_t need, SelLds& L) {
+  const int lane = threadIdx.x & 63, c = nbins >= 64 ? nbins / 64 : 1, top = nbins - 1 - lane * c;
+  uint32_t h[32], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    h[i] = (i < c && top - i >= 0) ? hist[hpad(top - i)] : 0u;
+    sum += h[i];
+  }
+  uint32_t incl = sum;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
+    const uint32_t n = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += n;
   }
-  if (lane == 63) L.wtot[w] = v;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
+  uint32_t run = incl - sum;
+  if (run < need && need <= incl) {
+    bool done = false;
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const uint32_t x = L.wtot[u];
-    off += u < w ? x : 0u;
-    tot += x;
+    for (int i = 0; i < 32; ++i) {
+      if (!done && run + h[i] >= need) {
+        L.digit = uint32_t(top - i);
+        L.above = run;
+        done = true;
+      }
+      run += h[i];
+    }
   }
-  *total = tot;
-  __syncthreads();
-  return v + off;
 }
 
-// Threshold key T and how many keys equal to T to take, for `need` <= number of valid keys.
-__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], uint32_t valid, uint32_t need,
+// Threshold key T and how many keys equal to T to take (in index order), given more than k valid
+// keys. Zero keys (scores clipped to zero) are the smallest: when at most k keys are positive, all
+// of those and the first k - n_pos zeros are taken. Otherwise the positive keys are bucketed over
+// their own range [lo, lo + 2^bw), 11 bits per pass (bucketing by the top bits of the raw float
+// pattern would put most keys of a wave into a few exponent bins and serialise the LDS atomics).
+// After a pass, a bucket of at most kGather keys is resolved at once: its keys are gathered and
+// wave 0 ranks them.
+__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], uint32_t valid, uint32_t k,
                                                 SelLds& L, uint32_t* T_out, uint32_t* need_eq) {
-  const int t = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
-  const int shifts[3] = {20, 9, 0}, bits[3] = {11, 11, 9};
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  uint32_t mn = 0xffffffffu, mx = 0, np = 0;
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass], nbins = 1 << bits[pass];
-    L.hist[t] = 0;
-    L.hist[t + kSelThreads] = 0;
-    __syncthreads();
+  for (int j = 0; j < kSelPer; ++j) {
+    const bool pos = ((valid >> j) & 1u) && key[j] > 0;
+    mn = pos ? min(mn, key[j]) : mn;
+    mx = pos ? max(mx, key[j]) : mx;
+    np += pos;
+  }
 #pragma unroll
-    for (int j = 0; j < kSelPer; ++j)
-      if (((valid >> j) & 1u) && (key[j] & pmask) == prefix)
-        atomicAdd(&L.hist[(key[j] >> shift) & uint32_t(nbins - 1)], 1u);
-    __syncthreads();
-    // thread t: bins nbins-1-2t and nbins-2-2t, so the scan runs from the top bin down
-    const bool mine = 2 * t < nbins;
-    const uint32_t hh = mine ? L.hist[nbins - 1 - 2 * t] : 0u, hl = mine ? L.hist[nbins - 2 - 2 * t] : 0u;
-    uint32_t tot;
-    const uint32_t incl = block_scan(hh + hl, L, &tot);
-    const uint32_t excl = incl - hh - hl;
-    if (mine && excl < need && need <= incl) {
-      if (excl + hh >= need) {
-        L.digit = uint32_t(nbins - 1 - 2 * t);
-        L.above = excl;
-      } else {
-        L.digit = uint32_t(nbins - 2 - 2 * t);
-        L.above = excl + hh;
-      }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, uint32_t(__shfl_xor(mn, o, kWave)));
+    mx = max(mx, uint32_t(__shfl_xor(mx, o, kWave)));
+    np += uint32_t(__shfl_xor(np, o, kWave));
+  }
+  if (lane == 0) {
+    L.wmin[w] = mn;
+    L.wmax[w] = mx;
+    L.wpos[w] = np;
+  }
+  for (int i = t; i < 3 * kHistPad; i += kSelThreads) (&L.hist[0][0])[i] = 0;
+  if (t == 0) L.ngather = 0;
+  __syncthreads();
+  mn = 0xffffffffu, mx = 0, np = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    mn = min(mn, L.wmin[u]);
+    mx = max(mx, L.wmax[u]);
+    np += L.wpos[u];
+  }
+  if (np <= k) {
+    *T_out = 0;
+    *need_eq = k - np;
+    return;
+  }
+  uint32_t lo = mn, need = k;
+  int bw = 32 - __clz(mx - mn);  // bits of the range: keys in [lo, lo + 2^bw)
+  for (int pass = 0; pass < 3 && bw > 0; ++pass) {
+    const int sh = max(bw - 11, 0), nbins = 1 << (bw - sh);
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      const uint32_t d = key[j] - lo;
+      if (((valid >> j) & 1u) && key[j] >= lo && (uint64_t(d) >> bw) == 0)
+        atomicAdd(&L.hist[pass][hpad(int(d >> sh))], 1u);
     }
     __syncthreads();
-    need -= L.above;
-    prefix |= L.digit << shift;
-    pmask |= uint32_t(nbins - 1) << shift;
+    if (t < kWave) find_digit(L.hist[pass], nbins, need, L);
     __syncthreads();
+    const uint32_t dg = L.digit;
+    const uint32_t cnt = L.hist[pass][hpad(int(dg))];
+    need -= L.above;
+    lo += dg << sh;
+    bw = sh;
+    if (bw > 0 && cnt <= kGather) {
+      // the bucket [lo, lo + 2^bw) is small: gather its keys and rank them
+#pragma unroll
+      for (int j = 0; j < kSelPer; ++j) {
+        const uint32_t d = key[j] - lo;
+        if (((valid >> j) & 1u) && key[j] >= lo && (uint64_t(d) >> bw) == 0)
+          L.gkey[atomicAdd(&L.ngather, 1u)] = key[j];
+      }
+      __syncthreads();
+      if (t < kWave) {
+        const uint32_t n = L.ngather;
+        for (uint32_t c = lane; c < n; c += kWave) {
+          const uint32_t x = L.gkey[c];
+          uint32_t gt = 0, eq = 0;
+          for (uint32_t o = 0; o < n; ++o) {
+            const uint32_t y = L.gkey[o];
+            gt += y > x;
+            eq += y == x;
+          }
+          if (gt < need && need <= gt + eq) {  // every lane that lands here holds the same key
+            L.digit = x;
+            L.above = gt;
+          }
+        }
+      }
+      __syncthreads();
+      *T_out = L.digit;
+      *need_eq = need - L.above;
+      return;
+    }
   }
-  *T_out = prefix;
+  *T_out = lo;
   *need_eq = need;
 }
 
@@ -380,11 +452,29 @@ __device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], 
     if (lane == 0) L.table[j * 16 + w] = (uint32_t(__popcll(bg)) << 16) | uint32_t(__popcll(be));
   }
   __syncthreads();
-  const uint32_t tv = t < kSelPer * 16 ? L.table[t] : 0u;
-  uint32_t tot;
-  const uint32_t incl = block_scan(tv, L, &tot);
-  if (t < kSelPer * 16) L.table[t] = incl - tv;
+  if (t < kWave) {  // exclusive scan of the 256 (slot, wave) counts, 4 per lane, in index order
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = L.table[4 * lane + e];
+      sum += c[e];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t n = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += n;
+    }
+    uint32_t run = incl - sum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      L.table[4 * lane + e] = run;
+      run += c[e];
+    }
+    if (lane == 63) L.total = incl;
+  }
   __syncthreads();
+  const uint32_t tot = L.total;
 #pragma unroll
   for (int j = 0; j < kSelPer; ++j) {
     const bool v = (valid >> j) & 1u;
@@ -514,29 +604,17 @@ hipError_t launch_qsa_compress(const QsaShape& sh, int n_seqs, int64_t T, const 
   return hipGetLastError();
 }
 
-hipError_t launch_qsa_append(const QsaShape& sh, int B, const int32_t* n_tok, const void* k, int64_t ld_k,
-                             const float* norm_w, void* pending, void* kbar, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((B + 3) / 4));
-  if (sh.bf16)
-    hipLaunchKernelGGL(k_qsa_append<bf16>, grid, dim3(64), 0, s, sh, B, n_tok, static_cast<const bf16*>(k), ld_k,
-                       norm_w, static_cast<bf16*>(pending), static_cast<bf16*>(kbar));
-  else
-    hipLaunchKernelGGL(k_qsa_append<float>, grid, dim3(64), 0, s, sh, B, n_tok, static_cast<const float*>(k), ld_k,
-                       norm_w, static_cast<float*>(pending), static_cast<float*>(kbar));
-  return hipGetLastError();
-}
-
 hipError_t launch_qsa_rows(const QsaShape& sh, const QsaWs& ws, int64_t row0, int64_t rows, const int32_t* cu,
-                           int n_seqs, const int32_t* n_tok, const void* q, int64_t ld_q, const void* kbar,
-                           int32_t* sel, int32_t* n_sel, int32_t* tail, hipStream_t s) {
+                           int n_seqs, const int32_t* n_tok, const QsaAppend& ap, const void* q, int64_t ld_q,
+                           const void* kbar, int32_t* sel, int32_t* n_sel, int32_t* tail, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const dim3 rgrid(static_cast<unsigned>(rows));
   if (sh.bf16)
     hipLaunchKernelGGL(k_qsa_qprep<bf16>, rgrid, dim3(64), 0, s, sh, static_cast<const bf16*>(q), ld_q, row0, cu,
-                       n_seqs, n_tok, ws.qr, ws.info);
+                       n_seqs, n_tok, ap, ws.qr, ws.info);
   else
     hipLaunchKernelGGL(k_qsa_qprep<float>, rgrid, dim3(64), 0, s, sh, static_cast<const float*>(q), ld_q, row0, cu,
-                       n_seqs, n_tok, ws.qr, ws.info);
+                       n_seqs, n_tok, ap, ws.qr, ws.info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 sgrid(unsigned(rows), unsigned(std::max<int64_t>(1, (sh.cap + kScoreChunk - 1) / kScoreChunk)));

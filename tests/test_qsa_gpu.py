@@ -223,3 +223,67 @@ def test_decode_one_million_tokens(dtype):
         qrow = _np(x.q[int(last[b])].unsqueeze(0))
         _check_rows(dtype, qrow, np.array([L - 1]), kb, sel[b:b + 1], n_sel[b:b + 1], tail[b:b + 1], cfg.topk)
     assert n_sel.tolist() == [512, 512]
+
+
+def test_prefill_select_long_rows_merge():
+    """One 66000-token sequence: tokens past 65536 see more than 16384 blocks (two select segments and
+    the merge). Sampled rows, including the last ones, against the oracle."""
+    dtype = torch.bfloat16
+    T = 66000
+    x = indexer_inputs([T], io_dtype=dtype, seed=16, device=DEV)
+    cfg = qsa.cfg_for(dtype)
+    kbar, _ = _compress(cfg, x, T // 4, pending=False)
+    sel, n_sel, tail = qsa.qsa_select(cfg, x.cu_seqlens, x.q, kbar)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(T - 6, T), np.random.default_rng(0).integers(0, T, 10), [3, 2050, 65539]])
+    kb = O.qsa_compress(_np(x.k), _np(x.norm_w))
+    r_t = torch.as_tensor(rows, device=DEV)
+    _check_rows(dtype, _np(x.q[r_t]), rows, kb, sel[r_t].cpu().numpy(), n_sel[r_t].cpu().numpy(),
+                tail[r_t].cpu().numpy(), cfg.topk)
+
+
+@pytest.mark.parametrize("case", ["zero_scores", "equal_scores", "two_levels"])
+def test_select_ties_exact(case):
+    """Scores with exact ties, where the selection is fully determined: ties go to the lower block.
+    zero_scores: q = 0, so every score is ReLU(0) = 0 -> blocks 0..k-1. equal_scores: no rotation
+    (rope_dims 0) and one repeated key, q along it -> one positive score everywhere -> blocks 0..k-1.
+    two_levels: even blocks hold key a, odd blocks key b, with q.a > q.b > 0 -> the first k even
+    blocks. Checked for a prefill (one segment) and a decode row of 17500 blocks (two segments and
+    the merge)."""
+    dtype = torch.bfloat16
+    k_top = 512
+    cfg = qsa.cfg_for(dtype, topk=k_top, rope_dims=0 if case != "zero_scores" else 64)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    a = torch.randn(128, generator=g, device=DEV)
+    b = torch.randn(128, generator=g, device=DEV)
+    b = b - (b @ a) / (a @ a) * a  # orthogonal to a
+    for T in (4 * 1500, 70000):
+        nblk = T // 4
+        if case == "two_levels":
+            blk = torch.where(torch.arange(nblk, device=DEV) % 2 == 0, 0, 1)
+            keys = torch.stack([a, a + 0.5 * b])[blk]           # q.a > q.(a + b/2) > 0 for q = a + small
+            k = keys.repeat_interleave(4, 0)
+        else:
+            k = a.expand(T, 128)
+        k = k.to(dtype).contiguous()
+        if case == "zero_scores":
+            q = torch.zeros(1, 4, 128, dtype=dtype, device=DEV)
+        else:
+            q = (a - 0.1 * b).to(dtype).expand(1, 4, 128).contiguous()
+        want = np.arange(k_top) if case != "two_levels" else 2 * np.arange(k_top)
+        # decode row: the cache holds T - 1 keys, the T-th completes the last block
+        kbar = torch.zeros((1, nblk, 128), dtype=dtype, device=DEV)
+        pend = torch.zeros((1, 3, 128), dtype=dtype, device=DEV)
+        cu = torch.tensor([0, T - 1], dtype=torch.int32, device=DEV)
+        qsa.qsa_compress(cfg, cu, k[:T - 1].contiguous(), torch.ones(128, device=DEV), kbar, pend)
+        sel, n_sel, _ = qsa.qsa_decode(cfg, torch.tensor([T], dtype=torch.int32, device=DEV), q,
+                                       k[T - 1:].contiguous(), torch.ones(128, device=DEV), pend, kbar)
+        torch.cuda.synchronize()
+        assert int(n_sel[0]) == k_top
+        assert np.array_equal(sel[0].cpu().numpy(), want), (case, T)
+        if T <= 6000:  # prefill: the last token's row sees the same blocks
+            cu2 = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+            sel2, _, _ = qsa.qsa_select(cfg, cu2, q.expand(T, 4, 128).contiguous(), kbar)
+            torch.cuda.synchronize()
+            assert np.array_equal(sel2[T - 1].cpu().numpy(), want), (case, "prefill")

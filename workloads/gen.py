@@ -240,14 +240,15 @@ class IndexerInputs:
 
 
 def indexer_inputs(lengths: Sequence[int], *, io_dtype: torch.dtype = torch.bfloat16, seed: int = 0,
-                   device="cpu") -> IndexerInputs:
+                   device="cpu", queries: bool = True) -> IndexerInputs:
     """q, k ~ N(0, 1) per element (the scale of a projection of the normalised residual stream);
-    norm_w ~ U(0.5, 1.5). Drawn in the order q, k, norm_w."""
+    norm_w ~ U(0.5, 1.5). Drawn in the order q, k, norm_w; with queries=False (a key cache only)
+    q is None and the draws start at k."""
     T = int(sum(lengths))
     cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32, device=device)
     g = torch.Generator(device=device)
     g.manual_seed(seed)
-    q = _normal(g, (T, 4, 128), 1.0, device).to(io_dtype)
+    q = _normal(g, (T, 4, 128), 1.0, device).to(io_dtype) if queries else None
     k = _normal(g, (T, 128), 1.0, device).to(io_dtype)
     norm_w = torch.rand((128,), generator=g, device=device) + 0.5
     return IndexerInputs(cu, q, k, norm_w)
