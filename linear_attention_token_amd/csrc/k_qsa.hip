@@ -10,8 +10,10 @@
 //                   decode, also the new key joins its sequence's pending block, or completes it;
 //   k_qsa_score     a row's compressed keys streamed by 16-lane groups, 16 B per lane (HBM-bound
 //                   in decode, where the cache is read once per step);
-//   k_qsa_select    one 1024-thread block per 16384 scores: exact top-k by a 3-digit radix select
-//                   on the score bits held in registers, then an ordered compaction;
+//   k_qsa_score_mfma  bf16 prefill: 16 query rows x 16 compressed keys per bf16 MFMA step;
+//   k_qsa_select    one block per row and segment of 16 scores per thread (1024 threads: 16384
+//                   scores; 256 or 512 threads for short rows): exact top-k by a radix select on
+//                   the score bits held in registers, then an ordered compaction;
 //   k_qsa_merge     rows longer than one segment: the same select over the segments' candidates
 //                   (every global top-k block is in its own segment's top-k).
 //
@@ -29,8 +31,8 @@ constexpr int kQsaD = 128;       // head dim of indexer queries and keys
 constexpr int kQsaHeads = 4;     // query heads
 constexpr int kScoreChunk = 1024;  // blocks per workgroup of the score kernel
 constexpr int kScoreUnroll = 8;    // blocks per 16-lane group in flight
-constexpr int kSelThreads = 1024;
-constexpr int kSelPer = 16;        // scores per thread
+constexpr int kMfmaChunk = 1024;   // blocks per workgroup of the MFMA score kernel
+constexpr int kSelPer = 16;        // scores per thread of the select
 
 // ---- rotation -------------------------------------------------------------------------------
 struct RopeLane {
@@ -283,6 +285,88 @@ __global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __r
   }
 }
 
+// ---- prefill scores on bf16 MFMA: one wave per 16 query rows, 16 compressed keys per step -------
+// D_h = Q_h K^T for each head (16x16x32 MFMA, fp32 accumulate), then sum_h ReLU(D_h). The rotated
+// queries are rounded to bf16 for the A operands; the keys are the stored bf16 cache. A wave's rows
+// can span sequences (packed batches): it runs once per sequence it touches, storing only its rows.
+__global__ void __launch_bounds__(256) k_qsa_score_mfma(QsaShape sh, const float* __restrict__ qr,
+                                                        const int2* __restrict__ info, int64_t rows,
+                                                        const uint16_t* __restrict__ kbar,
+                                                        float* __restrict__ scores, int64_t ld_s) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
+  const int64_t r0 = (int64_t(blockIdx.x) * 4 + w) * 16;
+  if (r0 >= rows) return;
+  const int64_t rn = min(r0 + 16, rows);
+  // output rows of this lane: r0 + 4 lq + r
+  int oseq[4];
+  int64_t onb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t row = r0 + 4 * lq + r;
+    const int2 in = info[min(row, rn - 1)];
+    oseq[r] = row < rn ? in.x : -1;
+    onb[r] = row_blocks(in.y, sh.cap);
+  }
+  const int s_first = info[r0].x, s_last = info[rn - 1].x;
+  const int c0 = blockIdx.y * kMfmaChunk;
+  {  // most of the causal triangle's (rows, chunk) pairs are empty: leave before loading queries
+    int most = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) most = oseq[r] >= 0 ? max(most, int(onb[r])) : most;
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) most = max(most, __shfl_xor(most, o, kWave));
+    if (c0 >= most) return;
+  }
+  // A operand of head h, k-step ks: row r0 + li, dims 32 ks + 8 lq .. + 7
+  const int64_t ra = min(r0 + li, rn - 1);
+  short8 a[kQsaHeads][4];
+#pragma unroll
+  for (int h = 0; h < kQsaHeads; ++h)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float* p = qr + ra * (kQsaHeads * kQsaD) + h * kQsaD + 32 * ks + 8 * lq;
+      const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
+      a[h][ks] = pack8(f32x4{x0.x, x0.y, x0.z, x0.w}, f32x4{x1.x, x1.y, x1.z, x1.w});
+    }
+
+  for (int sq = s_first; sq <= s_last; ++sq) {
+    int nbmax = 0;  // blocks of the wave's rows in this sequence (<= cap < 2^20)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) nbmax = oseq[r] == sq ? max(nbmax, int(onb[r])) : nbmax;
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) nbmax = max(nbmax, __shfl_xor(nbmax, o, kWave));
+    const int cend = min(nbmax, c0 + kMfmaChunk);  // this workgroup's slice of the blocks
+    if (c0 >= cend) continue;
+    const uint16_t* kb = kbar + int64_t(sq) * sh.cap * kQsaD + 8 * lq;
+    short8 bv[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bv[ks] = ld_short8(kb + int64_t(min(c0 + li, cend - 1)) * kQsaD + 32 * ks);
+    for (int64_t b0 = c0; b0 < cend; b0 += 16) {
+      short8 nx[4];
+      const int64_t bn = min(b0 + 16 + li, int64_t(cend - 1));  // next step's keys (clamped: loaded, unused)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) nx[ks] = ld_short8(kb + bn * kQsaD + 32 * ks);
+      f32x4 acc[kQsaHeads];
+#pragma unroll
+      for (int h = 0; h < kQsaHeads; ++h) {
+        acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc[h] = mfma16x16x32(a[h][ks], bv[ks], acc[h]);
+      }
+      const int64_t b = b0 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = 0.f;
+#pragma unroll
+        for (int h = 0; h < kQsaHeads; ++h) v += fmaxf(acc[h][r], 0.f);
+        if (oseq[r] == sq && b < onb[r]) scores[(r0 + 4 * lq + r) * ld_s + b] = v;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bv[ks] = nx[ks];
+    }
+  }
+}
+
 // ---- exact top-k of up to 16384 keys held 16 per thread by 1024 threads ------------------------
 // Keys are score bits with the sign cleared: scores are >= 0, so the unsigned order of the bits is
 // the order of the scores. The k-th largest key is found digit by digit (bits 30..20, 19..9, 8..0),
@@ -293,43 +377,44 @@ constexpr int kGather = 256;                 // bucket sizes resolved by ranking
 
 __device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
 
+template <int NT>
 struct SelLds {
+  static constexpr int NW = NT / 64;
   uint32_t hist[3][kHistPad];    // one histogram per digit, all cleared up front
-  uint32_t table[kSelPer * 16];  // per (slot, wave): selected-above count << 16 | equal count
+  uint32_t table[kSelPer * NW];  // per (slot, wave): selected-above count << 16 | equal count
   uint32_t gkey[kGather];        // keys of the threshold bucket, when it is small
-  uint32_t wmin[16], wmax[16], wpos[16];
+  uint32_t wmin[NW], wmax[NW], wpos[NW];
   uint32_t digit, above, total, ngather;
 };
 
-// Wave 0 finds the bin holding the need-th largest key: lane l holds its run of nbins/64 bins (from
-// the top bin down) in registers, a wave scan gives the count above each run, and the lane whose
-// run crosses `need` walks its registers.
-__device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint32_t need, SelLds& L) {
-  const int lane = threadIdx.x & 63, c = nbins >= 64 ? nbins / 64 : 1, top = nbins - 1 - lane * c;
-  uint32_t h[32], sum = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    h[i] = (i < c && top - i >= 0) ? hist[hpad(top - i)] : 0u;
-    sum += h[i];
-  }
-  uint32_t incl = sum;
+// Wave 0 finds the bin holding the need-th largest key in two wave scans: lane l first sums its run
+// of c = nbins/64 bins (from the top bin down); the lane whose run crosses `need` is found, then the
+// lanes take one bin each of that run (c <= 32) and a second scan finds the bin.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t n = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += n;
+    const uint32_t n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
   }
-  uint32_t run = incl - sum;
-  if (run < need && need <= incl) {
-    bool done = false;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (!done && run + h[i] >= need) {
-        L.digit = uint32_t(top - i);
-        L.above = run;
-        done = true;
-      }
-      run += h[i];
-    }
+  return v;
+}
+
+template <typename LDS>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint32_t need, LDS& L) {
+  const int lane = threadIdx.x & 63, c = nbins >= 64 ? nbins / 64 : 1, top = nbins - 1 - lane * c;
+  uint32_t sum = 0;
+  for (int i = 0; i < c; ++i) sum += top - i >= 0 ? hist[hpad(top - i)] : 0u;
+  const uint32_t incl = wave_incl_scan(sum, lane);
+  const bool cross = incl - sum < need && need <= incl;
+  const uint64_t who = __ballot(cross);
+  const int src = int(__ffsll(static_cast<unsigned long long>(who))) - 1;  // exactly one lane crosses
+  const uint32_t above_run = __shfl(incl - sum, src, kWave);
+  const int top_run = nbins - 1 - src * c;
+  const uint32_t h = (lane < c && top_run - lane >= 0) ? hist[hpad(top_run - lane)] : 0u;
+  const uint32_t in2 = wave_incl_scan(h, lane) + above_run;
+  if (lane < c && in2 - h < need && need <= in2) {
+    L.digit = uint32_t(top_run - lane);
+    L.above = in2 - h;
   }
 }
 
@@ -340,8 +425,10 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint
 // pattern would put most keys of a wave into a few exponent bins and serialise the LDS atomics).
 // After a pass, a bucket of at most kGather keys is resolved at once: its keys are gathered and
 // wave 0 ranks them.
+template <int NT>
 __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], uint32_t valid, uint32_t k,
-                                                SelLds& L, uint32_t* T_out, uint32_t* need_eq) {
+                                                SelLds<NT>& L, uint32_t* T_out, uint32_t* need_eq) {
+  constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint32_t mn = 0xffffffffu, mx = 0, np = 0;
 #pragma unroll
@@ -362,12 +449,12 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
     L.wmax[w] = mx;
     L.wpos[w] = np;
   }
-  for (int i = t; i < 3 * kHistPad; i += kSelThreads) (&L.hist[0][0])[i] = 0;
+  for (int i = t; i < 3 * kHistPad; i += NT) (&L.hist[0][0])[i] = 0;
   if (t == 0) L.ngather = 0;
   __syncthreads();
   mn = 0xffffffffu, mx = 0, np = 0;
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
+  for (int u = 0; u < NW; ++u) {
     mn = min(mn, L.wmin[u]);
     mx = max(mx, L.wmax[u]);
     np += L.wpos[u];
@@ -409,6 +496,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
         for (uint32_t c = lane; c < n; c += kWave) {
           const uint32_t x = L.gkey[c];
           uint32_t gt = 0, eq = 0;
+#pragma unroll 8
           for (uint32_t o = 0; o < n; ++o) {
             const uint32_t y = L.gkey[o];
             gt += y > x;
@@ -433,30 +521,28 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
 // Selects (all valid keys when n_valid <= k, else the top k) and calls emit(j, out_pos) for each
 // selected key j of this thread, out_pos counting in index order (index = j * 1024 + thread).
 // Returns the number selected.
-template <typename F>
+template <int NT, typename F>
 __device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], uint32_t valid, uint32_t n_valid,
-                                                uint32_t k, SelLds& L, F&& emit) {
+                                                uint32_t k, SelLds<NT>& L, F&& emit) {
+  constexpr int NW = NT / 64, EPL = kSelPer * NW / 64;  // table entries per lane of wave 0
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const bool all = n_valid <= k;
   uint32_t T = 0, need_eq = 0;
   if (!all) radix_threshold(key, valid, k, L, &T, &need_eq);
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  uint32_t pg[kSelPer], pe[kSelPer];
 #pragma unroll
   for (int j = 0; j < kSelPer; ++j) {
     const bool v = (valid >> j) & 1u;
     const bool gt = v && (all || key[j] > T), eq = v && !all && key[j] == T;
     const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    pg[j] = __popcll(bg & below);
-    pe[j] = __popcll(be & below);
-    if (lane == 0) L.table[j * 16 + w] = (uint32_t(__popcll(bg)) << 16) | uint32_t(__popcll(be));
+    if (lane == 0) L.table[j * NW + w] = (uint32_t(__popcll(bg)) << 16) | uint32_t(__popcll(be));
   }
   __syncthreads();
-  if (t < kWave) {  // exclusive scan of the 256 (slot, wave) counts, 4 per lane, in index order
-    uint32_t c[4], sum = 0;
+  if (t < kWave) {  // exclusive scan of the (slot, wave) counts, EPL per lane, in index order
+    uint32_t c[EPL], sum = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      c[e] = L.table[4 * lane + e];
+    for (int e = 0; e < EPL; ++e) {
+      c[e] = L.table[EPL * lane + e];
       sum += c[e];
     }
     uint32_t incl = sum;
@@ -467,8 +553,8 @@ __device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], 
     }
     uint32_t run = incl - sum;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      L.table[4 * lane + e] = run;
+    for (int e = 0; e < EPL; ++e) {
+      L.table[EPL * lane + e] = run;
       run += c[e];
     }
     if (lane == 63) L.total = incl;
@@ -479,16 +565,18 @@ __device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], 
   for (int j = 0; j < kSelPer; ++j) {
     const bool v = (valid >> j) & 1u;
     const bool gt = v && (all || key[j] > T), eq = v && !all && key[j] == T;
-    const uint32_t base = L.table[j * 16 + w];
-    const uint32_t gb = (base >> 16) + pg[j], eb = (base & 0xffffu) + pe[j];
+    const uint32_t base = L.table[j * NW + w];
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);  // recomputed: cheaper than 32 live registers
+    const uint32_t gb = (base >> 16) + uint32_t(__popcll(bg & below)), eb = (base & 0xffffu) + uint32_t(__popcll(be & below));
     if (gt || (eq && eb < need_eq)) emit(j, gb + min(eb, need_eq));
   }
   return (tot >> 16) + min(tot & 0xffffu, need_eq);
 }
 
+template <int NT>
 __device__ __forceinline__ void finish_row(int32_t* sel_row, uint32_t count, uint32_t k, int pos, int32_t* n_sel,
                                            int32_t* tail) {
-  for (uint32_t p = count + threadIdx.x; p < k; p += kSelThreads) sel_row[p] = -1;
+  for (uint32_t p = count + threadIdx.x; p < k; p += NT) sel_row[p] = -1;
   if (threadIdx.x == 0) {
     *n_sel = int32_t(count);
     *tail = pos < 0 ? 0 : 4 * ((pos + 1) / 4);
@@ -497,27 +585,30 @@ __device__ __forceinline__ void finish_row(int32_t* sel_row, uint32_t count, uin
 
 // Segment pass: grid (rows, segments). A row with one segment is finished here; longer rows leave
 // their segment's top-k (key, block) candidates for k_qsa_merge.
-__global__ void __launch_bounds__(kSelThreads) k_qsa_select(QsaShape sh, const int2* __restrict__ info,
+template <int NT>
+__global__ void __launch_bounds__(NT, 8) k_qsa_select(QsaShape sh, const int2* __restrict__ info,
                                                             const float* __restrict__ scores, int64_t ld_s,
                                                             uint32_t* __restrict__ cand_key,
                                                             int32_t* __restrict__ cand_idx, int segmax,
                                                             int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
                                                             int32_t* __restrict__ tail) {
-  __shared__ SelLds L;
+  __shared__ SelLds<NT> L;
   const int t = threadIdx.x;
   const int64_t r = blockIdx.x;
   const int sg = blockIdx.y;
   const int pos = info[r].y;
   const int64_t nb = row_blocks(pos, sh.cap);
-  const int nseg = int((nb + kSelSeg - 1) / kSelSeg);
+  constexpr int SEG = NT * kSelPer;
+  // smaller workgroups are launched only when every row fits one segment (cap <= SEG)
+  const int nseg = SEG == kSelSeg ? int((nb + SEG - 1) / SEG) : int(nb > 0);
   if (sg >= max(nseg, 1)) return;
-  const int64_t seg0 = int64_t(sg) * kSelSeg;
-  const uint32_t n = uint32_t(min(int64_t(kSelSeg), nb - seg0 > 0 ? nb - seg0 : int64_t(0)));
+  const int64_t seg0 = int64_t(sg) * SEG;
+  const uint32_t n = uint32_t(min(int64_t(SEG), nb - seg0 > 0 ? nb - seg0 : int64_t(0)));
   const float* row = scores + r * ld_s + seg0;
   uint32_t key[kSelPer], valid = 0;
 #pragma unroll
   for (int j = 0; j < kSelPer; ++j) {
-    const uint32_t i = uint32_t(j * kSelThreads + t);
+    const uint32_t i = uint32_t(j * NT + t);
     const bool v = i < n;
     key[j] = v ? (__float_as_uint(row[i]) & 0x7fffffffu) : 0u;
     valid |= uint32_t(v) << j;
@@ -525,25 +616,26 @@ __global__ void __launch_bounds__(kSelThreads) k_qsa_select(QsaShape sh, const i
   const uint32_t k = uint32_t(sh.topk);
   if (nseg <= 1) {
     int32_t* srow = sel + r * sh.topk;
-    const uint32_t cnt = select_topk(key, valid, n, k, L, [&](int j, uint32_t p) { srow[p] = j * kSelThreads + t; });
-    finish_row(srow, cnt, k, pos, n_sel + r, tail + r);
+    const uint32_t cnt = select_topk<NT>(key, valid, n, k, L, [&](int j, uint32_t p) { srow[p] = j * NT + t; });
+    finish_row<NT>(srow, cnt, k, pos, n_sel + r, tail + r);
   } else {
     const int64_t c0 = (r * segmax + sg) * int64_t(sh.topk);
-    select_topk(key, valid, n, k, L, [&](int j, uint32_t p) {
+    select_topk<NT>(key, valid, n, k, L, [&](int j, uint32_t p) {
       cand_key[c0 + p] = key[j];
-      cand_idx[c0 + p] = int32_t(seg0 + j * kSelThreads + t);
+      cand_idx[c0 + p] = int32_t(seg0 + j * NT + t);
     });
   }
 }
 
 // Merge pass for rows of several segments: candidates of segment s sit at s * k .. s * k + c_s - 1,
 // in block order, so list position order is block order.
-__global__ void __launch_bounds__(kSelThreads) k_qsa_merge(QsaShape sh, const int2* __restrict__ info,
+template <int NT>
+__global__ void __launch_bounds__(NT) k_qsa_merge(QsaShape sh, const int2* __restrict__ info,
                                                            const uint32_t* __restrict__ cand_key,
                                                            const int32_t* __restrict__ cand_idx, int segmax,
                                                            int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
                                                            int32_t* __restrict__ tail) {
-  __shared__ SelLds L;
+  __shared__ SelLds<NT> L;
   const int t = threadIdx.x;
   const int64_t r = blockIdx.x;
   const int pos = info[r].y;
@@ -556,7 +648,7 @@ __global__ void __launch_bounds__(kSelThreads) k_qsa_merge(QsaShape sh, const in
   int32_t idx[kSelPer];
 #pragma unroll
   for (int j = 0; j < kSelPer; ++j) {
-    const uint32_t p = uint32_t(j * kSelThreads + t), s = p / k, i = p - s * k;
+    const uint32_t p = uint32_t(j * NT + t), s = p / k, i = p - s * k;
     const int64_t cs = s < uint32_t(nseg) ? min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)) : 0;
     const bool v = int64_t(i) < cs;
     key[j] = v ? cand_key[c0 + p] : 0u;
@@ -565,8 +657,8 @@ __global__ void __launch_bounds__(kSelThreads) k_qsa_merge(QsaShape sh, const in
   }
   for (int s = 0; s < nseg; ++s) nv += uint32_t(min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)));
   int32_t* srow = sel + r * sh.topk;
-  const uint32_t cnt = select_topk(key, valid, nv, k, L, [&](int j, uint32_t p) { srow[p] = idx[j]; });
-  finish_row(srow, cnt, k, pos, n_sel + r, tail + r);
+  const uint32_t cnt = select_topk<NT>(key, valid, nv, k, L, [&](int j, uint32_t p) { srow[p] = idx[j]; });
+  finish_row<NT>(srow, cnt, k, pos, n_sel + r, tail + r);
 }
 
 // ---- launchers ----------------------------------------------------------------------------------
@@ -619,7 +711,13 @@ hipError_t launch_qsa_rows(const QsaShape& sh, const QsaWs& ws, int64_t row0, in
   if (e != hipSuccess) return e;
   const dim3 sgrid(unsigned(rows), unsigned(std::max<int64_t>(1, (sh.cap + kScoreChunk - 1) / kScoreChunk)));
   if (sh.cap > 0) {
-    if (sh.bf16)
+    if (sh.bf16 && cu)  // prefill rows: many queries per sequence, a dense contraction
+      hipLaunchKernelGGL(k_qsa_score_mfma,
+                         dim3(static_cast<unsigned>((rows + 63) / 64),
+                              static_cast<unsigned>((sh.cap + kMfmaChunk - 1) / kMfmaChunk)),
+                         dim3(256), 0, s, sh, ws.qr, ws.info, rows, static_cast<const uint16_t*>(kbar), ws.scores,
+                         ws.ld_s);
+    else if (sh.bf16)
       hipLaunchKernelGGL(k_qsa_score<bf16>, sgrid, dim3(256), 0, s, sh, ws.qr, ws.info,
                          static_cast<const bf16*>(kbar), ws.scores, ws.ld_s);
     else
@@ -629,11 +727,21 @@ hipError_t launch_qsa_rows(const QsaShape& sh, const QsaWs& ws, int64_t row0, in
     if (e != hipSuccess) return e;
   }
   int32_t* sel_r = sel + row0 * sh.topk;
-  hipLaunchKernelGGL(k_qsa_select, dim3(unsigned(rows), unsigned(ws.segmax)), dim3(kSelThreads), 0, s, sh, ws.info,
-                     ws.scores, ws.ld_s, ws.cand_key, ws.cand_idx, ws.segmax, sel_r, n_sel + row0, tail + row0);
+  // one workgroup per row and segment; short rows (caches of <= 4096 or 8192 blocks) take smaller
+  // workgroups, several of which share a CU
+  const dim3 selgrid(static_cast<unsigned>(rows), static_cast<unsigned>(ws.segmax));
+  if (sh.cap <= 256 * kSelPer)
+    hipLaunchKernelGGL(k_qsa_select<256>, selgrid, dim3(256), 0, s, sh, ws.info, ws.scores, ws.ld_s, ws.cand_key,
+                       ws.cand_idx, ws.segmax, sel_r, n_sel + row0, tail + row0);
+  else if (sh.cap <= 512 * kSelPer)
+    hipLaunchKernelGGL(k_qsa_select<512>, selgrid, dim3(512), 0, s, sh, ws.info, ws.scores, ws.ld_s, ws.cand_key,
+                       ws.cand_idx, ws.segmax, sel_r, n_sel + row0, tail + row0);
+  else
+    hipLaunchKernelGGL(k_qsa_select<1024>, selgrid, dim3(1024), 0, s, sh, ws.info, ws.scores, ws.ld_s, ws.cand_key,
+                       ws.cand_idx, ws.segmax, sel_r, n_sel + row0, tail + row0);
   e = hipGetLastError();
   if (e != hipSuccess || ws.segmax <= 1) return e;
-  hipLaunchKernelGGL(k_qsa_merge, rgrid, dim3(kSelThreads), 0, s, sh, ws.info, ws.cand_key, ws.cand_idx, ws.segmax,
+  hipLaunchKernelGGL(k_qsa_merge<1024>, rgrid, dim3(1024), 0, s, sh, ws.info, ws.cand_key, ws.cand_idx, ws.segmax,
                      sel_r, n_sel + row0, tail + row0);
   return hipGetLastError();
 }

@@ -5,8 +5,9 @@ The selection is an integer result decided by floating point, so it is checked f
 list structure (ascending, complete blocks only, count min(topk, blocks), -1 padding, tail start)
 exactly, and the chosen set against the oracle's fp64 scores S within an error bound E on the
 kernel's scores. The kernel scores stored keys (rounded to the io dtype: |dk| <= 2^-8 |k| for bf16)
-with fp32 products and fp32 rotated queries, so per query and block
-    |s_kernel - S| <= sum_h sum_d |q_hd| |kbar_d| * c,   c = 2^-8 + 2e-5 (bf16), 2e-5 (fp32)
+against rotated queries (fp32, and rounded to bf16 for the prefill's bf16 MFMA: another 2^-8), with
+fp32 accumulation, so per query and block
+    |s_kernel - S| <= sum_h sum_d |q_hd| |kbar_d| * c,   c = 2^-7 + 2e-5 (bf16), 2e-5 (fp32)
 (ReLU is 1-Lipschitz). A valid selection then has min over chosen (S + E) >= max over the others
 (S - E); where the oracle's k-th and (k+1)-th scores are further apart than that, the chosen set
 is exactly the oracle's.
@@ -26,7 +27,7 @@ if not torch.cuda.is_available():
 
 DEV = "cuda:0"
 TOL_KBAR = {torch.bfloat16: 1e-2, torch.float32: 1e-4}
-C_SCORE = {torch.bfloat16: 2.0 ** -8 + 2e-5, torch.float32: 2e-5}
+C_SCORE = {torch.bfloat16: 2.0 ** -7 + 2e-5, torch.float32: 2e-5}
 
 
 def _np(t):
@@ -225,17 +226,18 @@ def test_decode_one_million_tokens(dtype):
     assert n_sel.tolist() == [512, 512]
 
 
-def test_prefill_select_long_rows_merge():
-    """One 66000-token sequence: tokens past 65536 see more than 16384 blocks (two select segments and
-    the merge). Sampled rows, including the last ones, against the oracle."""
+@pytest.mark.parametrize("T", [20000, 66000])
+def test_prefill_select_long_rows(T):
+    """One long sequence, sampled rows (including the last ones) against the oracle. 20000 tokens:
+    caches of 5000 blocks take the 512-thread select; 66000: tokens past 65536 see more than 16384
+    blocks (two select segments and the merge)."""
     dtype = torch.bfloat16
-    T = 66000
     x = indexer_inputs([T], io_dtype=dtype, seed=16, device=DEV)
     cfg = qsa.cfg_for(dtype)
     kbar, _ = _compress(cfg, x, T // 4, pending=False)
     sel, n_sel, tail = qsa.qsa_select(cfg, x.cu_seqlens, x.q, kbar)
     torch.cuda.synchronize()
-    rows = np.concatenate([np.arange(T - 6, T), np.random.default_rng(0).integers(0, T, 10), [3, 2050, 65539]])
+    rows = np.concatenate([np.arange(T - 6, T), np.random.default_rng(0).integers(0, T, 10), [3, 2050, T - 4461]])
     kb = O.qsa_compress(_np(x.k), _np(x.norm_w))
     r_t = torch.as_tensor(rows, device=DEV)
     _check_rows(dtype, _np(x.q[r_t]), rows, kb, sel[r_t].cpu().numpy(), n_sel[r_t].cpu().numpy(),
