@@ -122,6 +122,95 @@ def gated_delta_rule_product_form(q, k, v, alpha, beta, S0, scale=1.0):
     return y, S
 
 
+def gated_delta_rule_backward(q, k, v, alpha, beta, S0, dy, dS_final=None, scale=1.0):
+    """Reverse-mode derivatives of gated_delta_rule for one chain: given dL/dy_t (dy [L, d_v]) and
+    dL/dS_L (dS_final [d_k, d_v], None = 0), returns (dq, dk, dv, dalpha, dbeta, dS0).
+
+    The forward states are recomputed and kept; the reverse loop takes the statements of the error
+    form ([P2] §03 update equations) last to first and applies the chain rule to each:
+      y_t = scale S_t^T q_t        ->  dS += scale q_t dy_t^T,  dq_t = scale S_t dy_t
+      S_t = S~ + beta_t k_t e^T    ->  dbeta_t = k_t^T dS e,  dk_t = beta_t dS e,  de = beta_t dS^T k_t,
+                                       dS~ = dS
+      e = v_t - S~^T k_t           ->  dv_t = de,  dS~ -= k_t de^T,  dk_t -= S~ de
+      S~ = alpha_t S_{t-1}         ->  dalpha_t = <S_{t-1}, dS~>,  dS_{t-1} = alpha_t dS~
+    """
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    L, d_v = v.shape
+    d_k = k.shape[1]
+    states = [np.array(_f64(S0), dtype=np.float64, copy=True)]
+    errs = []
+    for t in range(L):
+        S_tilde = alpha[t] * states[-1]
+        e = v[t] - S_tilde.T @ k[t]
+        errs.append(e)
+        states.append(S_tilde + beta[t] * np.outer(k[t], e))
+    dS = np.zeros((d_k, d_v)) if dS_final is None else np.array(_f64(dS_final), dtype=np.float64, copy=True)
+    dq, dk, dv = np.zeros((L, d_k)), np.zeros((L, d_k)), np.zeros((L, d_v))
+    dalpha, dbeta = np.zeros(L), np.zeros(L)
+    for t in range(L - 1, -1, -1):
+        S_t, S_prev, e = states[t + 1], states[t], errs[t]
+        dS = dS + scale * np.outer(q[t], dy[t])
+        dq[t] = scale * (S_t @ dy[t])
+        dbeta[t] = k[t] @ dS @ e
+        de = beta[t] * (dS.T @ k[t])
+        dk[t] = beta[t] * (dS @ e)
+        dv[t] = de
+        S_tilde = alpha[t] * S_prev
+        dS_tilde = dS - np.outer(k[t], de)
+        dk[t] -= S_tilde @ de
+        dalpha[t] = np.sum(S_prev * dS_tilde)
+        dS = alpha[t] * dS_tilde
+    return dq, dk, dv, dalpha, dbeta, dS
+
+
+def recurrence_layer(q, k, v, alpha, beta, S0, cu, *, scale=1.0):
+    """The recurrence over a packed layer: q, k [T, HK, d_k], v [T, HV, d_v], alpha, beta [T, HV],
+    S0 [N, HV, d_k, d_v] or None; value head h reads QK head floor(h HK / HV). Returns (y [T, HV, d_v],
+    S_final [N, HV, d_k, d_v])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, beta = _f64(alpha), _f64(beta)
+    T, HK, d_k = k.shape
+    HV, d_v = v.shape[1], v.shape[2]
+    cu = np.asarray(cu)
+    N = len(cu) - 1
+    y = np.zeros((T, HV, d_v))
+    S_fin = np.zeros((N, HV, d_k, d_v))
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        for h in range(HV):
+            g = h * HK // HV
+            s0 = np.zeros((d_k, d_v)) if S0 is None else _f64(S0)[n, h]
+            y[a:b, h], S_fin[n, h] = gated_delta_rule(q[a:b, g], k[a:b, g], v[a:b, h], alpha[a:b, h],
+                                                      beta[a:b, h], s0, scale)
+    return y, S_fin
+
+
+def recurrence_layer_backward(q, k, v, alpha, beta, S0, cu, dy, dS_final=None, *, scale=1.0):
+    """Derivatives of recurrence_layer: (dq, dk [T, HK, d_k] -- summed over the value heads that read
+    each QK head --, dv [T, HV, d_v], dalpha, dbeta [T, HV], dS0 [N, HV, d_k, d_v])."""
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    alpha, beta = _f64(alpha), _f64(beta)
+    T, HK, d_k = k.shape
+    HV, d_v = v.shape[1], v.shape[2]
+    cu = np.asarray(cu)
+    N = len(cu) - 1
+    dq, dk = np.zeros((T, HK, d_k)), np.zeros((T, HK, d_k))
+    dv, da, db = np.zeros((T, HV, d_v)), np.zeros((T, HV)), np.zeros((T, HV))
+    dS0 = np.zeros((N, HV, d_k, d_v))
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        for h in range(HV):
+            g = h * HK // HV
+            s0 = np.zeros((d_k, d_v)) if S0 is None else _f64(S0)[n, h]
+            dsf = None if dS_final is None else _f64(dS_final)[n, h]
+            r = gated_delta_rule_backward(q[a:b, g], k[a:b, g], v[a:b, h], alpha[a:b, h], beta[a:b, h], s0,
+                                          dy[a:b, h], dsf, scale)
+            dq[a:b, g] += r[0]
+            dk[a:b, g] += r[1]
+            dv[a:b, h], da[a:b, h], db[a:b, h], dS0[n, h] = r[2], r[3], r[4], r[5]
+    return dq, dk, dv, da, db, dS0
+
+
 def zero_centred_rmsnorm(y, w, eps):
     """RMSNorm over the d_v channels of one head with gain (1 + w) ([P2] §03: zero-centred
     RMSNorm; [P5] Method: head outputs are normalised)."""
