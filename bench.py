@@ -150,6 +150,55 @@ def cpu_baseline(max_tokens: int):
                        f"{dt:.1f} s")
 
 
+def backward_leg(args, dev, stream):
+    """Recurrence backward at model shape (16 QK / 48 value heads, d = 128, fp32), one sequence: the
+    forward keeps every state (64 KB per token and value head) and the reverse pass reads them back."""
+    import torch
+    from linear_attention_token_amd import gdn
+
+    T = args.bwd_tokens
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    f = torch.float32
+    q = torch.nn.functional.normalize(torch.randn(T, HK, D, generator=g, device=dev), dim=-1)
+    k = torch.nn.functional.normalize(torch.randn(T, HK, D, generator=g, device=dev), dim=-1)
+    v = torch.randn(T, HV, D, generator=g, device=dev)
+    alpha = torch.exp(torch.log(torch.tensor(0.9, device=dev)) * torch.rand(T, HV, generator=g, device=dev))
+    beta = torch.sigmoid(torch.randn(T, HV, generator=g, device=dev))
+    dy = torch.randn(T, HV, D, generator=g, device=dev)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    cfg = gdn.cfg_for(HK, HV, D, D, f)
+    ws = torch.empty(gdn.gdn_recurrence_backward_workspace(cfg, 1, T), dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.gdn_recurrence_backward(cfg, cu, q, k, v, alpha, beta, dy, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    n = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    io_bytes = 4 * T * (2 * 2 * HK * D + 3 * HV * D + 4 * HV) + 4 * HV * D * D  # in + out, once each
+    spill = 2 * 4 * T * HV * D * D + 2 * 4 * T * HV * D  # states and errors written, then read back
+    gb = (io_bytes + spill) / (ms * 1e-3) / 1e9
+    del ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"recurrence backward, B=1, T={T}, 16 QK / 48 value heads, d=128, fp32: dq, dk, dv, dalpha, "
+                    f"dbeta, dS0 from dy",
+        "ms_per_call": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": dict(bound="hbm", achieved=round(gb, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                         frac=round(gb / HBM_PEAK_GBPS, 4), algorithmic_bytes=io_bytes, state_bytes=spill,
+                         note="achieved counts the kept states (written once, read once) with the inputs and "
+                              "outputs; one workgroup per (sequence, value head) runs token by token"),
+    }
+
+
 def indexer_leg(args, dev, stream):
     """QSA compressed indexer: a decode step of B sequences at a long context (append the token's key,
     score every complete block, keep the top 512) and a prefill of one sequence (compress, then
@@ -255,7 +304,8 @@ def main():
     ap.add_argument("--qsa-batch", type=int, default=8, help="sequences of the indexer decode")
     ap.add_argument("--qsa-prefill", type=int, default=32768, help="tokens of the indexer prefill (one sequence)")
     ap.add_argument("--qsa-steps", type=int, default=50)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "speculative", "layer", "indexer", "copy"],
+    ap.add_argument("--bwd-tokens", type=int, default=4096, help="tokens of the recurrence backward (one sequence)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "speculative", "layer", "indexer", "backward", "copy"],
                     default="all",
                     help="run one part only (for profilers); 'copy' times a plain 1 GiB device copy, the "
                          "reference kernel for scaling HBM byte counters")
@@ -568,6 +618,9 @@ def main():
 
     if args.only in ("all", "indexer"):
         result["indexer"] = indexer_leg(args, dev, stream)
+
+    if args.only in ("all", "backward"):
+        result["backward"] = backward_leg(args, dev, stream)
 
     if not args.no_cpu_baseline and args.only == "all":
         result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)

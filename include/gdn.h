@@ -219,6 +219,34 @@ gdn_status gdn_in_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const void
 gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const void* o, const void* w_out,
                         void* y, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Backward of the recurrence (step 3 above) for training: reverse-mode derivatives of
+ *     S~ = alpha_t S;  e = v_t - S~^T k_t;  S = S~ + beta_t k_t e^T;  y_t = scale * S^T q_t
+ * (analysis notes §03 update equations) for packed sequences, given dL/dy and dL/dS_final. Inputs are
+ * the recurrence's own: q and k after the conv, SiLU and L2 (the backward of those steps and of the
+ * output norm and gate is not part of this call). fp32 io (cfg->io_dtype = GDN_F32), d_k = d_v = 128,
+ * any HV multiple of HK; cfg->scale is used, cfg->flags are ignored.
+ *
+ *   cu_seqlens      device int32 [n_seqs+1], as for gdn_prefill.
+ *   q, k            fp32 [T][HK][128];  v fp32 [T][HV][128];  alpha, beta fp32 [T][HV].
+ *   state_in        fp32 [n_seqs][HV][128][128] initial states; NULL = zeros.
+ *   dy              fp32 [T][HV][128]: dL/dy.
+ *   dstate_out      fp32 [n_seqs][HV][128][128]: dL/dS_final; NULL = zeros.
+ *   dq, dk          fp32 [T][HK][128] out: summed over the value heads that read each QK head.
+ *   dv              fp32 [T][HV][128] out;  dalpha, dbeta fp32 [T][HV] out.
+ *   dstate_in       fp32 [n_seqs][HV][128][128] out (dL/dS_0), or NULL.
+ *   workspace       gdn_recurrence_backward_workspace() bytes, 256-byte aligned: every state of the
+ *                   forward (64 KB per token and value head) is kept there, so the reverse pass uses the
+ *                   forward's exact states; split long batches to bound it.
+ * One workgroup runs each (sequence, value head) chain token by token (forward, then reverse). */
+gdn_status gdn_recurrence_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                                             size_t* bytes);
+gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                                   const int32_t* cu_seqlens, const float* q, const float* k, const float* v,
+                                   const float* alpha, const float* beta, const float* state_in, const float* dy,
+                                   const float* dstate_out, float* dq, float* dk, float* dv, float* dalpha,
+                                   float* dbeta, float* dstate_in, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream);
+
 /* Stage timing for profilers (host-side, per calling thread). After this call, every gdn_prefill
  * on this thread records events[i] on its stream before stage i and events[GDN_N_STAGES] after the
  * last stage, for the stages

@@ -511,6 +511,86 @@ gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const voi
   return GDN_OK;
 }
 
+// Workspace of the recurrence backward: every state and error of the forward, and per-value-head
+// dq / dk when value heads share QK heads.
+static size_t bwd_workspace_bytes(int64_t T, int hk, int hv) {
+  size_t b = align256(sizeof(float) * size_t(T) * hv * 128 * 128) + align256(sizeof(float) * size_t(T) * hv * 128);
+  if (hv != hk) b += 2 * align256(sizeof(float) * size_t(T) * hv * 128);
+  return b;
+}
+
+static gdn_status check_bwd(const gdn_cfg* cfg, int32_t n_seqs, int64_t T, Problem& p) {
+  gdn_status st = check_cfg(cfg, p);
+  if (st != GDN_OK) return st;
+  if (cfg->io_dtype != GDN_F32) return fail(GDN_E_UNSUPPORTED, "the recurrence backward takes fp32 tensors");
+  if (p.dk != 128 || p.dv != 128) return fail(GDN_E_UNSUPPORTED, "the recurrence backward needs d_k = d_v = 128");
+  if (n_seqs < 0 || T < 0) return fail(GDN_E_SHAPE, "negative n_seqs or total_tokens");
+  if (n_seqs == 0 && T != 0) return fail(GDN_E_SHAPE, "tokens without sequences");
+  if (T >= (int64_t(1) << 31)) return fail(GDN_E_UNSUPPORTED, "total_tokens must stay below 2^31");
+  if (int64_t(n_seqs) * p.hv > int64_t(INT32_MAX)) return fail(GDN_E_UNSUPPORTED, "too many (sequence, head) chains");
+  return GDN_OK;
+}
+
+gdn_status gdn_recurrence_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, size_t* bytes) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_bwd(cfg, n_seqs, total_tokens, p);
+  if (st != GDN_OK) return st;
+  if (!bytes) return fail(GDN_E_NULL, "bytes is NULL");
+  *bytes = bwd_workspace_bytes(total_tokens, p.hk, p.hv);
+  return GDN_OK;
+}
+
+gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                                   const int32_t* cu_seqlens, const float* q, const float* k, const float* v,
+                                   const float* alpha, const float* beta, const float* state_in, const float* dy,
+                                   const float* dstate_out, float* dq, float* dk, float* dv, float* dalpha,
+                                   float* dbeta, float* dstate_in, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_bwd(cfg, n_seqs, total_tokens, p);
+  if (st != GDN_OK) return st;
+  if (n_seqs == 0) return GDN_OK;
+  if (!cu_seqlens) return fail(GDN_E_NULL, "cu_seqlens is required");
+  if (total_tokens > 0 && (!q || !k || !v || !alpha || !beta || !dy || !dq || !dk || !dv || !dalpha || !dbeta))
+    return fail(GDN_E_NULL, "q, k, v, alpha, beta, dy and the gradient outputs are required");
+  const void* ptrs[] = {q, k, v, state_in, dy, dstate_out, dq, dk, dv, dstate_in};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (!aligned4(alpha) || !aligned4(beta) || !aligned4(dalpha) || !aligned4(dbeta) || !aligned4(cu_seqlens))
+    return fail(GDN_E_ALIGN, "alpha, beta, dalpha, dbeta and cu_seqlens must be 4-byte aligned");
+  const size_t need = bwd_workspace_bytes(total_tokens, p.hk, p.hv);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
+  char* w = static_cast<char*>(workspace);
+  BwdArgs a{};
+  a.cu = cu_seqlens;
+  a.n_seqs = n_seqs;
+  a.T = total_tokens;
+  a.hk = p.hk;
+  a.hv = p.hv;
+  a.scale = p.scale;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.s0 = state_in; a.dy = dy; a.dsf = dstate_out;
+  a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.ds0 = dstate_in;
+  a.states = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * size_t(total_tokens) * p.hv * 128 * 128);
+  a.errs = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * size_t(total_tokens) * p.hv * 128);
+  if (p.hv != p.hk) {
+    a.dqv = reinterpret_cast<float*>(w);
+    w += align256(sizeof(float) * size_t(total_tokens) * p.hv * 128);
+    a.dkv = reinterpret_cast<float*>(w);
+  } else {
+    a.dqv = dq;
+    a.dkv = dk;
+  }
+  if (run(launch_bwd(a, dq, dk, static_cast<hipStream_t>(hip_stream)), "recurrence backward") != hipSuccess)
+    return GDN_E_HIP;
+  return GDN_OK;
+}
+
 void qsa_cfg_default(qsa_cfg* cfg) {
   if (!cfg) return;
   cfg->n_heads = 4;

@@ -135,6 +135,26 @@ hipError_t gemm_bf16_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t 
 hipError_t launch_gates(const void* x, int64_t ld_x, int64_t T, int H, const void* w_ab, int hv, const float* a_log,
                         const float* dt_bias, float* alpha, float* beta, hipStream_t s);
 
+// ---- recurrence backward (fp32, d = 128) ----
+struct BwdArgs {
+  const int32_t* cu;
+  int n_seqs;
+  int64_t T;
+  int hk, hv;
+  float scale;
+  const float *q, *k, *v;       // [T][HK][128], [T][HK][128], [T][HV][128]
+  const float *alpha, *beta;    // [T][HV]
+  const float* s0;              // [N][HV][128][128] or null (zeros)
+  const float* dy;              // [T][HV][128]
+  const float* dsf;             // [N][HV][128][128] or null (zeros)
+  float *dqv, *dkv;             // [T][HV][128] per value head
+  float *dv, *dalpha, *dbeta;   // outputs
+  float* ds0;                   // [N][HV][128][128] or null
+  float* states;                // workspace [T][HV][256][64]: every state, each thread's tile contiguous
+  float* errs;                  // workspace [T][HV][128]
+};
+hipError_t launch_bwd(const BwdArgs& a, float* dq, float* dk, hipStream_t s);
+
 // ---- QSA compressed indexer ----
 constexpr int kSelSeg = 16384;  // scores per select workgroup (1024 threads x 16)
 

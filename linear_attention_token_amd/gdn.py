@@ -22,6 +22,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_E_NULL", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE", 4: "
 EXPORTS = ("gdn_cfg_default", "gdn_prefill_workspace", "gdn_prefill", "gdn_decode_step",
            "gdn_verify_log_bytes", "gdn_verify", "gdn_commit",
            "gdn_proj_workspace", "gdn_in_proj", "gdn_out_proj",
+           "gdn_recurrence_backward_workspace", "gdn_recurrence_backward",
            "gdn_set_stage_events", "gdn_status_string", "gdn_last_error", "gdn_abi_version")
 N_STAGES = 6
 STAGE_NAMES = ("chunk_table", "conv_silu_l2", "wy_or_sequential", "state", "output_norm_gate", "conv_tail")
@@ -383,6 +384,54 @@ def gdn_out_proj(cfg: gdn_cfg, o, w_out, y=None, workspace=None, stream=None) ->
     _check(lib.gdn_out_proj(ctypes.byref(cfg), H, T, _ptr(o2), _ptr(w_out), _ptr(y), _ptr(workspace),
                             workspace.numel(), _stream(stream)))
     return y
+
+
+def _declare_bwd(lib):
+    if getattr(lib, "_bwd_declared", False):
+        return
+    C = ctypes.POINTER(gdn_cfg)
+    lib.gdn_recurrence_backward_workspace.argtypes = [C, ctypes.c_int32, _I64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_recurrence_backward.argtypes = [C, ctypes.c_int32, _I64] + [_P] * 16 + [ctypes.c_size_t, _P]
+    lib.gdn_recurrence_backward_workspace.restype = ctypes.c_int
+    lib.gdn_recurrence_backward.restype = ctypes.c_int
+    lib._bwd_declared = True
+
+
+def gdn_recurrence_backward_workspace(cfg: gdn_cfg, n_seqs: int, total_tokens: int) -> int:
+    lib = load_library()
+    _declare_bwd(lib)
+    n = ctypes.c_size_t()
+    _check(lib.gdn_recurrence_backward_workspace(ctypes.byref(cfg), n_seqs, total_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def gdn_recurrence_backward(cfg: gdn_cfg, cu_seqlens, q, k, v, alpha, beta, dy, state_in=None, dstate_out=None,
+                            want_dstate_in: bool = True, workspace=None, stream=None):
+    """Derivatives of the recurrence (fp32, d = 128): returns (dq, dk, dv, dalpha, dbeta, dstate_in or None)."""
+    lib = load_library()
+    _declare_bwd(lib)
+    n = int(cu_seqlens.numel()) - 1
+    T = int(q.shape[0])
+    hk, hv, d = cfg.n_qk_heads, cfg.n_v_heads, cfg.d_k
+    f = torch.float32
+    _expect(cu_seqlens, (n + 1,), torch.int32, "cu_seqlens")
+    for t, shape, name in ((q, (T, hk, d), "q"), (k, (T, hk, d), "k"), (v, (T, hv, d), "v"), (alpha, (T, hv), "alpha"),
+                           (beta, (T, hv), "beta"), (dy, (T, hv, d), "dy")):
+        _expect(t, shape, f, name)
+    _expect(state_in, (n, hv, d, d), f, "state_in", optional=True)
+    _expect(dstate_out, (n, hv, d, d), f, "dstate_out", optional=True)
+    dev = q.device
+    dq, dk = torch.empty((T, hk, d), dtype=f, device=dev), torch.empty((T, hk, d), dtype=f, device=dev)
+    dv = torch.empty((T, hv, d), dtype=f, device=dev)
+    da, db = torch.empty((T, hv), dtype=f, device=dev), torch.empty((T, hv), dtype=f, device=dev)
+    ds0 = torch.empty((n, hv, d, d), dtype=f, device=dev) if want_dstate_in else None
+    if workspace is None:
+        workspace = torch.empty(max(gdn_recurrence_backward_workspace(cfg, n, T), 1), dtype=torch.uint8, device=dev)
+    _check(lib.gdn_recurrence_backward(ctypes.byref(cfg), n, T, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _ptr(state_in), _ptr(dy), _ptr(dstate_out),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(ds0),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv, da, db, ds0
 
 
 def cfg_for(n_qk_heads: int, n_v_heads: int, d_k: int, d_v: int, dtype: torch.dtype,

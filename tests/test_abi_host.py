@@ -296,3 +296,27 @@ def test_qsa_reject_bad_arguments():
     _err(dec(wsb=64), 5)
     _err(dec(cap=-1), 2)
     assert dec(B=0, q=None, k=None) == 0
+
+
+def test_recurrence_backward_rejects_bad_arguments():
+    f32 = gdn.gdn_cfg_default(io_dtype=gdn.GDN_F32)
+    gdn._declare_bwd(lib)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_recurrence_backward_workspace(ctypes.byref(f32), 1, 4096, ctypes.byref(n)) == 0
+    assert n.value >= 4096 * 48 * 128 * 128 * 4   # every state of the forward is kept
+    _err(lib.gdn_recurrence_backward_workspace(ctypes.byref(gdn.gdn_cfg_default()), 1, 64, ctypes.byref(n)), 6)
+    _err(lib.gdn_recurrence_backward_workspace(
+        ctypes.byref(gdn.gdn_cfg_default(io_dtype=gdn.GDN_F32, d_k=64, d_v=64)), 1, 64, ctypes.byref(n)), 6)
+
+    def bwd(cfg=f32, N=1, T=64, cu=A, q=A, dy=A, dq=A, ws=A, wsb=1 << 40, da=A):
+        return lib.gdn_recurrence_backward(ctypes.byref(cfg), N, T, cu, q, A, A, A, A, None, dy, None, dq, A, A, da,
+                                           A, None, ws, wsb, None)
+
+    _err(bwd(dy=None), 1)
+    _err(bwd(cu=None), 1)
+    _err(bwd(wsb=1024), 5)
+    _err(bwd(ws=A + 16), 4)
+    _err(bwd(q=A + 4), 4)
+    _err(bwd(da=A + 2), 4)
+    _err(bwd(N=0), 2)
+    assert bwd(N=0, T=0) == 0
