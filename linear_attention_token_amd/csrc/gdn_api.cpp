@@ -511,12 +511,13 @@ gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const voi
   return GDN_OK;
 }
 
-// Workspace of the recurrence backward: every state and error of the forward, and per-value-head
-// dq / dk when value heads share QK heads.
+// Workspace of the recurrence backward: every state and error of the forward, per-slice partials of
+// dq and dk (8 slices of 16 value columns per value head) and of dalpha and dbeta.
 static size_t bwd_workspace_bytes(int64_t T, int hk, int hv) {
-  size_t b = align256(sizeof(float) * size_t(T) * hv * 128 * 128) + align256(sizeof(float) * size_t(T) * hv * 128);
-  if (hv != hk) b += 2 * align256(sizeof(float) * size_t(T) * hv * 128);
-  return b;
+  (void)hk;
+  const size_t th = size_t(T) * hv;
+  return align256(sizeof(float) * th * 128 * 128) + align256(sizeof(float) * th * 128) +
+         2 * align256(sizeof(float) * th * 8 * 128) + 2 * align256(sizeof(float) * th * 8);
 }
 
 static gdn_status check_bwd(const gdn_cfg* cfg, int32_t n_seqs, int64_t T, Problem& p) {
@@ -573,20 +574,21 @@ gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t t
   a.hv = p.hv;
   a.scale = p.scale;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.s0 = state_in; a.dy = dy; a.dsf = dstate_out;
-  a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.ds0 = dstate_in;
+  a.dv = dv;
+  a.ds0 = dstate_in;
+  const size_t th = size_t(total_tokens) * p.hv;
   a.states = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * size_t(total_tokens) * p.hv * 128 * 128);
+  w += align256(sizeof(float) * th * 128 * 128);
   a.errs = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * size_t(total_tokens) * p.hv * 128);
-  if (p.hv != p.hk) {
-    a.dqv = reinterpret_cast<float*>(w);
-    w += align256(sizeof(float) * size_t(total_tokens) * p.hv * 128);
-    a.dkv = reinterpret_cast<float*>(w);
-  } else {
-    a.dqv = dq;
-    a.dkv = dk;
-  }
-  if (run(launch_bwd(a, dq, dk, static_cast<hipStream_t>(hip_stream)), "recurrence backward") != hipSuccess)
+  w += align256(sizeof(float) * th * 128);
+  a.dqv = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 8 * 128);
+  a.dkv = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 8 * 128);
+  a.dalpha_part = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 8);
+  a.dbeta_part = reinterpret_cast<float*>(w);
+  if (run(launch_bwd(a, dq, dk, dalpha, dbeta, static_cast<hipStream_t>(hip_stream)), "recurrence backward") != hipSuccess)
     return GDN_E_HIP;
   return GDN_OK;
 }

@@ -136,24 +136,26 @@ hipError_t launch_gates(const void* x, int64_t ld_x, int64_t T, int H, const voi
                         const float* dt_bias, float* alpha, float* beta, hipStream_t s);
 
 // ---- recurrence backward (fp32, d = 128) ----
+// Each (sequence, value head) chain runs as 8 workgroups of 16 value columns.
 struct BwdArgs {
   const int32_t* cu;
   int n_seqs;
   int64_t T;
   int hk, hv;
   float scale;
-  const float *q, *k, *v;       // [T][HK][128], [T][HK][128], [T][HV][128]
-  const float *alpha, *beta;    // [T][HV]
-  const float* s0;              // [N][HV][128][128] or null (zeros)
-  const float* dy;              // [T][HV][128]
-  const float* dsf;             // [N][HV][128][128] or null (zeros)
-  float *dqv, *dkv;             // [T][HV][128] per value head
-  float *dv, *dalpha, *dbeta;   // outputs
-  float* ds0;                   // [N][HV][128][128] or null
-  float* states;                // workspace [T][HV][256][64]: every state, each thread's tile contiguous
-  float* errs;                  // workspace [T][HV][128]
+  const float *q, *k, *v;        // [T][HK][128], [T][HK][128], [T][HV][128]
+  const float *alpha, *beta;     // [T][HV]
+  const float* s0;               // [N][HV][128][128] or null (zeros)
+  const float* dy;               // [T][HV][128]
+  const float* dsf;              // [N][HV][128][128] or null (zeros)
+  float *dqv, *dkv;              // workspace [T][HV][8 slices][128]: per-slice partials
+  float *dalpha_part, *dbeta_part;  // workspace [T][HV][8]
+  float* dv;                     // [T][HV][128] out
+  float* ds0;                    // [N][HV][128][128] or null
+  float* states;                 // workspace [T][HV][8 slices][2 rows][256 threads][4]: every state
+  float* errs;                   // workspace [T][HV][128]
 };
-hipError_t launch_bwd(const BwdArgs& a, float* dq, float* dk, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, float* dq, float* dk, float* dalpha, float* dbeta, hipStream_t s);
 
 // ---- QSA compressed indexer ----
 constexpr int kSelSeg = 16384;  // scores per select workgroup (1024 threads x 16)

@@ -7,13 +7,15 @@
 //   e = v - S~^T k             ->  dv = de,  dS~ = dS - k de^T,  dk -= S~ de
 //   S~ = alpha S_{t-1}         ->  dalpha = <S_{t-1}, dS~>,  dS_{t-1} = alpha dS~
 //
-// One workgroup per (sequence, value head), 256 threads, each holding an 8x8 tile of the 128x128
-// state: rows 8 ti .. 8 ti + 7, columns 8 tj .. 8 tj + 7 with ti = thread / 16, tj = thread % 16.
-// Row sums (over a row's columns) are 16-lane shuffles; column sums (over a column's rows) are
-// shuffles across the 4 row groups of a wave plus one LDS exchange across the 4 waves. A forward pass
-// stores every state S_t (fp32, each thread's tile contiguous) and every error e_t in the workspace;
-// the reverse pass reads them back, so every state it uses is the forward's own, with no inversion
-// of the update.
+// Each value column of the state evolves on its own (the columns share only k, alpha, beta), so a
+// (sequence, value head) chain is split into 8 slices of 16 columns, one workgroup each: 256 threads,
+// each holding a 2x4 tile (rows 2 ti, 2 ti + 1, slice columns 4 tj .. 4 tj + 3; ti = thread / 4,
+// tj = thread % 4). Column sums are shuffles across a wave's 16 row groups plus one LDS exchange across
+// the 4 waves; row sums are 4-lane shuffles and give per-slice partials of dq and dk (and of dalpha and
+// dbeta), which k_bwd_reduce adds over the slices and over the value heads that share a QK head.
+// A forward pass stores every state S_t (fp32, slot-major so that the stores coalesce) and every error
+// e_t in the workspace; the reverse pass reads them back, so every state it uses is the forward's own,
+// with no inversion of the update.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -22,249 +24,307 @@ namespace gdn {
 namespace {
 
 constexpr int kBD = 128;
-constexpr int kBT = 256;  // threads per workgroup
-constexpr int kTile = 64; // state entries per thread
+constexpr int kBT = 256;         // threads per workgroup
+constexpr int kSC = 16;          // columns per slice
+constexpr int kNS = kBD / kSC;   // slices per chain
+constexpr int kR = 2, kC = 4;    // a thread's tile: kR rows x kC columns
+constexpr int kTJ = kSC / kC;    // column tiles per slice (threads per row)
+static_assert((kBD / kR) * kTJ == kBT, "the tiles must cover the slice with 256 threads");
 
 struct BwdLds {
-  float col[2][4][kBD];   // column-sum exchange, double-buffered by token parity
+  float col[2][4][kSC];   // column-sum exchange, double-buffered by token parity
   float dal[2][4];        // per-wave dalpha partials, written one token and read at the next
 };
 
-// Column sums: part[c] is this thread's sum over its 8 rows for column 8 tj + c; returns the sum over
-// all 128 rows in every thread of the column. One barrier.
-__device__ __forceinline__ void col_sum(float (&part)[8], float (&full)[8], BwdLds& L, int buf) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, tj = t & 15;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    part[c] += __shfl_xor(part[c], 16, kWave);
-    part[c] += __shfl_xor(part[c], 32, kWave);
-  }
-  if (lane < 16)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) L.col[buf][w][8 * tj + c] = part[c];
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-    full[c] = L.col[buf][0][8 * tj + c] + L.col[buf][1][8 * tj + c] + L.col[buf][2][8 * tj + c] +
-              L.col[buf][3][8 * tj + c];
+// Workgroup barrier that waits only for this thread's LDS accesses (lgkmcnt(0)), not for its global
+// loads: __syncthreads would also drain the loads issued ahead for the next token (vmcnt(0)). The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // vmcnt 63, expcnt 7, lgkmcnt 0
+  asm volatile("s_barrier" ::: "memory");
 }
 
-// Row sums over the 16 column tiles (16 consecutive lanes).
-__device__ __forceinline__ float row_sum(float x) {
-  x += __shfl_xor(x, 1, kWave);
-  x += __shfl_xor(x, 2, kWave);
-  x += __shfl_xor(x, 4, kWave);
-  x += __shfl_xor(x, 8, kWave);
+__device__ __forceinline__ void col_sum(float (&part)[kC], float (&full)[kC], BwdLds& L, int buf) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, tj = t % kTJ;
+#pragma unroll
+  for (int c = 0; c < kC; ++c)
+#pragma unroll
+    for (int o = kTJ; o < 64; o <<= 1) part[c] += __shfl_xor(part[c], o, kWave);
+  if (lane < kTJ)
+#pragma unroll
+    for (int c = 0; c < kC; ++c) L.col[buf][w][kC * tj + c] = part[c];
+  lds_barrier();
+#pragma unroll
+  for (int c = 0; c < kC; ++c)
+    full[c] = L.col[buf][0][kC * tj + c] + L.col[buf][1][kC * tj + c] + L.col[buf][2][kC * tj + c] +
+              L.col[buf][3][kC * tj + c];
+}
+
+__device__ __forceinline__ float row_sum(float x) {  // over the column tiles of a slice
+#pragma unroll
+  for (int o = 1; o < kTJ; o <<= 1) x += __shfl_xor(x, o, kWave);
   return x;
 }
 
-__device__ __forceinline__ void ld8f(const float* p, float (&o)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+__device__ __forceinline__ void ld4f(const float* p, float (&o)[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
 }
-
-__device__ __forceinline__ void st8f(float* p, const float (&o)[8]) {
+__device__ __forceinline__ void st4f(float* p, const float (&o)[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(o[4], o[5], o[6], o[7]);
 }
 
-// A 128x128 fp32 matrix [row][col] <-> this thread's tile.
-__device__ __forceinline__ void ld_tile_mat(const float* m, float (&s)[8][8], int ti, int tj) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) ld8f(m + (8 * ti + r) * kBD + 8 * tj, s[r]);
+__device__ __forceinline__ void st2f(float* p, const float (&o)[kR]) {
+  *reinterpret_cast<float2*>(p) = make_float2(o[0], o[1]);
 }
-__device__ __forceinline__ void st_tile_mat(float* m, const float (&s)[8][8], int ti, int tj) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) st8f(m + (8 * ti + r) * kBD + 8 * tj, s[r]);
+__device__ __forceinline__ void ldr(const float* p, float (&o)[kR]) {  // kR = 2 consecutive floats
+  const float2 a = *reinterpret_cast<const float2*>(p);
+  o[0] = a.x; o[1] = a.y;
 }
-// Workspace copy of a state: each thread's 64 entries contiguous.
-__device__ __forceinline__ void st_tile_ws(float* p, const float (&s)[8][8]) {
+
+// A 128x128 fp32 matrix [row][col] <-> this thread's tile (rows kR ti .., columns col ..).
+__device__ __forceinline__ void ld_tile_mat(const float* m, float (&s)[kR][kC], int ti, int col) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) st8f(p + 8 * r, s[r]);
+  for (int r = 0; r < kR; ++r) ld4f(m + (kR * ti + r) * kBD + col, s[r]);
 }
-__device__ __forceinline__ void ld_tile_ws(const float* p, float (&s)[8][8]) {
+__device__ __forceinline__ void st_tile_mat(float* m, const float (&s)[kR][kC], int ti, int col) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) ld8f(p + 8 * r, s[r]);
+  for (int r = 0; r < kR; ++r) st4f(m + (kR * ti + r) * kBD + col, s[r]);
+}
+// Workspace copy of a slice state, slot-major: row r of thread t at (r * 256 + t) * 4, so each store or
+// load instruction of a wave covers 1 KB of consecutive bytes.
+__device__ __forceinline__ void st_tile_ws(float* p, const float (&s)[kR][kC]) {
+#pragma unroll
+  for (int r = 0; r < kR; ++r) st4f(p + (r * kBT + threadIdx.x) * kC, s[r]);
+}
+__device__ __forceinline__ void ld_tile_ws(const float* p, float (&s)[kR][kC]) {
+#pragma unroll
+  for (int r = 0; r < kR; ++r) ld4f(p + (r * kBT + threadIdx.x) * kC, s[r]);
+}
+
+__device__ __forceinline__ void zero(float (&s)[kR][kC]) {
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int c = 0; c < kC; ++c) s[r][c] = 0.f;
 }
 
 }  // namespace
 
+// grid: n_seqs * HV * kNS workgroups; workgroup (n, h, slice).
 __global__ void __launch_bounds__(kBT) k_bwd_d128(BwdArgs a) {
   __shared__ BwdLds L;
-  const int t = threadIdx.x, ti = t >> 4, tj = t & 15;
-  const int n = blockIdx.x / a.hv, h = blockIdx.x - n * a.hv, g = h * a.hk / a.hv;
+  const int t = threadIdx.x, ti = t / kTJ, tj = t % kTJ;
+  const int sl = blockIdx.x % kNS, chain = blockIdx.x / kNS;
+  const int n = chain / a.hv, h = chain - n * a.hv, g = h * a.hk / a.hv;
+  const int col = sl * kSC + kC * tj;  // first value column of this thread
   const int64_t s0 = min(max(int64_t(a.cu[n]), int64_t(0)), a.T);
   const int64_t s1 = min(max(int64_t(a.cu[n + 1]), s0), a.T);
   const int64_t HV = a.hv, HK = a.hk;
+  const int64_t chain_off = (int64_t(n) * HV + h) * kBD * kBD;
+  auto ws_state = [&](int64_t tok) { return a.states + ((tok * HV + h) * kNS + sl) * (kBT * kR * kC); };
 
-  float S[8][8];
-  if (a.s0)
-    ld_tile_mat(a.s0 + (int64_t(n) * HV + h) * kBD * kBD, S, ti, tj);
-  else
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) S[r][c] = 0.f;
+  float S[kR][kC];
+  if (a.s0) ld_tile_mat(a.s0 + chain_off, S, ti, col); else zero(S);
 
-  // ---- forward: store S_t and e_t ----
+  // ---- forward: store S_t and e_t; the next token's inputs load while this one is processed ----
   int buf = 0;
+  float kr[kR], vc[kC], al = 1.f, be = 0.f;
+  if (s0 < s1) {
+    ldr(a.k + (s0 * HK + g) * kBD + kR * ti, kr);
+    ld4f(a.v + (s0 * HV + h) * kBD + col, vc);
+    al = a.alpha[s0 * HV + h];
+    be = a.beta[s0 * HV + h];
+  }
   for (int64_t tok = s0; tok < s1; ++tok, buf ^= 1) {
-    float kr[8], vc[8], part[8], full[8];
-    ld8f(a.k + (tok * HK + g) * kBD + 8 * ti, kr);
-    ld8f(a.v + (tok * HV + h) * kBD + 8 * tj, vc);
-    const float al = a.alpha[tok * HV + h], be = a.beta[tok * HV + h];
+    const int64_t nx = min(tok + 1, s1 - 1);
+    float kn[kR], vn[kC];
+    ldr(a.k + (nx * HK + g) * kBD + kR * ti, kn);
+    ld4f(a.v + (nx * HV + h) * kBD + col, vn);
+    const float aln = a.alpha[nx * HV + h], ben = a.beta[nx * HV + h];
+    float part[kC], full[kC];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < kC; ++c) {
       float acc = 0.f;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) acc = fmaf(S[r][c], kr[r], acc);
+      for (int r = 0; r < kR; ++r) acc = fmaf(S[r][c], kr[r], acc);
       part[c] = al * acc;  // (S~^T k) partial, S~ = alpha S
     }
     col_sum(part, full, L, buf);
-    float e[8];
+    float e[kC];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) e[c] = vc[c] - full[c];
+    for (int c = 0; c < kC; ++c) e[c] = vc[c] - full[c];
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+    for (int r = 0; r < kR; ++r)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) S[r][c] = fmaf(be * kr[r], e[c], al * S[r][c]);
-    st_tile_ws(a.states + ((tok * HV + h) * kBT + t) * kTile, S);
-    if (ti == 0) st8f(a.errs + (tok * HV + h) * kBD + 8 * tj, e);
+      for (int c = 0; c < kC; ++c) S[r][c] = fmaf(be * kr[r], e[c], al * S[r][c]);
+    st_tile_ws(ws_state(tok), S);
+    if (ti == 0) st4f(a.errs + (tok * HV + h) * kBD + col, e);
+#pragma unroll
+    for (int i = 0; i < kR; ++i) kr[i] = kn[i];
+#pragma unroll
+    for (int i = 0; i < kC; ++i) vc[i] = vn[i];
+    al = aln;
+    be = ben;
   }
   __threadfence();
   __syncthreads();
 
   // ---- reverse ----
-  float dS[8][8];
-  if (a.dsf)
-    ld_tile_mat(a.dsf + (int64_t(n) * HV + h) * kBD * kBD, dS, ti, tj);
-  else
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dS[r][c] = 0.f;
-  // S holds S_{s1-1} (the final state)
+  // Iteration t holds P = S_{t-1} and works on token t; it also loads S_{t-2} and token t-1's inputs
+  // for the next iteration, and computes token t-1's dq = scale S_{t-1} dy_{t-1} from the P it holds.
+  // The last token's dq uses S itself.
+  float dS[kR][kC];
+  if (a.dsf) ld_tile_mat(a.dsf + chain_off, dS, ti, col); else zero(dS);
   int64_t pending = -1;  // token whose dalpha partials wait in L.dal[pbuf]
   int pbuf = 0;
-  for (int64_t tok = s1 - 1; tok >= s0; --tok, buf ^= 1) {
-    float P[8][8];  // S_{t-1}
-    if (tok > s0)
-      ld_tile_ws(a.states + (((tok - 1) * HV + h) * kBT + t) * kTile, P);
-    else if (a.s0)
-      ld_tile_mat(a.s0 + (int64_t(n) * HV + h) * kBD * kBD, P, ti, tj);
-    else
+  const int64_t part_stride = kNS;  // per-slice partials: [T][HV][kNS][...]
+  if (s1 > s0) {
+    struct TokIn {
+      float q[kR], k[kR], dy[kC], e[kC], al, be;
+    };
+    auto load_in = [&](int64_t tk, TokIn& x) {
+      ldr(a.q + (tk * HK + g) * kBD + kR * ti, x.q);
+      ldr(a.k + (tk * HK + g) * kBD + kR * ti, x.k);
+      ld4f(a.dy + (tk * HV + h) * kBD + col, x.dy);
+      ld4f(a.errs + (tk * HV + h) * kBD + col, x.e);
+      x.al = a.alpha[tk * HV + h];
+      x.be = a.beta[tk * HV + h];
+    };
+    auto load_state = [&](int64_t tk, float (&st)[kR][kC]) {  // S_tk; tk = s0 - 1 is the initial state
+      if (tk >= s0) ld_tile_ws(ws_state(tk), st);
+      else if (a.s0) ld_tile_mat(a.s0 + chain_off, st, ti, col);
+      else zero(st);
+    };
+    auto store_dq = [&](int64_t tk, const float (&src)[kR][kC], const float (&dy4)[kC]) {
+      float dq[kR];
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
+      for (int r = 0; r < kR; ++r) {
+        float acc = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) P[r][c] = 0.f;
-    float qr[8], kr[8], dyc[8], ec[8];
-    ld8f(a.q + (tok * HK + g) * kBD + 8 * ti, qr);
-    ld8f(a.k + (tok * HK + g) * kBD + 8 * ti, kr);
-    ld8f(a.dy + (tok * HV + h) * kBD + 8 * tj, dyc);
-    ld8f(a.errs + (tok * HV + h) * kBD + 8 * tj, ec);
-    const float al = a.alpha[tok * HV + h], be = a.beta[tok * HV + h];
-    // y_t = scale S_t^T q_t
-    float dq[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        acc = fmaf(S[r][c], dyc[c], acc);
-        dS[r][c] = fmaf(a.scale * qr[r], dyc[c], dS[r][c]);
+        for (int c = 0; c < kC; ++c) acc = fmaf(src[r][c], dy4[c], acc);
+        dq[r] = row_sum(a.scale * acc);
       }
-      dq[r] = a.scale * acc;
-    }
-    // de = beta dS^T k (column sums)
-    float part[8], dsk[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float acc = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) acc = fmaf(dS[r][c], kr[r], acc);
-      part[c] = acc;
-    }
-    col_sum(part, dsk, L, buf);
-    if (t == 0 && pending >= 0)
-      a.dalpha[pending * HV + h] = L.dal[pbuf][0] + L.dal[pbuf][1] + L.dal[pbuf][2] + L.dal[pbuf][3];
-    float de[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) de[c] = be * dsk[c];
-    if (ti == 0) {
-      float db = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) db = fmaf(dsk[c], ec[c], db);
-      db = row_sum(db);
-      if (t == 0) a.dbeta[tok * HV + h] = db;
-      st8f(a.dv + (tok * HV + h) * kBD + 8 * tj, de);
-    }
-    // dk = beta dS e - alpha S_{t-1} de;  dS~ = dS - k de^T;  dalpha = <S_{t-1}, dS~>;  dS = alpha dS~
-    float dk[8], dal = 0.f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float x = 0.f, y = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        x = fmaf(dS[r][c], ec[c], x);
-        y = fmaf(P[r][c], de[c], y);
-        const float dst = fmaf(-kr[r], de[c], dS[r][c]);
-        dal = fmaf(P[r][c], dst, dal);
-        dS[r][c] = al * dst;
+      if (tj == 0) st2f(a.dqv + ((tk * HV + h) * part_stride + sl) * kBD + kR * ti, dq);
+    };
+    // One token: P = S_{tok-1}, x its inputs. Loads token tok-1's inputs, then S_{tok-2}, in that
+    // order, so that the dq of token tok-1 at the end waits only for the inputs.
+    auto step = [&](int64_t tok, float (&P)[kR][kC], float (&Pn)[kR][kC], const TokIn& x, TokIn& nx) {
+      const bool more = tok > s0;
+      if (more) {
+        load_in(tok - 1, nx);
+        load_state(tok - 2, Pn);
       }
-      dk[r] = be * x - al * y;
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+#pragma unroll
+        for (int c = 0; c < kC; ++c) dS[r][c] = fmaf(a.scale * x.q[r], x.dy[c], dS[r][c]);
+      float part[kC], dsk[kC];
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) acc = fmaf(dS[r][c], x.k[r], acc);
+        part[c] = acc;
+      }
+      col_sum(part, dsk, L, buf);
+      if (t == 0 && pending >= 0)
+        a.dalpha_part[(pending * HV + h) * kNS + sl] = L.dal[pbuf][0] + L.dal[pbuf][1] + L.dal[pbuf][2] + L.dal[pbuf][3];
+      float de[kC];
+#pragma unroll
+      for (int c = 0; c < kC; ++c) de[c] = x.be * dsk[c];
+      if (ti == 0) {
+        float db = 0.f;
+#pragma unroll
+        for (int c = 0; c < kC; ++c) db = fmaf(dsk[c], x.e[c], db);
+        db = row_sum(db);
+        if (t == 0) a.dbeta_part[(tok * HV + h) * kNS + sl] = db;
+        st4f(a.dv + (tok * HV + h) * kBD + col, de);
+      }
+      float dk[kR], dal = 0.f;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        float u = 0.f, y = 0.f;
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+          u = fmaf(dS[r][c], x.e[c], u);
+          y = fmaf(P[r][c], de[c], y);
+          const float dst = fmaf(-x.k[r], de[c], dS[r][c]);
+          dal = fmaf(P[r][c], dst, dal);
+          dS[r][c] = x.al * dst;
+        }
+        dk[r] = row_sum(x.be * u - x.al * y);
+      }
+      if (tj == 0) st2f(a.dkv + ((tok * HV + h) * part_stride + sl) * kBD + kR * ti, dk);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) dal += __shfl_xor(dal, o, kWave);
+      if ((t & 63) == 0) L.dal[buf][t >> 6] = dal;
+      pending = tok;
+      pbuf = buf;
+      buf ^= 1;
+      if (more) store_dq(tok - 1, P, nx.dy);  // dq_{tok-1} = scale S_{tok-1} dy_{tok-1}
+    };
+    TokIn A, B;
+    float P0[kR][kC], P1[kR][kC];
+    load_in(s1 - 1, A);
+    store_dq(s1 - 1, S, A.dy);  // the last token's dq from the final state
+    load_state(s1 - 2, P0);
+    // two tokens per trip with the register sets swapped, so no copy waits on a load in flight
+    for (int64_t tok = s1 - 1; tok >= s0; tok -= 2) {
+      step(tok, P0, P1, A, B);
+      if (tok - 1 >= s0) step(tok - 1, P1, P0, B, A);
     }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      dq[r] = row_sum(dq[r]);
-      dk[r] = row_sum(dk[r]);
-    }
-    if (tj == 0) {
-      st8f(a.dqv + (tok * HV + h) * kBD + 8 * ti, dq);
-      st8f(a.dkv + (tok * HV + h) * kBD + 8 * ti, dk);
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) dal += __shfl_xor(dal, o, kWave);
-    if ((t & 63) == 0) L.dal[buf][t >> 6] = dal;
-    pending = tok;
-    pbuf = buf;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) S[r][c] = P[r][c];
   }
   __syncthreads();
   if (t == 0 && pending >= 0)
-    a.dalpha[pending * HV + h] = L.dal[pbuf][0] + L.dal[pbuf][1] + L.dal[pbuf][2] + L.dal[pbuf][3];
-  if (a.ds0) st_tile_mat(a.ds0 + (int64_t(n) * HV + h) * kBD * kBD, dS, ti, tj);
+    a.dalpha_part[(pending * HV + h) * kNS + sl] = L.dal[pbuf][0] + L.dal[pbuf][1] + L.dal[pbuf][2] + L.dal[pbuf][3];
+  if (a.ds0) st_tile_mat(a.ds0 + chain_off, dS, ti, col);
 }
 
-// dq, dk per QK head: the sum over the value heads that read it.
-__global__ void __launch_bounds__(256) k_bwd_group_sum(int64_t T, int hk, int hv, const float* __restrict__ dqv,
-                                                       const float* __restrict__ dkv, float* __restrict__ dq,
-                                                       float* __restrict__ dk) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;  // over T * hk * 128
-  if (i >= T * hk * kBD) return;
-  const int64_t tok = i / (int64_t(hk) * kBD);
-  const int rem = int(i - tok * hk * kBD), gq = rem / kBD, d = rem - gq * kBD;
-  const int per = hv / hk;
-  float sq = 0.f, sk = 0.f;
-  for (int u = 0; u < per; ++u) {
-    const int64_t j = (tok * hv + gq * per + u) * kBD + d;
-    sq += dqv[j];
-    sk += dkv[j];
+// dq, dk per QK head: the sum over the slices and over the value heads that read it; dalpha, dbeta:
+// the sum over the slices.
+__global__ void __launch_bounds__(256) k_bwd_reduce(int64_t T, int hk, int hv, const float* __restrict__ dqv,
+                                                    const float* __restrict__ dkv, const float* __restrict__ dap,
+                                                    const float* __restrict__ dbp, float* __restrict__ dq,
+                                                    float* __restrict__ dk, float* __restrict__ dalpha,
+                                                    float* __restrict__ dbeta) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t nq = T * hk * kBD;
+  if (i < nq) {
+    const int64_t tok = i / (int64_t(hk) * kBD);
+    const int rem = int(i - tok * hk * kBD), gq = rem / kBD, d = rem - gq * kBD;
+    const int per = hv / hk;
+    float sq = 0.f, sk = 0.f;
+    for (int u = 0; u < per; ++u)
+#pragma unroll
+      for (int sl = 0; sl < kNS; ++sl) {
+        const int64_t j = ((tok * hv + gq * per + u) * kNS + sl) * kBD + d;
+        sq += dqv[j];
+        sk += dkv[j];
+      }
+    dq[i] = sq;
+    dk[i] = sk;
+  } else if (i < nq + T * hv) {
+    const int64_t j = i - nq;  // (tok, h)
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kNS; ++sl) {
+      sa += dap[j * kNS + sl];
+      sb += dbp[j * kNS + sl];
+    }
+    dalpha[j] = sa;
+    dbeta[j] = sb;
   }
-  dq[i] = sq;
-  dk[i] = sk;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, float* dq, float* dk, hipStream_t s) {
+hipError_t launch_bwd(const BwdArgs& a, float* dq, float* dk, float* dalpha, float* dbeta, hipStream_t s) {
   if (a.n_seqs == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bwd_d128, dim3(static_cast<unsigned>(a.n_seqs * a.hv)), dim3(kBT), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_d128, dim3(static_cast<unsigned>(a.n_seqs * a.hv * kNS)), dim3(kBT), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.hv == a.hk || a.T == 0) return e;
-  const int64_t n = a.T * a.hk * kBD;
-  hipLaunchKernelGGL(k_bwd_group_sum, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a.T, a.hk, a.hv,
-                     a.dqv, a.dkv, dq, dk);
+  if (e != hipSuccess || a.T == 0) return e;
+  const int64_t n = a.T * a.hk * kBD + a.T * a.hv;
+  hipLaunchKernelGGL(k_bwd_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a.T, a.hk, a.hv,
+                     a.dqv, a.dkv, a.dalpha_part, a.dbeta_part, dq, dk, dalpha, dbeta);
   return hipGetLastError();
 }
 
