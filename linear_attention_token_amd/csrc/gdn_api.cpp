@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <string.h>
 
-#include "gdn_internal.h"
+#include "ext_internal.h"
 
 namespace gdn {
 

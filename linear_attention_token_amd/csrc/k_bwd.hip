@@ -17,7 +17,7 @@
 // e_t in the workspace; the reverse pass reads them back, so every state it uses is the forward's own,
 // with no inversion of the update.
 #include "gdn_device.h"
-#include "gdn_internal.h"
+#include "ext_internal.h"
 
 namespace gdn {
 

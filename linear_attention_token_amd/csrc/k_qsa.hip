@@ -23,7 +23,7 @@
 #include <math.h>
 
 #include "gdn_device.h"
-#include "gdn_internal.h"
+#include "ext_internal.h"
 
 namespace gdn {
 
