@@ -5,5 +5,6 @@ from .gdn_oracle import (  # noqa: F401
     zero_centred_rmsnorm, gdn_chain, prefill_chain, conv_tail, gdn_prefill, gdn_decode,
     gdn_verify, gdn_commit, softplus, gate_alpha_beta, in_projection, out_projection,
     QSA_BLOCK, QSA_TOPK, partial_rope, qsa_compress, qsa_scores, qsa_select,
-    gated_delta_rule_backward, recurrence_layer, recurrence_layer_backward,
+    gated_delta_rule_backward, recurrence_layer, recurrence_layer_backward, gdn_chain_backward,
+    gdn_prefill_backward,
 )

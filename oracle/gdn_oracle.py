@@ -261,6 +261,114 @@ def gdn_chain(xq, xk, xv, wq, wk, wv, hq, hk_, hv_, alpha, beta, gate, norm_w, S
     return o, S
 
 
+def gdn_chain_backward(xq, xk, xv, wq, wk, wv, hq, hk_, hv_, alpha, beta, gate, norm_w, S0, do, dS_final=None,
+                       *, scale=1.0, l2_eps=1e-6, norm_eps=1e-6):
+    """Reverse-mode derivatives of gdn_chain with every step on, for one (sequence, value head) chain:
+    given dL/do (do [L, d_v]) and dL/dS_final, returns a dict of the derivatives for xq, xk, xv, wq, wk,
+    wv, hq, hk, hv, alpha, beta, gate, norm_w and S0. Each step of the forward is taken last to first:
+      o = n * sigmoid(gate)              ->  dn = do * s,  dgate = do * n * s (1 - s)
+      n = y / r * (1 + w),  r = sqrt(mean(y^2) + eps)
+                                         ->  dw = sum_t dn * y / r,
+                                             dy = (1 + w) dn / r - y <(1 + w) dn, y> / (d_v r^3)
+      the recurrence                     ->  gated_delta_rule_backward
+      a = a0 / sqrt(|a0|^2 + eps)        ->  da0 = (da - a <a, da>) / sqrt(|a0|^2 + eps)
+      a0 = silu(u)                       ->  du = da0 * sigmoid(u) (1 + u (1 - sigmoid(u)))
+      u[t] = sum_j w[:, j] x[t - 3 + j]  ->  dx[t - 3 + j] += w[:, j] du[t],  dw[:, j] = sum_t du[t] x[t - 3 + j]
+    (the history rows are x[-3..-1])."""
+    xq, xk, xv, do = _f64(xq), _f64(xk), _f64(xv), _f64(do)
+    L = xv.shape[0]
+    u = {}
+    pre = {}
+    act = {}
+    for name, x, w, hst in (("q", xq, wq, hq), ("k", xk, wk, hk_), ("v", xv, wv, hv_)):
+        u[name] = short_conv(x, w, hst)
+        pre[name] = silu(u[name])
+    act["q"] = l2_normalize(pre["q"], l2_eps)
+    act["k"] = l2_normalize(pre["k"], l2_eps)
+    act["v"] = pre["v"]
+    y, _ = gated_delta_rule(act["q"], act["k"], act["v"], alpha, beta, S0, scale)
+    d_v = y.shape[1]
+    r = np.sqrt(np.mean(y * y, axis=1, keepdims=True) + norm_eps)
+    n = y / r * (1.0 + norm_w)
+    sg = sigmoid(gate)
+    dn = do * sg
+    out = {"gate": do * n * sg * (1.0 - sg), "norm_w": np.sum(dn * y / r, axis=0)}
+    g1 = (1.0 + norm_w) * dn
+    dy = g1 / r - y * np.sum(g1 * y, axis=1, keepdims=True) / (d_v * r ** 3)
+    dq_a, dk_a, dv_a, out["alpha"], out["beta"], out["S0"] = gated_delta_rule_backward(
+        act["q"], act["k"], act["v"], alpha, beta, S0, dy, dS_final, scale)
+    dact = {"q": dq_a, "k": dk_a, "v": dv_a}
+    for name in ("q", "k"):
+        a0 = pre[name]
+        inv = 1.0 / np.sqrt(np.sum(a0 * a0, axis=1, keepdims=True) + l2_eps)
+        a = a0 * inv
+        dact[name] = (dact[name] - a * np.sum(a * dact[name], axis=1, keepdims=True)) * inv
+    for name, x, w, hst in (("q", xq, wq, hq), ("k", xk, wk, hk_), ("v", xv, wv, hv_)):
+        sgu = sigmoid(u[name])
+        du = dact[name] * sgu * (1.0 + u[name] * (1.0 - sgu))
+        xx = np.concatenate([_f64(hst), x], axis=0)
+        dxx = np.zeros_like(xx)
+        dw = np.zeros_like(_f64(w))
+        for j in range(CONV_WIDTH):
+            dxx[j:j + L] += _f64(w)[:, j][None, :] * du
+            dw[:, j] = np.sum(du * xx[j:j + L], axis=0)
+        out["x" + name], out["h" + name], out["w" + name] = dxx[CONV_WIDTH - 1:], dxx[:CONV_WIDTH - 1], dw
+    return out
+
+
+def gdn_prefill_backward(inp, dout, dstate_out=None, *, scale=1.0, l2_eps=1e-6, norm_eps=1e-6):
+    """Derivatives of gdn_prefill (every step on) for a packed layer, given dL/dout [T, HV, d_v] and dL/dS_final
+    [N, HV, d_k, d_v] (None = 0). Returns a dict with q, k [T, HK, d_k], v [T, HV, d_v], alpha, beta [T, HV],
+    gate [T, HV, d_v], conv_w [C, 4], norm_w (the shape of inp's norm_w), state_in [N, HV, d_k, d_v] and
+    conv_in [N, 3, C]. A QK head's derivatives (its inputs, conv taps and conv history) are the sums over
+    the value heads that read it."""
+    cu = np.asarray(_f64(inp["cu_seqlens"]), dtype=np.int64)
+    q, k, v = _f64(inp["q"]), _f64(inp["k"]), _f64(inp["v"])
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    N = len(cu) - 1
+    C = 2 * hk * dk + hv * dv
+    conv_w = _f64(inp["conv_w"])
+    nw_all = _f64(inp["norm_w"])
+    st, ci = inp.get("state_in"), inp.get("conv_in")
+    do = _f64(dout)
+    res = {"q": np.zeros_like(q), "k": np.zeros_like(k), "v": np.zeros_like(v), "alpha": np.zeros((T, hv)),
+           "beta": np.zeros((T, hv)), "gate": np.zeros((T, hv, dv)), "conv_w": np.zeros((C, CONV_WIDTH)),
+           "norm_w": np.zeros_like(nw_all), "state_in": np.zeros((N, hv, dk, dv)),
+           "conv_in": np.zeros((N, CONV_WIDTH - 1, C))}
+    for n in range(N):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        ci_n = _f64(ci[n]) if ci is not None else np.zeros((CONV_WIDTH - 1, C))
+        for h in range(hv):
+            g = (h * hk) // hv
+            cq, ck, cv = _head_channels(h, g, hk, hv, dk, dv)
+            S0 = _f64(st[n, h]) if st is not None else np.zeros((dk, dv))
+            nw = nw_all if nw_all.ndim == 1 else nw_all[h]
+            dsf = None if dstate_out is None else _f64(dstate_out)[n, h]
+            r = gdn_chain_backward(q[s0:s1, g], k[s0:s1, g], v[s0:s1, h], conv_w[cq], conv_w[ck], conv_w[cv],
+                                   ci_n[:, cq], ci_n[:, ck], ci_n[:, cv], _f64(inp["alpha"][s0:s1, h]),
+                                   _f64(inp["beta"][s0:s1, h]), _f64(inp["gate"][s0:s1, h]), nw, S0,
+                                   do[s0:s1, h], dsf, scale=scale, l2_eps=l2_eps, norm_eps=norm_eps)
+            res["q"][s0:s1, g] += r["xq"]
+            res["k"][s0:s1, g] += r["xk"]
+            res["v"][s0:s1, h] += r["xv"]
+            res["alpha"][s0:s1, h] = r["alpha"]
+            res["beta"][s0:s1, h] = r["beta"]
+            res["gate"][s0:s1, h] = r["gate"]
+            res["conv_w"][cq] += r["wq"]
+            res["conv_w"][ck] += r["wk"]
+            res["conv_w"][cv] += r["wv"]
+            if nw_all.ndim == 1:
+                res["norm_w"] += r["norm_w"]
+            else:
+                res["norm_w"][h] += r["norm_w"]
+            res["state_in"][n, h] = r["S0"]
+            res["conv_in"][n][:, cq] += r["hq"]
+            res["conv_in"][n][:, ck] += r["hk"]
+            res["conv_in"][n][:, cv] += r["hv"]
+    return res
+
+
 def prefill_chain(inp, n, h, *, flags=FLAG_ALL, scale=1.0, l2_eps=1e-6, norm_eps=1e-6,
                   state_in=None, conv_in=None):
     """Run one (sequence n, value head h) chain of a packed prefill.

@@ -84,3 +84,36 @@ def test_frozen_state_closed_form():
     assert np.allclose(dq, dy @ S0.T, rtol=1e-13)
     assert np.allclose(dS0, q.T @ dy + dSf, rtol=1e-13)
     assert np.all(dkk == 0) and np.all(dvv == 0)
+
+
+def test_mixer_backward_matches_finite_differences():
+    """The whole mixer (conv + SiLU, L2, recurrence, RMSNorm, gate) over a packed two-sequence layer with
+    one QK head read by two value heads, conv history and initial states: every partial derivative of
+    L = sum dout . o + <dS, S_final> by central differences of the oracle's gdn_prefill."""
+    rng = np.random.default_rng(24)
+    cu = np.array([0, 3, 8])
+    T, hk, hv, d = 8, 1, 2, 4
+    C = 2 * hk * d + hv * d
+    inp = {"cu_seqlens": cu, "q": rng.standard_normal((T, hk, d)), "k": rng.standard_normal((T, hk, d)),
+           "v": rng.standard_normal((T, hv, d)), "alpha": rng.uniform(0.5, 1, (T, hv)),
+           "beta": rng.uniform(0.1, 1, (T, hv)), "gate": rng.standard_normal((T, hv, d)),
+           "conv_w": 0.5 * rng.standard_normal((C, 4)), "norm_w": 0.2 * rng.standard_normal(d),
+           "state_in": 0.3 * rng.standard_normal((2, hv, d, d)), "conv_in": rng.standard_normal((2, 3, C))}
+    dout, dS = rng.standard_normal((T, hv, d)), rng.standard_normal((2, hv, d, d))
+
+    def loss(x):
+        o, S, _ = O.gdn_prefill(x)
+        return float(np.sum(dout * o) + np.sum(dS * S))
+
+    got = O.gdn_prefill_backward(inp, dout, dS)
+    h = 1e-6
+    for name in ("q", "k", "v", "alpha", "beta", "gate", "conv_w", "norm_w", "state_in", "conv_in"):
+        x = inp[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = dict(inp), dict(inp)
+            xp[name], xm[name] = x.copy(), x.copy()
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        assert np.allclose(got[name], fd, rtol=1e-5, atol=1e-7), name
