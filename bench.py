@@ -151,27 +151,25 @@ def cpu_baseline(max_tokens: int):
 
 
 def backward_leg(args, dev, stream):
-    """Recurrence backward at model shape (16 QK / 48 value heads, d = 128, fp32), one sequence: the
-    forward keeps every state (64 KB per token and value head) and the reverse pass reads them back."""
+    """Backward of the whole mixer (conv + SiLU, L2, recurrence, RMSNorm, gate) at model shape (16 QK / 48
+    value heads, d = 128, fp32), one sequence: the recurrence's forward keeps every state (64 KB per token
+    and value head) and its reverse pass reads them back."""
     import torch
     from linear_attention_token_amd import gdn
+    from workloads import prefill_inputs
 
     T = args.bwd_tokens
+    inp = prefill_inputs([T], n_qk_heads=HK, n_v_heads=HV, d_k=D, d_v=D, io_dtype=torch.float32, seed=11,
+                         device=dev)
     g = torch.Generator(device=dev)
-    g.manual_seed(11)
-    f = torch.float32
-    q = torch.nn.functional.normalize(torch.randn(T, HK, D, generator=g, device=dev), dim=-1)
-    k = torch.nn.functional.normalize(torch.randn(T, HK, D, generator=g, device=dev), dim=-1)
-    v = torch.randn(T, HV, D, generator=g, device=dev)
-    alpha = torch.exp(torch.log(torch.tensor(0.9, device=dev)) * torch.rand(T, HV, generator=g, device=dev))
-    beta = torch.sigmoid(torch.randn(T, HV, generator=g, device=dev))
-    dy = torch.randn(T, HV, D, generator=g, device=dev)
-    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
-    cfg = gdn.cfg_for(HK, HV, D, D, f)
-    ws = torch.empty(gdn.gdn_recurrence_backward_workspace(cfg, 1, T), dtype=torch.uint8, device=dev)
+    g.manual_seed(12)
+    dout = torch.randn(T, HV, D, generator=g, device=dev)
+    cfg = gdn.cfg_for(HK, HV, D, D, torch.float32)
+    ws = torch.empty(gdn.gdn_backward_workspace(cfg, 1, T), dtype=torch.uint8, device=dev)
 
     def step():
-        gdn.gdn_recurrence_backward(cfg, cu, q, k, v, alpha, beta, dy, workspace=ws)
+        gdn.gdn_backward(cfg, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.gate, inp.conv_w,
+                         inp.norm_w, dout, workspace=ws)
 
     step()
     torch.cuda.synchronize()
@@ -183,19 +181,21 @@ def backward_leg(args, dev, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    io_bytes = 4 * T * (2 * 2 * HK * D + 3 * HV * D + 4 * HV) + 4 * HV * D * D  # in + out, once each
-    spill = 2 * 4 * T * HV * D * D + 2 * 4 * T * HV * D  # states and errors written, then read back
+    C = 2 * HK * D + HV * D
+    # inputs (q, k, v, alpha, beta, gate, dout) read once, their derivatives written once, fp32
+    io_bytes = 2 * 4 * T * (C + 2 * HV + HV * D + HV * D // 2)
+    spill = 2 * 4 * T * HV * D * D  # the kept states, written then read back
     gb = (io_bytes + spill) / (ms * 1e-3) / 1e9
     del ws
     torch.cuda.empty_cache()
     return {
-        "workload": f"recurrence backward, B=1, T={T}, 16 QK / 48 value heads, d=128, fp32: dq, dk, dv, dalpha, "
-                    f"dbeta, dS0 from dy",
+        "workload": f"mixer backward, B=1, T={T}, 16 QK / 48 value heads, d=128, fp32, every step on: derivatives "
+                    f"for q, k, v, alpha, beta, gate, conv weights and norm gain from dout",
         "ms_per_call": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
         "roofline": dict(bound="hbm", achieved=round(gb, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                          frac=round(gb / HBM_PEAK_GBPS, 4), algorithmic_bytes=io_bytes, state_bytes=spill,
                          note="achieved counts the kept states (written once, read once) with the inputs and "
-                              "outputs; one workgroup per (sequence, value head) runs token by token"),
+                              "outputs; the recurrence runs token by token per (sequence, head, 16-column slice)"),
     }
 
 

@@ -247,6 +247,29 @@ gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t t
                                    float* dbeta, float* dstate_in, void* workspace, size_t workspace_bytes,
                                    void* hip_stream);
 
+/* Backward of the whole mixer (every step on: conv + SiLU, L2, recurrence, RMSNorm, gate), for
+ * training: given dL/dout and dL/dS_final, the derivatives for every input of gdn_prefill. fp32 io,
+ * d_k = d_v = 128, cfg->flags = GDN_ALL, one shared norm gain (norm_head_stride 0).
+ *   q, k, v, alpha, beta, gate, conv_w, norm_w, state_in (NULL = zeros), conv_in (NULL = zeros): as for
+ *                   gdn_prefill, rows contiguous ([T][HK][128], [T][HV][128]).
+ *   dout            fp32 [T][HV][128]: dL/dout.   dstate_out: fp32 [N][HV][128][128] or NULL (zeros).
+ *   dq, dk          fp32 [T][HK][128] out (raw inputs; a QK head collects every value head reading it);
+ *   dv, dgate       fp32 [T][HV][128] out;  dalpha, dbeta fp32 [T][HV] out;
+ *   dconv_w         fp32 [C_tot][4] out;  dnorm_w fp32 [128] out;
+ *   dstate_in       fp32 [N][HV][128][128] out or NULL;  dconv_in fp32 [N][3][C_tot] out or NULL.
+ *   workspace       gdn_backward_workspace() bytes, 256-byte aligned (about 64 KB per token and value
+ *                   head, for the kept states).
+ * dconv_w and dnorm_w are sums over tokens accumulated with atomics, so their last bits can vary
+ * between runs; every other output is reproducible. */
+gdn_status gdn_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, size_t* bytes);
+gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, const int32_t* cu_seqlens,
+                        const float* q, const float* k, const float* v, const float* alpha, const float* beta,
+                        const float* gate, const float* conv_w, const float* norm_w, const float* state_in,
+                        const float* conv_in, const float* dout, const float* dstate_out, float* dq, float* dk,
+                        float* dv, float* dalpha, float* dbeta, float* dgate, float* dconv_w, float* dnorm_w,
+                        float* dstate_in, float* dconv_in, void* workspace, size_t workspace_bytes,
+                        void* hip_stream);
+
 /* Stage timing for profilers (host-side, per calling thread). After this call, every gdn_prefill
  * on this thread records events[i] on its stream before stage i and events[GDN_N_STAGES] after the
  * last stage, for the stages

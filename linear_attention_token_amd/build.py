@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.cpp", "k_conv.hip", "k_seq.hip", "k_decode.hip", "k_mtp.hip", "k_proj.hip", "k_qsa.hip", "k_bwd.hip", "k_wy.hip", "k_state.hip",
+SOURCES = ["gdn_api.cpp", "k_conv.hip", "k_seq.hip", "k_decode.hip", "k_mtp.hip", "k_proj.hip", "k_qsa.hip", "k_bwd.hip", "k_bwd_mixer.hip", "k_wy.hip", "k_state.hip",
            "k_out.hip"]
 
 ARCH = "gfx950"

@@ -9,7 +9,10 @@ namespace gdn {
 
 // ---- recurrence backward (fp32, d = 128) ----
 // Each (sequence, value head) chain runs as 8 workgroups of 16 value columns.
+constexpr int kBwdForward = 1, kBwdReverse = 2, kBwdWriteY = 4;  // BwdArgs::mode bits
 struct BwdArgs {
+  int mode;                      // forward pass (keep states), reverse pass, y output in the forward
+  float* y;                      // [T][HV][128] raw recurrence output (kBwdWriteY)
   const int32_t* cu;
   int n_seqs;
   int64_t T;
@@ -28,6 +31,27 @@ struct BwdArgs {
   float* errs;                   // workspace [T][HV][128]
 };
 hipError_t launch_bwd(const BwdArgs& a, float* dq, float* dk, float* dalpha, float* dbeta, hipStream_t s);
+
+// The mixer's steps before the recurrence, backwards (conv + SiLU + L2), fp32, d = 128.
+struct BwdMixArgs {
+  const int32_t* cu;
+  int n_seqs;
+  int64_t T;
+  int hk, hv;
+  int64_t C;                    // 2 hk 128 + hv 128 conv channels
+  float l2_eps;
+  const float *q, *k, *v;       // raw inputs [T][HK][128], [T][HK][128], [T][HV][128]
+  const float* conv_w;          // [C][4]
+  const float* conv_in;         // [N][3][C] or null
+  const float *dqa, *dka, *dva; // dL/d(normalised q, k; activated v): [T][HK][128], [T][HK][128], [T][HV][128]
+  float* du;                    // workspace [T][C]: dL/d(conv output)
+  float *dq, *dk, *dv;          // out: dL/d(raw inputs)
+  float* dconv_w;               // out [C][4]
+  float* dconv_in;              // out [N][3][C] or null
+};
+hipError_t launch_norm_gate_bwd(int64_t rows, const float* y, const float* z, const float* dout, const float* norm_w,
+                                float eps, float* dy, float* dz, float* dnorm_w, hipStream_t s);
+hipError_t launch_mixer_input_bwd(const BwdMixArgs& m, hipStream_t s);
 
 // ---- QSA compressed indexer ----
 constexpr int kSelSeg = 16384;  // scores per select workgroup (1024 threads x 16)

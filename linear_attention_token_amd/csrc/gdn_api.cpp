@@ -567,6 +567,7 @@ gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t t
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
   char* w = static_cast<char*>(workspace);
   BwdArgs a{};
+  a.mode = kBwdForward | kBwdReverse;
   a.cu = cu_seqlens;
   a.n_seqs = n_seqs;
   a.T = total_tokens;
@@ -589,6 +590,130 @@ gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t t
   w += align256(sizeof(float) * th * 8);
   a.dbeta_part = reinterpret_cast<float*>(w);
   if (run(launch_bwd(a, dq, dk, dalpha, dbeta, static_cast<hipStream_t>(hip_stream)), "recurrence backward") != hipSuccess)
+    return GDN_E_HIP;
+  return GDN_OK;
+}
+
+// Workspace of the whole-mixer backward: the forward's normalised q/k/v, the recurrence backward's
+// regions, y and dy, the recurrence-input derivatives and the conv-output derivatives.
+static size_t mixer_bwd_workspace_bytes(const Problem& p, int64_t T) {
+  const size_t th = size_t(T) * p.hv, tk = size_t(T) * p.hk;
+  return align256(plan_workspace(p, nullptr).bytes) + bwd_workspace_bytes(T, p.hk, p.hv) +
+         2 * align256(sizeof(float) * th * 128) + 2 * align256(sizeof(float) * tk * 128) +
+         align256(sizeof(float) * th * 128) + align256(sizeof(float) * size_t(T) * size_t(p.C));
+}
+
+static gdn_status check_mixer_bwd(const gdn_cfg* cfg, int32_t n_seqs, int64_t T, Problem& p) {
+  gdn_status st = check_bwd(cfg, n_seqs, T, p);
+  if (st != GDN_OK) return st;
+  if (cfg->flags != GDN_ALL) return fail(GDN_E_UNSUPPORTED, "gdn_backward needs every step on (flags = GDN_ALL)");
+  if (cfg->norm_head_stride != 0) return fail(GDN_E_UNSUPPORTED, "gdn_backward needs one shared norm gain");
+  p.n_seqs = n_seqs;
+  p.T = T;
+  p.nc_max = T / kChunk + n_seqs;
+  return GDN_OK;
+}
+
+gdn_status gdn_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, size_t* bytes) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_mixer_bwd(cfg, n_seqs, total_tokens, p);
+  if (st != GDN_OK) return st;
+  if (!bytes) return fail(GDN_E_NULL, "bytes is NULL");
+  *bytes = mixer_bwd_workspace_bytes(p, total_tokens);
+  return GDN_OK;
+}
+
+gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, const int32_t* cu_seqlens,
+                        const float* q, const float* k, const float* v, const float* alpha, const float* beta,
+                        const float* gate, const float* conv_w, const float* norm_w, const float* state_in,
+                        const float* conv_in, const float* dout, const float* dstate_out, float* dq, float* dk,
+                        float* dv, float* dalpha, float* dbeta, float* dgate, float* dconv_w, float* dnorm_w,
+                        float* dstate_in, float* dconv_in, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
+  g_last_error[0] = 0;
+  Problem p{};
+  gdn_status st = check_mixer_bwd(cfg, n_seqs, total_tokens, p);
+  if (st != GDN_OK) return st;
+  if (n_seqs == 0) return GDN_OK;
+  if (!cu_seqlens || !conv_w || !norm_w || !dconv_w || !dnorm_w)
+    return fail(GDN_E_NULL, "cu_seqlens, conv_w, norm_w, dconv_w and dnorm_w are required");
+  if (total_tokens > 0 && (!q || !k || !v || !alpha || !beta || !gate || !dout || !dq || !dk || !dv || !dalpha ||
+                           !dbeta || !dgate))
+    return fail(GDN_E_NULL, "the inputs, dout and the gradient outputs are required");
+  const void* ptrs[] = {q, k, v, gate, conv_w, norm_w, state_in, conv_in, dout, dstate_out,
+                        dq, dk, dv, dgate, dconv_w, dnorm_w, dstate_in, dconv_in};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
+  if (!aligned4(alpha) || !aligned4(beta) || !aligned4(dalpha) || !aligned4(dbeta) || !aligned4(cu_seqlens))
+    return fail(GDN_E_ALIGN, "alpha, beta, dalpha, dbeta and cu_seqlens must be 4-byte aligned");
+  const size_t need = mixer_bwd_workspace_bytes(p, total_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char* w = static_cast<char*>(workspace);
+  const Workspace fws = plan_workspace(p, w);
+  w += align256(fws.bytes);
+  const size_t th = size_t(total_tokens) * p.hv, tk = size_t(total_tokens) * p.hk;
+  BwdArgs a{};
+  a.cu = cu_seqlens;
+  a.n_seqs = n_seqs;
+  a.T = total_tokens;
+  a.hk = p.hk;
+  a.hv = p.hv;
+  a.scale = p.scale;
+  a.q = static_cast<const float*>(fws.qhat);
+  a.k = static_cast<const float*>(fws.khat);
+  a.v = static_cast<const float*>(fws.vhat);
+  a.alpha = alpha; a.beta = beta; a.s0 = state_in; a.dsf = dstate_out; a.ds0 = dstate_in;
+  a.states = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 128 * 128);
+  a.errs = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 128);
+  a.dqv = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 8 * 128);
+  a.dkv = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 8 * 128);
+  a.dalpha_part = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 8);
+  a.dbeta_part = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 8);
+  float* y = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 128);
+  float* dy = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 128);
+  float* dqa = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * tk * 128);
+  float* dka = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * tk * 128);
+  float* dva = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * th * 128);
+  float* du = reinterpret_cast<float*>(w);
+  a.y = y;
+  a.dy = dy;
+  a.dv = dva;
+  const int64_t qrow = int64_t(p.hk) * 128, vrow = int64_t(p.hv) * 128;
+  BwdMixArgs m{};
+  m.cu = cu_seqlens;
+  m.n_seqs = n_seqs;
+  m.T = total_tokens;
+  m.hk = p.hk;
+  m.hv = p.hv;
+  m.C = p.C;
+  m.l2_eps = p.l2_eps;
+  m.q = q; m.k = k; m.v = v; m.conv_w = conv_w; m.conv_in = conv_in;
+  m.dqa = dqa; m.dka = dka; m.dva = dva; m.du = du;
+  m.dq = dq; m.dk = dk; m.dv = dv; m.dconv_w = dconv_w; m.dconv_in = dconv_in;
+  BwdArgs af = a, ar = a;
+  af.mode = kBwdForward | kBwdWriteY;
+  ar.mode = kBwdReverse;
+  if (run(launch_conv(p, cu_seqlens, q, k, v, qrow, qrow, vrow, conv_w, conv_in, fws, false, s), "backward conv") != hipSuccess ||
+      run(launch_bwd(af, dqa, dka, dalpha, dbeta, s), "backward forward pass") != hipSuccess ||
+      run(launch_norm_gate_bwd(int64_t(th), y, gate, dout, norm_w, p.norm_eps, dy, dgate, dnorm_w, s),
+          "backward norm and gate") != hipSuccess ||
+      run(launch_bwd(ar, dqa, dka, dalpha, dbeta, s), "backward recurrence") != hipSuccess ||
+      run(launch_mixer_input_bwd(m, s), "backward conv, SiLU, L2") != hipSuccess)
     return GDN_E_HIP;
   return GDN_OK;
 }

@@ -33,6 +33,7 @@ static_assert((kBD / kR) * kTJ == kBT, "the tiles must cover the slice with 256 
 
 struct BwdLds {
   float col[2][4][kSC];   // column-sum exchange, double-buffered by token parity
+  float coly[2][4][kSC];  // the same for y = S^T q (forward pass with y output)
   float dal[2][4];        // per-wave dalpha partials, written one token and read at the next
 };
 
@@ -44,7 +45,9 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+template <int which = 0>
 __device__ __forceinline__ void col_sum(float (&part)[kC], float (&full)[kC], BwdLds& L, int buf) {
+  float (*col)[4][kSC] = which == 0 ? L.col : L.coly;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, tj = t % kTJ;
 #pragma unroll
   for (int c = 0; c < kC; ++c)
@@ -52,12 +55,11 @@ __device__ __forceinline__ void col_sum(float (&part)[kC], float (&full)[kC], Bw
     for (int o = kTJ; o < 64; o <<= 1) part[c] += __shfl_xor(part[c], o, kWave);
   if (lane < kTJ)
 #pragma unroll
-    for (int c = 0; c < kC; ++c) L.col[buf][w][kC * tj + c] = part[c];
+    for (int c = 0; c < kC; ++c) col[buf][w][kC * tj + c] = part[c];
   lds_barrier();
 #pragma unroll
   for (int c = 0; c < kC; ++c)
-    full[c] = L.col[buf][0][kC * tj + c] + L.col[buf][1][kC * tj + c] + L.col[buf][2][kC * tj + c] +
-              L.col[buf][3][kC * tj + c];
+    full[c] = col[buf][0][kC * tj + c] + col[buf][1][kC * tj + c] + col[buf][2][kC * tj + c] + col[buf][3][kC * tj + c];
 }
 
 __device__ __forceinline__ float row_sum(float x) {  // over the column tiles of a slice
@@ -126,9 +128,11 @@ __global__ void __launch_bounds__(kBT) k_bwd_d128(BwdArgs a) {
 
   float S[kR][kC];
   if (a.s0) ld_tile_mat(a.s0 + chain_off, S, ti, col); else zero(S);
-
-  // ---- forward: store S_t and e_t; the next token's inputs load while this one is processed ----
+  const bool fwd = a.mode & kBwdForward, rev = a.mode & kBwdReverse, want_y = a.mode & kBwdWriteY;
   int buf = 0;
+  if (fwd) {
+
+  // ---- forward: store S_t and e_t (and y_t); the next token's inputs load while this one is processed ----
   float kr[kR], vc[kC], al = 1.f, be = 0.f;
   if (s0 < s1) {
     ldr(a.k + (s0 * HK + g) * kBD + kR * ti, kr);
@@ -160,6 +164,23 @@ __global__ void __launch_bounds__(kBT) k_bwd_d128(BwdArgs a) {
       for (int c = 0; c < kC; ++c) S[r][c] = fmaf(be * kr[r], e[c], al * S[r][c]);
     st_tile_ws(ws_state(tok), S);
     if (ti == 0) st4f(a.errs + (tok * HV + h) * kBD + col, e);
+    if (want_y) {  // y_t = scale S_t^T q_t (column sums)
+      float qq[kR], py[kC], fy[kC];
+      ldr(a.q + (tok * HK + g) * kBD + kR * ti, qq);
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) acc = fmaf(S[r][c], qq[r], acc);
+        py[c] = acc;
+      }
+      col_sum<1>(py, fy, L, buf);
+      if (ti == 0) {
+#pragma unroll
+        for (int c = 0; c < kC; ++c) fy[c] *= a.scale;
+        st4f(a.y + (tok * HV + h) * kBD + col, fy);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kR; ++i) kr[i] = kn[i];
 #pragma unroll
@@ -167,6 +188,8 @@ __global__ void __launch_bounds__(kBT) k_bwd_d128(BwdArgs a) {
     al = aln;
     be = ben;
   }
+  }  // forward
+  if (!rev) return;
   __threadfence();
   __syncthreads();
 
@@ -264,6 +287,7 @@ __global__ void __launch_bounds__(kBT) k_bwd_d128(BwdArgs a) {
       buf ^= 1;
       if (more) store_dq(tok - 1, P, nx.dy);  // dq_{tok-1} = scale S_{tok-1} dy_{tok-1}
     };
+    if (!fwd) load_state(s1 - 1, S);  // the final state, kept by an earlier forward launch
     TokIn A, B;
     float P0[kR][kC], P1[kR][kC];
     load_in(s1 - 1, A);
@@ -321,7 +345,7 @@ hipError_t launch_bwd(const BwdArgs& a, float* dq, float* dk, float* dalpha, flo
   if (a.n_seqs == 0) return hipSuccess;
   hipLaunchKernelGGL(k_bwd_d128, dim3(static_cast<unsigned>(a.n_seqs * a.hv * kNS)), dim3(kBT), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.T == 0) return e;
+  if (e != hipSuccess || a.T == 0 || !(a.mode & kBwdReverse)) return e;
   const int64_t n = a.T * a.hk * kBD + a.T * a.hv;
   hipLaunchKernelGGL(k_bwd_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a.T, a.hk, a.hv,
                      a.dqv, a.dkv, a.dalpha_part, a.dbeta_part, dq, dk, dalpha, dbeta);

@@ -22,7 +22,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_E_NULL", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE", 4: "
 EXPORTS = ("gdn_cfg_default", "gdn_prefill_workspace", "gdn_prefill", "gdn_decode_step",
            "gdn_verify_log_bytes", "gdn_verify", "gdn_commit",
            "gdn_proj_workspace", "gdn_in_proj", "gdn_out_proj",
-           "gdn_recurrence_backward_workspace", "gdn_recurrence_backward",
+           "gdn_recurrence_backward_workspace", "gdn_recurrence_backward", "gdn_backward_workspace", "gdn_backward",
            "gdn_set_stage_events", "gdn_status_string", "gdn_last_error", "gdn_abi_version")
 N_STAGES = 6
 STAGE_NAMES = ("chunk_table", "conv_silu_l2", "wy_or_sequential", "state", "output_norm_gate", "conv_tail")
@@ -394,6 +394,10 @@ def _declare_bwd(lib):
     lib.gdn_recurrence_backward.argtypes = [C, ctypes.c_int32, _I64] + [_P] * 16 + [ctypes.c_size_t, _P]
     lib.gdn_recurrence_backward_workspace.restype = ctypes.c_int
     lib.gdn_recurrence_backward.restype = ctypes.c_int
+    lib.gdn_backward_workspace.argtypes = [C, ctypes.c_int32, _I64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_backward.argtypes = [C, ctypes.c_int32, _I64] + [_P] * 24 + [ctypes.c_size_t, _P]
+    lib.gdn_backward_workspace.restype = ctypes.c_int
+    lib.gdn_backward.restype = ctypes.c_int
     lib._bwd_declared = True
 
 
@@ -432,6 +436,50 @@ def gdn_recurrence_backward(cfg: gdn_cfg, cu_seqlens, q, k, v, alpha, beta, dy, 
                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(ds0),
                                        _ptr(workspace), workspace.numel(), _stream(stream)))
     return dq, dk, dv, da, db, ds0
+
+
+def gdn_backward_workspace(cfg: gdn_cfg, n_seqs: int, total_tokens: int) -> int:
+    lib = load_library()
+    _declare_bwd(lib)
+    n = ctypes.c_size_t()
+    _check(lib.gdn_backward_workspace(ctypes.byref(cfg), n_seqs, total_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def gdn_backward(cfg: gdn_cfg, cu_seqlens, q, k, v, alpha, beta, gate, conv_w, norm_w, dout, state_in=None,
+                 conv_in=None, dstate_out=None, want_dstate_in=True, want_dconv_in=True, workspace=None,
+                 stream=None) -> dict:
+    """Derivatives of the whole mixer (fp32, d = 128, every step on) for every input of gdn_prefill; returns a
+    dict keyed like the inputs (q, k, v, alpha, beta, gate, conv_w, norm_w, state_in, conv_in)."""
+    lib = load_library()
+    _declare_bwd(lib)
+    n = int(cu_seqlens.numel()) - 1
+    T = int(q.shape[0])
+    hk, hv, d = cfg.n_qk_heads, cfg.n_v_heads, cfg.d_k
+    C = 2 * hk * d + hv * d
+    f = torch.float32
+    _expect(cu_seqlens, (n + 1,), torch.int32, "cu_seqlens")
+    for t, shape, name in ((q, (T, hk, d), "q"), (k, (T, hk, d), "k"), (v, (T, hv, d), "v"), (alpha, (T, hv), "alpha"),
+                           (beta, (T, hv), "beta"), (gate, (T, hv, d), "gate"), (conv_w, (C, 4), "conv_w"),
+                           (norm_w, (d,), "norm_w"), (dout, (T, hv, d), "dout")):
+        _expect(t, shape, f, name)
+    _expect(state_in, (n, hv, d, d), f, "state_in", optional=True)
+    _expect(conv_in, (n, 3, C), f, "conv_in", optional=True)
+    _expect(dstate_out, (n, hv, d, d), f, "dstate_out", optional=True)
+    dev = q.device
+    e = lambda *shape: torch.empty(shape, dtype=f, device=dev)
+    out = {"q": e(T, hk, d), "k": e(T, hk, d), "v": e(T, hv, d), "alpha": e(T, hv), "beta": e(T, hv),
+           "gate": e(T, hv, d), "conv_w": e(C, 4), "norm_w": e(d),
+           "state_in": e(n, hv, d, d) if want_dstate_in else None, "conv_in": e(n, 3, C) if want_dconv_in else None}
+    if workspace is None:
+        workspace = torch.empty(max(gdn_backward_workspace(cfg, n, T), 1), dtype=torch.uint8, device=dev)
+    _check(lib.gdn_backward(ctypes.byref(cfg), n, T, _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                            _ptr(beta), _ptr(gate), _ptr(conv_w), _ptr(norm_w), _ptr(state_in), _ptr(conv_in),
+                            _ptr(dout), _ptr(dstate_out), _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]),
+                            _ptr(out["alpha"]), _ptr(out["beta"]), _ptr(out["gate"]), _ptr(out["conv_w"]),
+                            _ptr(out["norm_w"]), _ptr(out["state_in"]), _ptr(out["conv_in"]), _ptr(workspace),
+                            workspace.numel(), _stream(stream)))
+    return out
 
 
 def cfg_for(n_qk_heads: int, n_v_heads: int, d_k: int, d_v: int, dtype: torch.dtype,

@@ -320,3 +320,27 @@ def test_recurrence_backward_rejects_bad_arguments():
     _err(bwd(da=A + 2), 4)
     _err(bwd(N=0), 2)
     assert bwd(N=0, T=0) == 0
+
+
+def test_mixer_backward_rejects_bad_arguments():
+    f32 = gdn.gdn_cfg_default(io_dtype=gdn.GDN_F32)
+    gdn._declare_bwd(lib)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_backward_workspace(ctypes.byref(f32), 1, 4096, ctypes.byref(n)) == 0
+    assert n.value >= 4096 * 48 * 128 * 128 * 4
+    _err(lib.gdn_backward_workspace(ctypes.byref(gdn.gdn_cfg_default(io_dtype=gdn.GDN_F32, flags=gdn.GDN_CONV)),
+                                    1, 64, ctypes.byref(n)), 6)
+    _err(lib.gdn_backward_workspace(ctypes.byref(gdn.gdn_cfg_default(io_dtype=gdn.GDN_F32, norm_head_stride=128)),
+                                    1, 64, ctypes.byref(n)), 6)
+    _err(lib.gdn_backward_workspace(ctypes.byref(gdn.gdn_cfg_default()), 1, 64, ctypes.byref(n)), 6)
+
+    def bwd(N=1, T=64, cu=A, q=A, dout=A, dconv_w=A, ws=A, wsb=1 << 40, gate=A):
+        return lib.gdn_backward(ctypes.byref(f32), N, T, cu, q, A, A, A, A, gate, A, A, None, None, dout, None,
+                                A, A, A, A, A, A, dconv_w, A, None, None, ws, wsb, None)
+
+    _err(bwd(dout=None), 1)
+    _err(bwd(gate=None), 1)
+    _err(bwd(dconv_w=None), 1)
+    _err(bwd(wsb=4096), 5)
+    _err(bwd(q=A + 8), 4)
+    assert bwd(N=0, T=0) == 0

@@ -75,3 +75,27 @@ def test_backward_model_shape_group():
                            ("dstate_in", ds0[0, h], r[5])):
             assert _rel(a, b) <= TOL, (name, h, _rel(a, b))
     assert _rel(dq[:, g], rq) <= TOL and _rel(dk[:, g], rk) <= TOL
+
+
+@pytest.mark.parametrize("lens,hk,hv,history", [([1, 5, 70, 0, 130], 2, 6, True), ([200], 1, 1, False)])
+def test_mixer_backward_matches_oracle(lens, hk, hv, history):
+    """gdn_backward (conv + SiLU, L2, recurrence, RMSNorm, gate) against the oracle's derivatives of the whole
+    mixer, every output element by element (rel-L2 <= 1e-4)."""
+    from workloads import prefill_inputs
+    inp = prefill_inputs(lens, n_qk_heads=hk, n_v_heads=hv, d_k=128, d_v=128, io_dtype=torch.float32, seed=41,
+                         s0_std=0.05 if history else 0.0, conv_in_std=1.0 if history else 0.0)
+    g = torch.Generator(device="cpu").manual_seed(42)
+    dout = torch.randn(sum(lens), hv, 128, generator=g)
+    dsf = 0.1 * torch.randn(len(lens), hv, 128, 128, generator=g)
+    cfg = gdn.cfg_for(hk, hv, 128, 128, torch.float32)
+    d = lambda t: None if t is None else t.to(DEV).contiguous()
+    si = inp.state_in if history else None
+    ci = inp.conv_in if history else None
+    got = gdn.gdn_backward(cfg, d(inp.cu_seqlens), d(inp.q), d(inp.k), d(inp.v), d(inp.alpha), d(inp.beta), d(inp.gate),
+                           d(inp.conv_w), d(inp.norm_w), d(dout), state_in=d(si), conv_in=d(ci), dstate_out=d(dsf))
+    torch.cuda.synchronize()
+    ref_in = {"cu_seqlens": inp.cu_seqlens, "q": inp.q, "k": inp.k, "v": inp.v, "alpha": inp.alpha, "beta": inp.beta,
+              "gate": inp.gate, "conv_w": inp.conv_w, "norm_w": inp.norm_w, "state_in": si, "conv_in": ci}
+    ref = O.gdn_prefill_backward(ref_in, dout, dsf)
+    for name in ("q", "k", "v", "alpha", "beta", "gate", "conv_w", "norm_w", "state_in", "conv_in"):
+        assert _rel(got[name], ref[name]) <= TOL, (name, _rel(got[name], ref[name]))
