@@ -33,7 +33,7 @@ static_assert((kBD / kR) * kTJ == kBT, "the tiles must cover the slice with 256 
 
 struct BwdLds {
   float col[2][4][kSC];   // column-sum exchange, double-buffered by token parity
-  float coly[2][4][kSC];  // the same for y = S^T q (forward pass with y output)
+  float coly[2][4][kSC + 4];  // forward pass with y output: S~^T q per column, and k.q
   float dal[2][4];        // per-wave dalpha partials, written one token and read at the next
 };
 
@@ -45,9 +45,42 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// The forward pass with y output exchanges S~^T q and k.q along with S~^T k (one barrier): y_t =
+// scale (S~^T q + beta e (k.q)) since S_t = S~ + beta k e^T.
+__device__ __forceinline__ void col_sum3(float (&part)[kC], float (&full)[kC], float (&party)[kC], float (&fully)[kC],
+                                         float& kq, BwdLds& L, int buf) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, tj = t % kTJ;
+#pragma unroll
+  for (int o = kTJ; o < 64; o <<= 1) {
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      part[c] += __shfl_xor(part[c], o, kWave);
+      party[c] += __shfl_xor(party[c], o, kWave);
+    }
+    kq += __shfl_xor(kq, o, kWave);
+  }
+  if (lane < kTJ) {
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      L.col[buf][w][kC * tj + c] = part[c];
+      L.coly[buf][w][kC * tj + c] = party[c];
+    }
+    if (tj == 0) L.coly[buf][w][kSC] = kq;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    full[c] = L.col[buf][0][kC * tj + c] + L.col[buf][1][kC * tj + c] + L.col[buf][2][kC * tj + c] +
+              L.col[buf][3][kC * tj + c];
+    fully[c] = L.coly[buf][0][kC * tj + c] + L.coly[buf][1][kC * tj + c] + L.coly[buf][2][kC * tj + c] +
+               L.coly[buf][3][kC * tj + c];
+  }
+  kq = L.coly[buf][0][kSC] + L.coly[buf][1][kSC] + L.coly[buf][2][kSC] + L.coly[buf][3][kSC];
+}
+
 template <int which = 0>
 __device__ __forceinline__ void col_sum(float (&part)[kC], float (&full)[kC], BwdLds& L, int buf) {
-  float (*col)[4][kSC] = which == 0 ? L.col : L.coly;
+  float (*col)[4][kSC] = L.col;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, tj = t % kTJ;
 #pragma unroll
   for (int c = 0; c < kC; ++c)
@@ -154,7 +187,24 @@ __global__ void __launch_bounds__(kBT) k_bwd_d128(BwdArgs a) {
       for (int r = 0; r < kR; ++r) acc = fmaf(S[r][c], kr[r], acc);
       part[c] = al * acc;  // (S~^T k) partial, S~ = alpha S
     }
-    col_sum(part, full, L, buf);
+    float fy[kC];
+    float kq = 0.f;
+    if (want_y) {  // y_t = scale (S~^T q + beta e (k.q)), exchanged with S~^T k
+      float qq[kR], py[kC];
+      ldr(a.q + (tok * HK + g) * kBD + kR * ti, qq);
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) acc = fmaf(S[r][c], qq[r], acc);
+        py[c] = al * acc;
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r) kq = fmaf(kr[r], qq[r], kq);
+      col_sum3(part, full, py, fy, kq, L, buf);
+    } else {
+      col_sum(part, full, L, buf);
+    }
     float e[kC];
 #pragma unroll
     for (int c = 0; c < kC; ++c) e[c] = vc[c] - full[c];
@@ -163,21 +213,11 @@ __global__ void __launch_bounds__(kBT) k_bwd_d128(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < kC; ++c) S[r][c] = fmaf(be * kr[r], e[c], al * S[r][c]);
     st_tile_ws(ws_state(tok), S);
-    if (ti == 0) st4f(a.errs + (tok * HV + h) * kBD + col, e);
-    if (want_y) {  // y_t = scale S_t^T q_t (column sums)
-      float qq[kR], py[kC], fy[kC];
-      ldr(a.q + (tok * HK + g) * kBD + kR * ti, qq);
+    if (ti == 0) {
+      st4f(a.errs + (tok * HV + h) * kBD + col, e);
+      if (want_y) {
 #pragma unroll
-      for (int c = 0; c < kC; ++c) {
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < kR; ++r) acc = fmaf(S[r][c], qq[r], acc);
-        py[c] = acc;
-      }
-      col_sum<1>(py, fy, L, buf);
-      if (ti == 0) {
-#pragma unroll
-        for (int c = 0; c < kC; ++c) fy[c] *= a.scale;
+        for (int c = 0; c < kC; ++c) fy[c] = a.scale * fmaf(be * kq, e[c], fy[c]);
         st4f(a.y + (tok * HV + h) * kBD + col, fy);
       }
     }
