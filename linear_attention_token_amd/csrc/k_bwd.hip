@@ -78,7 +78,8 @@ __device__ __forceinline__ void col_sum3(float (&part)[kC], float (&full)[kC], f
   kq = L.coly[buf][0][kSC] + L.coly[buf][1][kSC] + L.coly[buf][2][kSC] + L.coly[buf][3][kSC];
 }
 
-template <int which = 0>
+// Column sums: part[c] is this thread's sum over its rows for column c of its tile; returns the sum over
+// all 128 rows in every thread of the column. One barrier.
 __device__ __forceinline__ void col_sum(float (&part)[kC], float (&full)[kC], BwdLds& L, int buf) {
   float (*col)[4][kSC] = L.col;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, tj = t % kTJ;
@@ -128,13 +129,24 @@ __device__ __forceinline__ void st_tile_mat(float* m, const float (&s)[kR][kC], 
 }
 // Workspace copy of a slice state, slot-major: row r of thread t at (r * 256 + t) * 4, so each store or
 // load instruction of a wave covers 1 KB of consecutive bytes.
+// The kept states are written once and read back once, much later: non-temporal accesses keep them
+// from displacing the inputs in the caches.
 __device__ __forceinline__ void st_tile_ws(float* p, const float (&s)[kR][kC]) {
 #pragma unroll
-  for (int r = 0; r < kR; ++r) st4f(p + (r * kBT + threadIdx.x) * kC, s[r]);
+  for (int r = 0; r < kR; ++r) {
+    uint4 v;
+    v.x = __float_as_uint(s[r][0]); v.y = __float_as_uint(s[r][1]);
+    v.z = __float_as_uint(s[r][2]); v.w = __float_as_uint(s[r][3]);
+    stnt16(p + (r * kBT + threadIdx.x) * kC, v);
+  }
 }
 __device__ __forceinline__ void ld_tile_ws(const float* p, float (&s)[kR][kC]) {
 #pragma unroll
-  for (int r = 0; r < kR; ++r) ld4f(p + (r * kBT + threadIdx.x) * kC, s[r]);
+  for (int r = 0; r < kR; ++r) {
+    const uint4 v = ldnt16(p + (r * kBT + threadIdx.x) * kC);
+    s[r][0] = __uint_as_float(v.x); s[r][1] = __uint_as_float(v.y);
+    s[r][2] = __uint_as_float(v.z); s[r][3] = __uint_as_float(v.w);
+  }
 }
 
 __device__ __forceinline__ void zero(float (&s)[kR][kC]) {
