@@ -49,8 +49,9 @@ struct BwdMixArgs {
   float* dconv_w;               // out [C][4]
   float* dconv_in;              // out [N][3][C] or null
 };
+// dw_part: workspace of ceil(rows / 64) x 128 floats
 hipError_t launch_norm_gate_bwd(int64_t rows, const float* y, const float* z, const float* dout, const float* norm_w,
-                                float eps, float* dy, float* dz, float* dnorm_w, hipStream_t s);
+                                float eps, float* dy, float* dz, float* dnorm_w, float* dw_part, hipStream_t s);
 hipError_t launch_mixer_input_bwd(const BwdMixArgs& m, hipStream_t s);
 
 // ---- QSA compressed indexer ----

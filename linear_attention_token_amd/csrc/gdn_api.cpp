@@ -600,7 +600,8 @@ static size_t mixer_bwd_workspace_bytes(const Problem& p, int64_t T) {
   const size_t th = size_t(T) * p.hv, tk = size_t(T) * p.hk;
   return align256(plan_workspace(p, nullptr).bytes) + bwd_workspace_bytes(T, p.hk, p.hv) +
          2 * align256(sizeof(float) * th * 128) + 2 * align256(sizeof(float) * tk * 128) +
-         align256(sizeof(float) * th * 128) + align256(sizeof(float) * size_t(T) * size_t(p.C));
+         align256(sizeof(float) * th * 128) + align256(sizeof(float) * size_t(T) * size_t(p.C)) +
+         align256(sizeof(float) * ((th + 63) / 64) * 128);
 }
 
 static gdn_status check_mixer_bwd(const gdn_cfg* cfg, int32_t n_seqs, int64_t T, Problem& p) {
@@ -690,6 +691,8 @@ gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens
   float* dva = reinterpret_cast<float*>(w);
   w += align256(sizeof(float) * th * 128);
   float* du = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * size_t(total_tokens) * size_t(p.C));
+  float* dw_part = reinterpret_cast<float*>(w);
   a.y = y;
   a.dy = dy;
   a.dv = dva;
@@ -710,7 +713,7 @@ gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens
   ar.mode = kBwdReverse;
   if (run(launch_conv(p, cu_seqlens, q, k, v, qrow, qrow, vrow, conv_w, conv_in, fws, false, s), "backward conv") != hipSuccess ||
       run(launch_bwd(af, dqa, dka, dalpha, dbeta, s), "backward forward pass") != hipSuccess ||
-      run(launch_norm_gate_bwd(int64_t(th), y, gate, dout, norm_w, p.norm_eps, dy, dgate, dnorm_w, s),
+      run(launch_norm_gate_bwd(int64_t(th), y, gate, dout, norm_w, p.norm_eps, dy, dgate, dnorm_w, dw_part, s),
           "backward norm and gate") != hipSuccess ||
       run(launch_bwd(ar, dqa, dka, dalpha, dbeta, s), "backward recurrence") != hipSuccess ||
       run(launch_mixer_input_bwd(m, s), "backward conv, SiLU, L2") != hipSuccess)

@@ -1,6 +1,7 @@
 // Backward of the mixer's steps around the recurrence (fp32, d = 128), for gdn_backward:
 //   k_norm_gate_bwd   o = n * sigmoid(z), n = y / r * (1 + w), r = sqrt(mean(y^2) + eps):
-//                     dz = do * n * s (1 - s);  dn = do * s;  dw += dn * y / r;
+//                     dz = do * n * s (1 - s);  dn = do * s;  dw = sum of dn * y / r (per-block parts, then
+//                     k_sum_parts);
 //                     dy = (1 + w) dn / r - y <(1 + w) dn, y> / (128 r^3)
 //   k_l2silu_bwd      a = a0 / sqrt(|a0|^2 + eps) (q, k heads), a0 = silu(u), u the conv output:
 //                     da0 = (da - a <a, da>) / sqrt(|a0|^2 + eps);  du = da0 sigmoid(u) (1 + u (1 - sigmoid(u)))
@@ -44,7 +45,7 @@ __global__ void __launch_bounds__(256) k_norm_gate_bwd(int64_t rows, const float
                                                        const float* __restrict__ z, const float* __restrict__ dout,
                                                        const float* __restrict__ norm_w, float eps,
                                                        float* __restrict__ dy, float* __restrict__ dz,
-                                                       float* __restrict__ dnorm_w) {
+                                                       float* __restrict__ dw_part) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float w0 = 1.f + norm_w[lane], w1 = 1.f + norm_w[lane + 64];
   float dw0 = 0.f, dw1 = 0.f;
@@ -67,8 +68,33 @@ __global__ void __launch_bounds__(256) k_norm_gate_bwd(int64_t rows, const float
     dy[b + lane] = g0 * ir - y0 * dot;
     dy[b + lane + 64] = g1 * ir - y1 * dot;
   }
-  atomicAdd(&dnorm_w[lane], dw0);
-  atomicAdd(&dnorm_w[lane + 64], dw1);
+  // this block's part of the norm gain's derivative: the waves' sums, then one row of dw_part
+  __shared__ float red[4][kD];
+  red[w][lane] = dw0;
+  red[w][lane + 64] = dw1;
+  __syncthreads();
+  if (threadIdx.x < kD)
+    dw_part[int64_t(blockIdx.x) * kD + threadIdx.x] =
+        red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+}
+
+// dnorm_w[c] = sum over the blocks' rows of dw_part: 8 groups of 128 threads take every eighth row, then
+// the 8 group sums are added in a fixed order (reproducible).
+__global__ void __launch_bounds__(1024) k_sum_parts(const float* __restrict__ part, int64_t nblocks,
+                                                    float* __restrict__ out) {
+  __shared__ float red[8][kD];
+  const int c = threadIdx.x & (kD - 1), grp = threadIdx.x >> 7;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int64_t b = grp; b < nblocks; b += 8) acc += part[b * kD + c];
+  red[grp][c] = acc;
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += red[i][c];
+    out[c] = s;
+  }
 }
 
 // Conv output of channel c at packed token t (sequence n starting at s0): sum_j w[j] x[t - 3 + j] with the
@@ -189,11 +215,15 @@ __global__ void __launch_bounds__(256) k_conv_in_bwd(BwdMixArgs m) {
 }
 
 hipError_t launch_norm_gate_bwd(int64_t rows, const float* y, const float* z, const float* dout, const float* norm_w,
-                                float eps, float* dy, float* dz, float* dnorm_w, hipStream_t s) {
-  hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, s, dnorm_w, int64_t(kD));
-  if (rows == 0) return hipGetLastError();
-  hipLaunchKernelGGL(k_norm_gate_bwd, dim3(static_cast<unsigned>((rows + 63) / 64)), dim3(256), 0, s, rows, y, z, dout,
-                     norm_w, eps, dy, dz, dnorm_w);
+                                float eps, float* dy, float* dz, float* dnorm_w, float* dw_part, hipStream_t s) {
+  if (rows == 0) {
+    hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, s, dnorm_w, int64_t(kD));
+    return hipGetLastError();
+  }
+  const int64_t nb = (rows + 63) / 64;
+  hipLaunchKernelGGL(k_norm_gate_bwd, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, rows, y, z, dout, norm_w, eps,
+                     dy, dz, dw_part);
+  hipLaunchKernelGGL(k_sum_parts, dim3(1), dim3(1024), 0, s, dw_part, nb, dnorm_w);
   return hipGetLastError();
 }
 
