@@ -259,8 +259,7 @@ gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t t
  *   dstate_in       fp32 [N][HV][128][128] out or NULL;  dconv_in fp32 [N][3][C_tot] out or NULL.
  *   workspace       gdn_backward_workspace() bytes, 256-byte aligned (about 64 KB per token and value
  *                   head, for the kept states).
- * dconv_w is a sum over tokens accumulated with atomics, so its last bits can vary between runs; every
- * other output is reproducible. */
+ * Every output is reproducible for a fixed configuration (sums over tokens run in a fixed order). */
 gdn_status gdn_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, size_t* bytes);
 gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, const int32_t* cu_seqlens,
                         const float* q, const float* k, const float* v, const float* alpha, const float* beta,

@@ -47,6 +47,7 @@ struct BwdMixArgs {
   float* du;                    // workspace [T][C]: dL/d(conv output)
   float *dq, *dk, *dv;          // out: dL/d(raw inputs)
   float* dconv_w;               // out [C][4]
+  float* dw_part;               // workspace [ceil(T / 64)][C][4]: per-token-block parts of dconv_w
   float* dconv_in;              // out [N][3][C] or null
 };
 // dw_part: workspace of ceil(rows / 64) x 128 floats

@@ -601,7 +601,7 @@ static size_t mixer_bwd_workspace_bytes(const Problem& p, int64_t T) {
   return align256(plan_workspace(p, nullptr).bytes) + bwd_workspace_bytes(T, p.hk, p.hv) +
          2 * align256(sizeof(float) * th * 128) + 2 * align256(sizeof(float) * tk * 128) +
          align256(sizeof(float) * th * 128) + align256(sizeof(float) * size_t(T) * size_t(p.C)) +
-         align256(sizeof(float) * ((th + 63) / 64) * 128);
+         align256(sizeof(float) * ((th + 63) / 64) * 128) + align256(sizeof(float) * size_t((T + 63) / 64) * p.C * 4);
 }
 
 static gdn_status check_mixer_bwd(const gdn_cfg* cfg, int32_t n_seqs, int64_t T, Problem& p) {
@@ -693,6 +693,8 @@ gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens
   float* du = reinterpret_cast<float*>(w);
   w += align256(sizeof(float) * size_t(total_tokens) * size_t(p.C));
   float* dw_part = reinterpret_cast<float*>(w);
+  w += align256(sizeof(float) * ((th + 63) / 64) * 128);
+  float* dcw_part = reinterpret_cast<float*>(w);
   a.y = y;
   a.dy = dy;
   a.dv = dva;
@@ -707,7 +709,7 @@ gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens
   m.l2_eps = p.l2_eps;
   m.q = q; m.k = k; m.v = v; m.conv_w = conv_w; m.conv_in = conv_in;
   m.dqa = dqa; m.dka = dka; m.dva = dva; m.du = du;
-  m.dq = dq; m.dk = dk; m.dv = dv; m.dconv_w = dconv_w; m.dconv_in = dconv_in;
+  m.dq = dq; m.dk = dk; m.dv = dv; m.dconv_w = dconv_w; m.dconv_in = dconv_in; m.dw_part = dcw_part;
   BwdArgs af = a, ar = a;
   af.mode = kBwdForward | kBwdWriteY;
   ar.mode = kBwdReverse;

@@ -6,7 +6,8 @@
 //   k_l2silu_bwd      a = a0 / sqrt(|a0|^2 + eps) (q, k heads), a0 = silu(u), u the conv output:
 //                     da0 = (da - a <a, da>) / sqrt(|a0|^2 + eps);  du = da0 sigmoid(u) (1 + u (1 - sigmoid(u)))
 //   k_conv_bwd        u[t] = sum_j w[j] x[t - 3 + j]:  dx[t] = sum_j w[j] du[t + 3 - j] (inside the sequence),
-//                     dw[j] += sum_t du[t] x[t - 3 + j] (x[-3..-1] = the conv history)
+//                     dw[j] = sum_t du[t] x[t - 3 + j] (x[-3..-1] = the conv history; per 64-token block
+//                     parts, then k_conv_w_sum)
 //   k_conv_in_bwd     d history[r] = sum_j w[j] du[r - j] (r = 0..2 for positions -3..-1)
 // (the steps of the paper reading "On the Design of Qwen3.8-Next Architecture … 精读" §四 4.1 and the
 // analysis notes "Qwen3.8-Flash-Next：架构、效率与技术谱系" §03, differentiated).
@@ -196,8 +197,19 @@ __global__ void __launch_bounds__(256) k_conv_bwd(BwdMixArgs m) {
       dw[j] = fmaf(dut, xv, dw[j]);
     }
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) atomicAdd(&m.dconv_w[c * 4 + j], dw[j]);
+  *reinterpret_cast<float4*>(m.dw_part + (int64_t(blockIdx.y) * m.C + c) * 4) = make_float4(dw[0], dw[1], dw[2], dw[3]);
+}
+
+// dconv_w = the sum of the token blocks' parts, in block order (reproducible).
+__global__ void __launch_bounds__(256) k_conv_w_sum(BwdMixArgs m, int64_t nblocks) {
+  const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (c >= m.C) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t b = 0; b < nblocks; ++b) {
+    const float4 v = *reinterpret_cast<const float4*>(m.dw_part + (b * m.C + c) * 4);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  *reinterpret_cast<float4*>(m.dconv_w + c * 4) = acc;
 }
 
 // d conv_in[n][r][c] = sum_j w[c][j] du[s0 + r - j] for s0 + r - j in [s0, s1).
@@ -228,12 +240,14 @@ hipError_t launch_norm_gate_bwd(int64_t rows, const float* y, const float* z, co
 }
 
 hipError_t launch_mixer_input_bwd(const BwdMixArgs& m, hipStream_t s) {
-  hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>((m.C * 4 + 255) / 256)), dim3(256), 0, s, m.dconv_w, m.C * 4);
   if (m.T > 0) {
-    const int64_t items = m.T * (2 * m.hk + m.hv);
+    const int64_t items = m.T * (2 * m.hk + m.hv), nb = (m.T + 63) / 64;
     hipLaunchKernelGGL(k_l2silu_bwd, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0, s, m);
-    hipLaunchKernelGGL(k_conv_bwd, dim3(static_cast<unsigned>((m.C + 255) / 256), static_cast<unsigned>((m.T + 63) / 64)),
+    hipLaunchKernelGGL(k_conv_bwd, dim3(static_cast<unsigned>((m.C + 255) / 256), static_cast<unsigned>(nb)),
                        dim3(256), 0, s, m);
+    hipLaunchKernelGGL(k_conv_w_sum, dim3(static_cast<unsigned>((m.C + 255) / 256)), dim3(256), 0, s, m, nb);
+  } else {
+    hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>((m.C * 4 + 255) / 256)), dim3(256), 0, s, m.dconv_w, m.C * 4);
   }
   if (m.dconv_in && m.n_seqs > 0)
     hipLaunchKernelGGL(k_conv_in_bwd, dim3(static_cast<unsigned>((int64_t(m.n_seqs) * 3 * m.C + 255) / 256)),
