@@ -115,3 +115,40 @@ def test_mixer_backward_is_reproducible():
     torch.cuda.synchronize()
     for name in a:
         assert torch.equal(a[name], b[name]), name
+
+
+def test_mixer_backward_bench_shape_sampled_group():
+    """The benchmark's configuration (one 4096-token sequence, 16 QK / 48 value heads): every derivative that
+    depends only on QK group 5 (value heads 15-17) against the oracle's chains -- their raw q, k, v inputs,
+    alpha, beta, gate, and the conv taps of their channels."""
+    from workloads import prefill_inputs
+    T, g = 4096, 5
+    inp = prefill_inputs([T], n_qk_heads=16, n_v_heads=48, d_k=128, d_v=128, io_dtype=torch.float32, seed=11)
+    gg = torch.Generator(device="cpu").manual_seed(12)
+    dout = torch.randn(T, 48, 128, generator=gg)
+    cfg = gdn.cfg_for(16, 48, 128, 128, torch.float32)
+    d = lambda t: t.to(DEV).contiguous()
+    got = gdn.gdn_backward(cfg, d(inp.cu_seqlens), d(inp.q), d(inp.k), d(inp.v), d(inp.alpha), d(inp.beta),
+                           d(inp.gate), d(inp.conv_w), d(inp.norm_w), d(dout), want_dstate_in=False,
+                           want_dconv_in=False)
+    torch.cuda.synchronize()
+    C = 2 * 16 * 128 + 48 * 128
+    cw = inp.conv_w.double().numpy()
+    qs, ks = slice(128 * g, 128 * g + 128), slice(2048 + 128 * g, 2048 + 128 * g + 128)
+    zeros = np.zeros((3, 128))
+    dq = dk = dwq = dwk = 0.0
+    for h in range(3 * g, 3 * g + 3):
+        vs = slice(4096 + 128 * h, 4096 + 128 * h + 128)
+        r = O.gdn_chain_backward(inp.q[:, g], inp.k[:, g], inp.v[:, h], cw[qs], cw[ks], cw[vs], zeros, zeros, zeros,
+                                 inp.alpha[:, h].double().numpy(), inp.beta[:, h].double().numpy(),
+                                 inp.gate[:, h].double().numpy(), inp.norm_w.double().numpy(), np.zeros((128, 128)),
+                                 dout[:, h])
+        dq, dk, dwq, dwk = dq + r["xq"], dk + r["xk"], dwq + r["wq"], dwk + r["wk"]
+        for name, a, b in (("v", got["v"][:, h], r["xv"]), ("alpha", got["alpha"][:, h], r["alpha"]),
+                           ("beta", got["beta"][:, h], r["beta"]), ("gate", got["gate"][:, h], r["gate"]),
+                           ("conv_w v", got["conv_w"][vs], r["wv"])):
+            assert _rel(a, b) <= TOL, (name, h, _rel(a, b))
+    for name, a, b in (("q", got["q"][:, g], dq), ("k", got["k"][:, g], dk), ("conv_w q", got["conv_w"][qs], dwq),
+                       ("conv_w k", got["conv_w"][ks], dwk)):
+        assert _rel(a, b) <= TOL, (name, _rel(a, b))
+    assert got["conv_w"].shape == (C, 4)
