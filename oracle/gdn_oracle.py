@@ -534,10 +534,13 @@ QSA_ROPE_DIMS = 64   # rotated dims of the 128 (a reading: "partial RoPE")
 QSA_ROPE_BASE = 1e4
 
 
-def partial_rope(x, pos):
-    """Rotate dims (d, d + 32), d < 32, of x [..., 128] by angle pos * base^(-d/32) (fp64)."""
+def partial_rope(x, pos, rope_dims=QSA_ROPE_DIMS):
+    """Rotate dims (d, d + h), d < h = rope_dims / 2, of x [..., 128] by angle pos * base^(-d/h) (fp64);
+    64 rotated dims by default (dims 0..31 paired with 32..63)."""
     x = np.array(_f64(x), dtype=np.float64, copy=True)
-    half = QSA_ROPE_DIMS // 2
+    half = rope_dims // 2
+    if half == 0:
+        return x
     ang = np.asarray(pos, dtype=np.float64)[..., None] * QSA_ROPE_BASE ** (-np.arange(half) / half)
     c, s = np.cos(ang), np.sin(ang)
     a, b = x[..., :half].copy(), x[..., half:2 * half].copy()
@@ -546,7 +549,7 @@ def partial_rope(x, pos):
     return x
 
 
-def qsa_compress(k, w, eps=1e-6):
+def qsa_compress(k, w, eps=1e-6, rope_dims=QSA_ROPE_DIMS):
     """Compressed keys of the complete micro-blocks of one sequence ([P2] §04): the mean of each 4
     keys, RMS-normalised with gain w, then partial RoPE at the block's first position 4b.
     k [T, 128] -> [floor(T/4), 128] fp64."""
@@ -554,13 +557,13 @@ def qsa_compress(k, w, eps=1e-6):
     nb = k.shape[0] // QSA_BLOCK
     m = k[:nb * QSA_BLOCK].reshape(nb, QSA_BLOCK, k.shape[1]).mean(axis=1)
     m = m / np.sqrt(np.mean(m * m, axis=1, keepdims=True) + eps) * _f64(w)[None, :]
-    return partial_rope(m, QSA_BLOCK * np.arange(nb))
+    return partial_rope(m, QSA_BLOCK * np.arange(nb), rope_dims)
 
 
-def qsa_scores(q, kbar, pos):
+def qsa_scores(q, kbar, pos, rope_dims=QSA_ROPE_DIMS):
     """I[i, b] = sum over the 4 heads of ReLU(rope(q_ih, pos_i) . kbar_b) for the blocks complete at
     query i (4b + 3 <= pos_i); -inf elsewhere. q [M, 4, 128], kbar [N, 128], pos [M]."""
-    qr = partial_rope(q, np.asarray(pos)[:, None] * np.ones((1, _f64(q).shape[1])))
+    qr = partial_rope(q, np.asarray(pos)[:, None] * np.ones((1, _f64(q).shape[1])), rope_dims)
     sc = np.maximum(np.einsum("mhd,nd->mhn", qr, _f64(kbar)), 0.0).sum(axis=1)
     valid = (QSA_BLOCK * np.arange(sc.shape[1])[None, :] + QSA_BLOCK - 1) <= np.asarray(pos)[:, None]
     return np.where(valid, sc, -np.inf)

@@ -289,3 +289,33 @@ def test_select_ties_exact(case):
             sel2, _, _ = qsa.qsa_select(cfg, cu2, q.expand(T, 4, 128).contiguous(), kbar)
             torch.cuda.synchronize()
             assert np.array_equal(sel2[T - 1].cpu().numpy(), want), (case, "prefill")
+
+
+@pytest.mark.parametrize("rope_dims", [128, 16])
+def test_other_rope_widths(rope_dims):
+    """qsa_cfg.rope_dims other than 64: compressed keys (fp32) and selections against the oracle."""
+    dtype = torch.float32
+    lens = [300, 45]
+    x = indexer_inputs(lens, io_dtype=dtype, seed=17, device=DEV)
+    cfg = qsa.cfg_for(dtype, topk=16, rope_dims=rope_dims)
+    cap = 80
+    kbar, _ = _compress(cfg, x, cap, pending=False)
+    sel, n_sel, tail = qsa.qsa_select(cfg, x.cu_seqlens, x.q, kbar)
+    torch.cuda.synchronize()
+    cu = x.cu_seqlens.cpu().numpy()
+    k, w, q, kb_all = _np(x.k), _np(x.norm_w), _np(x.q), _np(kbar)
+    sel, n_sel, tail = sel.cpu().numpy(), n_sel.cpu().numpy(), tail.cpu().numpy()
+    for n, L in enumerate(lens):
+        s0 = cu[n]
+        kb = O.qsa_compress(k[s0:s0 + L], w, rope_dims=rope_dims)
+        assert _rel(kb_all[n, :L // 4], kb) <= TOL_KBAR[dtype]
+        S = O.qsa_scores(q[s0:s0 + L], kb, np.arange(L), rope_dims=rope_dims)
+        qr = np.stack([O.partial_rope(q[s0:s0 + L, h], np.arange(L, dtype=np.float64), rope_dims) for h in range(4)], 1)
+        E = C_SCORE[dtype] * np.einsum("mhd,nd->mn", np.abs(qr), np.abs(kb)) + 1e-30
+        for i in range(L):
+            nb = (i + 1) // 4
+            chosen = sel[s0 + i, :n_sel[s0 + i]]
+            assert n_sel[s0 + i] == min(16, nb) and np.all(np.diff(chosen) > 0)
+            rest = np.setdiff1d(np.arange(nb), chosen)
+            if len(rest):
+                assert np.min(S[i, chosen] + E[i, chosen]) >= np.max(S[i, rest] - E[i, rest])

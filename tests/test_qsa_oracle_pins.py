@@ -130,3 +130,22 @@ def test_select_against_lexsort():
         assert np.array_equal(sel[i], np.sort(order[:k]))
         assert len(sel[i]) == min(k, nb)
         assert tail[i] == 4 * ((pos[i] + 1) // 4) and tail[i] <= pos[i] + 1 < tail[i] + 4 + 1
+
+
+def test_rope_width():
+    """Other rotated widths: 128 pairs dim d with d + 64 at frequency 1e4^(-d/64) (dim 0 with 64 at
+    frequency 1, dim 63 with 127); 16 pairs d with d + 8 and leaves dims 16.. alone; 0 is the identity."""
+    x = np.zeros(128)
+    x[0] = 1.0
+    y = O.partial_rope(x, 2.0, rope_dims=128)
+    assert y[0] == pytest.approx(math.cos(2.0), abs=1e-15) and y[64] == pytest.approx(math.sin(2.0), abs=1e-15)
+    x = np.zeros(128)
+    x[63] = 1.0
+    y = O.partial_rope(x, 500.0, rope_dims=128)
+    f = 10000.0 ** (-63 / 64)
+    assert y[63] == pytest.approx(math.cos(500.0 * f), abs=1e-12) and y[127] == pytest.approx(math.sin(500.0 * f), abs=1e-12)
+    z = np.random.default_rng(10).standard_normal(128)
+    y = O.partial_rope(z, 77.0, rope_dims=16)
+    assert np.array_equal(y[16:], z[16:])
+    assert np.allclose(y[:8] ** 2 + y[8:16] ** 2, z[:8] ** 2 + z[8:16] ** 2, rtol=1e-12)
+    assert np.array_equal(O.partial_rope(z, 77.0, rope_dims=0), z)
