@@ -195,15 +195,15 @@ def test_decode_empty_sequences():
     assert torch.all(kbar == 7.0) and torch.all(pend == 7.0)
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16])
-def test_decode_one_million_tokens(dtype):
+@pytest.mark.parametrize("dtype,n_tok", [(torch.bfloat16, [1 << 20, 700001]), (torch.float32, [70001, 140000])])
+def test_decode_one_million_tokens(dtype, n_tok):
     """Model shape at the pages' longest context: two sequences at about 1M tokens (256K blocks, 16
-    segments of the select, then the merge), top-512, compressed by a prefill and one decode append."""
-    n_tok = [1 << 20, 700001]
+    segments of the select, then the merge), top-512, compressed by a prefill and one decode append; and
+    fp32 io at 70K / 140K tokens (2 and 3 segments)."""
     B = len(n_tok)
     x = indexer_inputs(n_tok, io_dtype=dtype, seed=15, device=DEV)
     cfg = qsa.cfg_for(dtype)
-    cap = (1 << 20) // 4
+    cap = max(n_tok) // 4
     cu = x.cu_seqlens.cpu().numpy()
     keep = torch.cat([torch.arange(cu[b], cu[b + 1] - 1, device=DEV) for b in range(B)])
     cu_p = torch.tensor([0, n_tok[0] - 1, n_tok[0] + n_tok[1] - 2], dtype=torch.int32, device=DEV)
