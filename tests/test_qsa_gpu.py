@@ -319,3 +319,45 @@ def test_other_rope_widths(rope_dims):
             rest = np.setdiff1d(np.arange(nb), chosen)
             if len(rest):
                 assert np.min(S[i, chosen] + E[i, chosen]) >= np.max(S[i, rest] - E[i, rest])
+
+
+def test_decode_graph_replay_matches_eager():
+    """qsa_decode captured once in a HIP graph (workspace and outputs allocated beforehand) and replayed
+    over four steps, with eager work and synchronisations in between: each replay equals an eager call
+    on copies of the same caches."""
+    dtype = torch.bfloat16
+    cfg = qsa.cfg_for(dtype, topk=32)
+    B, cap = 4, 600
+    x = indexer_inputs([2000] * B, io_dtype=dtype, seed=18, device=DEV)
+    kbar, pend = _compress(cfg, IndexerInputs(x.cu_seqlens, None, x.k, x.norm_w), cap)
+    n_tok = torch.full((B,), 2001, dtype=torch.int32, device=DEV)
+    q = torch.randn(B, 4, 128, device=DEV).to(dtype)
+    k = torch.randn(B, 128, device=DEV).to(dtype)
+    ws = torch.empty(qsa.qsa_workspace(cfg, B, cap), dtype=torch.uint8, device=DEV)
+    outs = (torch.empty((B, 32), dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.int32, device=DEV),
+            torch.empty(B, dtype=torch.int32, device=DEV))
+    kb_g, pd_g = kbar.clone(), pend.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        qsa.qsa_decode(cfg, n_tok, q, k, x.norm_w, pd_g, kb_g, *outs, workspace=ws)  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    kb_g.copy_(kbar)
+    pd_g.copy_(pend)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        qsa.qsa_decode(cfg, n_tok, q, k, x.norm_w, pd_g, kb_g, *outs, workspace=ws)
+    kb_e, pd_e = kbar.clone(), pend.clone()
+    kb_g.copy_(kbar)
+    pd_g.copy_(pend)
+    for step in range(4):
+        n_tok.add_(1)
+        q.normal_()
+        k.normal_()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = qsa.qsa_decode(cfg, n_tok, q, k, x.norm_w, pd_e, kb_e)
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), step
+        assert torch.equal(kb_g, kb_e) and torch.equal(pd_g, pd_e), step
