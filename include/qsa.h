@@ -95,7 +95,9 @@ gdn_status qsa_select(const qsa_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
  *   norm_w   fp32 [128].
  *   pending  io [B][3][128], updated in place;  kbar  io [B][cap_blocks][128], updated in place.
  *   sel, n_sel, tail  as for qsa_select, one row per sequence.
- *   workspace  at least qsa_workspace(cfg, B, cap_blocks) bytes. */
+ *   workspace  at least qsa_workspace(cfg, B, cap_blocks) bytes.
+ * The call enqueues kernels only (no allocation, copy or memset), so a serving loop can capture it in a
+ * HIP graph once and replay it with new n_tok, q and k in the same buffers. */
 gdn_status qsa_decode(const qsa_cfg* cfg, int32_t batch, const int32_t* n_tok, const void* q, int64_t ld_q,
                       const void* k, int64_t ld_k, const float* norm_w, void* pending, void* kbar,
                       int64_t cap_blocks, int32_t* sel, int32_t* n_sel, int32_t* tail,
