@@ -15,9 +15,10 @@
  *      the incomplete tail block [4 floor((i+1)/4), i], which every query keeps.
  * Readings where the pages are silent: RMSNorm is m / sqrt(mean(m^2) + norm_eps) * w; the rotary
  * part is the first rope_dims (64) dims, dim d paired with d + rope_dims/2 and turned by angle
- * pos * rope_base^(-2d/rope_dims); ties in the top-k go to the lower block index. Scores are fp32
- * from fp32 products of the stored compressed keys; rotation angles are reduced in fp64, so they
- * stay exact at 1M-token positions.
+ * pos * rope_base^(-2d/rope_dims); ties in the top-k go to the lower block index. Decode and
+ * fp32-io scores are fp32 products of the rotated queries and the stored compressed keys; the bf16
+ * prefill multiplies on bf16 MFMA (rotated queries rounded to bf16, fp32 accumulation). Rotation
+ * angles are reduced in fp64, so they stay exact at 1M-token positions.
  *
  * Conventions are those of gdn.h (device pointers owned by the caller, work enqueued on the
  * caller's stream, host-side validation before any enqueue, 16-byte alignment, strides in
