@@ -237,7 +237,8 @@ gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const voi
  *   workspace       gdn_recurrence_backward_workspace() bytes, 256-byte aligned: every state of the
  *                   forward (64 KB per token and value head) is kept there, so the reverse pass uses the
  *                   forward's exact states; split long batches to bound it.
- * One workgroup runs each (sequence, value head) chain token by token (forward, then reverse). */
+ * Each (sequence, value head) chain runs token by token (forward, then reverse) as 8 workgroups of 16
+ * value columns (the columns of the state evolve independently). */
 gdn_status gdn_recurrence_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
                                              size_t* bytes);
 gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
