@@ -209,7 +209,10 @@ __global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
   float* const gsh = act + nch;  // [R * 128] gate logits
   const int64_t qk_ch = int64_t(a.hk) * kD;
   const bool conv = (a.flags & GDN_CONV) != 0, gate = (a.flags & GDN_GATE) != 0;
-  const IO* const gsrc = static_cast<const IO*>(a.gate) + (size_t(b) * a.hv + size_t(g) * R) * kD;  // [R * 128]
+  // [R * 128]; without the gate the logits may be absent: the group's v row (also R * 128 values)
+  // stands in, and its values are discarded
+  const IO* const gsrc = gate ? static_cast<const IO*>(a.gate) + (size_t(b) * a.hv + size_t(g) * R) * kD
+                              : static_cast<const IO*>(a.v) + int64_t(b) * a.ld_v + int64_t(g) * nv;
   // Loads are issued unconditionally from clamped (always valid) addresses and converted only after
   // the whole pass is in flight; lanes past the end discard their values.
   float gv[2];

@@ -369,14 +369,13 @@ def gdn_prefill_backward(inp, dout, dstate_out=None, *, scale=1.0, l2_eps=1e-6, 
     return res
 
 
-def prefill_chain(inp, n, h, *, flags=FLAG_ALL, scale=1.0, l2_eps=1e-6, norm_eps=1e-6,
-                  state_in=None, conv_in=None):
-    """Run one (sequence n, value head h) chain of a packed prefill.
+def chain_inputs(inp, n, h, *, state_in=None, conv_in=None):
+    """The arguments of gdn_chain for one (sequence n, value head h) chain of a packed prefill, in fp64.
 
     ``inp`` holds q [T,HK,dk], k [T,HK,dk], v [T,HV,dv], alpha/beta [T,HV], gate [T,HV,dv],
     conv_w [C,4], norm_w [dv] or [HV,dv], cu_seqlens [N+1] and optional state_in
     [N,HV,dk,dv] / conv_in [N,3,C] (arrays or tensors; values are upcast to fp64 exactly).
-    Returns (o [L, d_v], S_final [d_k, d_v]) for that chain.
+    Value head h reads QK head floor(h * HK / HV).
     """
     cu = np.asarray(_f64(inp["cu_seqlens"]), dtype=np.int64)
     s0, s1 = int(cu[n]), int(cu[n + 1])
@@ -397,10 +396,18 @@ def prefill_chain(inp, n, h, *, flags=FLAG_ALL, scale=1.0, l2_eps=1e-6, norm_eps
     S0 = _f64(st[n, h]) if st is not None else np.zeros((dk, dv))
     nw = _f64(inp["norm_w"])
     nw = nw if nw.ndim == 1 else nw[h]
-    return gdn_chain(_f64(q[s0:s1, g]), _f64(k[s0:s1, g]), _f64(v[s0:s1, h]),
-                     conv_w[cq], conv_w[ck], conv_w[cv], hq, hk_, hv_,
-                     _f64(inp["alpha"][s0:s1, h]), _f64(inp["beta"][s0:s1, h]),
-                     _f64(inp["gate"][s0:s1, h]), nw, S0,
+    return dict(xq=_f64(q[s0:s1, g]), xk=_f64(k[s0:s1, g]), xv=_f64(v[s0:s1, h]),
+                wq=conv_w[cq], wk=conv_w[ck], wv=conv_w[cv], hq=hq, hk_=hk_, hv_=hv_,
+                alpha=_f64(inp["alpha"][s0:s1, h]), beta=_f64(inp["beta"][s0:s1, h]),
+                gate=_f64(inp["gate"][s0:s1, h]), norm_w=nw, S0=S0)
+
+
+def prefill_chain(inp, n, h, *, flags=FLAG_ALL, scale=1.0, l2_eps=1e-6, norm_eps=1e-6,
+                  state_in=None, conv_in=None):
+    """Run one (sequence n, value head h) chain of a packed prefill (inputs as for chain_inputs).
+    Returns (o [L, d_v], S_final [d_k, d_v]) for that chain.
+    """
+    return gdn_chain(**chain_inputs(inp, n, h, state_in=state_in, conv_in=conv_in),
                      flags=flags, scale=scale, l2_eps=l2_eps, norm_eps=norm_eps)
 
 

@@ -229,7 +229,51 @@ def test_rmsnorm_unit_mean_square_and_scale_invariance():
                                rtol=1e-13)
 
 
+def test_rmsnorm_constant_row_closed_form():
+    """No mean subtraction: a constant row y = c * 1 normalises to c / sqrt(c^2 + eps) * (1 + w)
+    channel by channel (about sign(c) (1 + w)); a mean-subtracting (LayerNorm-style) norm would map it
+    to zero. Closed form written out by hand for c = -3, eps = 1e-6."""
+    w = np.linspace(-0.05, 0.05, 16)
+    r = O.zero_centred_rmsnorm(np.full((1, 16), -3.0), w, 1e-6)
+    np.testing.assert_allclose(r[0], -3.0 / np.sqrt(9.0 + 1e-6) * (1.0 + w), rtol=1e-15)
+    assert np.all(r[0] < -0.9)
+    # a large common offset plus small noise stays near sign(c) (1 + w) instead of amplifying the noise
+    rng = np.random.default_rng(13)
+    y = 5.0 + 1e-3 * rng.standard_normal((8, 128))
+    r = O.zero_centred_rmsnorm(y, np.zeros(128), 1e-6)
+    np.testing.assert_allclose(r, 1.0, atol=1e-3)
+
+
+def test_rmsnorm_fixed_vector_by_hand():
+    """y = (1, 2, 3, 4), w = (0, 0.5, -0.5, 1), eps = 0: mean(y^2) = 30 / 4 = 7.5, so
+    r = y / sqrt(7.5) * (1 + w) = (1, 3, 1.5, 8) / sqrt(7.5). (A centred norm gives
+    (-1.5, -0.5, 0.5, 1.5) / sqrt(1.25) * (1 + w) instead.)"""
+    r = O.zero_centred_rmsnorm(np.array([[1.0, 2.0, 3.0, 4.0]]), np.array([0.0, 0.5, -0.5, 1.0]), 0.0)
+    np.testing.assert_allclose(r[0], np.array([1.0, 3.0, 1.5, 8.0]) / np.sqrt(7.5), rtol=1e-15)
+
+
 # ---------------------------------------------------------------- whole mixer -----------------
+
+def test_rmsnorm_per_head_gain_and_scale_through_the_chain():
+    """A per-head gain w[HV][d_v] reaches each value head with its own row, and the readout scale
+    multiplies the raw y (flags without NORM) but cancels under the norm up to eps."""
+    inp = _small([40], hk=1, hv=3)
+    rng = np.random.default_rng(14)
+    inp["norm_w"] = torch.from_numpy(0.1 * rng.standard_normal((3, 16)))
+    for h in range(3):
+        shared = dict(inp)
+        shared["norm_w"] = inp["norm_w"][h]
+        np.testing.assert_array_equal(O.prefill_chain(inp, 0, h)[0], O.prefill_chain(shared, 0, h)[0])
+    f = O.FLAG_CONV | O.FLAG_L2QK
+    y1, S1 = O.prefill_chain(inp, 0, 1, flags=f)
+    y2, S2 = O.prefill_chain(inp, 0, 1, flags=f, scale=0.5)
+    np.testing.assert_allclose(y2, 0.5 * y1, rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(S1, S2)
+    o1, _ = O.prefill_chain(inp, 0, 1, norm_eps=0.0)
+    o2, _ = O.prefill_chain(inp, 0, 1, scale=0.5, norm_eps=0.0)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-14)
+
+
 
 def _small(lengths, hk=2, hv=6, d=16, seed=0, **kw):
     inp = prefill_inputs(lengths, n_qk_heads=hk, n_v_heads=hv, d_k=d, d_v=d, io_dtype=torch.float32,
