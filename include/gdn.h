@@ -270,6 +270,29 @@ gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens
                         float* dstate_in, float* dconv_in, void* workspace, size_t workspace_bytes,
                         void* hip_stream);
 
+/* Allocation-free prefill, for callers that cannot allocate device memory or hand over a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments
+ * and results as gdn_prefill without `workspace`/`workspace_bytes`: its scratch is a static device
+ * array of GDN_STATIC_WORKSPACE_BYTES inside the library, one per GPU, which the loader places when
+ * the library's code first runs on that GPU and which stays until the process ends. The call allocates
+ * nothing and calls no allocating routine; the first call on a device looks up that device's copy of
+ * the array (hipGetSymbolAddress), later calls reuse the address.
+ *   - Returns GDN_E_WORKSPACE, enqueueing nothing, when gdn_prefill_workspace() for the problem
+ *     exceeds GDN_STATIC_WORKSPACE_BYTES (at the model shape, bf16: about 1,500 tokens per call).
+ *   - Uses the scratch of the calling thread's current device; `hip_stream` must belong to it.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents behind (the kernels need
+ *     none of it on entry). Calls that overlap on one GPU race: calls on different streams, or from
+ *     several threads, must be serialised by the caller. */
+#define GDN_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+gdn_status gdn_prefill_static(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                              const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                              const void* q, const void* k, const void* v,
+                              int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                              const float* alpha, const float* beta, const void* gate,
+                              const float* conv_w, const float* norm_w,
+                              const float* state_in, float* state_out,
+                              const void* conv_in, void* conv_out, void* out, void* hip_stream);
+
 /* Stage timing for profilers (host-side, per calling thread). After this call, every gdn_prefill
  * on this thread records events[i] on its stream before stage i and events[GDN_N_STAGES] after the
  * last stage, for the stages

@@ -27,6 +27,14 @@ static gdn_status fail(gdn_status st, const char* fmt, ...) {
   return st;
 }
 
+gdn_status report(gdn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -205,15 +213,21 @@ gdn_status gdn_prefill_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t tot
   return GDN_OK;
 }
 
-gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
-                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
-                       const void* q, const void* k, const void* v,
-                       int64_t ld_q, int64_t ld_k, int64_t ld_v,
-                       const float* alpha, const float* beta, const void* gate,
-                       const float* conv_w, const float* norm_w,
-                       const float* state_in, float* state_out,
-                       const void* conv_in, void* conv_out,
-                       void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+// gdn_prefill and gdn_prefill_static: every argument is validated first; with `scratch` set, the
+// workspace comes from it (after validation, so a rejected call makes no HIP call at all) and
+// `workspace_bytes` is the capacity it provides.
+gdn_status gdn::prefill_with(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             const void* q, const void* k, const void* v,
+                             int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                             const float* alpha, const float* beta, const void* gate,
+                             const float* conv_w, const float* norm_w,
+                             const float* state_in, float* state_out,
+                             const void* conv_in, void* conv_out,
+                             void* out, void* workspace, size_t workspace_bytes, ScratchFn scratch,
+                             void* hip_stream) {
   g_last_error[0] = 0;
   Problem p{};
   gdn_status st = check_cfg(cfg, p);
@@ -264,12 +278,22 @@ gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
       return fail(GDN_E_SHAPE, "cu_seqlens[%d] = %d, expected total_tokens = %lld", n_seqs, cu_seqlens_host[n_seqs], (long long)total_tokens);
   }
   const Workspace need = plan_workspace(p, nullptr);
-  if (!workspace && need.bytes > 0) return fail(GDN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need.bytes);
-  if (workspace_bytes < need.bytes) return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need.bytes);
-  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
+  if (scratch) {
+    if (workspace_bytes < need.bytes)
+      return fail(GDN_E_WORKSPACE, "this prefill needs %zu bytes of workspace; the static scratch holds %zu "
+                  "(split the batch or call gdn_prefill with a workspace)", need.bytes, workspace_bytes);
+  } else {
+    if (!workspace && need.bytes > 0) return fail(GDN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need.bytes);
+    if (workspace_bytes < need.bytes) return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need.bytes);
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
+  }
   if (n_seqs == 0) return GDN_OK;
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (scratch) {
+    const gdn_status sst = scratch(s, &workspace);
+    if (sst != GDN_OK) return sst;
+  }
   const Workspace ws = plan_workspace(p, workspace);
   const bool chunked = use_chunked(p);
   const bool any = total_tokens > 0;
@@ -296,6 +320,22 @@ gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
   if (run(mark(GDN_N_STAGES, s), "event record") != hipSuccess) return GDN_E_HIP;
 #undef GDN_STEP
   return GDN_OK;
+}
+
+extern "C" {
+
+gdn_status gdn_prefill(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
+                       const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                       const void* q, const void* k, const void* v,
+                       int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                       const float* alpha, const float* beta, const void* gate,
+                       const float* conv_w, const float* norm_w,
+                       const float* state_in, float* state_out,
+                       const void* conv_in, void* conv_out,
+                       void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return prefill_with(cfg, n_seqs, total_tokens, cu_seqlens, cu_seqlens_host, q, k, v, ld_q, ld_k, ld_v, alpha,
+                      beta, gate, conv_w, norm_w, state_in, state_out, conv_in, conv_out, out, workspace,
+                      workspace_bytes, nullptr, hip_stream);
 }
 
 gdn_status gdn_decode_step(const gdn_cfg* cfg, int32_t batch,

@@ -53,6 +53,20 @@ struct Workspace {
   size_t bytes = 0;
 };
 
+// Records a message for gdn_last_error() on this thread and returns `st`.
+gdn_status report(gdn_status st, const char* fmt, ...);
+
+// gdn_prefill with every argument validated before any HIP call. With `scratch` set, the workspace is
+// the device buffer scratch() returns (looked up after validation) and `workspace_bytes` its capacity;
+// otherwise `workspace` as given.
+using ScratchFn = gdn_status (*)(hipStream_t s, void** workspace);
+gdn_status prefill_with(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, const int32_t* cu_seqlens,
+                        const int32_t* cu_seqlens_host, const void* q, const void* k, const void* v, int64_t ld_q,
+                        int64_t ld_k, int64_t ld_v, const float* alpha, const float* beta, const void* gate,
+                        const float* conv_w, const float* norm_w, const float* state_in, float* state_out,
+                        const void* conv_in, void* conv_out, void* out, void* workspace, size_t workspace_bytes,
+                        ScratchFn scratch, void* hip_stream);
+
 // True when the chunked MFMA path serves this problem.
 inline bool use_chunked(const Problem& p) { return p.bf16 && p.dk == 128 && p.dv == 128; }
 

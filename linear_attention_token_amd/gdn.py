@@ -19,7 +19,7 @@ GDN_BF16, GDN_F32 = 0, 1
 GDN_CONV, GDN_L2QK, GDN_NORM, GDN_GATE, GDN_ALL = 1, 2, 4, 8, 15
 STATUS = {0: "GDN_OK", 1: "GDN_E_NULL", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE", 4: "GDN_E_ALIGN",
           5: "GDN_E_WORKSPACE", 6: "GDN_E_UNSUPPORTED", 7: "GDN_E_HIP", 8: "GDN_E_VALUE"}
-EXPORTS = ("gdn_cfg_default", "gdn_prefill_workspace", "gdn_prefill", "gdn_decode_step",
+EXPORTS = ("gdn_cfg_default", "gdn_prefill_workspace", "gdn_prefill", "gdn_prefill_static", "gdn_decode_step",
            "gdn_verify_log_bytes", "gdn_verify", "gdn_commit",
            "gdn_proj_workspace", "gdn_in_proj", "gdn_out_proj",
            "gdn_recurrence_backward_workspace", "gdn_recurrence_backward", "gdn_backward_workspace", "gdn_backward",
@@ -64,6 +64,9 @@ def load_library(path: str = LIB_PATH):
                                 _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 ctypes.c_size_t, _P]
     lib.gdn_prefill.restype = ctypes.c_int
+    lib.gdn_prefill_static.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, _I64, _P, _P, _P, _P, _P,
+                                       _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.gdn_prefill_static.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [ctypes.POINTER(gdn_cfg), ctypes.c_int32, _P, _P, _P, _I64, _I64,
                                     _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.gdn_decode_step.restype = ctypes.c_int
@@ -199,14 +202,8 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
-def gdn_prefill(cfg: gdn_cfg, cu_seqlens: torch.Tensor, q, k, v, alpha, beta, gate, conv_w, norm_w,
-                state_in=None, state_out=None, conv_in=None, conv_out=None, out=None, workspace=None,
-                cu_seqlens_host: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Packed prefill; returns ``out`` [T, HV, d_v] (allocated when not given).
-
-    Writes ``state_out`` / ``conv_out`` when given. ``workspace`` (uint8, >= gdn_prefill_workspace
-    bytes) is allocated when not given.
-    """
+def _prefill(cfg, cu_seqlens, q, k, v, alpha, beta, gate, conv_w, norm_w, state_in, state_out, conv_in, conv_out,
+             out, workspace, cu_seqlens_host, stream, static):
     lib = load_library()
     io = _io_dtype(cfg)
     n_seqs = int(cu_seqlens.numel()) - 1
@@ -220,23 +217,51 @@ def gdn_prefill(cfg: gdn_cfg, cu_seqlens: torch.Tensor, q, k, v, alpha, beta, ga
     _expect(state_out, sshape, torch.float32, "state_out", optional=True)
     _expect(conv_in, (n_seqs, 3, C), io, "conv_in", optional=True)
     _expect(conv_out, (n_seqs, 3, C), io, "conv_out", optional=True)
-    need = gdn_prefill_workspace(cfg, n_seqs, T)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if workspace.dtype != torch.uint8 or workspace.numel() < need:
-        raise ValueError(f"workspace needs {need} uint8 elements")
+    if not static:
+        need = gdn_prefill_workspace(cfg, n_seqs, T)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        if workspace.dtype != torch.uint8 or workspace.numel() < need:
+            raise ValueError(f"workspace needs {need} uint8 elements")
     host = None
     if cu_seqlens_host is not None:
         host = cu_seqlens_host.to(torch.int32).contiguous()
-    st = lib.gdn_prefill(ctypes.byref(cfg), n_seqs, T, _ptr(cu_seqlens),
-                         host.data_ptr() if host is not None else None,
-                         _ptr(q), _ptr(k), _ptr(v), _row_stride(q, cfg.n_qk_heads * cfg.d_k),
-                         _row_stride(k, cfg.n_qk_heads * cfg.d_k), _row_stride(v, cfg.n_v_heads * cfg.d_v),
-                         _ptr(alpha), _ptr(beta), _ptr(gate), _ptr(conv_w), _ptr(norm_w),
-                         _ptr(state_in), _ptr(state_out), _ptr(conv_in), _ptr(conv_out), _ptr(out),
-                         _ptr(workspace), workspace.numel(), _stream(stream))
+    args = [ctypes.byref(cfg), n_seqs, T, _ptr(cu_seqlens), host.data_ptr() if host is not None else None,
+            _ptr(q), _ptr(k), _ptr(v), _row_stride(q, cfg.n_qk_heads * cfg.d_k),
+            _row_stride(k, cfg.n_qk_heads * cfg.d_k), _row_stride(v, cfg.n_v_heads * cfg.d_v),
+            _ptr(alpha), _ptr(beta), _ptr(gate), _ptr(conv_w), _ptr(norm_w),
+            _ptr(state_in), _ptr(state_out), _ptr(conv_in), _ptr(conv_out), _ptr(out)]
+    if static:
+        st = lib.gdn_prefill_static(*args, _stream(stream))
+    else:
+        st = lib.gdn_prefill(*args, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st)
     return out
+
+
+def gdn_prefill(cfg: gdn_cfg, cu_seqlens: torch.Tensor, q, k, v, alpha, beta, gate, conv_w, norm_w,
+                state_in=None, state_out=None, conv_in=None, conv_out=None, out=None, workspace=None,
+                cu_seqlens_host: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Packed prefill; returns ``out`` [T, HV, d_v] (allocated when not given).
+
+    Writes ``state_out`` / ``conv_out`` when given. ``workspace`` (uint8, >= gdn_prefill_workspace
+    bytes) is allocated when not given.
+    """
+    return _prefill(cfg, cu_seqlens, q, k, v, alpha, beta, gate, conv_w, norm_w, state_in, state_out, conv_in,
+                    conv_out, out, workspace, cu_seqlens_host, stream, static=False)
+
+
+def gdn_prefill_static(cfg: gdn_cfg, cu_seqlens: torch.Tensor, q, k, v, alpha, beta, gate, conv_w, norm_w,
+                       state_in=None, state_out=None, conv_in=None, conv_out=None, out=None,
+                       cu_seqlens_host: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """gdn_prefill on the library's static scratch (no workspace): the call itself allocates nothing
+    when ``out`` is given. Problems whose workspace exceeds GDN_STATIC_WORKSPACE_BYTES raise
+    GDN_E_WORKSPACE; overlapping calls on one GPU race."""
+    return _prefill(cfg, cu_seqlens, q, k, v, alpha, beta, gate, conv_w, norm_w, state_in, state_out, conv_in,
+                    conv_out, out, None, cu_seqlens_host, stream, static=True)
+
+
+GDN_STATIC_WORKSPACE_BYTES = 128 << 20
 
 
 def gdn_decode_step(cfg: gdn_cfg, q, k, v, alpha, beta, gate, conv_w, norm_w, conv_state, state,

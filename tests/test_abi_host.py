@@ -37,6 +37,29 @@ def test_exports_every_declared_function():
         assert hasattr(lib, f), f"libgdn.so does not export {f}"
 
 
+def header_arity():
+    """Parameter count of every function the headers declare."""
+    arity = {}
+    for h in HEADERS:
+        txt = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for name, params in re.findall(r"\b((?:gdn|qsa)_[a-z_0-9]+)\s*\(([^;{]*?)\)\s*;", txt, flags=re.S):
+            ps = [p for p in params.split(",") if p.strip() and p.strip() != "void"]
+            arity[name] = len(ps)
+    return arity
+
+
+def test_bindings_declare_every_argument():
+    """Each ctypes declaration lists exactly the header's parameters: an argument missing from argtypes
+    would still be passed, as a C int, truncating a pointer such as the stream handle."""
+    gdn._declare_bwd(lib)
+    qsa._lib()
+    arity = header_arity()
+    assert set(arity) == set(header_functions())
+    for name, n in arity.items():
+        at = getattr(lib, name).argtypes
+        assert at is not None and len(at) == n, (name, None if at is None else len(at), n)
+
+
 def test_abi_version_and_defaults():
     assert lib.gdn_abi_version() == 1
     c = gdn.gdn_cfg_default()
@@ -125,6 +148,30 @@ def test_prefill_rejects_bad_arguments():
     _err(_prefill(c, n_seqs=2, cu_host=[0, 100, 90]), 2)              # decreasing
     _err(_prefill(c, cu_host=[0, T_ - 1]), 2)                         # cu[N] != T
     _err(_prefill(c, conv_in=A, conv_out=A + 256), 8)                 # partial overlap
+
+
+def _prefill_static(cfg, n_seqs=N_, T=T_, cu=A, q=A, k=A, v=A, ld_q=2048, ld_k=2048, ld_v=6144, alpha=A,
+                    beta=A, gate=A, conv_w=A, norm_w=A, out=A):
+    return lib.gdn_prefill_static(ctypes.byref(cfg), n_seqs, T, cu, None, q, k, v, ld_q, ld_k, ld_v, alpha, beta,
+                                  gate, conv_w, norm_w, None, None, None, None, out, None)
+
+
+def test_static_prefill_validates_before_any_hip_call():
+    """The allocation-free prefill refuses, with no HIP call (no GPU here), a problem whose workspace
+    exceeds its static scratch, and every argument gdn_prefill refuses."""
+    c = gdn.gdn_cfg_default()
+    assert gdn.gdn_prefill_workspace(c, 1, 4096) > gdn.GDN_STATIC_WORKSPACE_BYTES
+    _err(_prefill_static(c, T=4096), 5)
+    assert "static scratch" in lib.gdn_last_error().decode()
+    assert gdn.gdn_prefill_workspace(c, 1, 1024) <= gdn.GDN_STATIC_WORKSPACE_BYTES
+    _err(_prefill_static(gdn.gdn_cfg_default(n_v_heads=47)), 2)
+    _err(_prefill_static(c, q=None), 1)
+    _err(_prefill_static(c, ld_v=6148), 4)
+    _err(_prefill_static(c, out=A + 2), 4)
+    _err(_prefill_static(c, n_seqs=0, T=5), 2)
+    with open(HEADERS[0]) as f:
+        m = re.search(r"#define GDN_STATIC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == gdn.GDN_STATIC_WORKSPACE_BYTES
 
 
 def test_flags_relax_required_pointers():
