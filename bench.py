@@ -61,20 +61,37 @@ def stage_model(T: int, n_seqs: int):
     return per_tok
 
 
-def path_bytes(T: int, n_seqs: int, state_in: bool) -> float:
-    """Compulsory bytes of the whole prefill: raw q/k/v, gate, o, alpha/beta and the states."""
-    return 45440.0 * T + n_seqs * HV * 128 * 128 * 4 * (2 if state_in else 1)
+def path_bytes(lengths, state_in: bool, hk=HK, hv=HV, dk=D, dv=D, elem=2) -> float:
+    """Compulsory bytes of a whole packed prefill: raw q/k/v, gate logits and output in the io dtype,
+    alpha/beta fp32, the fp32 states (written; read too when given) and the conv tails written
+    (45,440 B per token at the model shape in bf16, plus 3 MiB per sequence per state direction)."""
+    T, N = sum(lengths), len(lengths)
+    C = 2 * hk * dk + hv * dv
+    per_tok = (C + 2 * hv * dv) * elem + hv * 8
+    return float(per_tok * T + N * hv * dk * dv * 4 * (2 if state_in else 1) + N * 3 * C * elem)
 
 
-def path_flops(T: int) -> float:
-    """Dense-tile MFMA flops of the chunked algorithm (8.65 MFLOP per token at this shape)."""
-    nc = -(-T // CH)
-    per_chunk_head = (3 * 2 * 64 * 64 * 128          # Gram, U, Wk
-                      + 2 * 2 * 64 * 128 * 128       # Wk S, K^T W
-                      + 2 * 64 * 64 * 128            # Q K^T
-                      + 2 * 64 * 128 * 128           # Q S
-                      + 2 * 64 * 64 * 128)           # P W
-    return float(nc * HV * per_chunk_head)
+def path_flops(lengths, hv=HV, dk=D, dv=D) -> float:
+    """Dense-tile MFMA flops of the chunked algorithm per (64-token chunk, value head): Gram, U and Wk
+    (3 x 2 C^2 d), the two state products (2 x 2 C d^2), Q K^T (2 C^2 d), Q S (2 C d^2) and P W
+    (2 C^2 d) -- 8.65 MFLOP per token at the model shape; a sequence's last chunk counts in full."""
+    nc = sum(-(-L // CH) for L in lengths)
+    per_chunk_head = (3 * 2 * CH * CH * dk + 2 * 2 * CH * dk * dv + 2 * CH * CH * dk + 2 * CH * dk * dv
+                      + 2 * CH * CH * dv)
+    return float(nc * hv * per_chunk_head)
+
+
+def path_roofline(lengths, state_in, ms, **shape):
+    """The step against both compulsory bounds: HBM (path_bytes at 8 TB/s) and bf16 MFMA (path_flops
+    at 2.5 PFLOP/s); `frac` is against the binding one, `frac_of_mfma_bound` the MFMA fraction alone."""
+    pb = path_bytes(lengths, state_in, **shape)
+    pf = path_flops(lengths, **{k: v for k, v in shape.items() if k in ("hv", "dk", "dv")})
+    t_hbm, t_mfma = pb / (HBM_PEAK_GBPS * 1e9), pf / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    s = ms * 1e-3
+    return dict(bytes=pb, flops=pf, hbm_bound_us=round(t_hbm * 1e6, 2), mfma_bound_us=round(t_mfma * 1e6, 2),
+                bound="hbm" if t_hbm >= t_mfma else "mfma", frac=round(max(t_hbm, t_mfma) / s, 4),
+                frac_of_hbm_bound=round(t_hbm / s, 4), frac_of_mfma_bound=round(t_mfma / s, 4),
+                achieved_GBps=round(pb / s / 1e9, 1), achieved_TFLOPs=round(pf / s / 1e12, 2))
 
 
 def decode_bytes(B: int) -> float:
@@ -130,24 +147,147 @@ def measured_traffic(stage: str, grid_tag: str):
     return round(float(k["traffic_bytes"]))
 
 
-def cpu_baseline(max_tokens: int):
-    """The fp64 oracle on the host: one layer at model shape (all 48 value heads), one thread."""
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
+
+
+def measured_mfma(stage: str, grid_tag: str):
+    """MFMA busy fraction of a stage's kernel from the committed counter summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs), or None when absent, taken at another
+    launch shape, or on a different kernel source than the one built now."""
+    try:
+        with open(MFMA_FILE) as fh:
+            k = json.load(fh)["kernels"][stage]
+    except (OSError, KeyError, ValueError):
+        return None
+    if k.get("workload") != grid_tag or k.get("source_sha256") != kernel_source_hash(STAGE_SOURCE[stage]):
+        return None
+    return k.get("mfma_busy")
+
+
+def prefill_step(gdn, inp, dev, with_state=True):
+    """One gdn_prefill call over `inp` with preallocated outputs and workspace (state_out and conv_out
+    written; state_in/conv_in as the workload gives them)."""
     import torch
-    from threadpoolctl import threadpool_limits
+    io = inp.io_dtype
+    N, T = inp.n_seqs, int(inp.q.shape[0])
+    cfg = gdn.cfg_for(inp.n_qk_heads, inp.n_v_heads, inp.d_k, inp.d_v, io)
+    out = torch.empty((T, inp.n_v_heads, inp.d_v), dtype=io, device=dev)
+    st = torch.empty((N, inp.n_v_heads, inp.d_k, inp.d_v), dtype=torch.float32, device=dev) if with_state else None
+    cv = torch.empty((N, 3, inp.n_channels), dtype=io, device=dev)
+    ws = torch.empty(max(1, gdn.gdn_prefill_workspace(cfg, N, T)), dtype=torch.uint8, device=dev)
+    cu_host = inp.cu_seqlens.cpu()
+
+    def step():
+        gdn.gdn_prefill(cfg, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.gate, inp.conv_w,
+                        inp.norm_w, state_in=inp.state_in, state_out=st, conv_in=inp.conv_in, conv_out=cv, out=out,
+                        workspace=ws, cu_seqlens_host=cu_host)
+
+    return step, (out, st, cv, ws)
+
+
+def step_distribution(step, n, stream):
+    """Per-step times (ms) from one event between consecutive steps: median, p10, p90, mean."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+    q = lambda f: t[min(n - 1, int(round(f * (n - 1))))]
+    return dict(median=round(q(0.5), 5), p10=round(q(0.1), 5), p90=round(q(0.9), 5), mean=round(sum(t) / n, 5), n=n)
+
+
+def stage_times(gdn, step, n, stream):
+    """Per-stage mean times (ms) from the library's stage events, in a separate eager pass."""
+    import ctypes
+    import torch
+    nev = gdn.N_STAGES + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in evs]
+    for i in range(n):
+        gdn.gdn_set_stage_events(handles[i])
+        step()
+    torch.cuda.synchronize()
+    gdn.gdn_set_stage_events(None)
+    return {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(n)) / n
+            for j, name in enumerate(gdn.STAGE_NAMES)}
+
+
+def config_legs(args, gdn, dev, stream):
+    """The other prefill workloads, each timed over repeated calls (median, p10, p90) with its path
+    roofline: the tiny fp32 case (token-sequential fp32 path, launch-bound), the 262,144-token prefill
+    and the 32-sequence variable-length pack with initial states."""
+    import torch
+    from workloads import config_tiny, config_long, config_varlen
+    legs = {}
+    specs = [
+        ("tiny", lambda: config_tiny(dev), 200,
+         "B=1, T=64, 1 QK / 1 value head, d=16, fp32 io (token-sequential fp32 path), full layer"),
+        ("long", lambda: config_long(dev, T=args.long_tokens), args.long_reps,
+         f"B=1, T={args.long_tokens}, 16 QK / 48 value heads, d=128, bf16 io, fp32 state, full layer"),
+        ("varlen", lambda: config_varlen(dev), args.long_reps,
+         "32 sequences, lengths log-uniform in [512, 32768] (seed 0), S0 ~ N(0, 0.01), 16 QK / 48 value heads, "
+         "d=128, bf16 io, fp32 state, full layer"),
+    ]
+    for name, make, reps, desc in specs:
+        inp = make()
+        lengths = [int(x) for x in torch.diff(inp.cu_seqlens.cpu()).tolist()]
+        step, bufs = prefill_step(gdn, inp, dev)
+        for _ in range(min(3, reps)):
+            step()
+        torch.cuda.synchronize()
+        d = step_distribution(step, reps, stream)
+        shape = dict(hk=inp.n_qk_heads, hv=inp.n_v_heads, dk=inp.d_k, dv=inp.d_v,
+                     elem=2 if inp.io_dtype == torch.bfloat16 else 4)
+        T = sum(lengths)
+        legs[name] = dict(workload=desc, tokens=T, sequences=len(lengths), ms_per_call=d,
+                          tokens_per_s=round(T / (d["median"] * 1e-3), 1),
+                          path_roofline=path_roofline(lengths, inp.state_in is not None, d["median"], **shape))
+        if name != "tiny":
+            legs[name]["stage_ms"] = {k: round(v, 4) for k, v in stage_times(gdn, step, min(3, reps), stream).items()}
+        del inp, bufs, step
+        torch.cuda.empty_cache()
+    legs["tiny"]["note"] = "launch-bound: the MFMA and HBM bounds of 64 tokens are far below one launch"
+    return legs
+
+
+def cpu_baseline(prefill_tokens: int, decode_batch: int):
+    """The fp64 oracle as it stands, on the host's cores (a process pool over independent (sequence,
+    value head) chains, one thread each): a prefill of the one-layer workload's first `prefill_tokens`
+    tokens, all 48 value heads, and one decode step of `decode_batch` sequences (every (sequence, value
+    head) chain with one token)."""
     import oracle as O
-    from workloads import config_layer
-    inp = config_layer("cpu", T=max_tokens)
+    from workloads import config_layer, decode_inputs
+    workers = O.default_workers()
+    inp = config_layer("cpu", T=prefill_tokens)
     d = vars(inp)
-    with threadpool_limits(1):
-        O.prefill_chain(d, 0, 0)          # first-call warm-up (library dispatch setup)
-        t0 = time.perf_counter()
-        for h in range(HV):
-            O.prefill_chain(d, 0, h)
-        dt = time.perf_counter() - t0
-    return dict(value=max_tokens / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"fp64 numpy oracle, one layer at model shape, B=1, T={max_tokens}, all 48 value "
-                       f"heads (conv + SiLU + L2 + per-token recurrence + RMSNorm + gate), one thread, "
-                       f"{dt:.1f} s")
+    O.prefill_chain(d, 0, 0)          # first-call warm-up in this process
+    t0 = time.perf_counter()
+    O.run_chains(d, [(0, h) for h in range(HV)], workers=workers)
+    dt = time.perf_counter() - t0
+    di = decode_inputs(decode_batch, 1, n_qk_heads=HK, n_v_heads=HV, d_k=D, d_v=D, seed=2)
+    pk = lambda x: x[0]
+    step = dict(q=pk(di.q), k=pk(di.k), v=pk(di.v), alpha=pk(di.alpha), beta=pk(di.beta), gate=pk(di.gate),
+                conv_w=di.conv_w, norm_w=di.norm_w, cu_seqlens=list(range(decode_batch + 1)),
+                state_in=di.state, conv_in=di.conv_state)
+    t1 = time.perf_counter()
+    O.run_chains(step, [(b, h) for b in range(decode_batch) for h in range(HV)], workers=workers)
+    dd = time.perf_counter() - t1
+    return dict(value=round(prefill_tokens / dt, 1), unit="tokens/s", cores=workers, kind="oracle",
+                cpu_model=O.cpu_model(), host_cores=O.host_cores(),
+                decode_us_per_step=round(dd * 1e6, 1),
+                sample=f"fp64 numpy oracle (conv + SiLU + L2 + per-token recurrence + RMSNorm + gate) over a pool of "
+                       f"{workers} single-thread processes: prefill of the first {prefill_tokens} tokens of the "
+                       f"one-layer workload (B=1, all 48 value heads) in {dt:.1f} s wall, scaled to tokens/s; one "
+                       f"decode step at B={decode_batch} (all {decode_batch * HV} chains, one token each) in "
+                       f"{dd:.1f} s wall")
 
 
 def backward_leg(args, dev, stream):
@@ -298,14 +438,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the reference timing of one captured HIP graph replayed per step")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=1024, help="tokens of the oracle's prefill sample")
+    ap.add_argument("--long-tokens", type=int, default=262144, help="tokens of the long prefill workload")
+    ap.add_argument("--long-reps", type=int, default=10, help="timed calls of the long and varlen workloads")
+    ap.add_argument("--no-configs", action="store_true", help="skip the tiny, long and varlen prefill workloads")
     ap.add_argument("--hidden", type=int, default=2560, help="residual width of the layer leg")
     ap.add_argument("--qsa-context", type=int, default=1 << 20, help="tokens per sequence of the indexer decode")
     ap.add_argument("--qsa-batch", type=int, default=8, help="sequences of the indexer decode")
     ap.add_argument("--qsa-prefill", type=int, default=32768, help="tokens of the indexer prefill (one sequence)")
     ap.add_argument("--qsa-steps", type=int, default=50)
     ap.add_argument("--bwd-tokens", type=int, default=4096, help="tokens of the recurrence backward (one sequence)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "speculative", "layer", "indexer", "backward", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "configs", "decode", "speculative", "layer", "indexer",
+                                       "backward", "copy"],
                     default="all",
                     help="run one part only (for profilers); 'copy' times a plain 1 GiB device copy, the "
                          "reference kernel for scaling HBM byte counters")
@@ -350,19 +494,10 @@ def main():
     cfg = gdn.cfg_for(HK, HV, D, D, torch.bfloat16)
     result = {}
     if args.only in ("all", "prefill"):
-        # ---------------- prefill: one layer, B=1, T tokens -----------------------------------------
+        # ---------------- headline prefill: one layer, B=1, T tokens ---------------------------------
         T = args.tokens
         inp = config_layer(dev, T=T)
-        out = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
-        state_out = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
-        conv_out = torch.empty((1, 3, inp.n_channels), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(gdn.gdn_prefill_workspace(cfg, 1, T), dtype=torch.uint8, device=dev)
-        cu_host = inp.cu_seqlens.cpu()
-
-        def step():
-            gdn.gdn_prefill(cfg, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.gate,
-                            inp.conv_w, inp.norm_w, state_in=None, state_out=state_out, conv_out=conv_out,
-                            out=out, workspace=ws, cu_seqlens_host=cu_host)
+        step, bufs = prefill_step(gdn, inp, dev)
 
         for _ in range(args.warmup):
             step()
@@ -379,6 +514,7 @@ def main():
         torch.cuda.synchronize()
         t_wall = time.perf_counter() - t_wall
         ms_step = start.elapsed_time(end) / args.steps
+        dist = step_distribution(step, args.steps, stream)
 
         # the same steps replayed from one captured HIP graph, for reference
         ms_step_graph = None
@@ -395,58 +531,40 @@ def main():
             torch.cuda.synchronize()
             ms_step_graph = start.elapsed_time(end) / args.steps
 
-        # per-stage times: a separate eager pass with the library's stage events (N_STAGES + 1 per
-        # step, created by recording once)
-        import ctypes
-        nev = gdn.N_STAGES + 1
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-        for row in evs:
-            for e in row:
-                e.record(stream)
-        torch.cuda.synchronize()
-        handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in row]) for row in evs]
-        for i in range(args.steps):
-            gdn.gdn_set_stage_events(handles[i])
-            step()
-        torch.cuda.synchronize()
-        gdn.gdn_set_stage_events(None)
-        stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-                    for j, name in enumerate(gdn.STAGE_NAMES)}
-
+        stage_ms = stage_times(gdn, step, args.steps, stream)
         model = stage_model(T, 1)
-        dom = max(stage_ms, key=stage_ms.get)
-        dm = model[dom]
-        dom_s = stage_ms[dom] * 1e-3
-        if dm["bound"] == "hbm":
-            achieved = dm["bytes"] / dom_s / 1e9
-            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=measured_traffic(dom, f"prefill T={T}"))
-        else:
-            achieved = dm["flops"] / dom_s / 1e12
-            roof = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                        traffic=measured_traffic(dom, f"prefill T={T}"))
-        roof["kernel"] = dom
-        roof["ms_per_launch"] = round(stage_ms[dom], 5)
-        roof["algorithmic_bytes"] = dm["bytes"]
-        roof["algorithmic_flops"] = dm["flops"]
-
-        pb, pf = path_bytes(T, 1, False), path_flops(T)
-        t_hbm, t_mfma = pb / (HBM_PEAK_GBPS * 1e9), pf / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-        s = ms_step * 1e-3
-        path = dict(bytes=pb, flops=pf, hbm_bound_us=round(t_hbm * 1e6, 2), mfma_bound_us=round(t_mfma * 1e6, 2),
-                    frac_of_roofline=round(max(t_hbm, t_mfma) / s, 4), frac_of_mfma_bound=round(t_mfma / s, 4),
-                    achieved_GBps=round(pb / s / 1e9, 1), achieved_TFLOPs=round(pf / s / 1e12, 2))
+        kernels = {}
+        for name, ms in stage_ms.items():
+            m = model[name]
+            if ms <= 0.0005 or m["bytes"] == 0:
+                continue
+            kernels[name] = dict(ms_per_launch=round(ms, 5), own_bytes=m["bytes"],
+                                 own_GBps=round(m["bytes"] / (ms * 1e-3) / 1e9, 1),
+                                 own_frac_of_hbm=round(m["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                 traffic=measured_traffic(name, f"prefill T={T}"),
+                                 mfma_busy=measured_mfma(name, f"prefill T={T}"))
+        path = path_roofline([T], False, ms_step)
+        traffic = [k["traffic"] for k in kernels.values()]
+        roof = dict(bound="hbm", achieved=path["achieved_GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(path["achieved_GBps"] / HBM_PEAK_GBPS, 4),
+                    traffic=(sum(traffic) if traffic and all(t is not None for t in traffic) else None),
+                    kernel="whole prefill step (conv, WY, state and output kernels)",
+                    ms_per_launch=round(ms_step, 5), algorithmic_bytes=path["bytes"],
+                    algorithmic_flops=path["flops"], frac_of_mfma_bound=path["frac_of_mfma_bound"],
+                    note="algorithmic bytes = compulsory traffic of the step (raw q/k/v, gate, o, alpha/beta, "
+                         "final states, conv tails); traffic = counter-measured HBM bytes summed over the "
+                         "step's kernels")
 
         result.update({
             "metric": "GDN prefill tokens/s/GPU (48 v-heads, d=128) + decode step us at B=256; % roofline",
-            "value": round(T / s, 1),
+            "value": round(T / (ms_step * 1e-3), 1),
             "unit": "tokens/s",
             "n_gpus": 1,
             "steps": args.steps,
             "warmup": args.warmup,
             "ms_per_step": round(ms_step, 5),
             "ms_per_step_graph_replay": round(ms_step_graph, 5) if ms_step_graph is not None else None,
+            "ms_per_step_distribution": dist,
             "higher_is_better": True,
             "scaling": "weak",
             "vs_baseline": None,
@@ -456,10 +574,16 @@ def main():
                                    f"bf16 io, fp32 state, conv4+SiLU+L2+RMSNorm+sigmoid gate",
                        "batch": 1, "seq_len": T},
             "roofline": roof,
-            "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
             "path_roofline": path,
+            "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+            "kernels": kernels,
             "wall_s": round(t_wall, 4),
         })
+        del inp, bufs
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "prefill", "configs") and not args.no_configs:
+        result["configs"] = config_legs(args, gdn, dev, stream)
 
     if args.only in ("all", "decode") and not args.no_decode:
         # ---------------- decode: B sequences, one token each ------------------------------------
@@ -490,12 +614,16 @@ def main():
         d1.record(stream)
         torch.cuda.synchronize()
         us = d0.elapsed_time(d1) * 1e3 / S
+        it = iter(range(S))
+        ddist = step_distribution(lambda: dstep(next(it)), S, stream)
         db = decode_bytes(B)
         gbps = db / (us * 1e-6) / 1e9
         result["decode"] = {
             "workload": f"decode step, B={B} sequences x 1 token, 16 QK / 48 value heads, d=128, bf16 io, "
                         f"fp32 state in place, {S} consecutive steps",
             "us_per_step": round(us, 2),
+            "us_per_step_median": round(ddist["median"] * 1e3, 2),
+            "us_per_step_p10_p90": [round(ddist["p10"] * 1e3, 2), round(ddist["p90"] * 1e3, 2)],
             "roofline": dict(bound="hbm", achieved=round(gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                              frac=round(gbps / HBM_PEAK_GBPS, 4),
                              traffic=measured_traffic("decode", f"decode B={B}"), kernel="decode",
@@ -623,7 +751,7 @@ def main():
         result["backward"] = backward_leg(args, dev, stream)
 
     if not args.no_cpu_baseline and args.only == "all":
-        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens, args.decode_batch)
 
     print(json.dumps(result), flush=True)
 
