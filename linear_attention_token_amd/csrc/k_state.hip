@@ -21,6 +21,8 @@
 // K^T, the wave's U, G), which two producer waves stream through an LDS ring; the compute waves
 // read the next chunk's operands from the ring into registers while the current chunk's MFMAs
 // run, and the barrier between chunks does not wait for those reads.
+#include <atomic>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -308,12 +310,17 @@ hipError_t launch_state(const Problem& p, const Workspace& ws, const float* stat
   const int64_t units = int64_t(p.n_seqs) * p.hk;
   StateArgs a{ws.seq_chunk_off, int(units), p.hk, p.hv, R, ws.G, ws.Wk, ws.U, ws.KT, ws.ST, ws.WT,
               state_in, state_out};
-  static bool attr_set = false;  // same value on every device; idempotent, so a race is harmless
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_state),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kStateSmem));
+  // the kernel's LDS limit is raised once per device (an idempotent call, so a race only repeats it)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (!(attr_set.load() & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_state), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            int(kStateSmem));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.fetch_or(bit);
   }
   hipLaunchKernelGGL(k_state, dim3(unsigned(xcd_blocks(units, R * kSlices))), dim3(64 * (kComputeWaves + kProducers)),
                      kStateSmem, s, a);
