@@ -13,9 +13,9 @@
  *   5. a sigmoid output gate, elementwise (paper summary, Method: normalised, then gated).
  *
  * Conventions shared by every entry point:
- *   - Tensor pointers are DEVICE pointers owned by the caller. The library allocates no memory
- *     (the projections' GEMM library keeps one handle per device), keeps no other state between
- *     calls and never synchronises: work is enqueued on the
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library allocates no memory,
+ *     keeps no state between calls (beyond, per device, the kernels' raised LDS limits and the
+ *     static scratch of gdn_prefill_static) and never synchronises: work is enqueued on the
  *     caller's stream (`hip_stream`, a hipStream_t; NULL = the default stream) and the call
  *     returns after the enqueue. Device faults surface at the caller's next synchronisation.
  *   - Arguments are validated on the host first. On failure the call returns a status, enqueues
@@ -196,9 +196,10 @@ gdn_status gdn_commit(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, const in
  *     alpha = exp(-exp(a_log[h]) * softplus(a + dt_bias[h])),  beta = sigmoid(b),  [a | b] = x W_ab^T.
  * Weights use the linear-layer layout [out features][in features], row-major, bf16.
  *
- * gdn_proj_workspace: bytes of device workspace both calls need (the GEMM library's scratch).
+ * gdn_proj_workspace: bytes of device workspace both calls need: 0 (the arguments are kept so callers
+ * need not change; `workspace` may be NULL).
  *
- * gdn_in_proj (T tokens, hidden width H, H % 32 == 0, HV <= 64):
+ * gdn_in_proj (T tokens, hidden width H, H % 32 == 0):
  *   x        bf16 [T][H], row stride ld_x (>= H, a multiple of 8): the normalised residual stream.
  *   w_qkv    bf16 [C_tot][H]: output channels in the conv's order (q heads, k heads, v heads).
  *   w_z      bf16 [HV*d_v][H]: gate logits.   w_ab  bf16 [2*HV][H]: a (rows 0..HV-1), then b.
@@ -208,9 +209,10 @@ gdn_status gdn_commit(const gdn_cfg* cfg, int32_t batch, int32_t n_tok, const in
  *   alpha, beta  fp32 [T][HV] out (gate pre-activations accumulated in fp32).
  * gdn_out_proj: y bf16 [T][H] = o W_out^T with o bf16 [T][HV*d_v] (the mixer output) and
  *   w_out bf16 [H][HV*d_v].
- * The plain products run in hipBLASLt (bf16 in, fp32 accumulate, bf16 out); the first call on a
- * device creates a hipBLASLt handle that lives until the process ends, and each GEMM shape's
- * algorithm is chosen once. Returns GDN_E_UNSUPPORTED for fp32 io. */
+ * Both calls are one hand-written bf16 MFMA GEMM kernel (fp32 accumulate): the input projection runs
+ * over the stacked weights [w_qkv | w_z | w_ab] in one launch, writes q | k | v and z in bf16 and
+ * applies the gate formula to the fp32 pre-activations [a | b] in its epilogue. They allocate nothing
+ * and keep no state. hidden must be a multiple of 32; returns GDN_E_UNSUPPORTED for fp32 io. */
 gdn_status gdn_proj_workspace(size_t* bytes);
 gdn_status gdn_in_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const void* x, int64_t ld_x,
                        const void* w_qkv, const void* w_z, const void* w_ab, const float* a_log,

@@ -110,6 +110,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const short8& a, const short8& b, 
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 MFMA, fp32 accumulate. With lane l, i = l % 32, q = l / 32:
+//   A operand: row i, 8 consecutive k starting at 8q;  B operand: column i, the same 8 k;
+//   accumulator element e: row 8 (e / 4) + 4q + e % 4, column i.
+// One wave per SIMD keeps the matrix pipe busier with this shape than with 16x16x32.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32x32x16(const short8& a, const short8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
 // 16x16x4 fp32 MFMA. A: row i, k = q; B: column i, k = q; accumulator as above.
 __device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -146,14 +156,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
 }
 // 16 (dma16) or 4 (dma4) bytes per lane from gptr to LDS address lds + size * lane; `lds` must be
-// the same in all lanes.
+// the same in all lanes. M0 (the LDS base of these loads) is an output of the asm, so the compiler
+// keeps no value of its own in M0 across it.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0v) : "memory");
+  int m0_out;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : "={m0}"(m0_out) : "v"(gptr), "s"(m0v) : "memory");
+  (void)m0_out;
 }
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(m0v) : "memory");
+  int m0_out;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" : "={m0}"(m0_out) : "v"(gptr), "s"(m0v) : "memory");
+  (void)m0_out;
 }
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
 template <int n>

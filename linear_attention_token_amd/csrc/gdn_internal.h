@@ -140,12 +140,13 @@ hipError_t launch_verify(const Problem& p, int batch, int n_tok, const void* q, 
 hipError_t launch_commit(const Problem& p, int batch, int n_tok, const int32_t* n_accept, const MtpLog& log,
                          void* conv_state, float* state, hipStream_t s);
 
-// Projections around the mixer (bf16): hipBLASLt GEMM D (M x N, column-major, ld ldd) = A^T B with
-// A (K x M, ld lda), B (K x N, ld ldb); and the fused gate kernel (alpha, beta from x W_ab^T).
-constexpr size_t kProjWorkspace = size_t(32) << 20;  // hipBLASLt workspace the projections need
-hipError_t gemm_bf16_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                        void* D, int64_t ldd, void* ws, size_t ws_bytes, hipStream_t s, const char** why);
-hipError_t launch_gates(const void* x, int64_t ld_x, int64_t T, int H, const void* w_ab, int hv, const float* a_log,
-                        const float* dt_bias, float* alpha, float* beta, hipStream_t s);
+// Projections around the mixer (bf16), one MFMA GEMM kernel: the input projection over the stacked
+// weights [W_qkv | W_z | W_ab] (q | k | v and gate logits in bf16, alpha and beta from the fp32 gate
+// pre-activations), and the output projection.
+hipError_t launch_in_proj(const Problem& p, int H, int64_t T, const void* x, int64_t ld_x, const void* w_qkv,
+                          const void* w_z, const void* w_ab, const float* a_log, const float* dt_bias, void* qkv,
+                          void* z, float* alpha, float* beta, hipStream_t s);
+hipError_t launch_out_proj(const Problem& p, int H, int64_t T, const void* o, const void* w_out, void* y,
+                           hipStream_t s);
 
 }  // namespace gdn

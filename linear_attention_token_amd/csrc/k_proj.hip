@@ -1,5 +1,5 @@
-// The layer's projections around the mixer: input projection (q | k | v and the gate logits from
-// one fused input matrix), the data-dependent decay and write gates, and the output projection.
+// The layer's projections around the mixer: input projection (q | k | v, the gate logits and the
+// decay / write gates from one fused input matrix) and the output projection.
 //
 // The paper reading "Qwen3.8-Flash-Next" (方法) sends the normalised residual stream through learned
 // projections before the short conv, with a data-dependent decay gate and a write gate; the analysis
@@ -9,195 +9,297 @@
 //     alpha = exp(-exp(A_h) softplus(a + delta_h)),   beta = sigmoid(b),
 // with [a | b] = x W_ab and per-head vectors A, delta.
 //
-// The plain products (q | k | v, gate logits, output projection) are library GEMMs (hipBLASLt, bf16
-// in, fp32 accumulate, bf16 out). The gate pre-activations must stay fp32 (alpha is steep in a), so
-// they come from a kernel of their own that multiplies on bf16 MFMA with fp32 accumulation and
-// applies the gate formula in the epilogue.
+// Both projections are one bf16 MFMA GEMM kernel, out[t][n] = sum_k x[t][k] W[n][k] with fp32
+// accumulation. The input projection runs it once over the stacked weight rows [W_qkv | W_z | W_ab]:
+// column blocks of q | k | v and of the gate logits leave in bf16, and the 2 HV gate columns go
+// through the gate formula in fp32 in the same epilogue (alpha is steep in a, so a must not be
+// rounded to bf16 first). Weights are in the linear-layer layout [out features][in features],
+// row-major, so both operands are K-contiguous rows.
 //
-// Weights are in the linear-layer layout [out features][in features], row-major: every MFMA operand
-// piece is then 16 consecutive bytes of a row.
-#include <hipblaslt/hipblaslt.h>
-
-#include <mutex>
-
+// Kernel: a block computes a 256 (or 128, for narrow outputs) out features x 256 tokens tile with four
+// waves (one per SIMD) of 128 (64) x 128 on 32x32x16 bf16 MFMA (out features as the A operand, tokens as the B operand; each lane
+// ends with runs of 4 consecutive output features of one token; the tile is staged in LDS and stored
+// as 16-byte pieces of token rows). K advances in steps of 32 through a
+// five-slot LDS ring filled by direct global->LDS loads three steps ahead. Blocks are numbered so that
+// the 32 blocks an XCD runs at once form a 4 x 8 group of tiles that share their operand panels in
+// that XCD's L2.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-constexpr int kGateTok = 16;   // tokens per block of the gate kernel
-constexpr int kGateWaves = 8;  // waves per block, each a slice of the k-steps
-constexpr int kGateBatch = 5;  // k-steps whose operands a wave loads before multiplying any
+namespace {
 
-// [a | b] = x W_ab^T for 16 tokens on 16x16x32 bf16 MFMA, NT column tiles of 16 (2 HV <= 16 NT).
-// Wave w takes k-steps w, w + 8, ...; it loads kGateBatch steps of operands (its x piece and the NT
-// weight pieces of each) before multiplying, so a block's whole reduction costs about two memory
-// round trips; the eight partial tiles are summed in LDS, then the gates.
-template <int NT>
-__global__ void __launch_bounds__(64 * kGateWaves) k_gates(const uint16_t* __restrict__ x, int64_t ld_x, int64_t T,
-                                                          int H, const uint16_t* __restrict__ w_ab, int hv,
-                                                          const float* __restrict__ a_log,
-                                                          const float* __restrict__ dt_bias,
-                                                          float* __restrict__ alpha, float* __restrict__ beta) {
-  __shared__ float part[kGateWaves][NT][16][16];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, li = lane & 15, lq = lane >> 4;
-  const int64_t t0 = int64_t(blockIdx.x) * kGateTok;
-  const int ncol = 2 * hv, nks = H / 32;
-  const int64_t row = min(t0 + li, T - 1);  // rows past the end read the last row, not stored
-  const uint16_t* xr = x + row * ld_x + 8 * lq;
-  const uint16_t* wr[NT];
+constexpr int kTok = 256;                // tokens per block
+constexpr int kKStep = 32;               // k per ring slot
+constexpr int kRingG = 5;                // ring slots
+constexpr int kAhead = kRingG - 2;       // k-steps loaded ahead of the one being multiplied
+constexpr int kGroupM = 8, kGroupT = 4;  // tiles of a block group: 8 feature tiles x 4 token tiles
+constexpr int kMaxGateHeads = 3072;      // value heads the epilogue's LDS holds gate vectors for
+
+// Per feature-tile width FT (256, or 128 when there are too few 256-wide tiles to fill the chip):
+template <int FT> struct Geo {
+  static constexpr int kPanelW = FT * kKStep * 2;                  // W panel bytes per slot
+  static constexpr int kPanelX = kTok * kKStep * 2;                // x panel bytes per slot
+  static constexpr int kSlot = kPanelW + kPanelX;
+  static constexpr int kWLoads = FT / 64, kLoads = FT / 64 + 4;    // 1 KB loads per wave and slot
+  static constexpr int kMI = FT / 64;                              // 32-row feature tiles per wave
+  static constexpr int kCLd = FT + 8;                              // bytes per token row of a wave's staged tile
+  static constexpr int kGateParams = 4 * 128 * kCLd;               // exp(a_log), dt_bias in the epilogue
+  static constexpr size_t kSmem = size_t(kRingG) * kSlot;
+  static_assert(kSmem <= 160 * 1024, "LDS budget");
+  static_assert(size_t(kGateParams) + 8 * kMaxGateHeads <= kSmem, "gate vectors fit beside the staged tiles");
+  static_assert(128 * kCLd >= 32 * 132 * 4, "a wave's staging area holds a 32-token fp32 gate tile");
+};
+
+// Rows of a panel are 64 bytes (four 16-byte pieces of k); piece p of row r sits at slot
+// p ^ ((r >> 2) & 3), so the operand reads of 16 consecutive rows at one piece hit distinct banks.
+__device__ __forceinline__ int pkey(int r) { return (r >> 2) & 3; }
+
+struct GemmArgs {
+  const uint16_t* x;        // [T][ld_x] bf16 activations
+  int64_t ld_x, T;
+  int K;                    // in features (a multiple of 32)
+  const uint16_t* w[3];     // weight segments [rows][K]
+  int64_t seg_end[3];       // cumulative row counts of the segments (output features)
+  uint16_t* out[2];         // bf16 outputs of segments 0 and 1: [T][ld_out]
+  int64_t ld_out[2];
+  // segment 2, when gates != 0: the gate pre-activations [a | b] (2 hv columns)
+  int gates, hv;
+  const float *a_log, *dt_bias;
+  float *alpha, *beta;      // [T][hv]
+  int n_tiles_m, n_tiles_t;
+};
+
+// Source row of output feature n (clamped into the last segment's rows).
+__device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& a, int64_t n) {
+  const int64_t N = a.seg_end[2];
+  n = min(n, N - 1);
+  if (n < a.seg_end[0]) return a.w[0] + n * a.K;
+  if (n < a.seg_end[1]) return a.w[1] + (n - a.seg_end[0]) * a.K;
+  return a.w[2] + (n - a.seg_end[1]) * a.K;
+}
+
+template <int FT>
+__global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
+  using G = Geo<FT>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // block -> tile: XCD x runs blocks b = 8 j + x; the 32 consecutive j of one XCD form one group
+  const int b = int(blockIdx.x), x = b & 7, j = b >> 3;
+  const int n_gm = (a.n_tiles_m + kGroupM - 1) / kGroupM;
+  const int grp = (j / (kGroupM * kGroupT)) * 8 + x, in = j % (kGroupM * kGroupT);
+  const int tmr = (grp % n_gm) * kGroupM + in % kGroupM, tt = (grp / n_gm) * kGroupT + in / kGroupM;
+  if (tmr >= a.n_tiles_m || tt >= a.n_tiles_t) return;
+  const int tm = a.n_tiles_m - 1 - tmr;  // the last feature tiles (the gate columns) go first
+  const int64_t n0 = int64_t(tm) * FT, t0 = int64_t(tt) * kTok;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wt = w >> 1;  // this wave's quarter: features (FT / 2) wm .., tokens 128 wt ..
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const int nks = a.K / kKStep;
+
+  // This wave's direct loads of one slot: W load i < kWLoads covers W panel rows 16 (kWLoads w + i) ..
+  // + 15, x load i covers x panel rows 16 (4w + i) .. + 15; lane l takes row 16 (.) + l / 4, slot l % 4.
+  const uint16_t* src[G::kLoads];
+  uint32_t dst[G::kLoads];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) wr[j] = w_ab + int64_t(min(16 * j + li, ncol - 1)) * H + 8 * lq;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = w; s0 < nks; s0 += kGateWaves * kGateBatch) {
-    short8 av[kGateBatch], bv[kGateBatch][NT];
-#pragma unroll
-    for (int u = 0; u < kGateBatch; ++u) {
-      const int s = min(s0 + kGateWaves * u, nks - 1);  // clamped steps are loaded and not used
-      av[u] = ld_short8(xr + 32 * s);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) bv[u][j] = ld_short8(wr[j] + 32 * s);
-    }
-#pragma unroll
-    for (int u = 0; u < kGateBatch; ++u)
-      if (s0 + kGateWaves * u < nks) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j] = mfma16x16x32(av[u], bv[u][j], acc[j]);
-      }
+  for (int i = 0; i < G::kLoads; ++i) {
+    const bool wl = i < G::kWLoads;
+    const int blk = wl ? G::kWLoads * w + i : 4 * w + (i - G::kWLoads);
+    const int r = 16 * blk + (lane >> 2), piece = (lane & 3) ^ pkey(r);
+    src[i] = (wl ? weight_row(a, n0 + r) : a.x + min(t0 + r, a.T - 1) * a.ld_x) + 8 * piece;
+    dst[i] = (wl ? 0 : G::kPanelW) + blk * 1024;
   }
-  // acc[j][r]: token 4lq + r, column 16j + li
+  auto issue = [&](int ks, int slot) {
+    const uint32_t sa = ring + uint32_t(slot * G::kSlot);
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
+    for (int i = 0; i < G::kLoads; ++i) dma16(src[i] + int64_t(ks) * kKStep, sa + dst[i]);
+  };
+  auto barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // acc[i][jt]: 32 x 32 tile, element e: feature 8 (e / 4) + 4 hq + e % 4, token l32 (within tiles i, jt)
+  const int l32 = lane & 31, hq = lane >> 5;
+  f32x16 acc[G::kMI][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[w][j][4 * lq + r][li] = acc[j][r];
-  __syncthreads();
-  for (int i = t; i < kGateTok * ncol; i += 64 * kGateWaves) {
-    const int tok = i / ncol, col = i - tok * ncol;
-    if (t0 + tok >= T) continue;
-    float v = 0.f;
+  for (int i = 0; i < G::kMI; ++i)
 #pragma unroll
-    for (int ww = 0; ww < kGateWaves; ++ww) v += part[ww][col >> 4][tok][col & 15];
-    if (col < hv) {
-      const float u = v + dt_bias[col];
-      const float sp = fmaxf(u, 0.f) + log1pf(__expf(-fabsf(u)));  // softplus without overflow
-      alpha[(t0 + tok) * hv + col] = __expf(-__expf(a_log[col]) * sp);
-    } else {
-      beta[(t0 + tok) * hv + (col - hv)] = sigmoidf_(v);
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][jt][e] = 0.f;
+
+  // waits until at most `later` k-steps issued after the next one are still in flight
+  auto settle = [&](int later) {
+    if (later >= 2) wait_vm<2 * G::kLoads>();
+    else if (later == 1) wait_vm<G::kLoads>();
+    else wait_vm<0>();
+  };
+  for (int k = 0; k < kAhead && k < nks; ++k) issue(k, k);
+  settle(min(kAhead, nks) - 1);
+  barrier();
+  for (int ks = 0; ks < nks; ++ks) {
+    if (ks + kAhead < nks) issue(ks + kAhead, (ks + kAhead) % kRingG);
+    const unsigned char* sb = smem + size_t(ks % kRingG) * G::kSlot;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // two k-substeps of 16: pieces 2u + hq of the 64-byte rows
+      short8 af[G::kMI], bf[4];
+#pragma unroll
+      for (int i = 0; i < G::kMI; ++i) {
+        const int r = (FT / 2) * wm + 32 * i + l32;
+        af[i] = *reinterpret_cast<const short8*>(sb + r * 64 + (((2 * u + hq) ^ pkey(r)) << 4));
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int r = 128 * wt + 32 * jt + l32;
+        bf[jt] = *reinterpret_cast<const short8*>(sb + G::kPanelW + r * 64 + (((2 * u + hq) ^ pkey(r)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < G::kMI; ++i)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) acc[i][jt] = mfma32x32x16(af[i], bf[jt], acc[i][jt]);
+    }
+    // the next step has landed (later steps may stay in flight)
+    settle(min(ks + kAhead, nks - 1) - (ks + 1));
+    barrier();
+  }
+
+  // ---- epilogue. The bf16 outputs go through this wave's tile in LDS (the ring is free after the
+  // last barrier) and leave as 16-byte pieces of token rows; the gate columns are finished from the
+  // fp32 registers. ----
+  unsigned char* const cs = smem + size_t(w) * 128 * G::kCLd;
+#pragma unroll
+  for (int i = 0; i < G::kMI; ++i)
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {  // features 32i + 8g + 4hq .. +3 of token 32jt + l32
+        const f32x16& v = acc[i][jt];
+        *reinterpret_cast<uint2*>(cs + (32 * jt + l32) * G::kCLd + (32 * i + 8 * g + 4 * hq) * 2) =
+            make_uint2(pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3]));
+      }
+  const int64_t nw = n0 + (FT / 2) * wm;  // first feature of this wave's tile
+  constexpr int kRowPieces = FT / 16;      // 16-byte pieces per staged token row (FT / 2 features)
+#pragma unroll 4
+  for (int k = 0; k < 2 * kRowPieces; ++k) {
+    const int pc = lane + 64 * k, tl = pc / kRowPieces, seg8 = pc % kRowPieces;
+    const int64_t t = t0 + 128 * wt + tl, n = nw + 8 * seg8;
+    if (t >= a.T || n >= a.seg_end[1]) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(cs + tl * G::kCLd + seg8 * 16);
+    if (n < a.seg_end[0]) *reinterpret_cast<uint4*>(a.out[0] + t * a.ld_out[0] + n) = v;
+    else *reinterpret_cast<uint4*>(a.out[1] + t * a.ld_out[1] + (n - a.seg_end[0])) = v;
+  }
+  if (!a.gates || nw + FT / 2 <= a.seg_end[1]) return;
+  // Gate columns. exp(a_log) and dt_bias are staged in LDS by this wave (another wave of the block may
+  // write the same values); then, per 32-token tile, the fp32 accumulators go to this wave's staging
+  // area (its bf16 rows are all stored by now) and a compact loop applies the formula.
+  float* const gp = reinterpret_cast<float*>(smem + G::kGateParams);
+  for (int c = lane; c < a.hv; c += 64) {
+    gp[c] = __expf(a.a_log[c]);
+    gp[a.hv + c] = a.dt_bias[c];
+  }
+  float* const fs = reinterpret_cast<float*>(cs);  // [32 tokens][132] fp32
+  const int c_lo = int(max<int64_t>(a.seg_end[1] - nw, 0)), c_hi = int(min<int64_t>(a.seg_end[2] - nw, FT / 2));
+  const int nc = c_hi - c_lo;
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+    for (int i = 0; i < G::kMI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& v = acc[i][jt];
+        *reinterpret_cast<float4*>(fs + l32 * 132 + 32 * i + 8 * g + 4 * hq) =
+            make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+      }
+    for (int e = lane; e < 32 * nc; e += 64) {
+      const int tl = e / nc, c = c_lo + (e - tl * nc);
+      const int64_t t = t0 + 128 * wt + 32 * jt + tl;
+      if (t >= a.T) continue;
+      const int col = int(nw + c - a.seg_end[1]);
+      const float v = fs[tl * 132 + c];
+      if (col < a.hv) {
+        const float uu = v + gp[a.hv + col];
+        const float sp = fmaxf(uu, 0.f) + __logf(1.f + __expf(-fabsf(uu)));  // softplus without overflow
+        a.alpha[t * a.hv + col] = __expf(-gp[col] * sp);
+      } else {
+        a.beta[t * a.hv + (col - a.hv)] = sigmoidf_(v);
+      }
     }
   }
 }
 
-// ---- hipBLASLt: D (M x N, column-major, ld ldd) = A^T B, A (K x M, ld lda), B (K x N, ld ldb); bf16
-// in and out, fp32 accumulate. A row-major [rows][K] matrix is a column-major K x rows one, so with
-// A = a weight [out][in] and B = activations [T][in] this is activations x weight^T, row-major
-// [T][out]. One handle per device, and the heuristic's first algorithm cached per shape. ----
-namespace {
-struct GemmKey {
-  int dev;
-  int64_t M, N, K, lda, ldb, ldd;
-  bool operator==(const GemmKey& o) const {
-    return dev == o.dev && M == o.M && N == o.N && K == o.K && lda == o.lda && ldb == o.ldb && ldd == o.ldd;
-  }
-};
-struct GemmEntry {
-  GemmKey key;
-  hipblasLtMatmulAlgo_t algo;
-  size_t ws;
-};
-std::mutex g_mu;
-hipblasLtHandle_t g_handle[64] = {};
-GemmEntry g_cache[64];
-int g_ncache = 0;
-}  // namespace
+bool g_smem_ok[2][64] = {};  // devices on which each kernel's LDS limit was raised (idempotent call)
 
-hipError_t gemm_bf16_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                        void* D, int64_t ldd, void* ws, size_t ws_bytes, hipStream_t s, const char** why) {
+template <int FT>
+hipError_t launch_ft(GemmArgs& a, hipStream_t s) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) { *why = "device index out of range"; return hipErrorInvalidDevice; }
-  hipblasLtMatmulDesc_t op = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-  hipblasLtMatmulAlgo_t algo;
-  bool have = false;
-  std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_handle[dev] && hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) {
-    g_handle[dev] = nullptr;
-    *why = "hipblasLtCreate failed";
-    return hipErrorUnknown;
+  bool& ok = g_smem_ok[FT == 256][dev & 63];
+  if (!ok) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm<FT>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            int(Geo<FT>::kSmem));
+    if (e != hipSuccess) return e;
+    ok = true;
   }
-  const hipblasLtHandle_t h = g_handle[dev];
-  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-  hipblasStatus_t st = hipblasLtMatmulDescCreate(&op, HIPBLAS_COMPUTE_32F, HIP_R_32F);
-  if (st == HIPBLAS_STATUS_SUCCESS)
-    st = hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta));
-  if (st == HIPBLAS_STATUS_SUCCESS)
-    st = hipblasLtMatmulDescSetAttribute(op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb));
-  if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, K, M, lda);
-  if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, K, N, ldb);
-  if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&ld, HIP_R_16BF, M, N, ldd);
-  const GemmKey key{dev, M, N, K, lda, ldb, ldd};
-  if (st == HIPBLAS_STATUS_SUCCESS) {
-    for (int i = 0; i < g_ncache; ++i)
-      if (g_cache[i].key == key && g_cache[i].ws <= ws_bytes) {
-        algo = g_cache[i].algo;
-        have = true;
-      }
-    if (!have) {
-      hipblasLtMatmulPreference_t pref = nullptr;
-      uint64_t cap = ws_bytes;
-      constexpr int kCand = 8;
-      hipblasLtMatmulHeuristicResult_t res[kCand];
-      int n = 0;
-      st = hipblasLtMatmulPreferenceCreate(&pref);
-      if (st == HIPBLAS_STATUS_SUCCESS)
-        st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof(cap));
-      if (st == HIPBLAS_STATUS_SUCCESS)
-        st = hipblasLtMatmulAlgoGetHeuristic(h, op, la, lb, ld, ld, pref, kCand, res, &n);
-      if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-      // a returned entry is usable only if its own state is success (its other fields are
-      // undefined otherwise) and its workspace fits the caller's
-      int pick = -1;
-      for (int i = 0; st == HIPBLAS_STATUS_SUCCESS && i < n && i < kCand && pick < 0; ++i)
-        if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes) pick = i;
-      if (st == HIPBLAS_STATUS_SUCCESS && pick < 0) st = HIPBLAS_STATUS_NOT_SUPPORTED;
-      if (st == HIPBLAS_STATUS_SUCCESS) {
-        algo = res[pick].algo;
-        have = true;
-        if (g_ncache < 64) g_cache[g_ncache++] = GemmEntry{key, algo, res[pick].workspaceSize};
-      }
-    }
-  }
-  const float one = 1.f, zero = 0.f;
-  if (st == HIPBLAS_STATUS_SUCCESS && have)
-    st = hipblasLtMatmul(h, op, &one, A, la, B, lb, &zero, D, ld, D, ld, &algo, ws, ws_bytes, s);
-  if (ld) hipblasLtMatrixLayoutDestroy(ld);
-  if (lb) hipblasLtMatrixLayoutDestroy(lb);
-  if (la) hipblasLtMatrixLayoutDestroy(la);
-  if (op) hipblasLtMatmulDescDestroy(op);
-  if (st != HIPBLAS_STATUS_SUCCESS) {
-    *why = "hipBLASLt matmul failed";
-    return hipErrorUnknown;
-  }
+  a.n_tiles_m = int((a.seg_end[2] + FT - 1) / FT);
+  a.n_tiles_t = int((a.T + kTok - 1) / kTok);
+  const int n_gm = (a.n_tiles_m + kGroupM - 1) / kGroupM, n_gt = (a.n_tiles_t + kGroupT - 1) / kGroupT;
+  const int64_t groups = int64_t(n_gm) * n_gt;
+  const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * kGroupT;  // every XCD walks whole groups
+  hipLaunchKernelGGL(k_gemm<FT>, dim3(unsigned(blocks)), dim3(256), Geo<FT>::kSmem, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gates(const void* x, int64_t ld_x, int64_t T, int H, const void* w_ab, int hv, const float* a_log,
-                        const float* dt_bias, float* alpha, float* beta, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const dim3 grid(unsigned((T + kGateTok - 1) / kGateTok)), block(64 * kGateWaves);
-  const auto* xp = static_cast<const uint16_t*>(x);
-  const auto* wp = static_cast<const uint16_t*>(w_ab);
-  switch ((2 * hv + 15) / 16) {  // column tiles; hv <= 64 is checked by the caller
-#define GDN_GATES(NT) \
-  case NT: hipLaunchKernelGGL(k_gates<NT>, grid, block, 0, s, xp, ld_x, T, H, wp, hv, a_log, dt_bias, alpha, beta); break;
-    GDN_GATES(1) GDN_GATES(2) GDN_GATES(3) GDN_GATES(4) GDN_GATES(5) GDN_GATES(6) GDN_GATES(7) GDN_GATES(8)
-#undef GDN_GATES
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+// 256-wide feature tiles unless there are too few of them to occupy a quarter of the chip's 256 CUs
+// (measured: at 160 tiles of 256 the wider tile is still faster than 320 of 128)
+hipError_t launch_gemm(GemmArgs& a, hipStream_t s) {
+  if (a.T == 0 || a.seg_end[2] == 0) return hipSuccess;
+  const int64_t tiles256 = ((a.seg_end[2] + 255) / 256) * ((a.T + kTok - 1) / kTok);
+  return tiles256 >= 64 ? launch_ft<256>(a, s) : launch_ft<128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_in_proj(const Problem& p, int H, int64_t T, const void* x, int64_t ld_x, const void* w_qkv,
+                          const void* w_z, const void* w_ab, const float* a_log, const float* dt_bias, void* qkv,
+                          void* z, float* alpha, float* beta, hipStream_t s) {
+  const int64_t C = p.C, vz = int64_t(p.hv) * p.dv;
+  GemmArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.ld_x = ld_x;
+  a.T = T;
+  a.K = H;
+  a.w[0] = static_cast<const uint16_t*>(w_qkv);
+  a.w[1] = static_cast<const uint16_t*>(w_z);
+  a.w[2] = static_cast<const uint16_t*>(w_ab);
+  a.seg_end[0] = C;
+  a.seg_end[1] = C + vz;
+  a.seg_end[2] = C + vz + 2 * p.hv;
+  a.out[0] = static_cast<uint16_t*>(qkv);
+  a.out[1] = static_cast<uint16_t*>(z);
+  a.ld_out[0] = C;
+  a.ld_out[1] = vz;
+  a.gates = 1;
+  a.hv = p.hv;
+  a.a_log = a_log;
+  a.dt_bias = dt_bias;
+  a.alpha = alpha;
+  a.beta = beta;
+  return launch_gemm(a, s);
+}
+
+hipError_t launch_out_proj(const Problem& p, int H, int64_t T, const void* o, const void* w_out, void* y,
+                           hipStream_t s) {
+  const int64_t vz = int64_t(p.hv) * p.dv;
+  GemmArgs a{};
+  a.x = static_cast<const uint16_t*>(o);
+  a.ld_x = vz;
+  a.T = T;
+  a.K = int(vz);
+  a.w[0] = a.w[1] = a.w[2] = static_cast<const uint16_t*>(w_out);
+  a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = H;
+  a.out[0] = a.out[1] = static_cast<uint16_t*>(y);
+  a.ld_out[0] = a.ld_out[1] = H;
+  a.gates = 0;
+  return launch_gemm(a, s);
 }
 
 }  // namespace gdn

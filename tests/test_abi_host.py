@@ -253,7 +253,8 @@ def test_verify_and_commit_reject_bad_arguments():
 def test_projections_reject_bad_arguments():
     c = gdn.gdn_cfg_default()
     n = ctypes.c_size_t(0)
-    assert lib.gdn_proj_workspace(ctypes.byref(n)) == 0 and n.value >= 1 << 20
+    n.value = 7
+    assert lib.gdn_proj_workspace(ctypes.byref(n)) == 0 and n.value == 0   # the kernels need no scratch
     _err(lib.gdn_proj_workspace(None), 1)
 
     def inp(cfg=c, H=2560, T=64, x=A, ld=2560, wq=A, wz=A, wab=A, al=A, dt=A, qkv=A, z=A, alpha=A, beta=A,
@@ -267,9 +268,7 @@ def test_projections_reject_bad_arguments():
         _err(call(cfg=gdn.gdn_cfg_default(io_dtype=gdn.GDN_F32)), 6)
         _err(call(H=100), 2)                     # hidden % 32
         _err(call(T=-1), 2)
-        _err(call(ws=None), 5)
-        _err(call(wsb=1024), 5)
-        _err(call(cfg=gdn.gdn_cfg_default(n_qk_heads=16, n_v_heads=80)), 6)  # HV > 64
+        _err(call(ws=None, wsb=0, T=-1), 2)      # no workspace is needed; the next problem is reported
     _err(inp(x=None), 1)
     _err(inp(beta=None), 1)
     _err(inp(ld=2000), 2)
