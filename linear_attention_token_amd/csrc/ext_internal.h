@@ -7,31 +7,6 @@
 
 namespace gdn {
 
-// ---- recurrence backward (fp32, d = 128) ----
-// Each (sequence, value head) chain runs as 8 workgroups of 16 value columns.
-constexpr int kBwdForward = 1, kBwdReverse = 2, kBwdWriteY = 4;  // BwdArgs::mode bits
-struct BwdArgs {
-  int mode;                      // forward pass (keep states), reverse pass, y output in the forward
-  float* y;                      // [T][HV][128] raw recurrence output (kBwdWriteY)
-  const int32_t* cu;
-  int n_seqs;
-  int64_t T;
-  int hk, hv;
-  float scale;
-  const float *q, *k, *v;        // [T][HK][128], [T][HK][128], [T][HV][128]
-  const float *alpha, *beta;     // [T][HV]
-  const float* s0;               // [N][HV][128][128] or null (zeros)
-  const float* dy;               // [T][HV][128]
-  const float* dsf;              // [N][HV][128][128] or null (zeros)
-  float *dqv, *dkv;              // workspace [T][HV][8 slices][128]: per-slice partials
-  float *dalpha_part, *dbeta_part;  // workspace [T][HV][8]
-  float* dv;                     // [T][HV][128] out
-  float* ds0;                    // [N][HV][128][128] or null
-  float* states;                 // workspace [T][HV][8 slices][2 rows][256 threads][4]: every state
-  float* errs;                   // workspace [T][HV][128]
-};
-hipError_t launch_bwd(const BwdArgs& a, float* dq, float* dk, float* dalpha, float* dbeta, hipStream_t s);
-
 // The mixer's steps before the recurrence, backwards (conv + SiLU + L2), fp32, d = 128.
 struct BwdMixArgs {
   const int32_t* cu;
@@ -54,6 +29,37 @@ struct BwdMixArgs {
 hipError_t launch_norm_gate_bwd(int64_t rows, const float* y, const float* z, const float* dout, const float* norm_w,
                                 float eps, float* dy, float* dz, float* dnorm_w, float* dw_part, hipStream_t s);
 hipError_t launch_mixer_input_bwd(const BwdMixArgs& m, hipStream_t s);
+
+// ---- chunked backward of the recurrence (fp32, d = 128, 64-token chunks) ----
+// Per-item arrays: item = chunk c x value head h (index c * hv + h), tiles zero-padded to 64 rows.
+struct CBwdArgs {
+  const int32_t* cu;
+  int n_seqs;
+  int64_t T;
+  int hk, hv, R;
+  float scale;
+  int64_t nc_max;                 // chunk slots: T / 64 + n_seqs
+  int32_t* seq_off;               // [n_seqs + 1] first chunk of each sequence
+  int4* tab;                      // [nc_max] (start token, length, sequence, 0)
+  const float *q, *k, *v;         // [T][HK][128], [T][HK][128], [T][HV][128] (normalised q, k; v)
+  const float *alpha, *beta;      // [T][HV]
+  const float *s0, *dy, *dsf;     // initial states (or null), dL/dy [T][HV][128], dL/dS_final (or null)
+  float* y;                       // raw y [T][HV][128] written by the forward pass (or null)
+  float *dv, *dalpha, *dbeta, *ds0;
+  float *dqh, *dkh;               // [T][HV][128] per value head, before the group sums
+  float *Qi, *Ki, *Vi, *dYi, *bV, *bgK, *U, *Wk, *W, *dW, *dKt, *X, *dWk, *dQ, *dK, *dbV, *dbgK;  // [I][64][128]
+  float *Kt, *gQ;                 // [I][64][128]: diag(exp(G_C - G)) K, diag(exp(G)) Q
+  float *KtT, *WkT;               // [I][128][64]: Kt^T, Wk^T
+  float *S, *dS;                  // [I][128][128]: state at the chunk start; dL/d(state after the chunk)
+  float *KK, *QK, *Am, *Pm, *Tm, *dP, *M1, *dT, *dA;  // [I][64][64]
+  float *G, *bt;                  // [I][64]
+  float* dgc;                     // [I][8] per-slice parts of <S, dS'>
+};
+size_t cbwd_workspace_bytes(int n_seqs, int64_t T, int hv);
+void cbwd_plan(CBwdArgs& a, void* base);  // sets nc_max and every workspace region
+// forward: chunk table, gather, WY, forward chunk pass (writes y when a.y); backward: the rest, then
+// dq, dk as sums over each QK head's value heads
+hipError_t launch_cbwd(const CBwdArgs& a, bool forward, bool backward, float* dq, float* dk, hipStream_t s);
 
 // ---- QSA compressed indexer ----
 constexpr int kSelSeg = 16384;  // scores per select workgroup (1024 threads x 16)

@@ -544,14 +544,9 @@ gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const voi
   return GDN_OK;
 }
 
-// Workspace of the recurrence backward: every state and error of the forward, per-slice partials of
-// dq and dk (8 slices of 16 value columns per value head) and of dalpha and dbeta.
-static size_t bwd_workspace_bytes(int64_t T, int hk, int hv) {
-  (void)hk;
-  const size_t th = size_t(T) * hv;
-  return align256(sizeof(float) * th * 128 * 128) + align256(sizeof(float) * th * 128) +
-         2 * align256(sizeof(float) * th * 8 * 128) + 2 * align256(sizeof(float) * th * 8);
-}
+// Workspace of the recurrence backward: per (64-token chunk, value head) item the chunk's tiles, its WY
+// factors and derivatives, the state at its start and the derivative of the state after it.
+static size_t bwd_workspace_bytes(int32_t n_seqs, int64_t T, int hv) { return cbwd_workspace_bytes(n_seqs, T, hv); }
 
 static gdn_status check_bwd(const gdn_cfg* cfg, int32_t n_seqs, int64_t T, Problem& p) {
   gdn_status st = check_cfg(cfg, p);
@@ -571,7 +566,7 @@ gdn_status gdn_recurrence_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs,
   gdn_status st = check_bwd(cfg, n_seqs, total_tokens, p);
   if (st != GDN_OK) return st;
   if (!bytes) return fail(GDN_E_NULL, "bytes is NULL");
-  *bytes = bwd_workspace_bytes(total_tokens, p.hk, p.hv);
+  *bytes = bwd_workspace_bytes(n_seqs, total_tokens, p.hv);
   return GDN_OK;
 }
 
@@ -594,35 +589,22 @@ gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t t
     if (ptr && !aligned16(ptr)) return fail(GDN_E_ALIGN, "a tensor pointer is not 16-byte aligned");
   if (!aligned4(alpha) || !aligned4(beta) || !aligned4(dalpha) || !aligned4(dbeta) || !aligned4(cu_seqlens))
     return fail(GDN_E_ALIGN, "alpha, beta, dalpha, dbeta and cu_seqlens must be 4-byte aligned");
-  const size_t need = bwd_workspace_bytes(total_tokens, p.hk, p.hv);
+  const size_t need = bwd_workspace_bytes(n_seqs, total_tokens, p.hv);
   if (!workspace || workspace_bytes < need)
     return fail(GDN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GDN_E_ALIGN, "workspace must be 256-byte aligned");
-  char* w = static_cast<char*>(workspace);
-  BwdArgs a{};
-  a.mode = kBwdForward | kBwdReverse;
+  CBwdArgs a{};
   a.cu = cu_seqlens;
   a.n_seqs = n_seqs;
   a.T = total_tokens;
   a.hk = p.hk;
   a.hv = p.hv;
+  a.R = p.hv / p.hk;
   a.scale = p.scale;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.s0 = state_in; a.dy = dy; a.dsf = dstate_out;
-  a.dv = dv;
-  a.ds0 = dstate_in;
-  const size_t th = size_t(total_tokens) * p.hv;
-  a.states = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 128 * 128);
-  a.errs = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 128);
-  a.dqv = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 8 * 128);
-  a.dkv = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 8 * 128);
-  a.dalpha_part = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 8);
-  a.dbeta_part = reinterpret_cast<float*>(w);
-  if (run(launch_bwd(a, dq, dk, dalpha, dbeta, static_cast<hipStream_t>(hip_stream)), "recurrence backward") != hipSuccess)
+  a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.ds0 = dstate_in;
+  cbwd_plan(a, workspace);
+  if (run(launch_cbwd(a, true, true, dq, dk, static_cast<hipStream_t>(hip_stream)), "recurrence backward") != hipSuccess)
     return GDN_E_HIP;
   return GDN_OK;
 }
@@ -631,7 +613,7 @@ gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t t
 // regions, y and dy, the recurrence-input derivatives and the conv-output derivatives.
 static size_t mixer_bwd_workspace_bytes(const Problem& p, int64_t T) {
   const size_t th = size_t(T) * p.hv, tk = size_t(T) * p.hk;
-  return align256(plan_workspace(p, nullptr).bytes) + bwd_workspace_bytes(T, p.hk, p.hv) +
+  return align256(plan_workspace(p, nullptr).bytes) + bwd_workspace_bytes(p.n_seqs, T, p.hv) +
          2 * align256(sizeof(float) * th * 128) + 2 * align256(sizeof(float) * tk * 128) +
          align256(sizeof(float) * th * 128) + align256(sizeof(float) * size_t(T) * size_t(p.C)) +
          align256(sizeof(float) * ((th + 63) / 64) * 128) + align256(sizeof(float) * size_t((T + 63) / 64) * p.C * 4);
@@ -690,29 +672,21 @@ gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens
   const Workspace fws = plan_workspace(p, w);
   w += align256(fws.bytes);
   const size_t th = size_t(total_tokens) * p.hv, tk = size_t(total_tokens) * p.hk;
-  BwdArgs a{};
+  CBwdArgs a{};
   a.cu = cu_seqlens;
   a.n_seqs = n_seqs;
   a.T = total_tokens;
   a.hk = p.hk;
   a.hv = p.hv;
+  a.R = p.hv / p.hk;
   a.scale = p.scale;
   a.q = static_cast<const float*>(fws.qhat);
   a.k = static_cast<const float*>(fws.khat);
   a.v = static_cast<const float*>(fws.vhat);
   a.alpha = alpha; a.beta = beta; a.s0 = state_in; a.dsf = dstate_out; a.ds0 = dstate_in;
-  a.states = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 128 * 128);
-  a.errs = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 128);
-  a.dqv = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 8 * 128);
-  a.dkv = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 8 * 128);
-  a.dalpha_part = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 8);
-  a.dbeta_part = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * th * 8);
+  a.dalpha = dalpha; a.dbeta = dbeta;
+  cbwd_plan(a, w);
+  w += align256(bwd_workspace_bytes(n_seqs, total_tokens, p.hv));
   float* y = reinterpret_cast<float*>(w);
   w += align256(sizeof(float) * th * 128);
   float* dy = reinterpret_cast<float*>(w);
@@ -743,14 +717,11 @@ gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens
   m.q = q; m.k = k; m.v = v; m.conv_w = conv_w; m.conv_in = conv_in;
   m.dqa = dqa; m.dka = dka; m.dva = dva; m.du = du;
   m.dq = dq; m.dk = dk; m.dv = dv; m.dconv_w = dconv_w; m.dconv_in = dconv_in; m.dw_part = dcw_part;
-  BwdArgs af = a, ar = a;
-  af.mode = kBwdForward | kBwdWriteY;
-  ar.mode = kBwdReverse;
   if (run(launch_conv(p, cu_seqlens, q, k, v, qrow, qrow, vrow, conv_w, conv_in, fws, false, s), "backward conv") != hipSuccess ||
-      run(launch_bwd(af, dqa, dka, dalpha, dbeta, s), "backward forward pass") != hipSuccess ||
+      run(launch_cbwd(a, true, false, dqa, dka, s), "backward forward pass") != hipSuccess ||
       run(launch_norm_gate_bwd(int64_t(th), y, gate, dout, norm_w, p.norm_eps, dy, dgate, dnorm_w, dw_part, s),
           "backward norm and gate") != hipSuccess ||
-      run(launch_bwd(ar, dqa, dka, dalpha, dbeta, s), "backward recurrence") != hipSuccess ||
+      run(launch_cbwd(a, false, true, dqa, dka, s), "backward recurrence") != hipSuccess ||
       run(launch_mixer_input_bwd(m, s), "backward conv, SiLU, L2") != hipSuccess)
     return GDN_E_HIP;
   return GDN_OK;

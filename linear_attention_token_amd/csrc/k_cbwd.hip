@@ -1,0 +1,713 @@
+// Chunked backward of the gated delta rule (fp32, d_k = d_v = 128, 64-token chunks).
+//
+// The forward recurrence of the analysis notes "Qwen3.8-Flash-Next：架构、效率与技术谱系" (§03 update
+// equations) re-associates, per chunk with chunk-start state S, G_t = sum_{s<=t} ln alpha_s, g = exp(G),
+// E[t,i] = exp(G_t - G_i), kd_i = exp(G_C - G_i) (C the chunk's last row), into
+//     A  = strict_lower(beta_t E[t,i] k_t.k_i),  T = (I + A)^-1,  U = T diag(beta) V,  Wk = T diag(beta g) K,
+//     W  = U - Wk S,   P = lower(E o Q K^T),   Y = scale (diag(g) Q S + P W),   S' = g_C S + K^T diag(kd) W.
+// Reverse mode takes these statements last to first. With dY scaled by `scale` and dS' the derivative of
+// the state after the chunk, the only sequential part is
+//     dW = diag(kd) K dS' + P^T dY,        dS = g_C dS' + Q^T diag(g) dY - Wk^T dW,
+// a pass over the chunks in reverse, independent per value column like the forward. Everything else is
+// chunk-parallel products of 64 x 64 and 64 x 128 tiles:
+//     dK~ = W dS'^T, dQ = diag(g) dY S^T + (dP o E) K, dP = lower(dY W^T), dWk = -dW S^T,
+//     dT = dW (beta V)^T + dWk (beta g K)^T, d(beta V) = T^T dW, d(beta g K) = T^T dWk,
+//     dA = -strict_lower(T^T dT T^T), and the rows' k, beta and G terms of A, E, g, kd;
+// then d ln alpha_s = sum_{t >= s} dG_t within the chunk (G is a within-chunk prefix sum).
+//
+// Only chunk-level states are kept (S and dS' per chunk and value head, O(chunks x heads x 128^2)); the
+// forward's own chunk quantities (T, U, Wk, W, P) are reused by the backward. Each product runs as one
+// launch of a batched kernel over all (chunk, value head) items, one block per item with both operands
+// staged in LDS; the two chunk passes run one block per (sequence, value head, 16-column slice).
+#include <atomic>
+
+#include "ext_internal.h"
+#include "gdn_device.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kC = 64, kD = 128, kSl = 16;  // chunk, head dim, value columns per slice of the chunk passes
+constexpr int kSlices = kD / kSl;
+
+// ---- chunk table: seq_off[n] = first chunk of sequence n; tab[c] = (start token, length, sequence) ----
+// Offsets stop at nc_max, so boundaries that break the contract (decreasing, overlapping) drop chunks
+// rather than index past the table.
+__global__ void __launch_bounds__(64) k_cb_offsets(const int32_t* __restrict__ cu, int n_seqs, int64_t T,
+                                                   int64_t nc_max, int32_t* __restrict__ seq_off) {
+  if (threadIdx.x != 0) return;
+  int64_t off = 0;
+  for (int n = 0; n < n_seqs; ++n) {
+    const int64_t s0 = min<int64_t>(max<int64_t>(cu[n], 0), T), s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), T);
+    seq_off[n] = int32_t(off);
+    off = min<int64_t>(off + (s1 - s0 + kC - 1) / kC, nc_max);
+  }
+  seq_off[n_seqs] = int32_t(off);
+}
+
+// one block per sequence, and block n_seqs marks the unused slots
+__global__ void __launch_bounds__(256) k_cb_table(const int32_t* __restrict__ cu, int n_seqs, int64_t T,
+                                                  int64_t nc_max, const int32_t* __restrict__ seq_off,
+                                                  int4* __restrict__ tab) {
+  const int n = blockIdx.x;
+  if (n == n_seqs) {
+    for (int64_t c = seq_off[n_seqs] + threadIdx.x; c < nc_max; c += blockDim.x) tab[c] = make_int4(0, 0, -1, 0);
+    return;
+  }
+  const int64_t s0 = min<int64_t>(max<int64_t>(cu[n], 0), T), s1 = min<int64_t>(max<int64_t>(cu[n + 1], s0), T);
+  const int64_t c0 = seq_off[n], nch = seq_off[n + 1] - c0;
+  for (int64_t j = threadIdx.x; j < nch; j += blockDim.x)
+    tab[c0 + j] = make_int4(int(s0 + j * kC), int(min<int64_t>(kC, s1 - s0 - j * kC)), n, 0);
+}
+
+// ---- gather: per item (chunk c, value head h), zero-padded 64-row tiles and the decay prefix ----
+// what: 1 = the forward's inputs (Q, K, V, G, beta), 2 = dY
+__global__ void __launch_bounds__(256) k_cb_gather(CBwdArgs a, int what) {
+  const int64_t item = blockIdx.x;
+  const int c = int(item / a.hv), h = int(item - int64_t(c) * a.hv), g = h / a.R;
+  const int4 ct = a.tab[c];
+  const int len = ct.y;
+  if (len <= 0) return;
+  const int64_t s = ct.x;
+  const int tid = threadIdx.x;
+  const int64_t qrow = int64_t(a.hk) * kD, vrow = int64_t(a.hv) * kD;
+  for (int idx = tid; idx < kC * kD / 4; idx += 256) {
+    const int t = idx / (kD / 4), c4 = (idx % (kD / 4)) * 4;
+    const int64_t o = item * (kC * kD) + t * kD + c4;
+    if (what & 1) {
+      float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv, vv = qv;
+      if (t < len) {
+        qv = *reinterpret_cast<const float4*>(a.q + (s + t) * qrow + g * kD + c4);
+        kv = *reinterpret_cast<const float4*>(a.k + (s + t) * qrow + g * kD + c4);
+        vv = *reinterpret_cast<const float4*>(a.v + (s + t) * vrow + h * kD + c4);
+      }
+      *reinterpret_cast<float4*>(a.Qi + o) = qv;
+      *reinterpret_cast<float4*>(a.Ki + o) = kv;
+      *reinterpret_cast<float4*>(a.Vi + o) = vv;
+    }
+    if (what & 2) {
+      float4 dv = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < len) {
+        dv = *reinterpret_cast<const float4*>(a.dy + (s + t) * vrow + h * kD + c4);
+        dv.x *= a.scale; dv.y *= a.scale; dv.z *= a.scale; dv.w *= a.scale;
+      }
+      *reinterpret_cast<float4*>(a.dYi + o) = dv;
+    }
+  }
+  if ((what & 1) && tid < 64) {  // padded rows: ln alpha = 0 (G stays), beta = 0
+    float la = 0.f, be = 0.f;
+    if (tid < len) {
+      la = logf(a.alpha[(s + tid) * a.hv + h]);
+      be = a.beta[(s + tid) * a.hv + h];
+    }
+    float G = la;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(G, o, 64);
+      if (tid >= o) G += y;
+    }
+    a.G[item * kC + tid] = G;
+    a.bt[item * kC + tid] = be;
+  }
+}
+
+// ---- batched product: per item, C (64 x N) = alpha op(A) op(B) (+ C), optional lower mask ----
+struct Bmm {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t sA, sB, sC;  // per-item strides (floats)
+  int N, K;            // C is 64 x N; the contraction has K terms (N, K in {64, 128})
+  int lda, ldb, ldc;   // row strides of the stored matrices
+  int ta, tb;          // op(A) = A^T (A stored [K][64]); op(B) = B^T (B stored [N][K])
+  float alpha;
+  int accumulate;
+  int mask;            // 0: none; 1: keep m >= n; 2: keep m > n
+  int tc;              // store C^T (C stored [N][64])
+};
+
+// One block per item, four waves; wave w computes rows 16w .. 16w + 15 of C over all N columns on 16x16x4
+// fp32 MFMAs. op(B) is staged in LDS as [K][N + 4] (the four lane groups of an operand read hit distinct
+// banks); each wave reads its own rows of op(A) straight into registers. At step (p, c) lane group q
+// contributes contraction index 16p + 4q + c, so a row-major A gives each lane float4 runs.
+template <int N, int K, bool TA, bool TB>
+__global__ void __launch_bounds__(256) k_cb_mm(Bmm b, const int4* __restrict__ tab, int hv) {
+  constexpr int kLd = N + 4;
+  extern __shared__ __attribute__((aligned(16))) float Bs[];  // [K][kLd]: Bs[k][n] = op(B)[k][n]
+  const int64_t item = blockIdx.x;
+  if (tab[item / hv].y <= 0) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lm = lane & 15, lg = lane >> 4;
+  const float* A = b.A + item * b.sA;
+  const float* B = b.B + item * b.sB;
+  // this wave's A operands: op(A)[16w + lm][16p + 4lg + c]
+  float av[K / 16][4];
+#pragma unroll
+  for (int p = 0; p < K / 16; ++p) {
+    if (!TA) {
+      const float4 v = *reinterpret_cast<const float4*>(A + int64_t(16 * w + lm) * b.lda + 16 * p + 4 * lg);
+      av[p][0] = v.x; av[p][1] = v.y; av[p][2] = v.z; av[p][3] = v.w;
+    } else {  // A stored [K][64]
+#pragma unroll
+      for (int c = 0; c < 4; ++c) av[p][c] = A[int64_t(16 * p + 4 * lg + c) * b.lda + 16 * w + lm];
+    }
+  }
+  if (!TB) {  // B stored [K][N]
+#pragma unroll
+    for (int r = 0; r < K * N / 1024; ++r) {
+      const int idx = tid + 256 * r, k = idx / (N / 4), n4 = (idx % (N / 4)) * 4;
+      *reinterpret_cast<float4*>(Bs + k * kLd + n4) = *reinterpret_cast<const float4*>(B + int64_t(k) * b.ldb + n4);
+    }
+  } else {  // B stored [N][K]
+#pragma unroll
+    for (int r = 0; r < K * N / 1024; ++r) {
+      const int idx = tid + 256 * r, n = idx / (K / 4), k4 = (idx % (K / 4)) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(B + int64_t(n) * b.ldb + k4);
+      Bs[(k4 + 0) * kLd + n] = v.x; Bs[(k4 + 1) * kLd + n] = v.y;
+      Bs[(k4 + 2) * kLd + n] = v.z; Bs[(k4 + 3) * kLd + n] = v.w;
+    }
+  }
+  __syncthreads();
+  f32x4 acc[N / 16];
+#pragma unroll
+  for (int j = 0; j < N / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < K / 16; ++p)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float* brow = Bs + (16 * p + 4 * lg + c) * kLd + lm;
+#pragma unroll
+      for (int j = 0; j < N / 16; ++j) acc[j] = mfma16x16x4f32(av[p][c], brow[16 * j], acc[j]);
+    }
+  float* C = b.C + item * b.sC;
+#pragma unroll
+  for (int j = 0; j < N / 16; ++j) {
+    const int n = 16 * j + lm;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * w + 4 * lg + e;
+      v[e] = b.alpha * acc[j][e];
+      if ((b.mask == 1 && n > m) || (b.mask == 2 && n >= m)) v[e] = 0.f;
+    }
+    if (b.tc) {  // C^T stored [N][64]: the lane's four rows are contiguous
+      float4* cp = reinterpret_cast<float4*>(C + int64_t(n) * b.ldc + 16 * w + 4 * lg);
+      float4 o = make_float4(v[0], v[1], v[2], v[3]);
+      if (b.accumulate) {
+        const float4 q = *cp;
+        o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+      }
+      *cp = o;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float* cp = C + int64_t(16 * w + 4 * lg + e) * b.ldc + n;
+        *cp = b.accumulate ? *cp + v[e] : v[e];
+      }
+    }
+  }
+}
+
+// ---- A = strict_lower(beta_t E KK), P = lower(E QK) ----
+__global__ void __launch_bounds__(256) k_cb_ap(CBwdArgs a) {
+  const int64_t item = blockIdx.x;
+  if (a.tab[item / a.hv].y <= 0) return;
+  const float* G = a.G + item * kC;
+  const float* bt = a.bt + item * kC;
+  for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
+    const int t = idx / kC, i = idx % kC;
+    const float e = __expf(fminf(G[t] - G[i], 0.f));
+    const int64_t o = item * kC * kC + idx;
+    a.Am[o] = i < t ? bt[t] * e * a.KK[o] : 0.f;
+    a.Pm[o] = i <= t ? e * a.QK[o] : 0.f;
+  }
+}
+
+// ---- T = (I + A)^-1 by forward substitution: one wave per item, lane = column ----
+__global__ void __launch_bounds__(64) k_cb_inv(CBwdArgs a) {
+  __shared__ float As[kC][kC + 1];
+  __shared__ float Xs[kC][kC + 1];
+  const int lane = threadIdx.x;
+  const int64_t item = blockIdx.x;
+  if (a.tab[item / a.hv].y <= 0) return;
+  const float* A = a.Am + item * kC * kC;
+  for (int r = 0; r < kC; ++r) As[r][lane] = A[r * kC + lane];
+  __syncthreads();
+  for (int t = 0; t < kC; ++t) {
+    float x = (t == lane) ? 1.f : 0.f;
+    for (int i = 0; i < t; ++i) x -= As[t][i] * Xs[i][lane];
+    Xs[t][lane] = x;
+    __syncthreads();
+  }
+  float* T = a.Tm + item * kC * kC;
+  for (int r = 0; r < kC; ++r) T[r * kC + lane] = Xs[r][lane];
+}
+
+// ---- bV = diag(beta) V, bgK = diag(beta g) K, Kt = diag(kd) K and its transpose, gQ = diag(g) Q ----
+__global__ void __launch_bounds__(256) k_cb_prep(CBwdArgs a) {
+  __shared__ float tile[kC][kC + 1];
+  const int64_t item = blockIdx.x;
+  if (a.tab[item / a.hv].y <= 0) return;
+  const float* G = a.G + item * kC;
+  const float GC = G[kC - 1];
+  const int64_t b2 = item * kC * kD;
+  for (int idx = threadIdx.x; idx < kC * kD; idx += 256) {
+    const int t = idx / kD;
+    const float be = a.bt[item * kC + t], g = __expf(G[t]);
+    const int64_t o = b2 + idx;
+    const float kv = a.Ki[o];
+    a.bV[o] = be * a.Vi[o];
+    a.bgK[o] = be * g * kv;
+    a.Kt[o] = __expf(GC - G[t]) * kv;
+    a.gQ[o] = g * a.Qi[o];
+  }
+  // KtT [128][64], through LDS in two 64-column halves
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
+      const int t = idx / kC, r = idx % kC;
+      tile[t][r] = __expf(GC - G[t]) * a.Ki[b2 + t * kD + 64 * half + r];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
+      const int r = idx / kC, t = idx % kC;
+      a.KtT[b2 + (64 * half + r) * kC + t] = tile[t][r];
+    }
+  }
+}
+
+// ---- the chunk passes: the only sequential part, one block per (sequence, value head, 16-column slice) ----
+// Both passes carry a 128 x 16 slice X of a state-sized matrix across the sequence's chunks:
+//     Z = B + s1 A1 X   (64 x 16),      X <- g_C X + H + s2 A2^T Z   (128 x 16),
+// forward (chunks in order):  X = S,   A1 = Wk, s1 = -1, B = U,       Z = W,  A2 = Kt, s2 = +1, H = 0;
+// backward (in reverse):      X = dS', A1 = Kt, s1 = +1, B = P^T dY,  Z = dW, A2 = Wk, s2 = -1, H = gQ^T dY.
+// The products run on 16x16x4 fp32 MFMAs; wave w computes rows 16w.. of Z and rows 32w.. of X, and X stays
+// in registers in the accumulator layout (lane l: rows 4 (l / 16) + e of each 16-row tile, column l % 16).
+// The contraction order is chosen so that each lane's A operands are float4 runs of one row: at step
+// (p, c) lane group q contributes index 16p + 4q + c. The chunk-independent operands of the next chunk
+// are loaded before the current chunk's products.
+constexpr int kXLd = 20;  // LDS row stride of X and Z (floats): the four lane groups hit distinct banks
+
+struct PassLoads {
+  float4 a1[8];      // A1 row 16w + l % 16, columns 4 (l / 16 + 4p) ..
+  float4 a2[2][4];   // A2^T rows 32w + 16i + l % 16, columns 4 (l / 16 + 4p) ..
+  float b[4];        // B rows 16w + 4 (l / 16) + e
+  float h[2][4];     // H (backward), rows 32w + 16i + 4 (l / 16) + e
+  float sv[2][4];    // S (backward), same rows: <S, dS'> for dG
+  float gc;
+};
+
+template <bool kBwd>
+__device__ __forceinline__ void pass_load(const CBwdArgs& a, int64_t item, int w, int lm, int lg, int col,
+                                          PassLoads& L) {
+  const float* A1 = (kBwd ? a.Kt : a.Wk) + item * kC * kD;
+  const float* A2T = (kBwd ? a.WkT : a.KtT) + item * kD * kC;
+  const float* B = (kBwd ? a.dW : a.U) + item * kC * kD;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) L.a1[p] = *reinterpret_cast<const float4*>(A1 + (16 * w + lm) * kD + 4 * (lg + 4 * p));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      L.a2[i][p] = *reinterpret_cast<const float4*>(A2T + (32 * w + 16 * i + lm) * kC + 4 * (lg + 4 * p));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) L.b[e] = B[(16 * w + 4 * lg + e) * kD + col];
+  if (kBwd) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t o = item * kD * kD + (32 * w + 16 * i + 4 * lg + e) * kD + col;
+        L.h[i][e] = a.dS[o];
+        L.sv[i][e] = a.S[o];
+      }
+  }
+  L.gc = __expf(a.G[item * kC + kC - 1]);
+}
+
+template <bool kBwd>
+__global__ void __launch_bounds__(256) k_cb_pass(CBwdArgs a) {
+  __shared__ float Xs[kD * kXLd];
+  __shared__ float Zs[kC * kXLd];
+  __shared__ float red[4];
+  const int chain = blockIdx.x / kSlices, sl = blockIdx.x % kSlices;
+  const int n = chain / a.hv, h = chain % a.hv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lm = lane & 15, lg = lane >> 4;
+  const int col = kSl * sl + lm;
+  const float s1 = kBwd ? 1.f : -1.f, s2 = kBwd ? -1.f : 1.f;
+  float* Zout = kBwd ? a.dW : a.W;
+  float* Xout = kBwd ? a.dS : a.S;
+  const float* x0 = kBwd ? a.dsf : a.s0;
+  const size_t sb = (size_t(n) * a.hv + h) * kD * kD;
+  f32x4 X[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[i][e] = x0 ? x0[sb + size_t(32 * w + 16 * i + 4 * lg + e) * kD + col] : 0.f;
+  const int c0 = a.seq_off[n], nch = a.seq_off[n + 1] - c0;
+  PassLoads cur, nxt;
+  if (nch > 0) pass_load<kBwd>(a, int64_t(kBwd ? c0 + nch - 1 : c0) * a.hv + h, w, lm, lg, col, cur);
+  for (int it = 0; it < nch; ++it) {
+    const int c = kBwd ? c0 + nch - 1 - it : c0 + it;
+    const int64_t item = int64_t(c) * a.hv + h;
+    if (it + 1 < nch) pass_load<kBwd>(a, int64_t(kBwd ? c - 1 : c + 1) * a.hv + h, w, lm, lg, col, nxt);
+    // X (the state at the chunk's start; backward: dL/d state after it) to LDS and to its buffer
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 32 * w + 16 * i + 4 * lg + e;
+        Xs[row * kXLd + lm] = X[i][e];
+        Xout[item * kD * kD + size_t(row) * kD + col] = X[i][e];
+        if (kBwd) part += cur.sv[i][e] * X[i][e];
+      }
+    if (kBwd) {
+      part = group_sum<64>(part);
+      if (lane == 0) red[w] = part;
+    }
+    __syncthreads();
+    if (kBwd && tid == 0) a.dgc[item * kSlices + sl] = red[0] + red[1] + red[2] + red[3];
+    // Z = B + s1 A1 X: rows 16w + 4 lg + e
+    f32x4 z = {cur.b[0], cur.b[1], cur.b[2], cur.b[3]};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float av[4] = {cur.a1[p].x, cur.a1[p].y, cur.a1[p].z, cur.a1[p].w};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) z = mfma16x16x4f32(s1 * av[cc], Xs[(16 * p + 4 * lg + cc) * kXLd + lm], z);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * w + 4 * lg + e;
+      Zs[t * kXLd + lm] = z[e];
+      Zout[item * kC * kD + t * kD + col] = z[e];
+    }
+    __syncthreads();
+    // X <- g_C X + H + s2 A2^T Z
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      f32x4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = cur.gc * X[i][e] + (kBwd ? cur.h[i][e] : 0.f);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float av[4] = {cur.a2[i][p].x, cur.a2[i][p].y, cur.a2[i][p].z, cur.a2[i][p].w};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          acc = mfma16x16x4f32(s2 * av[cc], Zs[(16 * p + 4 * lg + cc) * kXLd + lm], acc);
+      }
+      X[i] = acc;
+    }
+    cur = nxt;
+  }
+  if (kBwd && a.ds0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.ds0[sb + size_t(32 * w + 16 * i + 4 * lg + e) * kD + col] = X[i][e];
+  }
+}
+
+// ---- y = scale (gQ S + P W), gathered per item in X, scattered to the tokens ----
+__global__ void __launch_bounds__(256) k_cb_scatter_y(CBwdArgs a) {
+  const int64_t item = blockIdx.x;
+  const int c = int(item / a.hv), h = int(item - int64_t(c) * a.hv);
+  const int4 ct = a.tab[c];
+  for (int idx = threadIdx.x; idx < ct.y * (kD / 4); idx += 256) {
+    const int t = idx / (kD / 4), c4 = (idx % (kD / 4)) * 4;
+    float4 v = *reinterpret_cast<const float4*>(a.X + item * kC * kD + t * kD + c4);
+    v.x *= a.scale; v.y *= a.scale; v.z *= a.scale; v.w *= a.scale;
+    *reinterpret_cast<float4*>(a.y + (ct.x + t) * int64_t(a.hv) * kD + h * kD + c4) = v;
+  }
+}
+
+// ---- dQK = dP o E (into M1) and dE = dP o QK (in place of dP) ----
+__global__ void __launch_bounds__(256) k_cb_ew1(CBwdArgs a) {
+  const int64_t item = blockIdx.x;
+  if (a.tab[item / a.hv].y <= 0) return;
+  const float* G = a.G + item * kC;
+  for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
+    const int t = idx / kC, i = idx % kC;
+    const int64_t o = item * kC * kC + idx;
+    const float dp = a.dP[o];
+    a.M1[o] = dp * __expf(fminf(G[t] - G[i], 0.f));
+    a.dP[o] = dp * a.QK[o];
+  }
+}
+
+// ---- dAKK = dA o beta_t o E (into dT, free by now) ----
+__global__ void __launch_bounds__(256) k_cb_ew2(CBwdArgs a) {
+  const int64_t item = blockIdx.x;
+  if (a.tab[item / a.hv].y <= 0) return;
+  const float* G = a.G + item * kC;
+  for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
+    const int t = idx / kC, i = idx % kC;
+    const int64_t o = item * kC * kC + idx;
+    a.dT[o] = a.dA[o] * a.bt[item * kC + t] * __expf(fminf(G[t] - G[i], 0.f));
+  }
+}
+
+// ---- per item: the row terms, dG, d ln alpha, and the outputs of the chunk's tokens ----
+__global__ void __launch_bounds__(256) k_cb_final(CBwdArgs a) {
+  const int64_t item = blockIdx.x;
+  const int c = int(item / a.hv), h = int(item - int64_t(c) * a.hv);
+  const int4 ct = a.tab[c];
+  if (ct.y <= 0) return;
+  __shared__ float dG[kC], dbe[kC], dkd[kC], Gs[kC];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if (tid < kC) Gs[tid] = a.G[item * kC + tid];
+  __syncthreads();
+  const float GC = Gs[kC - 1];
+  const int64_t b2 = item * kC * kD, b1 = item * kC * kC;
+  // rows: one wave per 16 rows; lanes over the 128 columns (two each)
+  for (int t = 16 * w; t < 16 * w + 16; ++t) {
+    const float g = __expf(Gs[t]), kd = __expf(GC - Gs[t]), be = a.bt[item * kC + t];
+    float sqx = 0.f, sbk = 0.f, sbv = 0.f, skt = 0.f;
+    for (int cc = lane; cc < kD; cc += 64) {
+      const int64_t o = b2 + t * kD + cc;
+      const float X = a.X[o], Q = a.Qi[o], K = a.Ki[o], V = a.Vi[o];
+      const float dbgk = a.dbgK[o], dbv = a.dbV[o], dkt = a.dKt[o];
+      sqx += Q * X;
+      sbk += dbgk * K;
+      sbv += dbv * V;
+      skt += dkt * K;
+      if (t < ct.y) {
+        const int64_t tok = (ct.x + t) * int64_t(a.hv) * kD + h * kD + cc;
+        a.dqh[tok] = a.dQ[o] + g * X;
+        a.dkh[tok] = a.dK[o] + kd * dkt + be * g * dbgk;
+        a.dv[tok] = be * dbv;
+      }
+    }
+    sqx = group_sum<64>(sqx);
+    sbk = group_sum<64>(sbk);
+    sbv = group_sum<64>(sbv);
+    skt = group_sum<64>(skt);
+    if (lane == 0) {
+      dG[t] = (sqx + be * sbk) * g;  // dg_t g_t
+      dbe[t] = sbv + g * sbk;
+      dkd[t] = skt * kd;              // dkd_t kd_t
+    }
+  }
+  __syncthreads();
+  // E terms: dE (from dP o QK, plus dA o beta o KK), dbeta from dA o E o KK
+  if (tid < kC) {
+    const int t = tid;
+    const float be = a.bt[item * kC + t];
+    float rowsum = 0.f, colsum = 0.f, dbA = 0.f;
+    for (int i = 0; i < kC; ++i) {
+      const float e_ti = __expf(fminf(Gs[t] - Gs[i], 0.f)), e_it = __expf(fminf(Gs[i] - Gs[t], 0.f));
+      const float dA_ti = a.dA[b1 + t * kC + i], kk_ti = a.KK[b1 + t * kC + i];
+      const float dE_ti = (i <= t ? a.dP[b1 + t * kC + i] : 0.f) + dA_ti * be * kk_ti;
+      rowsum += dE_ti * e_ti;
+      dbA += dA_ti * e_ti * kk_ti;
+      const float be_i = a.bt[item * kC + i];
+      const float dE_it = (t <= i ? a.dP[b1 + i * kC + t] : 0.f) + a.dA[b1 + i * kC + t] * be_i * a.KK[b1 + i * kC + t];
+      colsum += dE_it * e_it;
+    }
+    dG[t] += rowsum - colsum - dkd[t];
+    dbe[t] += dbA;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.f;
+    for (int i = 0; i < kC; ++i) s += dkd[i];
+    float dgc = 0.f;
+    for (int k = 0; k < kSlices; ++k) dgc += a.dgc[item * kSlices + k];
+    dG[kC - 1] += s + dgc * __expf(GC);
+  }
+  __syncthreads();
+  if (tid < kC) {
+    // d ln alpha_s = sum_{t >= s} dG_t (reverse prefix sum over the chunk)
+    float v = dG[kC - 1 - tid];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(v, o, 64);
+      if (tid >= o) v += y;
+    }
+    const int sidx = kC - 1 - tid;
+    if (sidx < ct.y) {
+      const int64_t ai = (ct.x + sidx) * int64_t(a.hv) + h;
+      a.dalpha[ai] = v / a.alpha[ai];
+      a.dbeta[ai] = dbe[sidx];
+    }
+  }
+}
+
+// ---- dq, dk: sums over the value heads that read each QK head ----
+__global__ void __launch_bounds__(256) k_cb_group_sum(const float* __restrict__ dqh, const float* __restrict__ dkh,
+                                                      int64_t T, int hk, int hv, float* __restrict__ dq,
+                                                      float* __restrict__ dk) {
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;  // over T x hk x 128
+  if (idx >= T * hk * kD) return;
+  const int64_t t = idx / (int64_t(hk) * kD);
+  const int g = int((idx / kD) % hk), cc = int(idx % kD), R = hv / hk;
+  float sq = 0.f, sk = 0.f;
+  for (int r = 0; r < R; ++r) {
+    const int64_t o = (t * hv + g * R + r) * kD + cc;
+    sq += dqh[o];
+    sk += dkh[o];
+  }
+  dq[idx] = sq;
+  dk[idx] = sk;
+}
+
+}  // namespace
+
+size_t cbwd_workspace_bytes(int n_seqs, int64_t T, int hv) {
+  const size_t nc = size_t(T / kC + n_seqs), items = nc * hv;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t f = sizeof(float);
+  return al(sizeof(int32_t) * (n_seqs + 1)) + al(sizeof(int4) * nc) +
+         21 * al(f * items * kC * kD) +           // the 64 x 128 tiles (KtT, WkT stored 128 x 64)
+         2 * al(f * items * kD * kD) +            // S dS
+         9 * al(f * items * kC * kC) +            // KK QK Am Pm Tm dP M1 dT dA
+         2 * al(f * items * kC) + al(f * items * kSlices) +  // G bt dgc
+         2 * al(f * size_t(T) * hv * kD);          // dqh dkh
+}
+
+void cbwd_plan(CBwdArgs& a, void* base) {
+  const size_t nc = size_t(a.T / kC + a.n_seqs), items = nc * a.hv;
+  a.nc_max = int64_t(nc);
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    void* r = p;
+    p += (bytes + 255) & ~size_t(255);
+    return r;
+  };
+  const size_t f = sizeof(float), big = f * items * kC * kD, st = f * items * kD * kD, sm = f * items * kC * kC;
+  a.seq_off = static_cast<int32_t*>(take(sizeof(int32_t) * (a.n_seqs + 1)));
+  a.tab = static_cast<int4*>(take(sizeof(int4) * nc));
+  float** bigs[] = {&a.Qi, &a.Ki, &a.Vi, &a.dYi, &a.bV, &a.bgK, &a.U, &a.Wk, &a.W, &a.dW, &a.dKt, &a.X, &a.dWk,
+                    &a.dQ, &a.dK, &a.dbV, &a.dbgK, &a.Kt, &a.KtT, &a.WkT, &a.gQ};
+  for (float** q : bigs) *q = static_cast<float*>(take(big));
+  a.S = static_cast<float*>(take(st));
+  a.dS = static_cast<float*>(take(st));
+  float** sms[] = {&a.KK, &a.QK, &a.Am, &a.Pm, &a.Tm, &a.dP, &a.M1, &a.dT, &a.dA};
+  for (float** q : sms) *q = static_cast<float*>(take(sm));
+  a.G = static_cast<float*>(take(f * items * kC));
+  a.bt = static_cast<float*>(take(f * items * kC));
+  a.dgc = static_cast<float*>(take(f * items * kSlices));
+  a.dqh = static_cast<float*>(take(f * size_t(a.T) * a.hv * kD));
+  a.dkh = static_cast<float*>(take(f * size_t(a.T) * a.hv * kD));
+}
+
+namespace {
+template <int N, int K, bool TA, bool TB>
+hipError_t mm_launch(const Bmm& b, const CBwdArgs& a, hipStream_t s) {
+  const void* f = reinterpret_cast<const void*>(k_cb_mm<N, K, TA, TB>);
+  const int smem = int(sizeof(float) * K * (N + 4));
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  // this instance's LDS limit is raised once per device (an idempotent call, so a race only repeats it)
+  static std::atomic<uint64_t> raised{0};
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (!(raised.load() & bit)) {
+    if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, smem)) != hipSuccess) return e;
+    raised.fetch_or(bit);
+  }
+  hipLaunchKernelGGL((k_cb_mm<N, K, TA, TB>), dim3(unsigned(a.nc_max * a.hv)), dim3(256), size_t(smem), s, b, a.tab,
+                     a.hv);
+  return hipGetLastError();
+}
+
+// C (64 x N) = alpha op(A) op(B) (+ C) per item, op(A) 64 x K, op(B) K x N
+hipError_t bmm(const CBwdArgs& a, const float* A, int64_t sA, int lda, int ta, const float* B, int64_t sB, int ldb,
+               int tb, float* C, int64_t sC, int ldc, int N, int K, float alpha, int accumulate, int mask,
+               hipStream_t s, int tc = 0) {
+  const Bmm b{A, B, C, sA, sB, sC, N, K, lda, ldb, ldc, ta, tb, alpha, accumulate, mask, tc};
+  const int key = (N == 128) * 8 + (K == 128) * 4 + (ta != 0) * 2 + (tb != 0);
+  switch (key) {
+    case 0: return mm_launch<64, 64, false, false>(b, a, s);
+    case 1: return mm_launch<64, 64, false, true>(b, a, s);
+    case 2: return mm_launch<64, 64, true, false>(b, a, s);
+    case 3: return mm_launch<64, 64, true, true>(b, a, s);
+    case 4: return mm_launch<64, 128, false, false>(b, a, s);
+    case 5: return mm_launch<64, 128, false, true>(b, a, s);
+    case 8: return mm_launch<128, 64, false, false>(b, a, s);
+    case 9: return mm_launch<128, 64, false, true>(b, a, s);
+    case 10: return mm_launch<128, 64, true, false>(b, a, s);
+    case 12: return mm_launch<128, 128, false, false>(b, a, s);
+    case 13: return mm_launch<128, 128, false, true>(b, a, s);
+    default: return hipErrorInvalidValue;  // K = 128 with op(A) = A^T needs a 128-row A: not used
+  }
+}
+}  // namespace
+
+hipError_t launch_cbwd(const CBwdArgs& a, bool forward, bool backward, float* dq, float* dk, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  const int64_t items = a.nc_max * a.hv;
+  const unsigned nb = unsigned(items), chains = unsigned(int64_t(a.n_seqs) * a.hv * kSlices);
+  const int64_t I2 = kC * kD, I1 = kC * kC, I3 = kD * kD;
+  if (forward) {
+    hipLaunchKernelGGL(k_cb_offsets, dim3(1), dim3(64), 0, s, a.cu, a.n_seqs, a.T, a.nc_max, a.seq_off);
+    hipLaunchKernelGGL(k_cb_table, dim3(unsigned(a.n_seqs) + 1), dim3(256), 0, s, a.cu, a.n_seqs, a.T, a.nc_max,
+                       a.seq_off, a.tab);
+    hipLaunchKernelGGL(k_cb_gather, dim3(nb), dim3(256), 0, s, a, 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // KK = K K^T, QK = Q K^T
+    if ((e = bmm(a, a.Ki, I2, kD, 0, a.Ki, I2, kD, 1, a.KK, I1, kC, 64, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
+    if ((e = bmm(a, a.Qi, I2, kD, 0, a.Ki, I2, kD, 1, a.QK, I1, kC, 64, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_cb_ap, dim3(nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_cb_inv, dim3(nb), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_cb_prep, dim3(nb), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // U = T bV, Wk = T bgK (and Wk^T)
+    if ((e = bmm(a, a.Tm, I1, kC, 0, a.bV, I2, kD, 0, a.U, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+    if ((e = bmm(a, a.Tm, I1, kC, 0, a.bgK, I2, kD, 0, a.Wk, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+    if ((e = bmm(a, a.Tm, I1, kC, 0, a.bgK, I2, kD, 0, a.WkT, I2, kC, 128, 64, 1.f, 0, 0, s, 1)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(k_cb_pass<false>, dim3(chains), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.y) {  // y = scale (gQ S + P W), through X
+      if ((e = bmm(a, a.gQ, I2, kD, 0, a.S, I3, kD, 0, a.X, I2, kD, 128, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
+      if ((e = bmm(a, a.Pm, I1, kC, 0, a.W, I2, kD, 0, a.X, I2, kD, 128, 64, 1.f, 1, 0, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_cb_scatter_y, dim3(nb), dim3(256), 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  if (!backward) return hipSuccess;
+  // dY is needed from here on: gathered (scaled) now, since the forward may run before dy exists
+  hipLaunchKernelGGL(k_cb_gather, dim3(nb), dim3(256), 0, s, a, 2);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the backward pass's addends: dW <- P^T dY; dS <- gQ^T dY (128 x 128, as two 64-row halves)
+  if ((e = bmm(a, a.Pm, I1, kC, 1, a.dYi, I2, kD, 0, a.dW, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+  for (int half = 0; half < 2; ++half)
+    if ((e = bmm(a, a.gQ + 64 * half, I2, kD, 1, a.dYi, I2, kD, 0, a.dS + 64 * half * kD, I3, kD, 128, 64, 1.f, 0,
+                 0, s)) != hipSuccess)
+      return e;
+  hipLaunchKernelGGL(k_cb_pass<true>, dim3(chains), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // dK~ = W dS'^T; X = dY S^T; dWk = -dW S^T; dP = lower(dY W^T)
+  if ((e = bmm(a, a.W, I2, kD, 0, a.dS, I3, kD, 1, a.dKt, I2, kD, 128, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
+  if ((e = bmm(a, a.dYi, I2, kD, 0, a.S, I3, kD, 1, a.X, I2, kD, 128, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
+  if ((e = bmm(a, a.dW, I2, kD, 0, a.S, I3, kD, 1, a.dWk, I2, kD, 128, 128, -1.f, 0, 0, s)) != hipSuccess) return e;
+  if ((e = bmm(a, a.dYi, I2, kD, 0, a.W, I2, kD, 1, a.dP, I1, kC, 64, 128, 1.f, 0, 1, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cb_ew1, dim3(nb), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // dQ = dQK K; dK = dQK^T Q
+  if ((e = bmm(a, a.M1, I1, kC, 0, a.Ki, I2, kD, 0, a.dQ, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+  if ((e = bmm(a, a.M1, I1, kC, 1, a.Qi, I2, kD, 0, a.dK, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+  // dT = dW bV^T + dWk bgK^T
+  if ((e = bmm(a, a.dW, I2, kD, 0, a.bV, I2, kD, 1, a.dT, I1, kC, 64, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
+  if ((e = bmm(a, a.dWk, I2, kD, 0, a.bgK, I2, kD, 1, a.dT, I1, kC, 64, 128, 1.f, 1, 0, s)) != hipSuccess) return e;
+  // d(bV) = T^T dW; d(bgK) = T^T dWk
+  if ((e = bmm(a, a.Tm, I1, kC, 1, a.dW, I2, kD, 0, a.dbV, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+  if ((e = bmm(a, a.Tm, I1, kC, 1, a.dWk, I2, kD, 0, a.dbgK, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+  // dA = -strict_lower(T^T (dT T^T))
+  if ((e = bmm(a, a.dT, I1, kC, 0, a.Tm, I1, kC, 1, a.M1, I1, kC, 64, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+  if ((e = bmm(a, a.Tm, I1, kC, 1, a.M1, I1, kC, 0, a.dA, I1, kC, 64, 64, -1.f, 0, 2, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cb_ew2, dim3(nb), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // dK += dAKK K + dAKK^T K
+  if ((e = bmm(a, a.dT, I1, kC, 0, a.Ki, I2, kD, 0, a.dK, I2, kD, 128, 64, 1.f, 1, 0, s)) != hipSuccess) return e;
+  if ((e = bmm(a, a.dT, I1, kC, 1, a.Ki, I2, kD, 0, a.dK, I2, kD, 128, 64, 1.f, 1, 0, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_cb_final, dim3(nb), dim3(256), 0, s, a);
+  const int64_t nq = a.T * a.hk * kD;
+  if (nq > 0)
+    hipLaunchKernelGGL(k_cb_group_sum, dim3(unsigned((nq + 255) / 256)), dim3(256), 0, s, a.dqh, a.dkh, a.T, a.hk,
+                       a.hv, dq, dk);
+  return hipGetLastError();
+}
+
+}  // namespace gdn
