@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 
 # Shape of the layer (16 QK heads, 48 value heads, d = 128, chunk 64).
 HK, HV, D, CH = 16, 48, 128, 64
@@ -290,10 +291,26 @@ def cpu_baseline(prefill_tokens: int, decode_batch: int):
                        f"{dd:.1f} s wall")
 
 
+# Multiply-adds per (64-token chunk, value head) of the chunked backward, by product (M x N x K):
+# the forward recomputed (K K^T, Q K^T, U, Wk, the forward substitution of (I + A)^-1, the two state
+# products of the forward chunk pass, and y = gQ S + P W for the norm and gate backward), then the backward
+# (P^T dY, gQ^T dY, the two products of the reverse chunk pass, W dS'^T, dY S^T, dW S^T, dY W^T, dQK K,
+# dQK^T Q, dT's two, T^T dW, T^T dWk, dA's two and the two K terms of dA).
+CBWD_FMA_PER_CHUNK = (4 * 64 * 64 * 128 + 64 ** 3 // 6 + 2 * 64 * 128 * 128        # forward: WY and pass
+                      + 64 * 128 * 128 + 64 * 128 * 64                              # forward: y
+                      + 64 * 128 * 64 + 128 * 128 * 64 + 2 * 64 * 128 * 128         # backward pass and addends
+                      + 3 * 64 * 128 * 128 + 64 * 64 * 128 + 2 * 64 * 128 * 64        # dK~, X, dWk, dP, dQ, dK
+                      + 2 * 64 * 64 * 128 + 2 * 64 * 128 * 64 + 2 * 64 * 64 * 64      # dT, dbV, dbgK, dA
+                      + 2 * 64 * 128 * 64)                                          # dK from dA
+
+
 def backward_leg(args, dev, stream):
     """Backward of the whole mixer (conv + SiLU, L2, recurrence, RMSNorm, gate) at model shape (16 QK / 48
-    value heads, d = 128, fp32), one sequence: the recurrence's forward keeps every state (64 KB per token
-    and value head) and its reverse pass reads them back."""
+    value heads, d = 128, fp32), one sequence. The recurrence's part is the chunked form: per 64-token
+    chunk and value head the WY factors are recomputed, the two chunk passes carry the state and its
+    derivative across chunks, and the rest is chunk-parallel fp32 products, so the leg is priced against
+    the fp32 MFMA peak on the products' multiply-adds (the HBM figure, inputs and outputs only, is given
+    beside it)."""
     import torch
     from linear_attention_token_amd import gdn
     from workloads import prefill_inputs
@@ -313,7 +330,7 @@ def backward_leg(args, dev, stream):
 
     step()
     torch.cuda.synchronize()
-    n = 3
+    n = 5
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(n):
@@ -324,18 +341,22 @@ def backward_leg(args, dev, stream):
     C = 2 * HK * D + HV * D
     # inputs (q, k, v, alpha, beta, gate, dout) read once, their derivatives written once, fp32
     io_bytes = 2 * 4 * T * (C + 2 * HV + HV * D + HV * D // 2)
-    spill = 2 * 4 * T * HV * D * D  # the kept states, written then read back
-    gb = (io_bytes + spill) / (ms * 1e-3) / 1e9
+    gb = io_bytes / (ms * 1e-3) / 1e9
+    flops = 2 * CBWD_FMA_PER_CHUNK * (-(-T // CH)) * HV
+    tf = flops / (ms * 1e-3) / 1e12
+    ws_bytes = ws.numel()
     del ws
     torch.cuda.empty_cache()
     return {
         "workload": f"mixer backward, B=1, T={T}, 16 QK / 48 value heads, d=128, fp32, every step on: derivatives "
                     f"for q, k, v, alpha, beta, gate, conv weights and norm gain from dout",
-        "ms_per_call": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
-        "roofline": dict(bound="hbm", achieved=round(gb, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                         frac=round(gb / HBM_PEAK_GBPS, 4), algorithmic_bytes=io_bytes, state_bytes=spill,
-                         note="achieved counts the kept states (written once, read once) with the inputs and "
-                              "outputs; the recurrence runs token by token per (sequence, head, 16-column slice)"),
+        "ms_per_call": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1), "workspace_bytes": ws_bytes,
+        "roofline": dict(bound="mfma", achieved=round(tf, 2), peak=MFMA_FP32_PEAK_TFLOPS, unit="TFLOP/s",
+                         frac=round(tf / MFMA_FP32_PEAK_TFLOPS, 4), algorithmic_flops=flops,
+                         hbm_GBps_inputs_outputs=round(gb, 1), hbm_frac_inputs_outputs=round(gb / HBM_PEAK_GBPS, 4),
+                         note="flops: the chunked form's fp32 products (forward recomputed, y included) per 64-token "
+                              "chunk and value head; the chunk states and factors kept in the workspace are "
+                              "not counted as HBM bytes"),
     }
 
 

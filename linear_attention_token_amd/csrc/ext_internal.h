@@ -53,7 +53,7 @@ struct CBwdArgs {
   float *S, *dS;                  // [I][128][128]: state at the chunk start; dL/d(state after the chunk)
   float *KK, *QK, *Am, *Pm, *Tm, *dP, *M1, *dT, *dA;  // [I][64][64]
   float *G, *bt;                  // [I][64]
-  float* dgc;                     // [I][8] per-slice parts of <S, dS'>
+  float* dgc;                     // [I][8][4] per-(slice, wave) parts of <S, dS'>
 };
 size_t cbwd_workspace_bytes(int n_seqs, int64_t T, int hv);
 void cbwd_plan(CBwdArgs& a, void* base);  // sets nc_max and every workspace region

@@ -171,14 +171,26 @@ __global__ void __launch_bounds__(256) k_cb_mm(Bmm b, const int4* __restrict__ t
   f32x4 acc[N / 16];
 #pragma unroll
   for (int j = 0; j < N / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // B operands of step p + 1 are read from LDS while step p's MFMAs run (the scheduling barriers keep
+  // the compiler from sinking the reads next to their uses)
+  float bop[2][4][N / 16];
+  auto read_b = [&](int p, float (&dst)[4][N / 16]) {
 #pragma unroll
-  for (int p = 0; p < K / 16; ++p)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float* brow = Bs + (16 * p + 4 * lg + c) * kLd + lm;
+      for (int j = 0; j < N / 16; ++j) dst[c][j] = Bs[(16 * p + 4 * lg + c) * kLd + 16 * j + lm];
+  };
+  read_b(0, bop[0]);
 #pragma unroll
-      for (int j = 0; j < N / 16; ++j) acc[j] = mfma16x16x4f32(av[p][c], brow[16 * j], acc[j]);
-    }
+  for (int p = 0; p < K / 16; ++p) {
+    if (p + 1 < K / 16) read_b(p + 1, bop[(p + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < N / 16; ++j) acc[j] = mfma16x16x4f32(av[p][c], bop[p & 1][c][j], acc[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float* C = b.C + item * b.sC;
 #pragma unroll
   for (int j = 0; j < N / 16; ++j) {
@@ -290,53 +302,145 @@ constexpr int kXLd = 20;  // LDS row stride of X and Z (floats): the four lane g
 
 struct PassLoads {
   float4 a1[8];      // A1 row 16w + l % 16, columns 4 (l / 16 + 4p) ..
-  float4 a2[2][4];   // A2^T rows 32w + 16i + l % 16, columns 4 (l / 16 + 4p) ..
   float b[4];        // B rows 16w + 4 (l / 16) + e
-  float h[2][4];     // H (backward), rows 32w + 16i + 4 (l / 16) + e
-  float sv[2][4];    // S (backward), same rows: <S, dS'> for dG
-  float gc;
+  float Gc;          // G at the chunk's last row (exponentiated at use: a wait here would stall the loads)
 };
 
 template <bool kBwd>
 __device__ __forceinline__ void pass_load(const CBwdArgs& a, int64_t item, int w, int lm, int lg, int col,
                                           PassLoads& L) {
   const float* A1 = (kBwd ? a.Kt : a.Wk) + item * kC * kD;
-  const float* A2T = (kBwd ? a.WkT : a.KtT) + item * kD * kC;
   const float* B = (kBwd ? a.dW : a.U) + item * kC * kD;
 #pragma unroll
   for (int p = 0; p < 8; ++p) L.a1[p] = *reinterpret_cast<const float4*>(A1 + (16 * w + lm) * kD + 4 * (lg + 4 * p));
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      L.a2[i][p] = *reinterpret_cast<const float4*>(A2T + (32 * w + 16 * i + lm) * kC + 4 * (lg + 4 * p));
-#pragma unroll
   for (int e = 0; e < 4; ++e) L.b[e] = B[(16 * w + 4 * lg + e) * kD + col];
+  L.Gc = a.G[item * kC + kC - 1];
+}
+
+// One chunk of a pass: X (the state at the chunk's start; backward: dL/d state after it) is stored, Z
+// computed and stored, and X advanced.
+template <bool kBwd>
+__device__ __forceinline__ void pass_step(const CBwdArgs& a, int64_t item, const PassLoads& L, int64_t next_item,
+                                          PassLoads& N, f32x4 (&X)[2], float* Xs, float* Zs, int w, int lane,
+                                          int lm, int lg, int col, int sl) {
+  const float s1 = kBwd ? 1.f : -1.f, s2 = kBwd ? -1.f : 1.f;
+  float* Zout = kBwd ? a.dW : a.W;
+  float* Xout = kBwd ? a.dS : a.S;
+  // A2^T operands, and (backward) H (in the dS slot, about to be overwritten by X) and S of this chunk:
+  // first used after the first products, so their loads overlap those (the operands of the first
+  // products were loaded a step ahead)
+  float4 a2[2][4];  // A2^T rows 32w + 16i + l % 16, columns 4 (l / 16 + 4p) ..
+  {
+    const float* A2T = (kBwd ? a.WkT : a.KtT) + item * kD * kC;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        a2[i][p] = *reinterpret_cast<const float4*>(A2T + (32 * w + 16 * i + lm) * kC + 4 * (lg + 4 * p));
+  }
+  float hv[2][4], sv[2][4];
   if (kBwd) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t o = item * kD * kD + (32 * w + 16 * i + 4 * lg + e) * kD + col;
-        L.h[i][e] = a.dS[o];
-        L.sv[i][e] = a.S[o];
+        hv[i][e] = a.dS[o];
+        sv[i][e] = a.S[o];
       }
   }
-  L.gc = __expf(a.G[item * kC + kC - 1]);
+  // The next chunk's first operands are requested after this chunk's: memory counters drain in order, so
+  // a wait for this chunk's operands then does not also wait for the next chunk's.
+  __builtin_amdgcn_sched_barrier(0);
+  pass_load<kBwd>(a, next_item, w, lm, lg, col, N);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 32 * w + 16 * i + 4 * lg + e;
+      Xs[row * kXLd + lm] = X[i][e];
+      Xout[item * kD * kD + size_t(row) * kD + col] = X[i][e];
+    }
+  __syncthreads();
+  // Z = B + s1 A1 X: rows 16w + 4 lg + e. Loaded values join the accumulators only after the products,
+  // so that no accumulator set-up waits for loads in flight.
+  // All B operands are read from LDS before the products, and two accumulators alternate, so the
+  // MFMAs issue back to back.
+  float xb[8][4];
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) xb[p][cc] = Xs[(16 * p + 4 * lg + cc) * kXLd + lm];
+  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+  f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0;
+#pragma unroll
+  for (int p = 0; p < 8; p += 2) {
+    const float av0[4] = {L.a1[p].x, L.a1[p].y, L.a1[p].z, L.a1[p].w};
+    const float av1[4] = {L.a1[p + 1].x, L.a1[p + 1].y, L.a1[p + 1].z, L.a1[p + 1].w};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      z0 = mfma16x16x4f32(s1 * av0[cc], xb[p][cc], z0);
+      z1 = mfma16x16x4f32(s1 * av1[cc], xb[p + 1][cc], z1);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = 16 * w + 4 * lg + e;
+    const float v = z0[e] + z1[e] + L.b[e];
+    Zs[t * kXLd + lm] = v;
+    Zout[item * kC * kD + t * kD + col] = v;
+  }
+  __syncthreads();
+  // X <- g_C X + H + s2 A2^T Z
+  const float gc = __expf(L.Gc);
+  float zb[4][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) zb[p][cc] = Zs[(16 * p + 4 * lg + cc) * kXLd + lm];
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][e] = gc * X[i][e];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float av0[4] = {a2[0][p].x, a2[0][p].y, a2[0][p].z, a2[0][p].w};
+    const float av1[4] = {a2[1][p].x, a2[1][p].y, a2[1][p].z, a2[1][p].w};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      acc[0] = mfma16x16x4f32(s2 * av0[cc], zb[p][cc], acc[0]);
+      acc[1] = mfma16x16x4f32(s2 * av1[cc], zb[p][cc], acc[1]);
+    }
+  }
+  if (kBwd) {  // this wave's part of <S, dS'> (for dG), then X <- ... + H
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part += sv[i][e] * X[i][e];
+    part = group_sum<64>(part);
+    if (lane == 0) a.dgc[(item * kSlices + sl) * 4 + w] = part;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] += hv[i][e];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) X[i] = acc[i];
 }
 
 template <bool kBwd>
-__global__ void __launch_bounds__(256) k_cb_pass(CBwdArgs a) {
+__global__ void __launch_bounds__(256, 2) k_cb_pass(CBwdArgs a) {
   __shared__ float Xs[kD * kXLd];
   __shared__ float Zs[kC * kXLd];
-  __shared__ float red[4];
   const int chain = blockIdx.x / kSlices, sl = blockIdx.x % kSlices;
   const int n = chain / a.hv, h = chain % a.hv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lm = lane & 15, lg = lane >> 4;
   const int col = kSl * sl + lm;
-  const float s1 = kBwd ? 1.f : -1.f, s2 = kBwd ? -1.f : 1.f;
-  float* Zout = kBwd ? a.dW : a.W;
-  float* Xout = kBwd ? a.dS : a.S;
   const float* x0 = kBwd ? a.dsf : a.s0;
   const size_t sb = (size_t(n) * a.hv + h) * kD * kD;
   f32x4 X[2];
@@ -345,60 +449,22 @@ __global__ void __launch_bounds__(256) k_cb_pass(CBwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) X[i][e] = x0 ? x0[sb + size_t(32 * w + 16 * i + 4 * lg + e) * kD + col] : 0.f;
   const int c0 = a.seq_off[n], nch = a.seq_off[n + 1] - c0;
-  PassLoads cur, nxt;
-  if (nch > 0) pass_load<kBwd>(a, int64_t(kBwd ? c0 + nch - 1 : c0) * a.hv + h, w, lm, lg, col, cur);
-  for (int it = 0; it < nch; ++it) {
-    const int c = kBwd ? c0 + nch - 1 - it : c0 + it;
-    const int64_t item = int64_t(c) * a.hv + h;
-    if (it + 1 < nch) pass_load<kBwd>(a, int64_t(kBwd ? c - 1 : c + 1) * a.hv + h, w, lm, lg, col, nxt);
-    // X (the state at the chunk's start; backward: dL/d state after it) to LDS and to its buffer
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 32 * w + 16 * i + 4 * lg + e;
-        Xs[row * kXLd + lm] = X[i][e];
-        Xout[item * kD * kD + size_t(row) * kD + col] = X[i][e];
-        if (kBwd) part += cur.sv[i][e] * X[i][e];
-      }
-    if (kBwd) {
-      part = group_sum<64>(part);
-      if (lane == 0) red[w] = part;
+  // chunk of step it (the backward walks the chunks in reverse)
+  auto item_of = [&](int it) { return int64_t(kBwd ? c0 + nch - 1 - it : c0 + it) * a.hv + h; };
+  // two operand sets used in turn, so the next chunk's loads are in flight during this chunk's products
+  // (no register copies between them that would wait for those loads)
+  // (no register copies between them that would wait for those loads). The loads are unconditional
+  // (past the last chunk they repeat it), so every wait for them counts the same loads on every path.
+  PassLoads L0, L1;
+  if (nch > 0) {
+    const int last = nch - 1;
+    pass_load<kBwd>(a, item_of(0), w, lm, lg, col, L0);
+    for (int it = 0;; it += 2) {
+      pass_step<kBwd>(a, item_of(it), L0, item_of(min(it + 1, last)), L1, X, Xs, Zs, w, lane, lm, lg, col, sl);
+      if (it + 1 > last) break;
+      pass_step<kBwd>(a, item_of(it + 1), L1, item_of(min(it + 2, last)), L0, X, Xs, Zs, w, lane, lm, lg, col, sl);
+      if (it + 2 > last) break;
     }
-    __syncthreads();
-    if (kBwd && tid == 0) a.dgc[item * kSlices + sl] = red[0] + red[1] + red[2] + red[3];
-    // Z = B + s1 A1 X: rows 16w + 4 lg + e
-    f32x4 z = {cur.b[0], cur.b[1], cur.b[2], cur.b[3]};
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const float av[4] = {cur.a1[p].x, cur.a1[p].y, cur.a1[p].z, cur.a1[p].w};
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) z = mfma16x16x4f32(s1 * av[cc], Xs[(16 * p + 4 * lg + cc) * kXLd + lm], z);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * w + 4 * lg + e;
-      Zs[t * kXLd + lm] = z[e];
-      Zout[item * kC * kD + t * kD + col] = z[e];
-    }
-    __syncthreads();
-    // X <- g_C X + H + s2 A2^T Z
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      f32x4 acc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = cur.gc * X[i][e] + (kBwd ? cur.h[i][e] : 0.f);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float av[4] = {cur.a2[i][p].x, cur.a2[i][p].y, cur.a2[i][p].z, cur.a2[i][p].w};
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          acc = mfma16x16x4f32(s2 * av[cc], Zs[(16 * p + 4 * lg + cc) * kXLd + lm], acc);
-      }
-      X[i] = acc;
-    }
-    cur = nxt;
   }
   if (kBwd && a.ds0) {
 #pragma unroll
@@ -453,66 +519,97 @@ __global__ void __launch_bounds__(256) k_cb_final(CBwdArgs a) {
   const int c = int(item / a.hv), h = int(item - int64_t(c) * a.hv);
   const int4 ct = a.tab[c];
   if (ct.y <= 0) return;
-  __shared__ float dG[kC], dbe[kC], dkd[kC], Gs[kC];
+  __shared__ float dG[kC], dbe[kC], dkd[kC], Gs[kC], bts[kC];
+  __shared__ float dAs[kC][kC + 1], KKs[kC][kC + 1], dPs[kC][kC + 1];
+  __shared__ float part[4][kC][2];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   if (tid < kC) Gs[tid] = a.G[item * kC + tid];
   __syncthreads();
   const float GC = Gs[kC - 1];
   const int64_t b2 = item * kC * kD, b1 = item * kC * kC;
-  // rows: one wave per 16 rows; lanes over the 128 columns (two each)
-  for (int t = 16 * w; t < 16 * w + 16; ++t) {
+  // rows: one wave per 16 rows, two rows at a time (a half-wave each, four columns per lane)
+  const int hw = lane >> 5, c4 = 4 * (lane & 31);
+  for (int r2 = 0; r2 < 8; ++r2) {
+    const int t = 16 * w + 2 * r2 + hw;
     const float g = __expf(Gs[t]), kd = __expf(GC - Gs[t]), be = a.bt[item * kC + t];
-    float sqx = 0.f, sbk = 0.f, sbv = 0.f, skt = 0.f;
-    for (int cc = lane; cc < kD; cc += 64) {
-      const int64_t o = b2 + t * kD + cc;
-      const float X = a.X[o], Q = a.Qi[o], K = a.Ki[o], V = a.Vi[o];
-      const float dbgk = a.dbgK[o], dbv = a.dbV[o], dkt = a.dKt[o];
-      sqx += Q * X;
-      sbk += dbgk * K;
-      sbv += dbv * V;
-      skt += dkt * K;
-      if (t < ct.y) {
-        const int64_t tok = (ct.x + t) * int64_t(a.hv) * kD + h * kD + cc;
-        a.dqh[tok] = a.dQ[o] + g * X;
-        a.dkh[tok] = a.dK[o] + kd * dkt + be * g * dbgk;
-        a.dv[tok] = be * dbv;
-      }
+    const int64_t o = b2 + t * kD + c4;
+    const float4 X = *reinterpret_cast<const float4*>(a.X + o), Q = *reinterpret_cast<const float4*>(a.Qi + o);
+    const float4 K = *reinterpret_cast<const float4*>(a.Ki + o), V = *reinterpret_cast<const float4*>(a.Vi + o);
+    const float4 dbgk = *reinterpret_cast<const float4*>(a.dbgK + o);
+    const float4 dbv = *reinterpret_cast<const float4*>(a.dbV + o);
+    const float4 dkt = *reinterpret_cast<const float4*>(a.dKt + o);
+    float sqx = Q.x * X.x + Q.y * X.y + Q.z * X.z + Q.w * X.w;
+    float sbk = dbgk.x * K.x + dbgk.y * K.y + dbgk.z * K.z + dbgk.w * K.w;
+    float sbv = dbv.x * V.x + dbv.y * V.y + dbv.z * V.z + dbv.w * V.w;
+    float skt = dkt.x * K.x + dkt.y * K.y + dkt.z * K.z + dkt.w * K.w;
+    if (t < ct.y) {
+      const int64_t tok = (ct.x + t) * int64_t(a.hv) * kD + h * kD + c4;
+      const float4 dQ = *reinterpret_cast<const float4*>(a.dQ + o), dK = *reinterpret_cast<const float4*>(a.dK + o);
+      const float bg = be * g;
+      *reinterpret_cast<float4*>(a.dqh + tok) =
+          make_float4(dQ.x + g * X.x, dQ.y + g * X.y, dQ.z + g * X.z, dQ.w + g * X.w);
+      *reinterpret_cast<float4*>(a.dkh + tok) =
+          make_float4(dK.x + kd * dkt.x + bg * dbgk.x, dK.y + kd * dkt.y + bg * dbgk.y,
+                      dK.z + kd * dkt.z + bg * dbgk.z, dK.w + kd * dkt.w + bg * dbgk.w);
+      *reinterpret_cast<float4*>(a.dv + tok) = make_float4(be * dbv.x, be * dbv.y, be * dbv.z, be * dbv.w);
     }
-    sqx = group_sum<64>(sqx);
-    sbk = group_sum<64>(sbk);
-    sbv = group_sum<64>(sbv);
-    skt = group_sum<64>(skt);
-    if (lane == 0) {
+    sqx = group_sum<32>(sqx);
+    sbk = group_sum<32>(sbk);
+    sbv = group_sum<32>(sbv);
+    skt = group_sum<32>(skt);
+    if ((lane & 31) == 0) {
       dG[t] = (sqx + be * sbk) * g;  // dg_t g_t
       dbe[t] = sbv + g * sbk;
       dkd[t] = skt * kd;              // dkd_t kd_t
     }
   }
   __syncthreads();
-  // E terms: dE (from dP o QK, plus dA o beta o KK), dbeta from dA o E o KK
-  if (tid < kC) {
-    const int t = tid;
-    const float be = a.bt[item * kC + t];
+  // E terms: dE (from dP o QK, plus dA o beta o KK), dbeta from dA o E o KK. The three 64 x 64 tiles are
+  // staged in LDS (stride 65: row and column walks are both conflict-free); thread (t, q) covers
+  // i = 16q .. 16q + 15 of row t and of column t.
+  for (int idx = tid; idx < kC * kC / 4; idx += 256) {
+    const int r = idx / (kC / 4), c4 = (idx % (kC / 4)) * 4;
+    const float4 da = *reinterpret_cast<const float4*>(a.dA + b1 + r * kC + c4);
+    const float4 kk = *reinterpret_cast<const float4*>(a.KK + b1 + r * kC + c4);
+    const float4 dp = *reinterpret_cast<const float4*>(a.dP + b1 + r * kC + c4);
+    const float dav[4] = {da.x, da.y, da.z, da.w}, kkv[4] = {kk.x, kk.y, kk.z, kk.w}, dpv[4] = {dp.x, dp.y, dp.z, dp.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dAs[r][c4 + j] = dav[j];
+      KKs[r][c4 + j] = kkv[j];
+      dPs[r][c4 + j] = dpv[j];
+    }
+  }
+  if (tid < kC) bts[tid] = a.bt[item * kC + tid];
+  __syncthreads();
+  {
+    const int t = tid & 63, q = tid >> 6;
+    const float be = bts[t];
     float rowsum = 0.f, colsum = 0.f, dbA = 0.f;
-    for (int i = 0; i < kC; ++i) {
+    for (int i = 16 * q; i < 16 * q + 16; ++i) {
       const float e_ti = __expf(fminf(Gs[t] - Gs[i], 0.f)), e_it = __expf(fminf(Gs[i] - Gs[t], 0.f));
-      const float dA_ti = a.dA[b1 + t * kC + i], kk_ti = a.KK[b1 + t * kC + i];
-      const float dE_ti = (i <= t ? a.dP[b1 + t * kC + i] : 0.f) + dA_ti * be * kk_ti;
+      const float dA_ti = dAs[t][i], kk_ti = KKs[t][i];
+      const float dE_ti = (i <= t ? dPs[t][i] : 0.f) + dA_ti * be * kk_ti;
       rowsum += dE_ti * e_ti;
       dbA += dA_ti * e_ti * kk_ti;
-      const float be_i = a.bt[item * kC + i];
-      const float dE_it = (t <= i ? a.dP[b1 + i * kC + t] : 0.f) + a.dA[b1 + i * kC + t] * be_i * a.KK[b1 + i * kC + t];
+      const float dE_it = (t <= i ? dPs[i][t] : 0.f) + dAs[i][t] * bts[i] * KKs[i][t];
       colsum += dE_it * e_it;
     }
-    dG[t] += rowsum - colsum - dkd[t];
-    dbe[t] += dbA;
+    part[q][t][0] = rowsum - colsum;
+    part[q][t][1] = dbA;
+  }
+  __syncthreads();
+  if (tid < kC) {
+    const int t = tid;
+    dG[t] += part[0][t][0] + part[1][t][0] + part[2][t][0] + part[3][t][0] - dkd[t];
+    dbe[t] += part[0][t][1] + part[1][t][1] + part[2][t][1] + part[3][t][1];
   }
   __syncthreads();
   if (tid == 0) {
     float s = 0.f;
     for (int i = 0; i < kC; ++i) s += dkd[i];
     float dgc = 0.f;
-    for (int k = 0; k < kSlices; ++k) dgc += a.dgc[item * kSlices + k];
+    for (int k = 0; k < 4 * kSlices; ++k) dgc += a.dgc[item * kSlices * 4 + k];
     dG[kC - 1] += s + dgc * __expf(GC);
   }
   __syncthreads();
@@ -561,7 +658,7 @@ size_t cbwd_workspace_bytes(int n_seqs, int64_t T, int hv) {
          21 * al(f * items * kC * kD) +           // the 64 x 128 tiles (KtT, WkT stored 128 x 64)
          2 * al(f * items * kD * kD) +            // S dS
          9 * al(f * items * kC * kC) +            // KK QK Am Pm Tm dP M1 dT dA
-         2 * al(f * items * kC) + al(f * items * kSlices) +  // G bt dgc
+         2 * al(f * items * kC) + al(f * items * kSlices * 4) +  // G bt dgc
          2 * al(f * size_t(T) * hv * kD);          // dqh dkh
 }
 
@@ -586,7 +683,7 @@ void cbwd_plan(CBwdArgs& a, void* base) {
   for (float** q : sms) *q = static_cast<float*>(take(sm));
   a.G = static_cast<float*>(take(f * items * kC));
   a.bt = static_cast<float*>(take(f * items * kC));
-  a.dgc = static_cast<float*>(take(f * items * kSlices));
+  a.dgc = static_cast<float*>(take(f * items * kSlices * 4));
   a.dqh = static_cast<float*>(take(f * size_t(a.T) * a.hv * kD));
   a.dkh = static_cast<float*>(take(f * size_t(a.T) * a.hv * kD));
 }
