@@ -22,10 +22,14 @@ struct BwdMixArgs {
   float* du;                    // workspace [T][C]: dL/d(conv output)
   float *dq, *dk, *dv;          // out: dL/d(raw inputs)
   float* dconv_w;               // out [C][4]
-  float* dw_part;               // workspace [ceil(T / 64)][C][4]: per-token-block parts of dconv_w
+  float* dw_part;               // workspace [<= kConvWeightParts][C][4]: per-token-window-group parts of dconv_w
   float* dconv_in;              // out [N][3][C] or null
 };
-// dw_part: workspace of ceil(rows / 64) x 128 floats
+// Parts of the two weight derivatives that the backward sums in a fixed order: the norm gain's
+// (kNormGateParts x 128 floats of workspace) and the conv weights' (up to kConvWeightParts x C x 4).
+constexpr int kNormGateParts = 1024;
+constexpr int kConvWeightParts = 256;
+// dw_part: workspace of kNormGateParts x 128 floats
 hipError_t launch_norm_gate_bwd(int64_t rows, const float* y, const float* z, const float* dout, const float* norm_w,
                                 float eps, float* dy, float* dz, float* dnorm_w, float* dw_part, hipStream_t s);
 hipError_t launch_mixer_input_bwd(const BwdMixArgs& m, hipStream_t s);

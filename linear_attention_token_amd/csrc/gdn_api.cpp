@@ -616,7 +616,8 @@ static size_t mixer_bwd_workspace_bytes(const Problem& p, int64_t T) {
   return align256(plan_workspace(p, nullptr).bytes) + bwd_workspace_bytes(p.n_seqs, T, p.hv) +
          2 * align256(sizeof(float) * th * 128) + 2 * align256(sizeof(float) * tk * 128) +
          align256(sizeof(float) * th * 128) + align256(sizeof(float) * size_t(T) * size_t(p.C)) +
-         align256(sizeof(float) * ((th + 63) / 64) * 128) + align256(sizeof(float) * size_t((T + 63) / 64) * p.C * 4);
+         align256(sizeof(float) * kNormGateParts * 128) +
+         align256(sizeof(float) * size_t(std::min<int64_t>((T + 15) / 16, kConvWeightParts)) * p.C * 4);
 }
 
 static gdn_status check_mixer_bwd(const gdn_cfg* cfg, int32_t n_seqs, int64_t T, Problem& p) {
@@ -700,7 +701,7 @@ gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens
   float* du = reinterpret_cast<float*>(w);
   w += align256(sizeof(float) * size_t(total_tokens) * size_t(p.C));
   float* dw_part = reinterpret_cast<float*>(w);
-  w += align256(sizeof(float) * ((th + 63) / 64) * 128);
+  w += align256(sizeof(float) * kNormGateParts * 128);
   float* dcw_part = reinterpret_cast<float*>(w);
   a.y = y;
   a.dy = dy;

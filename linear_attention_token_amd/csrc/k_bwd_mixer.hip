@@ -6,11 +6,13 @@
 //   k_l2silu_bwd      a = a0 / sqrt(|a0|^2 + eps) (q, k heads), a0 = silu(u), u the conv output:
 //                     da0 = (da - a <a, da>) / sqrt(|a0|^2 + eps);  du = da0 sigmoid(u) (1 + u (1 - sigmoid(u)))
 //   k_conv_bwd        u[t] = sum_j w[j] x[t - 3 + j]:  dx[t] = sum_j w[j] du[t + 3 - j] (inside the sequence),
-//                     dw[j] = sum_t du[t] x[t - 3 + j] (x[-3..-1] = the conv history; per 64-token block
+//                     dw[j] = sum_t du[t] x[t - 3 + j] (x[-3..-1] = the conv history; per 16-token block
 //                     parts, then k_conv_w_sum)
 //   k_conv_in_bwd     d history[r] = sum_j w[j] du[r - j] (r = 0..2 for positions -3..-1)
 // (the steps of the paper reading "On the Design of Qwen3.8-Next Architecture … 精读" §四 4.1 and the
 // analysis notes "Qwen3.8-Flash-Next：架构、效率与技术谱系" §03, differentiated).
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "ext_internal.h"
 
@@ -41,42 +43,67 @@ __global__ void __launch_bounds__(256) k_zero(float* __restrict__ p, int64_t n) 
   if (i < n) p[i] = 0.f;
 }
 
-// One wave per (token, value head) row, lanes holding channels lane and lane + 64; 16 rows per wave.
+// Half a wave per (token, value head) row, four channels per lane; block b takes rows 8b + i, 8b + i +
+// 8 gridDim.x, ... (i its half-wave), so its part of dw is the sum over a fixed set of rows.
 __global__ void __launch_bounds__(256) k_norm_gate_bwd(int64_t rows, const float* __restrict__ y,
                                                        const float* __restrict__ z, const float* __restrict__ dout,
                                                        const float* __restrict__ norm_w, float eps,
                                                        float* __restrict__ dy, float* __restrict__ dz,
                                                        float* __restrict__ dw_part) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const float w0 = 1.f + norm_w[lane], w1 = 1.f + norm_w[lane + 64];
-  float dw0 = 0.f, dw1 = 0.f;
-  for (int i = 0; i < 16; ++i) {
-    const int64_t row = (int64_t(blockIdx.x) * 4 + w) * 16 + i;
-    if (row >= rows) break;
-    const int64_t b = row * kD;
-    const float y0 = y[b + lane], y1 = y[b + lane + 64];
-    const float r = sqrtf(wave_sum(y0 * y0 + y1 * y1) * (1.f / kD) + eps), ir = 1.f / r;
-    const float s0 = 1.f / (1.f + __expf(-z[b + lane])), s1 = 1.f / (1.f + __expf(-z[b + lane + 64]));
-    const float do0 = dout[b + lane], do1 = dout[b + lane + 64];
-    const float n0 = y0 * ir * w0, n1 = y1 * ir * w1;
-    dz[b + lane] = do0 * n0 * s0 * (1.f - s0);
-    dz[b + lane + 64] = do1 * n1 * s1 * (1.f - s1);
-    const float dn0 = do0 * s0, dn1 = do1 * s1;
-    dw0 = fmaf(dn0 * y0, ir, dw0);
-    dw1 = fmaf(dn1 * y1, ir, dw1);
-    const float g0 = w0 * dn0, g1 = w1 * dn1;
-    const float dot = wave_sum(g0 * y0 + g1 * y1) * ir * ir * ir * (1.f / kD);
-    dy[b + lane] = g0 * ir - y0 * dot;
-    dy[b + lane + 64] = g1 * ir - y1 * dot;
+  const int l = threadIdx.x & 31, hw = threadIdx.x >> 5, d0 = 4 * l;
+  const float4 nw = *reinterpret_cast<const float4*>(norm_w + d0);
+  const float wg[4] = {1.f + nw.x, 1.f + nw.y, 1.f + nw.z, 1.f + nw.w};
+  float dwa[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kBatch = 4;  // rows whose loads are issued together
+  const int64_t stride = int64_t(gridDim.x) * 8;
+  for (int64_t row0 = int64_t(blockIdx.x) * 8 + hw; row0 < rows; row0 += kBatch * stride) {
+  float4 y4s[kBatch], z4s[kBatch], o4s[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int64_t row = min(row0 + k * stride, rows - 1);
+    const int64_t b = row * kD + d0;
+    y4s[k] = *reinterpret_cast<const float4*>(y + b);
+    z4s[k] = *reinterpret_cast<const float4*>(z + b);
+    o4s[k] = *reinterpret_cast<const float4*>(dout + b);
   }
-  // this block's part of the norm gain's derivative: the waves' sums, then one row of dw_part
-  __shared__ float red[4][kD];
-  red[w][lane] = dw0;
-  red[w][lane + 64] = dw1;
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int64_t row = row0 + k * stride;
+    if (row >= rows) break;  // uniform over the half-wave
+    const int64_t b = row * kD + d0;
+    const float4 y4 = y4s[k], z4 = z4s[k], o4 = o4s[k];
+    const float yv[4] = {y4.x, y4.y, y4.z, y4.w}, zv[4] = {z4.x, z4.y, z4.z, z4.w};
+    const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+    const float r = sqrtf(group_sum<32>(yv[0] * yv[0] + yv[1] * yv[1] + yv[2] * yv[2] + yv[3] * yv[3]) * (1.f / kD) + eps);
+    const float ir = 1.f / r;
+    float dzv[4], g[4], gy = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sg = 1.f / (1.f + __expf(-zv[e]));
+      const float nv = yv[e] * ir * wg[e];
+      dzv[e] = ov[e] * nv * sg * (1.f - sg);
+      const float dn = ov[e] * sg;
+      dwa[e] = fmaf(dn * yv[e], ir, dwa[e]);
+      g[e] = wg[e] * dn;
+      gy += g[e] * yv[e];
+    }
+    const float dot = group_sum<32>(gy) * ir * ir * ir * (1.f / kD);
+    *reinterpret_cast<float4*>(dz + b) = make_float4(dzv[0], dzv[1], dzv[2], dzv[3]);
+    *reinterpret_cast<float4*>(dy + b) =
+        make_float4(g[0] * ir - yv[0] * dot, g[1] * ir - yv[1] * dot, g[2] * ir - yv[2] * dot, g[3] * ir - yv[3] * dot);
+  }
+  }
+  // this block's part of the norm gain's derivative: the half-waves' sums in a fixed order
+  __shared__ float red[8][kD];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[hw][d0 + e] = dwa[e];
   __syncthreads();
-  if (threadIdx.x < kD)
-    dw_part[int64_t(blockIdx.x) * kD + threadIdx.x] =
-        red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+  if (threadIdx.x < kD) {
+    float sacc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sacc += red[i][threadIdx.x];
+    dw_part[int64_t(blockIdx.x) * kD + threadIdx.x] = sacc;
+  }
 }
 
 // dnorm_w[c] = sum over the blocks' rows of dw_part: 8 groups of 128 threads take every eighth row, then
@@ -112,14 +139,16 @@ __device__ __forceinline__ float conv_at(const float* x, int64_t ld_x, int64_t c
   return u;
 }
 
-// One wave per (token, head) of q, k (L2 and SiLU) or v (SiLU): du into [T][C].
+// Half a wave per (token, head) of q, k (L2 and SiLU) or v (SiLU), four channels per lane: du into
+// [T][C]. Eight rows per block.
 __global__ void __launch_bounds__(256) k_l2silu_bwd(BwdMixArgs m) {
-  const int lane = threadIdx.x & 63;
-  const int64_t item = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 31;
+  const int64_t item = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 5);
   const int heads = 2 * m.hk + m.hv;
-  if (item >= m.T * heads) return;
-  const int64_t t = item / heads;
-  const int hd = int(item - t * heads);
+  const bool live = item < m.T * heads;  // the shuffles below run in every lane
+  const int64_t it = live ? item : 0;
+  const int64_t t = it / heads;
+  const int hd = int(it - t * heads);
   const int n = seq_of(m.cu, m.n_seqs, t);
   const int64_t s0 = m.cu[n];
   const float* hist = m.conv_in ? m.conv_in + int64_t(n) * 3 * m.C : nullptr;
@@ -138,33 +167,52 @@ __global__ void __launch_bounds__(256) k_l2silu_bwd(BwdMixArgs m) {
     da = m.dva + (t * m.hv + hd - 2 * m.hk) * kD;
     l2 = false;
   }
-  const int64_t cbase = int64_t(hd) * kD;  // conv channel of the head's first dim (q | k | v order)
-  float u[2], a0[2], g[2];
+  const int d0 = 4 * l;
+  const int64_t c0 = int64_t(hd) * kD + d0;  // conv channel of this lane's first dim (q | k | v order)
+  // the four taps' inputs (history before the sequence start) and the weights, as float4s
+  float4 xs[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int d = lane + 64 * i;
-    const int64_t c = cbase + d;
-    u[i] = conv_at(x, ld, col0 + d, m.conv_w + c * 4, t, s0, hist, m.C, c);
-    const float sg = 1.f / (1.f + __expf(-u[i]));
-    a0[i] = u[i] * sg;
-    g[i] = da[d];
-    u[i] = sg * (1.f + u[i] * (1.f - sg));  // silu'(u), kept in u
+  for (int j = 0; j < 4; ++j) {
+    const int64_t p = t - 3 + j;
+    xs[j] = p >= s0 ? *reinterpret_cast<const float4*>(x + p * ld + col0 + d0)
+                    : (hist ? *reinterpret_cast<const float4*>(hist + (p - s0 + 3) * m.C + c0) : make_float4(0.f, 0.f, 0.f, 0.f));
   }
-  if (l2) {
-    const float inv = 1.f / sqrtf(wave_sum(a0[0] * a0[0] + a0[1] * a0[1]) + m.l2_eps);
-    const float adot = wave_sum(a0[0] * g[0] + a0[1] * g[1]) * inv;  // <a, da> with a = a0 inv
+  float4 w4[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) g[i] = (g[i] - a0[i] * inv * adot) * inv;
+  for (int e = 0; e < 4; ++e) w4[e] = *reinterpret_cast<const float4*>(m.conv_w + (c0 + e) * 4);
+  const float4 g4 = *reinterpret_cast<const float4*>(da + d0);
+  float u[4], a0[4], g[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float wv[4] = {w4[e].x, w4[e].y, w4[e].z, w4[e].w};
+    float uu = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float xv = e == 0 ? xs[j].x : e == 1 ? xs[j].y : e == 2 ? xs[j].z : xs[j].w;
+      uu = fmaf(wv[j], xv, uu);
+    }
+    const float sg = 1.f / (1.f + __expf(-uu));
+    a0[e] = uu * sg;
+    u[e] = sg * (1.f + uu * (1.f - sg));  // silu'(u)
   }
+  if (l2) {  // uniform over the half-wave (one head)
+    const float inv = 1.f / sqrtf(group_sum<32>(a0[0] * a0[0] + a0[1] * a0[1] + a0[2] * a0[2] + a0[3] * a0[3]) + m.l2_eps);
+    const float adot = group_sum<32>(a0[0] * g[0] + a0[1] * g[1] + a0[2] * g[2] + a0[3] * g[3]) * inv;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) m.du[t * m.C + cbase + lane + 64 * i] = g[i] * u[i];
+    for (int e = 0; e < 4; ++e) g[e] = (g[e] - a0[e] * inv * adot) * inv;
+  }
+  if (live)
+    *reinterpret_cast<float4*>(m.du + t * m.C + c0) = make_float4(g[0] * u[0], g[1] * u[1], g[2] * u[2], g[3] * u[3]);
 }
 
-// Thread per channel, 64 packed tokens per block row: dx for those tokens and this block's part of dw.
+// Thread per channel, kConvBwdRows packed tokens per block row: dx for those tokens and this block's part
+// of dw. The du rows t .. t + 3 and x rows t - 3 .. t that the tokens read are loaded once each, all
+// before use (history rows of a sequence start are read where needed).
+constexpr int kConvBwdRows = 16;
 __global__ void __launch_bounds__(256) k_conv_bwd(BwdMixArgs m) {
+  constexpr int R = kConvBwdRows;
   const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (c >= m.C) return;
-  const int64_t t0 = int64_t(blockIdx.y) * 64, t1 = min(t0 + 64, m.T);
   // channel -> (input tensor, column, output tensor)
   const float* x;
   float* dx;
@@ -177,39 +225,68 @@ __global__ void __launch_bounds__(256) k_conv_bwd(BwdMixArgs m) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) w4[j] = m.conv_w[c * 4 + j];
   float dw[4] = {0.f, 0.f, 0.f, 0.f};
+  // windows blockIdx.y, + gridDim.y, ...: this block's part of dw sums a fixed set of tokens
+  for (int64_t t0 = int64_t(blockIdx.y) * R; t0 < m.T; t0 += int64_t(gridDim.y) * R) {
+  const int64_t t1 = min(t0 + R, m.T);
+  float duw[R + 3], xw[R + 3];  // du[t0 + i], x[t0 - 3 + i]
+#pragma unroll
+  for (int i = 0; i < R + 3; ++i) {
+    const int64_t tu = t0 + i, p = t0 - 3 + i;
+    duw[i] = tu < m.T ? m.du[tu * m.C + c] : 0.f;
+    xw[i] = (p >= 0 && p < m.T) ? x[p * ld + col] : 0.f;
+  }
   int n = seq_of(m.cu, m.n_seqs, t0);
-  for (int64_t t = t0; t < t1; ++t) {
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int64_t t = t0 + i;
+    if (t >= t1) break;
     while (n + 1 < m.n_seqs && int64_t(m.cu[n + 1]) <= t) ++n;
     const int64_t s0 = m.cu[n], s1 = m.cu[n + 1];
-    const float* hist = m.conv_in ? m.conv_in + int64_t(n) * 3 * m.C : nullptr;
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t tu = t + 3 - j;  // the conv output that reads x[t] through tap j
-      if (tu < s1) acc = fmaf(w4[j], m.du[tu * m.C + c], acc);
+      if (tu < s1) acc = fmaf(w4[j], duw[i + 3 - j], acc);
     }
     dx[t * ld + col] = acc;
-    const float dut = m.du[t * m.C + c];
+    const float dut = duw[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t p = t - 3 + j;
-      const float xv = p >= s0 ? x[p * ld + col] : (hist ? hist[(p - s0 + 3) * m.C + c] : 0.f);
+      float xv;
+      if (p >= s0) xv = xw[i + j];
+      else xv = m.conv_in ? m.conv_in[(int64_t(n) * 3 + (p - s0 + 3)) * m.C + c] : 0.f;
       dw[j] = fmaf(dut, xv, dw[j]);
     }
+  }
   }
   *reinterpret_cast<float4*>(m.dw_part + (int64_t(blockIdx.y) * m.C + c) * 4) = make_float4(dw[0], dw[1], dw[2], dw[3]);
 }
 
-// dconv_w = the sum of the token blocks' parts, in block order (reproducible).
+// dconv_w = the sum of the token-window groups' parts: thread (channel, q) adds parts q, q + 4, ..., then
+// the four sums are added in order (reproducible). 64 channels per block.
 __global__ void __launch_bounds__(256) k_conv_w_sum(BwdMixArgs m, int64_t nblocks) {
-  const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (c >= m.C) return;
+  __shared__ float4 red[4][64];
+  const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t c = int64_t(blockIdx.x) * 64 + cl;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t b = 0; b < nblocks; ++b) {
-    const float4 v = *reinterpret_cast<const float4*>(m.dw_part + (b * m.C + c) * 4);
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  if (c < m.C) {
+#pragma unroll 4
+    for (int64_t b = q; b < nblocks; b += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(m.dw_part + (b * m.C + c) * 4);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
   }
-  *reinterpret_cast<float4*>(m.dconv_w + c * 4) = acc;
+  red[q][cl] = acc;
+  __syncthreads();
+  if (q == 0 && c < m.C) {
+    float4 t = red[0][cl];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      t.x += red[i][cl].x; t.y += red[i][cl].y; t.z += red[i][cl].z; t.w += red[i][cl].w;
+    }
+    *reinterpret_cast<float4*>(m.dconv_w + c * 4) = t;
+  }
 }
 
 // d conv_in[n][r][c] = sum_j w[c][j] du[s0 + r - j] for s0 + r - j in [s0, s1).
@@ -232,7 +309,7 @@ hipError_t launch_norm_gate_bwd(int64_t rows, const float* y, const float* z, co
     hipLaunchKernelGGL(k_zero, dim3(1), dim3(256), 0, s, dnorm_w, int64_t(kD));
     return hipGetLastError();
   }
-  const int64_t nb = (rows + 63) / 64;
+  const int64_t nb = std::min<int64_t>((rows + 7) / 8, kNormGateParts);
   hipLaunchKernelGGL(k_norm_gate_bwd, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, rows, y, z, dout, norm_w, eps,
                      dy, dz, dw_part);
   hipLaunchKernelGGL(k_sum_parts, dim3(1), dim3(1024), 0, s, dw_part, nb, dnorm_w);
@@ -241,11 +318,12 @@ hipError_t launch_norm_gate_bwd(int64_t rows, const float* y, const float* z, co
 
 hipError_t launch_mixer_input_bwd(const BwdMixArgs& m, hipStream_t s) {
   if (m.T > 0) {
-    const int64_t items = m.T * (2 * m.hk + m.hv), nb = (m.T + 63) / 64;
-    hipLaunchKernelGGL(k_l2silu_bwd, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0, s, m);
+    const int64_t items = m.T * (2 * m.hk + m.hv);
+    const int64_t nb = std::min<int64_t>((m.T + kConvBwdRows - 1) / kConvBwdRows, kConvWeightParts);
+    hipLaunchKernelGGL(k_l2silu_bwd, dim3(static_cast<unsigned>((items + 7) / 8)), dim3(256), 0, s, m);
     hipLaunchKernelGGL(k_conv_bwd, dim3(static_cast<unsigned>((m.C + 255) / 256), static_cast<unsigned>(nb)),
                        dim3(256), 0, s, m);
-    hipLaunchKernelGGL(k_conv_w_sum, dim3(static_cast<unsigned>((m.C + 255) / 256)), dim3(256), 0, s, m, nb);
+    hipLaunchKernelGGL(k_conv_w_sum, dim3(static_cast<unsigned>((m.C + 63) / 64)), dim3(256), 0, s, m, nb);
   } else {
     hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>((m.C * 4 + 255) / 256)), dim3(256), 0, s, m.dconv_w, m.C * 4);
   }

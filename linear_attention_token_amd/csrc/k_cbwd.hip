@@ -224,66 +224,129 @@ __global__ void __launch_bounds__(256) k_cb_mm(Bmm b, const int4* __restrict__ t
 __global__ void __launch_bounds__(256) k_cb_ap(CBwdArgs a) {
   const int64_t item = blockIdx.x;
   if (a.tab[item / a.hv].y <= 0) return;
-  const float* G = a.G + item * kC;
-  const float* bt = a.bt + item * kC;
-  for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
-    const int t = idx / kC, i = idx % kC;
-    const float e = __expf(fminf(G[t] - G[i], 0.f));
-    const int64_t o = item * kC * kC + idx;
-    a.Am[o] = i < t ? bt[t] * e * a.KK[o] : 0.f;
-    a.Pm[o] = i <= t ? e * a.QK[o] : 0.f;
+  __shared__ float Gs[kC], Bs[kC];
+  if (threadIdx.x < kC) {
+    Gs[threadIdx.x] = a.G[item * kC + threadIdx.x];
+    Bs[threadIdx.x] = a.bt[item * kC + threadIdx.x];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kC * kC / 4; idx += 256) {
+    const int t = idx / (kC / 4), i0 = (idx % (kC / 4)) * 4;
+    const int64_t o = item * kC * kC + t * kC + i0;
+    const float4 kk = *reinterpret_cast<const float4*>(a.KK + o), qk = *reinterpret_cast<const float4*>(a.QK + o);
+    const float kkv[4] = {kk.x, kk.y, kk.z, kk.w}, qkv[4] = {qk.x, qk.y, qk.z, qk.w};
+    float av[4], pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e;
+      const float ex = __expf(fminf(Gs[t] - Gs[i], 0.f));
+      av[e] = i < t ? Bs[t] * ex * kkv[e] : 0.f;
+      pv[e] = i <= t ? ex * qkv[e] : 0.f;
+    }
+    *reinterpret_cast<float4*>(a.Am + o) = make_float4(av[0], av[1], av[2], av[3]);
+    *reinterpret_cast<float4*>(a.Pm + o) = make_float4(pv[0], pv[1], pv[2], pv[3]);
   }
 }
 
-// ---- T = (I + A)^-1 by forward substitution: one wave per item, lane = column ----
-__global__ void __launch_bounds__(64) k_cb_inv(CBwdArgs a) {
+// ---- T = (I + A)^-1, A strictly lower, by 16 x 16 blocks ----
+// The diagonal blocks D_i = (I + A_ii)^-1 by forward substitution (wave i, lane = column), then block
+// row by block row T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj (j < i).
+__global__ void __launch_bounds__(256) k_cb_inv(CBwdArgs a) {
   __shared__ float As[kC][kC + 1];
-  __shared__ float Xs[kC][kC + 1];
-  const int lane = threadIdx.x;
+  __shared__ float Ts[kC][kC + 1];
+  __shared__ float Rs[3][16][17];
   const int64_t item = blockIdx.x;
   if (a.tab[item / a.hv].y <= 0) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const float* A = a.Am + item * kC * kC;
-  for (int r = 0; r < kC; ++r) As[r][lane] = A[r * kC + lane];
+  for (int idx = tid; idx < kC * kC / 4; idx += 256) {
+    const int r = idx / (kC / 4), c4 = (idx % (kC / 4)) * 4;
+    const float4 v = *reinterpret_cast<const float4*>(A + r * kC + c4);
+    As[r][c4] = v.x; As[r][c4 + 1] = v.y; As[r][c4 + 2] = v.z; As[r][c4 + 3] = v.w;
+    Ts[r][c4] = 0.f; Ts[r][c4 + 1] = 0.f; Ts[r][c4 + 2] = 0.f; Ts[r][c4 + 3] = 0.f;
+  }
   __syncthreads();
-  for (int t = 0; t < kC; ++t) {
-    float x = (t == lane) ? 1.f : 0.f;
-    for (int i = 0; i < t; ++i) x -= As[t][i] * Xs[i][lane];
-    Xs[t][lane] = x;
+  if (lane < 16) {  // D_w, column `lane`
+    const int o = 16 * w;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+      for (int q = 0; q < r; ++q) v -= As[o + r][o + q] * x[q];
+      x[r] = v;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ts[o + r][o + lane] = x[r];
+  }
+  __syncthreads();
+  const int r = tid >> 4, c = tid & 15;
+  for (int i = 1; i < 4; ++i) {
+    // R_ij (j < i), element (r, c), into Rs[j]
+    for (int j = 0; j < i; ++j) {
+      float acc = 0.f;
+      for (int k = j; k < i; ++k)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc += As[16 * i + r][16 * k + q] * Ts[16 * k + q][16 * j + c];
+      Rs[j][r][c] = acc;
+    }
+    __syncthreads();
+    for (int j = 0; j < i; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc += Ts[16 * i + r][16 * i + q] * Rs[j][q][c];
+      Ts[16 * i + r][16 * j + c] = -acc;
+    }
     __syncthreads();
   }
   float* T = a.Tm + item * kC * kC;
-  for (int r = 0; r < kC; ++r) T[r * kC + lane] = Xs[r][lane];
+  for (int idx = tid; idx < kC * kC / 4; idx += 256) {
+    const int rr = idx / (kC / 4), c4 = (idx % (kC / 4)) * 4;
+    *reinterpret_cast<float4*>(T + rr * kC + c4) = make_float4(Ts[rr][c4], Ts[rr][c4 + 1], Ts[rr][c4 + 2], Ts[rr][c4 + 3]);
+  }
 }
 
 // ---- bV = diag(beta) V, bgK = diag(beta g) K, Kt = diag(kd) K and its transpose, gQ = diag(g) Q ----
 __global__ void __launch_bounds__(256) k_cb_prep(CBwdArgs a) {
   __shared__ float tile[kC][kC + 1];
+  __shared__ float gs[kC], kds[kC], bs[kC];
   const int64_t item = blockIdx.x;
   if (a.tab[item / a.hv].y <= 0) return;
-  const float* G = a.G + item * kC;
-  const float GC = G[kC - 1];
+  if (threadIdx.x < kC) {
+    const float* G = a.G + item * kC;
+    const float Gt = G[threadIdx.x];
+    gs[threadIdx.x] = __expf(Gt);
+    kds[threadIdx.x] = __expf(G[kC - 1] - Gt);
+    bs[threadIdx.x] = a.bt[item * kC + threadIdx.x];
+  }
+  __syncthreads();
   const int64_t b2 = item * kC * kD;
-  for (int idx = threadIdx.x; idx < kC * kD; idx += 256) {
-    const int t = idx / kD;
-    const float be = a.bt[item * kC + t], g = __expf(G[t]);
-    const int64_t o = b2 + idx;
-    const float kv = a.Ki[o];
-    a.bV[o] = be * a.Vi[o];
-    a.bgK[o] = be * g * kv;
-    a.Kt[o] = __expf(GC - G[t]) * kv;
-    a.gQ[o] = g * a.Qi[o];
+  for (int idx = threadIdx.x; idx < kC * kD / 4; idx += 256) {
+    const int t = idx / (kD / 4);
+    const int64_t o = b2 + 4 * idx;
+    const float be = bs[t], g = gs[t], kd = kds[t], bg = be * g;
+    const float4 kv = *reinterpret_cast<const float4*>(a.Ki + o);
+    const float4 vv = *reinterpret_cast<const float4*>(a.Vi + o);
+    const float4 qv = *reinterpret_cast<const float4*>(a.Qi + o);
+    *reinterpret_cast<float4*>(a.bV + o) = make_float4(be * vv.x, be * vv.y, be * vv.z, be * vv.w);
+    *reinterpret_cast<float4*>(a.bgK + o) = make_float4(bg * kv.x, bg * kv.y, bg * kv.z, bg * kv.w);
+    *reinterpret_cast<float4*>(a.Kt + o) = make_float4(kd * kv.x, kd * kv.y, kd * kv.z, kd * kv.w);
+    *reinterpret_cast<float4*>(a.gQ + o) = make_float4(g * qv.x, g * qv.y, g * qv.z, g * qv.w);
   }
   // KtT [128][64], through LDS in two 64-column halves
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
-      const int t = idx / kC, r = idx % kC;
-      tile[t][r] = __expf(GC - G[t]) * a.Ki[b2 + t * kD + 64 * half + r];
+    for (int idx = threadIdx.x; idx < kC * kC / 4; idx += 256) {
+      const int t = idx / (kC / 4), r4 = (idx % (kC / 4)) * 4;
+      const float4 kv = *reinterpret_cast<const float4*>(a.Ki + b2 + t * kD + 64 * half + r4);
+      const float kd = kds[t];
+      tile[t][r4] = kd * kv.x; tile[t][r4 + 1] = kd * kv.y; tile[t][r4 + 2] = kd * kv.z; tile[t][r4 + 3] = kd * kv.w;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
-      const int r = idx / kC, t = idx % kC;
-      a.KtT[b2 + (64 * half + r) * kC + t] = tile[t][r];
+    for (int idx = threadIdx.x; idx < kC * kC / 4; idx += 256) {
+      const int r = idx / (kC / 4), t4 = (idx % (kC / 4)) * 4;
+      *reinterpret_cast<float4*>(a.KtT + b2 + (64 * half + r) * kC + t4) =
+          make_float4(tile[t4][r], tile[t4 + 1][r], tile[t4 + 2][r], tile[t4 + 3][r]);
     }
   }
 }
@@ -491,13 +554,19 @@ __global__ void __launch_bounds__(256) k_cb_scatter_y(CBwdArgs a) {
 __global__ void __launch_bounds__(256) k_cb_ew1(CBwdArgs a) {
   const int64_t item = blockIdx.x;
   if (a.tab[item / a.hv].y <= 0) return;
-  const float* G = a.G + item * kC;
-  for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
-    const int t = idx / kC, i = idx % kC;
-    const int64_t o = item * kC * kC + idx;
-    const float dp = a.dP[o];
-    a.M1[o] = dp * __expf(fminf(G[t] - G[i], 0.f));
-    a.dP[o] = dp * a.QK[o];
+  __shared__ float Gs[kC];
+  if (threadIdx.x < kC) Gs[threadIdx.x] = a.G[item * kC + threadIdx.x];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kC * kC / 4; idx += 256) {
+    const int t = idx / (kC / 4), i0 = (idx % (kC / 4)) * 4;
+    const int64_t o = item * kC * kC + t * kC + i0;
+    const float4 dp = *reinterpret_cast<const float4*>(a.dP + o), qk = *reinterpret_cast<const float4*>(a.QK + o);
+    const float dpv[4] = {dp.x, dp.y, dp.z, dp.w};
+    float m1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m1[e] = dpv[e] * __expf(fminf(Gs[t] - Gs[i0 + e], 0.f));
+    *reinterpret_cast<float4*>(a.M1 + o) = make_float4(m1[0], m1[1], m1[2], m1[3]);
+    *reinterpret_cast<float4*>(a.dP + o) = make_float4(dp.x * qk.x, dp.y * qk.y, dp.z * qk.z, dp.w * qk.w);
   }
 }
 
@@ -505,11 +574,21 @@ __global__ void __launch_bounds__(256) k_cb_ew1(CBwdArgs a) {
 __global__ void __launch_bounds__(256) k_cb_ew2(CBwdArgs a) {
   const int64_t item = blockIdx.x;
   if (a.tab[item / a.hv].y <= 0) return;
-  const float* G = a.G + item * kC;
-  for (int idx = threadIdx.x; idx < kC * kC; idx += 256) {
-    const int t = idx / kC, i = idx % kC;
-    const int64_t o = item * kC * kC + idx;
-    a.dT[o] = a.dA[o] * a.bt[item * kC + t] * __expf(fminf(G[t] - G[i], 0.f));
+  __shared__ float Gs[kC], Bs[kC];
+  if (threadIdx.x < kC) {
+    Gs[threadIdx.x] = a.G[item * kC + threadIdx.x];
+    Bs[threadIdx.x] = a.bt[item * kC + threadIdx.x];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kC * kC / 4; idx += 256) {
+    const int t = idx / (kC / 4), i0 = (idx % (kC / 4)) * 4;
+    const int64_t o = item * kC * kC + t * kC + i0;
+    const float4 da = *reinterpret_cast<const float4*>(a.dA + o);
+    const float dav[4] = {da.x, da.y, da.z, da.w};
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = dav[e] * Bs[t] * __expf(fminf(Gs[t] - Gs[i0 + e], 0.f));
+    *reinterpret_cast<float4*>(a.dT + o) = make_float4(r[0], r[1], r[2], r[3]);
   }
 }
 
@@ -630,22 +709,23 @@ __global__ void __launch_bounds__(256) k_cb_final(CBwdArgs a) {
   }
 }
 
-// ---- dq, dk: sums over the value heads that read each QK head ----
+// ---- dq, dk: sums over the value heads that read each QK head (four channels per thread) ----
 __global__ void __launch_bounds__(256) k_cb_group_sum(const float* __restrict__ dqh, const float* __restrict__ dkh,
                                                       int64_t T, int hk, int hv, float* __restrict__ dq,
                                                       float* __restrict__ dk) {
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;  // over T x hk x 128
-  if (idx >= T * hk * kD) return;
-  const int64_t t = idx / (int64_t(hk) * kD);
-  const int g = int((idx / kD) % hk), cc = int(idx % kD), R = hv / hk;
-  float sq = 0.f, sk = 0.f;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;  // over T x hk x 32
+  if (idx >= T * hk * (kD / 4)) return;
+  const int64_t t = idx / (int64_t(hk) * (kD / 4));
+  const int g = int((idx / (kD / 4)) % hk), c4 = int(idx % (kD / 4)) * 4, R = hv / hk;
+  float4 sq = make_float4(0.f, 0.f, 0.f, 0.f), sk = sq;
   for (int r = 0; r < R; ++r) {
-    const int64_t o = (t * hv + g * R + r) * kD + cc;
-    sq += dqh[o];
-    sk += dkh[o];
+    const int64_t o = (t * hv + g * R + r) * kD + c4;
+    const float4 a = *reinterpret_cast<const float4*>(dqh + o), b = *reinterpret_cast<const float4*>(dkh + o);
+    sq.x += a.x; sq.y += a.y; sq.z += a.z; sq.w += a.w;
+    sk.x += b.x; sk.y += b.y; sk.z += b.z; sk.w += b.w;
   }
-  dq[idx] = sq;
-  dk[idx] = sk;
+  *reinterpret_cast<float4*>(dq + 4 * idx) = sq;
+  *reinterpret_cast<float4*>(dk + 4 * idx) = sk;
 }
 
 }  // namespace
@@ -746,7 +826,7 @@ hipError_t launch_cbwd(const CBwdArgs& a, bool forward, bool backward, float* dq
     if ((e = bmm(a, a.Ki, I2, kD, 0, a.Ki, I2, kD, 1, a.KK, I1, kC, 64, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
     if ((e = bmm(a, a.Qi, I2, kD, 0, a.Ki, I2, kD, 1, a.QK, I1, kC, 64, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_cb_ap, dim3(nb), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_cb_inv, dim3(nb), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_cb_inv, dim3(nb), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_cb_prep, dim3(nb), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // U = T bV, Wk = T bgK (and Wk^T)
@@ -800,7 +880,7 @@ hipError_t launch_cbwd(const CBwdArgs& a, bool forward, bool backward, float* dq
   if ((e = bmm(a, a.dT, I1, kC, 0, a.Ki, I2, kD, 0, a.dK, I2, kD, 128, 64, 1.f, 1, 0, s)) != hipSuccess) return e;
   if ((e = bmm(a, a.dT, I1, kC, 1, a.Ki, I2, kD, 0, a.dK, I2, kD, 128, 64, 1.f, 1, 0, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_cb_final, dim3(nb), dim3(256), 0, s, a);
-  const int64_t nq = a.T * a.hk * kD;
+  const int64_t nq = a.T * a.hk * (kD / 4);
   if (nq > 0)
     hipLaunchKernelGGL(k_cb_group_sum, dim3(unsigned((nq + 255) / 256)), dim3(256), 0, s, a.dqh, a.dkh, a.T, a.hk,
                        a.hv, dq, dk);
