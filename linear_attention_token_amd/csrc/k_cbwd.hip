@@ -20,6 +20,7 @@
 // launch of a batched kernel over all (chunk, value head) items, one block per item with both operands
 // staged in LDS; the two chunk passes run one block per (sequence, value head, 16-column slice).
 #include <atomic>
+#include <initializer_list>
 
 #include "ext_internal.h"
 #include "gdn_device.h"
@@ -112,110 +113,131 @@ __global__ void __launch_bounds__(256) k_cb_gather(CBwdArgs a, int what) {
   }
 }
 
-// ---- batched product: per item, C (64 x N) = alpha op(A) op(B) (+ C), optional lower mask ----
-struct Bmm {
+// ---- batched products: per item, up to three jobs C (64 x N) = alpha op(A) op(B) (+ C) ----
+// A job with `chain` set adds its product to the previous job's instead of storing its own; the last
+// job of a chain stores the sum with the first job's C, alpha, mask and accumulate settings.
+struct MmJob {
   const float* A;
   const float* B;
   float* C;
-  int64_t sA, sB, sC;  // per-item strides (floats)
-  int N, K;            // C is 64 x N; the contraction has K terms (N, K in {64, 128})
+  float* C2;           // optional transposed copy of C, stored [N][64]
+  int64_t sA, sB, sC;  // per-item strides (floats); C2 uses sC
   int lda, ldb, ldc;   // row strides of the stored matrices
-  int ta, tb;          // op(A) = A^T (A stored [K][64]); op(B) = B^T (B stored [N][K])
   float alpha;
-  int accumulate;
+  int accumulate;      // add C's previous contents
   int mask;            // 0: none; 1: keep m >= n; 2: keep m > n
-  int tc;              // store C^T (C stored [N][64])
+  int chain;
+  int reuse_b;         // same B as the previous job: not staged again
+};
+struct MmJobs {
+  MmJob j[3];
+  int n;
 };
 
 // One block per item, four waves; wave w computes rows 16w .. 16w + 15 of C over all N columns on 16x16x4
 // fp32 MFMAs. op(B) is staged in LDS as [K][N + 4] (the four lane groups of an operand read hit distinct
-// banks); each wave reads its own rows of op(A) straight into registers. At step (p, c) lane group q
-// contributes contraction index 16p + 4q + c, so a row-major A gives each lane float4 runs.
+// banks); each wave reads its own rows of op(A) straight into registers. At step (p, c) lane group q contributes contraction index 16p + 4q + c, so a
+// row-major A gives each lane float4 runs.
 template <int N, int K, bool TA, bool TB>
-__global__ void __launch_bounds__(256) k_cb_mm(Bmm b, const int4* __restrict__ tab, int hv) {
+__global__ void __launch_bounds__(256) k_cb_mm(MmJobs jobs, const int4* __restrict__ tab, int hv) {
   constexpr int kLd = N + 4;
   extern __shared__ __attribute__((aligned(16))) float Bs[];  // [K][kLd]: Bs[k][n] = op(B)[k][n]
   const int64_t item = blockIdx.x;
   if (tab[item / hv].y <= 0) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lm = lane & 15, lg = lane >> 4;
-  const float* A = b.A + item * b.sA;
-  const float* B = b.B + item * b.sB;
   // this wave's A operands: op(A)[16w + lm][16p + 4lg + c]
-  float av[K / 16][4];
+  auto load_a = [&](const MmJob& jb, float (&av)[K / 16][4]) {
+    const float* A = jb.A + item * jb.sA;
 #pragma unroll
-  for (int p = 0; p < K / 16; ++p) {
-    if (!TA) {
-      const float4 v = *reinterpret_cast<const float4*>(A + int64_t(16 * w + lm) * b.lda + 16 * p + 4 * lg);
-      av[p][0] = v.x; av[p][1] = v.y; av[p][2] = v.z; av[p][3] = v.w;
-    } else {  // A stored [K][64]
+    for (int p = 0; p < K / 16; ++p) {
+      if (!TA) {
+        const float4 v = *reinterpret_cast<const float4*>(A + int64_t(16 * w + lm) * jb.lda + 16 * p + 4 * lg);
+        av[p][0] = v.x; av[p][1] = v.y; av[p][2] = v.z; av[p][3] = v.w;
+      } else {  // A stored [K][64]
 #pragma unroll
-      for (int c = 0; c < 4; ++c) av[p][c] = A[int64_t(16 * p + 4 * lg + c) * b.lda + 16 * w + lm];
-    }
-  }
-  if (!TB) {  // B stored [K][N]
-#pragma unroll
-    for (int r = 0; r < K * N / 1024; ++r) {
-      const int idx = tid + 256 * r, k = idx / (N / 4), n4 = (idx % (N / 4)) * 4;
-      *reinterpret_cast<float4*>(Bs + k * kLd + n4) = *reinterpret_cast<const float4*>(B + int64_t(k) * b.ldb + n4);
-    }
-  } else {  // B stored [N][K]
-#pragma unroll
-    for (int r = 0; r < K * N / 1024; ++r) {
-      const int idx = tid + 256 * r, n = idx / (K / 4), k4 = (idx % (K / 4)) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(B + int64_t(n) * b.ldb + k4);
-      Bs[(k4 + 0) * kLd + n] = v.x; Bs[(k4 + 1) * kLd + n] = v.y;
-      Bs[(k4 + 2) * kLd + n] = v.z; Bs[(k4 + 3) * kLd + n] = v.w;
-    }
-  }
-  __syncthreads();
-  f32x4 acc[N / 16];
-#pragma unroll
-  for (int j = 0; j < N / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // B operands of step p + 1 are read from LDS while step p's MFMAs run (the scheduling barriers keep
-  // the compiler from sinking the reads next to their uses)
-  float bop[2][4][N / 16];
-  auto read_b = [&](int p, float (&dst)[4][N / 16]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int j = 0; j < N / 16; ++j) dst[c][j] = Bs[(16 * p + 4 * lg + c) * kLd + 16 * j + lm];
-  };
-  read_b(0, bop[0]);
-#pragma unroll
-  for (int p = 0; p < K / 16; ++p) {
-    if (p + 1 < K / 16) read_b(p + 1, bop[(p + 1) & 1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int j = 0; j < N / 16; ++j) acc[j] = mfma16x16x4f32(av[p][c], bop[p & 1][c][j], acc[j]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  float* C = b.C + item * b.sC;
-#pragma unroll
-  for (int j = 0; j < N / 16; ++j) {
-    const int n = 16 * j + lm;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = 16 * w + 4 * lg + e;
-      v[e] = b.alpha * acc[j][e];
-      if ((b.mask == 1 && n > m) || (b.mask == 2 && n >= m)) v[e] = 0.f;
-    }
-    if (b.tc) {  // C^T stored [N][64]: the lane's four rows are contiguous
-      float4* cp = reinterpret_cast<float4*>(C + int64_t(n) * b.ldc + 16 * w + 4 * lg);
-      float4 o = make_float4(v[0], v[1], v[2], v[3]);
-      if (b.accumulate) {
-        const float4 q = *cp;
-        o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+        for (int c = 0; c < 4; ++c) av[p][c] = A[int64_t(16 * p + 4 * lg + c) * jb.lda + 16 * w + lm];
       }
-      *cp = o;
-    } else {
+    }
+  };
+  auto stage_b = [&](const MmJob& jb) {
+    const float* B = jb.B + item * jb.sB;
+    if (!TB) {  // B stored [K][N]
+#pragma unroll
+      for (int r = 0; r < K * N / 1024; ++r) {
+        const int idx = tid + 256 * r, k = idx / (N / 4), n4 = (idx % (N / 4)) * 4;
+        *reinterpret_cast<float4*>(Bs + k * kLd + n4) = *reinterpret_cast<const float4*>(B + int64_t(k) * jb.ldb + n4);
+      }
+    } else {  // B stored [N][K]: a wave reads 64 contiguous bytes of each of 16 rows n, and its transposed
+              // LDS writes (rows k, 16 consecutive n per row) hit distinct banks
+#pragma unroll
+      for (int r = 0; r < K * N / 1024; ++r) {
+        const int f = tid + 256 * r, rest = f >> 6;
+        const int n = 16 * (rest % (N / 16)) + (f & 15), k4 = 16 * (rest / (N / 16)) + 4 * ((f >> 4) & 3);
+        const float4 v = *reinterpret_cast<const float4*>(B + int64_t(n) * jb.ldb + k4);
+        Bs[(k4 + 0) * kLd + n] = v.x; Bs[(k4 + 1) * kLd + n] = v.y;
+        Bs[(k4 + 2) * kLd + n] = v.z; Bs[(k4 + 3) * kLd + n] = v.w;
+      }
+    }
+  };
+  f32x4 acc[N / 16];
+  int head = 0;  // first job of the current chain
+#pragma unroll 1
+  for (int jj = 0; jj < jobs.n; ++jj) {
+    const MmJob& jb = jobs.j[jj];
+    float av[K / 16][4];
+    load_a(jb, av);  // in flight with the B staging
+    if (!jb.reuse_b) {
+      if (jj > 0) __syncthreads();  // every wave is done with the previous B
+      stage_b(jb);
+      __syncthreads();
+    }
+    if (!jb.chain) {
+      head = jj;
+#pragma unroll
+      for (int j = 0; j < N / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // B operands of step p + 1 are read from LDS while step p's MFMAs run (the scheduling barriers keep
+    // the compiler from sinking the reads next to their uses)
+    float bop[2][4][N / 16];
+    auto read_b = [&](int p, float (&dst)[4][N / 16]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < N / 16; ++j) dst[c][j] = Bs[(16 * p + 4 * lg + c) * kLd + 16 * j + lm];
+    };
+    read_b(0, bop[0]);
+#pragma unroll
+    for (int p = 0; p < K / 16; ++p) {
+      if (p + 1 < K / 16) read_b(p + 1, bop[(p + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < N / 16; ++j) acc[j] = mfma16x16x4f32(av[p][c], bop[p & 1][c][j], acc[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (jj + 1 < jobs.n && jobs.j[jj + 1].chain) continue;
+    // store the chain's sum with its first job's settings
+    const MmJob& hb = jobs.j[head];
+    float* C = hb.C + item * hb.sC;
+    float* C2 = hb.C2 ? hb.C2 + item * hb.sC : nullptr;
+#pragma unroll
+    for (int j = 0; j < N / 16; ++j) {
+      const int n = 16 * j + lm;
+      float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float* cp = C + int64_t(16 * w + 4 * lg + e) * b.ldc + n;
-        *cp = b.accumulate ? *cp + v[e] : v[e];
+        const int m = 16 * w + 4 * lg + e;
+        v[e] = hb.alpha * acc[j][e];
+        if ((hb.mask == 1 && n > m) || (hb.mask == 2 && n >= m)) v[e] = 0.f;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float* cp = C + int64_t(16 * w + 4 * lg + e) * hb.ldc + n;
+        *cp = hb.accumulate ? *cp + v[e] : v[e];
+      }
+      if (C2)  // [N][64]: the lane's four rows are contiguous
+        *reinterpret_cast<float4*>(C2 + int64_t(n) * kC + 16 * w + 4 * lg) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -393,14 +415,14 @@ __device__ __forceinline__ void pass_step(const CBwdArgs& a, int64_t item, const
   // A2^T operands, and (backward) H (in the dS slot, about to be overwritten by X) and S of this chunk:
   // first used after the first products, so their loads overlap those (the operands of the first
   // products were loaded a step ahead)
-  float4 a2[2][4];  // A2^T rows 32w + 16i + l % 16, columns 4 (l / 16 + 4p) ..
+  f32x4 a2[8];  // A2^T rows 32w + 16i + l % 16, columns 4 (l / 16 + 4p) .. (piece 4i + p)
   {
     const float* A2T = (kBwd ? a.WkT : a.KtT) + item * kD * kC;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        a2[i][p] = *reinterpret_cast<const float4*>(A2T + (32 * w + 16 * i + lm) * kC + 4 * (lg + 4 * p));
+        a2[4 * i + p] = *reinterpret_cast<const f32x4*>(A2T + (32 * w + 16 * i + lm) * kC + 4 * (lg + 4 * p));
   }
   float hv[2][4], sv[2][4];
   if (kBwd) {
@@ -471,8 +493,7 @@ __device__ __forceinline__ void pass_step(const CBwdArgs& a, int64_t item, const
     for (int e = 0; e < 4; ++e) acc[i][e] = gc * X[i][e];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const float av0[4] = {a2[0][p].x, a2[0][p].y, a2[0][p].z, a2[0][p].w};
-    const float av1[4] = {a2[1][p].x, a2[1][p].y, a2[1][p].z, a2[1][p].w};
+    const f32x4 av0 = a2[p], av1 = a2[4 + p];
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       acc[0] = mfma16x16x4f32(s2 * av0[cc], zb[p][cc], acc[0]);
@@ -770,7 +791,7 @@ void cbwd_plan(CBwdArgs& a, void* base) {
 
 namespace {
 template <int N, int K, bool TA, bool TB>
-hipError_t mm_launch(const Bmm& b, const CBwdArgs& a, hipStream_t s) {
+hipError_t mm_launch(const MmJobs& jobs, const CBwdArgs& a, hipStream_t s) {
   const void* f = reinterpret_cast<const void*>(k_cb_mm<N, K, TA, TB>);
   const int smem = int(sizeof(float) * K * (N + 4));
   int dev = 0;
@@ -783,30 +804,43 @@ hipError_t mm_launch(const Bmm& b, const CBwdArgs& a, hipStream_t s) {
     if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, smem)) != hipSuccess) return e;
     raised.fetch_or(bit);
   }
-  hipLaunchKernelGGL((k_cb_mm<N, K, TA, TB>), dim3(unsigned(a.nc_max * a.hv)), dim3(256), size_t(smem), s, b, a.tab,
-                     a.hv);
+  hipLaunchKernelGGL((k_cb_mm<N, K, TA, TB>), dim3(unsigned(a.nc_max * a.hv)), dim3(256), size_t(smem), s, jobs,
+                     a.tab, a.hv);
   return hipGetLastError();
 }
 
-// C (64 x N) = alpha op(A) op(B) (+ C) per item, op(A) 64 x K, op(B) K x N
-hipError_t bmm(const CBwdArgs& a, const float* A, int64_t sA, int lda, int ta, const float* B, int64_t sB, int ldb,
-               int tb, float* C, int64_t sC, int ldc, int N, int K, float alpha, int accumulate, int mask,
-               hipStream_t s, int tc = 0) {
-  const Bmm b{A, B, C, sA, sB, sC, N, K, lda, ldb, ldc, ta, tb, alpha, accumulate, mask, tc};
-  const int key = (N == 128) * 8 + (K == 128) * 4 + (ta != 0) * 2 + (tb != 0);
+// One product job: C (64 x N) = alpha op(A) op(B) (+ C), op(A) 64 x K, op(B) K x N.
+MmJob job(const float* A, int64_t sA, int lda, const float* B, int64_t sB, int ldb, float* C, int64_t sC, int ldc,
+          float alpha = 1.f, int accumulate = 0, int mask = 0) {
+  return MmJob{A, B, C, nullptr, sA, sB, sC, lda, ldb, ldc, alpha, accumulate, mask, 0, 0};
+}
+MmJob chained(MmJob j) {
+  j.chain = 1;
+  return j;
+}
+
+// Launches up to three jobs that share N, K and the transposition of A and B as one batched product.
+hipError_t mm(const CBwdArgs& a, int N, int K, bool ta, bool tb, std::initializer_list<MmJob> list, hipStream_t s) {
+  MmJobs jobs{};
+  for (const MmJob& jb : list) {
+    if (jobs.n == 3) return hipErrorInvalidValue;
+    jobs.j[jobs.n] = jb;
+    if (jobs.n > 0) {
+      const MmJob& pr = jobs.j[jobs.n - 1];
+      jobs.j[jobs.n].reuse_b = jb.B == pr.B && jb.sB == pr.sB && jb.ldb == pr.ldb;
+    }
+    ++jobs.n;
+  }
+  const int key = (N == 128) * 8 + (K == 128) * 4 + ta * 2 + tb;
   switch (key) {
-    case 0: return mm_launch<64, 64, false, false>(b, a, s);
-    case 1: return mm_launch<64, 64, false, true>(b, a, s);
-    case 2: return mm_launch<64, 64, true, false>(b, a, s);
-    case 3: return mm_launch<64, 64, true, true>(b, a, s);
-    case 4: return mm_launch<64, 128, false, false>(b, a, s);
-    case 5: return mm_launch<64, 128, false, true>(b, a, s);
-    case 8: return mm_launch<128, 64, false, false>(b, a, s);
-    case 9: return mm_launch<128, 64, false, true>(b, a, s);
-    case 10: return mm_launch<128, 64, true, false>(b, a, s);
-    case 12: return mm_launch<128, 128, false, false>(b, a, s);
-    case 13: return mm_launch<128, 128, false, true>(b, a, s);
-    default: return hipErrorInvalidValue;  // K = 128 with op(A) = A^T needs a 128-row A: not used
+    case 1: return mm_launch<64, 64, false, true>(jobs, a, s);
+    case 2: return mm_launch<64, 64, true, false>(jobs, a, s);
+    case 5: return mm_launch<64, 128, false, true>(jobs, a, s);
+    case 8: return mm_launch<128, 64, false, false>(jobs, a, s);
+    case 10: return mm_launch<128, 64, true, false>(jobs, a, s);
+    case 12: return mm_launch<128, 128, false, false>(jobs, a, s);
+    case 13: return mm_launch<128, 128, false, true>(jobs, a, s);
+    default: return hipErrorInvalidValue;  // shapes the backward does not use
   }
 }
 }  // namespace
@@ -823,22 +857,26 @@ hipError_t launch_cbwd(const CBwdArgs& a, bool forward, bool backward, float* dq
     hipLaunchKernelGGL(k_cb_gather, dim3(nb), dim3(256), 0, s, a, 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // KK = K K^T, QK = Q K^T
-    if ((e = bmm(a, a.Ki, I2, kD, 0, a.Ki, I2, kD, 1, a.KK, I1, kC, 64, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
-    if ((e = bmm(a, a.Qi, I2, kD, 0, a.Ki, I2, kD, 1, a.QK, I1, kC, 64, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
+    if ((e = mm(a, 64, 128, false, true, {job(a.Ki, I2, kD, a.Ki, I2, kD, a.KK, I1, kC),
+                                          job(a.Qi, I2, kD, a.Ki, I2, kD, a.QK, I1, kC)}, s)) != hipSuccess)
+      return e;
     hipLaunchKernelGGL(k_cb_ap, dim3(nb), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_cb_inv, dim3(nb), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_cb_prep, dim3(nb), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // U = T bV, Wk = T bgK (and Wk^T)
-    if ((e = bmm(a, a.Tm, I1, kC, 0, a.bV, I2, kD, 0, a.U, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
-    if ((e = bmm(a, a.Tm, I1, kC, 0, a.bgK, I2, kD, 0, a.Wk, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
-    if ((e = bmm(a, a.Tm, I1, kC, 0, a.bgK, I2, kD, 0, a.WkT, I2, kC, 128, 64, 1.f, 0, 0, s, 1)) != hipSuccess)
-      return e;
+    {
+      MmJob wk = job(a.Tm, I1, kC, a.bgK, I2, kD, a.Wk, I2, kD);
+      wk.C2 = a.WkT;
+      if ((e = mm(a, 128, 64, false, false, {job(a.Tm, I1, kC, a.bV, I2, kD, a.U, I2, kD), wk}, s)) != hipSuccess)
+        return e;
+    }
     hipLaunchKernelGGL(k_cb_pass<false>, dim3(chains), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.y) {  // y = scale (gQ S + P W), through X
-      if ((e = bmm(a, a.gQ, I2, kD, 0, a.S, I3, kD, 0, a.X, I2, kD, 128, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
-      if ((e = bmm(a, a.Pm, I1, kC, 0, a.W, I2, kD, 0, a.X, I2, kD, 128, 64, 1.f, 1, 0, s)) != hipSuccess) return e;
+      if ((e = mm(a, 128, 128, false, false, {job(a.gQ, I2, kD, a.S, I3, kD, a.X, I2, kD)}, s)) != hipSuccess) return e;
+      if ((e = mm(a, 128, 64, false, false, {job(a.Pm, I1, kC, a.W, I2, kD, a.X, I2, kD, 1.f, 1)}, s)) != hipSuccess)
+        return e;
       hipLaunchKernelGGL(k_cb_scatter_y, dim3(nb), dim3(256), 0, s, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -848,37 +886,41 @@ hipError_t launch_cbwd(const CBwdArgs& a, bool forward, bool backward, float* dq
   hipLaunchKernelGGL(k_cb_gather, dim3(nb), dim3(256), 0, s, a, 2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the backward pass's addends: dW <- P^T dY; dS <- gQ^T dY (128 x 128, as two 64-row halves)
-  if ((e = bmm(a, a.Pm, I1, kC, 1, a.dYi, I2, kD, 0, a.dW, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
-  for (int half = 0; half < 2; ++half)
-    if ((e = bmm(a, a.gQ + 64 * half, I2, kD, 1, a.dYi, I2, kD, 0, a.dS + 64 * half * kD, I3, kD, 128, 64, 1.f, 0,
-                 0, s)) != hipSuccess)
-      return e;
+  if ((e = mm(a, 128, 64, true, false, {job(a.Pm, I1, kC, a.dYi, I2, kD, a.dW, I2, kD),
+                                        job(a.gQ, I2, kD, a.dYi, I2, kD, a.dS, I3, kD),
+                                        job(a.gQ + 64, I2, kD, a.dYi, I2, kD, a.dS + 64 * kD, I3, kD)}, s)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL(k_cb_pass<true>, dim3(chains), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // dK~ = W dS'^T; X = dY S^T; dWk = -dW S^T; dP = lower(dY W^T)
-  if ((e = bmm(a, a.W, I2, kD, 0, a.dS, I3, kD, 1, a.dKt, I2, kD, 128, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
-  if ((e = bmm(a, a.dYi, I2, kD, 0, a.S, I3, kD, 1, a.X, I2, kD, 128, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
-  if ((e = bmm(a, a.dW, I2, kD, 0, a.S, I3, kD, 1, a.dWk, I2, kD, 128, 128, -1.f, 0, 0, s)) != hipSuccess) return e;
-  if ((e = bmm(a, a.dYi, I2, kD, 0, a.W, I2, kD, 1, a.dP, I1, kC, 64, 128, 1.f, 0, 1, s)) != hipSuccess) return e;
+  // X = dY S^T; dWk = -dW S^T; dK~ = W dS'^T
+  if ((e = mm(a, 128, 128, false, true, {job(a.dYi, I2, kD, a.S, I3, kD, a.X, I2, kD),
+                                         job(a.dW, I2, kD, a.S, I3, kD, a.dWk, I2, kD, -1.f),
+                                         job(a.W, I2, kD, a.dS, I3, kD, a.dKt, I2, kD)}, s)) != hipSuccess)
+    return e;
+  // dP = lower(dY W^T); dT = dW bV^T + dWk bgK^T
+  if ((e = mm(a, 64, 128, false, true, {job(a.dYi, I2, kD, a.W, I2, kD, a.dP, I1, kC, 1.f, 0, 1),
+                                        job(a.dW, I2, kD, a.bV, I2, kD, a.dT, I1, kC),
+                                        chained(job(a.dWk, I2, kD, a.bgK, I2, kD, nullptr, 0, 0))}, s)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL(k_cb_ew1, dim3(nb), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // dQ = dQK K; dK = dQK^T Q
-  if ((e = bmm(a, a.M1, I1, kC, 0, a.Ki, I2, kD, 0, a.dQ, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
-  if ((e = bmm(a, a.M1, I1, kC, 1, a.Qi, I2, kD, 0, a.dK, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
-  // dT = dW bV^T + dWk bgK^T
-  if ((e = bmm(a, a.dW, I2, kD, 0, a.bV, I2, kD, 1, a.dT, I1, kC, 64, 128, 1.f, 0, 0, s)) != hipSuccess) return e;
-  if ((e = bmm(a, a.dWk, I2, kD, 0, a.bgK, I2, kD, 1, a.dT, I1, kC, 64, 128, 1.f, 1, 0, s)) != hipSuccess) return e;
-  // d(bV) = T^T dW; d(bgK) = T^T dWk
-  if ((e = bmm(a, a.Tm, I1, kC, 1, a.dW, I2, kD, 0, a.dbV, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
-  if ((e = bmm(a, a.Tm, I1, kC, 1, a.dWk, I2, kD, 0, a.dbgK, I2, kD, 128, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
+  // dQ = dQK K; dK = dQK^T Q; d(bV) = T^T dW; d(bgK) = T^T dWk
+  if ((e = mm(a, 128, 64, false, false, {job(a.M1, I1, kC, a.Ki, I2, kD, a.dQ, I2, kD)}, s)) != hipSuccess) return e;
+  if ((e = mm(a, 128, 64, true, false, {job(a.M1, I1, kC, a.Qi, I2, kD, a.dK, I2, kD),
+                                        job(a.Tm, I1, kC, a.dW, I2, kD, a.dbV, I2, kD),
+                                        job(a.Tm, I1, kC, a.dWk, I2, kD, a.dbgK, I2, kD)}, s)) != hipSuccess)
+    return e;
   // dA = -strict_lower(T^T (dT T^T))
-  if ((e = bmm(a, a.dT, I1, kC, 0, a.Tm, I1, kC, 1, a.M1, I1, kC, 64, 64, 1.f, 0, 0, s)) != hipSuccess) return e;
-  if ((e = bmm(a, a.Tm, I1, kC, 1, a.M1, I1, kC, 0, a.dA, I1, kC, 64, 64, -1.f, 0, 2, s)) != hipSuccess) return e;
+  if ((e = mm(a, 64, 64, false, true, {job(a.dT, I1, kC, a.Tm, I1, kC, a.M1, I1, kC)}, s)) != hipSuccess) return e;
+  if ((e = mm(a, 64, 64, true, false, {job(a.Tm, I1, kC, a.M1, I1, kC, a.dA, I1, kC, -1.f, 0, 2)}, s)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL(k_cb_ew2, dim3(nb), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // dK += dAKK K + dAKK^T K
-  if ((e = bmm(a, a.dT, I1, kC, 0, a.Ki, I2, kD, 0, a.dK, I2, kD, 128, 64, 1.f, 1, 0, s)) != hipSuccess) return e;
-  if ((e = bmm(a, a.dT, I1, kC, 1, a.Ki, I2, kD, 0, a.dK, I2, kD, 128, 64, 1.f, 1, 0, s)) != hipSuccess) return e;
+  if ((e = mm(a, 128, 64, false, false, {job(a.dT, I1, kC, a.Ki, I2, kD, a.dK, I2, kD, 1.f, 1)}, s)) != hipSuccess)
+    return e;
+  if ((e = mm(a, 128, 64, true, false, {job(a.dT, I1, kC, a.Ki, I2, kD, a.dK, I2, kD, 1.f, 1)}, s)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL(k_cb_final, dim3(nb), dim3(256), 0, s, a);
   const int64_t nq = a.T * a.hk * (kD / 4);
   if (nq > 0)
