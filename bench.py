@@ -286,7 +286,8 @@ def cpu_baseline(prefill_tokens: int, decode_batch: int):
                 decode_us_per_step=round(dd * 1e6, 1),
                 sample=f"fp64 numpy oracle (conv + SiLU + L2 + per-token recurrence + RMSNorm + gate) over a pool of "
                        f"{workers} single-thread processes: prefill of the first {prefill_tokens} tokens of the "
-                       f"one-layer workload (B=1, all 48 value heads) in {dt:.1f} s wall, scaled to tokens/s; one "
+                       f"one-layer workload (B=1, all 48 value heads; 4096 is all of it) in {dt:.1f} s wall, "
+                       f"scaled to tokens/s; one "
                        f"decode step at B={decode_batch} (all {decode_batch * HV} chains, one token each) in "
                        f"{dd:.1f} s wall")
 
@@ -459,7 +460,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the reference timing of one captured HIP graph replayed per step")
-    ap.add_argument("--cpu-tokens", type=int, default=1024, help="tokens of the oracle's prefill sample")
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens of the oracle's prefill (4096: the whole one-layer workload)")
     ap.add_argument("--long-tokens", type=int, default=262144, help="tokens of the long prefill workload")
     ap.add_argument("--long-reps", type=int, default=10, help="timed calls of the long and varlen workloads")
     ap.add_argument("--no-configs", action="store_true", help="skip the tiny, long and varlen prefill workloads")

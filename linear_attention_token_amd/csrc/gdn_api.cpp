@@ -556,7 +556,10 @@ static gdn_status check_bwd(const gdn_cfg* cfg, int32_t n_seqs, int64_t T, Probl
   if (n_seqs < 0 || T < 0) return fail(GDN_E_SHAPE, "negative n_seqs or total_tokens");
   if (n_seqs == 0 && T != 0) return fail(GDN_E_SHAPE, "tokens without sequences");
   if (T >= (int64_t(1) << 31)) return fail(GDN_E_UNSUPPORTED, "total_tokens must stay below 2^31");
-  if (int64_t(n_seqs) * p.hv > int64_t(INT32_MAX)) return fail(GDN_E_UNSUPPORTED, "too many (sequence, head) chains");
+  // launch bounds: 8 blocks per (sequence, value head) chain, one block per (chunk, value head) item
+  if (int64_t(n_seqs) * p.hv > (int64_t(1) << 27)) return fail(GDN_E_UNSUPPORTED, "too many (sequence, head) chains");
+  if ((T / 64 + n_seqs) * int64_t(p.hv) >= (int64_t(1) << 31))
+    return fail(GDN_E_UNSUPPORTED, "too many (64-token chunk, value head) items");
   return GDN_OK;
 }
 

@@ -521,7 +521,11 @@ template <bool kBwd>
 __global__ void __launch_bounds__(256, 2) k_cb_pass(CBwdArgs a) {
   __shared__ float Xs[kD * kXLd];
   __shared__ float Zs[kC * kXLd];
-  const int chain = blockIdx.x / kSlices, sl = blockIdx.x % kSlices;
+  // the 8 slices of a chain read the same chunk operands: numbered to run on one XCD, so those come from
+  // HBM once and from that XCD's L2 for the others
+  int chain, sl;
+  xcd_item(int(blockIdx.x), kSlices, chain, sl);
+  if (chain >= a.n_seqs * a.hv) return;
   const int n = chain / a.hv, h = chain % a.hv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lm = lane & 15, lg = lane >> 4;
   const int col = kSl * sl + lm;
@@ -848,7 +852,7 @@ hipError_t mm(const CBwdArgs& a, int N, int K, bool ta, bool tb, std::initialize
 hipError_t launch_cbwd(const CBwdArgs& a, bool forward, bool backward, float* dq, float* dk, hipStream_t s) {
   hipError_t e = hipSuccess;
   const int64_t items = a.nc_max * a.hv;
-  const unsigned nb = unsigned(items), chains = unsigned(int64_t(a.n_seqs) * a.hv * kSlices);
+  const unsigned nb = unsigned(items), chains = unsigned(xcd_blocks(int64_t(a.n_seqs) * a.hv, kSlices));
   const int64_t I2 = kC * kD, I1 = kC * kC, I3 = kD * kD;
   if (forward) {
     hipLaunchKernelGGL(k_cb_offsets, dim3(1), dim3(64), 0, s, a.cu, a.n_seqs, a.T, a.nc_max, a.seq_off);
