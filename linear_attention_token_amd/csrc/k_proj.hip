@@ -16,13 +16,16 @@
 // rounded to bf16 first). Weights are in the linear-layer layout [out features][in features],
 // row-major, so both operands are K-contiguous rows.
 //
-// Kernel: a block computes a 256 (or 128, for narrow outputs) out features x 256 tokens tile with four
-// waves (one per SIMD) of 128 (64) x 128 on 32x32x16 bf16 MFMA (out features as the A operand, tokens as the B operand; each lane
+// Kernel: a block computes an FT out features x TT tokens tile (256 x 256; 320 x 128 or 128 x 256 when
+// those fill the chip's rounds better) with four waves (one per SIMD) of FT / 2 x TT / 2 on 32x32x16 bf16
+// MFMA (out features as the A operand, tokens as the B operand; each lane
 // ends with runs of 4 consecutive output features of one token; the tile is staged in LDS and stored
 // as 16-byte pieces of token rows). K advances in steps of 32 through a
 // five-slot LDS ring filled by direct global->LDS loads three steps ahead. Blocks are numbered so that
 // the 32 blocks an XCD runs at once form a 4 x 8 group of tiles that share their operand panels in
 // that XCD's L2.
+#include <atomic>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -30,26 +33,26 @@ namespace gdn {
 
 namespace {
 
-constexpr int kTok = 256;                // tokens per block
 constexpr int kKStep = 32;               // k per ring slot
 constexpr int kRingG = 5;                // ring slots
 constexpr int kAhead = kRingG - 2;       // k-steps loaded ahead of the one being multiplied
 constexpr int kGroupM = 8, kGroupT = 4;  // tiles of a block group: 8 feature tiles x 4 token tiles
 constexpr int kMaxGateHeads = 3072;      // value heads the epilogue's LDS holds gate vectors for
 
-// Per feature-tile width FT (256, or 128 when there are too few 256-wide tiles to fill the chip):
-template <int FT> struct Geo {
+// Per tile shape: FT output features x TT tokens (each a multiple of 64), four waves of FT / 2 x TT / 2:
+template <int FT, int TT> struct Geo {
   static constexpr int kPanelW = FT * kKStep * 2;                  // W panel bytes per slot
-  static constexpr int kPanelX = kTok * kKStep * 2;                // x panel bytes per slot
+  static constexpr int kPanelX = TT * kKStep * 2;                  // x panel bytes per slot
   static constexpr int kSlot = kPanelW + kPanelX;
-  static constexpr int kWLoads = FT / 64, kLoads = FT / 64 + 4;    // 1 KB loads per wave and slot
+  static constexpr int kWLoads = FT / 64, kLoads = FT / 64 + TT / 64;  // 1 KB loads per wave and slot
   static constexpr int kMI = FT / 64;                              // 32-row feature tiles per wave
+  static constexpr int kNJ = TT / 64;                              // 32-token tiles per wave
   static constexpr int kCLd = FT + 8;                              // bytes per token row of a wave's staged tile
-  static constexpr int kGateParams = 4 * 128 * kCLd;               // exp(a_log), dt_bias in the epilogue
+  static constexpr int kGateParams = 4 * (TT / 2) * kCLd;          // exp(a_log), dt_bias in the epilogue
   static constexpr size_t kSmem = size_t(kRingG) * kSlot;
   static_assert(kSmem <= 160 * 1024, "LDS budget");
   static_assert(size_t(kGateParams) + 8 * kMaxGateHeads <= kSmem, "gate vectors fit beside the staged tiles");
-  static_assert(128 * kCLd >= 32 * 132 * 4, "a wave's staging area holds a 32-token fp32 gate tile");
+  static_assert((TT / 2) * kCLd >= 32 * 132 * 4, "a wave's staging area holds a 32-token fp32 gate tile");
 };
 
 // Rows of a panel are 64 bytes (four 16-byte pieces of k); piece p of row r sits at slot
@@ -80,9 +83,9 @@ __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& a, int64_t
   return a.w[2] + (n - a.seg_end[1]) * a.K;
 }
 
-template <int FT>
+template <int FT, int TT>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
-  using G = Geo<FT>;
+  using G = Geo<FT, TT>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // block -> tile: XCD x runs blocks b = 8 j + x; the 32 consecutive j of one XCD form one group
   const int b = int(blockIdx.x), x = b & 7, j = b >> 3;
@@ -91,20 +94,21 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   const int tmr = (grp % n_gm) * kGroupM + in % kGroupM, tt = (grp / n_gm) * kGroupT + in / kGroupM;
   if (tmr >= a.n_tiles_m || tt >= a.n_tiles_t) return;
   const int tm = a.n_tiles_m - 1 - tmr;  // the last feature tiles (the gate columns) go first
-  const int64_t n0 = int64_t(tm) * FT, t0 = int64_t(tt) * kTok;
+  const int64_t n0 = int64_t(tm) * FT, t0 = int64_t(tt) * TT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w & 1, wt = w >> 1;  // this wave's quarter: features (FT / 2) wm .., tokens 128 wt ..
+  const int wm = w & 1, wt = w >> 1;  // this wave's quarter: features (FT / 2) wm .., tokens (TT / 2) wt ..
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const int nks = a.K / kKStep;
 
   // This wave's direct loads of one slot: W load i < kWLoads covers W panel rows 16 (kWLoads w + i) ..
-  // + 15, x load i covers x panel rows 16 (4w + i) .. + 15; lane l takes row 16 (.) + l / 4, slot l % 4.
+  // + 15, x load i covers x panel rows 16 (TT / 64 w + i) .. + 15; lane l takes row 16 (.) + l / 4,
+  // slot l % 4.
   const uint16_t* src[G::kLoads];
   uint32_t dst[G::kLoads];
 #pragma unroll
   for (int i = 0; i < G::kLoads; ++i) {
     const bool wl = i < G::kWLoads;
-    const int blk = wl ? G::kWLoads * w + i : 4 * w + (i - G::kWLoads);
+    const int blk = wl ? G::kWLoads * w + i : G::kNJ * w + (i - G::kWLoads);
     const int r = 16 * blk + (lane >> 2), piece = (lane & 3) ^ pkey(r);
     src[i] = (wl ? weight_row(a, n0 + r) : a.x + min(t0 + r, a.T - 1) * a.ld_x) + 8 * piece;
     dst[i] = (wl ? 0 : G::kPanelW) + blk * 1024;
@@ -118,11 +122,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 
   // acc[i][jt]: 32 x 32 tile, element e: feature 8 (e / 4) + 4 hq + e % 4, token l32 (within tiles i, jt)
   const int l32 = lane & 31, hq = lane >> 5;
-  f32x16 acc[G::kMI][4];
+  f32x16 acc[G::kMI][G::kNJ];
 #pragma unroll
   for (int i = 0; i < G::kMI; ++i)
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+    for (int jt = 0; jt < G::kNJ; ++jt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][jt][e] = 0.f;
 
@@ -140,21 +144,21 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     const unsigned char* sb = smem + size_t(ks % kRingG) * G::kSlot;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {  // two k-substeps of 16: pieces 2u + hq of the 64-byte rows
-      short8 af[G::kMI], bf[4];
+      short8 af[G::kMI], bf[G::kNJ];
 #pragma unroll
       for (int i = 0; i < G::kMI; ++i) {
         const int r = (FT / 2) * wm + 32 * i + l32;
         af[i] = *reinterpret_cast<const short8*>(sb + r * 64 + (((2 * u + hq) ^ pkey(r)) << 4));
       }
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int r = 128 * wt + 32 * jt + l32;
+      for (int jt = 0; jt < G::kNJ; ++jt) {
+        const int r = (TT / 2) * wt + 32 * jt + l32;
         bf[jt] = *reinterpret_cast<const short8*>(sb + G::kPanelW + r * 64 + (((2 * u + hq) ^ pkey(r)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < G::kMI; ++i)
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) acc[i][jt] = mfma32x32x16(af[i], bf[jt], acc[i][jt]);
+        for (int jt = 0; jt < G::kNJ; ++jt) acc[i][jt] = mfma32x32x16(af[i], bf[jt], acc[i][jt]);
     }
     // the next step has landed (later steps may stay in flight)
     settle(min(ks + kAhead, nks - 1) - (ks + 1));
@@ -164,11 +168,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   // ---- epilogue. The bf16 outputs go through this wave's tile in LDS (the ring is free after the
   // last barrier) and leave as 16-byte pieces of token rows; the gate columns are finished from the
   // fp32 registers. ----
-  unsigned char* const cs = smem + size_t(w) * 128 * G::kCLd;
+  unsigned char* const cs = smem + size_t(w) * (TT / 2) * G::kCLd;
 #pragma unroll
   for (int i = 0; i < G::kMI; ++i)
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+    for (int jt = 0; jt < G::kNJ; ++jt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {  // features 32i + 8g + 4hq .. +3 of token 32jt + l32
         const f32x16& v = acc[i][jt];
@@ -178,9 +182,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   const int64_t nw = n0 + (FT / 2) * wm;  // first feature of this wave's tile
   constexpr int kRowPieces = FT / 16;      // 16-byte pieces per staged token row (FT / 2 features)
 #pragma unroll 4
-  for (int k = 0; k < 2 * kRowPieces; ++k) {
+  for (int k = 0; k < (TT / 2) * kRowPieces / 64; ++k) {
     const int pc = lane + 64 * k, tl = pc / kRowPieces, seg8 = pc % kRowPieces;
-    const int64_t t = t0 + 128 * wt + tl, n = nw + 8 * seg8;
+    const int64_t t = t0 + (TT / 2) * wt + tl, n = nw + 8 * seg8;
     if (t >= a.T || n >= a.seg_end[1]) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(cs + tl * G::kCLd + seg8 * 16);
     if (n < a.seg_end[0]) *reinterpret_cast<uint4*>(a.out[0] + t * a.ld_out[0] + n) = v;
@@ -199,7 +203,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   const int c_lo = int(max<int64_t>(a.seg_end[1] - nw, 0)), c_hi = int(min<int64_t>(a.seg_end[2] - nw, FT / 2));
   const int nc = c_hi - c_lo;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
+  for (int jt = 0; jt < G::kNJ; ++jt) {
 #pragma unroll
     for (int i = 0; i < G::kMI; ++i)
 #pragma unroll
@@ -210,7 +214,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
       }
     for (int e = lane; e < 32 * nc; e += 64) {
       const int tl = e / nc, c = c_lo + (e - tl * nc);
-      const int64_t t = t0 + 128 * wt + 32 * jt + tl;
+      const int64_t t = t0 + (TT / 2) * wt + 32 * jt + tl;
       if (t >= a.T) continue;
       const int col = int(nw + c - a.seg_end[1]);
       const float v = fs[tl * 132 + c];
@@ -225,35 +229,43 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   }
 }
 
-bool g_smem_ok[2][64] = {};  // devices on which each kernel's LDS limit was raised (idempotent call)
-
-template <int FT>
-hipError_t launch_ft(GemmArgs& a, hipStream_t s) {
+template <int FT, int TT>
+hipError_t launch_tiles(GemmArgs& a, hipStream_t s) {
+  using G = Geo<FT, TT>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  bool& ok = g_smem_ok[FT == 256][dev & 63];
-  if (!ok) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm<FT>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            int(Geo<FT>::kSmem));
+  // this instance's LDS limit is raised once per device (an idempotent call, so a race only repeats it)
+  static std::atomic<uint64_t> raised{0};
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (!(raised.load() & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm<FT, TT>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            int(G::kSmem));
     if (e != hipSuccess) return e;
-    ok = true;
+    raised.fetch_or(bit);
   }
   a.n_tiles_m = int((a.seg_end[2] + FT - 1) / FT);
-  a.n_tiles_t = int((a.T + kTok - 1) / kTok);
+  a.n_tiles_t = int((a.T + TT - 1) / TT);
   const int n_gm = (a.n_tiles_m + kGroupM - 1) / kGroupM, n_gt = (a.n_tiles_t + kGroupT - 1) / kGroupT;
   const int64_t groups = int64_t(n_gm) * n_gt;
   const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * kGroupT;  // every XCD walks whole groups
-  hipLaunchKernelGGL(k_gemm<FT>, dim3(unsigned(blocks)), dim3(256), Geo<FT>::kSmem, s, a);
+  hipLaunchKernelGGL((k_gemm<FT, TT>), dim3(unsigned(blocks)), dim3(256), G::kSmem, s, a);
   return hipGetLastError();
 }
 
-// 256-wide feature tiles unless there are too few of them to occupy a quarter of the chip's 256 CUs
-// (measured: at 160 tiles of 256 the wider tile is still faster than 320 of 128)
+// Tile shape by the number of tiles, one block per CU: 256 x 256 tiles, unless they fill less than one
+// round of the chip's 256 CUs; then 320 x 128, or 128 x 256 when there are too few 256-wide tiles to
+// occupy a quarter of the chip.
 hipError_t launch_gemm(GemmArgs& a, hipStream_t s) {
   if (a.T == 0 || a.seg_end[2] == 0) return hipSuccess;
-  const int64_t tiles256 = ((a.seg_end[2] + 255) / 256) * ((a.T + kTok - 1) / kTok);
-  return tiles256 >= 64 ? launch_ft<256>(a, s) : launch_ft<128>(a, s);
+  auto tiles = [&](int ft, int tt) { return ((a.seg_end[2] + ft - 1) / ft) * ((a.T + tt - 1) / tt); };
+  const int64_t t256 = tiles(256, 256);
+  if (t256 < 64) return launch_tiles<128, 256>(a, s);
+  // under one round of 256 x 256 tiles, 320 x 128 tiles (5/8 the work each) spread it over more CUs;
+  // past that the larger tile's better ratio of MFMA work to operand traffic wins (measured: 427 against
+  // 400 us for the input projection at T = 4096, 137 against 178 us for the output projection)
+  if (t256 < 256 && tiles(320, 128) <= 256) return launch_tiles<320, 128>(a, s);
+  return launch_tiles<256, 256>(a, s);
 }
 
 }  // namespace
