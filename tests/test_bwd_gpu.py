@@ -58,6 +58,19 @@ def test_backward_matches_oracle(hk, hv, alpha_lo, with_state):
         assert _rel(a, b) <= TOL, (name, _rel(a, b))
 
 
+@pytest.mark.parametrize("lens", [[64, 128, 63, 65, 127, 129], [1, 2, 3] * 13 + [0, 200], [3000]])
+def test_backward_chunk_boundaries(lens):
+    """Sequence lengths at and around the 64-token chunk size, many tiny sequences (a chunk table of
+    41 entries, most with one chunk of 1-3 tokens, and an empty one), and one long sequence (47 chunks):
+    every output against the oracle."""
+    cu, q, k, v, alpha, beta, dy, s0, dsf = _inputs(lens, 1, 2, 33, 0.5, True)
+    cfg = gdn.cfg_for(1, 2, 128, 128, torch.float32, scale=0.9)
+    got = _run(cfg, cu, q, k, v, alpha, beta, dy, s0, dsf)
+    ref = O.recurrence_layer_backward(q, k, v, alpha, beta, s0, cu.numpy(), dy, dsf, scale=0.9)
+    for name, a, b in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dstate_in"), got, ref):
+        assert _rel(a, b) <= TOL, (name, _rel(a, b))
+
+
 def test_backward_model_shape_group():
     """16 QK / 48 value heads, one 1024-token sequence: every output of QK group 5 (value heads 15-17)
     against the oracle's chains, summed over the group for dq and dk."""
