@@ -48,11 +48,12 @@ template <int FT, int TT> struct Geo {
   static constexpr int kMI = FT / 64;                              // 32-row feature tiles per wave
   static constexpr int kNJ = TT / 64;                              // 32-token tiles per wave
   static constexpr int kCLd = FT + 8;                              // bytes per token row of a wave's staged tile
+  static constexpr int kFLd = FT / 2 + 4;                          // floats per token row of a staged fp32 gate tile
   static constexpr int kGateParams = 4 * (TT / 2) * kCLd;          // exp(a_log), dt_bias in the epilogue
   static constexpr size_t kSmem = size_t(kRingG) * kSlot;
   static_assert(kSmem <= 160 * 1024, "LDS budget");
   static_assert(size_t(kGateParams) + 8 * kMaxGateHeads <= kSmem, "gate vectors fit beside the staged tiles");
-  static_assert((TT / 2) * kCLd >= 32 * 132 * 4, "a wave's staging area holds a 32-token fp32 gate tile");
+  static_assert((TT / 2) * kCLd >= 32 * kFLd * 4, "a wave's staging area holds a 32-token fp32 gate tile");
 };
 
 // Rows of a panel are 64 bytes (four 16-byte pieces of k); piece p of row r sits at slot
@@ -199,7 +200,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     gp[c] = __expf(a.a_log[c]);
     gp[a.hv + c] = a.dt_bias[c];
   }
-  float* const fs = reinterpret_cast<float*>(cs);  // [32 tokens][132] fp32
+  float* const fs = reinterpret_cast<float*>(cs);  // [32 tokens][kFLd] fp32: every row holds the wave's FT / 2 columns
   const int c_lo = int(max<int64_t>(a.seg_end[1] - nw, 0)), c_hi = int(min<int64_t>(a.seg_end[2] - nw, FT / 2));
   const int nc = c_hi - c_lo;
 #pragma unroll
@@ -209,7 +210,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& v = acc[i][jt];
-        *reinterpret_cast<float4*>(fs + l32 * 132 + 32 * i + 8 * g + 4 * hq) =
+        *reinterpret_cast<float4*>(fs + l32 * G::kFLd + 32 * i + 8 * g + 4 * hq) =
             make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
       }
     for (int e = lane; e < 32 * nc; e += 64) {
@@ -217,7 +218,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
       const int64_t t = t0 + (TT / 2) * wt + 32 * jt + tl;
       if (t >= a.T) continue;
       const int col = int(nw + c - a.seg_end[1]);
-      const float v = fs[tl * 132 + c];
+      const float v = fs[tl * G::kFLd + c];
       if (col < a.hv) {
         const float uu = v + gp[a.hv + col];
         const float sp = fmaxf(uu, 0.f) + __logf(1.f + __expf(-fabsf(uu)));  // softplus without overflow
