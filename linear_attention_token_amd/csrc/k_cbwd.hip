@@ -29,7 +29,8 @@ namespace gdn {
 
 namespace {
 
-constexpr int kC = 64, kD = 128, kSl = 16;  // chunk, head dim, value columns per slice of the chunk passes
+constexpr int kC = 64, kD = 128, kSl = 32;  // chunk, head dim, value columns per slice of the chunk passes
+constexpr int kCT = kSl / 16;                // 16-column tiles of a slice
 constexpr int kSlices = kD / kSl;
 
 // ---- chunk table: seq_off[n] = first chunk of sequence n; tab[c] = (start token, length, sequence) ----
@@ -378,187 +379,231 @@ __global__ void __launch_bounds__(256) k_cb_prep(CBwdArgs a) {
 //     Z = B + s1 A1 X   (64 x 16),      X <- g_C X + H + s2 A2^T Z   (128 x 16),
 // forward (chunks in order):  X = S,   A1 = Wk, s1 = -1, B = U,       Z = W,  A2 = Kt, s2 = +1, H = 0;
 // backward (in reverse):      X = dS', A1 = Kt, s1 = +1, B = P^T dY,  Z = dW, A2 = Wk, s2 = -1, H = gQ^T dY.
-// The products run on 16x16x4 fp32 MFMAs; wave w computes rows 16w.. of Z and rows 32w.. of X, and X stays
-// in registers in the accumulator layout (lane l: rows 4 (l / 16) + e of each 16-row tile, column l % 16).
+// The products run on 16x16x4 fp32 MFMAs; wave w computes rows 16w.. of Z and rows 32w.. of X over the
+// slice's kCT 16-column tiles (each A operand read feeds every tile), and X stays in registers in the
+// accumulator layout (lane l: rows 4 (l / 16) + e of each 16-row tile, column l % 16 of each column tile).
 // The contraction order is chosen so that each lane's A operands are float4 runs of one row: at step
-// (p, c) lane group q contributes index 16p + 4q + c. The chunk-independent operands of the next chunk
-// are loaded before the current chunk's products.
-constexpr int kXLd = 20;  // LDS row stride of X and Z (floats): the four lane groups hit distinct banks
+// (p, c) lane group q contributes index 16p + 4q + c. A block is one chain's slice and runs alone on its
+// CU (four waves, one per SIMD), so every operand of the next chunk -- A1, A2^T, B, G and (backward) H
+// and S -- is requested before the current chunk's products, into the other of two register sets.
+// A wave's rows of B, H and S arrive as 16-byte pieces and reach the accumulator layout through a
+// per-wave LDS area, and its rows of X and Z leave as 16-byte pieces from the LDS tiles the products
+// read: few memory instructions per chunk, so every wait for this chunk's operands can leave the next
+// chunk's requests in flight (a wave tracks at most 63).
+constexpr int kXLd = kSl + 4;  // LDS row stride of X, Z and the staging areas (floats): the four lane groups
+                               // of an accumulator-layout access hit distinct banks
 
 struct PassLoads {
-  float4 a1[8];      // A1 row 16w + l % 16, columns 4 (l / 16 + 4p) ..
-  float b[4];        // B rows 16w + 4 (l / 16) + e
-  float Gc;          // G at the chunk's last row (exponentiated at use: a wait here would stall the loads)
+  float4 a1[8];   // A1 row 16w + l % 16, columns 4 (l / 16 + 4p) ..
+  f32x4 a2[8];    // A2^T rows 32w + 16i + l % 16, columns 4 (l / 16 + 4p) .. (piece 4i + p)
+  float4 b[2];    // B: piece l + 64k of the wave's 16 x kSl rows (row (l + 64k) / 8, columns 4 ((l + 64k) % 8) ..)
+  float4 h[4];    // backward: H and S, piece l + 64k of the wave's 32 x kSl rows (same mapping)
+  float4 sp[4];
+  float Gc;       // G at the chunk's last row (exponentiated at use: a wait here would stall the loads)
 };
+// per wave: B [16][kXLd], H [32][kXLd], S [32][kXLd]
+constexpr int kStageB = 0, kStageH = 16 * kXLd, kStageS = 48 * kXLd, kStageW = 80 * kXLd;
 
 template <bool kBwd>
-__device__ __forceinline__ void pass_load(const CBwdArgs& a, int64_t item, int w, int lm, int lg, int col,
-                                          PassLoads& L) {
+__device__ __forceinline__ void pass_load(const CBwdArgs& a, int64_t item, int w, int lane, int lm, int lg,
+                                          int c0, PassLoads& L) {
   const float* A1 = (kBwd ? a.Kt : a.Wk) + item * kC * kD;
+  const float* A2T = (kBwd ? a.WkT : a.KtT) + item * kD * kC;
   const float* B = (kBwd ? a.dW : a.U) + item * kC * kD;
 #pragma unroll
   for (int p = 0; p < 8; ++p) L.a1[p] = *reinterpret_cast<const float4*>(A1 + (16 * w + lm) * kD + 4 * (lg + 4 * p));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) L.b[e] = B[(16 * w + 4 * lg + e) * kD + col];
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      L.a2[4 * i + p] = *reinterpret_cast<const f32x4*>(A2T + (32 * w + 16 * i + lm) * kC + 4 * (lg + 4 * p));
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int pc = lane + 64 * k;
+    L.b[k] = *reinterpret_cast<const float4*>(B + (16 * w + pc / 8) * kD + c0 + 4 * (pc % 8));
+  }
+  if (kBwd) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int pc = lane + 64 * k;
+      const int64_t o = item * kD * kD + (32 * w + pc / 8) * kD + c0 + 4 * (pc % 8);
+      L.h[k] = *reinterpret_cast<const float4*>(a.dS + o);
+      L.sp[k] = *reinterpret_cast<const float4*>(a.S + o);
+    }
+  }
   L.Gc = a.G[item * kC + kC - 1];
 }
 
 // One chunk of a pass: X (the state at the chunk's start; backward: dL/d state after it) is stored, Z
-// computed and stored, and X advanced.
+// computed and stored, and X advanced. c0 is the slice's first column; St is this wave's staging area.
 template <bool kBwd>
 __device__ __forceinline__ void pass_step(const CBwdArgs& a, int64_t item, const PassLoads& L, int64_t next_item,
-                                          PassLoads& N, f32x4 (&X)[2], float* Xs, float* Zs, int w, int lane,
-                                          int lm, int lg, int col, int sl) {
+                                          PassLoads& N, f32x4 (&X)[kCT][2], float* Xs, float* Zs, float* St, int w,
+                                          int lane, int lm, int lg, int c0, int sl) {
   const float s1 = kBwd ? 1.f : -1.f, s2 = kBwd ? -1.f : 1.f;
   float* Zout = kBwd ? a.dW : a.W;
   float* Xout = kBwd ? a.dS : a.S;
-  // A2^T operands, and (backward) H (in the dS slot, about to be overwritten by X) and S of this chunk:
-  // first used after the first products, so their loads overlap those (the operands of the first
-  // products were loaded a step ahead)
-  f32x4 a2[8];  // A2^T rows 32w + 16i + l % 16, columns 4 (l / 16 + 4p) .. (piece 4i + p)
-  {
-    const float* A2T = (kBwd ? a.WkT : a.KtT) + item * kD * kC;
+  // The next chunk's operands are requested after this chunk's: memory counters drain in order, so a
+  // wait for this chunk's operands then does not also wait for the next chunk's. (H lives in the dS
+  // slot this chunk's X overwrites below; it was read a chunk ahead, before that store.)
+  __builtin_amdgcn_sched_barrier(0);
+  pass_load<kBwd>(a, next_item, w, lane, lm, lg, c0, N);
+  __builtin_amdgcn_sched_barrier(0);
+  // this chunk's B (and H, S) pieces into the wave's staging area
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        a2[4 * i + p] = *reinterpret_cast<const f32x4*>(A2T + (32 * w + 16 * i + lm) * kC + 4 * (lg + 4 * p));
+  for (int k = 0; k < 2; ++k) {
+    const int pc = lane + 64 * k;
+    *reinterpret_cast<float4*>(St + kStageB + (pc / 8) * kXLd + 4 * (pc % 8)) = L.b[k];
   }
-  float hv[2][4], sv[2][4];
   if (kBwd) {
 #pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int pc = lane + 64 * k;
+      *reinterpret_cast<float4*>(St + kStageH + (pc / 8) * kXLd + 4 * (pc % 8)) = L.h[k];
+      *reinterpret_cast<float4*>(St + kStageS + (pc / 8) * kXLd + 4 * (pc % 8)) = L.sp[k];
+    }
+  }
+  // X into the LDS tile; the wave's own rows then leave as 16-byte pieces (a wave's LDS accesses
+  // complete in order, so its own writes are visible to it without a barrier)
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t o = item * kD * kD + (32 * w + 16 * i + 4 * lg + e) * kD + col;
-        hv[i][e] = a.dS[o];
-        sv[i][e] = a.S[o];
-      }
-  }
-  // The next chunk's first operands are requested after this chunk's: memory counters drain in order, so
-  // a wait for this chunk's operands then does not also wait for the next chunk's.
-  __builtin_amdgcn_sched_barrier(0);
-  pass_load<kBwd>(a, next_item, w, lm, lg, col, N);
-  __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 4; ++e) Xs[(32 * w + 16 * i + 4 * lg + e) * kXLd + 16 * ct + lm] = X[ct][i][e];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int k = 0; k < 4; ++k) {
+    const int pc = lane + 64 * k, row = 32 * w + pc / 8;
+    *reinterpret_cast<float4*>(Xout + item * kD * kD + size_t(row) * kD + c0 + 4 * (pc % 8)) =
+        *reinterpret_cast<const float4*>(Xs + row * kXLd + 4 * (pc % 8));
+  }
+  __syncthreads();
+  // Z = B + s1 A1 X: rows 16w + 4 lg + e. B joins the accumulators only after the products.
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct) {
+    float xb[8][4];
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) xb[p][cc] = Xs[(16 * p + 4 * lg + cc) * kXLd + 16 * ct + lm];
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+    f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0;
+#pragma unroll
+    for (int p = 0; p < 8; p += 2) {
+      const float av0[4] = {L.a1[p].x, L.a1[p].y, L.a1[p].z, L.a1[p].w};
+      const float av1[4] = {L.a1[p + 1].x, L.a1[p + 1].y, L.a1[p + 1].z, L.a1[p + 1].w};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        z0 = mfma16x16x4f32(s1 * av0[cc], xb[p][cc], z0);
+        z1 = mfma16x16x4f32(s1 * av1[cc], xb[p + 1][cc], z1);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 32 * w + 16 * i + 4 * lg + e;
-      Xs[row * kXLd + lm] = X[i][e];
-      Xout[item * kD * kD + size_t(row) * kD + col] = X[i][e];
-    }
-  __syncthreads();
-  // Z = B + s1 A1 X: rows 16w + 4 lg + e. Loaded values join the accumulators only after the products,
-  // so that no accumulator set-up waits for loads in flight.
-  // All B operands are read from LDS before the products, and two accumulators alternate, so the
-  // MFMAs issue back to back.
-  float xb[8][4];
-#pragma unroll
-  for (int p = 0; p < 8; ++p)
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) xb[p][cc] = Xs[(16 * p + 4 * lg + cc) * kXLd + lm];
-  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-  f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0;
-#pragma unroll
-  for (int p = 0; p < 8; p += 2) {
-    const float av0[4] = {L.a1[p].x, L.a1[p].y, L.a1[p].z, L.a1[p].w};
-    const float av1[4] = {L.a1[p + 1].x, L.a1[p + 1].y, L.a1[p + 1].z, L.a1[p + 1].w};
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      z0 = mfma16x16x4f32(s1 * av0[cc], xb[p][cc], z0);
-      z1 = mfma16x16x4f32(s1 * av1[cc], xb[p + 1][cc], z1);
+      const int t = 4 * lg + e;  // row of the wave's 16
+      Zs[(16 * w + t) * kXLd + 16 * ct + lm] = z0[e] + z1[e] + St[kStageB + t * kXLd + 16 * ct + lm];
     }
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int t = 16 * w + 4 * lg + e;
-    const float v = z0[e] + z1[e] + L.b[e];
-    Zs[t * kXLd + lm] = v;
-    Zout[item * kC * kD + t * kD + col] = v;
+  for (int k = 0; k < 2; ++k) {
+    const int pc = lane + 64 * k, row = 16 * w + pc / 8;
+    *reinterpret_cast<float4*>(Zout + item * kC * kD + size_t(row) * kD + c0 + 4 * (pc % 8)) =
+        *reinterpret_cast<const float4*>(Zs + row * kXLd + 4 * (pc % 8));
   }
   __syncthreads();
   // X <- g_C X + H + s2 A2^T Z
   const float gc = __expf(L.Gc);
-  float zb[4][4];
+  float part = 0.f;
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
+  for (int ct = 0; ct < kCT; ++ct) {
+    float zb[4][4];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) zb[p][cc] = Zs[(16 * p + 4 * lg + cc) * kXLd + lm];
-  __builtin_amdgcn_sched_barrier(0);
-  f32x4 acc[2];
+    for (int p = 0; p < 4; ++p)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[i][e] = gc * X[i][e];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const f32x4 av0 = a2[p], av1 = a2[4 + p];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      acc[0] = mfma16x16x4f32(s2 * av0[cc], zb[p][cc], acc[0]);
-      acc[1] = mfma16x16x4f32(s2 * av1[cc], zb[p][cc], acc[1]);
-    }
-  }
-  if (kBwd) {  // this wave's part of <S, dS'> (for dG), then X <- ... + H
-    float part = 0.f;
+      for (int cc = 0; cc < 4; ++cc) zb[p][cc] = Zs[(16 * p + 4 * lg + cc) * kXLd + 16 * ct + lm];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part += sv[i][e] * X[i][e];
+      for (int e = 0; e < 4; ++e) acc[i][e] = gc * X[ct][i][e];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const f32x4 av0 = L.a2[p], av1 = L.a2[4 + p];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        acc[0] = mfma16x16x4f32(s2 * av0[cc], zb[p][cc], acc[0]);
+        acc[1] = mfma16x16x4f32(s2 * av1[cc], zb[p][cc], acc[1]);
+      }
+    }
+    if (kBwd) {  // this wave's part of <S, dS'> (for dG), then X <- ... + H
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int o = (16 * i + 4 * lg + e) * kXLd + 16 * ct + lm;
+          part += St[kStageS + o] * X[ct][i][e];
+          acc[i][e] += St[kStageH + o];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) X[ct][i] = acc[i];
+  }
+  if (kBwd) {
     part = group_sum<64>(part);
     if (lane == 0) a.dgc[(item * kSlices + sl) * 4 + w] = part;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][e] += hv[i][e];
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) X[i] = acc[i];
 }
 
 template <bool kBwd>
-__global__ void __launch_bounds__(256, 2) k_cb_pass(CBwdArgs a) {
+__global__ void __launch_bounds__(256, 1) k_cb_pass(CBwdArgs a) {
   __shared__ float Xs[kD * kXLd];
   __shared__ float Zs[kC * kXLd];
-  // the 8 slices of a chain read the same chunk operands: numbered to run on one XCD, so those come from
+  __shared__ float Stage[4 * kStageW];
+  // the slices of a chain read the same chunk operands: numbered to run on one XCD, so those come from
   // HBM once and from that XCD's L2 for the others
   int chain, sl;
   xcd_item(int(blockIdx.x), kSlices, chain, sl);
   if (chain >= a.n_seqs * a.hv) return;
   const int n = chain / a.hv, h = chain % a.hv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lm = lane & 15, lg = lane >> 4;
-  const int col = kSl * sl + lm;
+  const int cs0 = kSl * sl, col = cs0 + lm;  // the slice's first column; this lane's in column tile 0
+  float* const St = Stage + w * kStageW;
   const float* x0 = kBwd ? a.dsf : a.s0;
   const size_t sb = (size_t(n) * a.hv + h) * kD * kD;
-  f32x4 X[2];
+  f32x4 X[kCT][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) X[i][e] = x0 ? x0[sb + size_t(32 * w + 16 * i + 4 * lg + e) * kD + col] : 0.f;
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        X[ct][i][e] = x0 ? x0[sb + size_t(32 * w + 16 * i + 4 * lg + e) * kD + col + 16 * ct] : 0.f;
   const int c0 = a.seq_off[n], nch = a.seq_off[n + 1] - c0;
   // chunk of step it (the backward walks the chunks in reverse)
   auto item_of = [&](int it) { return int64_t(kBwd ? c0 + nch - 1 - it : c0 + it) * a.hv + h; };
   // two operand sets used in turn, so the next chunk's loads are in flight during this chunk's products
-  // (no register copies between them that would wait for those loads)
   // (no register copies between them that would wait for those loads). The loads are unconditional
   // (past the last chunk they repeat it), so every wait for them counts the same loads on every path.
   PassLoads L0, L1;
   if (nch > 0) {
     const int last = nch - 1;
-    pass_load<kBwd>(a, item_of(0), w, lm, lg, col, L0);
+    pass_load<kBwd>(a, item_of(0), w, lane, lm, lg, cs0, L0);
     for (int it = 0;; it += 2) {
-      pass_step<kBwd>(a, item_of(it), L0, item_of(min(it + 1, last)), L1, X, Xs, Zs, w, lane, lm, lg, col, sl);
+      pass_step<kBwd>(a, item_of(it), L0, item_of(min(it + 1, last)), L1, X, Xs, Zs, St, w, lane, lm, lg, cs0, sl);
       if (it + 1 > last) break;
-      pass_step<kBwd>(a, item_of(it + 1), L1, item_of(min(it + 2, last)), L0, X, Xs, Zs, w, lane, lm, lg, col, sl);
+      pass_step<kBwd>(a, item_of(it + 1), L1, item_of(min(it + 2, last)), L0, X, Xs, Zs, St, w, lane, lm, lg, cs0, sl);
       if (it + 2 > last) break;
     }
   }
   if (kBwd && a.ds0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a.ds0[sb + size_t(32 * w + 16 * i + 4 * lg + e) * kD + col] = X[i][e];
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a.ds0[sb + size_t(32 * w + 16 * i + 4 * lg + e) * kD + col + 16 * ct] = X[ct][i][e];
   }
 }
 
