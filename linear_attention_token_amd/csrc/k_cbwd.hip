@@ -135,16 +135,21 @@ struct MmJobs {
   int n;
 };
 
-// One block per item, four waves; wave w computes rows 16w .. 16w + 15 of C over all N columns on 16x16x4
-// fp32 MFMAs. op(B) is staged in LDS as [K][N + 4] (the four lane groups of an operand read hit distinct
+// One block per (item, NB-column block of C), four waves; wave w computes rows 16w .. 16w + 15 of C over the
+// block's NB columns on 16x16x4 fp32 MFMAs. The N / NB blocks of an item are numbered onto one XCD, so the
+// op(A) rows they all read come from HBM once; narrow blocks keep the LDS tile and the accumulators small,
+// so more blocks share a CU and one block's loads overlap another's products. op(B) is staged in LDS as [K][N + 4] (the four lane groups of an operand read hit distinct
 // banks); each wave reads its own rows of op(A) straight into registers. At step (p, c) lane group q contributes contraction index 16p + 4q + c, so a
 // row-major A gives each lane float4 runs.
-template <int N, int K, bool TA, bool TB>
-__global__ void __launch_bounds__(256) k_cb_mm(MmJobs jobs, const int4* __restrict__ tab, int hv) {
-  constexpr int kLd = N + 4;
-  extern __shared__ __attribute__((aligned(16))) float Bs[];  // [K][kLd]: Bs[k][n] = op(B)[k][n]
-  const int64_t item = blockIdx.x;
-  if (tab[item / hv].y <= 0) return;
+template <int N, int NB, int K, bool TA, bool TB>
+__global__ void __launch_bounds__(256) k_cb_mm(MmJobs jobs, const int4* __restrict__ tab, int hv, int64_t items) {
+  constexpr int kLd = NB + 4;
+  extern __shared__ __attribute__((aligned(16))) float Bs[];  // [K][kLd]: Bs[k][n] = op(B)[k][n0 + n]
+  int unit, half;
+  xcd_item(int(blockIdx.x), N / NB, unit, half);
+  const int64_t item = unit;
+  if (item >= items || tab[item / hv].y <= 0) return;
+  const int n0 = NB * half;  // first column of C in this block
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lm = lane & 15, lg = lane >> 4;
   // this wave's A operands: op(A)[16w + lm][16p + 4lg + c]
   auto load_a = [&](const MmJob& jb, float (&av)[K / 16][4]) {
@@ -164,23 +169,23 @@ __global__ void __launch_bounds__(256) k_cb_mm(MmJobs jobs, const int4* __restri
     const float* B = jb.B + item * jb.sB;
     if (!TB) {  // B stored [K][N]
 #pragma unroll
-      for (int r = 0; r < K * N / 1024; ++r) {
-        const int idx = tid + 256 * r, k = idx / (N / 4), n4 = (idx % (N / 4)) * 4;
-        *reinterpret_cast<float4*>(Bs + k * kLd + n4) = *reinterpret_cast<const float4*>(B + int64_t(k) * jb.ldb + n4);
+      for (int r = 0; r < K * NB / 1024; ++r) {
+        const int idx = tid + 256 * r, k = idx / (NB / 4), n4 = (idx % (NB / 4)) * 4;
+        *reinterpret_cast<float4*>(Bs + k * kLd + n4) = *reinterpret_cast<const float4*>(B + int64_t(k) * jb.ldb + n0 + n4);
       }
     } else {  // B stored [N][K]: a wave reads 64 contiguous bytes of each of 16 rows n, and its transposed
               // LDS writes (rows k, 16 consecutive n per row) hit distinct banks
 #pragma unroll
-      for (int r = 0; r < K * N / 1024; ++r) {
+      for (int r = 0; r < K * NB / 1024; ++r) {
         const int f = tid + 256 * r, rest = f >> 6;
-        const int n = 16 * (rest % (N / 16)) + (f & 15), k4 = 16 * (rest / (N / 16)) + 4 * ((f >> 4) & 3);
-        const float4 v = *reinterpret_cast<const float4*>(B + int64_t(n) * jb.ldb + k4);
+        const int n = 16 * (rest % (NB / 16)) + (f & 15), k4 = 16 * (rest / (NB / 16)) + 4 * ((f >> 4) & 3);
+        const float4 v = *reinterpret_cast<const float4*>(B + int64_t(n0 + n) * jb.ldb + k4);
         Bs[(k4 + 0) * kLd + n] = v.x; Bs[(k4 + 1) * kLd + n] = v.y;
         Bs[(k4 + 2) * kLd + n] = v.z; Bs[(k4 + 3) * kLd + n] = v.w;
       }
     }
   };
-  f32x4 acc[N / 16];
+  f32x4 acc[NB / 16];
   int head = 0;  // first job of the current chain
 #pragma unroll 1
   for (int jj = 0; jj < jobs.n; ++jj) {
@@ -195,16 +200,16 @@ __global__ void __launch_bounds__(256) k_cb_mm(MmJobs jobs, const int4* __restri
     if (!jb.chain) {
       head = jj;
 #pragma unroll
-      for (int j = 0; j < N / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NB / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // B operands of step p + 1 are read from LDS while step p's MFMAs run (the scheduling barriers keep
     // the compiler from sinking the reads next to their uses)
-    float bop[2][4][N / 16];
-    auto read_b = [&](int p, float (&dst)[4][N / 16]) {
+    float bop[2][4][NB / 16];
+    auto read_b = [&](int p, float (&dst)[4][NB / 16]) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int j = 0; j < N / 16; ++j) dst[c][j] = Bs[(16 * p + 4 * lg + c) * kLd + 16 * j + lm];
+        for (int j = 0; j < NB / 16; ++j) dst[c][j] = Bs[(16 * p + 4 * lg + c) * kLd + 16 * j + lm];
     };
     read_b(0, bop[0]);
 #pragma unroll
@@ -214,7 +219,7 @@ __global__ void __launch_bounds__(256) k_cb_mm(MmJobs jobs, const int4* __restri
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int j = 0; j < N / 16; ++j) acc[j] = mfma16x16x4f32(av[p][c], bop[p & 1][c][j], acc[j]);
+        for (int j = 0; j < NB / 16; ++j) acc[j] = mfma16x16x4f32(av[p][c], bop[p & 1][c][j], acc[j]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (jj + 1 < jobs.n && jobs.j[jj + 1].chain) continue;
@@ -223,8 +228,8 @@ __global__ void __launch_bounds__(256) k_cb_mm(MmJobs jobs, const int4* __restri
     float* C = hb.C + item * hb.sC;
     float* C2 = hb.C2 ? hb.C2 + item * hb.sC : nullptr;
 #pragma unroll
-    for (int j = 0; j < N / 16; ++j) {
-      const int n = 16 * j + lm;
+    for (int j = 0; j < NB / 16; ++j) {
+      const int n = n0 + 16 * j + lm;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -841,8 +846,9 @@ void cbwd_plan(CBwdArgs& a, void* base) {
 namespace {
 template <int N, int K, bool TA, bool TB>
 hipError_t mm_launch(const MmJobs& jobs, const CBwdArgs& a, hipStream_t s) {
-  const void* f = reinterpret_cast<const void*>(k_cb_mm<N, K, TA, TB>);
-  const int smem = int(sizeof(float) * K * (N + 4));
+  constexpr int NB = N == 128 ? 64 : 32;  // columns of C per block (measured best per width)
+  const void* f = reinterpret_cast<const void*>(k_cb_mm<N, NB, K, TA, TB>);
+  const int smem = int(sizeof(float) * K * (NB + 4));
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -853,8 +859,9 @@ hipError_t mm_launch(const MmJobs& jobs, const CBwdArgs& a, hipStream_t s) {
     if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, smem)) != hipSuccess) return e;
     raised.fetch_or(bit);
   }
-  hipLaunchKernelGGL((k_cb_mm<N, K, TA, TB>), dim3(unsigned(a.nc_max * a.hv)), dim3(256), size_t(smem), s, jobs,
-                     a.tab, a.hv);
+  const int64_t items = a.nc_max * a.hv;
+  hipLaunchKernelGGL((k_cb_mm<N, NB, K, TA, TB>), dim3(unsigned(xcd_blocks(items, N / NB))), dim3(256), size_t(smem), s,
+                     jobs, a.tab, a.hv, items);
   return hipGetLastError();
 }
 
