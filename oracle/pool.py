@@ -61,9 +61,8 @@ def run_chains(inp, chains, *, workers=None, timeout=3600.0, **kw):
     this process when one worker suffices or workers cannot be spawned; raises TimeoutError after
     ``timeout`` seconds."""
     chains = list(chains)
-    st, ci = O._f64(kw.pop("state_in", None)), O._f64(kw.pop("conv_in", None))
-    arrays = ("q", "k", "v", "alpha", "beta", "gate", "conv_w", "norm_w", "state_in", "conv_in")
-    inp = {key: (O._f64(val) if key in arrays else val) for key, val in inp.items()}
+    st, ci = kw.pop("state_in", None), kw.pop("conv_in", None)
+    # chain_inputs upcasts only each chain's slices, so long inputs are never copied whole to fp64
     jobs = [(O.chain_inputs(inp, n, h, state_in=st, conv_in=ci), kw) for n, h in chains]
     workers = min(workers or default_workers(), max(1, len(jobs)))
     if workers <= 1 or not _spawn_possible():

@@ -131,20 +131,37 @@ def _sampled(inp, chains, flags=gdn.GDN_ALL):
     return out, st, cv
 
 
+def _sampled_pool(inp, chains, flags=gdn.GDN_ALL):
+    """Like _sampled, with the oracle chains spread over a process pool."""
+    out, st, cv = run_prefill(inp, flags)
+    tol = TOL[inp.io_dtype]
+    refs = O.run_chains(vars(inp), chains, flags=flags)
+    for (n, h), (o_ref, s_ref) in zip(chains, refs):
+        s0, s1 = seq_bounds(inp, n)
+        e_o, e_s = rel_l2(out[s0:s1, h], o_ref), rel_l2(st[n, h], s_ref)
+        print(f"seq {n} head {h} len {s1 - s0}: rel_l2 out={e_o:.3e} state={e_s:.3e}", flush=True)
+        assert e_o <= tol and e_s <= tol, (n, h, e_o, e_s)
+    return out, st, cv
+
+
 def test_varlen_model_shape_sampled():
-    """32 packed sequences, lengths log-uniform in [512, 32768], S0 ~ N(0, 0.01): sampled chains."""
+    """32 packed sequences, lengths log-uniform in [512, 32768], S0 ~ N(0, 0.01): 16 chains, every
+    other sequence in order of length (shortest and longest included), heads spread over all 16 QK
+    groups."""
     inp = config_varlen(DEV)
     lens = np.diff(inp.cu_seqlens.cpu().numpy())
     order = np.argsort(lens)
-    chains = [(int(order[0]), 0), (int(order[len(order) // 2]), 25), (int(order[-1]), 47)]
-    _, st, _ = _sampled(inp, chains)
+    picks = list(order[::2][:15]) + [order[-1]]
+    chains = [(int(n), (7 * i + 3 * (i % 2)) % 48) for i, n in enumerate(picks)]
+    _, st, _ = _sampled_pool(inp, chains)
     assert torch.isfinite(st).all()
 
 
 def test_long_prefill_sampled():
-    """T = 262144 (native context), B=1, model shape: two value heads against the oracle."""
+    """T = 262144 (native context), B=1, model shape: eight value heads, in eight of the 16 QK groups,
+    against the oracle."""
     inp = config_long(DEV)
-    _sampled(inp, [(0, 0), (0, 46)])
+    _sampled_pool(inp, [(0, h) for h in (0, 7, 13, 20, 26, 33, 39, 46)])
 
 
 # ------------------------------------------------------------------ invariants -------------------
