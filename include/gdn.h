@@ -236,11 +236,13 @@ gdn_status gdn_out_proj(const gdn_cfg* cfg, int32_t hidden, int64_t T, const voi
  *   dq, dk          fp32 [T][HK][128] out: summed over the value heads that read each QK head.
  *   dv              fp32 [T][HV][128] out;  dalpha, dbeta fp32 [T][HV] out.
  *   dstate_in       fp32 [n_seqs][HV][128][128] out (dL/dS_0), or NULL.
- *   workspace       gdn_recurrence_backward_workspace() bytes, 256-byte aligned: every state of the
- *                   forward (64 KB per token and value head) is kept there, so the reverse pass uses the
- *                   forward's exact states; split long batches to bound it.
- * Each (sequence, value head) chain runs token by token (forward, then reverse) as 8 workgroups of 16
- * value columns (the columns of the state evolve independently). */
+ *   workspace       gdn_recurrence_backward_workspace() bytes, 256-byte aligned, about 16 KB per token
+ *                   and value head: the chunks' factors (T = (I + A)^-1, U, Wk, ...), every chunk-start
+ *                   state and the products of the reverse pass; split long batches to bound it.
+ * Chunked form, 64-token chunks: a forward pass over each chain's chunks recomputes the chunk factors
+ * and keeps the chunk-start states, a reverse pass over the chunks carries dL/dS, and everything else
+ * is chunk-parallel fp32 MFMA products; the two sequential passes split each (sequence, value head)
+ * chain into 4 workgroups of 32 value columns (the columns of the state evolve independently). */
 gdn_status gdn_recurrence_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
                                              size_t* bytes);
 gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens,
@@ -260,8 +262,9 @@ gdn_status gdn_recurrence_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t t
  *   dv, dgate       fp32 [T][HV][128] out;  dalpha, dbeta fp32 [T][HV] out;
  *   dconv_w         fp32 [C_tot][4] out;  dnorm_w fp32 [128] out;
  *   dstate_in       fp32 [N][HV][128][128] out or NULL;  dconv_in fp32 [N][3][C_tot] out or NULL.
- *   workspace       gdn_backward_workspace() bytes, 256-byte aligned (about 64 KB per token and value
- *                   head, for the kept states).
+ *   workspace       gdn_backward_workspace() bytes, 256-byte aligned (about 20 KB per token and value
+ *                   head: the recurrence backward's chunk factors and states, and the mixer's fp32
+ *                   intermediates).
  * Every output is reproducible for a fixed configuration (sums over tokens run in a fixed order). */
 gdn_status gdn_backward_workspace(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, size_t* bytes);
 gdn_status gdn_backward(const gdn_cfg* cfg, int32_t n_seqs, int64_t total_tokens, const int32_t* cu_seqlens,
