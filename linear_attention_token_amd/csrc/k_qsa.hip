@@ -286,9 +286,18 @@ __global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __r
 }
 
 // ---- prefill scores on bf16 MFMA: one wave per 16 query rows, 16 compressed keys per step -------
-// D_h = Q_h K^T for each head (16x16x32 MFMA, fp32 accumulate), then sum_h ReLU(D_h). The rotated
-// queries are rounded to bf16 for the A operands; the keys are the stored bf16 cache. A wave's rows
-// can span sequences (packed batches): it runs once per sequence it touches, storing only its rows.
+// D_h = K Q_h^T for each head (16x16x32 MFMA, fp32 accumulate), then sum_h ReLU(D_h). The keys are
+// the A operand (the stored bf16 cache), the rotated queries rounded to bf16 the B operand, so lane
+// (li, lq) ends a step with keys b0 + 4 lq .. + 3 of row r0 + li and stores them as one 16-byte
+// piece. A wave's rows can span sequences (packed batches): it runs once per sequence it touches.
+// Every step issues the same memory instructions in every lane (so the waits for the prefetched
+// keys are exact counts): the keys of step j + kMfmaRing are requested right after step j's MFMAs,
+// a lane stores its four scores whether or not they are wanted: past the row's last block (inside
+// the row's padding, which nothing reads) or, for a row of another sequence, past the last row, or
+// a step past the slice (the loop runs whole rounds of the ring), into the spare row `rows` of the
+// score buffer.
+constexpr int kMfmaRing = 3;  // key steps in flight per wave
+
 __global__ void __launch_bounds__(256) k_qsa_score_mfma(QsaShape sh, const float* __restrict__ qr,
                                                         const int2* __restrict__ info, int64_t rows,
                                                         const uint16_t* __restrict__ kbar,
@@ -297,72 +306,74 @@ __global__ void __launch_bounds__(256) k_qsa_score_mfma(QsaShape sh, const float
   const int64_t r0 = (int64_t(blockIdx.x) * 4 + w) * 16;
   if (r0 >= rows) return;
   const int64_t rn = min(r0 + 16, rows);
-  // output rows of this lane: r0 + 4 lq + r
-  int oseq[4];
-  int64_t onb[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t row = r0 + 4 * lq + r;
-    const int2 in = info[min(row, rn - 1)];
-    oseq[r] = row < rn ? in.x : -1;
-    onb[r] = row_blocks(in.y, sh.cap);
-  }
+  // this lane's output row r0 + li
+  const int64_t row = min(r0 + li, rn - 1);
+  const int2 in = info[row];
+  const int oseq = r0 + li < rn ? in.x : -1;
+  const int onb = int(row_blocks(in.y, sh.cap));
   const int s_first = info[r0].x, s_last = info[rn - 1].x;
   const int c0 = blockIdx.y * kMfmaChunk;
   {  // most of the causal triangle's (rows, chunk) pairs are empty: leave before loading queries
-    int most = 0;
+    int most = oseq >= 0 ? onb : 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) most = oseq[r] >= 0 ? max(most, int(onb[r])) : most;
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) most = max(most, __shfl_xor(most, o, kWave));
+    for (int o = 1; o < 16; o <<= 1) most = max(most, __shfl_xor(most, o, kWave));
     if (c0 >= most) return;
   }
-  // A operand of head h, k-step ks: row r0 + li, dims 32 ks + 8 lq .. + 7
-  const int64_t ra = min(r0 + li, rn - 1);
+  // B operand of head h, k-step ks: row r0 + li, dims 32 ks + 8 lq .. + 7
   short8 a[kQsaHeads][4];
 #pragma unroll
   for (int h = 0; h < kQsaHeads; ++h)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const float* p = qr + ra * (kQsaHeads * kQsaD) + h * kQsaD + 32 * ks + 8 * lq;
+      const float* p = qr + row * (kQsaHeads * kQsaD) + h * kQsaD + 32 * ks + 8 * lq;
       const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
       a[h][ks] = pack8(f32x4{x0.x, x0.y, x0.z, x0.w}, f32x4{x1.x, x1.y, x1.z, x1.w});
     }
+  float* const spare = scores + rows * ld_s + 4 * lq;
 
   for (int sq = s_first; sq <= s_last; ++sq) {
-    int nbmax = 0;  // blocks of the wave's rows in this sequence (<= cap < 2^20)
+    int nbmax = oseq == sq ? onb : 0;  // blocks of the wave's rows in this sequence (<= cap < 2^20)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) nbmax = oseq[r] == sq ? max(nbmax, int(onb[r])) : nbmax;
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) nbmax = max(nbmax, __shfl_xor(nbmax, o, kWave));
-    const int cend = min(nbmax, c0 + kMfmaChunk);  // this workgroup's slice of the blocks
+    for (int o = 1; o < 16; o <<= 1) nbmax = max(nbmax, __shfl_xor(nbmax, o, kWave));
+    const int cend = __builtin_amdgcn_readfirstlane(min(nbmax, c0 + kMfmaChunk));  // this workgroup's slice
     if (c0 >= cend) continue;
+    float* const dst = oseq == sq ? scores + (r0 + li) * ld_s + 4 * lq : spare;
     const uint16_t* kb = kbar + int64_t(sq) * sh.cap * kQsaD + 8 * lq;
-    short8 bv[4];
+    // A operands of the step at b0: key min(b0 + li, cend - 1), dims 32 ks + 8 lq .. + 7 (clamped
+    // rows past the slice are loaded and their scores land in padding)
+    auto load = [&](short8 (&kk)[4], int b0) {
+      const uint16_t* p = kb + int64_t(min(b0 + li, cend - 1)) * kQsaD;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) bv[ks] = ld_short8(kb + int64_t(min(c0 + li, cend - 1)) * kQsaD + 32 * ks);
-    for (int64_t b0 = c0; b0 < cend; b0 += 16) {
-      short8 nx[4];
-      const int64_t bn = min(b0 + 16 + li, int64_t(cend - 1));  // next step's keys (clamped: loaded, unused)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) nx[ks] = ld_short8(kb + bn * kQsaD + 32 * ks);
+      for (int ks = 0; ks < 4; ++ks) kk[ks] = ld_short8(p + 32 * ks);
+    };
+    auto step = [&](short8 (&kk)[4], int b0) {  // b0 past the slice: clamped keys, stored to the spare row
       f32x4 acc[kQsaHeads];
 #pragma unroll
       for (int h = 0; h < kQsaHeads; ++h) {
         acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc[h] = mfma16x16x32(a[h][ks], bv[ks], acc[h]);
+        for (int ks = 0; ks < 4; ++ks) acc[h] = mfma16x16x32(kk[ks], a[h][ks], acc[h]);
       }
-      const int64_t b = b0 + li;
+      load(kk, b0 + 16 * kMfmaRing);
+      f32x4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        float t = 0.f;
 #pragma unroll
-        for (int h = 0; h < kQsaHeads; ++h) v += fmaxf(acc[h][r], 0.f);
-        if (oseq[r] == sq && b < onb[r]) scores[(r0 + 4 * lq + r) * ld_s + b] = v;
+        for (int h = 0; h < kQsaHeads; ++h) t += fmaxf(acc[h][e], 0.f);
+        v[e] = t;
       }
+      *reinterpret_cast<f32x4*>(b0 < cend ? dst + b0 : spare) = v;
+    };
+    short8 ring[kMfmaRing][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bv[ks] = nx[ks];
+    for (int i = 0; i < kMfmaRing; ++i) {  // in ring order, as the loop consumes them
+      load(ring[i], c0 + 16 * i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int b0 = c0; b0 < cend; b0 += 16 * kMfmaRing) {
+#pragma unroll
+      for (int i = 0; i < kMfmaRing; ++i) step(ring[i], b0 + 16 * i);
     }
   }
 }
@@ -675,7 +686,8 @@ QsaWs plan_qsa_ws(const QsaShape& sh, int64_t rows, void* base, size_t* bytes) {
   ws.ld_s = (sh.cap + 63) & ~int64_t(63);
   ws.qr = static_cast<float*>(take(sizeof(float) * size_t(rows) * kQsaHeads * kQsaD));
   ws.info = static_cast<int2*>(take(sizeof(int2) * size_t(rows)));
-  ws.scores = static_cast<float*>(take(sizeof(float) * size_t(rows) * size_t(ws.ld_s)));
+  // one spare row past the last: the MFMA score kernel's unwanted stores
+  ws.scores = static_cast<float*>(take(sizeof(float) * size_t(rows + 1) * size_t(ws.ld_s)));
   const size_t nc = ws.segmax > 1 ? size_t(rows) * ws.segmax * size_t(sh.topk) : 0;
   ws.cand_key = static_cast<uint32_t*>(take(sizeof(uint32_t) * nc));
   ws.cand_idx = static_cast<int32_t*>(take(sizeof(int32_t) * nc));
