@@ -380,11 +380,16 @@ __global__ void __launch_bounds__(256) k_qsa_score_mfma(QsaShape sh, const float
 
 // ---- exact top-k of up to 16384 keys held 16 per thread by 1024 threads ------------------------
 // Keys are score bits with the sign cleared: scores are >= 0, so the unsigned order of the bits is
-// the order of the scores. The k-th largest key is found digit by digit (bits 30..20, 19..9, 8..0),
-// each digit from a 2048-bin LDS histogram of the keys that match the digits found so far; then the
-// keys above it and the first `need_eq` keys equal to it, in index order, are selected.
+// the order of the scores. Thread t holds keys t * 16 .. t * 16 + 15 (index order = thread order,
+// then slot order); a missing key (past the row) is kNoKey, which is negative as an int and so below
+// every real key in signed compares and outside every bucket range. The k-th largest key is found
+// digit by digit, each digit from a 2048-bin LDS histogram of the keys that match the digits found
+// so far; then the keys above it and the first `need_eq` keys equal to it, in index order, are
+// selected. The kernels issue few vector instructions per key: at 16 keys per thread they are bound
+// by instruction issue, not by memory.
 constexpr int kHistPad = 2048 + 2048 / 32;  // bin b at b + b / 32: the digit wave reads runs 33 words apart
 constexpr int kGather = 256;                 // bucket sizes resolved by ranking instead of more digits
+constexpr uint32_t kNoKey = 0xffffffffu;
 
 __device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
 
@@ -392,10 +397,10 @@ template <int NT>
 struct SelLds {
   static constexpr int NW = NT / 64;
   uint32_t hist[3][kHistPad];    // one histogram per digit, all cleared up front
-  uint32_t table[kSelPer * NW];  // per (slot, wave): selected-above count << 16 | equal count
   uint32_t gkey[kGather];        // keys of the threshold bucket, when it is small
   uint32_t wmin[NW], wmax[NW], wpos[NW];
-  uint32_t digit, above, total, ngather;
+  uint32_t wcnt[NW];             // per wave: selected-above count << 16 | equal count
+  uint32_t digit, above, ngather;
 };
 
 // Wave 0 finds the bin holding the need-th largest key in two wave scans: lane l first sums its run
@@ -429,45 +434,48 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint
   }
 }
 
-// Threshold key T and how many keys equal to T to take (in index order), given more than k valid
+// Threshold key T and how many keys equal to T to take (in index order), given more than k real
 // keys. Zero keys (scores clipped to zero) are the smallest: when at most k keys are positive, all
 // of those and the first k - n_pos zeros are taken. Otherwise the positive keys are bucketed over
 // their own range [lo, lo + 2^bw), 11 bits per pass (bucketing by the top bits of the raw float
-// pattern would put most keys of a wave into a few exponent bins and serialise the LDS atomics).
-// After a pass, a bucket of at most kGather keys is resolved at once: its keys are gathered and
-// wave 0 ranks them.
+// pattern would put most keys of a wave into a few exponent bins and serialise the LDS atomics); a
+// key is in the range when key - lo, as an unsigned number, is below 2^bw (zero and missing keys
+// wrap far above it). After a pass, a bucket of at most kGather keys is resolved at once: its keys
+// are gathered and wave 0 ranks them.
 template <int NT>
-__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], uint32_t valid, uint32_t k,
-                                                SelLds<NT>& L, uint32_t* T_out, uint32_t* need_eq) {
+__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], uint32_t k, SelLds<NT>& L,
+                                                uint32_t* T_out, uint32_t* need_eq) {
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  uint32_t mn = 0xffffffffu, mx = 0, np = 0;
+  uint32_t mn = 0xffffffffu, np = 0;
+  int mx = 0;
 #pragma unroll
   for (int j = 0; j < kSelPer; ++j) {
-    const bool pos = ((valid >> j) & 1u) && key[j] > 0;
-    mn = pos ? min(mn, key[j]) : mn;
-    mx = pos ? max(mx, key[j]) : mx;
+    const bool pos = int(key[j]) > 0;
+    mn = min(mn, pos ? key[j] : 0xffffffffu);
+    mx = max(mx, int(key[j]));
     np += pos;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     mn = min(mn, uint32_t(__shfl_xor(mn, o, kWave)));
-    mx = max(mx, uint32_t(__shfl_xor(mx, o, kWave)));
+    mx = max(mx, __shfl_xor(mx, o, kWave));
     np += uint32_t(__shfl_xor(np, o, kWave));
   }
   if (lane == 0) {
     L.wmin[w] = mn;
-    L.wmax[w] = mx;
+    L.wmax[w] = uint32_t(mx);
     L.wpos[w] = np;
   }
   for (int i = t; i < 3 * kHistPad; i += NT) (&L.hist[0][0])[i] = 0;
   if (t == 0) L.ngather = 0;
   __syncthreads();
-  mn = 0xffffffffu, mx = 0, np = 0;
+  uint32_t mxu = 0;
+  mn = 0xffffffffu, np = 0;
 #pragma unroll
   for (int u = 0; u < NW; ++u) {
     mn = min(mn, L.wmin[u]);
-    mx = max(mx, L.wmax[u]);
+    mxu = max(mxu, L.wmax[u]);
     np += L.wpos[u];
   }
   if (np <= k) {
@@ -476,14 +484,14 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
     return;
   }
   uint32_t lo = mn, need = k;
-  int bw = 32 - __clz(mx - mn);  // bits of the range: keys in [lo, lo + 2^bw)
+  int bw = 32 - __clz(mxu - mn);  // bits of the range: keys in [lo, lo + 2^bw), bw <= 31
   for (int pass = 0; pass < 3 && bw > 0; ++pass) {
     const int sh = max(bw - 11, 0), nbins = 1 << (bw - sh);
+    const uint32_t range = 1u << bw;
 #pragma unroll
     for (int j = 0; j < kSelPer; ++j) {
       const uint32_t d = key[j] - lo;
-      if (((valid >> j) & 1u) && key[j] >= lo && (uint64_t(d) >> bw) == 0)
-        atomicAdd(&L.hist[pass][hpad(int(d >> sh))], 1u);
+      if (d < range) atomicAdd(&L.hist[pass][hpad(int(d >> sh))], 1u);
     }
     __syncthreads();
     if (t < kWave) find_digit(L.hist[pass], nbins, need, L);
@@ -495,12 +503,10 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
     bw = sh;
     if (bw > 0 && cnt <= kGather) {
       // the bucket [lo, lo + 2^bw) is small: gather its keys and rank them
+      const uint32_t brange = 1u << bw;
 #pragma unroll
-      for (int j = 0; j < kSelPer; ++j) {
-        const uint32_t d = key[j] - lo;
-        if (((valid >> j) & 1u) && key[j] >= lo && (uint64_t(d) >> bw) == 0)
-          L.gkey[atomicAdd(&L.ngather, 1u)] = key[j];
-      }
+      for (int j = 0; j < kSelPer; ++j)
+        if (key[j] - lo < brange) L.gkey[atomicAdd(&L.ngather, 1u)] = key[j];
       __syncthreads();
       if (t < kWave) {
         const uint32_t n = L.ngather;
@@ -529,57 +535,41 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
   *need_eq = need;
 }
 
-// Selects (all valid keys when n_valid <= k, else the top k) and calls emit(j, out_pos) for each
-// selected key j of this thread, out_pos counting in index order (index = j * 1024 + thread).
+// Selects (all real keys when n_valid <= k, else the top k) and calls emit(j, out_pos) for each
+// selected key j of this thread, out_pos counting in index order (index = thread * 16 + j): one
+// block-wide scan of each thread's counts (above | equal, packed) gives every thread its start.
 // Returns the number selected.
 template <int NT, typename F>
-__device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], uint32_t valid, uint32_t n_valid,
-                                                uint32_t k, SelLds<NT>& L, F&& emit) {
-  constexpr int NW = NT / 64, EPL = kSelPer * NW / 64;  // table entries per lane of wave 0
+__device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], uint32_t n_valid, uint32_t k,
+                                                SelLds<NT>& L, F&& emit) {
+  constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const bool all = n_valid <= k;
   uint32_t T = 0, need_eq = 0;
-  if (!all) radix_threshold(key, valid, k, L, &T, &need_eq);
-  const uint64_t below = (uint64_t(1) << lane) - 1;
+  if (!all) radix_threshold(key, k, L, &T, &need_eq);
+  // all: every real key counts as above (T = -1 as an int); else above means > T, equal means == T
+  const int Ti = all ? -1 : int(T);
+  const uint32_t Te = all ? kNoKey : T;
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kSelPer; ++j) cnt += int(key[j]) > Ti ? 0x10000u : (key[j] == Te ? 1u : 0u);
+  const uint32_t incl = wave_incl_scan(cnt, lane);
+  if (lane == 63) L.wcnt[w] = incl;
+  __syncthreads();
+  uint32_t pre = incl - cnt, tot = 0;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    const uint32_t x = L.wcnt[u];
+    pre += u < w ? x : 0u;
+    tot += x;
+  }
+  uint32_t gb = pre >> 16, eb = pre & 0xffffu;
 #pragma unroll
   for (int j = 0; j < kSelPer; ++j) {
-    const bool v = (valid >> j) & 1u;
-    const bool gt = v && (all || key[j] > T), eq = v && !all && key[j] == T;
-    const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    if (lane == 0) L.table[j * NW + w] = (uint32_t(__popcll(bg)) << 16) | uint32_t(__popcll(be));
-  }
-  __syncthreads();
-  if (t < kWave) {  // exclusive scan of the (slot, wave) counts, EPL per lane, in index order
-    uint32_t c[EPL], sum = 0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      c[e] = L.table[EPL * lane + e];
-      sum += c[e];
-    }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t n = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += n;
-    }
-    uint32_t run = incl - sum;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      L.table[EPL * lane + e] = run;
-      run += c[e];
-    }
-    if (lane == 63) L.total = incl;
-  }
-  __syncthreads();
-  const uint32_t tot = L.total;
-#pragma unroll
-  for (int j = 0; j < kSelPer; ++j) {
-    const bool v = (valid >> j) & 1u;
-    const bool gt = v && (all || key[j] > T), eq = v && !all && key[j] == T;
-    const uint32_t base = L.table[j * NW + w];
-    const uint64_t bg = __ballot(gt), be = __ballot(eq);  // recomputed: cheaper than 32 live registers
-    const uint32_t gb = (base >> 16) + uint32_t(__popcll(bg & below)), eb = (base & 0xffffu) + uint32_t(__popcll(be & below));
+    const bool gt = int(key[j]) > Ti, eq = key[j] == Te;
     if (gt || (eq && eb < need_eq)) emit(j, gb + min(eb, need_eq));
+    gb += gt;
+    eb += eq;
   }
   return (tot >> 16) + min(tot & 0xffffu, need_eq);
 }
@@ -616,24 +606,27 @@ __global__ void __launch_bounds__(NT, 8) k_qsa_select(QsaShape sh, const int2* _
   const int64_t seg0 = int64_t(sg) * SEG;
   const uint32_t n = uint32_t(min(int64_t(SEG), nb - seg0 > 0 ? nb - seg0 : int64_t(0)));
   const float* row = scores + r * ld_s + seg0;
-  uint32_t key[kSelPer], valid = 0;
+  const uint32_t i0 = uint32_t(t) * kSelPer;  // this thread's first key
+  uint32_t key[kSelPer];
 #pragma unroll
-  for (int j = 0; j < kSelPer; ++j) {
-    const uint32_t i = uint32_t(j * NT + t);
-    const bool v = i < n;
-    key[j] = v ? (__float_as_uint(row[i]) & 0x7fffffffu) : 0u;
-    valid |= uint32_t(v) << j;
+  for (int q = 0; q < kSelPer / 4; ++q) {  // 16-byte pieces (the row stride is a multiple of 64 keys,
+                                           // so a piece that starts before n stays inside the row)
+    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i0 + 4 * q < n) x = *reinterpret_cast<const f32x4*>(row + i0 + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      key[4 * q + e] = i0 + 4 * q + e < n ? (__float_as_uint(x[e]) & 0x7fffffffu) : kNoKey;
   }
   const uint32_t k = uint32_t(sh.topk);
   if (nseg <= 1) {
     int32_t* srow = sel + r * sh.topk;
-    const uint32_t cnt = select_topk<NT>(key, valid, n, k, L, [&](int j, uint32_t p) { srow[p] = j * NT + t; });
+    const uint32_t cnt = select_topk<NT>(key, n, k, L, [&](int j, uint32_t p) { srow[p] = int32_t(i0) + j; });
     finish_row<NT>(srow, cnt, k, pos, n_sel + r, tail + r);
   } else {
     const int64_t c0 = (r * segmax + sg) * int64_t(sh.topk);
-    select_topk<NT>(key, valid, n, k, L, [&](int j, uint32_t p) {
+    select_topk<NT>(key, n, k, L, [&](int j, uint32_t p) {
       cand_key[c0 + p] = key[j];
-      cand_idx[c0 + p] = int32_t(seg0 + j * NT + t);
+      cand_idx[c0 + p] = int32_t(seg0 + i0 + j);
     });
   }
 }
@@ -655,20 +648,19 @@ __global__ void __launch_bounds__(NT) k_qsa_merge(QsaShape sh, const int2* __res
   if (nseg <= 1) return;
   const uint32_t k = uint32_t(sh.topk);
   const int64_t c0 = r * segmax * int64_t(sh.topk);
-  uint32_t key[kSelPer], valid = 0, nv = 0;
+  uint32_t key[kSelPer], nv = 0;
   int32_t idx[kSelPer];
 #pragma unroll
-  for (int j = 0; j < kSelPer; ++j) {
-    const uint32_t p = uint32_t(j * NT + t), s = p / k, i = p - s * k;
+  for (int j = 0; j < kSelPer; ++j) {  // list position t * 16 + j: segment s, slot i
+    const uint32_t p = uint32_t(t * kSelPer + j), s = p / k, i = p - s * k;
     const int64_t cs = s < uint32_t(nseg) ? min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)) : 0;
     const bool v = int64_t(i) < cs;
-    key[j] = v ? cand_key[c0 + p] : 0u;
+    key[j] = v ? cand_key[c0 + p] : kNoKey;
     idx[j] = v ? cand_idx[c0 + p] : 0;
-    valid |= uint32_t(v) << j;
   }
   for (int s = 0; s < nseg; ++s) nv += uint32_t(min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)));
   int32_t* srow = sel + r * sh.topk;
-  const uint32_t cnt = select_topk<NT>(key, valid, nv, k, L, [&](int j, uint32_t p) { srow[p] = idx[j]; });
+  const uint32_t cnt = select_topk<NT>(key, nv, k, L, [&](int j, uint32_t p) { srow[p] = idx[j]; });
   finish_row<NT>(srow, cnt, k, pos, n_sel + r, tail + r);
 }
 
