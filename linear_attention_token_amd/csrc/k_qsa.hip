@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __r
 // the row's padding, which nothing reads) or, for a row of another sequence, past the last row, or
 // a step past the slice (the loop runs whole rounds of the ring), into the spare row `rows` of the
 // score buffer.
-constexpr int kMfmaRing = 3;  // key steps in flight per wave
+constexpr int kMfmaRing = 4;  // key steps in flight per wave (deeper rings measured slower: 2 waves per SIMD either way)
 
 __global__ void __launch_bounds__(256) k_qsa_score_mfma(QsaShape sh, const float* __restrict__ qr,
                                                         const int2* __restrict__ info, int64_t rows,
