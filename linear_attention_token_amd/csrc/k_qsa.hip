@@ -22,6 +22,8 @@
 // the angle is formed and reduced mod 2 pi in fp64, so positions near 2^20 keep fp32 accuracy.
 #include <math.h>
 
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "ext_internal.h"
 
@@ -442,15 +444,15 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint
 // key is in the range when key - lo, as an unsigned number, is below 2^bw (zero and missing keys
 // wrap far above it). After a pass, a bucket of at most kGather keys is resolved at once: its keys
 // are gathered and wave 0 ranks them.
-template <int NT>
-__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], uint32_t k, SelLds<NT>& L,
+template <int NT, int S>
+__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[S], uint32_t k, SelLds<NT>& L,
                                                 uint32_t* T_out, uint32_t* need_eq) {
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint32_t mn = 0xffffffffu, np = 0;
   int mx = 0;
 #pragma unroll
-  for (int j = 0; j < kSelPer; ++j) {
+  for (int j = 0; j < S; ++j) {
     const bool pos = int(key[j]) > 0;
     mn = min(mn, pos ? key[j] : 0xffffffffu);
     mx = max(mx, int(key[j]));
@@ -489,7 +491,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
     const int sh = max(bw - 11, 0), nbins = 1 << (bw - sh);
     const uint32_t range = 1u << bw;
 #pragma unroll
-    for (int j = 0; j < kSelPer; ++j) {
+    for (int j = 0; j < S; ++j) {
       const uint32_t d = key[j] - lo;
       if (d < range) atomicAdd(&L.hist[pass][hpad(int(d >> sh))], 1u);
     }
@@ -505,7 +507,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
       // the bucket [lo, lo + 2^bw) is small: gather its keys and rank them
       const uint32_t brange = 1u << bw;
 #pragma unroll
-      for (int j = 0; j < kSelPer; ++j)
+      for (int j = 0; j < S; ++j)
         if (key[j] - lo < brange) L.gkey[atomicAdd(&L.ngather, 1u)] = key[j];
       __syncthreads();
       if (t < kWave) {
@@ -536,23 +538,23 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kSelPer], 
 }
 
 // Selects (all real keys when n_valid <= k, else the top k) and calls emit(j, out_pos) for each
-// selected key j of this thread, out_pos counting in index order (index = thread * 16 + j): one
+// selected key j of this thread, out_pos counting in index order (index = thread * S + j): one
 // block-wide scan of each thread's counts (above | equal, packed) gives every thread its start.
 // Returns the number selected.
-template <int NT, typename F>
-__device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], uint32_t n_valid, uint32_t k,
+template <int NT, int S, typename F>
+__device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[S], uint32_t n_valid, uint32_t k,
                                                 SelLds<NT>& L, F&& emit) {
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const bool all = n_valid <= k;
   uint32_t T = 0, need_eq = 0;
-  if (!all) radix_threshold(key, k, L, &T, &need_eq);
+  if (!all) radix_threshold<NT, S>(key, k, L, &T, &need_eq);
   // all: every real key counts as above (T = -1 as an int); else above means > T, equal means == T
   const int Ti = all ? -1 : int(T);
   const uint32_t Te = all ? kNoKey : T;
   uint32_t cnt = 0;
 #pragma unroll
-  for (int j = 0; j < kSelPer; ++j) cnt += int(key[j]) > Ti ? 0x10000u : (key[j] == Te ? 1u : 0u);
+  for (int j = 0; j < S; ++j) cnt += int(key[j]) > Ti ? 0x10000u : (key[j] == Te ? 1u : 0u);
   const uint32_t incl = wave_incl_scan(cnt, lane);
   if (lane == 63) L.wcnt[w] = incl;
   __syncthreads();
@@ -565,7 +567,7 @@ __device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[kSelPer], 
   }
   uint32_t gb = pre >> 16, eb = pre & 0xffffu;
 #pragma unroll
-  for (int j = 0; j < kSelPer; ++j) {
+  for (int j = 0; j < S; ++j) {
     const bool gt = int(key[j]) > Ti, eq = key[j] == Te;
     if (gt || (eq && eb < need_eq)) emit(j, gb + min(eb, need_eq));
     gb += gt;
@@ -606,28 +608,43 @@ __global__ void __launch_bounds__(NT, 8) k_qsa_select(QsaShape sh, const int2* _
   const int64_t seg0 = int64_t(sg) * SEG;
   const uint32_t n = uint32_t(min(int64_t(SEG), nb - seg0 > 0 ? nb - seg0 : int64_t(0)));
   const float* row = scores + r * ld_s + seg0;
-  const uint32_t i0 = uint32_t(t) * kSelPer;  // this thread's first key
-  uint32_t key[kSelPer];
-#pragma unroll
-  for (int q = 0; q < kSelPer / 4; ++q) {  // 16-byte pieces (the row stride is a multiple of 64 keys,
-                                           // so a piece that starts before n stays inside the row)
-    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (i0 + 4 * q < n) x = *reinterpret_cast<const f32x4*>(row + i0 + 4 * q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      key[4 * q + e] = i0 + 4 * q + e < n ? (__float_as_uint(x[e]) & 0x7fffffffu) : kNoKey;
-  }
   const uint32_t k = uint32_t(sh.topk);
-  if (nseg <= 1) {
-    int32_t* srow = sel + r * sh.topk;
-    const uint32_t cnt = select_topk<NT>(key, n, k, L, [&](int j, uint32_t p) { srow[p] = int32_t(i0) + j; });
-    finish_row<NT>(srow, cnt, k, pos, n_sel + r, tail + r);
+  // S keys per thread: the fewest slots that hold the segment, so short rows do less work per thread
+  // (the select is bound by vector instruction issue, and most of it is per key)
+  auto run = [&](auto s_tag) {
+    constexpr int S = decltype(s_tag)::value;
+    const uint32_t i0 = uint32_t(t) * S;  // this thread's first key
+    uint32_t key[S];
+#pragma unroll
+    for (int q = 0; q < S / 4; ++q) {  // 16-byte pieces (the row stride is a multiple of 64 keys, so a
+                                       // piece that starts before n stays inside the row)
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i0 + 4 * q < n) x = *reinterpret_cast<const f32x4*>(row + i0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        key[4 * q + e] = i0 + 4 * q + e < n ? (__float_as_uint(x[e]) & 0x7fffffffu) : kNoKey;
+    }
+    if (nseg <= 1) {
+      int32_t* srow = sel + r * sh.topk;
+      const uint32_t cnt = select_topk<NT, S>(key, n, k, L, [&](int j, uint32_t p) { srow[p] = int32_t(i0) + j; });
+      finish_row<NT>(srow, cnt, k, pos, n_sel + r, tail + r);
+    } else {
+      const int64_t c0 = (r * segmax + sg) * int64_t(sh.topk);
+      select_topk<NT, S>(key, n, k, L, [&](int j, uint32_t p) {
+        cand_key[c0 + p] = key[j];
+        cand_idx[c0 + p] = int32_t(seg0 + i0 + j);
+      });
+    }
+  };
+  if constexpr (NT == 1024) {  // decode rows (segments of 16384 scores): the short paths would spill
+    run(std::integral_constant<int, kSelPer>{});
   } else {
-    const int64_t c0 = (r * segmax + sg) * int64_t(sh.topk);
-    select_topk<NT>(key, n, k, L, [&](int j, uint32_t p) {
-      cand_key[c0 + p] = key[j];
-      cand_idx[c0 + p] = int32_t(seg0 + i0 + j);
-    });
+    if (n <= 4u * NT)
+      run(std::integral_constant<int, 4>{});
+    else if (n <= 8u * NT)
+      run(std::integral_constant<int, 8>{});
+    else
+      run(std::integral_constant<int, kSelPer>{});
   }
 }
 
@@ -660,7 +677,7 @@ __global__ void __launch_bounds__(NT) k_qsa_merge(QsaShape sh, const int2* __res
   }
   for (int s = 0; s < nseg; ++s) nv += uint32_t(min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)));
   int32_t* srow = sel + r * sh.topk;
-  const uint32_t cnt = select_topk<NT>(key, nv, k, L, [&](int j, uint32_t p) { srow[p] = idx[j]; });
+  const uint32_t cnt = select_topk<NT, kSelPer>(key, nv, k, L, [&](int j, uint32_t p) { srow[p] = idx[j]; });
   finish_row<NT>(srow, cnt, k, pos, n_sel + r, tail + r);
 }
 
