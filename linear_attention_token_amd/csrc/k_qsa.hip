@@ -11,9 +11,10 @@
 //   k_qsa_score     a row's compressed keys streamed by 16-lane groups, 16 B per lane (HBM-bound
 //                   in decode, where the cache is read once per step);
 //   k_qsa_score_mfma  bf16 prefill: 16 query rows x 16 compressed keys per bf16 MFMA step;
-//   k_qsa_select    one block per row and segment of 16 scores per thread (1024 threads: 16384
-//                   scores; 256 or 512 threads for short rows): exact top-k by a radix select on
-//                   the score bits held in registers, then an ordered compaction;
+//   k_qsa_select    one block per row and segment, up to 16 consecutive scores per thread (1024
+//                   threads: 16384 scores; 256 or 512 threads for short rows): exact top-k by a
+//                   radix select on the score bits held in registers, then an ordered compaction
+//                   by one block scan of per-thread counts;
 //   k_qsa_merge     rows longer than one segment: the same select over the segments' candidates
 //                   (every global top-k block is in its own segment's top-k).
 //
