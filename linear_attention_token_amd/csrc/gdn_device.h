@@ -214,6 +214,18 @@ __device__ __forceinline__ float4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, int voff
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
 }
 
+// 16 bytes through the caches.
+__device__ __forceinline__ float4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Item of block b of n when each of the 8 XCDs (to which blocks are dispatched round robin) walks
+// its own contiguous range of items: block b serves item (b % 8) (n / 8) + b / 8, for n a multiple
+// of 8 (else item b).
+__device__ __forceinline__ unsigned xcd_range_item(unsigned b, unsigned n) {
+  return n % 8u == 0u ? (b % 8u) * (n / 8u) + b / 8u : b;
+}
+
 // One fp32 accumulator tile -> bf16 operand; two bf16 tiles -> one 16-byte piece.
 __device__ __forceinline__ short4v pack4(const f32x4& a) {
   typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
