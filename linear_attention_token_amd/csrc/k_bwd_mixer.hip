@@ -205,15 +205,17 @@ __global__ void __launch_bounds__(256) k_l2silu_bwd(BwdMixArgs m) {
     *reinterpret_cast<float4*>(m.du + t * m.C + c0) = make_float4(g[0] * u[0], g[1] * u[1], g[2] * u[2], g[3] * u[3]);
 }
 
-// Thread per channel, kConvBwdRows packed tokens per block row: dx for those tokens and this block's part
-// of dw. The du rows t .. t + 3 and x rows t - 3 .. t that the tokens read are loaded once each, all
-// before use (history rows of a sequence start are read where needed).
+// Four channels per thread (16-byte loads and stores), windows of kConvBwdRows packed tokens per
+// block row, walked in register halves of kConvBwdHalf tokens: dx for those tokens and this block's
+// part of dw. The du rows t .. t + 3 and x rows t - 3 .. t that a half reads are loaded once each,
+// all before use (history rows of a sequence start are read where needed).
 constexpr int kConvBwdRows = 16;
+constexpr int kConvBwdHalf = 8;
 __global__ void __launch_bounds__(256) k_conv_bwd(BwdMixArgs m) {
-  constexpr int R = kConvBwdRows;
-  const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  constexpr int R = kConvBwdHalf;
+  const int64_t c = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;  // first of the thread's channels
   if (c >= m.C) return;
-  // channel -> (input tensor, column, output tensor)
+  // channel -> (input tensor, column, output tensor); the tensor boundaries are multiples of 128
   const float* x;
   float* dx;
   int64_t ld, col;
@@ -221,19 +223,20 @@ __global__ void __launch_bounds__(256) k_conv_bwd(BwdMixArgs m) {
   if (c < qk) { x = m.q; dx = m.dq; ld = qk; col = c; }
   else if (c < 2 * qk) { x = m.k; dx = m.dk; ld = qk; col = c - qk; }
   else { x = m.v; dx = m.dv; ld = int64_t(m.hv) * kD; col = c - 2 * qk; }
-  float w4[4];
+  float4 w4[4];  // w4[e] = taps of channel c + e
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w4[j] = m.conv_w[c * 4 + j];
-  float dw[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 4; ++e) w4[e] = *reinterpret_cast<const float4*>(m.conv_w + (c + e) * 4);
+  float dw[4][4] = {};  // dw[e][j]
   // windows blockIdx.y, + gridDim.y, ...: this block's part of dw sums a fixed set of tokens
-  for (int64_t t0 = int64_t(blockIdx.y) * R; t0 < m.T; t0 += int64_t(gridDim.y) * R) {
+  for (int64_t t00 = int64_t(blockIdx.y) * kConvBwdRows; t00 < m.T; t00 += int64_t(gridDim.y) * kConvBwdRows) {
+  for (int64_t t0 = t00; t0 < min(t00 + kConvBwdRows, m.T); t0 += R) {
   const int64_t t1 = min(t0 + R, m.T);
-  float duw[R + 3], xw[R + 3];  // du[t0 + i], x[t0 - 3 + i]
+  float4 duw[R + 3], xw[R + 3];  // du[t0 + i], x[t0 - 3 + i]
 #pragma unroll
   for (int i = 0; i < R + 3; ++i) {
     const int64_t tu = t0 + i, p = t0 - 3 + i;
-    duw[i] = tu < m.T ? m.du[tu * m.C + c] : 0.f;
-    xw[i] = (p >= 0 && p < m.T) ? x[p * ld + col] : 0.f;
+    duw[i] = tu < m.T ? *reinterpret_cast<const float4*>(m.du + tu * m.C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    xw[i] = (p >= 0 && p < m.T) ? *reinterpret_cast<const float4*>(x + p * ld + col) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   int n = seq_of(m.cu, m.n_seqs, t0);
 #pragma unroll
@@ -242,25 +245,39 @@ __global__ void __launch_bounds__(256) k_conv_bwd(BwdMixArgs m) {
     if (t >= t1) break;
     while (n + 1 < m.n_seqs && int64_t(m.cu[n + 1]) <= t) ++n;
     const int64_t s0 = m.cu[n], s1 = m.cu[n + 1];
-    float acc = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t tu = t + 3 - j;  // the conv output that reads x[t] through tap j
-      if (tu < s1) acc = fmaf(w4[j], duw[i + 3 - j], acc);
+      if (tu < s1) {
+        const float4 d = duw[i + 3 - j];
+        acc.x = fmaf(w4[0][j], d.x, acc.x);
+        acc.y = fmaf(w4[1][j], d.y, acc.y);
+        acc.z = fmaf(w4[2][j], d.z, acc.z);
+        acc.w = fmaf(w4[3][j], d.w, acc.w);
+      }
     }
-    dx[t * ld + col] = acc;
-    const float dut = duw[i];
+    *reinterpret_cast<float4*>(dx + t * ld + col) = acc;
+    const float4 dut = duw[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t p = t - 3 + j;
-      float xv;
+      float4 xv;
       if (p >= s0) xv = xw[i + j];
-      else xv = m.conv_in ? m.conv_in[(int64_t(n) * 3 + (p - s0 + 3)) * m.C + c] : 0.f;
-      dw[j] = fmaf(dut, xv, dw[j]);
+      else xv = m.conv_in ? *reinterpret_cast<const float4*>(m.conv_in + (int64_t(n) * 3 + (p - s0 + 3)) * m.C + c)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      dw[0][j] = fmaf(dut.x, xv.x, dw[0][j]);
+      dw[1][j] = fmaf(dut.y, xv.y, dw[1][j]);
+      dw[2][j] = fmaf(dut.z, xv.z, dw[2][j]);
+      dw[3][j] = fmaf(dut.w, xv.w, dw[3][j]);
     }
   }
   }
-  *reinterpret_cast<float4*>(m.dw_part + (int64_t(blockIdx.y) * m.C + c) * 4) = make_float4(dw[0], dw[1], dw[2], dw[3]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    *reinterpret_cast<float4*>(m.dw_part + (int64_t(blockIdx.y) * m.C + c + e) * 4) =
+        make_float4(dw[e][0], dw[e][1], dw[e][2], dw[e][3]);
 }
 
 // dconv_w = the sum of the token-window groups' parts: thread (channel, q) adds parts q, q + 4, ..., then
@@ -321,7 +338,7 @@ hipError_t launch_mixer_input_bwd(const BwdMixArgs& m, hipStream_t s) {
     const int64_t items = m.T * (2 * m.hk + m.hv);
     const int64_t nb = std::min<int64_t>((m.T + kConvBwdRows - 1) / kConvBwdRows, kConvWeightParts);
     hipLaunchKernelGGL(k_l2silu_bwd, dim3(static_cast<unsigned>((items + 7) / 8)), dim3(256), 0, s, m);
-    hipLaunchKernelGGL(k_conv_bwd, dim3(static_cast<unsigned>((m.C + 255) / 256), static_cast<unsigned>(nb)),
+    hipLaunchKernelGGL(k_conv_bwd, dim3(static_cast<unsigned>((m.C / 4 + 255) / 256), static_cast<unsigned>(nb)),
                        dim3(256), 0, s, m);
     hipLaunchKernelGGL(k_conv_w_sum, dim3(static_cast<unsigned>((m.C + 63) / 64)), dim3(256), 0, s, m, nb);
   } else {
