@@ -10,7 +10,7 @@
 //                   decode, also the new key joins its sequence's pending block, or completes it;
 //   k_qsa_score     a row's compressed keys streamed by 16-lane groups, 16 B per lane (HBM-bound
 //                   in decode, where the cache is read once per step);
-//   k_qsa_score_mfma  bf16 prefill: 16 query rows x 16 compressed keys per bf16 MFMA step;
+//   k_qsa_score_mfma  bf16 prefill: 2 x 16 query rows x 16 compressed keys per bf16 MFMA step;
 //   k_qsa_select    one block per row and segment, up to 16 consecutive scores per thread (1024
 //                   threads: 16384 scores; 256 or 512 threads for short rows): exact top-k by a
 //                   radix select on the score bits held in registers, then an ordered compaction
@@ -288,59 +288,76 @@ __global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __r
   }
 }
 
-// ---- prefill scores on bf16 MFMA: one wave per 16 query rows, 16 compressed keys per step -------
-// D_h = K Q_h^T for each head (16x16x32 MFMA, fp32 accumulate), then sum_h ReLU(D_h). The keys are
-// the A operand (the stored bf16 cache), the rotated queries rounded to bf16 the B operand, so lane
-// (li, lq) ends a step with keys b0 + 4 lq .. + 3 of row r0 + li and stores them as one 16-byte
-// piece. A wave's rows can span sequences (packed batches): it runs once per sequence it touches.
-// Every step issues the same memory instructions in every lane (so the waits for the prefetched
-// keys are exact counts): the keys of step j + kMfmaRing are requested right after step j's MFMAs,
-// a lane stores its four scores whether or not they are wanted: past the row's last block (inside
-// the row's padding, which nothing reads) or, for a row of another sequence, past the last row, or
-// a step past the slice (the loop runs whole rounds of the ring), into the spare row `rows` of the
-// score buffer.
-constexpr int kMfmaRing = 4;  // key steps in flight per wave (deeper rings measured slower: 2 waves per SIMD either way)
+// ---- prefill scores on bf16 MFMA: one wave per 32 query rows (two 16-row tiles), 16 compressed
+// keys per step -----------------------------------------------------------------------------------
+// D_h = K Q_h^T for each head and tile (16x16x32 MFMA, fp32 accumulate), then sum_h ReLU(D_h). The
+// keys are the A operand (the stored bf16 cache), shared by the two tiles; the rotated queries
+// rounded to bf16 are the B operands, so lane (li, lq) ends a step with keys b0 + 4 lq .. + 3 of
+// rows r0 + li and r0 + 16 + li and stores each as one 16-byte piece. A wave's rows can span
+// sequences (packed batches): it runs once per sequence it touches. Every step issues the same
+// memory instructions in every lane (so the waits for the prefetched keys are exact counts): the
+// keys of step j + kMfmaRing are requested right after step j's MFMAs, and a lane stores its scores
+// whether or not they are wanted: past the row's last block (inside the row's padding, which
+// nothing reads) or, for a row of another sequence, past the last row, or a step past the slice (the
+// loop runs whole rounds of the ring), into the spare row `rows` of the score buffer.
+constexpr int kMfmaRing = 2;   // key steps in flight per wave (three: the same time, more spills)
+constexpr int kMfmaTiles = 2;  // 16-row query tiles per wave
+constexpr int kMfmaRows = 16 * kMfmaTiles * 4;  // query rows per workgroup
 
-__global__ void __launch_bounds__(256) k_qsa_score_mfma(QsaShape sh, const float* __restrict__ qr,
+__global__ void __launch_bounds__(256, 2) k_qsa_score_mfma(QsaShape sh, const float* __restrict__ qr,
                                                         const int2* __restrict__ info, int64_t rows,
                                                         const uint16_t* __restrict__ kbar,
                                                         float* __restrict__ scores, int64_t ld_s) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lq = lane >> 4;
-  const int64_t r0 = (int64_t(blockIdx.x) * 4 + w) * 16;
+  const int64_t r0 = (int64_t(blockIdx.x) * 4 + w) * (16 * kMfmaTiles);
   if (r0 >= rows) return;
-  const int64_t rn = min(r0 + 16, rows);
-  // this lane's output row r0 + li
-  const int64_t row = min(r0 + li, rn - 1);
-  const int2 in = info[row];
-  const int oseq = r0 + li < rn ? in.x : -1;
-  const int onb = int(row_blocks(in.y, sh.cap));
+  const int64_t rn = min(r0 + 16 * kMfmaTiles, rows);
+  // this lane's output rows r0 + 16 tt + li
+  int64_t row[kMfmaTiles];
+  int oseq[kMfmaTiles], onb[kMfmaTiles];
+#pragma unroll
+  for (int tt = 0; tt < kMfmaTiles; ++tt) {
+    row[tt] = min(r0 + 16 * tt + li, rn - 1);
+    const int2 in = info[row[tt]];
+    oseq[tt] = r0 + 16 * tt + li < rn ? in.x : -1;
+    onb[tt] = int(row_blocks(in.y, sh.cap));
+  }
   const int s_first = info[r0].x, s_last = info[rn - 1].x;
   const int c0 = blockIdx.y * kMfmaChunk;
   {  // most of the causal triangle's (rows, chunk) pairs are empty: leave before loading queries
-    int most = oseq >= 0 ? onb : 0;
+    int most = 0;
+#pragma unroll
+    for (int tt = 0; tt < kMfmaTiles; ++tt) most = oseq[tt] >= 0 ? max(most, onb[tt]) : most;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) most = max(most, __shfl_xor(most, o, kWave));
     if (c0 >= most) return;
   }
-  // B operand of head h, k-step ks: row r0 + li, dims 32 ks + 8 lq .. + 7
-  short8 a[kQsaHeads][4];
+  // B operand of tile tt, head h, k-step ks: row r0 + 16 tt + li, dims 32 ks + 8 lq .. + 7
+  short8 a[kMfmaTiles][kQsaHeads][4];
 #pragma unroll
-  for (int h = 0; h < kQsaHeads; ++h)
+  for (int tt = 0; tt < kMfmaTiles; ++tt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const float* p = qr + row * (kQsaHeads * kQsaD) + h * kQsaD + 32 * ks + 8 * lq;
-      const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
-      a[h][ks] = pack8(f32x4{x0.x, x0.y, x0.z, x0.w}, f32x4{x1.x, x1.y, x1.z, x1.w});
-    }
+    for (int h = 0; h < kQsaHeads; ++h)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float* p = qr + row[tt] * (kQsaHeads * kQsaD) + h * kQsaD + 32 * ks + 8 * lq;
+        const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
+        a[tt][h][ks] = pack8(f32x4{x0.x, x0.y, x0.z, x0.w}, f32x4{x1.x, x1.y, x1.z, x1.w});
+      }
   float* const spare = scores + rows * ld_s + 4 * lq;
 
   for (int sq = s_first; sq <= s_last; ++sq) {
-    int nbmax = oseq == sq ? onb : 0;  // blocks of the wave's rows in this sequence (<= cap < 2^20)
+    int nbmax = 0;  // blocks of the wave's rows in this sequence (<= cap < 2^20)
+#pragma unroll
+    for (int tt = 0; tt < kMfmaTiles; ++tt) nbmax = oseq[tt] == sq ? max(nbmax, onb[tt]) : nbmax;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) nbmax = max(nbmax, __shfl_xor(nbmax, o, kWave));
     const int cend = __builtin_amdgcn_readfirstlane(min(nbmax, c0 + kMfmaChunk));  // this workgroup's slice
     if (c0 >= cend) continue;
-    float* const dst = oseq == sq ? scores + (r0 + li) * ld_s + 4 * lq : spare;
+    float* dst[kMfmaTiles];
+#pragma unroll
+    for (int tt = 0; tt < kMfmaTiles; ++tt)
+      dst[tt] = oseq[tt] == sq ? scores + (r0 + 16 * tt + li) * ld_s + 4 * lq : spare;
     const uint16_t* kb = kbar + int64_t(sq) * sh.cap * kQsaD + 8 * lq;
     // A operands of the step at b0: key min(b0 + li, cend - 1), dims 32 ks + 8 lq .. + 7 (clamped
     // rows past the slice are loaded and their scores land in padding)
@@ -350,23 +367,28 @@ __global__ void __launch_bounds__(256) k_qsa_score_mfma(QsaShape sh, const float
       for (int ks = 0; ks < 4; ++ks) kk[ks] = ld_short8(p + 32 * ks);
     };
     auto step = [&](short8 (&kk)[4], int b0) {  // b0 past the slice: clamped keys, stored to the spare row
-      f32x4 acc[kQsaHeads];
+      f32x4 acc[kMfmaTiles][kQsaHeads];
 #pragma unroll
-      for (int h = 0; h < kQsaHeads; ++h) {
-        acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < kMfmaTiles; ++tt)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc[h] = mfma16x16x32(kk[ks], a[h][ks], acc[h]);
-      }
+        for (int h = 0; h < kQsaHeads; ++h) {
+          acc[tt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc[tt][h] = mfma16x16x32(kk[ks], a[tt][h][ks], acc[tt][h]);
+        }
       load(kk, b0 + 16 * kMfmaRing);
-      f32x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float t = 0.f;
+      for (int tt = 0; tt < kMfmaTiles; ++tt) {
+        f32x4 v;
 #pragma unroll
-        for (int h = 0; h < kQsaHeads; ++h) t += fmaxf(acc[h][e], 0.f);
-        v[e] = t;
+        for (int e = 0; e < 4; ++e) {
+          float t = 0.f;
+#pragma unroll
+          for (int h = 0; h < kQsaHeads; ++h) t += fmaxf(acc[tt][h][e], 0.f);
+          v[e] = t;
+        }
+        *reinterpret_cast<f32x4*>(b0 < cend ? dst[tt] + b0 : spare) = v;
       }
-      *reinterpret_cast<f32x4*>(b0 < cend ? dst + b0 : spare) = v;
     };
     short8 ring[kMfmaRing][4];
 #pragma unroll
@@ -735,7 +757,7 @@ hipError_t launch_qsa_rows(const QsaShape& sh, const QsaWs& ws, int64_t row0, in
   if (sh.cap > 0) {
     if (sh.bf16 && cu)  // prefill rows: many queries per sequence, a dense contraction
       hipLaunchKernelGGL(k_qsa_score_mfma,
-                         dim3(static_cast<unsigned>((rows + 63) / 64),
+                         dim3(static_cast<unsigned>((rows + kMfmaRows - 1) / kMfmaRows),
                               static_cast<unsigned>((sh.cap + kMfmaChunk - 1) / kMfmaChunk)),
                          dim3(256), 0, s, sh, ws.qr, ws.info, rows, static_cast<const uint16_t*>(kbar), ws.scores,
                          ws.ld_s);
