@@ -419,7 +419,7 @@ constexpr uint32_t kNoKey = 0xffffffffu;
 __device__ __forceinline__ int hpad(int b) { return b + (b >> 5); }
 
 template <int NT>
-struct SelLds {
+struct __attribute__((aligned(16))) SelLds {
   static constexpr int NW = NT / 64;
   uint32_t hist[3][kHistPad];    // one histogram per digit, all cleared up front
   uint32_t gkey[kGather];        // keys of the threshold bucket, when it is small
@@ -492,7 +492,8 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[S], uint32
     L.wmax[w] = uint32_t(mx);
     L.wpos[w] = np;
   }
-  for (int i = t; i < 3 * kHistPad; i += NT) (&L.hist[0][0])[i] = 0;
+  static_assert((3 * kHistPad) % 4 == 0, "histograms cleared in 16-byte pieces");
+  for (int i = t; i < 3 * kHistPad / 4; i += NT) reinterpret_cast<uint4*>(&L.hist[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
   if (t == 0) L.ngather = 0;
   __syncthreads();
   uint32_t mxu = 0;
