@@ -17,8 +17,10 @@
 // row-major, so both operands are K-contiguous rows.
 //
 // Kernel: a block computes an FT out features x TT tokens tile (256 x 256; 320 x 128 or 128 x 256 when
-// those fill the chip's rounds better) with four waves (one per SIMD) of FT / 2 x TT / 2 on 32x32x16 bf16
-// MFMA (out features as the A operand, tokens as the B operand; each lane
+// those fill the chip's rounds better) with waves of FT / 2 features x a share of the tokens on 32x32x16
+// bf16 MFMA: eight waves (two per SIMD, 128 x 64 each) for 256 x 256, so one wave's MFMAs run while the
+// other waits at the LDS reads or the barrier; four (one per SIMD) for the other shapes (out features
+// as the A operand, tokens as the B operand; each lane
 // ends with runs of 4 consecutive output features of one token; the tile is staged in LDS and stored
 // as 16-byte pieces of token rows). K advances in steps of 32 through a
 // five-slot LDS ring filled by direct global->LDS loads three steps ahead. Blocks are numbered so that
@@ -37,23 +39,29 @@ constexpr int kKStep = 32;               // k per ring slot
 constexpr int kRingG = 5;                // ring slots
 constexpr int kAhead = kRingG - 2;       // k-steps loaded ahead of the one being multiplied
 constexpr int kGroupM = 8, kGroupT = 4;  // tiles of a block group: 8 feature tiles x 4 token tiles
+constexpr int kWaves256 = 8;             // waves of a 256 x 256 tile block
 constexpr int kMaxGateHeads = 3072;      // value heads the epilogue's LDS holds gate vectors for
 
-// Per tile shape: FT output features x TT tokens (each a multiple of 64), four waves of FT / 2 x TT / 2:
-template <int FT, int TT> struct Geo {
+// Per tile shape: FT output features x TT tokens (each a multiple of 64) with WV waves, 2 along the
+// features and WV / 2 along the tokens, each wave computing FT / 2 x TT / (WV / 2):
+template <int FT, int TT, int WV> struct Geo {
   static constexpr int kPanelW = FT * kKStep * 2;                  // W panel bytes per slot
   static constexpr int kPanelX = TT * kKStep * 2;                  // x panel bytes per slot
   static constexpr int kSlot = kPanelW + kPanelX;
-  static constexpr int kWLoads = FT / 64, kLoads = FT / 64 + TT / 64;  // 1 KB loads per wave and slot
+  static constexpr int kWLoads = FT / (16 * WV);                   // 1 KB W panel loads per wave and slot
+  static constexpr int kXLoads = TT / (16 * WV);                   // 1 KB x panel loads per wave and slot
+  static constexpr int kLoads = kWLoads + kXLoads;
   static constexpr int kMI = FT / 64;                              // 32-row feature tiles per wave
-  static constexpr int kNJ = TT / 64;                              // 32-token tiles per wave
+  static constexpr int kTW = TT / (WV / 2);                        // tokens per wave
+  static constexpr int kNJ = kTW / 32;                             // 32-token tiles per wave
   static constexpr int kCLd = FT + 8;                              // bytes per token row of a wave's staged tile
   static constexpr int kFLd = FT / 2 + 4;                          // floats per token row of a staged fp32 gate tile
-  static constexpr int kGateParams = 4 * (TT / 2) * kCLd;          // exp(a_log), dt_bias in the epilogue
+  static constexpr int kGateParams = WV * kTW * kCLd;              // exp(a_log), dt_bias in the epilogue
   static constexpr size_t kSmem = size_t(kRingG) * kSlot;
+  static_assert(FT % (16 * WV) == 0 && TT % (16 * WV) == 0 && kTW % 32 == 0, "whole loads and tiles per wave");
   static_assert(kSmem <= 160 * 1024, "LDS budget");
   static_assert(size_t(kGateParams) + 8 * kMaxGateHeads <= kSmem, "gate vectors fit beside the staged tiles");
-  static_assert((TT / 2) * kCLd >= 32 * kFLd * 4, "a wave's staging area holds a 32-token fp32 gate tile");
+  static_assert(kTW * kCLd >= 32 * kFLd * 4, "a wave's staging area holds a 32-token fp32 gate tile");
 };
 
 // Rows of a panel are 64 bytes (four 16-byte pieces of k); piece p of row r sits at slot
@@ -84,9 +92,9 @@ __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& a, int64_t
   return a.w[2] + (n - a.seg_end[1]) * a.K;
 }
 
-template <int FT, int TT>
-__global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
-  using G = Geo<FT, TT>;
+template <int FT, int TT, int WV>
+__global__ void __launch_bounds__(64 * WV) k_gemm(GemmArgs a) {
+  using G = Geo<FT, TT, WV>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // block -> tile: XCD x runs blocks b = 8 j + x; the 32 consecutive j of one XCD form one group
   const int b = int(blockIdx.x), x = b & 7, j = b >> 3;
@@ -97,19 +105,19 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   const int tm = a.n_tiles_m - 1 - tmr;  // the last feature tiles (the gate columns) go first
   const int64_t n0 = int64_t(tm) * FT, t0 = int64_t(tt) * TT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w & 1, wt = w >> 1;  // this wave's quarter: features (FT / 2) wm .., tokens (TT / 2) wt ..
+  const int wm = w & 1, wt = w >> 1;  // this wave's part: features (FT / 2) wm .., tokens kTW wt ..
   const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const int nks = a.K / kKStep;
 
   // This wave's direct loads of one slot: W load i < kWLoads covers W panel rows 16 (kWLoads w + i) ..
-  // + 15, x load i covers x panel rows 16 (TT / 64 w + i) .. + 15; lane l takes row 16 (.) + l / 4,
-  // slot l % 4.
+  // + 15, x load i covers x panel rows 16 (kXLoads w + i - kWLoads) .. + 15; lane l takes row
+  // 16 (.) + l / 4, slot l % 4.
   const uint16_t* src[G::kLoads];
   uint32_t dst[G::kLoads];
 #pragma unroll
   for (int i = 0; i < G::kLoads; ++i) {
     const bool wl = i < G::kWLoads;
-    const int blk = wl ? G::kWLoads * w + i : G::kNJ * w + (i - G::kWLoads);
+    const int blk = wl ? G::kWLoads * w + i : G::kXLoads * w + (i - G::kWLoads);
     const int r = 16 * blk + (lane >> 2), piece = (lane & 3) ^ pkey(r);
     src[i] = (wl ? weight_row(a, n0 + r) : a.x + min(t0 + r, a.T - 1) * a.ld_x) + 8 * piece;
     dst[i] = (wl ? 0 : G::kPanelW) + blk * 1024;
@@ -153,7 +161,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
       }
 #pragma unroll
       for (int jt = 0; jt < G::kNJ; ++jt) {
-        const int r = (TT / 2) * wt + 32 * jt + l32;
+        const int r = G::kTW * wt + 32 * jt + l32;
         bf[jt] = *reinterpret_cast<const short8*>(sb + G::kPanelW + r * 64 + (((2 * u + hq) ^ pkey(r)) << 4));
       }
 #pragma unroll
@@ -169,7 +177,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   // ---- epilogue. The bf16 outputs go through this wave's tile in LDS (the ring is free after the
   // last barrier) and leave as 16-byte pieces of token rows; the gate columns are finished from the
   // fp32 registers. ----
-  unsigned char* const cs = smem + size_t(w) * (TT / 2) * G::kCLd;
+  unsigned char* const cs = smem + size_t(w) * G::kTW * G::kCLd;
 #pragma unroll
   for (int i = 0; i < G::kMI; ++i)
 #pragma unroll
@@ -183,9 +191,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   const int64_t nw = n0 + (FT / 2) * wm;  // first feature of this wave's tile
   constexpr int kRowPieces = FT / 16;      // 16-byte pieces per staged token row (FT / 2 features)
 #pragma unroll 4
-  for (int k = 0; k < (TT / 2) * kRowPieces / 64; ++k) {
+  for (int k = 0; k < G::kTW * kRowPieces / 64; ++k) {
     const int pc = lane + 64 * k, tl = pc / kRowPieces, seg8 = pc % kRowPieces;
-    const int64_t t = t0 + (TT / 2) * wt + tl, n = nw + 8 * seg8;
+    const int64_t t = t0 + G::kTW * wt + tl, n = nw + 8 * seg8;
     if (t >= a.T || n >= a.seg_end[1]) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(cs + tl * G::kCLd + seg8 * 16);
     if (n < a.seg_end[0]) *reinterpret_cast<uint4*>(a.out[0] + t * a.ld_out[0] + n) = v;
@@ -215,7 +223,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
       }
     for (int e = lane; e < 32 * nc; e += 64) {
       const int tl = e / nc, c = c_lo + (e - tl * nc);
-      const int64_t t = t0 + (TT / 2) * wt + 32 * jt + tl;
+      const int64_t t = t0 + G::kTW * wt + 32 * jt + tl;
       if (t >= a.T) continue;
       const int col = int(nw + c - a.seg_end[1]);
       const float v = fs[tl * G::kFLd + c];
@@ -230,9 +238,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   }
 }
 
-template <int FT, int TT>
+template <int FT, int TT, int WV = 4>
 hipError_t launch_tiles(GemmArgs& a, hipStream_t s) {
-  using G = Geo<FT, TT>;
+  using G = Geo<FT, TT, WV>;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -240,7 +248,7 @@ hipError_t launch_tiles(GemmArgs& a, hipStream_t s) {
   static std::atomic<uint64_t> raised{0};
   const uint64_t bit = uint64_t(1) << (dev & 63);
   if (!(raised.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm<FT, TT>), hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm<FT, TT, WV>), hipFuncAttributeMaxDynamicSharedMemorySize,
                             int(G::kSmem));
     if (e != hipSuccess) return e;
     raised.fetch_or(bit);
@@ -250,7 +258,7 @@ hipError_t launch_tiles(GemmArgs& a, hipStream_t s) {
   const int n_gm = (a.n_tiles_m + kGroupM - 1) / kGroupM, n_gt = (a.n_tiles_t + kGroupT - 1) / kGroupT;
   const int64_t groups = int64_t(n_gm) * n_gt;
   const int64_t blocks = ((groups + 7) / 8) * 8 * kGroupM * kGroupT;  // every XCD walks whole groups
-  hipLaunchKernelGGL((k_gemm<FT, TT>), dim3(unsigned(blocks)), dim3(256), G::kSmem, s, a);
+  hipLaunchKernelGGL((k_gemm<FT, TT, WV>), dim3(unsigned(blocks)), dim3(64 * WV), G::kSmem, s, a);
   return hipGetLastError();
 }
 
@@ -266,7 +274,7 @@ hipError_t launch_gemm(GemmArgs& a, hipStream_t s) {
   // past that the larger tile's better ratio of MFMA work to operand traffic wins (measured: 427 against
   // 400 us for the input projection at T = 4096, 137 against 178 us for the output projection)
   if (t256 < 256 && tiles(320, 128) <= 256) return launch_tiles<320, 128>(a, s);
-  return launch_tiles<256, 256>(a, s);
+  return launch_tiles<256, 256, kWaves256>(a, s);
 }
 
 }  // namespace
