@@ -691,13 +691,33 @@ __global__ void __launch_bounds__(NT) k_qsa_merge(QsaShape sh, const int2* __res
   const int64_t c0 = r * segmax * int64_t(sh.topk);
   uint32_t key[kSelPer], nv = 0;
   int32_t idx[kSelPer];
+  const int64_t lim = int64_t(segmax) * k;  // this row's candidate slots; nothing past them is read
+  if (k % 4 == 0) {  // 16-byte pieces of the candidate lists (c0 and lim are then multiples of 4)
 #pragma unroll
-  for (int j = 0; j < kSelPer; ++j) {  // list position t * 16 + j: segment s, slot i
+    for (int q = 0; q < kSelPer / 4; ++q) {
+      const int64_t p0 = int64_t(t) * kSelPer + 4 * q;
+      uint4 kq = make_uint4(kNoKey, kNoKey, kNoKey, kNoKey);
+      int4 iq = make_int4(0, 0, 0, 0);
+      if (p0 < lim) {
+        kq = *reinterpret_cast<const uint4*>(cand_key + c0 + p0);
+        iq = *reinterpret_cast<const int4*>(cand_idx + c0 + p0);
+      }
+      key[4 * q] = kq.x; key[4 * q + 1] = kq.y; key[4 * q + 2] = kq.z; key[4 * q + 3] = kq.w;
+      idx[4 * q] = iq.x; idx[4 * q + 1] = iq.y; idx[4 * q + 2] = iq.z; idx[4 * q + 3] = iq.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      const int64_t p = int64_t(t) * kSelPer + j;
+      key[j] = p < lim ? cand_key[c0 + p] : kNoKey;
+      idx[j] = p < lim ? cand_idx[c0 + p] : 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kSelPer; ++j) {  // list position t * 16 + j: segment s, slot i; unfilled slots are no keys
     const uint32_t p = uint32_t(t * kSelPer + j), s = p / k, i = p - s * k;
     const int64_t cs = s < uint32_t(nseg) ? min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)) : 0;
-    const bool v = int64_t(i) < cs;
-    key[j] = v ? cand_key[c0 + p] : kNoKey;
-    idx[j] = v ? cand_idx[c0 + p] : 0;
+    if (int64_t(i) >= cs) key[j] = kNoKey;
   }
   for (int s = 0; s < nseg; ++s) nv += uint32_t(min(int64_t(k), min(int64_t(kSelSeg), nb - int64_t(s) * kSelSeg)));
   int32_t* srow = sel + r * sh.topk;
