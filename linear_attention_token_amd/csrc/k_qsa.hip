@@ -565,7 +565,10 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[S], uint32
 // selected key j of this thread, out_pos counting in index order (index = thread * S + j): one
 // block-wide scan of each thread's counts (above | equal, packed) gives every thread its start.
 // Returns the number selected.
-template <int NT, int S, typename F>
+// kSparse: emit needs only j (not key[j]), so the thread walks the set bits of its above / equal
+// masks instead of every slot (a thread emits about k / NT keys; the wave loops as often as its
+// busiest lane).
+template <int NT, int S, bool kSparse = false, typename F>
 __device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[S], uint32_t n_valid, uint32_t k,
                                                 SelLds<NT>& L, F&& emit) {
   constexpr int NW = NT / 64;
@@ -576,9 +579,18 @@ __device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[S], uint32
   // all: every real key counts as above (T = -1 as an int); else above means > T, equal means == T
   const int Ti = all ? -1 : int(T);
   const uint32_t Te = all ? kNoKey : T;
-  uint32_t cnt = 0;
+  uint32_t cnt = 0, mg = 0, me = 0;
+  if constexpr (kSparse) {
 #pragma unroll
-  for (int j = 0; j < S; ++j) cnt += int(key[j]) > Ti ? 0x10000u : (key[j] == Te ? 1u : 0u);
+    for (int j = 0; j < S; ++j) {
+      mg |= uint32_t(int(key[j]) > Ti) << j;
+      me |= uint32_t(key[j] == Te) << j;
+    }
+    cnt = (uint32_t(__popc(mg)) << 16) | uint32_t(__popc(me));
+  } else {
+#pragma unroll
+    for (int j = 0; j < S; ++j) cnt += int(key[j]) > Ti ? 0x10000u : (key[j] == Te ? 1u : 0u);
+  }
   const uint32_t incl = wave_incl_scan(cnt, lane);
   if (lane == 63) L.wcnt[w] = incl;
   __syncthreads();
@@ -590,12 +602,22 @@ __device__ __forceinline__ uint32_t select_topk(const uint32_t (&key)[S], uint32
     tot += x;
   }
   uint32_t gb = pre >> 16, eb = pre & 0xffffu;
+  if constexpr (kSparse) {
+    for (uint32_t m = mg | me; m != 0u; m &= m - 1u) {
+      const int j = __ffs(m) - 1;
+      const uint32_t below = (1u << j) - 1u;
+      const uint32_t gbj = gb + uint32_t(__popc(mg & below)), ebj = eb + uint32_t(__popc(me & below));
+      if ((mg >> j) & 1u) emit(j, gbj + min(ebj, need_eq));
+      else if (ebj < need_eq) emit(j, gbj + ebj);
+    }
+  } else {
 #pragma unroll
-  for (int j = 0; j < S; ++j) {
-    const bool gt = int(key[j]) > Ti, eq = key[j] == Te;
-    if (gt || (eq && eb < need_eq)) emit(j, gb + min(eb, need_eq));
-    gb += gt;
-    eb += eq;
+    for (int j = 0; j < S; ++j) {
+      const bool gt = int(key[j]) > Ti, eq = key[j] == Te;
+      if (gt || (eq && eb < need_eq)) emit(j, gb + min(eb, need_eq));
+      gb += gt;
+      eb += eq;
+    }
   }
   return (tot >> 16) + min(tot & 0xffffu, need_eq);
 }
@@ -650,7 +672,7 @@ __global__ void __launch_bounds__(NT, 8) k_qsa_select(QsaShape sh, const int2* _
     }
     if (nseg <= 1) {
       int32_t* srow = sel + r * sh.topk;
-      const uint32_t cnt = select_topk<NT, S>(key, n, k, L, [&](int j, uint32_t p) { srow[p] = int32_t(i0) + j; });
+      const uint32_t cnt = select_topk<NT, S, true>(key, n, k, L, [&](int j, uint32_t p) { srow[p] = int32_t(i0) + j; });
       finish_row<NT>(srow, cnt, k, pos, n_sel + r, tail + r);
     } else {
       const int64_t c0 = (r * segmax + sg) * int64_t(sh.topk);
