@@ -226,18 +226,21 @@ def test_decode_one_million_tokens(dtype, n_tok):
     assert n_sel.tolist() == [512, 512]
 
 
-@pytest.mark.parametrize("T", [20000, 66000])
-def test_prefill_select_long_rows(T):
+@pytest.mark.parametrize("T,topk", [(20000, 512), (66000, 512), (66000, 509)])
+def test_prefill_select_long_rows(T, topk):
     """One long sequence, sampled rows (including the last ones) against the oracle. 20000 tokens:
-    caches of 5000 blocks take the 512-thread select; 66000: tokens past 65536 see more than 16384
-    blocks (two select segments and the merge)."""
+    caches of 5000 blocks take the 512-thread select, with 4, 8 or 16 scores per thread by row length
+    (rows 8191 / 8195 and 16383 / 16387 sit on either side of 2048 and 4096 blocks); 66000: tokens past
+    65536 see more than 16384 blocks (two select segments and the merge), and a top-k that is not a
+    multiple of 4 takes the merge's 4-byte candidate reads."""
     dtype = torch.bfloat16
     x = indexer_inputs([T], io_dtype=dtype, seed=16, device=DEV)
-    cfg = qsa.cfg_for(dtype)
+    cfg = qsa.cfg_for(dtype, topk=topk)
     kbar, _ = _compress(cfg, x, T // 4, pending=False)
     sel, n_sel, tail = qsa.qsa_select(cfg, x.cu_seqlens, x.q, kbar)
     torch.cuda.synchronize()
-    rows = np.concatenate([np.arange(T - 6, T), np.random.default_rng(0).integers(0, T, 10), [3, 2050, T - 4461]])
+    rows = np.concatenate([np.arange(T - 6, T), np.random.default_rng(0).integers(0, T, 10),
+                           [3, 2050, T - 4461, 8191, 8195, 16383, 16387]])
     kb = O.qsa_compress(_np(x.k), _np(x.norm_w))
     r_t = torch.as_tensor(rows, device=DEV)
     _check_rows(dtype, _np(x.q[r_t]), rows, kb, sel[r_t].cpu().numpy(), n_sel[r_t].cpu().numpy(),
