@@ -209,9 +209,16 @@ __global__ void __launch_bounds__(64) k_qsa_qprep(QsaShape sh, const IO* __restr
   ld8(q + row * ld_q + h * kQsaD + 8 * m, y);
   const RopeLane rl = rope_lane(m, sh);
   rope8(y, rl, double(max(pos, 0)), t);
-  float* o = qr + r * (kQsaHeads * kQsaD) + h * kQsaD + 8 * m;
-  *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
-  *reinterpret_cast<float4*>(o + 4) = make_float4(y[4], y[5], y[6], y[7]);
+  if (std::is_same<IO, bf16>::value && cu) {
+    // bf16 prefill: the MFMA score kernel's operands, rounded here once ([rows][4][128] bf16 in the
+    // same buffer)
+    *reinterpret_cast<short8*>(reinterpret_cast<uint16_t*>(qr) + r * (kQsaHeads * kQsaD) + h * kQsaD + 8 * m) =
+        pack8(f32x4{y[0], y[1], y[2], y[3]}, f32x4{y[4], y[5], y[6], y[7]});
+  } else {
+    float* o = qr + r * (kQsaHeads * kQsaD) + h * kQsaD + 8 * m;
+    *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(y[4], y[5], y[6], y[7]);
+  }
   if (t == 0) info[r] = make_int2(seq, pos);
 }
 
@@ -291,8 +298,8 @@ __global__ void __launch_bounds__(256) k_qsa_score(QsaShape sh, const float* __r
 // ---- prefill scores on bf16 MFMA: one wave per 32 query rows (two 16-row tiles), 16 compressed
 // keys per step -----------------------------------------------------------------------------------
 // D_h = K Q_h^T for each head and tile (16x16x32 MFMA, fp32 accumulate), then sum_h ReLU(D_h). The
-// keys are the A operand (the stored bf16 cache), shared by the two tiles; the rotated queries
-// rounded to bf16 are the B operands, so lane (li, lq) ends a step with keys b0 + 4 lq .. + 3 of
+// keys are the A operand (the stored bf16 cache), shared by the two tiles; the rotated queries,
+// which the query prep rounds to bf16 for this kernel, are the B operands, so lane (li, lq) ends a step with keys b0 + 4 lq .. + 3 of
 // rows r0 + li and r0 + 16 + li and stores each as one 16-byte piece. A wave's rows can span
 // sequences (packed batches): it runs once per sequence it touches. Every step issues the same
 // memory instructions in every lane (so the waits for the prefetched keys are exact counts): the
@@ -304,7 +311,7 @@ constexpr int kMfmaRing = 2;   // key steps in flight per wave (three: the same 
 constexpr int kMfmaTiles = 2;  // 16-row query tiles per wave
 constexpr int kMfmaRows = 16 * kMfmaTiles * 4;  // query rows per workgroup
 
-__global__ void __launch_bounds__(256, 2) k_qsa_score_mfma(QsaShape sh, const float* __restrict__ qr,
+__global__ void __launch_bounds__(256, 2) k_qsa_score_mfma(QsaShape sh, const uint16_t* __restrict__ qr,
                                                         const int2* __restrict__ info, int64_t rows,
                                                         const uint16_t* __restrict__ kbar,
                                                         float* __restrict__ scores, int64_t ld_s) {
@@ -340,9 +347,7 @@ __global__ void __launch_bounds__(256, 2) k_qsa_score_mfma(QsaShape sh, const fl
     for (int h = 0; h < kQsaHeads; ++h)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const float* p = qr + row[tt] * (kQsaHeads * kQsaD) + h * kQsaD + 32 * ks + 8 * lq;
-        const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
-        a[tt][h][ks] = pack8(f32x4{x0.x, x0.y, x0.z, x0.w}, f32x4{x1.x, x1.y, x1.z, x1.w});
+        a[tt][h][ks] = ld_short8(qr + row[tt] * (kQsaHeads * kQsaD) + h * kQsaD + 32 * ks + 8 * lq);
       }
   float* const spare = scores + rows * ld_s + 4 * lq;
 
@@ -802,8 +807,8 @@ hipError_t launch_qsa_rows(const QsaShape& sh, const QsaWs& ws, int64_t row0, in
       hipLaunchKernelGGL(k_qsa_score_mfma,
                          dim3(static_cast<unsigned>((rows + kMfmaRows - 1) / kMfmaRows),
                               static_cast<unsigned>((sh.cap + kMfmaChunk - 1) / kMfmaChunk)),
-                         dim3(256), 0, s, sh, ws.qr, ws.info, rows, static_cast<const uint16_t*>(kbar), ws.scores,
-                         ws.ld_s);
+                         dim3(256), 0, s, sh, reinterpret_cast<const uint16_t*>(ws.qr), ws.info, rows,
+                         static_cast<const uint16_t*>(kbar), ws.scores, ws.ld_s);
     else if (sh.bf16)
       hipLaunchKernelGGL(k_qsa_score<bf16>, sgrid, dim3(256), 0, s, sh, ws.qr, ws.info,
                          static_cast<const bf16*>(kbar), ws.scores, ws.ld_s);
