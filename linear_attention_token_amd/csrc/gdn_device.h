@@ -149,6 +149,41 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// The same sums without LDS traffic (group_sum's shuffles become ds_bpermute on this target):
+// rotations inside each 16-lane row by DPP (row_ror 8, 4, 2, 1 leave every lane of the row with the
+// row's sum), then gfx950's row swaps add row pairs (v_permlane16_swap: rows 0+1 and 2+3) and the two
+// wave halves (v_permlane32_swap). Each step adds a lane's value to its partner's, so every lane of a
+// group ends with bitwise the same sum.
+template <int ctrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+}
+// v + v of lane ^ 32 and v + v of lane ^ 16. The swaps are written as inline asm on two copies of v:
+// this compiler folds the two results of its permlane-swap builtins into one register when both
+// inputs are the same value (it then adds a result to itself). The s_nops cover the wait states
+// between a VALU write and a permlane read, and between the swap and the next read.
+__device__ __forceinline__ float half_pair_sum(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+__device__ __forceinline__ float row_pair_sum(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+template <int width>
+__device__ __forceinline__ float wave_sum(float v) {
+  static_assert(width == 16 || width == 32 || width == 64, "16, 32 or 64 lanes");
+  v += dpp_f32<0x128>(v);  // row_ror:8
+  v += dpp_f32<0x124>(v);  // row_ror:4
+  v += dpp_f32<0x122>(v);  // row_ror:2
+  v += dpp_f32<0x121>(v);  // row_ror:1
+  if (width >= 32) v = row_pair_sum(v);
+  if (width == 64) v = half_pair_sum(v);
+  return v;
+}
+
 // ---- direct global -> LDS loads with explicit waits ----------------------------------------------
 // The compiler's own wait insertion treats these loads conservatively (a full vmcnt(0) at barriers),
 // so they are issued from inline asm and waited for with explicit vmcnt counts.

@@ -273,12 +273,12 @@ __global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
   const float u = u_qk;
   // |q|^2 (waves 0, 1) and |k|^2 (waves 2, 3), then q.k
   {
-    const float ss = group_sum<64>(u * u);
+    const float ss = wave_sum<64>(u * u);
     if (lane == 0) nrm[w] = ss;
   }
   __syncthreads();
   if (t < kD) {
-    const float d = group_sum<64>(u * act[kD + t]);
+    const float d = wave_sum<64>(u * act[kD + t]);
     if (lane == 0) nrm[4 + w] = d;
   }
   __syncthreads();
@@ -303,10 +303,10 @@ __global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
       pa.x += S[j].x * ki; pa.y += S[j].y * ki; pa.z += S[j].z * ki; pa.w += S[j].w * ki;
       pb.x += S[j].x * qi; pb.y += S[j].y * qi; pb.z += S[j].z * qi; pb.w += S[j].w * qi;
     }
-    pa.x += __shfl_xor(pa.x, 32, 64); pa.y += __shfl_xor(pa.y, 32, 64);
-    pa.z += __shfl_xor(pa.z, 32, 64); pa.w += __shfl_xor(pa.w, 32, 64);
-    pb.x += __shfl_xor(pb.x, 32, 64); pb.y += __shfl_xor(pb.y, 32, 64);
-    pb.z += __shfl_xor(pb.z, 32, 64); pb.w += __shfl_xor(pb.w, 32, 64);
+    pa.x = half_pair_sum(pa.x); pa.y = half_pair_sum(pa.y);
+    pa.z = half_pair_sum(pa.z); pa.w = half_pair_sum(pa.w);
+    pb.x = half_pair_sum(pb.x); pb.y = half_pair_sum(pb.y);
+    pb.z = half_pair_sum(pb.z); pb.w = half_pair_sum(pb.w);
     float* const rb = red + (r & 1) * (8 * kD);  // two buffers: one barrier per head suffices
     if (lane < 32) {
       *reinterpret_cast<float4*>(&rb[(2 * w) * kD + col]) = pa;
@@ -344,7 +344,7 @@ __global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
     for (int j = 0; j < 16; ++j) S[j] = N[j];
     // RMSNorm over the head's 128 outputs (every row group holds them all), gain, gate; wave w
     // stores channel col + w of each column group (its two row groups write the same values)
-    const float ss = group_sum<32>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
+    const float ss = wave_sum<32>(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
     const float rs = (a.flags & GDN_NORM) ? 1.0f / sqrtf(ss / float(kD) + a.norm_eps) : 1.0f;
     const float yw = w == 0 ? y[0] : w == 1 ? y[1] : w == 2 ? y[2] : y[3];
     float o = yw * rs * nwsh[r * kD + col + w];

@@ -120,11 +120,6 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
   const float* const S0 = a.state_in + (size_t(b) * a.hv + size_t(g) * R) * head;
   const int soff = (rg * kD + col) * 4;  // row j of this thread: soff + 4096 j bytes into the head
   float4 S[16], N[16];
-  {
-    const auto rs = buf_rsrc(S0, int(head * 4));
-#pragma unroll
-    for (int j = 0; j < 16; ++j) S[j] = buf_ld16_nt(rs, soff, 4096 * j);
-  }
 
   // ---- inputs of the group, all requested together as 16-byte pieces: the drafts' raw q | k | v
   // rows (into act, and copied to the log for the commit), the conv cache rows, the gate logits;
@@ -134,29 +129,29 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
   constexpr int VEC = vec16<IO>::N;     // io elements per piece
   const int prow = nch / VEC, pv = nv / VEC;
   const int n_raw = K * prow, n_cache = conv ? 3 * prow : 0, n_all = n_raw + n_cache + (gate ? K * pv : 0);
+  // Conv weights and gains come through buffer ranges that are empty when the flag is off (zeros,
+  // no memory access), so every load is unconditional and none waits before the next is issued.
   float4 cw[3];
+  {
+    const auto rw = buf_rsrc(a.conv_w, conv ? int(a.C * 16) : 0);
 #pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int c = min(t + 256 * u, nch - 1);
-    cw[u] = conv ? reinterpret_cast<const float4*>(a.conv_w)[group_channel(c, g, R, a.hk)] : make_float4(0.f, 0.f, 0.f, 1.f);
+    for (int u = 0; u < 3; ++u) cw[u] = buf_ld16(rw, int(group_channel(min(t + 256 * u, nch - 1), g, R, a.hk)) * 16, 0);
   }
-  for (int i = t; i < nv / 4; i += 256) {
-    float4 nw = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a.flags & GDN_NORM)
-      nw = *reinterpret_cast<const float4*>(a.norm_w + size_t(g * R + (4 * i) / kD) * a.norm_stride + (4 * i) % kD);
-    *reinterpret_cast<float4*>(nwsh + 4 * i) = make_float4(1.f + nw.x, 1.f + nw.y, 1.f + nw.z, 1.f + nw.w);
-  }
-  for (int i = t; i < 2 * R * K; i += 256) {
-    const int tt = i / (2 * R), j = i - tt * 2 * R, r = j < R ? j : j - R;
-    const int64_t ix = (row0 + tt) * a.hv + int64_t(g) * R + r;
-    const float val = (j < R ? a.alpha : a.beta)[ix];
-    absh[i] = val;
-    a.log.ab[ix * 2 + (j < R ? 0 : 1)] = val;
-  }
-  for (int base = 0; base < n_all; base += 4 * 256) {
-    uint4 pc[4];
+  const auto rn = buf_rsrc(a.norm_w, (a.flags & GDN_NORM) ? int((size_t(a.hv - 1) * a.norm_stride + kD) * 4) : 0);
+  auto gain_off = [&](int i) { return int(size_t(g * R + (4 * i) / kD) * a.norm_stride + (4 * i) % kD) * 4; };
+  auto ab_ix = [&](int i, bool& is_alpha) {
+    const int tt = i / (2 * R), j = i - tt * 2 * R;
+    is_alpha = j < R;
+    return (row0 + tt) * a.hv + int64_t(g) * R + (j < R ? j : j - R);
+  };
+  const int i_ab = min(t, 2 * R * K - 1);
+  bool ab_alpha;
+  const int64_t ix_ab = ab_ix(i_ab, ab_alpha);
+  const float4 nw0 = buf_ld16(rn, gain_off(min(t, nv / 4 - 1)), 0);
+  const float ab0 = (ab_alpha ? a.alpha : a.beta)[ix_ab];
+  auto issue_pieces = [&](int base, uint4 (&pc)[4]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // issue up to four pieces per thread before using any
+    for (int u = 0; u < 4; ++u) {  // up to four pieces per thread are requested before any is used
       const int i = base + u * 256 + t;
       pc[u] = make_uint4(0u, 0u, 0u, 0u);
       if (i < n_raw) {
@@ -174,6 +169,8 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
         pc[u] = *reinterpret_cast<const uint4*>(static_cast<const IO*>(a.gate) + ((row0 + tt) * a.hv + int64_t(g) * R) * kD + c0);
       }
     }
+  };
+  auto place_pieces = [&](int base, const uint4 (&pc)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = base + u * 256 + t;
@@ -195,6 +192,44 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
     }
+  };
+  // the first 1024 pieces in straight-line code, so their loads share one wait with the loads above
+  {
+    uint4 pc[4];
+    issue_pieces(0, pc);
+    place_pieces(0, pc);
+  }
+  for (int base = 4 * 256; base < n_all; base += 4 * 256) {
+    uint4 pc[4];
+    issue_pieces(base, pc);
+    place_pieces(base, pc);
+  }
+  if (t < nv / 4) *reinterpret_cast<float4*>(nwsh + 4 * t) = make_float4(1.f + nw0.x, 1.f + nw0.y, 1.f + nw0.z, 1.f + nw0.w);
+  if (t < 2 * R * K) {
+    absh[t] = ab0;
+    a.log.ab[ix_ab * 2 + (ab_alpha ? 0 : 1)] = ab0;
+  }
+  for (int i = t + 256; i < nv / 4; i += 256) {
+    const float4 nw = buf_ld16(rn, gain_off(i), 0);
+    *reinterpret_cast<float4*>(nwsh + 4 * i) = make_float4(1.f + nw.x, 1.f + nw.y, 1.f + nw.z, 1.f + nw.w);
+  }
+  for (int i = t + 256; i < 2 * R * K; i += 256) {
+    bool al;
+    const int64_t ix = ab_ix(i, al);
+    const float val = (al ? a.alpha : a.beta)[ix];
+    absh[i] = val;
+    a.log.ab[ix * 2 + (al ? 0 : 1)] = val;
+  }
+  // The first head's state is requested only now: loads complete in order, so had it been
+  // requested first, every input of the prologue would have waited for its 64 KB. The conv weights
+  // are marked ready here (an empty asm that takes them), so that no later use of them waits on the
+  // state.
+#pragma unroll
+  for (int u = 0; u < 3; ++u) asm volatile("" : "+v"(cw[u].x), "+v"(cw[u].y), "+v"(cw[u].z), "+v"(cw[u].w));
+  {
+    const auto rs = buf_rsrc(S0, int(head * 4));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) S[j] = buf_ld16_nt(rs, soff, 4096 * j);
   }
   __syncthreads();
   // conv + SiLU in place, one channel column per thread (tap 3 on the current token)
@@ -224,7 +259,7 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
     float* const aq = act + tt * nch;
     float* const ak = aq + kD;
     const float q0 = aq[2 * lane], q1 = aq[2 * lane + 1], k0 = ak[2 * lane], k1 = ak[2 * lane + 1];
-    const float sq = group_sum<64>(q0 * q0 + q1 * q1), sk = group_sum<64>(k0 * k0 + k1 * k1);
+    const float sq = wave_sum<64>(q0 * q0 + q1 * q1), sk = wave_sum<64>(k0 * k0 + k1 * k1);
     const float rq = l2 ? 1.0f / sqrtf(sq + a.l2_eps) : 1.0f, rk = l2 ? 1.0f / sqrtf(sk + a.l2_eps) : 1.0f;
     const float kh0 = k0 * rk, kh1 = k1 * rk;
     aq[2 * lane] = q0 * rq;
@@ -247,7 +282,7 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
     if (i > tt || (!isq && i == tt)) continue;  // wave-uniform
     const float* const x = act + tt * nch + (isq ? 0 : kD);
     const float* const y = act + i * nch + kD;
-    const float d = group_sum<64>(x[2 * lane] * y[2 * lane] + x[2 * lane + 1] * y[2 * lane + 1]);
+    const float d = wave_sum<64>(x[2 * lane] * y[2 * lane] + x[2 * lane + 1] * y[2 * lane + 1]);
     if (lane == 0) (isq ? dqk : dkk)[tt * K + i] = d;
   }
   __syncthreads();
@@ -280,10 +315,10 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
         pa.x += S[j].x * ki; pa.y += S[j].y * ki; pa.z += S[j].z * ki; pa.w += S[j].w * ki;
         pb.x += S[j].x * qi; pb.y += S[j].y * qi; pb.z += S[j].z * qi; pb.w += S[j].w * qi;
       }
-      pa.x += __shfl_xor(pa.x, 32, 64); pa.y += __shfl_xor(pa.y, 32, 64);
-      pa.z += __shfl_xor(pa.z, 32, 64); pa.w += __shfl_xor(pa.w, 32, 64);
-      pb.x += __shfl_xor(pb.x, 32, 64); pb.y += __shfl_xor(pb.y, 32, 64);
-      pb.z += __shfl_xor(pb.z, 32, 64); pb.w += __shfl_xor(pb.w, 32, 64);
+      pa.x = half_pair_sum(pa.x); pa.y = half_pair_sum(pa.y);
+      pa.z = half_pair_sum(pa.z); pa.w = half_pair_sum(pa.w);
+      pb.x = half_pair_sum(pb.x); pb.y = half_pair_sum(pb.y);
+      pb.z = half_pair_sum(pb.z); pb.w = half_pair_sum(pb.w);
       if (lane < 32) {
         *reinterpret_cast<float4*>(&red[((tt * 2) * 4 + w) * kD + col]) = pa;
         *reinterpret_cast<float4*>(&red[((tt * 2 + 1) * 4 + w) * kD + col]) = pb;
@@ -319,7 +354,7 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
 #pragma unroll
     for (int tt = 0; tt < kMaxDrafts; ++tt)
       if (tt < K) {
-        const float ss = group_sum<64>(y[tt] * y[tt]);
+        const float ss = wave_sum<64>(y[tt] * y[tt]);
         if (lane == 0) ssr[w * K + tt] = ss;
       }
     __syncthreads();
