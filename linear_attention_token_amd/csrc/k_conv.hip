@@ -201,7 +201,13 @@ __global__ void __launch_bounds__(256) k_conv(ConvArgs a) {
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) ss += y[e] * y[e];
-      for (int o = width >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+      if (width == 16) {  // a q/k head of 128 channels in one DPP row (bf16 pieces)
+        ss = wave_sum<16>(ss);
+      } else if (width == 32) {  // fp32 pieces: two rows
+        ss = wave_sum<32>(ss);
+      } else {
+        for (int o = width >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+      }
       if (isqk) {
         const float r = 1.0f / sqrtf(ss + a.l2_eps);
 #pragma unroll

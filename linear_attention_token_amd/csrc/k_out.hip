@@ -171,8 +171,7 @@ __global__ void __launch_bounds__(256, 4) k_out(OutArgs a, ConvTailArgs tail) {
         acc[tt][nt][r] *= a.scale;
         ss += acc[tt][nt][r] * acc[tt][nt][r];
       }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ss = half_pair_sum(row_pair_sum(ss));
     if (lq == 0) red[w][16 * tt + li] = ss;
   }
   __syncthreads();  // every wave is past its last read of Q and P

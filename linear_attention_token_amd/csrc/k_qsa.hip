@@ -102,7 +102,7 @@ __device__ __forceinline__ void finish_block(float (&y)[8], const float (&w)[8],
     y[i] *= 0.25f;
     ss += y[i] * y[i];
   }
-  ss = group_sum<16>(ss);
+  ss = wave_sum<16>(ss);
   const float r = 1.0f / sqrtf(ss * (1.0f / kQsaD) + eps);
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] *= r * w[i];
@@ -228,19 +228,23 @@ __device__ __forceinline__ int64_t row_blocks(int pos, int64_t cap) {
 
 // Sum over the 4 heads of ReLU(dot) for one compressed key: p[h] are a lane's partial dots over its
 // 8 dims. The heads are spread over the lanes while being reduced (lane bits 3, 2 pick the head), so
-// the whole reduction takes 7 shuffles instead of 16.
+// the whole reduction takes 7 lane exchanges instead of 16. The exchanges stay inside the key's 16
+// lanes (one DPP row), so they are DPP moves: lane ^ 8 is a rotation by 8; lane ^ 4 is a rotation
+// by 4 (lanes with bit 2 set, reading lane - 4) or by 12 (reading lane + 4); lane ^ 2 and lane ^ 1
+// are quad permutations; the last two sums add the four quads by rotations.
 __device__ __forceinline__ float head_relu_sum(const float (&p)[4], int m) {
   const bool b3 = m & 8, b2 = m & 4;
-  const float r0 = __shfl_xor(b3 ? p[0] : p[2], 8, kWave);
-  const float r1 = __shfl_xor(b3 ? p[1] : p[3], 8, kWave);
+  const float r0 = dpp_f32<0x128>(b3 ? p[0] : p[2]);  // lane ^ 8
+  const float r1 = dpp_f32<0x128>(b3 ? p[1] : p[3]);
   const float k0 = (b3 ? p[2] : p[0]) + r0, k1 = (b3 ? p[3] : p[1]) + r1;  // heads 2 b3, 2 b3 + 1
-  const float r = __shfl_xor(b2 ? k0 : k1, 4, kWave);
-  float v = (b2 ? k1 : k0) + r;  // head 2 b3 + b2, summed over 4 lanes
-  v += __shfl_xor(v, 2, kWave);
-  v += __shfl_xor(v, 1, kWave);
+  const float x = b2 ? k0 : k1;
+  const float r4 = dpp_f32<0x124>(x), r12 = dpp_f32<0x12C>(x);
+  float v = (b2 ? k1 : k0) + (b2 ? r4 : r12);  // head 2 b3 + b2, summed over 4 lanes
+  v += dpp_f32<0x4E>(v);  // quad_perm [2, 3, 0, 1]: lane ^ 2
+  v += dpp_f32<0xB1>(v);  // quad_perm [1, 0, 3, 2]: lane ^ 1
   v = fmaxf(v, 0.f);
-  v += __shfl_xor(v, 4, kWave);
-  v += __shfl_xor(v, 8, kWave);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x128>(v);
   return v;
 }
 
