@@ -198,11 +198,6 @@ __global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
   float* const S0 = a.state + (size_t(b) * a.hv + size_t(g) * R) * head;
   const int soff = (rg * kD + col) * 4;  // row j of this thread: soff + 4096 j bytes into the head
   float4 S[16], N[16];  // this head's state and the next head's, in flight meanwhile
-  {
-    const auto rs = buf_rsrc(S0, int(head * 4));
-#pragma unroll
-    for (int j = 0; j < 16; ++j) S[j] = buf_ld16(rs, soff, 4096 * j);
-  }
 
   // ---- conv + SiLU of the group's channels (single writer of their cache) and the group's gate
   // logits. A pass covers 768 channels (all of them for up to 4 value heads per group) and issues
@@ -220,6 +215,16 @@ __global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
   float gv[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) gv[u] = io<IO>::ld(gsrc + min(t + 256 * u, nv - 1));
+  // gains (through a buffer range that is empty without the norm: zeros, no memory access) and
+  // alpha | beta of the group, requested with the conv pass
+  const auto rnw = buf_rsrc(a.norm_w, (a.flags & GDN_NORM) ? int((size_t(a.hv - 1) * a.norm_stride + kD) * 4) : 0);
+  auto gain_off = [&](int c) { return int(size_t(g * R + c / kD) * a.norm_stride + c % kD) * 4; };
+  float nwv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    nwv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rnw, gain_off(min(t + 256 * u, nv - 1)), 0, 0));
+  const int iab = min(t, 2 * R - 1);
+  const float abv = (iab < R ? a.alpha : a.beta)[size_t(b) * a.hv + g * R + (iab < R ? iab : iab - R)];
   float u_qk = 0.f;  // this thread's q (t < 128) or k channel after conv + SiLU
   for (int c0 = 0; c0 < nch; c0 += 768) {
     float x[3], h[3][3];
@@ -244,6 +249,12 @@ __global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
       cw[u] = conv ? reinterpret_cast<const float4*>(a.conv_w)[gcs[u]] : *reinterpret_cast<const float4*>(S0);
     }
     asm volatile("" ::: "memory");  // keeps the loads above from being sunk into the branches below
+    if (c0 == 0) {  // the first head's state, requested after the first pass's inputs: loads complete
+                    // in order, so requested first it would hold up every input of the prologue
+      const auto rs = buf_rsrc(S0, int(head * 4));
+#pragma unroll
+      for (int j = 0; j < 16; ++j) S[j] = buf_ld16(rs, soff, 4096 * j);
+    }
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int c = c0 + t + 256 * u;
@@ -267,9 +278,12 @@ __global__ void __launch_bounds__(256, 3) k_decode_d128(DecodeArgs a) {
       if (t + 256 * u < nv) gsh[t + 256 * u] = gv[u];
     for (int c = t + 512; c < nv; c += 256) gsh[c] = io<IO>::ld(gsrc + c);
   }
-  for (int c = t; c < nv; c += 256)
-    nwsh[c] = 1.0f + ((a.flags & GDN_NORM) ? a.norm_w[size_t(g * R + c / kD) * a.norm_stride + c % kD] : 0.f);
-  for (int c = t; c < 2 * R; c += 256) absh[c] = (c < R ? a.alpha : a.beta)[size_t(b) * a.hv + g * R + (c < R ? c : c - R)];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (t + 256 * u < nv) nwsh[t + 256 * u] = 1.0f + nwv[u];
+  for (int c = t + 512; c < nv; c += 256)
+    nwsh[c] = 1.0f + __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rnw, gain_off(c), 0, 0));
+  if (t < 2 * R) absh[t] = abv;
   const float u = u_qk;
   // |q|^2 (waves 0, 1) and |k|^2 (waves 2, 3), then q.k
   {
