@@ -15,12 +15,13 @@
 // the raw conv inputs -- and commit applies the first n of them, in order, to the stored state.
 // Verify reads each state once and writes none; commit reads and writes it once.
 //
-// Both kernels run one 256-thread block per (sequence, QK group) with the register layout of the
-// decode step: thread (cg, rg) = (t % 32, t / 32) holds columns 4cg .. +3 of rows rg + 8j (j < 16)
-// of a head's state. The next head's state is prefetched (non-temporal) while the current one is
-// worked on -- after the last head through an empty buffer range, which reads zeros without
-// touching memory -- and every wave issues the same memory instructions per head, so the waits for
-// the prefetch are exact counts that leave earlier stores in flight.
+// Verify runs one 256-thread block per (sequence, value head), commit one per (sequence, QK group);
+// both use the register layout of the decode step: thread (cg, rg) = (t % 32, t / 32) holds columns
+// 4cg .. +3 of rows rg + 8j (j < 16) of a head's state. Commit prefetches the next head's state
+// (non-temporal) while the current one is worked on -- after the last head through an empty buffer
+// range, which reads zeros without touching memory -- and every wave issues the same memory
+// instructions per head, so the waits for the prefetch are exact counts that leave earlier stores in
+// flight.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -63,6 +64,15 @@ __device__ __forceinline__ int64_t group_channel(int c, int g, int R, int hk) {
   return 2 * qk_ch + int64_t(g) * R * kD + (c - 2 * kD);
 }
 
+// Conv channel of channel c of a block serving QK group g and value heads from h0 on: its q head,
+// its k head, then its value heads.
+__device__ __forceinline__ int64_t block_channel(int c, int g, int h0, int hk) {
+  const int64_t qk_ch = int64_t(hk) * kD;
+  if (c < kD) return int64_t(g) * kD + c;
+  if (c < 2 * kD) return qk_ch + int64_t(g) * kD + (c - kD);
+  return 2 * qk_ch + int64_t(h0) * kD + (c - 2 * kD);
+}
+
 // LDS layout of the verify kernel (offsets in floats, every region 16-byte aligned).
 struct VerifyLds {
   int act, cst, gsh, nwsh, absh, Gh, cA, cB, dkk, dqk, red, ssr, total;
@@ -71,8 +81,7 @@ __host__ __device__ inline VerifyLds verify_lds(int K, int R) {
   auto pad = [](int n) { return (n + 3) & ~3; };
   VerifyLds L;
   L.act = 0;                                   // [K][(2 + R) 128]
-  L.cst = L.act + K * (2 + R) * kD;            // [3][(2 + R) 128] conv cache rows
-  L.gsh = L.cst + 3 * (2 + R) * kD;            // [K][R 128]
+  L.gsh = L.act + K * (2 + R) * kD;            // [K][R 128]
   L.nwsh = L.gsh + K * R * kD;                 // [R 128]
   L.absh = L.nwsh + R * kD;                    // [K][2R]
   L.Gh = L.absh + pad(2 * R * K);              // [R][K]
@@ -81,7 +90,8 @@ __host__ __device__ inline VerifyLds verify_lds(int K, int R) {
   L.dkk = L.cB + pad(R * K * K);               // [K][K]
   L.dqk = L.dkk + pad(K * K);                  // [K][K]
   L.red = L.dqk + pad(K * K);                  // [K][2][4][128]
-  L.ssr = L.red + K * 2 * 4 * kD;              // [4][K]
+  L.cst = L.red;                               // [3][(2 + R) 128], read only by the conv, before red is used
+  L.ssr = L.red + (K * 2 * 4 * kD > 3 * (2 + R) * kD ? K * 2 * 4 * kD : 3 * (2 + R) * kD);  // [4][K]
   L.total = L.ssr + pad(4 * K);
   return L;
 }
@@ -95,13 +105,22 @@ size_t commit_smem_floats(int K, int R) { return size_t(K) * kD + size_t(K) * R 
 //   y_t = gamma_t S0^T q_t + sum_{i<=t} exp(G_t - G_i) (q_t.k_i) beta_i e_i.
 // So a head needs one pass over S0 for the 2K products S0^T k_t, S0^T q_t (one barrier), then a
 // K-step recurrence that is independent per column, instead of K dependent steps.
+//
+// One block per (sequence, value head): the q | k prologue of a QK group is computed by each of its
+// value heads' blocks, but no block carries a second state in registers (88 VGPRs, 31 KB of LDS at
+// K = 5), so five blocks fit on a CU and their state loads overlap each other's prologues. (One
+// block per QK group walking its three value heads with the next head's state prefetched held two
+// states in registers, three blocks per CU: 210-215 us against 200 us at B = 256, K = 5.)
 template <typename IO>
-__global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
+__global__ void __launch_bounds__(256, 5) k_verify_d128(MtpArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  const int b = int(blockIdx.x / unsigned(a.hk)), g = int(blockIdx.x - unsigned(b) * unsigned(a.hk));
+  const int b = int(blockIdx.x / unsigned(a.hv)), h0 = int(blockIdx.x - unsigned(b) * unsigned(a.hv));
+  const int g = h0 / a.R;                  // QK group
+  const bool lead = h0 % a.R == 0;         // the block that logs the group's k^ and raw q | k
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int cg = t & 31, rg = t >> 5, col = 4 * cg;
-  const int R = a.R, K = a.K, nch = (2 + R) * kD, nv = R * kD;
+  constexpr int R = 1;                     // value heads of the block
+  const int K = a.K, nch = (2 + R) * kD, nv = R * kD;
   const VerifyLds L = verify_lds(K, R);
   float* const act = smem + L.act;    // [K][nch]: q^ | k^ | v^ of each draft token
   float* const cst = smem + L.cst;    // [3][nch] conv cache rows
@@ -117,9 +136,9 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
   float* const ssr = smem + L.ssr;    // [4 waves][K] partial sums of squares
 
   const size_t head = size_t(kD) * kD;
-  const float* const S0 = a.state_in + (size_t(b) * a.hv + size_t(g) * R) * head;
+  const float* const S0 = a.state_in + (size_t(b) * a.hv + size_t(h0)) * head;
   const int soff = (rg * kD + col) * 4;  // row j of this thread: soff + 4096 j bytes into the head
-  float4 S[16], N[16];
+  float4 S[16];
 
   // ---- inputs of the group, all requested together as 16-byte pieces: the drafts' raw q | k | v
   // rows (into act, and copied to the log for the commit), the conv cache rows, the gate logits;
@@ -135,14 +154,14 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
   {
     const auto rw = buf_rsrc(a.conv_w, conv ? int(a.C * 16) : 0);
 #pragma unroll
-    for (int u = 0; u < 3; ++u) cw[u] = buf_ld16(rw, int(group_channel(min(t + 256 * u, nch - 1), g, R, a.hk)) * 16, 0);
+    for (int u = 0; u < 3; ++u) cw[u] = buf_ld16(rw, int(block_channel(min(t + 256 * u, nch - 1), g, h0, a.hk)) * 16, 0);
   }
   const auto rn = buf_rsrc(a.norm_w, (a.flags & GDN_NORM) ? int((size_t(a.hv - 1) * a.norm_stride + kD) * 4) : 0);
-  auto gain_off = [&](int i) { return int(size_t(g * R + (4 * i) / kD) * a.norm_stride + (4 * i) % kD) * 4; };
+  auto gain_off = [&](int i) { return int(size_t(h0 + (4 * i) / kD) * a.norm_stride + (4 * i) % kD) * 4; };
   auto ab_ix = [&](int i, bool& is_alpha) {
     const int tt = i / (2 * R), j = i - tt * 2 * R;
     is_alpha = j < R;
-    return (row0 + tt) * a.hv + int64_t(g) * R + (j < R ? j : j - R);
+    return (row0 + tt) * a.hv + int64_t(h0) + (j < R ? j : j - R);
   };
   const int i_ab = min(t, 2 * R * K - 1);
   bool ab_alpha;
@@ -158,15 +177,15 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
         const int tt = i / prow, c0 = (i - tt * prow) * VEC;
         const IO* src = c0 < kD ? static_cast<const IO*>(a.q) + (row0 + tt) * a.ld_q + int64_t(g) * kD + c0
                       : c0 < 2 * kD ? static_cast<const IO*>(a.k) + (row0 + tt) * a.ld_k + int64_t(g) * kD + (c0 - kD)
-                                    : static_cast<const IO*>(a.v) + (row0 + tt) * a.ld_v + int64_t(g) * nv + (c0 - 2 * kD);
+                                    : static_cast<const IO*>(a.v) + (row0 + tt) * a.ld_v + int64_t(h0) * kD + (c0 - 2 * kD);
         pc[u] = *reinterpret_cast<const uint4*>(src);
       } else if (i < n_raw + n_cache) {
         const int j = (i - n_raw) / prow, c0 = (i - n_raw - j * prow) * VEC;
         pc[u] = *reinterpret_cast<const uint4*>(static_cast<const IO*>(a.conv_in) + (int64_t(b) * 3 + j) * a.C +
-                                                group_channel(c0, g, R, a.hk));
+                                                block_channel(c0, g, h0, a.hk));
       } else if (i < n_all) {
         const int i2 = i - n_raw - n_cache, tt = i2 / pv, c0 = (i2 - tt * pv) * VEC;
-        pc[u] = *reinterpret_cast<const uint4*>(static_cast<const IO*>(a.gate) + ((row0 + tt) * a.hv + int64_t(g) * R) * kD + c0);
+        pc[u] = *reinterpret_cast<const uint4*>(static_cast<const IO*>(a.gate) + ((row0 + tt) * a.hv + int64_t(h0)) * kD + c0);
       }
     }
   };
@@ -181,7 +200,7 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
       if (i < n_raw) {
         const int tt = i / prow, c0 = (i - tt * prow) * VEC;
         dst = act + tt * nch + c0;
-        if (conv) *reinterpret_cast<uint4*>(static_cast<IO*>(a.log.raw) + (row0 + tt) * a.C + group_channel(c0, g, R, a.hk)) = pc[u];
+        if (conv && (lead || c0 >= 2 * kD)) *reinterpret_cast<uint4*>(static_cast<IO*>(a.log.raw) + (row0 + tt) * a.C + block_channel(c0, g, h0, a.hk)) = pc[u];
       } else if (i < n_raw + n_cache) {
         const int j = (i - n_raw) / prow, c0 = (i - n_raw - j * prow) * VEC;
         dst = cst + j * nch + c0;
@@ -266,7 +285,7 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
     aq[2 * lane + 1] = q1 * rq;
     ak[2 * lane] = kh0;
     ak[2 * lane + 1] = kh1;
-    *reinterpret_cast<float2*>(a.log.kh + ((row0 + tt) * a.hk + g) * kD + 2 * lane) = make_float2(kh0, kh1);
+    if (lead) *reinterpret_cast<float2*>(a.log.kh + ((row0 + tt) * a.hk + g) * kD + 2 * lane) = make_float2(kh0, kh1);
   }
   if (t < R) {
     float gsum = 0.f;
@@ -294,16 +313,11 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
   }
   __syncthreads();
 
-  // ---- value heads in turn ----
+  // ---- the value head ----
   const int c = t & (kD - 1);  // column of the per-column phase
   const bool store_e = t < kD;  // threads 0..127 log e, threads 128..255 store the outputs
   for (int r = 0; r < R; ++r) {
-    const int h = g * R + r;
-    {  // the next head's state; after the last head an empty range (zeros, no memory access)
-      const auto rn = buf_rsrc(S0 + size_t(r + 1 < R ? r + 1 : r) * head, r + 1 < R ? int(head * 4) : 0);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) N[j] = buf_ld16_nt(rn, soff, 4096 * j);
-    }
+    const int h = h0 + r;
     // S0^T k_t and S0^T q_t of every draft token over this thread's rows, then over row-group pairs
     for (int tt = 0; tt < K; ++tt) {
       const float* const aq = act + tt * nch;
@@ -371,8 +385,6 @@ __global__ void __launch_bounds__(256, 3) k_verify_d128(MtpArgs a) {
           io<IO>::st(static_cast<IO*>(a.out) + ((row0 + tt) * a.hv + h) * kD + c, o);
         }
       }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) S[j] = N[j];
   }
 }
 
@@ -477,8 +489,8 @@ hipError_t launch_verify(const Problem& p, int batch, int n_tok, const void* q, 
   MtpArgs a{n_tok, p.hk, p.hv, R, p.C, q, k, v, ld_q, ld_k, ld_v, alpha, beta, gate, conv_w, norm_w,
             p.norm_stride, conv_state, nullptr, state, nullptr, out, log, nullptr, p.flags, p.scale,
             p.l2_eps, p.norm_eps};
-  const size_t smem = verify_smem_floats(n_tok, R) * 4;
-  const dim3 grid(unsigned(batch) * unsigned(p.hk));
+  const size_t smem = verify_smem_floats(n_tok, 1) * 4;
+  const dim3 grid(unsigned(batch) * unsigned(p.hv));
   if (p.bf16) hipLaunchKernelGGL(k_verify_d128<bf16>, grid, dim3(256), smem, s, a);
   else hipLaunchKernelGGL(k_verify_d128<float>, grid, dim3(256), smem, s, a);
   return hipGetLastError();
