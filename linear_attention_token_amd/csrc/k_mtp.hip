@@ -15,13 +15,9 @@
 // the raw conv inputs -- and commit applies the first n of them, in order, to the stored state.
 // Verify reads each state once and writes none; commit reads and writes it once.
 //
-// Verify runs one 256-thread block per (sequence, value head), commit one per (sequence, QK group);
-// both use the register layout of the decode step: thread (cg, rg) = (t % 32, t / 32) holds columns
-// 4cg .. +3 of rows rg + 8j (j < 16) of a head's state. Commit prefetches the next head's state
-// (non-temporal) while the current one is worked on -- after the last head through an empty buffer
-// range, which reads zeros without touching memory -- and every wave issues the same memory
-// instructions per head, so the waits for the prefetch are exact counts that leave earlier stores in
-// flight.
+// Both kernels run one 256-thread block per (sequence, value head) with the register layout of the
+// decode step: thread (cg, rg) = (t % 32, t / 32) holds columns 4cg .. +3 of rows rg + 8j (j < 16)
+// of the head's state.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -53,15 +49,6 @@ struct MtpArgs {
 __device__ __forceinline__ float4 rank1(const float4& s, float al, float bk, const float4& e) {
   return make_float4(fmaf(bk, e.x, al * s.x), fmaf(bk, e.y, al * s.y), fmaf(bk, e.z, al * s.z),
                      fmaf(bk, e.w, al * s.w));
-}
-
-// Conv channel index (q, then k, then v channels of all heads) of channel c of QK group g, where a
-// group's channels are its q head, its k head and its R value heads.
-__device__ __forceinline__ int64_t group_channel(int c, int g, int R, int hk) {
-  const int64_t qk_ch = int64_t(hk) * kD;
-  if (c < kD) return int64_t(g) * kD + c;
-  if (c < 2 * kD) return qk_ch + int64_t(g) * kD + (c - kD);
-  return 2 * qk_ch + int64_t(g) * R * kD + (c - 2 * kD);
 }
 
 // Conv channel of channel c of a block serving QK group g and value heads from h0 on: its q head,
@@ -388,48 +375,46 @@ __global__ void __launch_bounds__(256, 5) k_verify_d128(MtpArgs a) {
   }
 }
 
+// Commit: one block per (sequence, value head), like verify (one state in registers, five blocks per
+// CU); the block of a group's first value head also rolls the group's q | k conv-cache channels, each
+// block its own value head's channels (each cache channel has one writer).
 template <typename IO>
-__global__ void __launch_bounds__(256, 3) k_commit_d128(MtpArgs a) {
+__global__ void __launch_bounds__(256, 5) k_commit_d128(MtpArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  // each XCD walks its own contiguous run of (sequence, group) items (301 -> 291 us at B = 256, K = 5;
-  // plain state loads, which help the decode step, made this kernel slower)
+  // each XCD walks its own contiguous run of (sequence, value head) items
   const unsigned item = xcd_range_item(blockIdx.x, gridDim.x);
-  const int b = int(item / unsigned(a.hk)), g = int(item - unsigned(b) * unsigned(a.hk));
+  const int b = int(item / unsigned(a.hv)), h0 = int(item - unsigned(b) * unsigned(a.hv));
+  const int g = h0 / a.R;
+  const bool lead = h0 % a.R == 0;
   const int t = threadIdx.x, cg = t & 31, rg = t >> 5, col = 4 * cg;
-  const int R = a.R, K = a.K, nch = (2 + R) * kD;
+  const int K = a.K;
   const int n = min(max(a.n_accept[b], 0), K);  // out-of-range counts are clamped
   if (n == 0) return;                           // nothing accepted: the cache stays as it is
   float* const kh = smem;                       // [n][128] k^ of the group's QK head
-  float* const es = kh + K * kD;                // [n][R][128] e of the group's value heads
-  float* const ab = es + K * R * kD;            // [n][R][alpha, beta]
+  float* const es = kh + K * kD;                // [n][128] e of the block's value head
+  float* const ab = es + K * kD;                // [n][alpha, beta]
   const int64_t row0 = int64_t(b) * K;
 
   const size_t head = size_t(kD) * kD;
-  float* const S0 = a.state + (size_t(b) * a.hv + size_t(g) * R) * head;
+  float* const Sp = a.state + (size_t(b) * a.hv + size_t(h0)) * head;
   const int soff = (rg * kD + col) * 4;
-  float4 S[16], N[16];
+  float4 S[16];
   {
-    const auto rs = buf_rsrc(S0, int(head * 4));
+    const auto rs = buf_rsrc(Sp, int(head * 4));
 #pragma unroll
     for (int j = 0; j < 16; ++j) S[j] = buf_ld16_nt(rs, soff, 4096 * j);
   }
   for (int i = t; i < n * kD; i += 256) {
-    const int tt = i / kD;
-    kh[i] = a.log.kh[((row0 + tt) * a.hk + g) * kD + (i - tt * kD)];
+    const int tt = i / kD, c = i - tt * kD;
+    kh[i] = a.log.kh[((row0 + tt) * a.hk + g) * kD + c];
+    es[i] = a.log.e[((row0 + tt) * a.hv + h0) * kD + c];
   }
-  for (int i = t; i < n * R * kD; i += 256) {
-    const int tt = i / (R * kD);
-    es[i] = a.log.e[((row0 + tt) * a.hv + int64_t(g) * R) * kD + (i - tt * R * kD)];
-  }
-  for (int i = t; i < n * 2 * R; i += 256) {
-    const int tt = i / (2 * R);
-    ab[i] = a.log.ab[((row0 + tt) * a.hv + int64_t(g) * R) * 2 + (i - tt * 2 * R)];
-  }
-  // conv cache: the last 3 of (cached inputs, accepted raw inputs), per channel of the group; each
-  // thread reads its channel's three new rows before writing any
+  for (int i = t; i < n * 2; i += 256) ab[i] = a.log.ab[((row0 + i / 2) * a.hv + h0) * 2 + (i & 1)];
+  // conv cache: the last 3 of (cached inputs, accepted raw inputs), per channel; each thread reads
+  // its channel's three new rows before writing any
   if (a.flags & GDN_CONV) {
-    for (int c = t; c < nch; c += 256) {
-      const int64_t gc = group_channel(c, g, R, a.hk);
+    for (int c = lead ? t : 2 * kD + t; c < 3 * kD; c += 256) {
+      const int64_t gc = block_channel(c, g, h0, a.hk);
       IO* const cs = static_cast<IO*>(a.conv_state) + int64_t(b) * 3 * a.C + gc;
       const IO* const rw = static_cast<const IO*>(a.log.raw) + row0 * a.C + gc;
       IO z[3];
@@ -441,25 +426,15 @@ __global__ void __launch_bounds__(256, 3) k_commit_d128(MtpArgs a) {
   }
   __syncthreads();
 
-  for (int r = 0; r < R; ++r) {
-    {  // the next head's state; after the last head an empty range (zeros, no memory access)
-      const auto rn = buf_rsrc(S0 + size_t(r + 1 < R ? r + 1 : r) * head, r + 1 < R ? int(head * 4) : 0);
+  for (int tt = 0; tt < n; ++tt) {
+    const float al = ab[2 * tt], be = ab[2 * tt + 1];
+    const float4 ev = *reinterpret_cast<const float4*>(&es[tt * kD + col]);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) N[j] = buf_ld16_nt(rn, soff, 4096 * j);
-    }
-    for (int tt = 0; tt < n; ++tt) {
-      const float al = ab[tt * 2 * R + 2 * r], be = ab[tt * 2 * R + 2 * r + 1];
-      const float4 ev = *reinterpret_cast<const float4*>(&es[(tt * R + r) * kD + col]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) S[j] = rank1(S[j], al, be * kh[tt * kD + rg + 8 * j], ev);
-    }
-    float* const Sp = S0 + size_t(r) * head;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      __builtin_nontemporal_store(__builtin_bit_cast(f32x4, S[j]), reinterpret_cast<f32x4*>(Sp + (rg + 8 * j) * kD + col));
-#pragma unroll
-    for (int j = 0; j < 16; ++j) S[j] = N[j];
+    for (int j = 0; j < 16; ++j) S[j] = rank1(S[j], al, be * kh[tt * kD + rg + 8 * j], ev);
   }
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    __builtin_nontemporal_store(__builtin_bit_cast(f32x4, S[j]), reinterpret_cast<f32x4*>(Sp + (rg + 8 * j) * kD + col));
 }
 
 MtpLog plan_mtp_log(const Problem& p, int batch, int n_tok, void* base) {
@@ -503,8 +478,8 @@ hipError_t launch_commit(const Problem& p, int batch, int n_tok, const int32_t* 
   MtpArgs a{n_tok, p.hk, p.hv, R, p.C, nullptr, nullptr, nullptr, 0, 0, 0, nullptr, nullptr, nullptr,
             nullptr, nullptr, p.norm_stride, nullptr, conv_state, nullptr, state, nullptr, log, n_accept,
             p.flags, p.scale, p.l2_eps, p.norm_eps};
-  const size_t smem = commit_smem_floats(n_tok, R) * 4;
-  const dim3 grid(unsigned(batch) * unsigned(p.hk));
+  const size_t smem = commit_smem_floats(n_tok, 1) * 4;
+  const dim3 grid(unsigned(batch) * unsigned(p.hv));
   if (p.bf16) hipLaunchKernelGGL(k_commit_d128<bf16>, grid, dim3(256), smem, s, a);
   else hipLaunchKernelGGL(k_commit_d128<float>, grid, dim3(256), smem, s, a);
   return hipGetLastError();
